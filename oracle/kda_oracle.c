@@ -1,0 +1,144 @@
+/*
+ * KDA oracle: the gated delta rule with per-channel decay, token by token, in float64.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path links, loads or calls this file;
+ * only the test suite, the smoke check and the benchmark's CPU-baseline leg do. It shares
+ * no code with the HIP kernels.
+ *
+ * What it computes (Kimi Delta Attention). Each (sequence, head) keeps a d_k x d_v state
+ * S whose rows are key channels ("a fixed-size state matrix that does not grow with the
+ * sequence": KimiLinear page, section 2). Per token t, with log-decay g_t <= 0 per key
+ * channel, write strength beta_t, key k_t, value v_t and query q_t:
+ *
+ *   1. a   = exp(g_t)                 channel-wise forget gate (per-channel, "fine-grained"
+ *                                     gating: Kimi Linear page, the KDA section)
+ *   2. S  <- Diag(a) S                decay acts on the key channels (rows)
+ *   3. p   = S^T k_t                  what the decayed state predicts for k_t
+ *   4. S  <- S + beta_t k_t (v_t - p)^T
+ *                                     delta-rule erase-and-write; steps 2-4 together are
+ *                                     S_t = (I - beta k k^T) Diag(a) S_{t-1} + beta k v^T,
+ *                                     the erase term (I - beta k k^T) of KimiLinear page,
+ *                                     section 5
+ *   5. o_t = S^T (scale * q_t)        read-out with the updated state
+ *
+ * Plain float64 loops, no blocking or reordering beyond the definition; no compensated
+ * summation (relative error ~ d_k * 2^-53). Sequences and heads are independent, so the
+ * only parallelism is over (sequence, head) chains.
+ *
+ * Layouts (all dense, row-major, last dimension innermost):
+ *   q, k, g : [T_total, H, K]     v, o : [T_total, H, V]     beta : [T_total, H]
+ *   s0, s_out : [N, H, K, V]      cu_seqlens : [N + 1], cu[0] = 0, non-decreasing
+ * s0 may be NULL (zero initial state); s_out may be NULL (not written) and may alias s0.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static void chain(int64_t t0, int64_t t1, int64_t h, int64_t H, int64_t K, int64_t V,
+                  const double *q, const double *k, const double *v, const double *g,
+                  const double *beta, double scale, const double *s0, double *o,
+                  double *S, double *a, double *p)
+{
+    if (s0)
+        memcpy(S, s0, (size_t)(K * V) * sizeof(double));
+    else
+        memset(S, 0, (size_t)(K * V) * sizeof(double));
+
+    for (int64_t t = t0; t < t1; ++t) {
+        const double *qt = q + (t * H + h) * K;
+        const double *kt = k + (t * H + h) * K;
+        const double *gt = g + (t * H + h) * K;
+        const double *vt = v + (t * H + h) * V;
+        const double bt = beta[t * H + h];
+        double *ot = o + (t * H + h) * V;
+
+        /* 1-2: decay every key channel (row) of the state */
+        for (int64_t c = 0; c < K; ++c)
+            a[c] = exp(gt[c]);
+        for (int64_t c = 0; c < K; ++c)
+            for (int64_t j = 0; j < V; ++j)
+                S[c * V + j] *= a[c];
+
+        /* 3: prediction p = S^T k */
+        for (int64_t j = 0; j < V; ++j)
+            p[j] = 0.0;
+        for (int64_t c = 0; c < K; ++c)
+            for (int64_t j = 0; j < V; ++j)
+                p[j] += S[c * V + j] * kt[c];
+
+        /* 4: erase-and-write with the correction u = beta (v - p) */
+        for (int64_t j = 0; j < V; ++j)
+            p[j] = bt * (vt[j] - p[j]);
+        for (int64_t c = 0; c < K; ++c)
+            for (int64_t j = 0; j < V; ++j)
+                S[c * V + j] += kt[c] * p[j];
+
+        /* 5: read-out with the updated state */
+        for (int64_t j = 0; j < V; ++j)
+            ot[j] = 0.0;
+        for (int64_t c = 0; c < K; ++c) {
+            const double qc = scale * qt[c];
+            for (int64_t j = 0; j < V; ++j)
+                ot[j] += S[c * V + j] * qc;
+        }
+    }
+}
+
+/* Returns 0 on success, 1 on invalid arguments, 2 on allocation failure. */
+int kda_oracle_fwd(int64_t n_seqs, const int64_t *cu_seqlens, int64_t H, int64_t K, int64_t V,
+                   const double *q, const double *k, const double *v, const double *g,
+                   const double *beta, double scale, const double *s0, double *o,
+                   double *s_out, int nthreads)
+{
+    if (n_seqs < 0 || H <= 0 || K <= 0 || V <= 0 || !cu_seqlens)
+        return 1;
+    if (cu_seqlens[0] != 0)
+        return 1;
+    for (int64_t n = 0; n < n_seqs; ++n)
+        if (cu_seqlens[n + 1] < cu_seqlens[n])
+            return 1;
+    if (cu_seqlens[n_seqs] > 0 && (!q || !k || !v || !g || !beta || !o))
+        return 1;
+
+    const int64_t items = n_seqs * H;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel reduction(| : err)
+#endif
+    {
+        double *S = (double *)malloc((size_t)(K * V + K + V) * sizeof(double));
+        if (!S) {
+            err |= 2;
+        } else {
+            double *a = S + K * V, *p = a + K;
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t it = 0; it < items; ++it) {
+                const int64_t n = it / H, h = it % H;
+                const double *init = s0 ? s0 + (n * H + h) * K * V : NULL;
+                chain(cu_seqlens[n], cu_seqlens[n + 1], h, H, K, V, q, k, v, g, beta, scale,
+                      init, o, S, a, p);
+                if (s_out)
+                    memcpy(s_out + (n * H + h) * K * V, S, (size_t)(K * V) * sizeof(double));
+            }
+            free(S);
+        }
+    }
+    return err ? 2 : 0;
+}
+
+int kda_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,181 @@
+"""MI355X (gfx950) KDA core: Kimi Delta Attention's gated delta rule with per-channel decay.
+
+A thin binding over the C ABI of ``include/kda.h`` (``libkda.so``, built in-tree by
+``gated_delta_rule_26_amd/build.py``). The functions carry the C names and only marshal
+arguments: shapes and pointers are taken from torch tensors on the HIP device, outputs are
+allocated with torch, and every step of the computation runs in the library's HIP kernels
+on the caller's current torch stream. There is no CPU or PyTorch fallback: if the library
+is missing, loading fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["KdaError", "kda_chunk_fwd", "kda_decode_step", "load_library", "KDA_F32",
+           "KDA_BF16"]
+
+KDA_F32, KDA_BF16 = 0, 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
+           3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
+
+_LIB = None
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+
+class KdaError(RuntimeError):
+    """A non-OK kda_status, with the library's detail message."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libkda.so (once) and declare the C signatures. Raises if it is not built."""
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libkda.so not found at {p}: build it with "
+                           "`python gated_delta_rule_26_amd/build.py`")
+    lib = ctypes.CDLL(p)
+    i32, f32, vp, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [i32]
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_version.restype = i32
+    lib.kda_version.argtypes = []
+    lib.kda_chunk_fwd_workspace_bytes.restype = sz
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i32] * 8
+    lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.kda_decode_step.restype = i32
+    lib.kda_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, f32,
+                                    vp, vp, vp, vp, vp, vp, vp, vp]
+    if path is None:
+        _LIB = lib
+    return lib
+
+
+def _check(lib, status: int):
+    if status != 0:
+        raise KdaError(status, lib.kda_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _req(t, name, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a torch tensor on the HIP device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def kda_chunk_fwd(q, k, v, g, beta, *, initial_state=None, output_final_state: bool = True,
+                  final_state=None, cu_seqlens=None, chunk: int = 64, scale: float = 1.0,
+                  o=None, stream=None):
+    """Chunked KDA prefill (C: kda_chunk_fwd).
+
+    q, k: [B, T, H, Dk] (or [T, H, Dk] with ``cu_seqlens``), bf16 or float32, unit L2 norm
+    per token and head; v: [.., H, Dv] same dtype; g: float32 log-decay like q; beta:
+    float32 [.., H]; initial_state: float32 [N, H, Dk, Dv] or None (zeros); cu_seqlens:
+    int32 [N + 1] on the device (packed sequences, B = 1). ``final_state`` may be given
+    (it may be ``initial_state`` itself) or is allocated when ``output_final_state``.
+    Returns (o float32 [.., H, Dv], final_state or None).
+    """
+    import torch
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _req(t, nm, q.dtype)
+    _req(g, "g", torch.float32)
+    _req(beta, "beta", torch.float32)
+    if cu_seqlens is not None:
+        _req(cu_seqlens, "cu_seqlens", torch.int32)
+        if q.dim() == 4:
+            if q.shape[0] != 1:
+                raise ValueError("cu_seqlens requires B == 1")
+        B, T = 1, q.shape[-3]
+        N = cu_seqlens.numel() - 1
+    else:
+        if q.dim() != 4:
+            raise ValueError("q must be [B, T, H, Dk] without cu_seqlens")
+        B, T = q.shape[0], q.shape[1]
+        N = B
+    H, Dk = q.shape[-2], q.shape[-1]
+    Dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:-1] != q.shape[:-1] or \
+            beta.shape != q.shape[:-1]:
+        raise ValueError("inconsistent q/k/v/g/beta shapes")
+    if initial_state is not None:
+        _req(initial_state, "initial_state", torch.float32)
+        if tuple(initial_state.shape) != (N, H, Dk, Dv):
+            raise ValueError(f"initial_state must be [{N}, {H}, {Dk}, {Dv}]")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _req(final_state, "final_state", torch.float32)
+        if tuple(final_state.shape) != (N, H, Dk, Dv):
+            raise ValueError(f"final_state must be [{N}, {H}, {Dk}, {Dv}]")
+    if o is None:
+        o = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    else:
+        _req(o, "o", torch.float32)
+    ws = lib.kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, _dtype_code(q), N)
+    workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    st = lib.kda_chunk_fwd(B, T, H, Dk, Dv, chunk, _dtype_code(q), KDA_F32, float(scale),
+                           _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                           _ptr(initial_state), _ptr(final_state), _ptr(o),
+                           _ptr(cu_seqlens), N, _ptr(workspace), ws, _stream(stream))
+    _check(lib, st)
+    return o, final_state
+
+
+def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, o=None, stream=None):
+    """One KDA decode step (C: kda_decode_step): q, k, g [N, H, Dk]; v [N, H, Dv]; beta
+    [N, H]; ``state`` float32 [N, H, Dk, Dv] is updated in place. Returns o float32 [N, H, Dv]."""
+    import torch
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _req(t, nm, q.dtype)
+    _req(g, "g", torch.float32)
+    _req(beta, "beta", torch.float32)
+    _req(state, "state", torch.float32)
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or tuple(v.shape) != (N, H, Dv) or \
+            tuple(beta.shape) != (N, H) or tuple(state.shape) != (N, H, Dk, Dv):
+        raise ValueError("inconsistent decode shapes")
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=torch.float32, device=q.device)
+    else:
+        _req(o, "o", torch.float32)
+    st = lib.kda_decode_step(N, H, Dk, Dv, _dtype_code(q), KDA_F32, float(scale),
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                             _ptr(o), _stream(stream))
+    _check(lib, st)
+    return o

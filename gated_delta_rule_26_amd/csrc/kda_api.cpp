@@ -1,0 +1,156 @@
+// C ABI of libkda (include/kda.h): host-side argument validation and kernel dispatch.
+// Every check runs before any HIP call, so invalid requests launch nothing and leave the
+// outputs untouched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kda_status fail(kda_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kda_status ok() {
+    g_err[0] = '\0';
+    return KDA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int32_t d) { return d == KDA_F32 || d == KDA_BF16; }
+
+kda_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(int32_t status) {
+    switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    default: return "KDA_ERR_UNKNOWN";
+    }
+}
+
+const char *kda_last_error(void) { return g_err; }
+
+int32_t kda_version(void) { return (1 << 16) | 0; }
+
+size_t kda_chunk_fwd_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,
+                                     int32_t, int32_t) {
+    return 0;
+}
+
+kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                         int32_t in_dtype, int32_t out_dtype, float scale,
+                         const void *q, const void *k, const void *v,
+                         const float *g, const float *beta,
+                         const float *initial_state, float *final_state, void *o,
+                         const int32_t *cu_seqlens, int32_t num_seqs,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    (void)workspace;
+    if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || chunk < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive (B=%d T=%d H=%d Dk=%d Dv=%d chunk=%d)",
+                    B, T, H, Dk, Dv, chunk);
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype code (in=%d out=%d)", in_dtype, out_dtype);
+    if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (cu_seqlens) {
+        if (B != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens requires B == 1 (got B=%d)", B);
+        if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
+    } else if (num_seqs != B) {
+        return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs (%d) must equal B (%d) without cu_seqlens",
+                    num_seqs, B);
+    }
+    const int64_t tokens = (int64_t)B * T;
+    if (tokens * H * (Dk > Dv ? Dk : Dv) > ((int64_t)1 << 40))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "problem too large");
+    if (tokens > 0 && (!q || !k || !v || !g || !beta || !o))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and o are required");
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    if (workspace_bytes < kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, in_dtype, num_seqs))
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+    if (out_dtype != KDA_F32) return fail(KDA_ERR_UNSUPPORTED, "only float32 o is supported");
+    if (!kda::chunk_fwd_supported(in_dtype, chunk, Dk, Dv))
+        return fail(KDA_ERR_UNSUPPORTED, "no instantiation for in_dtype=%d chunk=%d Dk=%d Dv=%d",
+                    in_dtype, chunk, Dk, Dv);
+    if (num_seqs == 0) return ok();
+
+    kda::ChunkArgs a;
+    a.n_seqs = num_seqs;
+    a.seq_len = T;
+    a.cu_seqlens = cu_seqlens;
+    a.H = H;
+    a.scale = scale;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.s0 = initial_state;
+    a.s_out = final_state;
+    a.o = static_cast<float *>(o);
+    return hip_status(kda::launch_chunk_fwd(in_dtype, chunk, Dk, Dv, a,
+                                            static_cast<hipStream_t>(stream)),
+                      "kda_chunk_fwd launch");
+}
+
+kda_status kda_decode_step(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
+                           int32_t in_dtype, int32_t out_dtype, float scale,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           float *state, void *o, void *stream) {
+    if (N < 0 || H < 1 || Dk < 1 || Dv < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes (N=%d H=%d Dk=%d Dv=%d)", N, H, Dk, Dv);
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype code (in=%d out=%d)", in_dtype, out_dtype);
+    if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if ((int64_t)N * H > 0x7fffffff) return fail(KDA_ERR_INVALID_ARGUMENT, "N*H too large");
+    if (N > 0 && (!q || !k || !v || !g || !beta || !state || !o))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, g, beta, state and o are required");
+    const void *ptrs[] = {q, k, v, g, beta, state, o};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    if (out_dtype != KDA_F32) return fail(KDA_ERR_UNSUPPORTED, "only float32 o is supported");
+    if (!kda::decode_supported(in_dtype, Dk, Dv))
+        return fail(KDA_ERR_UNSUPPORTED, "no decode instantiation for in_dtype=%d Dk=%d Dv=%d",
+                    in_dtype, Dk, Dv);
+    if (N == 0) return ok();
+    kda::DecodeArgs a;
+    a.N = N;
+    a.H = H;
+    a.scale = scale;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.o = static_cast<float *>(o);
+    return hip_status(kda::launch_decode(in_dtype, Dk, Dv, a, static_cast<hipStream_t>(stream)),
+                      "kda_decode_step launch");
+}
+
+}  // extern "C"

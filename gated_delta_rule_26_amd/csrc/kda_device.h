@@ -1,0 +1,185 @@
+// Device-side helpers shared by the KDA kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Storage type of bf16 inputs: raw 16-bit patterns.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ __bf16 f32_to_bf16(float x) { return static_cast<__bf16>(x); }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
+
+// Two consecutive input elements as floats (8-byte or 4-byte aligned load).
+__device__ __forceinline__ f32x2 load2(const float *p) { return *reinterpret_cast<const f32x2 *>(p); }
+__device__ __forceinline__ f32x2 load2(const bf16_t *p) {
+    const uint32_t u = *reinterpret_cast<const uint32_t *>(p);
+    f32x2 r;
+    r.x = __uint_as_float(u << 16);
+    r.y = __uint_as_float(u & 0xffff0000u);
+    return r;
+}
+
+// Four consecutive input elements as floats.
+__device__ __forceinline__ f32x4 load4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ f32x4 load4(const bf16_t *p) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    f32x4 r;
+    r.x = __uint_as_float(u.x << 16);
+    r.y = __uint_as_float(u.x & 0xffff0000u);
+    r.z = __uint_as_float(u.y << 16);
+    r.w = __uint_as_float(u.y & 0xffff0000u);
+    return r;
+}
+
+// ---------------------------------------------------------------------------------------
+// 16x16 matrix-core tiles.
+//
+// Both operand fragments of a 16 x 16 x 16 product are read the same way: lane l holds
+// "row" (l % 16) and the four consecutive reduction indices 4*(l/16) .. 4*(l/16)+3. For the
+// A operand the row is an output row; for the B operand it is an output column, so B is
+// stored transposed ([n][k]). The accumulator holds D[4*(l/16) + e][l % 16], e = 0..3,
+// which is also exactly the B-fragment layout of a [k][n] operand with k = row: a product
+// can feed the next one as its B operand without leaving registers.
+//
+// OP = __bf16: one v_mfma_f32_16x16x16_bf16.
+// OP = _Float16: one v_mfma_f32_16x16x16_f16.
+// OP = float : four v_mfma_f32_16x16x4_f32; instruction e takes reduction index 4*(l/16)+e
+//              from every lane, so the four together cover all 16 indices.
+// ---------------------------------------------------------------------------------------
+template <typename OP> struct Mma;
+
+template <> struct Mma<__bf16> {
+    typedef __bf16 elem;
+    typedef bf16x4 frag;
+    static __device__ __forceinline__ frag load(const __bf16 *p) {
+        return *reinterpret_cast<const frag *>(p);
+    }
+    static __device__ __forceinline__ frag from_f32(f32x4 x) {
+        frag r;
+        r.x = f32_to_bf16(x.x);
+        r.y = f32_to_bf16(x.y);
+        r.z = f32_to_bf16(x.z);
+        r.w = f32_to_bf16(x.w);
+        return r;
+    }
+    static __device__ __forceinline__ f32x4 to_f32(frag x) {
+        f32x4 r;
+        r.x = static_cast<float>(x.x);
+        r.y = static_cast<float>(x.y);
+        r.z = static_cast<float>(x.z);
+        r.w = static_cast<float>(x.w);
+        return r;
+    }
+    static __device__ __forceinline__ void mma(f32x4 &acc, frag a, frag b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                         __builtin_bit_cast(i16x4, b), acc, 0, 0, 0);
+    }
+    // acc += a * b with both factors given in float32, to ~float32 accuracy: each factor is
+    // split into a bf16 head and a bf16 tail, and the three leading cross products are summed.
+    static __device__ __forceinline__ void mma_split(f32x4 &acc, f32x4 a, f32x4 b) {
+        const frag ah = from_f32(a), bh = from_f32(b);
+        const frag al = from_f32(a - to_f32(ah)), bl = from_f32(b - to_f32(bh));
+        mma(acc, al, bh);
+        mma(acc, ah, bl);
+        mma(acc, ah, bh);
+    }
+    static __device__ __forceinline__ void store_pair(__bf16 *p, float a, float b) {
+        bf16x2 v;
+        v.x = f32_to_bf16(a);
+        v.y = f32_to_bf16(b);
+        *reinterpret_cast<bf16x2 *>(p) = v;
+    }
+    static __device__ __forceinline__ void store4(__bf16 *p, f32x4 x) {
+        *reinterpret_cast<frag *>(p) = from_f32(x);
+    }
+};
+
+// OP = _Float16: one v_mfma_f32_16x16x16_f16. Same fragment layouts as bf16; 3 more
+// mantissa bits, 8x smaller rounding error, but a narrow exponent range (about 2^+-15).
+template <> struct Mma<_Float16> {
+    typedef _Float16 elem;
+    typedef f16x4 frag;
+    static __device__ __forceinline__ frag load(const _Float16 *p) {
+        return *reinterpret_cast<const frag *>(p);
+    }
+    static __device__ __forceinline__ frag from_f32(f32x4 x) {
+        frag r;
+        r.x = static_cast<_Float16>(x.x);
+        r.y = static_cast<_Float16>(x.y);
+        r.z = static_cast<_Float16>(x.z);
+        r.w = static_cast<_Float16>(x.w);
+        return r;
+    }
+    static __device__ __forceinline__ f32x4 to_f32(frag x) {
+        f32x4 r;
+        r.x = static_cast<float>(x.x);
+        r.y = static_cast<float>(x.y);
+        r.z = static_cast<float>(x.z);
+        r.w = static_cast<float>(x.w);
+        return r;
+    }
+    static __device__ __forceinline__ void mma(f32x4 &acc, frag a, frag b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, acc, 0, 0, 0);
+    }
+    // float32-accurate product with float32's range: bf16 head and tail of each factor
+    static __device__ __forceinline__ void mma_split(f32x4 &acc, f32x4 a, f32x4 b) {
+        Mma<__bf16>::mma_split(acc, a, b);
+    }
+    static __device__ __forceinline__ void store_pair(_Float16 *p, float a, float b) {
+        f16x2 v;
+        v.x = static_cast<_Float16>(a);
+        v.y = static_cast<_Float16>(b);
+        *reinterpret_cast<f16x2 *>(p) = v;
+    }
+    static __device__ __forceinline__ void store4(_Float16 *p, f32x4 x) {
+        *reinterpret_cast<frag *>(p) = from_f32(x);
+    }
+};
+
+template <> struct Mma<float> {
+    typedef float elem;
+    typedef f32x4 frag;
+    static __device__ __forceinline__ frag load(const float *p) {
+        return *reinterpret_cast<const frag *>(p);
+    }
+    static __device__ __forceinline__ frag from_f32(f32x4 x) { return x; }
+    static __device__ __forceinline__ f32x4 to_f32(frag x) { return x; }
+    static __device__ __forceinline__ void mma(f32x4 &acc, frag a, frag b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+    }
+    static __device__ __forceinline__ void mma_split(f32x4 &acc, f32x4 a, f32x4 b) { mma(acc, a, b); }
+    static __device__ __forceinline__ void store_pair(float *p, float a, float b) {
+        f32x2 v;
+        v.x = a;
+        v.y = b;
+        *reinterpret_cast<f32x2 *>(p) = v;
+    }
+    static __device__ __forceinline__ void store4(float *p, f32x4 x) {
+        *reinterpret_cast<f32x4 *>(p) = x;
+    }
+};
+
+}  // namespace kda

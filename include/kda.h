@@ -1,0 +1,147 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) KDA core: Kimi Delta Attention, the gated delta rule
+ * with a per-channel (fine-grained) forget gate.
+ *
+ * The operation (per sequence n and head h, over its tokens t = 1..L_n):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T (scale * q_t)
+ *
+ * Sources (web pages on Kimi Linear; short names used throughout this code):
+ *   [KV-cache page]  "Starting from the KV-cache explosion: what KimiLinear's linear
+ *                    attention solves" (hands-on guide, sections 1-6)
+ *   [loading page]   "Starting from a loading error: configuring Kimi Linear's KDA and
+ *                    NoPE" (walk-through of the modelling code, sections 1-6)
+ *   [overview page]  "How to fit a million tokens on an ordinary GPU with Kimi Linear"
+ *   [revolution page] "Linear attention revolution: Kimi Linear ..." (model overview)
+ *
+ * S is a d_k x d_v state per (sequence, head) whose rows are key channels: KDA keeps a
+ * fixed-size state matrix that does not grow with the sequence ([KV-cache page] section 2).
+ * exp(g_t) is KDA's channel-wise forget gate, the fine-grained gating that refines Gated
+ * DeltaNet ([revolution page], the KDA section; [overview page], "How Kimi Delta Attention
+ * works"). (I - beta k k^T) is the delta-rule erase term, which keeps the state bounded only
+ * for unit-norm keys ([KV-cache page] section 5: without L2-normalised q and k the state
+ * blows up to NaN). The library does not normalise: callers pass normalised q and k.
+ *
+ * Two entry points do the work:
+ *   kda_chunk_fwd    prefill: the chunkwise-parallel form of the recurrence ([KV-cache page]
+ *                    section 3: chunk_size 64; section 6: chunked parallel form with a WY
+ *                    representation), over fixed-length batches or packed variable-length
+ *                    sequences, with optional initial and final states. It computes exactly
+ *                    the recurrence above, up to floating-point rounding.
+ *   kda_decode_step  one token per (sequence, head) on a persistent float32 state, updated in
+ *                    place (the token-by-token "fused_recurrent" mode and the recurrent state
+ *                    that the decode cache carries across calls: [loading page] sections 2,
+ *                    5 and 6).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers. Every tensor pointer is a DEVICE pointer (HIP device memory) owned by the
+ *   caller; the library allocates nothing and keeps no per-call state. Tensors are dense and
+ *   contiguous with the last dimension innermost ("... h d" layout), and 16-byte aligned.
+ * - Dtypes. q, k, v are KDA_F32 or KDA_BF16 (in_dtype); g (log-decay, <= 0), beta, states
+ *   and o are float32 (out_dtype must be KDA_F32).
+ * - Streams. `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work on
+ *   it and never synchronise the host. Calls on different streams are independent.
+ * - Errors. Arguments are validated on the host before any HIP call: on an error nothing is
+ *   launched and no output is touched. A failed launch returns KDA_ERR_HIP. The message of
+ *   the last error on the calling thread is available from kda_last_error().
+ * - Not checked (preconditions): the contents of device arrays (cu_seqlens values, NaN or
+ *   Inf inputs, which propagate), and overlaps between outputs and inputs other than the
+ *   allowed final_state == initial_state aliasing.
+ * - Supported sizes: see kda_chunk_fwd and kda_decode_step.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* NULL or misaligned pointer, bad size, bad dtype code */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid request with no compiled instantiation */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 3,
+    KDA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} kda_status;
+
+typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Human-readable name of a status code (static storage). */
+const char *kda_status_string(int32_t status);
+
+/* Detail of the last non-OK status returned on the calling thread (static, thread-local
+ * storage; empty string if none). */
+const char *kda_last_error(void);
+
+/* Library version, (major << 16) | minor. */
+int32_t kda_version(void);
+
+/*
+ * kda_chunk_fwd_workspace_bytes - device workspace kda_chunk_fwd needs for these sizes.
+ * Currently 0 for every supported configuration; callers may pass workspace = NULL.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                                     int32_t chunk, int32_t in_dtype, int32_t num_seqs);
+
+/*
+ * kda_chunk_fwd - chunked prefill.
+ *
+ * Sequences. Without cu_seqlens: B sequences of T tokens each (num_seqs must equal B), and
+ * the token index of (b, t) is b*T + t. With cu_seqlens (device int32 [num_seqs + 1],
+ * cu[0] = 0, non-decreasing, cu[num_seqs] = T): B must be 1 and sequence n is tokens
+ * cu[n] .. cu[n+1]-1 of the packed batch; zero-length sequences are allowed (their final
+ * state is their initial state). T = 0 is allowed.
+ *
+ *   q, k          [B*T, H, Dk]  in_dtype, unit L2 norm per (token, head)
+ *   v             [B*T, H, Dv]  in_dtype
+ *   g             [B*T, H, Dk]  float32 log-decay (the gate is exp(g) <= 1)
+ *   beta          [B*T, H]      float32 write strength in [0, 1]
+ *   initial_state [N, H, Dk, Dv] float32, or NULL for zeros (N = num_seqs)
+ *   final_state   [N, H, Dk, Dv] float32 output, or NULL to skip; may equal initial_state
+ *                 (exact aliasing: each state is read before it is overwritten)
+ *   o             [B*T, H, Dv]  out_dtype (KDA_F32)
+ *   chunk         tokens per chunk of the chunkwise form (a tuning choice: every chunk
+ *                 size gives the same result up to rounding)
+ *   scale         multiplies q (finite)
+ *   workspace     device buffer of at least kda_chunk_fwd_workspace_bytes(...) bytes
+ *
+ * Compiled instantiations (in_dtype, chunk, Dk = Dv):
+ *   (KDA_BF16, 64, 128)   bf16 matrix-core path, float32 accumulation and state
+ *   (KDA_F32, 16, 16), (KDA_F32, 64, 32), (KDA_F32, 64, 64)
+ *                         float32 matrix-core path (reference-precision instantiations)
+ * Other combinations return KDA_ERR_UNSUPPORTED.
+ */
+kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                         int32_t in_dtype, int32_t out_dtype, float scale,
+                         const void *q, const void *k, const void *v,
+                         const float *g, const float *beta,
+                         const float *initial_state, float *final_state, void *o,
+                         const int32_t *cu_seqlens, int32_t num_seqs,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_decode_step - one recurrent step for N independent (sequence, head) states.
+ *
+ *   q, k    [N, H, Dk] in_dtype (unit L2 norm)     v [N, H, Dv] in_dtype
+ *   g       [N, H, Dk] float32 log-decay             beta [N, H] float32
+ *   state   [N, H, Dk, Dv] float32, read and updated in place (S_{t-1} -> S_t)
+ *   o       [N, H, Dv] out_dtype (KDA_F32): S_t^T (scale * q)
+ *
+ * Dk = Dv in {16, 32, 64, 128}; in_dtype KDA_F32 or KDA_BF16.
+ */
+kda_status kda_decode_step(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
+                           int32_t in_dtype, int32_t out_dtype, float scale,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           float *state, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

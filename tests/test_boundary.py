@@ -1,0 +1,118 @@
+"""The C ABI (include/kda.h) without a GPU: the library loads, exports every declared
+entry point, and rejects invalid requests on the host before any HIP call.
+
+Invalid calls pass fake, aligned, non-NULL pointers: validation must return before anything
+dereferences them or touches the HIP runtime (there is no GPU here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_26_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+P = ctypes.c_void_p(0x100000)     # fake aligned device pointer, never dereferenced
+MIS = ctypes.c_void_p(0x100004)   # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load_library()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_last_error",
+              "kda_version", "kda_chunk_fwd_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.kda_status_string(OK) == b"KDA_OK"
+    assert lib.kda_status_string(INVALID) == b"KDA_ERR_INVALID_ARGUMENT"
+    assert lib.kda_status_string(UNSUPPORTED) == b"KDA_ERR_UNSUPPORTED"
+    assert lib.kda_status_string(WS_SMALL) == b"KDA_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.kda_status_string(HIP) == b"KDA_ERR_HIP"
+    assert lib.kda_status_string(99) == b"KDA_ERR_UNKNOWN"
+    assert lib.kda_version() >> 16 >= 1
+
+
+def test_workspace_is_zero(lib):
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, 64, BF16, 1) == 0
+
+
+def chunk(lib, B=1, T=64, H=2, Dk=128, Dv=128, C=64, ind=BF16, outd=F32, scale=1.0,
+          q=P, k=P, v=P, g=P, beta=P, s0=None, s1=None, o=P, cu=None, N=None, ws=None, wsb=0):
+    N = B if N is None else N
+    return lib.kda_chunk_fwd(B, T, H, Dk, Dv, C, ind, outd, scale, q, k, v, g, beta, s0, s1,
+                             o, cu, N, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), INVALID), (dict(T=-1), INVALID), (dict(H=0), INVALID),
+    (dict(Dk=0), INVALID), (dict(C=0), INVALID),
+    (dict(ind=7), INVALID), (dict(outd=-1), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(B=2, cu=P, N=1), INVALID), (dict(cu=P, N=-1), INVALID), (dict(B=2, N=1), INVALID),
+    (dict(q=None), INVALID), (dict(g=None), INVALID), (dict(o=None), INVALID),
+    (dict(beta=None), INVALID),
+    (dict(k=MIS), INVALID), (dict(s0=MIS), INVALID), (dict(cu=MIS), INVALID),
+    (dict(Dk=96, Dv=96), UNSUPPORTED), (dict(Dk=128, Dv=64), UNSUPPORTED),
+    (dict(C=32), UNSUPPORTED), (dict(ind=F32), UNSUPPORTED), (dict(outd=BF16), UNSUPPORTED),
+    (dict(ind=F32, Dk=16, Dv=16, C=64), UNSUPPORTED),
+])
+def test_chunk_fwd_rejects_before_launch(lib, kw, status):
+    assert chunk(lib, **kw) == status
+    assert len(lib.kda_last_error()) > 0
+
+
+def test_chunk_fwd_empty_work_is_ok_without_launch(lib):
+    # zero sequences in a packed batch: nothing to compute, no HIP call
+    assert chunk(lib, T=0, cu=P, N=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+    assert lib.kda_last_error() == b""
+
+
+def decode(lib, N=4, H=2, Dk=128, Dv=128, ind=BF16, outd=F32, scale=1.0, q=P, k=P, v=P, g=P,
+           beta=P, state=P, o=P):
+    return lib.kda_decode_step(N, H, Dk, Dv, ind, outd, scale, q, k, v, g, beta, state, o, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), INVALID), (dict(H=0), INVALID), (dict(Dk=0), INVALID), (dict(ind=3), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(state=None), INVALID), (dict(o=None), INVALID),
+    (dict(q=MIS), INVALID), (dict(N=70000, H=40000), INVALID),
+    (dict(Dk=96, Dv=96), UNSUPPORTED), (dict(Dk=128, Dv=64), UNSUPPORTED),
+    (dict(Dk=256, Dv=256), UNSUPPORTED), (dict(outd=BF16), UNSUPPORTED),
+])
+def test_decode_rejects_before_launch(lib, kw, status):
+    assert decode(lib, **kw) == status
+    assert len(lib.kda_last_error()) > 0
+
+
+def test_decode_zero_sequences_is_ok(lib):
+    assert decode(lib, N=0, q=None, k=None, v=None, g=None, beta=None, state=None, o=None) == OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not found"):
+        kda.load_library(str(tmp_path / "missing.so"))
+
+
+def test_binding_raises_kda_error_type():
+    e = kda.KdaError(2, "no instantiation")
+    assert e.status == 2 and "KDA_ERR_UNSUPPORTED" in str(e)

@@ -1,0 +1,244 @@
+"""Benchmark of the KDA core on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  1. kda_chunk_fwd on the long-context prefill workload (B=1, T=131072, H=32,
+     Dk=Dv=128, chunk 64, bf16 q/k/v, float32 gates, zero initial state, float32 o and
+     final state), and
+  2. one kda_decode_step on the decode workload (256 sequences x 32 heads of float32
+     128x128 states, built by a 2048-token prefill of the same-style inputs; one bf16 token
+     per sequence and head per step).
+
+Inputs are generated on the host (seeded, synth/) and are resident in HBM before the timed
+region. The headline value is prefill tokens/s (H=32, d=128); the decode step's state
+bandwidth is reported next to it. Per-kernel times come from HIP events recorded on the
+stream the kernels run on. The roofline fraction uses algorithmic bytes per launch.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (H=32,d=128) + decode state-update HBM GB/s, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_prefill_128k_h32_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_26_amd", "csrc", "kda_chunk.hip")
+
+
+def prefill_bytes_per_token_head(K: int, V: int) -> int:
+    """Algorithmic HBM bytes per (token, head): bf16 q and k, bf16 v, float32 g, float32
+    beta, float32 o."""
+    return 2 * K * 2 + V * 2 + K * 4 + 4 + V * 4
+
+
+def prefill_flops_per_token_head(K: int, V: int, C: int) -> float:
+    """Algorithmic flops per (token, head) of the chunkwise form: per chunk 3C^2K + 2C^2V +
+    6CKV + C^3/3 (A, M and W; U~ and M U; W S, (q e^G) S and the state update; the
+    triangular inverse)."""
+    return (3 * C * C * K + 2 * C * C * V + 6 * C * K * V + C ** 3 / 3) / C
+
+
+def decode_bytes_per_step(N: int, H: int, K: int, V: int) -> int:
+    """State read + write (float32) plus one bf16 q, k, v, float32 g, beta and float32 o per
+    (sequence, head)."""
+    return 2 * N * H * K * V * 4 + N * H * (2 * K * 2 + V * 2 + K * 4 + 4) + N * H * V * 4
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(launch_bytes: float):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, or None when it is
+    missing or was taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x: dict, sample_tokens: int) -> dict:
+    """The float64 oracle (unchanged) on the first ``sample_tokens`` tokens of the prefill
+    workload, all heads, on the host's cores."""
+    import numpy as np
+
+    import oracle
+    import synth
+    threads = min(os.cpu_count() or 1, x["q"].shape[1])
+    sl = slice(0, sample_tokens)
+    args = (synth.stored_to_f64(x["q"][sl], "bf16"), synth.stored_to_f64(x["k"][sl], "bf16"),
+            synth.stored_to_f64(x["v"][sl], "bf16"), x["g"][sl].astype(np.float64),
+            x["beta"][sl].astype(np.float64))
+    t0 = time.perf_counter()
+    oracle.kda_fwd(*args, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"prefill_128k_h32, first {sample_tokens} tokens x {x['q'].shape[1]} heads "
+                      f"(float64 recurrence, {dt:.1f} s wall)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
+    ap.add_argument("--decode-seqs", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the KDA core needs no collectives: (sequence, head) chains are independent)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_26_amd as kda
+    import synth
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    dev = "cuda"
+    to_dev = lambda a, bf=False: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16))  # noqa: E731
+                                  .view(torch.bfloat16) if bf else torch.from_numpy(a)).to(dev)
+
+    # ---------------------------------------------------------------- prefill workload
+    wp = synth.WORKLOADS["prefill_128k_h32"]
+    t0 = time.perf_counter()
+    xp = synth.make_inputs(wp)
+    log(f"generated prefill inputs in {time.perf_counter() - t0:.1f}s")
+    T, H, K, V, C = wp.T, wp.H, wp.K, wp.V, wp.chunk
+    pq, pk, pv = (to_dev(xp[n][None], True) for n in ("q", "k", "v"))
+    pg, pb = to_dev(xp["g"][None]), to_dev(xp["beta"][None])
+    po = torch.empty((1, T, H, V), dtype=torch.float32, device=dev)
+    pS = torch.empty((1, H, K, V), dtype=torch.float32, device=dev)
+
+    # ----------------------------------------------------------------- decode workload
+    wd = synth.WORKLOADS["decode_256x32"]
+    nsteps = args.warmup + args.steps
+    wd = wd.with_(decode_steps=nsteps)
+    t0 = time.perf_counter()
+    xd = synth.make_inputs(wd, seqs=range(args.decode_seqs))
+    log(f"generated decode inputs in {time.perf_counter() - t0:.1f}s")
+    N = args.decode_seqs
+    dq, dk, dv = (to_dev(xd[n].reshape(N, wd.prefill_T, H, K), True) for n in ("q", "k", "v"))
+    dg = to_dev(xd["g"].reshape(N, wd.prefill_T, H, K))
+    db = to_dev(xd["beta"].reshape(N, wd.prefill_T, H))
+    state = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    kda.kda_chunk_fwd(dq, dk, dv, dg, db, final_state=state)  # the 2048-token prefill
+    del dq, dk, dv, dg, db
+    tq, tk, tv = (to_dev(xd["dec_" + n], True) for n in ("q", "k", "v"))
+    tg, tb = to_dev(xd["dec_g"]), to_dev(xd["dec_beta"])
+    to = torch.empty((N, H, V), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log("inputs resident in HBM")
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev:
+            ev[0].record(stream)
+        kda.kda_chunk_fwd(pq, pk, pv, pg, pb, final_state=pS, o=po)
+        if ev:
+            ev[1].record(stream)
+        kda.kda_decode_step(tq[i], tk[i], tv[i], tg[i], tb[i], state, o=to)
+        if ev:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+
+    tok_s = T / (pre_avg * 1e-3)
+    p_bytes = T * H * prefill_bytes_per_token_head(K, V) + H * K * V * 4  # + final state
+    p_flops = T * H * prefill_flops_per_token_head(K, V, C)
+    achieved_gbs = p_bytes / (pre_avg * 1e-3) / 1e9
+    d_bytes = decode_bytes_per_step(N, H, K, V)
+    d_gbs = d_bytes / (dec_avg * 1e-3) / 1e9
+
+    traffic = load_traffic(p_bytes)
+    res = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill_128k_h32 + decode_256x32",
+            "prefill": {"B": 1, "T": T, "H": H, "dk": K, "dv": V, "chunk": C,
+                        "inputs": "bf16 q/k/v, f32 g/beta", "outputs": "f32 o and final state"},
+            "decode": {"N": N, "H": H, "dk": K, "dv": V, "state": "f32, updated in place",
+                       "state_init": "2048-token prefill"},
+            "compute": "fp16 matrix-core operands, f32 accumulation and state",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kda_chunk_fwd (prefill_128k_h32)",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": p_bytes,
+            "avg_launch_ms": round(pre_avg, 4),
+            "mfma_frac_algorithmic": round(p_flops / (pre_avg * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        },
+        "decode": {
+            "kernel": "kda_decode_step (decode_256x32)",
+            "avg_launch_us": round(dec_avg * 1e3, 2),
+            "steps_per_s": round(1e3 / dec_avg, 1),
+            "tokens_per_s": round(N * 1e3 / dec_avg, 1),
+            "achieved_gbs": round(d_gbs, 1),
+            "peak_gbs": HBM_PEAK_GBS,
+            "frac": round(d_gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_step": d_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(xp, min(args.cpu_sample_tokens, T))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,23 +14,25 @@
 // which equals the token-by-token recurrence S_t = (I - beta k k^T) Diag(e^g) S + beta k v^T,
 // o_t = S_t^T (scale q) exactly up to rounding (unroll the recurrence inside the chunk).
 //
-// Mapping to the MI355X:
-// * One workgroup (4 waves) runs one chain: a (sequence, head, V-block of VB columns). The
-//   chunks of a chain are sequential; columns of S evolve independently (column j of U, O
-//   and S' only depends on column j of S), so V-blocks multiply the parallelism. Workgroups
-//   of one (sequence, head) get the same blockIdx % 8, i.e. the same XCD and L2, which then
-//   serves the q/k/g tiles they all read.
-// * The state stays on chip for the whole sequence: each wave owns a fixed set of 16x16
-//   tiles of S in float32 accumulator registers, and a transposed bf16 copy sits in LDS as
-//   the matrix-core operand.
-// * All C x C and C x D products are 16x16 matrix-core tiles (bf16 inputs, float32
-//   accumulation; a float32 instantiation uses the float32 matrix cores).
-// * Decay factors never overflow: inside a chunk every e^{G_i - G_j} is split at a 16-token
-//   block boundary, so each operand carries a factor <= 1 (or, inside one diagonal 16x16
-//   block, at most the inverse decay of 16 tokens). Only one exp per (token, channel).
-// * T is built in float32: forward substitution on the four diagonal 16x16 blocks, then
-//   block merges T_IJ = -T_II sum_K A_IK T_KJ on the matrix cores with each float32 factor
-//   split into a bf16 head and tail (about float32 accuracy).
+// Mapping to the MI355X (one workgroup of NW waves per (sequence, head) chain):
+// * The chunks of a chain run in order; everything inside a chunk is parallel. Each wave
+//   owns DV/(16 NW) 16-column tiles of the state for the whole sequence, in float32
+//   accumulator registers. The state pass (U, O, S update) runs entirely from registers:
+//   an accumulator tile is directly a matrix-core B fragment, so the only shared operands
+//   are the per-chunk A-side matrices in LDS and the state pass has no barrier.
+// * The next chunk's q, k, g and beta are loaded into registers while the current chunk
+//   computes (all loads unconditional; rows past the sequence end are clamped and masked).
+// * Decay factors never overflow: inside a chunk every e^{G_i - G_j} is split at a
+//   16-token block boundary, so each operand carries a factor <= 1 or, inside a diagonal
+//   16x16 block, at most the inverse decay of 16 tokens. One exp per (token, channel).
+//   With fp16 operands each channel of a block is balanced by a power of two near
+//   D^(-1/2) (D = the block's decay), keeping every factor within fp16's range; a chunk in
+//   which some block decays below e^-20 computes A and M with bf16 operands instead, with
+//   the diagonal of M (q_i . k_i, no decay) added exactly in float32.
+// * T is never formed beyond its 16x16 diagonal blocks: those are inverted in registers as
+//   (I - L)(I + L^2)(I + L^4)(I + L^8) on the matrix cores (float32-accurate split-bf16
+//   products, transposes by products with the identity), and W and U~ come from block
+//   forward substitution (I + A) W = beta k e^G, (I + A) U~ = Diag(beta) V.
 #include <type_traits>
 
 #include "kda_device.h"
@@ -41,58 +43,65 @@ namespace {
 
 constexpr int align16(int x) { return (x + 15) & ~15; }
 
-template <typename OP, int C, int DK, int DV, int VB> struct ChunkShape {
-    static constexpr int NT = 256;
+template <typename T> struct Tag {
+    typedef T type;
+};
+
+// A 16-token block whose decay reaches this (per channel) is "extreme": its balanced
+// fp16 decay factors (up to 2^(-log2(D)/2)) would leave fp16's range.
+constexpr float kExtremeBlockDecay = 2.0611536e-9f;  // e^-20
+
+template <typename OP, int C, int DK, int DV, int NW> struct ChunkShape {
+    static constexpr int NT = 64 * NW;
     static constexpr int NB = C / 16;                       // 16-token blocks per chunk
     static constexpr int NFAR = (NB - 1) * (NB - 2) / 2;    // block pairs (J, I), I >= J + 2
-    static constexpr int PAD = 16 / (int)sizeof(OP);         // 16-byte row padding
-    static constexpr int LDK = DK + PAD;                     // [token][channel] operand rows
-    static constexpr int LDC = C + PAD;                      // [channel or column][token] rows
-    static constexpr int LCF = C + 4;                        // float32 [token][token] rows
-    static constexpr int NVB = DV / VB;
-    static constexpr int VT = VB / 16;                       // 16-wide column tiles per V-block
+    static constexpr int PAD = 16 / (int)sizeof(OP);        // 16-byte row padding
+    static constexpr int LDK = DK + PAD;                    // [token][channel] operand rows
+    static constexpr int LDC = C + PAD;                     // [channel][token] operand rows
+    static constexpr int LCF = C + 4;                       // float32 [token][token] rows
     static constexpr int KT = DK / 16;
-    static constexpr int NUT = NB * VT;                      // U / O tiles
-    static constexpr int NST = KT * VT;                      // state tiles
-    static constexpr int UPW = (NUT + 3) / 4;
-    static constexpr int SPW = (NST + 3) / 4;
-    static constexpr int NBLK = NB * (NB + 1) / 2;           // lower 16x16 blocks of a C x C
-    static constexpr int AMPW = (2 * NBLK + 3) / 4;
-    static constexpr int NPAIR = NB * DK / 2;                // (block, channel pair) jobs
-    static constexpr int WPW = (NB * KT + 3) / 4;
+    static constexpr int VT = DV / 16;
+    static constexpr int CPW = VT >= NW ? VT / NW : 1;      // state column tiles per wave
+    static constexpr int WPW = KT >= NW ? KT / NW : 1;      // W column tiles per wave
+    static constexpr int NOFF = NB * (NB - 1);              // off-diagonal A and M blocks
+    static constexpr int OFFW = NW > NB ? NW - NB : NW;     // waves doing off-diagonal jobs
+    static constexpr int OPW = NOFF > 0 ? (NOFF + OFFW - 1) / OFFW : 1;
+    static constexpr int NGRP = DK >= 64 ? DK / 64 : 1;     // 32-lane channel groups
+    static constexpr int NVJ = (C / 4) * (DV / 4);          // 4x4 value-tile jobs per chunk
+    static constexpr int VPT = (NVJ + NT - 1) / NT;           // value-tile jobs per thread
+    static constexpr int NEJ = NB * (DK / 2);                 // (block, channel pair) jobs
+    static constexpr int JPT = (NEJ + 32 * NW - 1) / (32 * NW);  // per 32-lane half-wave slot
     static constexpr int SZ = (int)sizeof(OP);
 
-    // --- LDS map (bytes). Region P first holds the A/M operands, then (after A and M have
-    // been formed) the float32 A and T, M and W.
+    // LDS map (bytes). Region P first holds the A/M operands, then float32 A and T, M, W.
     static constexpr int oLk = 0;
     static constexpr int oLq = oLk + align16(C * LDK * SZ);
-    static constexpr int oR = oLq + align16(C * LDK * SZ);
-    static constexpr int oRd = oR + align16(C * LDK * SZ);
+    static constexpr int oRk = oLq + align16(C * LDK * SZ);
+    static constexpr int oRd = oRk + align16(C * LDK * SZ);
     static constexpr int oRfar = oRd + align16(C * LDK * SZ);
     static constexpr int P_OPS = oRfar + align16(NFAR * 16 * LDK * SZ);
     static constexpr int oAf = 0;
     static constexpr int oTf = oAf + align16(C * LCF * 4);
-    static constexpr int oTtf = oTf + align16(C * LCF * 4);
-    static constexpr int oMb = oTtf + align16(C * LCF * 4);
+    static constexpr int oMb = oTf + align16(C * LCF * 4);
     static constexpr int oWb = oMb + align16(C * LDC * SZ);
     static constexpr int P_REUSE = oWb + align16(C * LDK * SZ);
     static constexpr int P_END = P_OPS > P_REUSE ? P_OPS : P_REUSE;
-    // region Q: operands of the state pass
-    static constexpr int oXt = P_END;
-    static constexpr int oQg = oXt + align16(DK * LDC * SZ);
-    static constexpr int oKdT = oQg + align16(C * LDK * SZ);
-    // small buffers
-    static constexpr int oYt = oKdT + align16(DK * LDC * SZ);
-    static constexpr int oUt = oYt + align16(VB * LDC * SZ);
-    static constexpr int oSt = oUt + align16(VB * LDC * SZ);
-    static constexpr int oDd = oSt + align16(VB * LDK * SZ);
+    static constexpr int oXt = P_END;                        // (beta k e^G)^T  [channel][token]
+    static constexpr int oQg = oXt + align16(DK * LDC * SZ); // scale q e^G     [token][channel]
+    static constexpr int oKdT = oQg + align16(C * LDK * SZ); // (k e^{G_C-G})^T [channel][token]
+    static constexpr int oYt = oKdT + align16(DK * LDC * SZ); // V^T        [column][token]
+    static constexpr int oDd = oYt + align16(DV * LDC * SZ);
     static constexpr int oGc = oDd + align16(NB * DK * 4);
     static constexpr int oBeta = oGc + align16(DK * 4);
-    static constexpr int oMdiag = oBeta + align16(C * 4);
-    static constexpr int BYTES = oMdiag + align16(C * 4);
+    static constexpr int oMdp = oBeta + align16(C * 4);
+    static constexpr int BYTES = oMdp + align16(NGRP * C * 4);
 
     static_assert(C % 16 == 0 && C >= 16 && C <= 64, "chunk must be 16, 32, 48 or 64");
-    static_assert(DK % 16 == 0 && DV % VB == 0 && VB % 16 == 0, "bad tile sizes");
+    static_assert(DK % 16 == 0 && DV % 16 == 0, "head dims must be multiples of 16");
+    static_assert(VT < NW || VT % NW == 0, "state tiles must spread evenly over waves");
+    static_assert(KT < NW || KT % NW == 0, "W tiles must spread evenly over waves");
+    static_assert(NB <= NW, "one wave per diagonal block");
+    static_assert(C % Step<OP>::KS == 0 && DK % Step<OP>::KS == 0, "step size");
     static_assert(BYTES <= 160 * 1024, "LDS budget of one CU exceeded");
 };
 
@@ -103,62 +112,104 @@ __device__ __forceinline__ int far_index(int NB, int J, int I) {
     return idx + (I - J - 2);
 }
 
-template <typename T> struct Tag {
-    typedef T type;
-};
+// (I, J) of the x-th strictly-lower 16x16 block, row-major order.
+__device__ __forceinline__ void lower_block(int x, int &I, int &J) {
+    I = 1;
+    while (x >= I) {
+        x -= I;
+        ++I;
+    }
+    J = x;
+}
 
-// A 16-token block whose decay reaches this (per channel) is "extreme": its balanced
-// fp16 decay factors (up to 2^(-log2(D)/2)) would leave fp16's range.
-constexpr float kExtremeBlockDecay = 2.0611536e-9f;  // e^-20
-
-template <typename OP> __device__ __forceinline__ float exp_gate(float x);
-template <> __device__ __forceinline__ float exp_gate<_Float16>(float x) { return __expf(x); }
+template <typename OP> __device__ __forceinline__ float exp_gate(float x) { return __expf(x); }
 template <> __device__ __forceinline__ float exp_gate<float>(float x) { return expf(x); }
 
-template <typename Tin, typename OP, int C, int DK, int DV, int VB>
-__global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
-    using Sh = ChunkShape<OP, C, DK, DV, VB>;
+// Raw pair of consecutive inputs as loaded (bf16 pair in 32 bits, or two floats).
+template <typename Tin> struct Raw2;
+template <> struct Raw2<bf16_t> {
+    typedef uint32_t type;
+    static __device__ __forceinline__ type load(rsrc_t r, int voff, int soff) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ f32x2 f32(type u) {
+        return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
+    }
+};
+template <> struct Raw2<float> {
+    typedef f32x2 type;
+    static __device__ __forceinline__ type load(rsrc_t r, int voff, int soff) {
+        return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    }
+    static __device__ __forceinline__ f32x2 f32(type u) { return u; }
+};
+
+// Raw four consecutive inputs as loaded.
+template <typename Tin> struct Raw4;
+template <> struct Raw4<bf16_t> {
+    typedef uint2 type;
+    static __device__ __forceinline__ type load(rsrc_t r, int voff, int soff) {
+        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    }
+    static __device__ __forceinline__ f32x4 f32(type u) {
+        return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+    }
+};
+template <> struct Raw4<float> {
+    typedef f32x4 type;
+    static __device__ __forceinline__ type load(rsrc_t r, int voff, int soff) {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    }
+    static __device__ __forceinline__ f32x4 f32(type u) { return u; }
+};
+
+// Float32-accurate (split-bf16) product of two 16x16 accumulator tiles: X^T Y.
+// An accumulator tile used as the A fragment is read transposed (lane holds X[4q+e][l%16],
+// which the A operand takes as A[l%16][4q+e]).
+__device__ __forceinline__ f32x4 mm_tn(f32x4 x, f32x4 y) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    Mma<__bf16>::mma_split(acc, x, y);
+    return acc;
+}
+
+template <typename Tin, typename OP, int C, int DK, int DV, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
+    using Sh = ChunkShape<OP, C, DK, DV, NW>;
     using MM = Mma<OP>;
-    typedef typename MM::frag frag;
-    constexpr int NB = Sh::NB, LDK = Sh::LDK, LDC = Sh::LDC, LCF = Sh::LCF, VT = Sh::VT,
-                  KT = Sh::KT;
+    using ST = Step<OP>;
+    using RW = Raw2<Tin>;
+    using R4 = Raw4<Tin>;
+    constexpr int NB = Sh::NB, LDK = Sh::LDK, LDC = Sh::LDC, LCF = Sh::LCF, KT = Sh::KT,
+                  CPW = Sh::CPW, KS = ST::KS, TPS = ST::TPS;
+    constexpr bool kDual = std::is_same<OP, _Float16>::value;  // bf16 fallback for A and M
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Sh::BYTES];
     OP *const Lk = reinterpret_cast<OP *>(smem + Sh::oLk);
     OP *const Lq = reinterpret_cast<OP *>(smem + Sh::oLq);
-    OP *const Rk = reinterpret_cast<OP *>(smem + Sh::oR);
+    OP *const Rk = reinterpret_cast<OP *>(smem + Sh::oRk);
     OP *const Rd = reinterpret_cast<OP *>(smem + Sh::oRd);
     OP *const Rfar = reinterpret_cast<OP *>(smem + Sh::oRfar);
     float *const Af = reinterpret_cast<float *>(smem + Sh::oAf);
     float *const Tf = reinterpret_cast<float *>(smem + Sh::oTf);
-    float *const Ttf = reinterpret_cast<float *>(smem + Sh::oTtf);
     OP *const Mb = reinterpret_cast<OP *>(smem + Sh::oMb);
     OP *const Wb = reinterpret_cast<OP *>(smem + Sh::oWb);
     OP *const Xt = reinterpret_cast<OP *>(smem + Sh::oXt);
     OP *const Qg = reinterpret_cast<OP *>(smem + Sh::oQg);
     OP *const KdT = reinterpret_cast<OP *>(smem + Sh::oKdT);
     OP *const Yt = reinterpret_cast<OP *>(smem + Sh::oYt);
-    OP *const Ut = reinterpret_cast<OP *>(smem + Sh::oUt);
-    OP *const St = reinterpret_cast<OP *>(smem + Sh::oSt);
     float *const Dd = reinterpret_cast<float *>(smem + Sh::oDd);
     float *const gC = reinterpret_cast<float *>(smem + Sh::oGc);
     float *const sbeta = reinterpret_cast<float *>(smem + Sh::oBeta);
-    float *const mdiag = reinterpret_cast<float *>(smem + Sh::oMdiag);
-    // fp16 operands: A and M may switch to bf16 for one chunk if its decay is extreme
-    constexpr bool kDual = std::is_same<OP, _Float16>::value;
-    static_assert(!kDual || DK == 128, "the fp16 path maps one wave to one 16-token block");
+    float *const mdp = reinterpret_cast<float *>(smem + Sh::oMdp);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 15, lq = lane >> 4;
+    const int lr = lane & 15, q4 = lane >> 4;
 
-    // ---- work item: blockIdx -> (sequence, head, V-block); same XCD for one (seq, head)
-    const int G = a.n_seqs * a.H;
-    const int x8 = blockIdx.x & 7, s8 = blockIdx.x >> 3;
-    const int vb = s8 % Sh::NVB;
-    const int gi = (s8 / Sh::NVB) * 8 + x8;
-    if (gi >= G) return;
-    const int n = gi / a.H, h = gi % a.H;
+    // ---- chain: blockIdx -> (sequence, head)
     const int H = a.H;
+    if ((int)blockIdx.x >= a.n_seqs * H) return;
+    const int n = blockIdx.x / H, h = blockIdx.x % H;
     int64_t tok0, L;
     if (a.cu_seqlens) {
         tok0 = a.cu_seqlens[n];
@@ -170,416 +221,499 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
     const Tin *const qg = static_cast<const Tin *>(a.q);
     const Tin *const kg = static_cast<const Tin *>(a.k);
     const Tin *const vg = static_cast<const Tin *>(a.v);
-    const int64_t state_base = ((int64_t)n * H + h) * DK * DV + (int64_t)vb * VB;
+    const int64_t sbase = ((int64_t)n * H + h) * DK * DV;
 
-    // ---- the state: wave-owned 16x16 tiles, float32, accumulator layout
-    f32x4 S[Sh::SPW];
+    // ---- per-thread element jobs: (16-token block b, channel pair, half hh of the block);
+    // the two halves of a block sit in lanes l and l^32 of one wave
+    const int hh = lane >> 5;
+    int jb[Sh::JPT], jc[Sh::JPT], jg[Sh::JPT];
+    bool jok[Sh::JPT];
 #pragma unroll
-    for (int j = 0; j < Sh::SPW; ++j) {
-        const int s = wave + 4 * j;
-        S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (s < Sh::NST) {
-            const int rK = s / VT, cv = s % VT;
-            if (a.s0) {
+    for (int jj = 0; jj < Sh::JPT; ++jj) {
+        const int lidx = wave * 32 + (lane & 31) + jj * 32 * NW;
+        jb[jj] = lidx / (DK / 2);
+        jc[jj] = 2 * (lidx % (DK / 2));
+        jg[jj] = (lidx % (DK / 2)) / 32;
+        jok[jj] = jb[jj] < NB;
+    }
+
+    // ---- state: this wave's column tiles (cv = wave + NW*j), float32 accumulator layout
+    const bool owns = wave < Sh::VT;
+    f32x4 S[CPW][KT];
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+        const int cv = wave + NW * j;
+#pragma unroll
+        for (int r = 0; r < KT; ++r) {
+            S[j][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (owns && a.s0) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    S[j][e] = a.s0[state_base + (int64_t)(16 * rK + 4 * lq + e) * DV + 16 * cv + lr];
+                    S[j][r][e] = a.s0[sbase + (int64_t)(16 * r + 4 * q4 + e) * DV + 16 * cv + lr];
             }
-            MM::store4(St + (16 * cv + lr) * LDK + 16 * rK + 4 * lq, S[j]);
         }
     }
 
+    // ---- register prefetch of one chunk's q, k, g (this thread's 8 tokens x 2 channels),
+    // beta, and a 4-token x 4-column tile of v
+    typename RW::type pk[Sh::JPT][8], pq[Sh::JPT][8];
+    typename R4::type pv[Sh::VPT][4];
+    f32x2 pg[Sh::JPT][8];
+    float pbeta = 0.f;
+    auto vjob = [&](int vv, int &tg, int &cg) {
+        const int x = tid + vv * Sh::NT;
+        tg = x / (DV / 4);
+        cg = x % (DV / 4);
+        return x < Sh::NVJ;
+    };
+    // Per-lane byte offsets from a chunk's first token (rows past the chunk end, or lanes
+    // without a job, land beyond the buffer bound and read as zero: alpha = e^0 = 1, k = q =
+    // v = beta = 0, i.e. padding tokens that change nothing).
+    constexpr int ESZ = (int)sizeof(Tin);
+    const int krow = H * DK, vrow = H * DV;  // elements per token row
+    int ko[Sh::JPT], vo[Sh::VPT];
+#pragma unroll
+    for (int jj = 0; jj < Sh::JPT; ++jj)
+        ko[jj] = jok[jj] ? (16 * jb[jj] + 8 * hh) * krow + h * DK + jc[jj] : C * krow;
+#pragma unroll
+    for (int vv = 0; vv < Sh::VPT; ++vv) {
+        int tg, cg;
+        vo[vv] = vjob(vv, tg, cg) ? 4 * tg * vrow + h * DV + 4 * cg : C * vrow;
+    }
+    auto prefetch = [&](int64_t t0, int Lc) {
+        const rsrc_t rq = make_rsrc(qg + t0 * krow, (uint32_t)(Lc * krow * ESZ));
+        const rsrc_t rk = make_rsrc(kg + t0 * krow, (uint32_t)(Lc * krow * ESZ));
+        const rsrc_t rg = make_rsrc(a.g + t0 * krow, (uint32_t)(Lc * krow * 4));
+        const rsrc_t rv = make_rsrc(vg + t0 * vrow, (uint32_t)(Lc * vrow * ESZ));
+        const rsrc_t rb = make_rsrc(a.beta + t0 * H, (uint32_t)(Lc * H * 4));
+#pragma unroll
+        for (int vv = 0; vv < Sh::VPT; ++vv)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pv[vv][r] = R4::load(rv, vo[vv] * ESZ, r * vrow * ESZ);
+#pragma unroll
+        for (int jj = 0; jj < Sh::JPT; ++jj) {
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) {
+                pg[jj][ii] = Raw2<float>::load(rg, ko[jj] * 4, ii * krow * 4);
+                pk[jj][ii] = RW::load(rk, ko[jj] * ESZ, ii * krow * ESZ);
+                pq[jj][ii] = RW::load(rq, ko[jj] * ESZ, ii * krow * ESZ);
+            }
+        }
+        pbeta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                              rb, (tid < C ? tid * H + h : C * H) * 4, 0, 0));
+    };
+
     const int64_t nchunks = (L + C - 1) / C;
+    if (nchunks > 0) prefetch(tok0, (int)(L < C ? L : C));
+
     for (int64_t ci = 0; ci < nchunks; ++ci) {
         const int64_t t0 = tok0 + ci * C;
         const int Lc = (int)((L - ci * C) < C ? (L - ci * C) : C);
-        __syncthreads();
+        __syncthreads();  // the previous chunk's readers of LDS are done
 
-        // ---- phase 0: stage beta and the V-block; per-(block, channel) decay factors
-        if (tid < C) sbeta[tid] = tid < Lc ? a.beta[(t0 + tid) * H + h] : 0.f;
-        for (int idx = tid; idx < C * (VB / 4); idx += Sh::NT) {
-            const int i = idx / (VB / 4), n4 = (idx % (VB / 4)) * 4;
-            f32x4 vv = {0.f, 0.f, 0.f, 0.f};
-            if (i < Lc) vv = load4(vg + ((t0 + i) * H + h) * DV + vb * VB + n4);
+        // ---- P0: gates -> within-block decay products (prefix incl., suffix excl.)
+        float al0[Sh::JPT][8], al1[Sh::JPT][8], sf0[Sh::JPT][8], sf1[Sh::JPT][8];
+        float dk0[Sh::JPT], dk1[Sh::JPT];  // decay of the job's whole 16-token block
+        // k and q of token ii of job jj (zero past the sequence end), from the prefetch registers
+        auto kq = [&](int jj, int ii, float &k0, float &k1, float &q0, float &q1) {
+            const f32x2 kk = RW::f32(pk[jj][ii]), qq = RW::f32(pq[jj][ii]);
+            k0 = kk.x;
+            k1 = kk.y;
+            q0 = qq.x * a.scale;
+            q1 = qq.y * a.scale;
+        };
+        bool ext_local = false;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Yt[(n4 + e) * LDC + i] = static_cast<OP>(vv[e]);
-        }
-
-        const bool pj = tid < Sh::NPAIR;
-        const int b = tid / (DK / 2), c0 = 2 * (tid % (DK / 2));
-        float al0[16], al1[16], sf0[16], sf1[16], k0[16], k1[16], q0[16], q1[16];
-        float dblk0 = 1.f, dblk1 = 1.f;
-        if (pj) {
+        for (int jj = 0; jj < Sh::JPT; ++jj) {
+            float h0 = 1.f, h1 = 1.f;
 #pragma unroll
-            for (int ii = 0; ii < 16; ++ii) {
-                const int i = 16 * b + ii;
-                if (i < Lc) {
-                    const int64_t base = ((t0 + i) * H + h) * DK + c0;
-                    const f32x2 gg = load2(a.g + base);
-                    const f32x2 kk = load2(kg + base);
-                    const f32x2 qq = load2(qg + base);
-                    al0[ii] = exp_gate<OP>(gg.x);
-                    al1[ii] = exp_gate<OP>(gg.y);
-                    k0[ii] = kk.x;
-                    k1[ii] = kk.y;
-                    q0[ii] = qq.x * a.scale;
-                    q1[ii] = qq.y * a.scale;
-                } else {
-                    al0[ii] = al1[ii] = 1.f;
-                    k0[ii] = k1[ii] = q0[ii] = q1[ii] = 0.f;
+            for (int ii = 0; ii < 8; ++ii) {
+                al0[jj][ii] = exp_gate<OP>(pg[jj][ii].x);
+                al1[jj][ii] = exp_gate<OP>(pg[jj][ii].y);
+            }
+#pragma unroll
+            for (int ii = 7; ii >= 0; --ii) {  // exclusive suffix within this half
+                sf0[jj][ii] = h0;
+                sf1[jj][ii] = h1;
+                h0 *= al0[jj][ii];
+                h1 *= al1[jj][ii];
+            }
+            const float o0 = __shfl_xor(h0, 32), o1 = __shfl_xor(h1, 32);  // the other half
+            float r0 = hh ? o0 : 1.f, r1 = hh ? o1 : 1.f;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) {  // inclusive prefix from the block start
+                r0 *= al0[jj][ii];
+                r1 *= al1[jj][ii];
+                al0[jj][ii] = r0;
+                al1[jj][ii] = r1;
+                if (!hh) {
+                    sf0[jj][ii] *= o0;
+                    sf1[jj][ii] *= o1;
                 }
             }
-            // exclusive suffix products (decay from token i+1 to the block end) ...
-            float r0 = 1.f, r1 = 1.f;
-#pragma unroll
-            for (int ii = 15; ii >= 0; --ii) {
-                sf0[ii] = r0;
-                sf1[ii] = r1;
-                r0 *= al0[ii];
-                r1 *= al1[ii];
+            dk0[jj] = h0 * o0;
+            dk1[jj] = h1 * o1;
+            if (jok[jj] && !hh) {
+                Dd[jb[jj] * DK + jc[jj]] = dk0[jj];
+                Dd[jb[jj] * DK + jc[jj] + 1] = dk1[jj];
             }
-            // ... and inclusive prefix products (decay from the block start to token i)
-            r0 = r1 = 1.f;
+            ext_local |= jok[jj] && (dk0[jj] < kExtremeBlockDecay || dk1[jj] < kExtremeBlockDecay);
+        }
+        if (tid < C) sbeta[tid] = pbeta;
 #pragma unroll
-            for (int ii = 0; ii < 16; ++ii) {
-                r0 *= al0[ii];
-                r1 *= al1[ii];
-                al0[ii] = r0;
-                al1[ii] = r1;
+        for (int vv = 0; vv < Sh::VPT; ++vv) {  // v^T: 4 columns x 4 consecutive tokens per store
+            int tg, cg;
+            if (vjob(vv, tg, cg)) {
+                f32x4 vr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vr[r] = R4::f32(pv[vv][r]);
+                typedef typename MM::frag f4;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    *reinterpret_cast<f4 *>(Yt + (4 * cg + c) * LDC + 4 * tg) =
+                        MM::from_f32(f32x4{vr[0][c], vr[1][c], vr[2][c], vr[3][c]});
             }
-            Dd[b * DK + c0] = r0;  // whole-block decay
-            Dd[b * DK + c0 + 1] = r1;
-            dblk0 = r0;
-            dblk1 = r1;
         }
         bool extreme = false;
         if constexpr (kDual) {
-            extreme = __syncthreads_or(pj && (dblk0 < kExtremeBlockDecay || dblk1 < kExtremeBlockDecay));
+            extreme = __syncthreads_or(ext_local);
             if (extreme) {
-                // exact scale * q_i . k_i for the diagonal of M (one wave = one block)
+                // exact scale * q_i . k_i for the diagonal of M, per 64-channel group
 #pragma unroll
-                for (int ii = 0; ii < 16; ++ii) {
-                    float d = q0[ii] * k0[ii] + q1[ii] * k1[ii];
+                for (int jj = 0; jj < Sh::JPT; ++jj) {
 #pragma unroll
-                    for (int m = 32; m > 0; m >>= 1) d += __shfl_xor(d, m);
-                    if (lane == 0) mdiag[16 * b + ii] = d;
+                    for (int ii = 0; ii < 8; ++ii) {
+                        float k0, k1, q0, q1;
+                        kq(jj, ii, k0, k1, q0, q1);
+                        float d = q0 * k0 + q1 * k1;
+#pragma unroll
+                        for (int m = 16; m > 0; m >>= 1) d += __shfl_xor(d, m);
+                        if (jok[jj] && (lane & 31) == 0) mdp[jg[jj] * C + 16 * jb[jj] + 8 * hh + ii] = d;
+                    }
                 }
             }
         } else {
             __syncthreads();
         }
 
-        if (pj) {
-            float pre0 = 1.f, pre1 = 1.f, post0 = 1.f, post1 = 1.f;
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) {
-                if (bb < b) {
-                    pre0 *= Dd[bb * DK + c0];
-                    pre1 *= Dd[bb * DK + c0 + 1];
-                } else if (bb > b) {
-                    post0 *= Dd[bb * DK + c0];
-                    post1 *= Dd[bb * DK + c0 + 1];
-                }
-            }
-            const float d0 = Dd[b * DK + c0], d1 = Dd[b * DK + c0 + 1];
-            if (b == 0) {
-                gC[c0] = d0 * post0;
-                gC[c0 + 1] = d1 * post1;
-            }
-            const float inv0 = 1.f / d0, inv1 = 1.f / d1;
-            // fp16 A/M operands: rows of block I are multiplied by a per-channel power of two
-            // near D_I^(-1/2), the right operands paired with block I by its inverse. Products
-            // are unchanged (exact scaling); the diagonal blocks' factors then stay within
-            // [D^(1/2), D^(-1/2)] instead of [D, 1/D].
-            const bool bal = kDual && !extreme;
-            auto balance = [&](float d) {
-                return bal ? ldexpf(1.f, (int)floorf(-0.5f * __log2f(d))) : 1.f;
+        // ---- P1: matrix-core operands
+        // fp16: rows of block I carry a per-channel power of two 2^e_I near D_I^(-1/2) and the
+        // right operands paired with block I carry 2^-e_I (exact: products are unchanged)
+        auto p1 = [&](auto tag, bool bal) {
+            typedef typename decltype(tag)::type E;  // element type of the A/M operands
+            auto bexp = [&](float d) { return bal ? (int)floorf(-0.5f * __log2f(d)) : 0; };
+            auto st = [&](OP *p, float x, float y) {
+                if constexpr (std::is_same<E, OP>::value) MM::store_pair(p, x, y);
+                else Mma<__bf16>::store_pair(reinterpret_cast<__bf16 *>(p), x, y);
             };
-            auto st_am = [&](OP *p, float x, float y) {
-                if constexpr (kDual) {
-                    if (extreme) {
-                        Mma<__bf16>::store_pair(reinterpret_cast<__bf16 *>(p), x, y);
-                        return;
+#pragma unroll
+            for (int jj = 0; jj < Sh::JPT; ++jj) {
+                if (!jok[jj]) continue;
+                const int b = jb[jj], c0 = jc[jj];
+                float k0[8], k1[8], q0[8], q1[8];
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) kq(jj, ii, k0[ii], k1[ii], q0[ii], q1[ii]);
+                float pre0 = 1.f, pre1 = 1.f, post0 = 1.f, post1 = 1.f;
+#pragma unroll
+                for (int bb = 0; bb < NB; ++bb) {
+                    if (bb < b) {
+                        pre0 *= Dd[bb * DK + c0];
+                        pre1 *= Dd[bb * DK + c0 + 1];
+                    } else if (bb > b) {
+                        post0 *= Dd[bb * DK + c0];
+                        post1 *= Dd[bb * DK + c0 + 1];
                     }
                 }
-                MM::store_pair(p, x, y);
-            };
-            const float sb0 = balance(d0), sb1 = balance(d1);
-            const float nx0 = b + 1 < NB ? 1.f / balance(Dd[(b + 1) * DK + c0]) : 1.f;
-            const float nx1 = b + 1 < NB ? 1.f / balance(Dd[(b + 1) * DK + c0 + 1]) : 1.f;
-            OP xt0[16], xt1[16], kd0[16], kd1[16];
-#pragma unroll
-            for (int ii = 0; ii < 16; ++ii) {
-                const int i = 16 * b + ii;
-                const float bt = sbeta[i];
-                const float ks0 = k0[ii] * sf0[ii], ks1 = k1[ii] * sf1[ii];
-                st_am(Lk + i * LDK + c0, bt * k0[ii] * al0[ii] * sb0, bt * k1[ii] * al1[ii] * sb1);
-                st_am(Lq + i * LDK + c0, q0[ii] * al0[ii] * sb0, q1[ii] * al1[ii] * sb1);
-                st_am(Rk + i * LDK + c0, ks0 * nx0, ks1 * nx1);
-                st_am(Rd + i * LDK + c0, ks0 * inv0 / sb0, ks1 * inv1 / sb1);
-                MM::store_pair(Qg + i * LDK + c0, q0[ii] * al0[ii] * pre0, q1[ii] * al1[ii] * pre1);
-                xt0[ii] = static_cast<OP>(bt * k0[ii] * al0[ii] * pre0);
-                xt1[ii] = static_cast<OP>(bt * k1[ii] * al1[ii] * pre1);
-                kd0[ii] = static_cast<OP>(ks0 * post0);
-                kd1[ii] = static_cast<OP>(ks1 * post1);
-            }
-            // right operands of blocks (I, b) with I >= b + 2 carry the decay of the blocks
-            // strictly between them
-            float m0 = 1.f, m1 = 1.f;
-#pragma unroll
-            for (int I = 2; I < NB; ++I) {
-                if (I >= b + 2) {
-                    m0 *= Dd[(I - 1) * DK + c0];
-                    m1 *= Dd[(I - 1) * DK + c0 + 1];
-                    const float f0 = m0 / balance(Dd[I * DK + c0]);
-                    const float f1 = m1 / balance(Dd[I * DK + c0 + 1]);
-                    OP *dst = Rfar + far_index(NB, b, I) * 16 * LDK + c0;
-#pragma unroll
-                    for (int ii = 0; ii < 16; ++ii)
-                        st_am(dst + ii * LDK, k0[ii] * sf0[ii] * f0, k1[ii] * sf1[ii] * f1);
+                const float d0 = dk0[jj], d1 = dk1[jj];
+                if (b == 0 && !hh) {
+                    gC[c0] = d0 * post0;
+                    gC[c0 + 1] = d1 * post1;
                 }
-            }
+                const int e0 = bexp(d0), e1 = bexp(d1);
+                const int n0 = b + 1 < NB ? bexp(Dd[(b + 1) * DK + c0]) : 0;
+                const int n1 = b + 1 < NB ? bexp(Dd[(b + 1) * DK + c0 + 1]) : 0;
+                const float sb0 = ldexpf(1.f, e0), sb1 = ldexpf(1.f, e1);      // left scale
+                const float nx0 = ldexpf(1.f, -n0), nx1 = ldexpf(1.f, -n1);    // right, block b+1
+                const float rd0 = __frcp_rn(d0) * ldexpf(1.f, n0 - e0);         // Rd = Rk * rd
+                const float rd1 = __frcp_rn(d1) * ldexpf(1.f, n1 - e1);
+                const float pq0 = pre0 * ldexpf(1.f, -e0), pq1 = pre1 * ldexpf(1.f, -e1);
+                const float po0 = post0 * ldexpf(1.f, n0), po1 = post1 * ldexpf(1.f, n1);
+                const int cp = ST::perm(c0);  // c0 even: c0, c0+1 stay adjacent in perm order
+                OP xt0[8], xt1[8], kd0[8], kd1[8];
 #pragma unroll
-            for (int ii = 0; ii < 16; ii += 4) {
-                typedef typename MM::frag f4;
-                f4 x0, x1, y0, y1;
-                x0 = f4{xt0[ii], xt0[ii + 1], xt0[ii + 2], xt0[ii + 3]};
-                x1 = f4{xt1[ii], xt1[ii + 1], xt1[ii + 2], xt1[ii + 3]};
-                y0 = f4{kd0[ii], kd0[ii + 1], kd0[ii + 2], kd0[ii + 3]};
-                y1 = f4{kd1[ii], kd1[ii + 1], kd1[ii + 2], kd1[ii + 3]};
-                *reinterpret_cast<f4 *>(Xt + c0 * LDC + 16 * b + ii) = x0;
-                *reinterpret_cast<f4 *>(Xt + (c0 + 1) * LDC + 16 * b + ii) = x1;
-                *reinterpret_cast<f4 *>(KdT + c0 * LDC + 16 * b + ii) = y0;
-                *reinterpret_cast<f4 *>(KdT + (c0 + 1) * LDC + 16 * b + ii) = y1;
-            }
-        }
-        __syncthreads();
-
-        // ---- phase A: lower 16x16 blocks of A (strictly lower) and M (lower) on the MFMAs
-        f32x4 am[Sh::AMPW];
-        auto am_phase = [&](auto tag) {
-            using AM = typename decltype(tag)::type;
-            typedef typename AM::elem E;
+                for (int ii = 0; ii < 8; ++ii) {
+                    const int i = 16 * b + 8 * hh + ii;
+                    const float bt = sbeta[i];
+                    const float lk0 = bt * k0[ii] * al0[jj][ii] * sb0, lk1 = bt * k1[ii] * al1[jj][ii] * sb1;
+                    const float lq0 = q0[ii] * al0[jj][ii] * sb0, lq1 = q1[ii] * al1[jj][ii] * sb1;
+                    const float rk0 = k0[ii] * sf0[jj][ii] * nx0, rk1 = k1[ii] * sf1[jj][ii] * nx1;
+                    st(Lk + i * LDK + c0, lk0, lk1);
+                    st(Lq + i * LDK + c0, lq0, lq1);
+                    st(Rk + i * LDK + c0, rk0, rk1);
+                    st(Rd + i * LDK + c0, rk0 * rd0, rk1 * rd1);
+                    MM::store_pair(Qg + i * LDK + cp, lq0 * pq0, lq1 * pq1);
+                    xt0[ii] = static_cast<OP>(lk0 * pq0);
+                    xt1[ii] = static_cast<OP>(lk1 * pq1);
+                    kd0[ii] = static_cast<OP>(rk0 * po0);
+                    kd1[ii] = static_cast<OP>(rk1 * po1);
+                }
+                // right operands of blocks (I, b), I >= b + 2: decay of the blocks in between
+                float m0 = ldexpf(1.f, n0), m1 = ldexpf(1.f, n1);  // undo the block b+1 scale
 #pragma unroll
-            for (int j = 0; j < Sh::AMPW; ++j) {
-                const int x = wave + 4 * j;
-                am[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (x < 2 * Sh::NBLK) {
-                    const bool isM = x >= Sh::NBLK;
-                    int y = isM ? x - Sh::NBLK : x, I = 0;
-                    while (y > I) { y -= I + 1; ++I; }
-                    const int J = y;
-                    const OP *left = (isM ? Lq : Lk) + (16 * I + lr) * LDK + 4 * lq;
-                    const OP *right;
-                    if (I == J) right = Rd + (16 * J + lr) * LDK;
-                    else if (I == J + 1) right = Rk + (16 * J + lr) * LDK;
-                    else right = Rfar + (far_index(NB, J, I) * 16 + lr) * LDK;
-                    right += 4 * lq;
-                    const E *le = reinterpret_cast<const E *>(left);
-                    const E *ri = reinterpret_cast<const E *>(right);
+                for (int I = 2; I < NB; ++I) {
+                    if (I >= b + 2) {
+                        m0 *= Dd[(I - 1) * DK + c0];
+                        m1 *= Dd[(I - 1) * DK + c0 + 1];
+                        const float f0 = m0 * ldexpf(1.f, -bexp(Dd[I * DK + c0]));
+                        const float f1 = m1 * ldexpf(1.f, -bexp(Dd[I * DK + c0 + 1]));
+                        OP *dst = Rfar + (far_index(NB, b, I) * 16 + 8 * hh) * LDK + c0;
 #pragma unroll
-                    for (int kk = 0; kk < KT; ++kk)
-                        AM::mma(am[j], AM::load(le + 16 * kk), AM::load(ri + 16 * kk));
-                    if (I == J) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int row = 4 * lq + e;
-                            if (isM ? (row < lr) : (row <= lr)) am[j][e] = 0.f;
-                            if (kDual && extreme && isM && row == lr) am[j][e] = mdiag[16 * I + lr];
+                        for (int ii = 0; ii < 8; ++ii) {
+                            const float rk0 = k0[ii] * sf0[jj][ii] * nx0, rk1 = k1[ii] * sf1[jj][ii] * nx1;
+                            st(dst + ii * LDK, rk0 * f0, rk1 * f1);
                         }
                     }
+                }
+                typedef typename MM::frag f4;
+                const int tcol = 16 * b + 8 * hh;
+#pragma unroll
+                for (int ii = 0; ii < 8; ii += 4) {
+                    const int tp = ST::perm(tcol + ii);  // groups of 4 tokens stay contiguous
+                    *reinterpret_cast<f4 *>(Xt + c0 * LDC + tcol + ii) = f4{xt0[ii], xt0[ii + 1], xt0[ii + 2], xt0[ii + 3]};
+                    *reinterpret_cast<f4 *>(Xt + (c0 + 1) * LDC + tcol + ii) = f4{xt1[ii], xt1[ii + 1], xt1[ii + 2], xt1[ii + 3]};
+                    *reinterpret_cast<f4 *>(KdT + c0 * LDC + tp) = f4{kd0[ii], kd0[ii + 1], kd0[ii + 2], kd0[ii + 3]};
+                    *reinterpret_cast<f4 *>(KdT + (c0 + 1) * LDC + tp) = f4{kd1[ii], kd1[ii + 1], kd1[ii + 2], kd1[ii + 3]};
                 }
             }
         };
         if constexpr (kDual) {
-            if (extreme) am_phase(Tag<Mma<__bf16>>{});
-            else am_phase(Tag<MM>{});
+            if (extreme) p1(Tag<__bf16>{}, false);
+            else p1(Tag<OP>{}, true);
         } else {
-            am_phase(Tag<MM>{});
+            p1(Tag<OP>{}, false);
         }
-        __syncthreads();  // operands of phase A are dead from here on
+        // the next chunk's inputs are in flight from here on
+        if (ci + 1 < nchunks) {
+            const int64_t rem = L - (ci + 1) * C;
+            prefetch(t0 + C, (int)(rem < C ? rem : C));
+        }
+        __syncthreads();
+
+        // ---- P2: A and M 16x16 blocks; the diagonal blocks' waves also invert I + A_II
+        auto block_am = [&](auto tag, bool isM, int I, int J) {
+            using SA = typename decltype(tag)::type;
+            typedef typename std::conditional<std::is_same<SA, Step<__bf16>>::value, __bf16, OP>::type E;
+            const OP *left = (isM ? Lq : Lk) + (16 * I + lr) * LDK;
+            const OP *right = I == J       ? Rd + (16 * J + lr) * LDK
+                              : I == J + 1 ? Rk + (16 * J + lr) * LDK
+                                           : Rfar + (far_index(NB, J, I) * 16 + lr) * LDK;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < Sh::AMPW; ++j) {
-            const int x = wave + 4 * j;
-            if (x < 2 * Sh::NBLK) {
-                const bool isM = x >= Sh::NBLK;
-                int y = isM ? x - Sh::NBLK : x, I = 0;
-                while (y > I) { y -= I + 1; ++I; }
-                const int J = y;
+            for (int kk = 0; kk < DK; kk += SA::KS)
+                SA::mma(acc, SA::contig(reinterpret_cast<const E *>(left), kk, q4),
+                        SA::contig(reinterpret_cast<const E *>(right), kk, q4));
+            return acc;
+        };
+        auto am = [&](bool isM, int I, int J) {
+            if constexpr (kDual) {
+                if (extreme) return block_am(Tag<Step<__bf16>>{}, isM, I, J);
+            }
+            return block_am(Tag<ST>{}, isM, I, J);
+        };
+        f32x4 tdiag = {0.f, 0.f, 0.f, 0.f}, mdiag = {0.f, 0.f, 0.f, 0.f};
+        const bool dj = wave < NB;
+        if (dj) {
+            const int I = wave;
+            f32x4 Lm = am(false, I, I);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * q4 + e <= lr) Lm[e] = 0.f;  // strictly lower
+            // (I + L)^{-1} = (I - L)(I + L^2)(I + L^4)(I + L^8), L strictly lower 16x16
+            f32x4 Id;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Id[e] = (4 * q4 + e == lr) ? 1.f : 0.f;
+            const f32x4 Lt = mm_tn(Lm, Id);
+            const f32x4 L2 = mm_tn(Lt, Lm), L2t = mm_tn(Lm, Lt);
+            const f32x4 L4 = mm_tn(L2t, L2), L4t = mm_tn(L2, L2t);
+            const f32x4 L8 = mm_tn(L4t, L4);
+            const f32x4 P1 = Id - Lm, P1t = Id - Lt;
+            const f32x4 P2 = P1 + mm_tn(P1t, L2), P2t = P1t + mm_tn(L2, P1t);
+            const f32x4 P3 = P2 + mm_tn(P2t, L4), P3t = P2t + mm_tn(L4, P2t);
+            tdiag = P3 + mm_tn(P3t, L8);
+            mdiag = am(true, I, I);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 4 * q4 + e;
+                if (row < lr) mdiag[e] = 0.f;
+                if (kDual && extreme && row == lr) {
+                    float d = 0.f;
+#pragma unroll
+                    for (int g = 0; g < Sh::NGRP; ++g) d += mdp[g * C + 16 * I + lr];
+                    mdiag[e] = d;
+                }
+            }
+        }
+        f32x4 offv[Sh::OPW];
+        const int ow = NW > NB ? wave - NB : wave;  // index among the off-diagonal waves
+#pragma unroll
+        for (int j = 0; j < Sh::OPW; ++j) {
+            offv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (Sh::NOFF > 0) {
+                const int x = ow + Sh::OFFW * j;
+                if (ow >= 0 && x < Sh::NOFF) {
+                    int I, J;
+                    lower_block(x % (Sh::NOFF / 2), I, J);
+                    offv[j] = am(x >= Sh::NOFF / 2, I, J);
+                }
+            }
+        }
+        __syncthreads();  // A/M operands are dead from here on
+        if (dj) {
+            const int I = wave;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * I + 4 * q4 + e, col = 16 * I + lr;
+                Tf[row * LCF + col] = tdiag[e];
+                Mb[row * LDC + ST::perm(col)] = static_cast<OP>(mdiag[e]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < Sh::OPW; ++j) {
+            const int x = ow + Sh::OFFW * j;
+            if (Sh::NOFF > 0 && ow >= 0 && x < Sh::NOFF) {
+                int I, J;
+                lower_block(x % (Sh::NOFF > 0 ? Sh::NOFF / 2 : 1), I, J);
+                const bool isM = x >= Sh::NOFF / 2;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int row = 16 * I + 4 * lq + e, col = 16 * J + lr;
-                    if (isM) Mb[row * LDC + col] = static_cast<OP>(am[j][e]);
-                    else Af[row * LCF + col] = am[j][e];
+                    const int row = 16 * I + 4 * q4 + e, col = 16 * J + lr;
+                    if (isM) Mb[row * LDC + ST::perm(col)] = static_cast<OP>(offv[j][e]);
+                    else Af[row * LCF + col] = offv[j][e];
                 }
             }
         }
-        __syncthreads();
-
-        // ---- phase T: T = (I + A)^{-1}; diagonal blocks by forward substitution
-        if (wave < NB && lane < 16) {
-            const int o = 16 * wave, c = lane;
-            float xv[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = (i == c) ? 1.f : 0.f;
-#pragma unroll
-                for (int j = 0; j < i; ++j) s -= Af[(o + i) * LCF + o + j] * xv[j];
-                xv[i] = s;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) Tf[(o + i) * LCF + o + c] = xv[i];
-#pragma unroll
-            for (int i = 0; i < 16; i += 4)
-                *reinterpret_cast<f32x4 *>(Ttf + (o + c) * LCF + o + i) =
-                    f32x4{xv[i], xv[i + 1], xv[i + 2], xv[i + 3]};
+        // zero the upper blocks of M (read by the paired-tile steps of M U)
+        for (int idx = tid; idx < C * C; idx += Sh::NT) {
+            const int row = idx / C, col = idx % C;
+            if (col / 16 > row / 16) Mb[row * LDC + ST::perm(col)] = static_cast<OP>(0.f);
         }
         __syncthreads();
-        // off-diagonal blocks by distance: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
-#pragma unroll
-        for (int d = 1; d < NB; ++d) {
-            for (int J = wave; J < NB - d; J += 4) {
-                const int I = J + d;
-                f32x4 P = {0.f, 0.f, 0.f, 0.f};
-                for (int K = J; K < I; ++K) {
-                    const f32x4 av = *reinterpret_cast<const f32x4 *>(Af + (16 * I + lr) * LCF + 16 * K + 4 * lq);
-                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(Ttf + (16 * J + lr) * LCF + 16 * K + 4 * lq);
-                    MM::mma_split(P, av, bv);
-                }
-                const f32x4 tii = *reinterpret_cast<const f32x4 *>(Tf + (16 * I + lr) * LCF + 16 * I + 4 * lq);
-                f32x4 Tij = {0.f, 0.f, 0.f, 0.f};
-                MM::mma_split(Tij, tii, P);
-                Tij = -Tij;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Tf[(16 * I + 4 * lq + e) * LCF + 16 * J + lr] = Tij[e];
-                *reinterpret_cast<f32x4 *>(Ttf + (16 * J + lr) * LCF + 16 * I + 4 * lq) = Tij;
-            }
-            __syncthreads();
-        }
 
-        // ---- phase W: W = T X (X = beta k e^G), and U~ = T Diag(beta) V
+        // ---- P4: block forward substitution for W (fp16 result, to LDS) and U~ (registers)
 #pragma unroll
         for (int j = 0; j < Sh::WPW; ++j) {
-            const int x = wave + 4 * j;
-            if (x < NB * KT) {
-                const int I = x / KT, cK = x % KT;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                for (int J = 0; J <= I; ++J) {
-                    const f32x4 tv = *reinterpret_cast<const f32x4 *>(Tf + (16 * I + lr) * LCF + 16 * J + 4 * lq);
-                    MM::mma(acc, MM::from_f32(tv), MM::load(Xt + (16 * cK + lr) * LDC + 16 * J + 4 * lq));
-                }
+            const int cK = wave + NW * j;
+            if (cK < KT) {
+                f32x4 Wt[NB];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    Wb[(16 * I + 4 * lq + e) * LDK + 16 * cK + lr] = static_cast<OP>(acc[e]);
-            }
-        }
-        f32x4 Ur[Sh::UPW];
+                for (int I = 0; I < NB; ++I) {
+                    f32x4 R = MM::to_f32(MM::load(Xt + (16 * cK + lr) * LDC + 16 * I + 4 * q4));
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < Sh::UPW; ++j) {
-            const int u = wave + 4 * j;
-            Ur[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (u < Sh::NUT) {
-                const int I = u / VT, cv = u % VT;
-                for (int J = 0; J <= I; ++J) {
-                    f32x4 tv = *reinterpret_cast<const f32x4 *>(Tf + (16 * I + lr) * LCF + 16 * J + 4 * lq);
-                    const f32x4 bt = *reinterpret_cast<const f32x4 *>(sbeta + 16 * J + 4 * lq);
-                    tv *= bt;
-                    const frag th = MM::from_f32(tv);
-                    const frag tl = MM::from_f32(tv - MM::to_f32(th));
-                    const frag yv = MM::load(Yt + (16 * cv + lr) * LDC + 16 * J + 4 * lq);
-                    MM::mma(Ur[j], tl, yv);
-                    MM::mma(Ur[j], th, yv);
+                    for (int J = 0; J < I; ++J)
+                        MM::mma(acc, MM::from_f32(*reinterpret_cast<const f32x4 *>(Af + (16 * I + lr) * LCF + 16 * J + 4 * q4)),
+                                MM::from_f32(Wt[J]));
+                    R -= acc;
+                    f32x4 w = {0.f, 0.f, 0.f, 0.f};
+                    MM::mma(w, MM::from_f32(*reinterpret_cast<const f32x4 *>(Tf + (16 * I + lr) * LCF + 16 * I + 4 * q4)),
+                            MM::from_f32(R));
+                    Wt[I] = w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        Wb[(16 * I + 4 * q4 + e) * LDK + ST::perm(16 * cK + lr)] = static_cast<OP>(w[e]);
                 }
             }
         }
-        __syncthreads();
-
-        // ---- state pass (a): U = U~ - W S
+        f32x4 Ur[CPW][NB];
 #pragma unroll
-        for (int j = 0; j < Sh::UPW; ++j) {
-            const int u = wave + 4 * j;
-            if (u < Sh::NUT) {
-                const int I = u / VT, cv = u % VT;
-                f32x4 ws = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < CPW; ++j) {
 #pragma unroll
-                for (int kk = 0; kk < KT; ++kk)
-                    MM::mma(ws, MM::load(Wb + (16 * I + lr) * LDK + 16 * kk + 4 * lq),
-                            MM::load(St + (16 * cv + lr) * LDK + 16 * kk + 4 * lq));
-                MM::store4(Ut + (16 * cv + lr) * LDC + 16 * I + 4 * lq, Ur[j] - ws);
-            }
-        }
-        __syncthreads();
-
-        // ---- (b): O = (scale q e^G) S + M U, written straight to HBM
-#pragma unroll
-        for (int j = 0; j < Sh::UPW; ++j) {
-            const int u = wave + 4 * j;
-            if (u < Sh::NUT) {
-                const int I = u / VT, cv = u % VT;
+            for (int I = 0; I < NB; ++I) {
+                const int cv = wave + NW * j;
+                f32x4 R = MM::to_f32(MM::load(Yt + (16 * cv + lr) * LDC + 16 * I + 4 * q4)) *
+                          *reinterpret_cast<const f32x4 *>(sbeta + 16 * I + 4 * q4);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < KT; ++kk)
-                    MM::mma(acc, MM::load(Qg + (16 * I + lr) * LDK + 16 * kk + 4 * lq),
-                            MM::load(St + (16 * cv + lr) * LDK + 16 * kk + 4 * lq));
-                for (int J = 0; J <= I; ++J)
-                    MM::mma(acc, MM::load(Mb + (16 * I + lr) * LDC + 16 * J + 4 * lq),
-                            MM::load(Ut + (16 * cv + lr) * LDC + 16 * J + 4 * lq));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 16 * I + 4 * lq + e;
-                    if (row < Lc) a.o[((t0 + row) * H + h) * DV + vb * VB + 16 * cv + lr] = acc[e];
-                }
-            }
-        }
-
-        // ---- (c): S <- Diag(e^{G_C}) S + (k e^{G_C - G})^T U
-#pragma unroll
-        for (int j = 0; j < Sh::SPW; ++j) {
-            const int s = wave + 4 * j;
-            if (s < Sh::NST) {
-                const int rK = s / VT, cv = s % VT;
-                const f32x4 dec = *reinterpret_cast<const f32x4 *>(gC + 16 * rK + 4 * lq);
-                f32x4 acc = S[j] * dec;
-#pragma unroll
-                for (int J = 0; J < NB; ++J)
-                    MM::mma(acc, MM::load(KdT + (16 * rK + lr) * LDC + 16 * J + 4 * lq),
-                            MM::load(Ut + (16 * cv + lr) * LDC + 16 * J + 4 * lq));
-                S[j] = acc;
+                for (int J = 0; J < I; ++J)
+                    Mma<__bf16>::mma_split(acc, *reinterpret_cast<const f32x4 *>(Af + (16 * I + lr) * LCF + 16 * J + 4 * q4),
+                                           Ur[j][J]);
+                R -= acc;
+                f32x4 u = {0.f, 0.f, 0.f, 0.f};
+                Mma<__bf16>::mma_split(u, *reinterpret_cast<const f32x4 *>(Tf + (16 * I + lr) * LCF + 16 * I + 4 * q4), R);
+                Ur[j][I] = u;
             }
         }
         __syncthreads();
+
+        // ---- P5: state pass, registers only: U = U~ - W S; O = Qg S + M U; S' = gC S + Kd^T U
+        if (owns) {
+            const rsrc_t ro = make_rsrc(a.o + t0 * vrow, (uint32_t)(Lc * vrow * 4));
 #pragma unroll
-        for (int j = 0; j < Sh::SPW; ++j) {
-            const int s = wave + 4 * j;
-            if (s < Sh::NST) {
-                const int rK = s / VT, cv = s % VT;
-                MM::store4(St + (16 * cv + lr) * LDK + 16 * rK + 4 * lq, S[j]);
+            for (int j = 0; j < CPW; ++j) {
+                const int cv = wave + NW * j;
+                const int oo = (4 * q4 * vrow + h * DV + 16 * cv + lr) * 4;
+                typename ST::frag sfr[DK / KS];
+#pragma unroll
+                for (int p = 0; p < DK / KS; ++p) sfr[p] = ST::regs(&S[j][p * TPS]);
+                f32x4 U[NB];
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    f32x4 ws = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int p = 0; p < DK / KS; ++p)
+                        ST::mma(ws, ST::permuted(Wb + (16 * I + lr) * LDK, p * KS, q4), sfr[p]);
+                    U[I] = Ur[j][I] - ws;
+                }
+                typename ST::frag ufr[C / KS];
+#pragma unroll
+                for (int p = 0; p < C / KS; ++p) ufr[p] = ST::regs(&U[p * TPS]);
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int p = 0; p < DK / KS; ++p)
+                        ST::mma(o, ST::permuted(Qg + (16 * I + lr) * LDK, p * KS, q4), sfr[p]);
+#pragma unroll
+                    for (int p = 0; p <= I / TPS; ++p)
+                        ST::mma(o, ST::permuted(Mb + (16 * I + lr) * LDC, p * KS, q4), ufr[p]);
+                    // rows past the chunk end are dropped by the buffer bound
+                    const int so = 16 * I * vrow * 4;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.x), ro, oo, so, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.y), ro, oo, so + vrow * 4, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.z), ro, oo, so + 2 * vrow * 4, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.w), ro, oo, so + 3 * vrow * 4, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < KT; ++r) {
+                    f32x4 acc = S[j][r] * *reinterpret_cast<const f32x4 *>(gC + 16 * r + 4 * q4);
+#pragma unroll
+                    for (int p = 0; p < C / KS; ++p)
+                        ST::mma(acc, ST::permuted(KdT + (16 * r + lr) * LDC, p * KS, q4), ufr[p]);
+                    S[j][r] = acc;
+                }
             }
         }
     }
 
-    if (a.s_out) {
+    if (a.s_out && owns) {
 #pragma unroll
-        for (int j = 0; j < Sh::SPW; ++j) {
-            const int s = wave + 4 * j;
-            if (s < Sh::NST) {
-                const int rK = s / VT, cv = s % VT;
+        for (int j = 0; j < CPW; ++j) {
+            const int cv = wave + NW * j;
+#pragma unroll
+            for (int r = 0; r < KT; ++r)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    a.s_out[state_base + (int64_t)(16 * rK + 4 * lq + e) * DV + 16 * cv + lr] = S[j][e];
-            }
+                    a.s_out[sbase + (int64_t)(16 * r + 4 * q4 + e) * DV + 16 * cv + lr] = S[j][r][e];
         }
     }
 }
 
-template <typename Tin, typename OP, int C, int DK, int DV, int VB>
+template <typename Tin, typename OP, int C, int DK, int DV, int NW>
 hipError_t launch_t(const ChunkArgs &a, hipStream_t stream) {
-    using Sh = ChunkShape<OP, C, DK, DV, VB>;
-    const int64_t G = (int64_t)a.n_seqs * a.H;
-    const int64_t blocks = ((G + 7) / 8) * 8 * Sh::NVB;
+    const int64_t blocks = (int64_t)a.n_seqs * a.H;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, VB>), dim3((unsigned)blocks),
-                       dim3(Sh::NT), 0, stream, a);
+    hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NW>), dim3((unsigned)blocks),
+                       dim3(64 * NW), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -597,10 +731,10 @@ hipError_t launch_chunk_fwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t
                             const ChunkArgs &a, hipStream_t stream) {
     if (!chunk_fwd_supported(in_dtype, chunk, Dk, Dv)) return hipErrorInvalidValue;
     if (a.n_seqs == 0) return hipSuccess;
-    if (in_dtype == 1) return launch_t<bf16_t, _Float16, 64, 128, 128, 32>(a, stream);
-    if (chunk == 16) return launch_t<float, float, 16, 16, 16, 16>(a, stream);
-    if (Dk == 32) return launch_t<float, float, 64, 32, 32, 32>(a, stream);
-    return launch_t<float, float, 64, 64, 64, 16>(a, stream);
+    if (in_dtype == 1) return launch_t<bf16_t, _Float16, 64, 128, 128, 4>(a, stream);
+    if (chunk == 16) return launch_t<float, float, 16, 16, 16, 4>(a, stream);
+    if (Dk == 32) return launch_t<float, float, 64, 32, 32, 4>(a, stream);
+    return launch_t<float, float, 64, 64, 64, 4>(a, stream);
 }
 
 }  // namespace kda

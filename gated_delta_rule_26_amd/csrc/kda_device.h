@@ -13,6 +13,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Buffer resource (scalar descriptor): base address plus a byte bound. Loads at offsets at
+// or past the bound return zero and stores there are dropped, by the hardware.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
 
 // Storage type of bf16 inputs: raw 16-bit patterns.
 struct bf16_t {
@@ -180,6 +189,83 @@ template <> struct Mma<float> {
     static __device__ __forceinline__ void store4(float *p, f32x4 x) {
         *reinterpret_cast<f32x4 *>(p) = x;
     }
+};
+
+// ---------------------------------------------------------------------------------------
+// Reduction steps of the widest matrix-core instruction of each operand type.
+//
+// A step adds KS reduction indices to a 16x16 float32 accumulator. Lane group q = lane/16
+// supplies, for output row/column lane%16, the values of its own KS/4 reduction indices;
+// A and B must supply matching indices, which is all the hardware requires. Two index
+// assignments are used:
+//  * contig: lane group q takes KS/4 consecutive indices starting at k0 + q*KS/4 (one
+//    vector load from a row of a [row][k] LDS operand);
+//  * split: lane group q takes indices 4q..4q+3 of each 16-index tile in the step, so that
+//    a 16x16 accumulator tile held in registers (rows 4q..4q+3) is directly a B fragment
+//    (regs()). The matching A fragment is one 8-byte load per tile (split()), or a single
+//    16-byte load (permuted()) from an operand stored in perm() order.
+// f16 / bf16: one v_mfma_f32_16x16x32 per step (KS = 32, two tiles); float: four
+// v_mfma_f32_16x16x4 (KS = 16, one tile).
+// ---------------------------------------------------------------------------------------
+template <typename OP> struct Step;
+
+template <typename H, typename V8, typename V4> struct Step16 {
+    static constexpr int KS = 32;
+    static constexpr int TPS = 2;
+    typedef V8 frag;
+    // Storage position of reduction index k in an operand read with perm(): within each
+    // 32-index step the groups of four are ordered 0,4,1,5,2,6,3,7, so that the split index
+    // set of lane group q (groups q and q+4) is 8 contiguous elements at 8q.
+    static __device__ __forceinline__ int perm(int k) {
+        const int g = (k >> 2) & 7;
+        return (k & ~31) | (((g & 3) << 1 | (g >> 2)) << 2) | (k & 3);
+    }
+    static __device__ __forceinline__ frag permuted(const H *row, int k0, int q) {
+        return *reinterpret_cast<const V8 *>(row + k0 + 8 * q);
+    }
+    static __device__ __forceinline__ frag contig(const H *row, int k0, int q) {
+        return *reinterpret_cast<const V8 *>(row + k0 + 8 * q);
+    }
+    static __device__ __forceinline__ frag split(const H *row, int k0, int q) {
+        const V4 a = *reinterpret_cast<const V4 *>(row + k0 + 4 * q);
+        const V4 b = *reinterpret_cast<const V4 *>(row + k0 + 16 + 4 * q);
+        return frag{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    }
+    static __device__ __forceinline__ frag regs(const f32x4 *t) {
+        return frag{static_cast<H>(t[0].x), static_cast<H>(t[0].y), static_cast<H>(t[0].z),
+                    static_cast<H>(t[0].w), static_cast<H>(t[1].x), static_cast<H>(t[1].y),
+                    static_cast<H>(t[1].z), static_cast<H>(t[1].w)};
+    }
+};
+
+template <> struct Step<_Float16> : Step16<_Float16, f16x8, f16x4> {
+    static __device__ __forceinline__ void mma(f32x4 &acc, frag a, frag b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+    }
+};
+
+template <> struct Step<__bf16> : Step16<__bf16, bf16x8, bf16x4> {
+    static __device__ __forceinline__ void mma(f32x4 &acc, frag a, frag b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+};
+
+template <> struct Step<float> {
+    static constexpr int KS = 16;
+    static constexpr int TPS = 1;
+    typedef f32x4 frag;
+    static __device__ __forceinline__ frag contig(const float *row, int k0, int q) {
+        return *reinterpret_cast<const f32x4 *>(row + k0 + 4 * q);
+    }
+    static __device__ __forceinline__ frag split(const float *row, int k0, int q) {
+        return contig(row, k0, q);
+    }
+    static __device__ __forceinline__ frag regs(const f32x4 *t) { return t[0]; }
+    static __device__ __forceinline__ int perm(int k) { return k; }
+    static __device__ __forceinline__ frag permuted(const float *row, int k0, int q) {
+        return contig(row, k0, q);
+    }
+    static __device__ __forceinline__ void mma(f32x4 &acc, frag a, frag b) { Mma<float>::mma(acc, a, b); }
 };
 
 }  // namespace kda

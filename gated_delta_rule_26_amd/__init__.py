@@ -98,7 +98,7 @@ def _req(t, name, dtype=None):
 
 def kda_chunk_fwd(q, k, v, g, beta, *, initial_state=None, output_final_state: bool = True,
                   final_state=None, cu_seqlens=None, chunk: int = 64, scale: float = 1.0,
-                  o=None, stream=None):
+                  o=None, stream=None, split: bool = True):
     """Chunked KDA prefill (C: kda_chunk_fwd).
 
     q, k: [B, T, H, Dk] (or [T, H, Dk] with ``cu_seqlens``), bf16 or float32, unit L2 norm
@@ -106,6 +106,8 @@ def kda_chunk_fwd(q, k, v, g, beta, *, initial_state=None, output_final_state: b
     float32 [.., H]; initial_state: float32 [N, H, Dk, Dv] or None (zeros); cu_seqlens:
     int32 [N + 1] on the device (packed sequences, B = 1). ``final_state`` may be given
     (it may be ``initial_state`` itself) or is allocated when ``output_final_state``.
+    ``split`` provides the optional workspace with which the library cuts long sequences
+    into segments run in parallel (few chains); False computes each chain in one pass.
     Returns (o float32 [.., H, Dv], final_state or None).
     """
     import torch
@@ -145,7 +147,7 @@ def kda_chunk_fwd(q, k, v, g, beta, *, initial_state=None, output_final_state: b
         o = torch.empty(v.shape, dtype=torch.float32, device=q.device)
     else:
         _req(o, "o", torch.float32)
-    ws = lib.kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, _dtype_code(q), N)
+    ws = lib.kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, _dtype_code(q), N) if split else 0
     workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
     st = lib.kda_chunk_fwd(B, T, H, Dk, Dv, chunk, _dtype_code(q), KDA_F32, float(scale),
                            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),

@@ -56,9 +56,12 @@ const char *kda_last_error(void) { return g_err; }
 
 int32_t kda_version(void) { return (1 << 16) | 0; }
 
-size_t kda_chunk_fwd_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,
-                                     int32_t, int32_t) {
-    return 0;
+size_t kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                                     int32_t chunk, int32_t in_dtype, int32_t num_seqs) {
+    if (B < 1 || T < 0 || H < 1 || !valid_dtype(in_dtype) ||
+        !kda::chunk_fwd_supported(in_dtype, chunk, Dk, Dv))
+        return 0;
+    return kda::chunk_fwd_split_bytes(B, T, H, Dk, Dv, chunk, num_seqs);
 }
 
 kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
@@ -68,7 +71,6 @@ kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv
                          const float *initial_state, float *final_state, void *o,
                          const int32_t *cu_seqlens, int32_t num_seqs,
                          void *workspace, size_t workspace_bytes, void *stream) {
-    (void)workspace;
     if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || chunk < 1)
         return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive (B=%d T=%d H=%d Dk=%d Dv=%d chunk=%d)",
                     B, T, H, Dk, Dv, chunk);
@@ -90,8 +92,8 @@ kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv
     const void *ptrs[] = {q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
-    if (workspace_bytes < kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, in_dtype, num_seqs))
-        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+    if (workspace_bytes > 0 && !workspace)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace_bytes > 0 with a NULL workspace");
     if (out_dtype != KDA_F32) return fail(KDA_ERR_UNSUPPORTED, "only float32 o is supported");
     if (!kda::chunk_fwd_supported(in_dtype, chunk, Dk, Dv))
         return fail(KDA_ERR_UNSUPPORTED, "no instantiation for in_dtype=%d chunk=%d Dk=%d Dv=%d",
@@ -112,7 +114,10 @@ kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv
     a.s0 = initial_state;
     a.s_out = final_state;
     a.o = static_cast<float *>(o);
-    return hip_status(kda::launch_chunk_fwd(in_dtype, chunk, Dk, Dv, a,
+    a.seg_len = 0;
+    a.nseg = 1;
+    a.ws_r = a.ws_x = a.ws_s = nullptr;
+    return hip_status(kda::launch_chunk_fwd(in_dtype, chunk, Dk, Dv, a, workspace, workspace_bytes,
                                             static_cast<hipStream_t>(stream)),
                       "kda_chunk_fwd launch");
 }

@@ -24,15 +24,17 @@
 //   computes (all loads unconditional; rows past the sequence end are clamped and masked).
 // * Decay factors never overflow: inside a chunk every e^{G_i - G_j} is split at a
 //   16-token block boundary, so each operand carries a factor <= 1 or, inside a diagonal
-//   16x16 block, at most the inverse decay of 16 tokens. One exp per (token, channel).
-//   With fp16 operands each channel of a block is balanced by a power of two near
-//   D^(-1/2) (D = the block's decay), keeping every factor within fp16's range; a chunk in
-//   which some block decays below e^-20 computes A and M with bf16 operands instead, with
-//   the diagonal of M (q_i . k_i, no decay) added exactly in float32.
+//   16x16 block, at most the inverse decay D^-1 of the block's 16 tokens. One exp per
+//   (token, channel). With fp16 operands each channel of a block is balanced by a power of
+//   two near D^(-1/2), keeping every factor within fp16's range. A chunk in which some
+//   block decays below e^-12 (float32 operands: e^-60) is "extreme": its diagonal blocks of
+//   A and M are summed pair by pair in float32 from the cumulative log-decay (one exp per
+//   pair and channel, exact for any decay), and its off-diagonal blocks, whose factors are
+//   all <= 1, use unbalanced operands.
 // * T is never formed beyond its 16x16 diagonal blocks: those are inverted in registers as
-//   (I - L)(I + L^2)(I + L^4)(I + L^8) on the matrix cores (float32-accurate split-bf16
-//   products, transposes by products with the identity), and W and U~ come from block
-//   forward substitution (I + A) W = beta k e^G, (I + A) U~ = Diag(beta) V.
+//   (I - L)(I + L^2)(I + L^4)(I + L^8) on the matrix cores (transposes by products with the
+//   identity), and W and U~ come from block forward substitution (I + A) W = beta k e^G,
+//   (I + A) U~ = Diag(beta) V.
 #include <type_traits>
 
 #include "kda_device.h"
@@ -43,15 +45,16 @@ namespace {
 
 constexpr int align16(int x) { return (x + 15) & ~15; }
 
-template <typename T> struct Tag {
-    typedef T type;
-};
+// A 16-token block whose decay D falls below this (in some channel) is "extreme": its
+// diagonal-block factors span D^-1, which float32 cannot hold beyond e^-60 and which fp16,
+// even balanced to D^(+-1/2), holds only with subnormal (imprecise) small factors beyond
+// about e^-12. Such a chunk computes its diagonal blocks pair by pair.
+template <typename OP> constexpr float extreme_block_decay() {
+    return std::is_same<OP, float>::value ? 8.7565108e-27f   // e^-60
+                                          : 6.1442124e-6f;   // e^-12
+}
 
-// A 16-token block whose decay reaches this (per channel) is "extreme": its balanced
-// fp16 decay factors (up to 2^(-log2(D)/2)) would leave fp16's range.
-constexpr float kExtremeBlockDecay = 2.0611536e-9f;  // e^-20
-
-template <typename OP, int C, int DK, int DV, int NW> struct ChunkShape {
+template <typename OP, int TSZ, int C, int DK, int DV, int NW, bool TRANS> struct ChunkShape {
     static constexpr int NT = 64 * NW;
     static constexpr int NB = C / 16;                       // 16-token blocks per chunk
     static constexpr int NFAR = (NB - 1) * (NB - 2) / 2;    // block pairs (J, I), I >= J + 2
@@ -61,12 +64,14 @@ template <typename OP, int C, int DK, int DV, int NW> struct ChunkShape {
     static constexpr int LCF = C + 4;                       // float32 [token][token] rows
     static constexpr int KT = DK / 16;
     static constexpr int VT = DV / 16;
-    static constexpr int CPW = VT >= NW ? VT / NW : 1;      // state column tiles per wave
+    // state column tiles: the value columns of S, or (transition pass) the Dk columns of X
+    static constexpr int NCT = VT;
+    static constexpr int CPW = NCT >= NW ? NCT / NW : 1;    // state column tiles per wave
     static constexpr int WPW = KT >= NW ? KT / NW : 1;      // W column tiles per wave
-    static constexpr int NOFF = NB * (NB - 1);              // off-diagonal A and M blocks
+    static constexpr int NOFFA = NB * (NB - 1) / 2;         // off-diagonal blocks of A
+    static constexpr int NOFF = TRANS ? NOFFA : 2 * NOFFA;  // ... and of M (no M: no outputs)
     static constexpr int OFFW = NW > NB ? NW - NB : NW;     // waves doing off-diagonal jobs
     static constexpr int OPW = NOFF > 0 ? (NOFF + OFFW - 1) / OFFW : 1;
-    static constexpr int NGRP = DK >= 64 ? DK / 64 : 1;     // 32-lane channel groups
     static constexpr int NVJ = (C / 4) * (DV / 4);          // 4x4 value-tile jobs per chunk
     static constexpr int VPT = (NVJ + NT - 1) / NT;           // value-tile jobs per thread
     static constexpr int NEJ = NB * (DK / 2);                 // (block, channel pair) jobs
@@ -86,6 +91,18 @@ template <typename OP, int C, int DK, int DV, int NW> struct ChunkShape {
     static constexpr int oWb = oMb + align16(C * LDC * SZ);
     static constexpr int P_REUSE = oWb + align16(C * LDK * SZ);
     static constexpr int P_END = P_OPS > P_REUSE ? P_OPS : P_REUSE;
+    // Extreme chunks, before the operands are built (so over region P and the Xt, Qg, KdT
+    // arrays): float64 cumulative log-decay and raw k, q (input type, TSZ bytes), all
+    // [channel][token], and the partial sums of the channel-split waves.
+    static constexpr int SPL = (NW / NB < DK / 32 ? NW / NB : DK / 32) > 1
+                                   ? (NW / NB < DK / 32 ? NW / NB : DK / 32) : 1;
+    static constexpr int LDG = C + 2;
+    static constexpr int LDT = C + 16 / TSZ;
+    static constexpr int oXG = 0;
+    static constexpr int oXK = oXG + align16(DK * LDG * 8);
+    static constexpr int oXQ = oXK + align16(DK * LDT * TSZ);
+    static constexpr int oXP = oXQ + align16(DK * LDT * TSZ);
+    static constexpr int X_END = oXP + align16((SPL - 1) * NB * 8 * 64 * 4);
     static constexpr int oXt = P_END;                        // (beta k e^G)^T  [channel][token]
     static constexpr int oQg = oXt + align16(DK * LDC * SZ); // scale q e^G     [token][channel]
     static constexpr int oKdT = oQg + align16(C * LDK * SZ); // (k e^{G_C-G})^T [channel][token]
@@ -93,16 +110,18 @@ template <typename OP, int C, int DK, int DV, int NW> struct ChunkShape {
     static constexpr int oDd = oYt + align16(DV * LDC * SZ);
     static constexpr int oGc = oDd + align16(NB * DK * 4);
     static constexpr int oBeta = oGc + align16(DK * 4);
-    static constexpr int oMdp = oBeta + align16(C * 4);
-    static constexpr int BYTES = oMdp + align16(NGRP * C * 4);
+    static constexpr int BYTES = oBeta + align16(C * 4);
 
     static_assert(C % 16 == 0 && C >= 16 && C <= 64, "chunk must be 16, 32, 48 or 64");
     static_assert(DK % 16 == 0 && DV % 16 == 0, "head dims must be multiples of 16");
-    static_assert(VT < NW || VT % NW == 0, "state tiles must spread evenly over waves");
+    static_assert(NCT < NW || NCT % NW == 0, "state tiles must spread evenly over waves");
     static_assert(KT < NW || KT % NW == 0, "W tiles must spread evenly over waves");
     static_assert(NB <= NW, "one wave per diagonal block");
     static_assert(C % Step<OP>::KS == 0 && DK % Step<OP>::KS == 0, "step size");
     static_assert(BYTES <= 160 * 1024, "LDS budget of one CU exceeded");
+    static_assert(X_END <= oYt, "extreme-chunk staging must fit before the V^T array");
+    static_assert(DK % (4 * SPL) == 0, "channel split");
+    static_assert(!TRANS || DK == DV, "the transition pass keeps X in the state's tiles");
 };
 
 // Index of the off-diagonal block pair (J, I), I >= J + 2, in the far-operand table.
@@ -164,25 +183,59 @@ template <> struct Raw4<float> {
     static __device__ __forceinline__ f32x4 f32(type u) { return u; }
 };
 
-// Float32-accurate (split-bf16) product of two 16x16 accumulator tiles: X^T Y.
+// Raw inputs staged in LDS (exact: bf16 values keep their 16 bits).
+template <typename Tin> struct Stage;
+template <> struct Stage<bf16_t> {
+    static __device__ __forceinline__ void store8(bf16_t *p, const float *v) {
+        uint4 u;
+        u.x = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xffff0000u);
+        u.y = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xffff0000u);
+        u.z = (__float_as_uint(v[4]) >> 16) | (__float_as_uint(v[5]) & 0xffff0000u);
+        u.w = (__float_as_uint(v[6]) >> 16) | (__float_as_uint(v[7]) & 0xffff0000u);
+        *reinterpret_cast<uint4 *>(p) = u;
+    }
+    static __device__ __forceinline__ f32x4 load4(const bf16_t *p) {
+        return Raw4<bf16_t>::f32(*reinterpret_cast<const uint2 *>(p));
+    }
+    static __device__ __forceinline__ float load1(const bf16_t *p) { return bf16_to_f32(p->bits); }
+};
+template <> struct Stage<float> {
+    static __device__ __forceinline__ void store8(float *p, const float *v) {
+        *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4 *>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
+    static __device__ __forceinline__ f32x4 load4(const float *p) {
+        return *reinterpret_cast<const f32x4 *>(p);
+    }
+    static __device__ __forceinline__ float load1(const float *p) { return *p; }
+};
+
+// Product of two 16x16 accumulator tiles, X^T Y, on the matrix cores of operand type OP.
 // An accumulator tile used as the A fragment is read transposed (lane holds X[4q+e][l%16],
 // which the A operand takes as A[l%16][4q+e]).
-__device__ __forceinline__ f32x4 mm_tn(f32x4 x, f32x4 y) {
+template <typename OP> __device__ __forceinline__ f32x4 mm_tn(f32x4 x, f32x4 y) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    Mma<__bf16>::mma_split(acc, x, y);
+    Mma<OP>::mma(acc, Mma<OP>::from_f32(x), Mma<OP>::from_f32(y));
     return acc;
 }
 
-template <typename Tin, typename OP, int C, int DK, int DV, int NW>
+// TRANS = false: the chunked forward (outputs and final states). With a sequence split,
+//   block (chain, segment p) starts from ws_s[p] and writes the final state for the last p.
+// TRANS = true: the split's first pass, no outputs. Two blocks per (chain, p), p < nseg-1,
+//   run segment p: role R carries S from the initial state (p = 0) or zero and writes it to
+//   ws_r[p] (the segment's map applied to its start state); role X carries X = I with no
+//   values (U~ = 0) and writes ws_x[p] (the segment's linear part), so that
+//   S_{p+1} = X_p S_p + R_p.
+template <typename Tin, typename OP, int C, int DK, int DV, int NW, bool TRANS>
 __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
-    using Sh = ChunkShape<OP, C, DK, DV, NW>;
+    using Sh = ChunkShape<OP, (int)sizeof(Tin), C, DK, DV, NW, TRANS>;
     using MM = Mma<OP>;
     using ST = Step<OP>;
     using RW = Raw2<Tin>;
     using R4 = Raw4<Tin>;
     constexpr int NB = Sh::NB, LDK = Sh::LDK, LDC = Sh::LDC, LCF = Sh::LCF, KT = Sh::KT,
                   CPW = Sh::CPW, KS = ST::KS, TPS = ST::TPS;
-    constexpr bool kDual = std::is_same<OP, _Float16>::value;  // bf16 fallback for A and M
+    constexpr bool kBalance = std::is_same<OP, _Float16>::value;  // fp16 range balancing
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Sh::BYTES];
     OP *const Lk = reinterpret_cast<OP *>(smem + Sh::oLk);
@@ -201,15 +254,23 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     float *const Dd = reinterpret_cast<float *>(smem + Sh::oDd);
     float *const gC = reinterpret_cast<float *>(smem + Sh::oGc);
     float *const sbeta = reinterpret_cast<float *>(smem + Sh::oBeta);
-    float *const mdp = reinterpret_cast<float *>(smem + Sh::oMdp);
+    double *const xG = reinterpret_cast<double *>(smem + Sh::oXG);
+    Tin *const xK = reinterpret_cast<Tin *>(smem + Sh::oXK);
+    Tin *const xQ = reinterpret_cast<Tin *>(smem + Sh::oXQ);
+    float *const xP = reinterpret_cast<float *>(smem + Sh::oXP);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, q4 = lane >> 4;
 
-    // ---- chain: blockIdx -> (sequence, head)
+    // ---- blockIdx -> (chain = (sequence, head), segment)
     const int H = a.H;
-    if ((int)blockIdx.x >= a.n_seqs * H) return;
-    const int n = blockIdx.x / H, h = blockIdx.x % H;
+    const int chains = a.n_seqs * H;
+    const int segs = a.seg_len ? (TRANS ? a.nseg - 1 : a.nseg) : 1;
+    const int bid = TRANS ? (int)blockIdx.x >> 1 : (int)blockIdx.x;
+    const bool isx = TRANS && (blockIdx.x & 1);  // transition block: state = X, no values
+    if (bid >= chains * segs) return;
+    const int chain = bid / segs, seg = bid % segs;
+    const int n = chain / H, h = chain % H;
     int64_t tok0, L;
     if (a.cu_seqlens) {
         tok0 = a.cu_seqlens[n];
@@ -217,6 +278,10 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     } else {
         tok0 = (int64_t)n * a.seq_len;
         L = a.seq_len;
+    }
+    if (a.seg_len) {
+        tok0 += (int64_t)seg * a.seg_len;
+        L = L - (int64_t)seg * a.seg_len < a.seg_len ? L - (int64_t)seg * a.seg_len : a.seg_len;
     }
     const Tin *const qg = static_cast<const Tin *>(a.q);
     const Tin *const kg = static_cast<const Tin *>(a.k);
@@ -226,30 +291,38 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     // ---- per-thread element jobs: (16-token block b, channel pair, half hh of the block);
     // the two halves of a block sit in lanes l and l^32 of one wave
     const int hh = lane >> 5;
-    int jb[Sh::JPT], jc[Sh::JPT], jg[Sh::JPT];
+    int jb[Sh::JPT], jc[Sh::JPT];
     bool jok[Sh::JPT];
 #pragma unroll
     for (int jj = 0; jj < Sh::JPT; ++jj) {
         const int lidx = wave * 32 + (lane & 31) + jj * 32 * NW;
         jb[jj] = lidx / (DK / 2);
         jc[jj] = 2 * (lidx % (DK / 2));
-        jg[jj] = (lidx % (DK / 2)) / 32;
         jok[jj] = jb[jj] < NB;
     }
 
-    // ---- state: this wave's column tiles (cv = wave + NW*j), float32 accumulator layout
-    const bool owns = wave < Sh::VT;
+    // ---- state: this wave's column tiles (ct = wave + NW*j) of S (or X), float32
+    // accumulator layout
+    const bool owns = wave < Sh::NCT;
+    const float *sinit = a.s0 ? a.s0 + sbase : nullptr;
+    if (a.seg_len && !TRANS) sinit = a.ws_s + ((int64_t)seg * chains + chain) * DK * DV;
+    if (TRANS && seg > 0) sinit = nullptr;
     f32x4 S[CPW][KT];
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
-        const int cv = wave + NW * j;
+        const int ct = wave + NW * j;
 #pragma unroll
         for (int r = 0; r < KT; ++r) {
             S[j][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (owns && a.s0) {
+            if (owns && !isx && sinit) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    S[j][r][e] = a.s0[sbase + (int64_t)(16 * r + 4 * q4 + e) * DV + 16 * cv + lr];
+                    S[j][r][e] = sinit[(int64_t)(16 * r + 4 * q4 + e) * DV + 16 * ct + lr];
+            }
+            if (owns && isx) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    S[j][r][e] = (16 * r + 4 * q4 + e == 16 * ct + lr) ? 1.f : 0.f;
             }
         }
     }
@@ -286,17 +359,19 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         const rsrc_t rg = make_rsrc(a.g + t0 * krow, (uint32_t)(Lc * krow * 4));
         const rsrc_t rv = make_rsrc(vg + t0 * vrow, (uint32_t)(Lc * vrow * ESZ));
         const rsrc_t rb = make_rsrc(a.beta + t0 * H, (uint32_t)(Lc * H * 4));
+        if (!isx) {
 #pragma unroll
-        for (int vv = 0; vv < Sh::VPT; ++vv)
+            for (int vv = 0; vv < Sh::VPT; ++vv)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pv[vv][r] = R4::load(rv, vo[vv] * ESZ, r * vrow * ESZ);
+                for (int r = 0; r < 4; ++r) pv[vv][r] = R4::load(rv, vo[vv] * ESZ, r * vrow * ESZ);
+        }
 #pragma unroll
         for (int jj = 0; jj < Sh::JPT; ++jj) {
 #pragma unroll
             for (int ii = 0; ii < 8; ++ii) {
                 pg[jj][ii] = Raw2<float>::load(rg, ko[jj] * 4, ii * krow * 4);
                 pk[jj][ii] = RW::load(rk, ko[jj] * ESZ, ii * krow * ESZ);
-                pq[jj][ii] = RW::load(rq, ko[jj] * ESZ, ii * krow * ESZ);
+                if constexpr (!TRANS) pq[jj][ii] = RW::load(rq, ko[jj] * ESZ, ii * krow * ESZ);
             }
         }
         pbeta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -316,7 +391,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         float dk0[Sh::JPT], dk1[Sh::JPT];  // decay of the job's whole 16-token block
         // k and q of token ii of job jj (zero past the sequence end), from the prefetch registers
         auto kq = [&](int jj, int ii, float &k0, float &k1, float &q0, float &q1) {
-            const f32x2 kk = RW::f32(pk[jj][ii]), qq = RW::f32(pq[jj][ii]);
+            const f32x2 kk = RW::f32(pk[jj][ii]);
+            const f32x2 qq = TRANS ? f32x2{0.f, 0.f} : RW::f32(pq[jj][ii]);
             k0 = kk.x;
             k1 = kk.y;
             q0 = qq.x * a.scale;
@@ -357,13 +433,14 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 Dd[jb[jj] * DK + jc[jj]] = dk0[jj];
                 Dd[jb[jj] * DK + jc[jj] + 1] = dk1[jj];
             }
-            ext_local |= jok[jj] && (dk0[jj] < kExtremeBlockDecay || dk1[jj] < kExtremeBlockDecay);
+            ext_local |= jok[jj] && (dk0[jj] < extreme_block_decay<OP>() ||
+                                     dk1[jj] < extreme_block_decay<OP>());
         }
         if (tid < C) sbeta[tid] = pbeta;
 #pragma unroll
         for (int vv = 0; vv < Sh::VPT; ++vv) {  // v^T: 4 columns x 4 consecutive tokens per store
             int tg, cg;
-            if (vjob(vv, tg, cg)) {
+            if (!isx && vjob(vv, tg, cg)) {
                 f32x4 vr[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) vr[r] = R4::f32(pv[vv][r]);
@@ -374,38 +451,115 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                         MM::from_f32(f32x4{vr[0][c], vr[1][c], vr[2][c], vr[3][c]});
             }
         }
-        bool extreme = false;
-        if constexpr (kDual) {
-            extreme = __syncthreads_or(ext_local);
-            if (extreme) {
-                // exact scale * q_i . k_i for the diagonal of M, per 64-channel group
+        const bool extreme = __syncthreads_or(ext_local);
+
+        // ---- extreme chunks: the diagonal 16x16 blocks of A and M pair by pair in float32,
+        // A_ij = beta_i sum_c k_i[c] k_j[c] e^{G_i[c]-G_j[c]}, M_ij likewise with scale q_i,
+        // from the cumulative log-decay G summed in float64 (G_i - G_j keeps float32 accuracy
+        // however large G grows; no factor leaves the float range for any decay)
+        f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dM = {0.f, 0.f, 0.f, 0.f};
+        if (extreme) {
 #pragma unroll
-                for (int jj = 0; jj < Sh::JPT; ++jj) {
+            for (int jj = 0; jj < Sh::JPT; ++jj) {
+                double G0[8], G1[8];
+                float kk0[8], kk1[8], qq0[8], qq1[8];
+                double c0s = 0.0, c1s = 0.0;
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) {
+                    c0s += (double)pg[jj][ii].x;
+                    c1s += (double)pg[jj][ii].y;
+                    G0[ii] = c0s;
+                    G1[ii] = c1s;
+                    const f32x2 kk = RW::f32(pk[jj][ii]);
+                    const f32x2 qq = TRANS ? f32x2{0.f, 0.f} : RW::f32(pq[jj][ii]);
+                    kk0[ii] = kk.x;
+                    kk1[ii] = kk.y;
+                    qq0[ii] = qq.x;
+                    qq1[ii] = qq.y;
+                }
+                const double f0 = __shfl_xor(c0s, 32), f1 = __shfl_xor(c1s, 32);  // first half
+                if (jok[jj]) {
 #pragma unroll
                     for (int ii = 0; ii < 8; ++ii) {
-                        float k0, k1, q0, q1;
-                        kq(jj, ii, k0, k1, q0, q1);
-                        float d = q0 * k0 + q1 * k1;
+                        G0[ii] += hh ? f0 : 0.0;
+                        G1[ii] += hh ? f1 : 0.0;
+                    }
+                    const int c0 = jc[jj], tc = 16 * jb[jj] + 8 * hh;
 #pragma unroll
-                        for (int m = 16; m > 0; m >>= 1) d += __shfl_xor(d, m);
-                        if (jok[jj] && (lane & 31) == 0) mdp[jg[jj] * C + 16 * jb[jj] + 8 * hh + ii] = d;
+                    for (int ii = 0; ii < 8; ii += 2) {
+                        *reinterpret_cast<f64x2 *>(xG + c0 * Sh::LDG + tc + ii) = f64x2{G0[ii], G0[ii + 1]};
+                        *reinterpret_cast<f64x2 *>(xG + (c0 + 1) * Sh::LDG + tc + ii) = f64x2{G1[ii], G1[ii + 1]};
+                    }
+                    Stage<Tin>::store8(xK + c0 * Sh::LDT + tc, kk0);
+                    Stage<Tin>::store8(xK + (c0 + 1) * Sh::LDT + tc, kk1);
+                    if constexpr (!TRANS) {
+                        Stage<Tin>::store8(xQ + c0 * Sh::LDT + tc, qq0);
+                        Stage<Tin>::store8(xQ + (c0 + 1) * Sh::LDT + tc, qq1);
                     }
                 }
             }
-        } else {
             __syncthreads();
+            const int I = wave % NB, sp = wave / NB;
+            f32x4 a4 = {0.f, 0.f, 0.f, 0.f}, m4 = {0.f, 0.f, 0.f, 0.f};
+            if (sp < Sh::SPL) {
+                constexpr int CH = DK / Sh::SPL;
+                const int ti = 16 * I + 4 * q4, tj = 16 * I + lr;
+#pragma unroll 4
+                for (int c = sp * CH; c < (sp + 1) * CH; ++c) {
+                    const f64x2 gi01 = *reinterpret_cast<const f64x2 *>(xG + c * Sh::LDG + ti);
+                    const f64x2 gi23 = *reinterpret_cast<const f64x2 *>(xG + c * Sh::LDG + ti + 2);
+                    const double gj = xG[c * Sh::LDG + tj];
+                    const float gd[4] = {(float)(gi01.x - gj), (float)(gi01.y - gj),
+                                         (float)(gi23.x - gj), (float)(gi23.y - gj)};
+                    const f32x4 ki = Stage<Tin>::load4(xK + c * Sh::LDT + ti);
+                    const f32x4 qi = TRANS ? f32x4{0.f, 0.f, 0.f, 0.f} : Stage<Tin>::load4(xQ + c * Sh::LDT + ti);
+                    const float kj = Stage<Tin>::load1(xK + c * Sh::LDT + tj);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float ex = kj * exp_gate<OP>(fminf(gd[e], 0.f));
+                        a4[e] += ki[e] * ex;
+                        m4[e] += qi[e] * ex;
+                    }
+                }
+                if (sp > 0) {
+                    float *dst = xP + ((sp - 1) * NB + I) * 512 + lane;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dst[e * 64] = a4[e];
+                        dst[(4 + e) * 64] = m4[e];
+                    }
+                }
+            }
+            __syncthreads();
+            if (sp == 0) {
+#pragma unroll
+                for (int r = 1; r < Sh::SPL; ++r) {
+                    const float *src = xP + ((r - 1) * NB + I) * 512 + lane;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        a4[e] += src[e * 64];
+                        m4[e] += src[(4 + e) * 64];
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 4 * q4 + e;
+                    dA[e] = row > lr ? sbeta[16 * I + row] * a4[e] : 0.f;
+                    dM[e] = row >= lr ? a.scale * m4[e] : 0.f;
+                }
+            }
+            __syncthreads();  // the staging area is overwritten by the operands below
         }
 
         // ---- P1: matrix-core operands
-        // fp16: rows of block I carry a per-channel power of two 2^e_I near D_I^(-1/2) and the
-        // right operands paired with block I carry 2^-e_I (exact: products are unchanged)
-        auto p1 = [&](auto tag, bool bal) {
-            typedef typename decltype(tag)::type E;  // element type of the A/M operands
+        // fp16, ordinary chunks: rows of block I carry a per-channel power of two 2^e_I near
+        // D_I^(-1/2) and the right operands paired with block I carry 2^-e_I (exact: products
+        // are unchanged). Extreme chunks need no Rd and no balancing: every factor left is
+        // <= 1, so fp16 underflow costs at most 2^-25 absolutely.
+        {
+            const bool bal = kBalance && !extreme, wrd = !extreme;
             auto bexp = [&](float d) { return bal ? (int)floorf(-0.5f * __log2f(d)) : 0; };
-            auto st = [&](OP *p, float x, float y) {
-                if constexpr (std::is_same<E, OP>::value) MM::store_pair(p, x, y);
-                else Mma<__bf16>::store_pair(reinterpret_cast<__bf16 *>(p), x, y);
-            };
+            auto st = [&](OP *p, float x, float y) { MM::store_pair(p, x, y); };
 #pragma unroll
             for (int jj = 0; jj < Sh::JPT; ++jj) {
                 if (!jok[jj]) continue;
@@ -448,10 +602,10 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                     const float lq0 = q0[ii] * al0[jj][ii] * sb0, lq1 = q1[ii] * al1[jj][ii] * sb1;
                     const float rk0 = k0[ii] * sf0[jj][ii] * nx0, rk1 = k1[ii] * sf1[jj][ii] * nx1;
                     st(Lk + i * LDK + c0, lk0, lk1);
-                    st(Lq + i * LDK + c0, lq0, lq1);
+                    if constexpr (!TRANS) st(Lq + i * LDK + c0, lq0, lq1);
                     st(Rk + i * LDK + c0, rk0, rk1);
-                    st(Rd + i * LDK + c0, rk0 * rd0, rk1 * rd1);
-                    MM::store_pair(Qg + i * LDK + cp, lq0 * pq0, lq1 * pq1);
+                    if (wrd) st(Rd + i * LDK + c0, rk0 * rd0, rk1 * rd1);
+                    if constexpr (!TRANS) MM::store_pair(Qg + i * LDK + cp, lq0 * pq0, lq1 * pq1);
                     xt0[ii] = static_cast<OP>(lk0 * pq0);
                     xt1[ii] = static_cast<OP>(lk1 * pq1);
                     kd0[ii] = static_cast<OP>(rk0 * po0);
@@ -485,13 +639,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                     *reinterpret_cast<f4 *>(KdT + (c0 + 1) * LDC + tp) = f4{kd1[ii], kd1[ii + 1], kd1[ii + 2], kd1[ii + 3]};
                 }
             }
-        };
-        if constexpr (kDual) {
-            if (extreme) p1(Tag<__bf16>{}, false);
-            else p1(Tag<OP>{}, true);
-        } else {
-            p1(Tag<OP>{}, false);
         }
+
         // the next chunk's inputs are in flight from here on
         if (ci + 1 < nchunks) {
             const int64_t rem = L - (ci + 1) * C;
@@ -500,31 +649,22 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         __syncthreads();
 
         // ---- P2: A and M 16x16 blocks; the diagonal blocks' waves also invert I + A_II
-        auto block_am = [&](auto tag, bool isM, int I, int J) {
-            using SA = typename decltype(tag)::type;
-            typedef typename std::conditional<std::is_same<SA, Step<__bf16>>::value, __bf16, OP>::type E;
+        auto am = [&](bool isM, int I, int J) {
             const OP *left = (isM ? Lq : Lk) + (16 * I + lr) * LDK;
             const OP *right = I == J       ? Rd + (16 * J + lr) * LDK
                               : I == J + 1 ? Rk + (16 * J + lr) * LDK
                                            : Rfar + (far_index(NB, J, I) * 16 + lr) * LDK;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < DK; kk += SA::KS)
-                SA::mma(acc, SA::contig(reinterpret_cast<const E *>(left), kk, q4),
-                        SA::contig(reinterpret_cast<const E *>(right), kk, q4));
+            for (int kk = 0; kk < DK; kk += KS)
+                ST::mma(acc, ST::contig(left, kk, q4), ST::contig(right, kk, q4));
             return acc;
-        };
-        auto am = [&](bool isM, int I, int J) {
-            if constexpr (kDual) {
-                if (extreme) return block_am(Tag<Step<__bf16>>{}, isM, I, J);
-            }
-            return block_am(Tag<ST>{}, isM, I, J);
         };
         f32x4 tdiag = {0.f, 0.f, 0.f, 0.f}, mdiag = {0.f, 0.f, 0.f, 0.f};
         const bool dj = wave < NB;
         if (dj) {
             const int I = wave;
-            f32x4 Lm = am(false, I, I);
+            f32x4 Lm = extreme ? dA : am(false, I, I);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (4 * q4 + e <= lr) Lm[e] = 0.f;  // strictly lower
@@ -532,25 +672,22 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             f32x4 Id;
 #pragma unroll
             for (int e = 0; e < 4; ++e) Id[e] = (4 * q4 + e == lr) ? 1.f : 0.f;
-            const f32x4 Lt = mm_tn(Lm, Id);
-            const f32x4 L2 = mm_tn(Lt, Lm), L2t = mm_tn(Lm, Lt);
-            const f32x4 L4 = mm_tn(L2t, L2), L4t = mm_tn(L2, L2t);
-            const f32x4 L8 = mm_tn(L4t, L4);
+            const f32x4 Lt = mm_tn<OP>(Lm, Id);
+            const f32x4 L2 = mm_tn<OP>(Lt, Lm), L2t = mm_tn<OP>(Lm, Lt);
+            const f32x4 L4 = mm_tn<OP>(L2t, L2), L4t = mm_tn<OP>(L2, L2t);
+            const f32x4 L8 = mm_tn<OP>(L4t, L4);
             const f32x4 P1 = Id - Lm, P1t = Id - Lt;
-            const f32x4 P2 = P1 + mm_tn(P1t, L2), P2t = P1t + mm_tn(L2, P1t);
-            const f32x4 P3 = P2 + mm_tn(P2t, L4), P3t = P2t + mm_tn(L4, P2t);
-            tdiag = P3 + mm_tn(P3t, L8);
-            mdiag = am(true, I, I);
+            const f32x4 P2 = P1 + mm_tn<OP>(P1t, L2), P2t = P1t + mm_tn<OP>(L2, P1t);
+            const f32x4 P3 = P2 + mm_tn<OP>(P2t, L4), P3t = P2t + mm_tn<OP>(L4, P2t);
+            tdiag = P3 + mm_tn<OP>(P3t, L8);
+            if (TRANS) {
+            } else if (extreme) {
+                mdiag = dM;
+            } else {
+                mdiag = am(true, I, I);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 4 * q4 + e;
-                if (row < lr) mdiag[e] = 0.f;
-                if (kDual && extreme && row == lr) {
-                    float d = 0.f;
-#pragma unroll
-                    for (int g = 0; g < Sh::NGRP; ++g) d += mdp[g * C + 16 * I + lr];
-                    mdiag[e] = d;
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (4 * q4 + e < lr) mdiag[e] = 0.f;
             }
         }
         f32x4 offv[Sh::OPW];
@@ -562,8 +699,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 const int x = ow + Sh::OFFW * j;
                 if (ow >= 0 && x < Sh::NOFF) {
                     int I, J;
-                    lower_block(x % (Sh::NOFF / 2), I, J);
-                    offv[j] = am(x >= Sh::NOFF / 2, I, J);
+                    lower_block(x % Sh::NOFFA, I, J);
+                    offv[j] = am(x >= Sh::NOFFA, I, J);
                 }
             }
         }
@@ -574,7 +711,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * I + 4 * q4 + e, col = 16 * I + lr;
                 Tf[row * LCF + col] = tdiag[e];
-                Mb[row * LDC + ST::perm(col)] = static_cast<OP>(mdiag[e]);
+                if constexpr (!TRANS) Mb[row * LDC + ST::perm(col)] = static_cast<OP>(mdiag[e]);
             }
         }
 #pragma unroll
@@ -582,8 +719,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             const int x = ow + Sh::OFFW * j;
             if (Sh::NOFF > 0 && ow >= 0 && x < Sh::NOFF) {
                 int I, J;
-                lower_block(x % (Sh::NOFF > 0 ? Sh::NOFF / 2 : 1), I, J);
-                const bool isM = x >= Sh::NOFF / 2;
+                lower_block(x % (Sh::NOFFA > 0 ? Sh::NOFFA : 1), I, J);
+                const bool isM = x >= Sh::NOFFA;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int row = 16 * I + 4 * q4 + e, col = 16 * J + lr;
@@ -593,7 +730,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             }
         }
         // zero the upper blocks of M (read by the paired-tile steps of M U)
-        for (int idx = tid; idx < C * C; idx += Sh::NT) {
+        for (int idx = tid; idx < (TRANS ? 0 : C * C); idx += Sh::NT) {
             const int row = idx / C, col = idx % C;
             if (col / 16 > row / 16) Mb[row * LDC + ST::perm(col)] = static_cast<OP>(0.f);
         }
@@ -627,19 +764,25 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         f32x4 Ur[CPW][NB];
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
+            const int cv = wave + NW * j;
+            if (isx) {  // transition block: X has no value columns, U~ = 0
+#pragma unroll
+                for (int I = 0; I < NB; ++I) Ur[j][I] = f32x4{0.f, 0.f, 0.f, 0.f};
+                continue;
+            }
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
-                const int cv = wave + NW * j;
                 f32x4 R = MM::to_f32(MM::load(Yt + (16 * cv + lr) * LDC + 16 * I + 4 * q4)) *
                           *reinterpret_cast<const f32x4 *>(sbeta + 16 * I + 4 * q4);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int J = 0; J < I; ++J)
-                    Mma<__bf16>::mma_split(acc, *reinterpret_cast<const f32x4 *>(Af + (16 * I + lr) * LCF + 16 * J + 4 * q4),
-                                           Ur[j][J]);
+                    MM::mma(acc, MM::from_f32(*reinterpret_cast<const f32x4 *>(Af + (16 * I + lr) * LCF + 16 * J + 4 * q4)),
+                            MM::from_f32(Ur[j][J]));
                 R -= acc;
                 f32x4 u = {0.f, 0.f, 0.f, 0.f};
-                Mma<__bf16>::mma_split(u, *reinterpret_cast<const f32x4 *>(Tf + (16 * I + lr) * LCF + 16 * I + 4 * q4), R);
+                MM::mma(u, MM::from_f32(*reinterpret_cast<const f32x4 *>(Tf + (16 * I + lr) * LCF + 16 * I + 4 * q4)),
+                        MM::from_f32(R));
                 Ur[j][I] = u;
             }
         }
@@ -669,6 +812,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 for (int p = 0; p < C / KS; ++p) ufr[p] = ST::regs(&U[p * TPS]);
 #pragma unroll
                 for (int I = 0; I < NB; ++I) {
+                    if (TRANS) break;  // the transition pass produces no outputs
                     f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int p = 0; p < DK / KS; ++p)
@@ -695,26 +839,138 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         }
     }
 
-    if (a.s_out && owns) {
+    float *dst = nullptr;
+    if (TRANS)
+        dst = (isx ? a.ws_x : a.ws_r) + ((int64_t)seg * chains + chain) * DK * DV;
+    else if (a.s_out && seg == segs - 1)
+        dst = a.s_out + sbase;
+    if (owns && dst) {
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
-            const int cv = wave + NW * j;
+            const int ct = wave + NW * j;
+            constexpr int ld = DV;
+            const int col = 16 * ct + lr;
 #pragma unroll
             for (int r = 0; r < KT; ++r)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    a.s_out[sbase + (int64_t)(16 * r + 4 * q4 + e) * DV + 16 * cv + lr] = S[j][r][e];
+                    dst[(int64_t)(16 * r + 4 * q4 + e) * ld + col] = S[j][r][e];
         }
     }
 }
 
-template <typename Tin, typename OP, int C, int DK, int DV, int NW>
+
+// Split combine: S_0 = the initial state (or zero), S_1 = R_0, S_{p+1} = X_p S_p + R_p.
+// One workgroup per (chain, 16-column block); float32 FMA with the running block in LDS.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void split_combine_kernel(ChunkArgs a) {
+    __shared__ float cur[DK][16];
+    const int chains = a.n_seqs * a.H;
+    const int chain = blockIdx.x / (DV / 16), cb = blockIdx.x % (DV / 16);
+    if (chain >= chains) return;
+    const int tid = threadIdx.x;
+    const int64_t cstride = (int64_t)chains * DK * DV;
+    float *s0 = a.ws_s + (int64_t)chain * DK * DV + 16 * cb;
+    for (int idx = tid; idx < DK * 16; idx += 256) {
+        const int r = idx / 16, c = idx % 16;
+        const float v = a.s0 ? a.s0[(int64_t)chain * DK * DV + (int64_t)r * DV + 16 * cb + c] : 0.f;
+        s0[(int64_t)r * DV + c] = v;
+        cur[r][c] = a.ws_r[(int64_t)chain * DK * DV + (int64_t)r * DV + 16 * cb + c];  // R_0
+    }
+    __syncthreads();
+    for (int p = 1; p < a.nseg; ++p) {
+        float *sp = s0 + p * cstride;
+        for (int idx = tid; idx < DK * 16; idx += 256) sp[(int64_t)(idx / 16) * DV + idx % 16] = cur[idx / 16][idx % 16];
+        if (p + 1 >= a.nseg) break;
+        // next = X_p cur + R_p
+        const float *X = a.ws_x + ((int64_t)p * chains + chain) * DK * DK;
+        const float *R = a.ws_r + ((int64_t)p * chains + chain) * DK * DV + 16 * cb;
+        constexpr int PER = DK * 16 / 256;  // outputs per thread
+        float acc[PER];
+        const int r = tid / (256 / DK), c0 = (tid % (256 / DK)) * PER;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) acc[u] = R[(int64_t)r * DV + c0 + u];
+        for (int kk = 0; kk < DK; ++kk) {
+            const float x = X[(int64_t)r * DK + kk];
+#pragma unroll
+            for (int u = 0; u < PER; ++u) acc[u] += x * cur[kk][c0 + u];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < PER; ++u) cur[r][c0 + u] = acc[u];
+        __syncthreads();
+    }
+}
+
+template <typename Tin, typename OP, int C, int DK, int DV, int NW, int NWT = NW>
 hipError_t launch_t(const ChunkArgs &a, hipStream_t stream) {
-    const int64_t blocks = (int64_t)a.n_seqs * a.H;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NW>), dim3((unsigned)blocks),
-                       dim3(64 * NW), 0, stream, a);
+    const int64_t chains = (int64_t)a.n_seqs * a.H;
+    if (2 * chains * (a.seg_len ? a.nseg : 1) > 0x7fffffff) return hipErrorInvalidValue;
+    if (a.seg_len) {
+        hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NWT, true>),
+                           dim3((unsigned)(2 * chains * (a.nseg - 1))), dim3(64 * NWT), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((split_combine_kernel<DK, DV>), dim3((unsigned)(chains * (DV / 16))),
+                           dim3(256), 0, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NW, false>),
+                       dim3((unsigned)(chains * (a.seg_len ? a.nseg : 1))), dim3(64 * NW), 0,
+                       stream, a);
     return hipGetLastError();
+}
+
+// Sequence-split plan for B sequences of T tokens. One workgroup fills a compute unit
+// (its LDS), so a launch runs in ceil(blocks / CUs) rounds. Without a split that is
+// ceil(chains / CUs) rounds of the whole sequence; cutting it into P segments costs one
+// transition pass (two blocks per chain and segment but the last, no outputs) plus the
+// full pass over P segments, each round 1/P of the sequence. P is picked by that estimate.
+struct SplitPlan {
+    int nseg = 1, seg_len = 0;
+    size_t bytes = 0;
+};
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+SplitPlan plan_split(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk) {
+    SplitPlan sp;
+    const int64_t chains = (int64_t)B * H;
+    const int64_t cus = device_cus();
+    if (chains <= 0 || cus <= 0 || T <= 0 || Dk != Dv) return sp;
+    const int64_t nchunks = ((int64_t)T + chunk - 1) / chunk;
+    auto rounds = [&](int64_t blocks) { return (double)((blocks + cus - 1) / cus); };
+    constexpr double kTransCost = 0.85;   // transition chunk vs full chunk (no M, no outputs)
+    constexpr double kFixedCost = 4.0;    // extra launches and the combine, in chunk times
+    double best = rounds(chains) * (double)nchunks;
+    for (int64_t P = 2; P <= 16; ++P) {
+        const int64_t per = (nchunks + P - 1) / P;  // chunks per segment
+        if (per < 8) break;
+        const int64_t nseg = (nchunks + per - 1) / per;
+        if (nseg < 2) continue;
+        const double cost = rounds(2 * chains * (nseg - 1)) * per * kTransCost +
+                            rounds(chains * nseg) * per + kFixedCost + 0.25 * (nseg - 2);
+        if (cost < 0.9 * best) {
+            best = cost;
+            sp.nseg = (int)nseg;
+            sp.seg_len = (int)(per * chunk);
+        }
+    }
+    if (sp.nseg < 2) return SplitPlan{};
+    sp.bytes = (size_t)(sp.nseg - 1) * chains * ((size_t)Dk * Dv + (size_t)Dk * Dk) * 4 +
+               (size_t)sp.nseg * chains * Dk * Dv * 4;
+    return sp;
 }
 
 }  // namespace
@@ -727,11 +983,33 @@ bool chunk_fwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv
     return false;
 }
 
+size_t chunk_fwd_split_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                             int32_t chunk, int32_t num_seqs) {
+    if (num_seqs != B || (!chunk_fwd_supported(1, chunk, Dk, Dv) && !chunk_fwd_supported(0, chunk, Dk, Dv)))
+        return 0;
+    return plan_split(B, T, H, Dk, Dv, chunk).bytes;
+}
+
 hipError_t launch_chunk_fwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv,
-                            const ChunkArgs &a, hipStream_t stream) {
+                            const ChunkArgs &args, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
     if (!chunk_fwd_supported(in_dtype, chunk, Dk, Dv)) return hipErrorInvalidValue;
-    if (a.n_seqs == 0) return hipSuccess;
-    if (in_dtype == 1) return launch_t<bf16_t, _Float16, 64, 128, 128, 4>(a, stream);
+    if (args.n_seqs == 0) return hipSuccess;
+    ChunkArgs a = args;
+    a.seg_len = 0;
+    a.nseg = 1;
+    if (!a.cu_seqlens && workspace) {
+        const SplitPlan sp = plan_split(a.n_seqs, a.seq_len, a.H, Dk, Dv, chunk);
+        if (sp.nseg > 1 && workspace_bytes >= sp.bytes) {
+            const size_t chains = (size_t)a.n_seqs * a.H;
+            a.seg_len = sp.seg_len;
+            a.nseg = sp.nseg;
+            a.ws_r = static_cast<float *>(workspace);
+            a.ws_x = a.ws_r + (size_t)(sp.nseg - 1) * chains * Dk * Dv;
+            a.ws_s = a.ws_x + (size_t)(sp.nseg - 1) * chains * Dk * Dk;
+        }
+    }
+    if (in_dtype == 1) return launch_t<bf16_t, _Float16, 64, 128, 128, 8>(a, stream);
     if (chunk == 16) return launch_t<float, float, 16, 16, 16, 4>(a, stream);
     if (Dk == 32) return launch_t<float, float, 64, 32, 32, 4>(a, stream);
     return launch_t<float, float, 64, 64, 64, 4>(a, stream);

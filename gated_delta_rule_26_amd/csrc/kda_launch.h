@@ -17,6 +17,12 @@ struct ChunkArgs {
     const float *s0;             // [N, H, Dk, Dv] or nullptr
     float *s_out;                // [N, H, Dk, Dv] or nullptr
     float *o;                    // [tokens, H, Dv]
+    // sequence split (fixed-length batches with few chains): each sequence is cut into nseg
+    // segments of seg_len tokens (a multiple of the chunk); 0 = no split
+    int32_t seg_len, nseg;
+    float *ws_r;                 // [nseg-1][N*H][Dk][Dv] segment final states from the split start
+    float *ws_x;                 // [nseg-1][N*H][Dk][Dk] segment transitions
+    float *ws_s;                 // [nseg][N*H][Dk][Dv]   initial state of every segment
 };
 
 struct DecodeArgs {
@@ -28,13 +34,21 @@ struct DecodeArgs {
     float *o;
 };
 
+// Workspace bytes the sequence split needs for this problem on the current device (0: no
+// split). The split is used only when the call provides at least this much workspace.
+size_t chunk_fwd_split_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                             int32_t chunk, int32_t num_seqs);
+
 // True if an instantiation exists for these parameters (in_dtype is a kda_dtype code).
 bool chunk_fwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv);
 bool decode_supported(int32_t in_dtype, int32_t Dk, int32_t Dv);
 
 // Enqueue the kernel on `stream`; returns the launch status (hipGetLastError).
+// Enqueue kda_chunk_fwd. `workspace` (may be null) enables the sequence split when it holds
+// chunk_fwd_split_bytes(...) bytes and the batch has no cu_seqlens.
 hipError_t launch_chunk_fwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv,
-                            const ChunkArgs &a, hipStream_t stream);
+                            const ChunkArgs &a, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 hipError_t launch_decode(int32_t in_dtype, int32_t Dk, int32_t Dv, const DecodeArgs &a,
                          hipStream_t stream);
 

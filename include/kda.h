@@ -82,8 +82,15 @@ const char *kda_last_error(void);
 int32_t kda_version(void);
 
 /*
- * kda_chunk_fwd_workspace_bytes - device workspace kda_chunk_fwd needs for these sizes.
- * Currently 0 for every supported configuration; callers may pass workspace = NULL.
+ * kda_chunk_fwd_workspace_bytes - device workspace that lets kda_chunk_fwd split long
+ * sequences for these sizes on the current device (0 when no split applies).
+ *
+ * With few (sequence, head) chains the recurrence would occupy only a few compute units,
+ * so a batch without cu_seqlens may be cut into segments along the sequence: a first pass
+ * computes every segment's state map in parallel, a small pass chains the maps, and the
+ * chunked forward then runs all segments in parallel. The workspace holds the per-segment
+ * maps and states. It is optional: with less workspace (or NULL) the call is computed
+ * without the split, with the same result up to rounding.
  */
 size_t kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
                                      int32_t chunk, int32_t in_dtype, int32_t num_seqs);
@@ -108,7 +115,8 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk
  *   chunk         tokens per chunk of the chunkwise form (a tuning choice: every chunk
  *                 size gives the same result up to rounding)
  *   scale         multiplies q (finite)
- *   workspace     device buffer of at least kda_chunk_fwd_workspace_bytes(...) bytes
+ *   workspace     optional device buffer (see kda_chunk_fwd_workspace_bytes); its contents
+ *                 are scratch, overwritten by the call
  *
  * Compiled instantiations (in_dtype, chunk, Dk = Dv):
  *   (KDA_BF16, 64, 128)   bf16 matrix-core path, float32 accumulation and state

@@ -17,7 +17,7 @@ TOL_F32 = 1e-4
 TOL_BF16 = 2e-2
 
 
-def gpu_chunk(x, stored, *, B=1, chunk, s0=None, cu=None, scale=1.0, alias=False):
+def gpu_chunk(x, stored, *, B=1, chunk, s0=None, cu=None, scale=1.0, alias=False, split=True):
     torch = torch_mod()
     T = x["q"].shape[0] // B
     sh = lambda a: a.reshape(B, T, *a.shape[1:]) if cu is None else a  # noqa: E731
@@ -26,7 +26,7 @@ def gpu_chunk(x, stored, *, B=1, chunk, s0=None, cu=None, scale=1.0, alias=False
     init = None if s0 is None else to_dev(np.ascontiguousarray(s0, dtype=np.float32))
     cu_t = None if cu is None else to_dev(np.asarray(cu, dtype=np.int32))
     o, S = kda.kda_chunk_fwd(q, k, v, g, beta, initial_state=init, cu_seqlens=cu_t, chunk=chunk,
-                             scale=scale, final_state=init if alias else None)
+                             scale=scale, final_state=init if alias else None, split=split)
     torch.cuda.synchronize()
     return o.reshape(x["v"].shape).cpu().numpy(), S.cpu().numpy()
 
@@ -99,6 +99,36 @@ def test_f32_strong_decay(D, C):
     assert_close(S, S_ref, TOL_F32, "final state")
 
 
+def extreme_gates(x, seed: int, g_min: float):
+    """Overwrite a seeded half of the channels of every head with per-token log-decays drawn
+    uniformly from [g_min, 0.8 g_min] on a random third of the tokens: the mix of decays that
+    no single reference per 16-token block can represent (a factor e^{16 |g|} overflows
+    float32 for |g| > 5.5) next to ordinary channels."""
+    rng = np.random.default_rng(seed)
+    T, H, K = x["g"].shape
+    tok = rng.random(T) < 1 / 3
+    ch = rng.random((H, K)) < 0.5
+    sel = tok[:, None, None] & ch[None]
+    vals = rng.uniform(g_min, 0.8 * g_min, size=x["g"].shape).astype(np.float32)
+    x["g"][sel] = vals[sel]
+    return x
+
+
+@pytest.mark.parametrize("D,C", [(16, 16), (32, 64), (64, 64)])
+@pytest.mark.parametrize("g_min", [-8.0, -40.0, -400.0])
+def test_f32_extreme_decay(D, C, g_min):
+    """Per-token decays down to e^-400 (block decays far below e^-60): the diagonal blocks are
+    summed pair by pair from the cumulative log-decay."""
+    T, H = 333, 2
+    x = extreme_gates(random_inputs(135, T, H, D, "f32"), 136, g_min)
+    s0 = random_states(137, 1, H, D)
+    note(f"f32 extreme decay D={D} g_min={g_min}")
+    o, S = gpu_chunk(x, "f32", chunk=C, s0=s0, scale=D ** -0.5)
+    o_ref, S_ref = run_oracle(x, "f32", scale=D ** -0.5, initial_state=s0)
+    assert_close(o, o_ref, TOL_F32, "o")
+    assert_close(S, S_ref, TOL_F32, "final state")
+
+
 # ----------------------------------------------------------------------- bf16 instantiation
 
 def test_bf16_prefill_4k_h16_workload():
@@ -148,6 +178,36 @@ def test_bf16_strong_decay():
     assert_close(S, S_ref, TOL_BF16, "final state")
 
 
+@pytest.mark.parametrize("g_min", [-2.0, -8.0, -40.0, -400.0])
+def test_bf16_extreme_decay(g_min):
+    """Chunks whose blocks decay below e^-20 in some channels: bf16 off-diagonal operands and
+    float32 pair-by-pair diagonal blocks, for decays up to e^-400 per token."""
+    T, H, D = 1000, 2, 128
+    x = extreme_gates(random_inputs(165, T, H, D, "bf16"), 166, g_min)
+    s0 = random_states(167, 1, H, D)
+    note(f"bf16 extreme decay g_min={g_min}")
+    o, S = gpu_chunk(x, "bf16", chunk=64, s0=s0, scale=D ** -0.5)
+    o_ref, S_ref = run_oracle(x, "bf16", scale=D ** -0.5, initial_state=s0)
+    assert_close(o, o_ref, TOL_BF16, "o")
+    assert_close(S, S_ref, TOL_BF16, "final state")
+
+
+@pytest.mark.parametrize("g_c", [-0.6, -0.74, -1.2, -3.0])
+def test_bf16_constant_channel_decay(g_c):
+    """Half the channels decay by e^{g_c} on every token (16-token block decay e^{16 g_c}):
+    around e^-12 the balanced fp16 factors meet the pair-by-pair diagonal path."""
+    T, H, D = 640, 2, 128
+    x = random_inputs(175, T, H, D, "bf16")
+    ch = np.random.default_rng(176).random((H, D)) < 0.5
+    x["g"][:, ch] = np.float32(g_c)
+    s0 = random_states(177, 1, H, D)
+    note(f"bf16 constant channel decay g={g_c}")
+    o, S = gpu_chunk(x, "bf16", chunk=64, s0=s0, scale=D ** -0.5)
+    o_ref, S_ref = run_oracle(x, "bf16", scale=D ** -0.5, initial_state=s0)
+    assert_close(o, o_ref, TOL_BF16, "o")
+    assert_close(S, S_ref, TOL_BF16, "final state")
+
+
 def test_bf16_prefill_then_decode_equals_prefill():
     torch = torch_mod()
     P, steps, H, D = 200, 24, 2, 128
@@ -190,3 +250,63 @@ def test_zero_length_batch_keeps_state():
     torch.cuda.synchronize()
     assert o.shape == (3, 0, H, D)
     np.testing.assert_array_equal(S.cpu().numpy(), s0)
+
+
+# --------------------------------------------------------------- sequence split (few chains)
+
+def split_bytes(B, T, H, D, C, stored):
+    lib = kda.load_library()
+    return lib.kda_chunk_fwd_workspace_bytes(B, T, H, D, D, C, 1 if stored == "bf16" else 0, B)
+
+
+SPLIT_CASES = [
+    # (stored, D, C, B, T, H): each gives few chains and enough chunks for several segments
+    ("bf16", 128, 64, 1, 5000, 2),
+    ("bf16", 128, 64, 2, 8192 + 37, 3),
+    ("bf16", 128, 64, 1, 2048, 1),
+    ("f32", 16, 16, 1, 700, 1),
+    ("f32", 32, 64, 1, 3000, 2),
+    ("f32", 64, 64, 2, 4100, 2),
+]
+
+
+@pytest.mark.parametrize("stored,D,C,B,T,H", SPLIT_CASES)
+def test_split_matches_oracle_and_unsplit(stored, D, C, B, T, H):
+    """Long sequences on few chains run as parallel segments chained through their state
+    maps; outputs and final states match the oracle and the one-pass computation."""
+    assert split_bytes(B, T, H, D, C, stored) > 0, "case does not exercise the split"
+    x = random_inputs(300 + T + D, B * T, H, D, stored)
+    s0 = random_states(301 + T, B, H, D)
+    tol = TOL_BF16 if stored == "bf16" else TOL_F32
+    note(f"split {stored} D={D} C={C} B={B} T={T} H={H}")
+    o, S = gpu_chunk(x, stored, B=B, chunk=C, s0=s0, scale=D ** -0.5)
+    cu = np.arange(B + 1) * T
+    o_ref, S_ref = run_oracle(x, stored, scale=D ** -0.5, initial_state=s0, cu=cu)
+    assert_close(o, o_ref, tol, "o (split)")
+    assert_close(S, S_ref, tol, "final state (split)")
+    o1, S1 = gpu_chunk(x, stored, B=B, chunk=C, s0=s0, scale=D ** -0.5, split=False)
+    assert_close(o, o1, tol, "o split vs one pass")
+    assert_close(S, S1, tol, "state split vs one pass")
+
+
+def test_split_bf16_strong_decay_and_aliasing():
+    """Split with near-total forgetting (tiny state maps) and final_state == initial_state."""
+    B, T, H, D = 1, 4096 + 100, 2, 128
+    x = random_inputs(320, T, H, D, "bf16")
+    x["g"][: T // 3] = np.float32(-6.0)
+    s0 = random_states(321, B, H, D)
+    note("split bf16 strong decay + aliasing")
+    o, S = gpu_chunk(x, "bf16", chunk=64, s0=s0, alias=True)
+    o_ref, S_ref = run_oracle(x, "bf16", initial_state=s0)
+    assert_close(o, o_ref, TOL_BF16, "o (split, strong decay)")
+    assert_close(S, S_ref, TOL_BF16, "final state (split, strong decay, aliased)")
+
+
+def test_split_without_initial_state():
+    B, T, H, D = 1, 3 * 1024 + 64 * 16, 2, 128
+    x = random_inputs(330, T, H, D, "bf16")
+    note("split bf16 zero initial state")
+    o, S = gpu_chunk(x, "bf16", chunk=64)
+    o_ref, S_ref = run_oracle(x, "bf16")
+    assert_close(o, o_ref, TOL_BF16, "o (split, no s0)")
+    assert_close(S, S_ref, TOL_BF16, "final state (split, no s0)")

@@ -9,11 +9,19 @@ One step = one pass of the whole hot path over one batch of synthetic input:
      per sequence and head per step).
 
 Inputs are generated on the host (seeded, synth/) and are resident in HBM before the timed
-region. The headline value is prefill tokens/s (H=32, d=128); the decode step's state
-bandwidth is reported next to it. Per-kernel times come from HIP events recorded on the
-stream the kernels run on. The roofline fraction uses algorithmic bytes per launch.
+region, as is the prefill's optional split workspace. The headline value is prefill tokens/s
+(H=32, d=128); the decode step's state bandwidth is reported next to it. Times come from HIP
+events recorded on the stream the kernels run on (one kda_chunk_fwd call = the transition,
+combine and chunked-forward kernels). The roofline fraction uses algorithmic bytes per call.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py --counter-pass [--steps K]
+      only the prefill calls, then a plain copy-like kernel (out = -x over COPY_BYTES) as the
+      HBM-counter calibration; run it under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE
+  python bench.py --traffic-from FETCH_CSV WRITE_CSV
+      turn the two counter_collection.csv files of those runs into the per-call HBM traffic
+      (profiles/kda_chunk_fwd_prefill_128k_h32_traffic.json), tagged with the kernel source hash
 """
 
 from __future__ import annotations
@@ -34,6 +42,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_prefill_128k_h32_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_26_amd", "csrc", "kda_chunk.hip")
+PREFILL_KERNELS = ("chunk_fwd_kernel", "split_combine_kernel")  # one kda_chunk_fwd call
+COPY_BYTES = 1 << 30  # calibration: read 1 GiB, write 1 GiB
 
 
 def prefill_bytes_per_token_head(K: int, V: int) -> int:
@@ -73,6 +83,64 @@ def load_traffic(launch_bytes: float):
     return t.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(path: str):
+    import csv
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            yield row["Kernel_Name"], int(row["Dispatch_Id"]), row["Counter_Name"], float(row["Counter_Value"])
+
+
+def traffic_from(fetch_csv: str, write_csv: str) -> dict:
+    """Per-call HBM bytes of the prefill from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by known bytes / counted bytes of the copy-like calibration kernel
+    (it reads and writes COPY_BYTES)."""
+    out = {}
+    for key, path in (("fetch", fetch_csv), ("write", write_csv)):
+        per_kernel, copy, calls = {}, [], set()
+        for name, disp, cname, val in _counter_rows(path):
+            if cname not in ("FETCH_SIZE", "WRITE_SIZE"):
+                continue
+            if any(k in name for k in PREFILL_KERNELS):
+                short = name.split("(")[0].replace("void ", "").replace("kda::(anonymous namespace)::", "")
+                kib, n = per_kernel.get(short, (0.0, 0))
+                per_kernel[short] = (kib + val, n + 1)
+                if "chunk_fwd_kernel" in name and ("false>" in name or "Lb0E" in name):
+                    calls.add(disp)  # one forward dispatch per call
+            elif "neg_kernel" in name:
+                copy.append(val)
+        if not copy or not calls:
+            raise SystemExit(f"{path}: no prefill or calibration dispatches found")
+        copy_kib = sum(copy) / len(copy)
+        scale = (COPY_BYTES / 1024.0) / copy_kib
+        total_kib = sum(kib for kib, _ in per_kernel.values())
+        out[key] = {
+            "calls": len(calls),
+            "copy_counter_kib": copy_kib,
+            "scale": scale,
+            "bytes_per_call": total_kib / len(calls) * 1024.0 * scale,
+            "per_kernel_kib_per_dispatch": {k: kib / n for k, (kib, n) in per_kernel.items()},
+        }
+    return out
+
+
+def write_traffic(fetch_csv: str, write_csv: str) -> None:
+    t = traffic_from(fetch_csv, write_csv)
+    res = {
+        "kernel_source_sha": kernel_sha(),
+        "workload": "prefill_128k_h32 (one kda_chunk_fwd call)",
+        "hbm_bytes_per_launch": round(t["fetch"]["bytes_per_call"] + t["write"]["bytes_per_call"]),
+        "fetch_bytes_per_launch": round(t["fetch"]["bytes_per_call"]),
+        "write_bytes_per_launch": round(t["write"]["bytes_per_call"]),
+        "calibration": {"kernel": "torch.neg over 1 GiB float32 (reads 1 GiB, writes 1 GiB)",
+                        "fetch_scale": t["fetch"]["scale"], "write_scale": t["write"]["scale"]},
+        "counters": t,
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
 def cpu_baseline(x: dict, sample_tokens: int) -> dict:
     """The float64 oracle (unchanged) on the first ``sample_tokens`` tokens of the prefill
     workload, all heads, on the host's cores."""
@@ -80,7 +148,7 @@ def cpu_baseline(x: dict, sample_tokens: int) -> dict:
 
     import oracle
     import synth
-    threads = min(os.cpu_count() or 1, x["q"].shape[1])
+    threads = min(os.cpu_count() or 1, x["q"].shape[1], 16)
     sl = slice(0, sample_tokens)
     args = (synth.stored_to_f64(x["q"][sl], "bf16"), synth.stored_to_f64(x["k"][sl], "bf16"),
             synth.stored_to_f64(x["v"][sl], "bf16"), x["g"][sl].astype(np.float64),
@@ -101,7 +169,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--decode-seqs", type=int, default=256)
+    ap.add_argument("--counter-pass", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the KDA core needs no collectives: (sequence, head) chains are independent)",
@@ -131,6 +204,21 @@ def main():
     pg, pb = to_dev(xp["g"][None]), to_dev(xp["beta"][None])
     po = torch.empty((1, T, H, V), dtype=torch.float32, device=dev)
     pS = torch.empty((1, H, K, V), dtype=torch.float32, device=dev)
+    ws_bytes = kda.chunk_fwd_workspace_bytes(pq, pv, chunk=C)
+    pws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    if args.counter_pass:
+        # prefill calls only, then the copy-like calibration kernel
+        for _ in range(args.warmup + args.steps):
+            kda.kda_chunk_fwd(pq, pk, pv, pg, pb, final_state=pS, o=po, workspace=pws)
+        torch.cuda.synchronize()
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"counter pass: {args.warmup + args.steps} prefill calls "
+            f"(workspace {ws_bytes} B), 3 calibration copies of {COPY_BYTES} B")
+        return
 
     # ----------------------------------------------------------------- decode workload
     wd = synth.WORKLOADS["decode_256x32"]
@@ -157,7 +245,7 @@ def main():
     def step(i, ev=None):
         if ev:
             ev[0].record(stream)
-        kda.kda_chunk_fwd(pq, pk, pv, pg, pb, final_state=pS, o=po)
+        kda.kda_chunk_fwd(pq, pk, pv, pg, pb, final_state=pS, o=po, workspace=pws)
         if ev:
             ev[1].record(stream)
         kda.kda_decode_step(tq[i], tk[i], tv[i], tg[i], tb[i], state, o=to)

@@ -13,8 +13,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["KdaError", "kda_chunk_fwd", "kda_decode_step", "load_library", "KDA_F32",
-           "KDA_BF16"]
+__all__ = ["KdaError", "kda_chunk_fwd", "kda_decode_step", "chunk_fwd_workspace_bytes",
+           "load_library", "KDA_F32", "KDA_BF16"]
 
 KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
@@ -98,7 +98,7 @@ def _req(t, name, dtype=None):
 
 def kda_chunk_fwd(q, k, v, g, beta, *, initial_state=None, output_final_state: bool = True,
                   final_state=None, cu_seqlens=None, chunk: int = 64, scale: float = 1.0,
-                  o=None, stream=None, split: bool = True):
+                  o=None, stream=None, split: bool = True, workspace=None):
     """Chunked KDA prefill (C: kda_chunk_fwd).
 
     q, k: [B, T, H, Dk] (or [T, H, Dk] with ``cu_seqlens``), bf16 or float32, unit L2 norm
@@ -108,6 +108,8 @@ def kda_chunk_fwd(q, k, v, g, beta, *, initial_state=None, output_final_state: b
     (it may be ``initial_state`` itself) or is allocated when ``output_final_state``.
     ``split`` provides the optional workspace with which the library cuts long sequences
     into segments run in parallel (few chains); False computes each chain in one pass.
+    ``workspace`` (a device uint8 tensor of at least ``chunk_fwd_workspace_bytes(...)``
+    bytes) is used instead of allocating one per call.
     Returns (o float32 [.., H, Dv], final_state or None).
     """
     import torch
@@ -147,14 +149,30 @@ def kda_chunk_fwd(q, k, v, g, beta, *, initial_state=None, output_final_state: b
         o = torch.empty(v.shape, dtype=torch.float32, device=q.device)
     else:
         _req(o, "o", torch.float32)
-    ws = lib.kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, _dtype_code(q), N) if split else 0
-    workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    if not split:
+        workspace, ws = None, 0
+    elif workspace is not None:
+        _req(workspace, "workspace", torch.uint8)
+        ws = workspace.numel()
+    else:
+        ws = lib.kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, _dtype_code(q), N)
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
     st = lib.kda_chunk_fwd(B, T, H, Dk, Dv, chunk, _dtype_code(q), KDA_F32, float(scale),
                            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                            _ptr(initial_state), _ptr(final_state), _ptr(o),
                            _ptr(cu_seqlens), N, _ptr(workspace), ws, _stream(stream))
     _check(lib, st)
     return o, final_state
+
+
+def chunk_fwd_workspace_bytes(q, v, *, chunk: int = 64, num_seqs: int | None = None) -> int:
+    """Bytes of optional workspace kda_chunk_fwd can use for q [B, T, H, Dk] / v (C:
+    kda_chunk_fwd_workspace_bytes); 0 when no sequence split applies."""
+    lib = load_library()
+    B, T, H, Dk = q.shape if q.dim() == 4 else (1, *q.shape)
+    N = B if num_seqs is None else num_seqs
+    return int(lib.kda_chunk_fwd_workspace_bytes(B, T, H, Dk, v.shape[-1], chunk,
+                                                 _dtype_code(q), N))
 
 
 def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, o=None, stream=None):

@@ -951,7 +951,7 @@ SplitPlan plan_split(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, in
     if (chains <= 0 || cus <= 0 || T <= 0 || Dk != Dv) return sp;
     const int64_t nchunks = ((int64_t)T + chunk - 1) / chunk;
     auto rounds = [&](int64_t blocks) { return (double)((blocks + cus - 1) / cus); };
-    constexpr double kTransCost = 0.85;   // transition chunk vs full chunk (no M, no outputs)
+    constexpr double kTransCost = 0.73;   // transition chunk vs full chunk (measured, bf16 D=128)
     constexpr double kFixedCost = 4.0;    // extra launches and the combine, in chunk times
     double best = rounds(chains) * (double)nchunks;
     for (int64_t P = 2; P <= 16; ++P) {
@@ -961,7 +961,7 @@ SplitPlan plan_split(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, in
         if (nseg < 2) continue;
         const double cost = rounds(2 * chains * (nseg - 1)) * per * kTransCost +
                             rounds(chains * nseg) * per + kFixedCost + 0.25 * (nseg - 2);
-        if (cost < 0.9 * best) {
+        if (cost < (sp.nseg > 1 ? 0.98 : 0.9) * best) {  // a split must gain 10%; more segments 2%
             best = cost;
             sp.nseg = (int)nseg;
             sp.seg_len = (int)(per * chunk);

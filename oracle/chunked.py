@@ -1,6 +1,7 @@
 """Chunkwise form of the KDA recurrence in float64 numpy (test infrastructure only).
 
-The KimiLinear page (section 6) names the chunked parallel form with a WY representation
+The KV-cache page ("Starting from the KV-cache explosion: what KimiLinear's linear
+attention solves", section 6) names the chunked parallel form with a WY representation
 as what turns the recurrence into GPU-friendly matrix products, with chunk sizes of 64 to
 128 (section 3: chunk_size 64). This module writes that form out plainly, one chunk at a
 time, so that the algebra the GPU kernel implements is itself checked against the

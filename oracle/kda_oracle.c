@@ -5,20 +5,25 @@
  * only the test suite, the smoke check and the benchmark's CPU-baseline leg do. It shares
  * no code with the HIP kernels.
  *
- * What it computes (Kimi Delta Attention). Each (sequence, head) keeps a d_k x d_v state
- * S whose rows are key channels ("a fixed-size state matrix that does not grow with the
- * sequence": KimiLinear page, section 2). Per token t, with log-decay g_t <= 0 per key
- * channel, write strength beta_t, key k_t, value v_t and query q_t:
+ * Sources: the KV-cache page ("Starting from the KV-cache explosion: what KimiLinear's
+ * linear attention solves") and the revolution page ("Linear attention revolution: Kimi
+ * Linear ...").
  *
- *   1. a   = exp(g_t)                 channel-wise forget gate (per-channel, "fine-grained"
- *                                     gating: Kimi Linear page, the KDA section)
+ * What it computes (Kimi Delta Attention). Each (sequence, head) keeps a d_k x d_v state
+ * S whose rows are key channels; its size is fixed, whatever the sequence length (KV-cache
+ * page, section 2). Per token t, with log-decay g_t <= 0 per key channel, write strength
+ * beta_t, key k_t, value v_t and query q_t:
+ *
+ *   1. a   = exp(g_t)                 the forget gate, one value per channel (the per-channel
+ *                                     gating that distinguishes KDA from Gated DeltaNet:
+ *                                     revolution page, the KDA section)
  *   2. S  <- Diag(a) S                decay acts on the key channels (rows)
  *   3. p   = S^T k_t                  what the decayed state predicts for k_t
  *   4. S  <- S + beta_t k_t (v_t - p)^T
  *                                     delta-rule erase-and-write; steps 2-4 together are
  *                                     S_t = (I - beta k k^T) Diag(a) S_{t-1} + beta k v^T,
- *                                     the erase term (I - beta k k^T) of KimiLinear page,
- *                                     section 5
+ *                                     with the erase term (I - beta k k^T) of the KV-cache
+ *                                     page, section 5
  *   5. o_t = S^T (scale * q_t)        read-out with the updated state
  *
  * Plain float64 loops, no blocking or reordering beyond the definition; no compensated

@@ -3,7 +3,7 @@
 Each test checks the oracle against something the pages or the mathematics fix: a
 hand-derived closed form, exact rational arithmetic on the defining matrix equation,
 reductions to the textbook delta rule, exact-overwrite and pure-decay identities, the
-spectral behaviour the KimiLinear page (section 5) describes for unnormalised keys,
+spectral behaviour the KV-cache page (section 5) describes for unnormalised keys,
 linearity, split/resume and packed-vs-separate equalities. Together they catch a dropped
 term, a wrong sign, decay on the wrong axis, a read-out before the write, a transposed
 operand or a chunk/sequence boundary slip.
@@ -167,7 +167,7 @@ def test_orthonormal_keys_store_and_recall():
 
 
 def test_unnormalised_key_blows_up_state():
-    """The KimiLinear page (section 5) warns that with |k| != 1 the erase term
+    """The KV-cache page (section 5) warns that with |k| != 1 the erase term
     (I - beta k k^T) leaves the unit disc and the state explodes. Its eigenvalues are
     1 (d-1 times) and 1 - beta |k|^2, so with v = 0, alpha = 1 and one repeated key:
     S_T = S_0 + ((1 - beta |k|^2)^T - 1) khat khat^T S_0."""

@@ -101,7 +101,11 @@ def traffic_from(fetch_csv: str, write_csv: str) -> dict:
             if cname not in ("FETCH_SIZE", "WRITE_SIZE"):
                 continue
             if any(k in name for k in PREFILL_KERNELS):
-                short = name.split("(")[0].replace("void ", "").replace("kda::(anonymous namespace)::", "")
+                if "chunk_fwd_kernel" in name:
+                    fwd = "false>" in name or "Lb0E" in name
+                    short = "chunk_fwd_kernel (" + ("forward" if fwd else "transition") + ")"
+                else:
+                    short = "split_combine_kernel"
                 kib, n = per_kernel.get(short, (0.0, 0))
                 per_kernel[short] = (kib + val, n + 1)
                 if "chunk_fwd_kernel" in name and ("false>" in name or "Lb0E" in name):

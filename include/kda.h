@@ -119,7 +119,10 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk
  *                 are scratch, overwritten by the call
  *
  * Compiled instantiations (in_dtype, chunk, Dk = Dv):
- *   (KDA_BF16, 64, 128)   bf16 matrix-core path, float32 accumulation and state
+ *   (KDA_BF16, 64, 128)   bf16 inputs; fp16 matrix-core operands (decay factors balanced
+ *                         by powers of two into fp16's range), float32 accumulation and
+ *                         state; exact for any finite g <= 0 (chunks whose 16-token decay
+ *                         falls below e^-12 sum their diagonal blocks pair by pair)
  *   (KDA_F32, 16, 16), (KDA_F32, 64, 32), (KDA_F32, 64, 64)
  *                         float32 matrix-core path (reference-precision instantiations)
  * Other combinations return KDA_ERR_UNSUPPORTED.

@@ -61,7 +61,6 @@ template <typename OP, int TSZ, int C, int DK, int DV, int NW, bool TRANS> struc
     static constexpr int PAD = 16 / (int)sizeof(OP);        // 16-byte row padding
     static constexpr int LDK = DK + PAD;                    // [token][channel] operand rows
     static constexpr int LDC = C + PAD;                     // [channel][token] operand rows
-    static constexpr int LCF = C + 4;                       // float32 [token][token] rows
     static constexpr int KT = DK / 16;
     static constexpr int VT = DV / 16;
     // state column tiles: the value columns of S, or (transition pass) the Dk columns of X
@@ -78,16 +77,17 @@ template <typename OP, int TSZ, int C, int DK, int DV, int NW, bool TRANS> struc
     static constexpr int JPT = (NEJ + 32 * NW - 1) / (32 * NW);  // per 32-lane half-wave slot
     static constexpr int SZ = (int)sizeof(OP);
 
-    // LDS map (bytes). Region P first holds the A/M operands, then float32 A and T, M, W.
+    // LDS map (bytes). Region P first holds the A/M operands, then -A, the diagonal blocks
+    // of T and M ([token][token], columns in perm order) and W.
     static constexpr int oLk = 0;
     static constexpr int oLq = oLk + align16(C * LDK * SZ);
     static constexpr int oRk = oLq + align16(C * LDK * SZ);
     static constexpr int oRd = oRk + align16(C * LDK * SZ);
     static constexpr int oRfar = oRd + align16(C * LDK * SZ);
     static constexpr int P_OPS = oRfar + align16(NFAR * 16 * LDK * SZ);
-    static constexpr int oAf = 0;
-    static constexpr int oTf = oAf + align16(C * LCF * 4);
-    static constexpr int oMb = oTf + align16(C * LCF * 4);
+    static constexpr int oAn = 0;
+    static constexpr int oTd = oAn + align16(C * LDC * SZ);
+    static constexpr int oMb = oTd + align16(C * LDC * SZ);
     static constexpr int oWb = oMb + align16(C * LDC * SZ);
     static constexpr int P_REUSE = oWb + align16(C * LDK * SZ);
     static constexpr int P_END = P_OPS > P_REUSE ? P_OPS : P_REUSE;
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     using ST = Step<OP>;
     using RW = Raw2<Tin>;
     using R4 = Raw4<Tin>;
-    constexpr int NB = Sh::NB, LDK = Sh::LDK, LDC = Sh::LDC, LCF = Sh::LCF, KT = Sh::KT,
+    constexpr int NB = Sh::NB, LDK = Sh::LDK, LDC = Sh::LDC, KT = Sh::KT,
                   CPW = Sh::CPW, KS = ST::KS, TPS = ST::TPS;
     constexpr bool kBalance = std::is_same<OP, _Float16>::value;  // fp16 range balancing
 
@@ -243,8 +243,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     OP *const Rk = reinterpret_cast<OP *>(smem + Sh::oRk);
     OP *const Rd = reinterpret_cast<OP *>(smem + Sh::oRd);
     OP *const Rfar = reinterpret_cast<OP *>(smem + Sh::oRfar);
-    float *const Af = reinterpret_cast<float *>(smem + Sh::oAf);
-    float *const Tf = reinterpret_cast<float *>(smem + Sh::oTf);
+    OP *const An = reinterpret_cast<OP *>(smem + Sh::oAn);  // -A (strictly lower blocks)
+    OP *const Td = reinterpret_cast<OP *>(smem + Sh::oTd);  // diagonal blocks of T
     OP *const Mb = reinterpret_cast<OP *>(smem + Sh::oMb);
     OP *const Wb = reinterpret_cast<OP *>(smem + Sh::oWb);
     OP *const Xt = reinterpret_cast<OP *>(smem + Sh::oXt);
@@ -261,6 +261,10 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, q4 = lane >> 4;
+    f32x4 Id;  // 16x16 identity in accumulator layout (transposes by products)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Id[e] = (4 * q4 + e == lr) ? 1.f : 0.f;
+    typedef typename MM::frag frag4;
 
     // ---- blockIdx -> (chain = (sequence, head), segment)
     const int H = a.H;
@@ -453,11 +457,12 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         }
         const bool extreme = __syncthreads_or(ext_local);
 
-        // ---- extreme chunks: the diagonal 16x16 blocks of A and M pair by pair in float32,
+        // ---- extreme chunks: the diagonal 16x16 blocks of A and M pair by pair in float32
+        // (as transposed tiles: lane (lr, q) holds row lr, columns 4q..4q+3),
         // A_ij = beta_i sum_c k_i[c] k_j[c] e^{G_i[c]-G_j[c]}, M_ij likewise with scale q_i,
         // from the cumulative log-decay G summed in float64 (G_i - G_j keeps float32 accuracy
         // however large G grows; no factor leaves the float range for any decay)
-        f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dM = {0.f, 0.f, 0.f, 0.f};
+        f32x4 dAt = {0.f, 0.f, 0.f, 0.f}, dMt = {0.f, 0.f, 0.f, 0.f};
         if (extreme) {
 #pragma unroll
             for (int jj = 0; jj < Sh::JPT; ++jj) {
@@ -503,22 +508,22 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             f32x4 a4 = {0.f, 0.f, 0.f, 0.f}, m4 = {0.f, 0.f, 0.f, 0.f};
             if (sp < Sh::SPL) {
                 constexpr int CH = DK / Sh::SPL;
-                const int ti = 16 * I + 4 * q4, tj = 16 * I + lr;
+                const int ti = 16 * I + lr, tj = 16 * I + 4 * q4;  // row token i, column tokens j
 #pragma unroll 4
                 for (int c = sp * CH; c < (sp + 1) * CH; ++c) {
-                    const f64x2 gi01 = *reinterpret_cast<const f64x2 *>(xG + c * Sh::LDG + ti);
-                    const f64x2 gi23 = *reinterpret_cast<const f64x2 *>(xG + c * Sh::LDG + ti + 2);
-                    const double gj = xG[c * Sh::LDG + tj];
-                    const float gd[4] = {(float)(gi01.x - gj), (float)(gi01.y - gj),
-                                         (float)(gi23.x - gj), (float)(gi23.y - gj)};
-                    const f32x4 ki = Stage<Tin>::load4(xK + c * Sh::LDT + ti);
-                    const f32x4 qi = TRANS ? f32x4{0.f, 0.f, 0.f, 0.f} : Stage<Tin>::load4(xQ + c * Sh::LDT + ti);
-                    const float kj = Stage<Tin>::load1(xK + c * Sh::LDT + tj);
+                    const double gi = xG[c * Sh::LDG + ti];
+                    const f64x2 gj01 = *reinterpret_cast<const f64x2 *>(xG + c * Sh::LDG + tj);
+                    const f64x2 gj23 = *reinterpret_cast<const f64x2 *>(xG + c * Sh::LDG + tj + 2);
+                    const float gd[4] = {(float)(gi - gj01.x), (float)(gi - gj01.y),
+                                         (float)(gi - gj23.x), (float)(gi - gj23.y)};
+                    const float ki = Stage<Tin>::load1(xK + c * Sh::LDT + ti);
+                    const float qi = TRANS ? 0.f : Stage<Tin>::load1(xQ + c * Sh::LDT + ti);
+                    const f32x4 kj = Stage<Tin>::load4(xK + c * Sh::LDT + tj);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float ex = kj * exp_gate<OP>(fminf(gd[e], 0.f));
-                        a4[e] += ki[e] * ex;
-                        m4[e] += qi[e] * ex;
+                        const float ex = kj[e] * exp_gate<OP>(fminf(gd[e], 0.f));
+                        a4[e] += ki * ex;
+                        m4[e] += qi * ex;
                     }
                 }
                 if (sp > 0) {
@@ -541,11 +546,12 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                         m4[e] += src[(4 + e) * 64];
                     }
                 }
+                const float bi = sbeta[16 * I + lr];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int row = 4 * q4 + e;
-                    dA[e] = row > lr ? sbeta[16 * I + row] * a4[e] : 0.f;
-                    dM[e] = row >= lr ? a.scale * m4[e] : 0.f;
+                    const int col = 4 * q4 + e;
+                    dAt[e] = lr > col ? bi * a4[e] : 0.f;
+                    dMt[e] = lr >= col ? a.scale * m4[e] : 0.f;
                 }
             }
             __syncthreads();  // the staging area is overwritten by the operands below
@@ -557,13 +563,15 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         // are unchanged). Extreme chunks need no Rd and no balancing: every factor left is
         // <= 1, so fp16 underflow costs at most 2^-25 absolutely.
         {
-            const bool bal = kBalance && !extreme, wrd = !extreme;
+            const bool bal = kBalance && !extreme;
             auto bexp = [&](float d) { return bal ? (int)floorf(-0.5f * __log2f(d)) : 0; };
             auto st = [&](OP *p, float x, float y) { MM::store_pair(p, x, y); };
 #pragma unroll
             for (int jj = 0; jj < Sh::JPT; ++jj) {
                 if (!jok[jj]) continue;
-                const int b = jb[jj], c0 = jc[jj];
+                // with Dk >= 64 a wave's jobs share one block: keep b in a scalar register
+                const int b = DK >= 64 ? __builtin_amdgcn_readfirstlane(jb[jj]) : jb[jj];
+                const int c0 = jc[jj];
                 float k0[8], k1[8], q0[8], q1[8];
 #pragma unroll
                 for (int ii = 0; ii < 8; ++ii) kq(jj, ii, k0[ii], k1[ii], q0[ii], q1[ii]);
@@ -588,23 +596,27 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 const int n1 = b + 1 < NB ? bexp(Dd[(b + 1) * DK + c0 + 1]) : 0;
                 const float sb0 = ldexpf(1.f, e0), sb1 = ldexpf(1.f, e1);      // left scale
                 const float nx0 = ldexpf(1.f, -n0), nx1 = ldexpf(1.f, -n1);    // right, block b+1
-                const float rd0 = __frcp_rn(d0) * ldexpf(1.f, n0 - e0);         // Rd = Rk * rd
-                const float rd1 = __frcp_rn(d1) * ldexpf(1.f, n1 - e1);
+                // Rd = Rk * rd (unused, and possibly not finite, in extreme chunks)
+                const float rd0 = __builtin_amdgcn_rcpf(d0) * ldexpf(1.f, n0 - e0);
+                const float rd1 = __builtin_amdgcn_rcpf(d1) * ldexpf(1.f, n1 - e1);
                 const float pq0 = pre0 * ldexpf(1.f, -e0), pq1 = pre1 * ldexpf(1.f, -e1);
                 const float po0 = post0 * ldexpf(1.f, n0), po1 = post1 * ldexpf(1.f, n1);
                 const int cp = ST::perm(c0);  // c0 even: c0, c0+1 stay adjacent in perm order
                 OP xt0[8], xt1[8], kd0[8], kd1[8];
+                float btv[8];
+                *reinterpret_cast<f32x4 *>(btv) = *reinterpret_cast<const f32x4 *>(sbeta + 16 * b + 8 * hh);
+                *reinterpret_cast<f32x4 *>(btv + 4) = *reinterpret_cast<const f32x4 *>(sbeta + 16 * b + 8 * hh + 4);
 #pragma unroll
                 for (int ii = 0; ii < 8; ++ii) {
                     const int i = 16 * b + 8 * hh + ii;
-                    const float bt = sbeta[i];
+                    const float bt = btv[ii];
                     const float lk0 = bt * k0[ii] * al0[jj][ii] * sb0, lk1 = bt * k1[ii] * al1[jj][ii] * sb1;
                     const float lq0 = q0[ii] * al0[jj][ii] * sb0, lq1 = q1[ii] * al1[jj][ii] * sb1;
                     const float rk0 = k0[ii] * sf0[jj][ii] * nx0, rk1 = k1[ii] * sf1[jj][ii] * nx1;
                     st(Lk + i * LDK + c0, lk0, lk1);
                     if constexpr (!TRANS) st(Lq + i * LDK + c0, lq0, lq1);
                     st(Rk + i * LDK + c0, rk0, rk1);
-                    if (wrd) st(Rd + i * LDK + c0, rk0 * rd0, rk1 * rd1);
+                    st(Rd + i * LDK + c0, rk0 * rd0, rk1 * rd1);
                     if constexpr (!TRANS) MM::store_pair(Qg + i * LDK + cp, lq0 * pq0, lq1 * pq1);
                     xt0[ii] = static_cast<OP>(lk0 * pq0);
                     xt1[ii] = static_cast<OP>(lk1 * pq1);
@@ -648,8 +660,10 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         }
         __syncthreads();
 
-        // ---- P2: A and M 16x16 blocks; the diagonal blocks' waves also invert I + A_II
-        auto am = [&](bool isM, int I, int J) {
+        // ---- P2: A and M 16x16 blocks, as transposed tiles (lane (lr, q) holds row 16I+lr,
+        // columns 16J+4q..+3, which the write-out stores as one vector); the diagonal blocks'
+        // waves also invert I + A_II
+        auto am_t = [&](bool isM, int I, int J) {
             const OP *left = (isM ? Lq : Lk) + (16 * I + lr) * LDK;
             const OP *right = I == J       ? Rd + (16 * J + lr) * LDK
                               : I == J + 1 ? Rk + (16 * J + lr) * LDK
@@ -657,37 +671,35 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < DK; kk += KS)
-                ST::mma(acc, ST::contig(left, kk, q4), ST::contig(right, kk, q4));
+                ST::mma(acc, ST::contig(right, kk, q4), ST::contig(left, kk, q4));
             return acc;
         };
-        f32x4 tdiag = {0.f, 0.f, 0.f, 0.f}, mdiag = {0.f, 0.f, 0.f, 0.f};
+        f32x4 tdiag_t = {0.f, 0.f, 0.f, 0.f}, mdiag_t = {0.f, 0.f, 0.f, 0.f};
         const bool dj = wave < NB;
         if (dj) {
             const int I = wave;
-            f32x4 Lm = extreme ? dA : am(false, I, I);
+            f32x4 Lt = extreme ? dAt : am_t(false, I, I);  // L^T in accumulator layout
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (4 * q4 + e <= lr) Lm[e] = 0.f;  // strictly lower
+                if (lr <= 4 * q4 + e) Lt[e] = 0.f;  // L strictly lower
             // (I + L)^{-1} = (I - L)(I + L^2)(I + L^4)(I + L^8), L strictly lower 16x16
-            f32x4 Id;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Id[e] = (4 * q4 + e == lr) ? 1.f : 0.f;
-            const f32x4 Lt = mm_tn<OP>(Lm, Id);
+            const f32x4 Lm = mm_tn<OP>(Lt, Id);
             const f32x4 L2 = mm_tn<OP>(Lt, Lm), L2t = mm_tn<OP>(Lm, Lt);
             const f32x4 L4 = mm_tn<OP>(L2t, L2), L4t = mm_tn<OP>(L2, L2t);
             const f32x4 L8 = mm_tn<OP>(L4t, L4);
             const f32x4 P1 = Id - Lm, P1t = Id - Lt;
             const f32x4 P2 = P1 + mm_tn<OP>(P1t, L2), P2t = P1t + mm_tn<OP>(L2, P1t);
             const f32x4 P3 = P2 + mm_tn<OP>(P2t, L4), P3t = P2t + mm_tn<OP>(L4, P2t);
-            tdiag = P3 + mm_tn<OP>(P3t, L8);
+            (void)P3;
+            tdiag_t = P3t + mm_tn<OP>(L8, P3t);  // T^T = P3^T + L8^T P3^T
             if (TRANS) {
             } else if (extreme) {
-                mdiag = dM;
+                mdiag_t = dMt;
             } else {
-                mdiag = am(true, I, I);
+                mdiag_t = am_t(true, I, I);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (4 * q4 + e < lr) mdiag[e] = 0.f;
+                    if (lr < 4 * q4 + e) mdiag_t[e] = 0.f;  // M lower, diagonal included
             }
         }
         f32x4 offv[Sh::OPW];
@@ -700,19 +712,16 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 if (ow >= 0 && x < Sh::NOFF) {
                     int I, J;
                     lower_block(x % Sh::NOFFA, I, J);
-                    offv[j] = am(x >= Sh::NOFFA, I, J);
+                    offv[j] = am_t(x >= Sh::NOFFA, I, J);
                 }
             }
         }
         __syncthreads();  // A/M operands are dead from here on
         if (dj) {
-            const int I = wave;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * I + 4 * q4 + e, col = 16 * I + lr;
-                Tf[row * LCF + col] = tdiag[e];
-                if constexpr (!TRANS) Mb[row * LDC + ST::perm(col)] = static_cast<OP>(mdiag[e]);
-            }
+            const int I = wave, off = (16 * I + lr) * LDC + ST::perm(16 * I + 4 * q4);
+            *reinterpret_cast<frag4 *>(Td + off) = MM::from_f32(tdiag_t);
+            *reinterpret_cast<frag4 *>(An + off) = MM::from_f32(f32x4{0.f, 0.f, 0.f, 0.f});
+            if constexpr (!TRANS) *reinterpret_cast<frag4 *>(Mb + off) = MM::from_f32(mdiag_t);
         }
 #pragma unroll
         for (int j = 0; j < Sh::OPW; ++j) {
@@ -720,44 +729,48 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             if (Sh::NOFF > 0 && ow >= 0 && x < Sh::NOFF) {
                 int I, J;
                 lower_block(x % (Sh::NOFFA > 0 ? Sh::NOFFA : 1), I, J);
-                const bool isM = x >= Sh::NOFFA;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 16 * I + 4 * q4 + e, col = 16 * J + lr;
-                    if (isM) Mb[row * LDC + ST::perm(col)] = static_cast<OP>(offv[j][e]);
-                    else Af[row * LCF + col] = offv[j][e];
-                }
+                const int off = (16 * I + lr) * LDC + ST::perm(16 * J + 4 * q4);
+                if (x >= Sh::NOFFA) *reinterpret_cast<frag4 *>(Mb + off) = MM::from_f32(offv[j]);
+                else *reinterpret_cast<frag4 *>(An + off) = MM::from_f32(-offv[j]);
             }
         }
-        // zero the upper blocks of M (read by the paired-tile steps of M U)
-        for (int idx = tid; idx < (TRANS ? 0 : C * C); idx += Sh::NT) {
-            const int row = idx / C, col = idx % C;
-            if (col / 16 > row / 16) Mb[row * LDC + ST::perm(col)] = static_cast<OP>(0.f);
+        // zero the upper blocks (I, I+1), I even, of M: the paired-tile steps of M U read them
+        if constexpr (!TRANS && TPS == 2) {
+            constexpr int NZB = NB / 2;  // even I with I + 1 < NB
+            for (int idx = tid; idx < NZB * 64; idx += Sh::NT) {
+                const int z = idx / 64, r = (idx / 4) % 16, gq = idx % 4;
+                const int I = 2 * z;
+                *reinterpret_cast<typename MM::frag *>(Mb + (16 * I + r) * LDC + ST::perm(16 * (I + 1) + 4 * gq)) =
+                    MM::from_f32(f32x4{0.f, 0.f, 0.f, 0.f});
+            }
         }
         __syncthreads();
 
-        // ---- P4: block forward substitution for W (fp16 result, to LDS) and U~ (registers)
+        // ---- P4: block forward substitution for W (fp16 result, to LDS) and U~ (registers):
+        // X_I <- T_II (X_I - sum_{J<I} A_IJ X_J), the sum in paired-tile steps over -A
+        auto subst_row = [&](f32x4 *Xs, int I, f32x4 r) {
+#pragma unroll
+            for (int p = 0; p < (I + TPS - 1) / TPS; ++p)
+                ST::mma(r, ST::permuted(An + (16 * I + lr) * LDC, p * KS, q4), ST::regs(&Xs[p * TPS]));
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            MM::mma(x, *reinterpret_cast<const frag4 *>(Td + (16 * I + lr) * LDC + ST::perm(16 * I + 4 * q4)),
+                    MM::from_f32(r));
+            return x;
+        };
 #pragma unroll
         for (int j = 0; j < Sh::WPW; ++j) {
             const int cK = wave + NW * j;
             if (cK < KT) {
                 f32x4 Wt[NB];
 #pragma unroll
+                for (int I = 0; I < NB; ++I) Wt[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
                 for (int I = 0; I < NB; ++I) {
-                    f32x4 R = MM::to_f32(MM::load(Xt + (16 * cK + lr) * LDC + 16 * I + 4 * q4));
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int J = 0; J < I; ++J)
-                        MM::mma(acc, MM::from_f32(*reinterpret_cast<const f32x4 *>(Af + (16 * I + lr) * LCF + 16 * J + 4 * q4)),
-                                MM::from_f32(Wt[J]));
-                    R -= acc;
-                    f32x4 w = {0.f, 0.f, 0.f, 0.f};
-                    MM::mma(w, MM::from_f32(*reinterpret_cast<const f32x4 *>(Tf + (16 * I + lr) * LCF + 16 * I + 4 * q4)),
-                            MM::from_f32(R));
+                    const f32x4 w = subst_row(Wt, I, MM::to_f32(MM::load(Xt + (16 * cK + lr) * LDC + 16 * I + 4 * q4)));
                     Wt[I] = w;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        Wb[(16 * I + 4 * q4 + e) * LDK + ST::perm(16 * cK + lr)] = static_cast<OP>(w[e]);
+                    // row-major store of the tile through its transpose: 4 channels per lane
+                    *reinterpret_cast<frag4 *>(Wb + (16 * I + lr) * LDK + ST::perm(16 * cK + 4 * q4)) =
+                        MM::from_f32(mm_tn<OP>(w, Id));
                 }
             }
         }
@@ -771,20 +784,11 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 continue;
             }
 #pragma unroll
-            for (int I = 0; I < NB; ++I) {
-                f32x4 R = MM::to_f32(MM::load(Yt + (16 * cv + lr) * LDC + 16 * I + 4 * q4)) *
-                          *reinterpret_cast<const f32x4 *>(sbeta + 16 * I + 4 * q4);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int I = 0; I < NB; ++I) Ur[j][I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int J = 0; J < I; ++J)
-                    MM::mma(acc, MM::from_f32(*reinterpret_cast<const f32x4 *>(Af + (16 * I + lr) * LCF + 16 * J + 4 * q4)),
-                            MM::from_f32(Ur[j][J]));
-                R -= acc;
-                f32x4 u = {0.f, 0.f, 0.f, 0.f};
-                MM::mma(u, MM::from_f32(*reinterpret_cast<const f32x4 *>(Tf + (16 * I + lr) * LCF + 16 * I + 4 * q4)),
-                        MM::from_f32(R));
-                Ur[j][I] = u;
-            }
+            for (int I = 0; I < NB; ++I)
+                Ur[j][I] = subst_row(Ur[j], I, MM::to_f32(MM::load(Yt + (16 * cv + lr) * LDC + 16 * I + 4 * q4)) *
+                                                   *reinterpret_cast<const f32x4 *>(sbeta + 16 * I + 4 * q4));
         }
         __syncthreads();
 

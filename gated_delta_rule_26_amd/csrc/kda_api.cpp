@@ -61,7 +61,7 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk
     if (B < 1 || T < 0 || H < 1 || !valid_dtype(in_dtype) ||
         !kda::chunk_fwd_supported(in_dtype, chunk, Dk, Dv))
         return 0;
-    return kda::chunk_fwd_split_bytes(B, T, H, Dk, Dv, chunk, num_seqs);
+    return kda::chunk_fwd_split_bytes(B, T, H, Dk, Dv, chunk, in_dtype, num_seqs);
 }
 
 kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
@@ -117,6 +117,8 @@ kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv
     a.seg_len = 0;
     a.nseg = 1;
     a.ws_r = a.ws_x = a.ws_s = nullptr;
+    a.rec = nullptr;
+    a.rec_chunks = 0;
     return hip_status(kda::launch_chunk_fwd(in_dtype, chunk, Dk, Dv, a, workspace, workspace_bytes,
                                             static_cast<hipStream_t>(stream)),
                       "kda_chunk_fwd launch");

@@ -54,7 +54,7 @@ template <typename OP> constexpr float extreme_block_decay() {
                                           : 6.1442124e-6f;   // e^-12
 }
 
-template <typename OP, int TSZ, int C, int DK, int DV, int NW, bool TRANS> struct ChunkShape {
+template <typename OP, int TSZ, int C, int DK, int DV, int NW> struct ChunkShape {
     static constexpr int NT = 64 * NW;
     static constexpr int NB = C / 16;                       // 16-token blocks per chunk
     static constexpr int NFAR = (NB - 1) * (NB - 2) / 2;    // block pairs (J, I), I >= J + 2
@@ -68,7 +68,7 @@ template <typename OP, int TSZ, int C, int DK, int DV, int NW, bool TRANS> struc
     static constexpr int CPW = NCT >= NW ? NCT / NW : 1;    // state column tiles per wave
     static constexpr int WPW = KT >= NW ? KT / NW : 1;      // W column tiles per wave
     static constexpr int NOFFA = NB * (NB - 1) / 2;         // off-diagonal blocks of A
-    static constexpr int NOFF = TRANS ? NOFFA : 2 * NOFFA;  // ... and of M (no M: no outputs)
+    static constexpr int NOFF = 2 * NOFFA;                  // ... and of M
     static constexpr int OFFW = NW > NB ? NW - NB : NW;     // waves doing off-diagonal jobs
     static constexpr int OPW = NOFF > 0 ? (NOFF + OFFW - 1) / OFFW : 1;
     static constexpr int NVJ = (C / 4) * (DV / 4);          // 4x4 value-tile jobs per chunk
@@ -121,7 +121,22 @@ template <typename OP, int TSZ, int C, int DK, int DV, int NW, bool TRANS> struc
     static_assert(BYTES <= 160 * 1024, "LDS budget of one CU exceeded");
     static_assert(X_END <= oYt, "extreme-chunk staging must fit before the V^T array");
     static_assert(DK % (4 * SPL) == 0, "channel split");
-    static_assert(!TRANS || DK == DV, "the transition pass keeps X in the state's tiles");
+};
+
+// Per-chunk record of a split segment (global memory, written by the chunked forward and read
+// by the replay passes). Dense copies of the LDS operands in the same element order:
+// W [C][Dk] and Qg [C][Dk] (columns in step order), Kd^T [Dk][C], M [C][C] (columns in step
+// order), then gC [Dk] float32 and U~ float32 in accumulator order [Dv/16][C/16][64 lanes][4].
+template <typename OP, int C, int DK, int DV> struct Record {
+    static constexpr int SZ = (int)sizeof(OP);
+    static constexpr int oW = 0;
+    static constexpr int oQ = oW + C * DK * SZ;
+    static constexpr int oK = oQ + C * DK * SZ;
+    static constexpr int oM = oK + DK * C * SZ;
+    static constexpr int OPS = oM + C * C * SZ;  // the LDS-staged part
+    static constexpr int oG = OPS;
+    static constexpr int oU = oG + DK * 4;
+    static constexpr int BYTES = (oU + C * DV * 4 + 255) & ~255;
 };
 
 // Index of the off-diagonal block pair (J, I), I >= J + 2, in the far-operand table.
@@ -219,16 +234,14 @@ template <typename OP> __device__ __forceinline__ f32x4 mm_tn(f32x4 x, f32x4 y) 
     return acc;
 }
 
-// TRANS = false: the chunked forward (outputs and final states). With a sequence split,
-//   block (chain, segment p) starts from ws_s[p] and writes the final state for the last p.
-// TRANS = true: the split's first pass, no outputs. Two blocks per (chain, p), p < nseg-1,
-//   run segment p: role R carries S from the initial state (p = 0) or zero and writes it to
-//   ws_r[p] (the segment's map applied to its start state); role X carries X = I with no
-//   values (U~ = 0) and writes ws_x[p] (the segment's linear part), so that
-//   S_{p+1} = X_p S_p + R_p.
-template <typename Tin, typename OP, int C, int DK, int DV, int NW, bool TRANS>
+// The chunked forward, one workgroup per chain (STORE = false), or, for a sequence split,
+// one per (chain, segment) (STORE = true): segment 0 starts from the initial state and every
+// later segment from zero; no outputs are written; each chunk's record (W, the read-out and
+// state-update operands, U~) is stored for the replay passes, and the segment's final state
+// R_p goes to ws_r[p] (p < nseg-1).
+template <typename Tin, typename OP, int C, int DK, int DV, int NW, bool STORE>
 __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
-    using Sh = ChunkShape<OP, (int)sizeof(Tin), C, DK, DV, NW, TRANS>;
+    using Sh = ChunkShape<OP, (int)sizeof(Tin), C, DK, DV, NW>;
     using MM = Mma<OP>;
     using ST = Step<OP>;
     using RW = Raw2<Tin>;
@@ -269,11 +282,10 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     // ---- blockIdx -> (chain = (sequence, head), segment)
     const int H = a.H;
     const int chains = a.n_seqs * H;
-    const int segs = a.seg_len ? (TRANS ? a.nseg - 1 : a.nseg) : 1;
-    const int bid = TRANS ? (int)blockIdx.x >> 1 : (int)blockIdx.x;
-    const bool isx = TRANS && (blockIdx.x & 1);  // transition block: state = X, no values
-    if (bid >= chains * segs) return;
-    const int chain = bid / segs, seg = bid % segs;
+    const int segs = STORE ? a.nseg : 1;
+    if ((int)blockIdx.x >= chains * segs) return;
+    const int chain = blockIdx.x / segs, seg = blockIdx.x % segs;
+    constexpr bool store = STORE;
     const int n = chain / H, h = chain % H;
     int64_t tok0, L;
     if (a.cu_seqlens) {
@@ -309,8 +321,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     // accumulator layout
     const bool owns = wave < Sh::NCT;
     const float *sinit = a.s0 ? a.s0 + sbase : nullptr;
-    if (a.seg_len && !TRANS) sinit = a.ws_s + ((int64_t)seg * chains + chain) * DK * DV;
-    if (TRANS && seg > 0) sinit = nullptr;
+    if (STORE && seg > 0) sinit = nullptr;
     f32x4 S[CPW][KT];
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
@@ -318,15 +329,10 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
         for (int r = 0; r < KT; ++r) {
             S[j][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (owns && !isx && sinit) {
+            if (owns && sinit) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     S[j][r][e] = sinit[(int64_t)(16 * r + 4 * q4 + e) * DV + 16 * ct + lr];
-            }
-            if (owns && isx) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    S[j][r][e] = (16 * r + 4 * q4 + e == 16 * ct + lr) ? 1.f : 0.f;
             }
         }
     }
@@ -363,19 +369,17 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         const rsrc_t rg = make_rsrc(a.g + t0 * krow, (uint32_t)(Lc * krow * 4));
         const rsrc_t rv = make_rsrc(vg + t0 * vrow, (uint32_t)(Lc * vrow * ESZ));
         const rsrc_t rb = make_rsrc(a.beta + t0 * H, (uint32_t)(Lc * H * 4));
-        if (!isx) {
 #pragma unroll
-            for (int vv = 0; vv < Sh::VPT; ++vv)
+        for (int vv = 0; vv < Sh::VPT; ++vv)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) pv[vv][r] = R4::load(rv, vo[vv] * ESZ, r * vrow * ESZ);
-        }
+            for (int r = 0; r < 4; ++r) pv[vv][r] = R4::load(rv, vo[vv] * ESZ, r * vrow * ESZ);
 #pragma unroll
         for (int jj = 0; jj < Sh::JPT; ++jj) {
 #pragma unroll
             for (int ii = 0; ii < 8; ++ii) {
                 pg[jj][ii] = Raw2<float>::load(rg, ko[jj] * 4, ii * krow * 4);
                 pk[jj][ii] = RW::load(rk, ko[jj] * ESZ, ii * krow * ESZ);
-                if constexpr (!TRANS) pq[jj][ii] = RW::load(rq, ko[jj] * ESZ, ii * krow * ESZ);
+                pq[jj][ii] = RW::load(rq, ko[jj] * ESZ, ii * krow * ESZ);
             }
         }
         pbeta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -383,12 +387,39 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     };
 
     const int64_t nchunks = (L + C - 1) / C;
+    // record the LDS operands (W, Qg, Kd^T, M, gC) of chunk cr of a split segment
+    // (each thread copies 16-byte pieces tid, tid + NT, ...: one base offset per row width)
+    auto record_ops = [&](int64_t cr) {
+        using Rc = Record<OP, C, DK, DV>;
+        uint8_t *const rp = a.rec + (((int64_t)seg * chains + chain) * a.rec_chunks + cr) * Rc::BYTES;
+        constexpr int NT = Sh::NT;
+        auto copy_rows = [&](const OP *src, int ld, auto rows_c, auto per_c, uint8_t *dst) {
+            constexpr int rows = decltype(rows_c)::value, per = decltype(per_c)::value;  // per: pieces per row
+            const int r0 = tid / per, c0 = tid % per;
+            const uint8_t *s0 = reinterpret_cast<const uint8_t *>(src + r0 * ld) + c0 * 16;
+#pragma unroll
+            for (int m = 0; m < (rows * per + NT - 1) / NT; ++m) {
+                if ((rows * per) % NT == 0 || tid + m * NT < rows * per)
+                    *reinterpret_cast<u32x4 *>(dst + (tid + m * NT) * 16) =
+                        *reinterpret_cast<const u32x4 *>(s0 + (m * NT / per) * ld * (int)sizeof(OP));
+            }
+        };
+        using IC = std::integral_constant<int, 0>;
+        (void)IC{};
+        copy_rows(Wb, LDK, std::integral_constant<int, C>{}, std::integral_constant<int, DK * Rc::SZ / 16>{}, rp + Rc::oW);
+        copy_rows(Qg, LDK, std::integral_constant<int, C>{}, std::integral_constant<int, DK * Rc::SZ / 16>{}, rp + Rc::oQ);
+        copy_rows(KdT, LDC, std::integral_constant<int, DK>{}, std::integral_constant<int, C * Rc::SZ / 16>{}, rp + Rc::oK);
+        copy_rows(Mb, LDC, std::integral_constant<int, C>{}, std::integral_constant<int, C * Rc::SZ / 16>{}, rp + Rc::oM);
+        if (tid < DK / 4)
+            *reinterpret_cast<f32x4 *>(rp + Rc::oG + 16 * tid) = *reinterpret_cast<const f32x4 *>(gC + 4 * tid);
+    };
     if (nchunks > 0) prefetch(tok0, (int)(L < C ? L : C));
 
     for (int64_t ci = 0; ci < nchunks; ++ci) {
         const int64_t t0 = tok0 + ci * C;
         const int Lc = (int)((L - ci * C) < C ? (L - ci * C) : C);
         __syncthreads();  // the previous chunk's readers of LDS are done
+        if (store && ci > 0) record_ops(ci - 1);
 
         // ---- P0: gates -> within-block decay products (prefix incl., suffix excl.)
         float al0[Sh::JPT][8], al1[Sh::JPT][8], sf0[Sh::JPT][8], sf1[Sh::JPT][8];
@@ -396,7 +427,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         // k and q of token ii of job jj (zero past the sequence end), from the prefetch registers
         auto kq = [&](int jj, int ii, float &k0, float &k1, float &q0, float &q1) {
             const f32x2 kk = RW::f32(pk[jj][ii]);
-            const f32x2 qq = TRANS ? f32x2{0.f, 0.f} : RW::f32(pq[jj][ii]);
+            const f32x2 qq = RW::f32(pq[jj][ii]);
             k0 = kk.x;
             k1 = kk.y;
             q0 = qq.x * a.scale;
@@ -444,7 +475,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
         for (int vv = 0; vv < Sh::VPT; ++vv) {  // v^T: 4 columns x 4 consecutive tokens per store
             int tg, cg;
-            if (!isx && vjob(vv, tg, cg)) {
+            if (vjob(vv, tg, cg)) {
                 f32x4 vr[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) vr[r] = R4::f32(pv[vv][r]);
@@ -476,7 +507,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                     G0[ii] = c0s;
                     G1[ii] = c1s;
                     const f32x2 kk = RW::f32(pk[jj][ii]);
-                    const f32x2 qq = TRANS ? f32x2{0.f, 0.f} : RW::f32(pq[jj][ii]);
+                    const f32x2 qq = RW::f32(pq[jj][ii]);
                     kk0[ii] = kk.x;
                     kk1[ii] = kk.y;
                     qq0[ii] = qq.x;
@@ -497,10 +528,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                     }
                     Stage<Tin>::store8(xK + c0 * Sh::LDT + tc, kk0);
                     Stage<Tin>::store8(xK + (c0 + 1) * Sh::LDT + tc, kk1);
-                    if constexpr (!TRANS) {
-                        Stage<Tin>::store8(xQ + c0 * Sh::LDT + tc, qq0);
-                        Stage<Tin>::store8(xQ + (c0 + 1) * Sh::LDT + tc, qq1);
-                    }
+                    Stage<Tin>::store8(xQ + c0 * Sh::LDT + tc, qq0);
+                    Stage<Tin>::store8(xQ + (c0 + 1) * Sh::LDT + tc, qq1);
                 }
             }
             __syncthreads();
@@ -517,7 +546,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                     const float gd[4] = {(float)(gi - gj01.x), (float)(gi - gj01.y),
                                          (float)(gi - gj23.x), (float)(gi - gj23.y)};
                     const float ki = Stage<Tin>::load1(xK + c * Sh::LDT + ti);
-                    const float qi = TRANS ? 0.f : Stage<Tin>::load1(xQ + c * Sh::LDT + ti);
+                    const float qi = Stage<Tin>::load1(xQ + c * Sh::LDT + ti);
                     const f32x4 kj = Stage<Tin>::load4(xK + c * Sh::LDT + tj);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -614,10 +643,10 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                     const float lq0 = q0[ii] * al0[jj][ii] * sb0, lq1 = q1[ii] * al1[jj][ii] * sb1;
                     const float rk0 = k0[ii] * sf0[jj][ii] * nx0, rk1 = k1[ii] * sf1[jj][ii] * nx1;
                     st(Lk + i * LDK + c0, lk0, lk1);
-                    if constexpr (!TRANS) st(Lq + i * LDK + c0, lq0, lq1);
+                    st(Lq + i * LDK + c0, lq0, lq1);
                     st(Rk + i * LDK + c0, rk0, rk1);
                     st(Rd + i * LDK + c0, rk0 * rd0, rk1 * rd1);
-                    if constexpr (!TRANS) MM::store_pair(Qg + i * LDK + cp, lq0 * pq0, lq1 * pq1);
+                    MM::store_pair(Qg + i * LDK + cp, lq0 * pq0, lq1 * pq1);
                     xt0[ii] = static_cast<OP>(lk0 * pq0);
                     xt1[ii] = static_cast<OP>(lk1 * pq1);
                     kd0[ii] = static_cast<OP>(rk0 * po0);
@@ -692,8 +721,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             const f32x4 P3 = P2 + mm_tn<OP>(P2t, L4), P3t = P2t + mm_tn<OP>(L4, P2t);
             (void)P3;
             tdiag_t = P3t + mm_tn<OP>(L8, P3t);  // T^T = P3^T + L8^T P3^T
-            if (TRANS) {
-            } else if (extreme) {
+            if (extreme) {
                 mdiag_t = dMt;
             } else {
                 mdiag_t = am_t(true, I, I);
@@ -721,7 +749,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             const int I = wave, off = (16 * I + lr) * LDC + ST::perm(16 * I + 4 * q4);
             *reinterpret_cast<frag4 *>(Td + off) = MM::from_f32(tdiag_t);
             *reinterpret_cast<frag4 *>(An + off) = MM::from_f32(f32x4{0.f, 0.f, 0.f, 0.f});
-            if constexpr (!TRANS) *reinterpret_cast<frag4 *>(Mb + off) = MM::from_f32(mdiag_t);
+            *reinterpret_cast<frag4 *>(Mb + off) = MM::from_f32(mdiag_t);
         }
 #pragma unroll
         for (int j = 0; j < Sh::OPW; ++j) {
@@ -735,7 +763,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             }
         }
         // zero the upper blocks (I, I+1), I even, of M: the paired-tile steps of M U read them
-        if constexpr (!TRANS && TPS == 2) {
+        if constexpr (TPS == 2) {
             constexpr int NZB = NB / 2;  // even I with I + 1 < NB
             for (int idx = tid; idx < NZB * 64; idx += Sh::NT) {
                 const int z = idx / 64, r = (idx / 4) % 16, gq = idx % 4;
@@ -778,11 +806,6 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
             const int cv = wave + NW * j;
-            if (isx) {  // transition block: X has no value columns, U~ = 0
-#pragma unroll
-                for (int I = 0; I < NB; ++I) Ur[j][I] = f32x4{0.f, 0.f, 0.f, 0.f};
-                continue;
-            }
 #pragma unroll
             for (int I = 0; I < NB; ++I) Ur[j][I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -791,6 +814,18 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                                                    *reinterpret_cast<const f32x4 *>(sbeta + 16 * I + 4 * q4));
         }
         __syncthreads();
+
+        // ---- split segments after the first: record U~ of this chunk (the LDS operands are
+        // recorded at the top of the next iteration, where fewer registers are live)
+        if (store && owns) {
+            using Rc = Record<OP, C, DK, DV>;
+            uint8_t *const rp = a.rec + (((int64_t)seg * chains + chain) * a.rec_chunks + ci) * Rc::BYTES;
+#pragma unroll
+            for (int j = 0; j < CPW; ++j)
+#pragma unroll
+                for (int I = 0; I < NB; ++I)
+                    *reinterpret_cast<f32x4 *>(rp + Rc::oU + (((wave + NW * j) * NB + I) * 64 + lane) * 16) = Ur[j][I];
+        }
 
         // ---- P5: state pass, registers only: U = U~ - W S; O = Qg S + M U; S' = gC S + Kd^T U
         if (owns) {
@@ -816,7 +851,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 for (int p = 0; p < C / KS; ++p) ufr[p] = ST::regs(&U[p * TPS]);
 #pragma unroll
                 for (int I = 0; I < NB; ++I) {
-                    if (TRANS) break;  // the transition pass produces no outputs
+                    if (STORE) break;  // split: the outputs come from the replay
                     f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int p = 0; p < DK / KS; ++p)
@@ -843,10 +878,15 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         }
     }
 
+    if (store && nchunks > 0) {
+        __syncthreads();
+        record_ops(nchunks - 1);
+    }
+
     float *dst = nullptr;
-    if (TRANS)
-        dst = (isx ? a.ws_x : a.ws_r) + ((int64_t)seg * chains + chain) * DK * DV;
-    else if (a.s_out && seg == segs - 1)
+    if (STORE)  // split: segment p's final state (from the initial state for p = 0, else zero)
+        dst = seg < segs - 1 ? a.ws_r + ((int64_t)seg * chains + chain) * DK * DV : nullptr;
+    else if (a.s_out)
         dst = a.s_out + sbase;
     if (owns && dst) {
 #pragma unroll
@@ -864,8 +904,203 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
 }
 
 
-// Split combine: S_0 = the initial state (or zero), S_1 = R_0, S_{p+1} = X_p S_p + R_p.
-// One workgroup per (chain, 16-column block); float32 FMA with the running block in LDS.
+// Replay of split segments from their records (no inputs are read again).
+// XMODE: segment p's linear part X_p (state X = I, U~ = 0, no outputs) -> ws_x[p], for
+//        p = 1 .. nseg-2.
+// else:  segment p from its true start state S_p = ws_s[p]: outputs, and the final state of
+//        the last segment, for p = 0 .. nseg-1.
+// The state pass is the forward kernel's: U = U~ - W S; O = Qg S + M U; S' = gC S + Kd^T U.
+// Each chunk's staged operands are loaded into registers one chunk ahead.
+template <typename OP, int C, int DK, int DV, int NW, bool XMODE>
+__global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
+    using Sh = ChunkShape<OP, 2, C, DK, DV, NW>;
+    using Rc = Record<OP, C, DK, DV>;
+    using MM = Mma<OP>;
+    using ST = Step<OP>;
+    constexpr int NB = Sh::NB, LDK = Sh::LDK, LDC = Sh::LDC, KT = Sh::KT, CPW = Sh::CPW,
+                  KS = ST::KS, TPS = ST::TPS, NT = 64 * NW, SZ = Rc::SZ;
+    static_assert(DK == DV || !XMODE, "X lives in the state's column tiles");
+    constexpr int WROW = DK * SZ, KROW = C * SZ, MROW = C * SZ;  // record row bytes
+    // 16-byte pieces to stage: W, Qg, Kd^T, M (XMODE: W and Kd^T)
+    constexpr int N16 = (XMODE ? Rc::oQ + (Rc::oM - Rc::oK) : Rc::OPS) / 16;
+    constexpr int PPT = (N16 + NT - 1) / NT;                      // pieces per thread
+
+    __shared__ __attribute__((aligned(16))) OP Wl[C * LDK];
+    __shared__ __attribute__((aligned(16))) OP Ql[XMODE ? 8 : C * LDK];
+    __shared__ __attribute__((aligned(16))) OP Kl[DK * LDC];
+    __shared__ __attribute__((aligned(16))) OP Ml[XMODE ? 8 : C * LDC];
+    __shared__ __attribute__((aligned(16))) float gl[DK];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, q4 = lane >> 4;
+    const int H = a.H, chains = a.n_seqs * H;
+    const int segs = XMODE ? a.nseg - 2 : a.nseg;
+    if (segs <= 0 || (int)blockIdx.x >= chains * segs) return;
+    const int chain = blockIdx.x / segs, p = (XMODE ? 1 : 0) + (int)blockIdx.x % segs;
+    const int n = chain / H, h = chain % H;
+    const int64_t tok0 = (int64_t)n * a.seq_len + (int64_t)p * a.seg_len;
+    const int64_t rem = (int64_t)a.seq_len - (int64_t)p * a.seg_len;
+    const int64_t L = rem < a.seg_len ? rem : a.seg_len;
+    const int nch = (int)((L + C - 1) / C);
+    const uint8_t *const rbase = a.rec + ((int64_t)p * chains + chain) * a.rec_chunks * Rc::BYTES;
+    const int vrow = H * DV;
+
+    const bool owns = wave < Sh::NCT;
+    f32x4 S[CPW][KT];
+    const float *sinit = XMODE ? nullptr : a.ws_s + ((int64_t)p * chains + chain) * DK * DV;
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+        const int ct = wave + NW * j;
+#pragma unroll
+        for (int r = 0; r < KT; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * r + 4 * q4 + e;
+                S[j][r][e] = !owns ? 0.f
+                             : XMODE ? (row == 16 * ct + lr ? 1.f : 0.f)
+                                     : sinit[(int64_t)row * DV + 16 * ct + lr];
+            }
+    }
+
+    // staged piece x -> its byte offset in the record and its LDS address
+    auto rec_off = [](int x) {
+        const int b = 16 * x;
+        return (XMODE && b >= Rc::oQ) ? b - Rc::oQ + Rc::oK : b;
+    };
+    auto lds_of = [&](int b) -> OP * {
+        if (b < Rc::oQ) return Wl + (b / WROW) * LDK + (b % WROW) / SZ;
+        if (b < Rc::oK) return Ql + ((b - Rc::oQ) / WROW) * LDK + ((b - Rc::oQ) % WROW) / SZ;
+        if (b < Rc::oM) return Kl + ((b - Rc::oK) / KROW) * LDC + ((b - Rc::oK) % KROW) / SZ;
+        return Ml + ((b - Rc::oM) / MROW) * LDC + ((b - Rc::oM) % MROW) / SZ;
+    };
+    u32x4 pre[PPT];
+    f32x4 preg = {0.f, 0.f, 0.f, 0.f};
+    f32x4 preu[CPW][NB];
+    if (nch > 0)
+        {
+            const uint8_t *rp_ = rbase + (int64_t)(0) * Rc::BYTES;
+#pragma unroll
+            for (int m = 0; m < PPT; ++m) {
+                const int x = tid + m * NT;
+                pre[m] = *reinterpret_cast<const u32x4 *>(rp_ + rec_off(x < N16 ? x : 0));
+            }
+            if (tid < DK / 4) preg = *reinterpret_cast<const f32x4 *>(rp_ + Rc::oG + 16 * tid);
+            if (!XMODE && owns) {
+#pragma unroll
+                for (int j = 0; j < CPW; ++j)
+#pragma unroll
+                    for (int I = 0; I < NB; ++I)
+                        preu[j][I] = *reinterpret_cast<const f32x4 *>(
+                            rp_ + Rc::oU + (((wave + NW * j) * NB + I) * 64 + lane) * 16);
+            }
+        }
+
+
+    for (int ci = 0; ci < nch; ++ci) {
+        __syncthreads();  // the previous chunk's readers of LDS are done
+#pragma unroll
+        for (int m = 0; m < PPT; ++m) {
+            const int x = tid + m * NT;
+            if (x < N16) *reinterpret_cast<u32x4 *>(lds_of(rec_off(x))) = pre[m];
+        }
+        if (tid < DK / 4) *reinterpret_cast<f32x4 *>(gl + 4 * tid) = preg;
+        f32x4 Ur[CPW][NB];
+#pragma unroll
+        for (int j = 0; j < CPW; ++j)
+#pragma unroll
+            for (int I = 0; I < NB; ++I) Ur[j][I] = XMODE ? f32x4{0.f, 0.f, 0.f, 0.f} : preu[j][I];
+        __syncthreads();
+        if (ci + 1 < nch)  // in flight during the state pass
+            {
+                const uint8_t *rp_ = rbase + (int64_t)(ci + 1) * Rc::BYTES;
+#pragma unroll
+                for (int m = 0; m < PPT; ++m) {
+                    const int x = tid + m * NT;
+                    pre[m] = *reinterpret_cast<const u32x4 *>(rp_ + rec_off(x < N16 ? x : 0));
+                }
+                if (tid < DK / 4) preg = *reinterpret_cast<const f32x4 *>(rp_ + Rc::oG + 16 * tid);
+                if (!XMODE && owns) {
+#pragma unroll
+                    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+                        for (int I = 0; I < NB; ++I)
+                            preu[j][I] = *reinterpret_cast<const f32x4 *>(
+                                rp_ + Rc::oU + (((wave + NW * j) * NB + I) * 64 + lane) * 16);
+                }
+            }
+
+
+        const int64_t t0 = tok0 + (int64_t)ci * C;
+        const int Lc = (int)((L - (int64_t)ci * C) < C ? (L - (int64_t)ci * C) : C);
+        if (owns) {
+            const rsrc_t ro = make_rsrc(a.o + t0 * vrow, XMODE ? 0u : (uint32_t)(Lc * vrow * 4));
+#pragma unroll
+            for (int j = 0; j < CPW; ++j) {
+                const int cv = wave + NW * j;
+                const int oo = (4 * q4 * vrow + h * DV + 16 * cv + lr) * 4;
+                typename ST::frag sfr[DK / KS];
+#pragma unroll
+                for (int pp = 0; pp < DK / KS; ++pp) sfr[pp] = ST::regs(&S[j][pp * TPS]);
+                f32x4 U[NB];
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    f32x4 ws = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int pp = 0; pp < DK / KS; ++pp)
+                        ST::mma(ws, ST::permuted(Wl + (16 * I + lr) * LDK, pp * KS, q4), sfr[pp]);
+                    U[I] = Ur[j][I] - ws;
+                }
+                typename ST::frag ufr[C / KS];
+#pragma unroll
+                for (int pp = 0; pp < C / KS; ++pp) ufr[pp] = ST::regs(&U[pp * TPS]);
+                if constexpr (!XMODE) {
+#pragma unroll
+                    for (int I = 0; I < NB; ++I) {
+                        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int pp = 0; pp < DK / KS; ++pp)
+                            ST::mma(o, ST::permuted(Ql + (16 * I + lr) * LDK, pp * KS, q4), sfr[pp]);
+#pragma unroll
+                        for (int pp = 0; pp <= I / TPS; ++pp)
+                            ST::mma(o, ST::permuted(Ml + (16 * I + lr) * LDC, pp * KS, q4), ufr[pp]);
+                        const int so = 16 * I * vrow * 4;
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.x), ro, oo, so, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.y), ro, oo, so + vrow * 4, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.z), ro, oo, so + 2 * vrow * 4, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.w), ro, oo, so + 3 * vrow * 4, 0);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < KT; ++r) {
+                    f32x4 acc = S[j][r] * *reinterpret_cast<const f32x4 *>(gl + 16 * r + 4 * q4);
+#pragma unroll
+                    for (int pp = 0; pp < C / KS; ++pp)
+                        ST::mma(acc, ST::permuted(Kl + (16 * r + lr) * LDC, pp * KS, q4), ufr[pp]);
+                    S[j][r] = acc;
+                }
+            }
+        }
+    }
+
+    float *dst = nullptr;
+    if (XMODE)
+        dst = a.ws_x + ((int64_t)p * chains + chain) * DK * DV;
+    else if (a.s_out && p == a.nseg - 1)
+        dst = a.s_out + (int64_t)chain * DK * DV;
+    if (owns && dst) {
+#pragma unroll
+        for (int j = 0; j < CPW; ++j)
+#pragma unroll
+            for (int r = 0; r < KT; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[(int64_t)(16 * r + 4 * q4 + e) * DV + 16 * (wave + NW * j) + lr] = S[j][r][e];
+    }
+}
+
+// Split combine: S_0 = the initial state (or zero), S_1 = R_0 (segment 0 ran from the
+// initial state), then S_{p+1} = X_p S_p + R_p. One workgroup per (chain, 16-column block);
+// float32 FMA with the running block in LDS. Writes ws_s[p] for p = 0 .. nseg-1.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void split_combine_kernel(ChunkArgs a) {
     __shared__ float cur[DK][16];
@@ -874,16 +1109,16 @@ __global__ __launch_bounds__(256) void split_combine_kernel(ChunkArgs a) {
     if (chain >= chains) return;
     const int tid = threadIdx.x;
     const int64_t cstride = (int64_t)chains * DK * DV;
-    float *s0 = a.ws_s + (int64_t)chain * DK * DV + 16 * cb;
+    float *const s_base = a.ws_s + (int64_t)chain * DK * DV + 16 * cb;
     for (int idx = tid; idx < DK * 16; idx += 256) {
         const int r = idx / 16, c = idx % 16;
-        const float v = a.s0 ? a.s0[(int64_t)chain * DK * DV + (int64_t)r * DV + 16 * cb + c] : 0.f;
-        s0[(int64_t)r * DV + c] = v;
-        cur[r][c] = a.ws_r[(int64_t)chain * DK * DV + (int64_t)r * DV + 16 * cb + c];  // R_0
+        const int64_t e = (int64_t)chain * DK * DV + (int64_t)r * DV + 16 * cb + c;
+        s_base[(int64_t)r * DV + c] = a.s0 ? a.s0[e] : 0.f;  // S_0
+        cur[r][c] = a.ws_r[e];                              // S_1 = R_0
     }
     __syncthreads();
     for (int p = 1; p < a.nseg; ++p) {
-        float *sp = s0 + p * cstride;
+        float *sp = s_base + p * cstride;
         for (int idx = tid; idx < DK * 16; idx += 256) sp[(int64_t)(idx / 16) * DV + idx % 16] = cur[idx / 16][idx % 16];
         if (p + 1 >= a.nseg) break;
         // next = X_p cur + R_p
@@ -906,31 +1141,42 @@ __global__ __launch_bounds__(256) void split_combine_kernel(ChunkArgs a) {
     }
 }
 
-template <typename Tin, typename OP, int C, int DK, int DV, int NW, int NWT = NW>
+template <typename Tin, typename OP, int C, int DK, int DV, int NW>
 hipError_t launch_t(const ChunkArgs &a, hipStream_t stream) {
     const int64_t chains = (int64_t)a.n_seqs * a.H;
-    if (2 * chains * (a.seg_len ? a.nseg : 1) > 0x7fffffff) return hipErrorInvalidValue;
-    if (a.seg_len) {
-        hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NWT, true>),
-                           dim3((unsigned)(2 * chains * (a.nseg - 1))), dim3(64 * NWT), 0, stream, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    if (chains * (a.seg_len ? a.nseg : 1) > 0x7fffffff) return hipErrorInvalidValue;
+    if (!a.seg_len) {
+        hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NW, false>), dim3((unsigned)chains),
+                           dim3(64 * NW), 0, stream, a);
+        return hipGetLastError();
+    }
+    hipError_t e;
+    if constexpr (DK == DV) {
+        hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NW, true>),
+                           dim3((unsigned)(chains * a.nseg)), dim3(64 * NW), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (a.nseg > 2) {
+            hipLaunchKernelGGL((replay_kernel<OP, C, DK, DV, NW, true>),
+                               dim3((unsigned)(chains * (a.nseg - 2))), dim3(64 * NW), 0, stream, a);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
         hipLaunchKernelGGL((split_combine_kernel<DK, DV>), dim3((unsigned)(chains * (DV / 16))),
                            dim3(256), 0, stream, a);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((replay_kernel<OP, C, DK, DV, NW, false>),
+                           dim3((unsigned)(chains * a.nseg)), dim3(64 * NW), 0, stream, a);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;  // the split is planned only for Dk == Dv
     }
-    hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NW, false>),
-                       dim3((unsigned)(chains * (a.seg_len ? a.nseg : 1))), dim3(64 * NW), 0,
-                       stream, a);
-    return hipGetLastError();
 }
 
-// Sequence-split plan for B sequences of T tokens. One workgroup fills a compute unit
-// (its LDS), so a launch runs in ceil(blocks / CUs) rounds. Without a split that is
-// ceil(chains / CUs) rounds of the whole sequence; cutting it into P segments costs one
-// transition pass (two blocks per chain and segment but the last, no outputs) plus the
-// full pass over P segments, each round 1/P of the sequence. P is picked by that estimate.
+// Sequence-split plan for B sequences of T tokens. One workgroup fills a compute unit (its
+// LDS), so a launch runs in ceil(blocks / CUs) rounds. Without a split that is
+// ceil(chains / CUs) rounds of the whole sequence. Cut into P segments, the forward pass runs
+// all segments at once (1/P of the sequence per round); the replay passes then re-run the
+// state pass alone from the records: X for segments 1..P-2, outputs for segments 1..P-1.
+// P is picked by that estimate, in chunk times.
 struct SplitPlan {
     int nseg = 1, seg_len = 0;
     size_t bytes = 0;
@@ -948,23 +1194,31 @@ int device_cus() {
     return cached[dev];
 }
 
-SplitPlan plan_split(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk) {
+int64_t record_bytes(int32_t in_dtype, int32_t C, int32_t Dk, int32_t Dv) {
+    const int64_t sz = in_dtype == 1 ? 2 : 4;  // matrix-core operand size
+    const int64_t b = (2 * (int64_t)C * Dk + (int64_t)Dk * C + (int64_t)C * C) * sz + Dk * 4 + (int64_t)C * Dv * 4;
+    return (b + 255) & ~(int64_t)255;
+}
+
+SplitPlan plan_split(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                     int32_t in_dtype) {
     SplitPlan sp;
     const int64_t chains = (int64_t)B * H;
     const int64_t cus = device_cus();
     if (chains <= 0 || cus <= 0 || T <= 0 || Dk != Dv) return sp;
     const int64_t nchunks = ((int64_t)T + chunk - 1) / chunk;
     auto rounds = [&](int64_t blocks) { return (double)((blocks + cus - 1) / cus); };
-    constexpr double kTransCost = 0.73;   // transition chunk vs full chunk (measured, bf16 D=128)
-    constexpr double kFixedCost = 4.0;    // extra launches and the combine, in chunk times
+    constexpr double kXCost = 0.15;     // replay chunk, X pass, vs forward chunk
+    constexpr double kOutCost = 0.3;    // replay chunk, output pass
+    constexpr double kFixedCost = 4.0;  // extra launches and the combine, in chunk times
     double best = rounds(chains) * (double)nchunks;
     for (int64_t P = 2; P <= 16; ++P) {
         const int64_t per = (nchunks + P - 1) / P;  // chunks per segment
         if (per < 8) break;
         const int64_t nseg = (nchunks + per - 1) / per;
         if (nseg < 2) continue;
-        const double cost = rounds(2 * chains * (nseg - 1)) * per * kTransCost +
-                            rounds(chains * nseg) * per + kFixedCost + 0.25 * (nseg - 2);
+        const double cost = rounds(chains * nseg) * per + rounds(chains * (nseg - 2)) * per * kXCost +
+                            rounds(chains * nseg) * per * kOutCost + kFixedCost + 0.25 * (nseg - 2);
         if (cost < (sp.nseg > 1 ? 0.98 : 0.9) * best) {  // a split must gain 10%; more segments 2%
             best = cost;
             sp.nseg = (int)nseg;
@@ -972,8 +1226,10 @@ SplitPlan plan_split(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, in
         }
     }
     if (sp.nseg < 2) return SplitPlan{};
-    sp.bytes = (size_t)(sp.nseg - 1) * chains * ((size_t)Dk * Dv + (size_t)Dk * Dk) * 4 +
-               (size_t)sp.nseg * chains * Dk * Dv * 4;
+    const int64_t rec_chunks = sp.seg_len / chunk;
+    sp.bytes = (size_t)(sp.nseg - 1) * chains * ((size_t)Dk * Dv + (size_t)Dk * Dk) * 4 +  // R, X
+               (size_t)sp.nseg * chains * Dk * Dv * 4 +                                  // S_p
+               (size_t)sp.nseg * chains * rec_chunks * record_bytes(in_dtype, chunk, Dk, Dv);
     return sp;
 }
 
@@ -988,10 +1244,9 @@ bool chunk_fwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv
 }
 
 size_t chunk_fwd_split_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
-                             int32_t chunk, int32_t num_seqs) {
-    if (num_seqs != B || (!chunk_fwd_supported(1, chunk, Dk, Dv) && !chunk_fwd_supported(0, chunk, Dk, Dv)))
-        return 0;
-    return plan_split(B, T, H, Dk, Dv, chunk).bytes;
+                             int32_t chunk, int32_t in_dtype, int32_t num_seqs) {
+    if (num_seqs != B || !chunk_fwd_supported(in_dtype, chunk, Dk, Dv)) return 0;
+    return plan_split(B, T, H, Dk, Dv, chunk, in_dtype).bytes;
 }
 
 hipError_t launch_chunk_fwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv,
@@ -1003,7 +1258,7 @@ hipError_t launch_chunk_fwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t
     a.seg_len = 0;
     a.nseg = 1;
     if (!a.cu_seqlens && workspace) {
-        const SplitPlan sp = plan_split(a.n_seqs, a.seq_len, a.H, Dk, Dv, chunk);
+        const SplitPlan sp = plan_split(a.n_seqs, a.seq_len, a.H, Dk, Dv, chunk, in_dtype);
         if (sp.nseg > 1 && workspace_bytes >= sp.bytes) {
             const size_t chains = (size_t)a.n_seqs * a.H;
             a.seg_len = sp.seg_len;
@@ -1011,6 +1266,8 @@ hipError_t launch_chunk_fwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t
             a.ws_r = static_cast<float *>(workspace);
             a.ws_x = a.ws_r + (size_t)(sp.nseg - 1) * chains * Dk * Dv;
             a.ws_s = a.ws_x + (size_t)(sp.nseg - 1) * chains * Dk * Dk;
+            a.rec = reinterpret_cast<uint8_t *>(a.ws_s + (size_t)sp.nseg * chains * Dk * Dv);
+            a.rec_chunks = sp.seg_len / chunk;
         }
     }
     if (in_dtype == 1) return launch_t<bf16_t, _Float16, 64, 128, 128, 8>(a, stream);

@@ -18,11 +18,14 @@ struct ChunkArgs {
     float *s_out;                // [N, H, Dk, Dv] or nullptr
     float *o;                    // [tokens, H, Dv]
     // sequence split (fixed-length batches with few chains): each sequence is cut into nseg
-    // segments of seg_len tokens (a multiple of the chunk); 0 = no split
+    // segments of seg_len tokens (a multiple of the chunk); seg_len 0 = no split
     int32_t seg_len, nseg;
-    float *ws_r;                 // [nseg-1][N*H][Dk][Dv] segment final states from the split start
-    float *ws_x;                 // [nseg-1][N*H][Dk][Dk] segment transitions
-    float *ws_s;                 // [nseg][N*H][Dk][Dv]   initial state of every segment
+    float *ws_r;                 // [nseg-1][N*H][Dk][Dv] R_p: segment p's final state (p = 0:
+                                 //   from the initial state; p > 0: from zero)
+    float *ws_x;                 // [nseg-1][N*H][Dk][Dk] X_p: segment p's linear part (p >= 1)
+    float *ws_s;                 // [nseg][N*H][Dk][Dv]   S_p: segment p's true start state
+    uint8_t *rec;                // [nseg][N*H][rec_chunks] chunk records of every segment
+    int32_t rec_chunks;          // chunks per segment (seg_len / chunk)
 };
 
 struct DecodeArgs {
@@ -37,7 +40,7 @@ struct DecodeArgs {
 // Workspace bytes the sequence split needs for this problem on the current device (0: no
 // split). The split is used only when the call provides at least this much workspace.
 size_t chunk_fwd_split_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
-                             int32_t chunk, int32_t num_seqs);
+                             int32_t chunk, int32_t in_dtype, int32_t num_seqs);
 
 // True if an instantiation exists for these parameters (in_dtype is a kda_dtype code).
 bool chunk_fwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv);

@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_prefill_128k_h32_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_26_amd", "csrc", "kda_chunk.hip")
-PREFILL_KERNELS = ("chunk_fwd_kernel", "split_combine_kernel")  # one kda_chunk_fwd call
+PREFILL_KERNELS = ("chunk_fwd_kernel", "replay_kernel", "split_combine_kernel")  # one call
 COPY_BYTES = 1 << 30  # calibration: read 1 GiB, write 1 GiB
 
 
@@ -90,6 +90,17 @@ def _counter_rows(path: str):
             yield row["Kernel_Name"], int(row["Dispatch_Id"]), row["Counter_Name"], float(row["Counter_Value"])
 
 
+def kernel_label(name: str) -> str:
+    """Readable label of a prefill kernel from its (possibly mangled) name."""
+    if "chunk_fwd_kernel" in name:
+        split = "true>" in name or "Lb1EEEv" in name
+        return "chunk_fwd_kernel (" + ("split forward, records" if split else "forward") + ")"
+    if "replay_kernel" in name:
+        x = "true>" in name or "Lb1EEEv" in name
+        return "replay_kernel (" + ("segment maps X" if x else "outputs") + ")"
+    return "split_combine_kernel"
+
+
 def traffic_from(fetch_csv: str, write_csv: str) -> dict:
     """Per-call HBM bytes of the prefill from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by known bytes / counted bytes of the copy-like calibration kernel
@@ -101,14 +112,10 @@ def traffic_from(fetch_csv: str, write_csv: str) -> dict:
             if cname not in ("FETCH_SIZE", "WRITE_SIZE"):
                 continue
             if any(k in name for k in PREFILL_KERNELS):
-                if "chunk_fwd_kernel" in name:
-                    fwd = "false>" in name or "Lb0E" in name
-                    short = "chunk_fwd_kernel (" + ("forward" if fwd else "transition") + ")"
-                else:
-                    short = "split_combine_kernel"
+                short = kernel_label(name)
                 kib, n = per_kernel.get(short, (0.0, 0))
                 per_kernel[short] = (kib + val, n + 1)
-                if "chunk_fwd_kernel" in name and ("false>" in name or "Lb0E" in name):
+                if "chunk_fwd_kernel" in name:
                     calls.add(disp)  # one forward dispatch per call
             elif "neg_kernel" in name:
                 copy.append(val)

@@ -41,6 +41,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     if not os.path.exists(p):
         raise RuntimeError(f"libkda.so not found at {p}: build it with "
                            "`python gated_delta_rule_26_amd/build.py`")
+    # torch first: its HIP runtime must be the one the process uses (libkda resolves against
+    # the already loaded runtime), or torch and the library would disagree on devices/streams
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     i32, f32, vp, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
     lib.kda_status_string.restype = ctypes.c_char_p

@@ -126,7 +126,8 @@ template <typename OP, int TSZ, int C, int DK, int DV, int NW> struct ChunkShape
 // Per-chunk record of a split segment (global memory, written by the chunked forward and read
 // by the replay passes). Dense copies of the LDS operands in the same element order:
 // W [C][Dk] and Qg [C][Dk] (columns in step order), Kd^T [Dk][C], M [C][C] (columns in step
-// order), then gC [Dk] float32 and U~ float32 in accumulator order [Dv/16][C/16][64 lanes][4].
+// order), then gC [Dk] float32 and U~ (operand type) in accumulator order
+// [Dv/16][C/16][64 lanes][4].
 template <typename OP, int C, int DK, int DV> struct Record {
     static constexpr int SZ = (int)sizeof(OP);
     static constexpr int oW = 0;
@@ -136,7 +137,7 @@ template <typename OP, int C, int DK, int DV> struct Record {
     static constexpr int OPS = oM + C * C * SZ;  // the LDS-staged part
     static constexpr int oG = OPS;
     static constexpr int oU = oG + DK * 4;
-    static constexpr int BYTES = (oU + C * DV * 4 + 255) & ~255;
+    static constexpr int BYTES = (oU + C * DV * SZ + 255) & ~255;
 };
 
 // Index of the off-diagonal block pair (J, I), I >= J + 2, in the far-operand table.
@@ -824,7 +825,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             for (int j = 0; j < CPW; ++j)
 #pragma unroll
                 for (int I = 0; I < NB; ++I)
-                    *reinterpret_cast<f32x4 *>(rp + Rc::oU + (((wave + NW * j) * NB + I) * 64 + lane) * 16) = Ur[j][I];
+                    *reinterpret_cast<frag4 *>(rp + Rc::oU + (((wave + NW * j) * NB + I) * 64 + lane) * 4 * Rc::SZ) =
+                        MM::from_f32(Ur[j][I]);
         }
 
         // ---- P5: state pass, registers only: U = U~ - W S; O = Qg S + M U; S' = gC S + Kd^T U
@@ -975,7 +977,7 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
     };
     u32x4 pre[PPT];
     f32x4 preg = {0.f, 0.f, 0.f, 0.f};
-    f32x4 preu[CPW][NB];
+    typename MM::frag preu[CPW][NB];
     if (nch > 0)
         {
             const uint8_t *rp_ = rbase + (int64_t)(0) * Rc::BYTES;
@@ -990,8 +992,8 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
                 for (int j = 0; j < CPW; ++j)
 #pragma unroll
                     for (int I = 0; I < NB; ++I)
-                        preu[j][I] = *reinterpret_cast<const f32x4 *>(
-                            rp_ + Rc::oU + (((wave + NW * j) * NB + I) * 64 + lane) * 16);
+                        preu[j][I] = *reinterpret_cast<const typename MM::frag *>(
+                            rp_ + Rc::oU + (((wave + NW * j) * NB + I) * 64 + lane) * 4 * SZ);
             }
         }
 
@@ -1008,7 +1010,7 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < CPW; ++j)
 #pragma unroll
-            for (int I = 0; I < NB; ++I) Ur[j][I] = XMODE ? f32x4{0.f, 0.f, 0.f, 0.f} : preu[j][I];
+            for (int I = 0; I < NB; ++I) Ur[j][I] = XMODE ? f32x4{0.f, 0.f, 0.f, 0.f} : MM::to_f32(preu[j][I]);
         __syncthreads();
         if (ci + 1 < nch)  // in flight during the state pass
             {
@@ -1024,8 +1026,8 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
                     for (int j = 0; j < CPW; ++j)
 #pragma unroll
                         for (int I = 0; I < NB; ++I)
-                            preu[j][I] = *reinterpret_cast<const f32x4 *>(
-                                rp_ + Rc::oU + (((wave + NW * j) * NB + I) * 64 + lane) * 16);
+                            preu[j][I] = *reinterpret_cast<const typename MM::frag *>(
+                                rp_ + Rc::oU + (((wave + NW * j) * NB + I) * 64 + lane) * 4 * SZ);
                 }
             }
 
@@ -1196,7 +1198,7 @@ int device_cus() {
 
 int64_t record_bytes(int32_t in_dtype, int32_t C, int32_t Dk, int32_t Dv) {
     const int64_t sz = in_dtype == 1 ? 2 : 4;  // matrix-core operand size
-    const int64_t b = (2 * (int64_t)C * Dk + (int64_t)Dk * C + (int64_t)C * C) * sz + Dk * 4 + (int64_t)C * Dv * 4;
+    const int64_t b = (2 * (int64_t)C * Dk + (int64_t)Dk * C + (int64_t)C * C + (int64_t)C * Dv) * sz + Dk * 4;
     return (b + 255) & ~(int64_t)255;
 }
 

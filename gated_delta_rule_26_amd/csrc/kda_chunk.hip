@@ -287,7 +287,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     if ((int)blockIdx.x >= chains * segs) return;
     const int chain = blockIdx.x / segs, seg = blockIdx.x % segs;
     constexpr bool store = STORE;
-    const int n = chain / H, h = chain % H;
+    // packed batches run their sequences longest first when an order is given
+    const int n = a.order ? a.order[chain / H] : chain / H, h = chain % H;
     int64_t tok0, L;
     if (a.cu_seqlens) {
         tok0 = a.cu_seqlens[n];
@@ -1143,6 +1144,20 @@ __global__ __launch_bounds__(256) void split_combine_kernel(ChunkArgs a) {
     }
 }
 
+// Longest-first order of the packed sequences: order[rank] = n, rank = the number of longer
+// sequences plus the equal ones before n. One thread per sequence, O(N^2) comparisons.
+__global__ __launch_bounds__(256) void order_kernel(const int32_t *cu, int32_t N, int32_t *order) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= N) return;
+    const int32_t li = cu[i + 1] - cu[i];
+    int rank = 0;
+    for (int j = 0; j < N; ++j) {
+        const int32_t lj = cu[j + 1] - cu[j];
+        rank += (lj > li) || (lj == li && j < i);
+    }
+    order[rank] = i;
+}
+
 template <typename Tin, typename OP, int C, int DK, int DV, int NW>
 hipError_t launch_t(const ChunkArgs &a, hipStream_t stream) {
     const int64_t chains = (int64_t)a.n_seqs * a.H;
@@ -1237,6 +1252,8 @@ SplitPlan plan_split(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, in
 
 }  // namespace
 
+constexpr int32_t kMaxOrderedSeqs = 4096;  // packed batches ordered longest first up to this
+
 bool chunk_fwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv) {
     if (Dk != Dv) return false;
     if (in_dtype == 1) return chunk == 64 && Dk == 128;
@@ -1247,7 +1264,9 @@ bool chunk_fwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv
 
 size_t chunk_fwd_split_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
                              int32_t chunk, int32_t in_dtype, int32_t num_seqs) {
-    if (num_seqs != B || !chunk_fwd_supported(in_dtype, chunk, Dk, Dv)) return 0;
+    if (!chunk_fwd_supported(in_dtype, chunk, Dk, Dv)) return 0;
+    if (num_seqs != B)  // packed batch: the longest-first order
+        return num_seqs > 1 && num_seqs <= kMaxOrderedSeqs ? (size_t)num_seqs * sizeof(int32_t) : 0;
     return plan_split(B, T, H, Dk, Dv, chunk, in_dtype).bytes;
 }
 
@@ -1259,6 +1278,15 @@ hipError_t launch_chunk_fwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t
     ChunkArgs a = args;
     a.seg_len = 0;
     a.nseg = 1;
+    if (a.cu_seqlens && workspace && a.n_seqs <= kMaxOrderedSeqs &&
+        workspace_bytes >= (size_t)a.n_seqs * sizeof(int32_t)) {
+        int32_t *order = static_cast<int32_t *>(workspace);
+        hipLaunchKernelGGL(order_kernel, dim3((unsigned)((a.n_seqs + 255) / 256)), dim3(256), 0, stream,
+                           a.cu_seqlens, a.n_seqs, order);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        a.order = order;
+    }
     if (!a.cu_seqlens && workspace) {
         const SplitPlan sp = plan_split(a.n_seqs, a.seq_len, a.H, Dk, Dv, chunk, in_dtype);
         if (sp.nseg > 1 && workspace_bytes >= sp.bytes) {

@@ -10,6 +10,7 @@ struct ChunkArgs {
     int32_t n_seqs;              // number of sequences N
     int32_t seq_len;             // tokens per sequence when cu_seqlens == nullptr
     const int32_t *cu_seqlens;   // device [N+1] or nullptr
+    const int32_t *order;        // device [N]: sequence of each rank (longest first), or nullptr
     int32_t H;
     float scale;
     const void *q, *k, *v;       // [tokens, H, Dk] / [tokens, H, Dv], in_dtype

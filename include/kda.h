@@ -82,15 +82,20 @@ const char *kda_last_error(void);
 int32_t kda_version(void);
 
 /*
- * kda_chunk_fwd_workspace_bytes - device workspace that lets kda_chunk_fwd split long
- * sequences for these sizes on the current device (0 when no split applies).
+ * kda_chunk_fwd_workspace_bytes - optional device workspace for kda_chunk_fwd with these
+ * sizes on the current device (0 when it would not be used).
  *
- * With few (sequence, head) chains the recurrence would occupy only a few compute units,
- * so a batch without cu_seqlens may be cut into segments along the sequence: a first pass
- * computes every segment's state map in parallel, a small pass chains the maps, and the
- * chunked forward then runs all segments in parallel. The workspace holds the per-segment
- * maps and states. It is optional: with less workspace (or NULL) the call is computed
- * without the split, with the same result up to rounding.
+ * Fixed-length batches (num_seqs == B): with few (sequence, head) chains the recurrence
+ * would occupy only a few compute units, so each sequence may be cut into segments. The
+ * chunked forward runs all segments at once (segment 0 from the initial state, the others
+ * from zero) and records each chunk's operands; a replay pass computes each segment's
+ * linear state map from the records, the maps are chained into the true start state of
+ * every segment, and a second replay pass produces the outputs and the final state. The
+ * workspace holds the records, maps and states (about 74 KB per chunk and head for the bf16
+ * instantiation, plus three states per segment).
+ * Packed batches (cu_seqlens): num_seqs int32 for running the sequences longest first.
+ * The workspace is optional: with less (or NULL) the call runs unsplit / in the given order,
+ * with the same result up to rounding.
  */
 size_t kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
                                      int32_t chunk, int32_t in_dtype, int32_t num_seqs);

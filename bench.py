@@ -152,6 +152,59 @@ def write_traffic(fetch_csv: str, write_csv: str) -> None:
     print(json.dumps(res, indent=1))
 
 
+def other_workloads(kda, synth, to_dev, torch, np, log) -> dict:
+    """Prefill tokens/s on the 4K-token and the packed variable-length workloads, and the
+    device's copy bandwidth as a practical HBM reference (events on the current stream)."""
+    out = {}
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    w = synth.WORKLOADS["prefill_4k_h16"]
+    x = synth.make_inputs(w)
+    q, k, v = (to_dev(x[n][None], True) for n in ("q", "k", "v"))
+    g, b = to_dev(x["g"][None]), to_dev(x["beta"][None])
+    ws = torch.empty(max(kda.chunk_fwd_workspace_bytes(q, v), 1), dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: kda.kda_chunk_fwd(q, k, v, g, b, workspace=ws), 20)
+    out["prefill_4k_h16"] = {"ms": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+                             "B": 1, "T": w.T, "H": w.H, "dk": w.K, "dv": w.V, "chunk": w.chunk}
+    del q, k, v, g, b, ws, x
+    log("timed prefill_4k_h16")
+
+    w = synth.WORKLOADS["varlen_64seq_h16"]
+    x = synth.make_inputs(w)
+    cu = torch.from_numpy(x["cu_seqlens"].astype(np.int32)).cuda()
+    q, k, v = (to_dev(x[n], True) for n in ("q", "k", "v"))
+    g, b = to_dev(x["g"]), to_dev(x["beta"])
+    s0 = to_dev(x["initial_state"])
+    n_tok = int(x["cu_seqlens"][-1])
+    ws = torch.empty(max(kda.chunk_fwd_workspace_bytes(q, v, num_seqs=len(x["lengths"])), 1),
+                     dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: kda.kda_chunk_fwd(q, k, v, g, b, initial_state=s0, cu_seqlens=cu,
+                                         workspace=ws), 3)
+    out["varlen_64seq_h16"] = {"ms": round(ms, 4), "tokens_per_s": round(n_tok / (ms * 1e-3), 1),
+                               "sequences": len(x["lengths"]), "tokens": n_tok,
+                               "longest": int(max(x["lengths"])), "H": w.H, "dk": w.K,
+                               "order": "longest first"}
+    del q, k, v, g, b, s0, cu, ws, x
+    log("timed varlen_64seq_h16")
+
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src), 10)
+    out["copy_reference"] = {"bytes": 2 << 30, "gbs": round((2 << 30) / (ms * 1e-3) / 1e9, 1),
+                             "what": "device-to-device copy of 1 GiB (read + write)"}
+    return out
+
+
 def cpu_baseline(x: dict, sample_tokens: int) -> dict:
     """The float64 oracle (unchanged) on the first ``sample_tokens`` tokens of the prefill
     workload, all heads, on the host's cores."""
@@ -181,6 +234,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--decode-seqs", type=int, default=256)
     ap.add_argument("--counter-pass", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads (4K prefill, packed varlen) and the copy reference")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
     if args.traffic_from:
@@ -332,7 +387,11 @@ def main():
             "algorithmic_bytes_per_step": d_bytes,
         },
         "cpu_baseline": None,
+        "other_workloads": None,
     }
+    if not args.no_extra:
+        del pq, pk, pv, pg, pb, po, pws, tq, tk, tv, tg, tb
+        res["other_workloads"] = other_workloads(kda, synth, to_dev, torch, np, log)
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(xp, min(args.cpu_sample_tokens, T))

@@ -14,6 +14,10 @@ Functions
                      one-token sequences.
 ``chunked_fwd``      (oracle/chunked.py) the chunkwise form of the same recurrence in
                      float64 numpy, pinned by equality with ``kda_fwd``.
+``fused``            (oracle/fused.py) the layer's fusions around the core: the forget gate
+                     from its pre-activation, q/k L2 normalisation, the gated RMSNorm of the
+                     output, and their composition with ``kda_fwd`` (``kda_fused_fwd``,
+                     ``kda_fused_decode_step``). Pinned by tests/test_oracle_fused_pins.py.
 
 Nothing here is "parity unpinned".
 """
@@ -116,3 +120,7 @@ def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, threads: int
     cu = np.arange(N + 1, dtype=np.int64)
     return kda_fwd(q, k, v, g, beta, scale=scale, initial_state=state, cu_seqlens=cu,
                    threads=threads)
+
+
+from . import fused  # noqa: E402,F401  (needs kda_fwd above)
+from .fused import kda_fused_decode_step, kda_fused_fwd  # noqa: E402,F401

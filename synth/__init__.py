@@ -12,10 +12,13 @@ from .gen import (  # noqa: F401
     Workload,
     bf16_bits_to_f32,
     bf16_bits_to_f64,
+    NORM_EPS,
     f64_to_bf16_bits,
+    fused_slab,
     gate_params,
     initial_state,
     make_inputs,
+    norm_weight,
     seq_lengths,
     slab,
     stored_to_f64,

@@ -20,6 +20,14 @@ stable delta-rule erase term):
 * optional initial states: M ~ N(0,1)^{K x V} in float64 divided by its largest singular
   value, stored as float32.
 * packed lengths: round(LogNormal(ln 8192, 1.4)), clipped to [1024, 65536].
+
+Fused-layer inputs (``fused_slab``, ``make_fused_inputs``): the raw values that the layer
+feeds the fused entry points, drawn from streams of their own. q, k ~ N(0, 1) are NOT
+normalised; the gate's pre-activation x ~ N(0, 1) and the output gate's pre-activation
+z ~ N(0, 1) are rounded to the storage dtype like q, k, v; A_log = a_h and dt_bias = b_{h,c}
+are the gate parameters above, stored as float32; the output norm's gain is
+1 + N(0, 0.1^2) per value channel (float32) and its epsilon 1e-6. v and beta are the same
+as in the core workloads.
 """
 
 from __future__ import annotations
@@ -36,6 +44,8 @@ ROOT_SEED = 20260
 # tensor ids inside the seed key
 _T_Q, _T_K, _T_V, _T_BETA, _T_X, _T_S0 = 0, 1, 2, 3, 4, 6
 _P_A, _P_B, _P_LEN = 10, 11, 12
+_T_QR, _T_KR, _T_XG, _T_Z, _P_W = 20, 21, 22, 23, 13
+NORM_EPS = 1e-6
 
 
 @dataclass(frozen=True)
@@ -191,13 +201,32 @@ def slab(w: Workload, n: int, h: int, L: int | None = None,
     return out
 
 
+def norm_weight(w: Workload) -> np.ndarray:
+    """float32 [V] gain of the output norm."""
+    return (1.0 + 0.1 * _rng(w.wid, _P_W).standard_normal(w.V)).astype(np.float32)
+
+
+def fused_slab(w: Workload, n: int, h: int, L: int | None = None) -> dict:
+    """Raw fused-layer inputs of sequence ``n``, head ``h``: q, k, x [L, K] and v, z [L, V]
+    as stored arrays (unnormalised q and k), beta float32 [L]."""
+    if L is None:
+        L = int(seq_lengths(w)[n]) if w.packed else w.tokens_per_seq
+    out = {}
+    for name, tid, D in (("q", _T_QR, w.K), ("k", _T_KR, w.K), ("x", _T_XG, w.K),
+                         ("z", _T_Z, w.V), ("v", _T_V, w.V)):
+        out[name] = _store(_rng(w.wid, tid, n, h).standard_normal((L, D)), w.dtype)
+    z = _rng(w.wid, _T_BETA, n, h).standard_normal(L) + w.beta_mu
+    out["beta"] = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+    return out
+
+
 def _workers(workers: int | None) -> int:
     if workers:
         return workers
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def make_inputs(w: Workload, seqs=None, workers: int | None = None) -> dict:
+def make_inputs(w: Workload, seqs=None, workers: int | None = None, fused: bool = False) -> dict:
     """Assemble whole token-major tensors for a workload (or for the sequences ``seqs``,
     whose slabs are identical to those of the full workload).
 
@@ -206,6 +235,10 @@ def make_inputs(w: Workload, seqs=None, workers: int | None = None) -> dict:
     float32 [N, H, K, V] or None. For decode workloads the tensors cover the
     ``prefill_T``-token prefill, and ``dec_q``... ``dec_beta`` hold the decode tokens as
     [steps, N, H, D] (step-major, one token per sequence and head per step).
+
+    ``fused=True``: the fused layer's raw inputs instead (``fused_slab``): q, k, x
+    [T_total, H, K]; v, z [T_total, H, V]; beta; plus ``A_log`` float32 [H], ``dt_bias``
+    float32 [H, K], ``norm_weight`` float32 [V] and ``norm_eps``.
     """
     all_len = seq_lengths(w)
     seqs = list(range(len(all_len))) if seqs is None else list(seqs)
@@ -218,31 +251,37 @@ def make_inputs(w: Workload, seqs=None, workers: int | None = None) -> dict:
     Tt = int(cu[-1])
     kdt = np.uint16 if w.dtype == "bf16" else np.float32
     H, K, V = w.H, w.K, w.V
-    res = {
-        "q": np.empty((Tt, H, K), kdt), "k": np.empty((Tt, H, K), kdt),
-        "v": np.empty((Tt, H, V), kdt), "g": np.empty((Tt, H, K), np.float32),
-        "beta": np.empty((Tt, H), np.float32),
-        "cu_seqlens": cu, "lengths": pre, "seqs": np.asarray(seqs),
-        "initial_state": None,
-    }
+    if fused:  # name -> (width, dtype)
+        spec = {"q": (K, kdt), "k": (K, kdt), "v": (V, kdt), "x": (K, kdt), "z": (V, kdt),
+                "beta": (0, np.float32)}
+    else:
+        spec = {"q": (K, kdt), "k": (K, kdt), "v": (V, kdt), "g": (K, np.float32),
+                "beta": (0, np.float32)}
+    shp = lambda lead, D: lead + ((D,) if D else ())  # noqa: E731
+    res = {name: np.empty(shp((Tt, H), D), dt) for name, (D, dt) in spec.items()}
+    res.update({"cu_seqlens": cu, "lengths": pre, "seqs": np.asarray(seqs),
+                "initial_state": None})
     S = w.decode_steps
     N = len(seqs)
     if S:
-        res.update({
-            "dec_q": np.empty((S, N, H, K), kdt), "dec_k": np.empty((S, N, H, K), kdt),
-            "dec_v": np.empty((S, N, H, V), kdt), "dec_g": np.empty((S, N, H, K), np.float32),
-            "dec_beta": np.empty((S, N, H), np.float32),
-        })
+        res.update({"dec_" + name: np.empty(shp((S, N, H), D), dt)
+                    for name, (D, dt) in spec.items()})
     if w.spectral_init:
         res["initial_state"] = np.empty((N, H, K, V), np.float32)
     params = gate_params(w)
+    if fused:
+        res["A_log"] = params[0].astype(np.float32)
+        res["dt_bias"] = params[1].astype(np.float32)
+        res["norm_weight"] = norm_weight(w)
+        res["norm_eps"] = NORM_EPS
 
     def job(i_n_h):
         i, n, h = i_n_h
-        s = slab(w, n, h, int(lengths[i]), params)
+        s = (fused_slab(w, n, h, int(lengths[i])) if fused
+             else slab(w, n, h, int(lengths[i]), params))
         t0, t1 = int(cu[i]), int(cu[i + 1])
         P = t1 - t0
-        for key in ("q", "k", "v", "g", "beta"):
+        for key in spec:
             res[key][t0:t1, h] = s[key][:P]
             if S:
                 res["dec_" + key][:, i, h] = s[key][P:P + S]

@@ -13,8 +13,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["KdaError", "kda_chunk_fwd", "kda_decode_step", "chunk_fwd_workspace_bytes",
-           "load_library", "KDA_F32", "KDA_BF16"]
+__all__ = ["KdaError", "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_fused",
+           "kda_decode_step_fused", "chunk_fwd_workspace_bytes", "load_library", "KDA_F32",
+           "KDA_BF16"]
 
 KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
@@ -22,6 +23,14 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
 
 _LIB = None
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+
+class _Fusion(ctypes.Structure):
+    """Mirror of the C struct kda_fusion (include/kda.h)."""
+    _fields_ = [("gate_x", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("normalize_qk", ctypes.c_int32),
+                ("o_gate", ctypes.c_void_p), ("o_weight", ctypes.c_void_p),
+                ("o_eps", ctypes.c_float)]
 
 
 class KdaError(RuntimeError):
@@ -60,6 +69,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_decode_step.restype = i32
     lib.kda_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, f32,
                                     vp, vp, vp, vp, vp, vp, vp, vp]
+    fp = ctypes.POINTER(_Fusion)
+    lib.kda_chunk_fwd_fused.restype = i32
+    lib.kda_chunk_fwd_fused.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                                        vp, vp, vp, fp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.kda_decode_step_fused.restype = i32
+    lib.kda_decode_step_fused.argtypes = [i32, i32, i32, i32, i32, i32, f32,
+                                          vp, vp, vp, fp, vp, vp, vp]
     if path is None:
         _LIB = lib
     return lib
@@ -99,6 +115,92 @@ def _req(t, name, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _prefill_layout(q, k, v, beta, cu_seqlens):
+    """(B, T, N, H, Dk, Dv) of a prefill call, after checking q, k, v, beta, cu_seqlens."""
+    import torch
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _req(t, nm, q.dtype)
+    _req(beta, "beta", torch.float32)
+    if cu_seqlens is not None:
+        _req(cu_seqlens, "cu_seqlens", torch.int32)
+        if q.dim() == 4:
+            if q.shape[0] != 1:
+                raise ValueError("cu_seqlens requires B == 1")
+        B, T = 1, q.shape[-3]
+        N = cu_seqlens.numel() - 1
+    else:
+        if q.dim() != 4:
+            raise ValueError("q must be [B, T, H, Dk] without cu_seqlens")
+        B, T = q.shape[0], q.shape[1]
+        N = B
+    H, Dk = q.shape[-2], q.shape[-1]
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or beta.shape != q.shape[:-1]:
+        raise ValueError("inconsistent q/k/v/beta shapes")
+    return B, T, N, H, Dk, Dv
+
+
+def _prefill_states(q, N, H, Dk, Dv, initial_state, final_state, output_final_state):
+    import torch
+    if initial_state is not None:
+        _req(initial_state, "initial_state", torch.float32)
+        if tuple(initial_state.shape) != (N, H, Dk, Dv):
+            raise ValueError(f"initial_state must be [{N}, {H}, {Dk}, {Dv}]")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _req(final_state, "final_state", torch.float32)
+        if tuple(final_state.shape) != (N, H, Dk, Dv):
+            raise ValueError(f"final_state must be [{N}, {H}, {Dk}, {Dv}]")
+    return final_state
+
+
+def _prefill_workspace(lib, q, B, T, N, H, Dk, Dv, chunk, split, workspace):
+    import torch
+    if not split:
+        return None, 0
+    if workspace is not None:
+        _req(workspace, "workspace", torch.uint8)
+        return workspace, workspace.numel()
+    ws = lib.kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, _dtype_code(q), N)
+    return (torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None), ws
+
+
+def _fusion(q, k, gate_x, A_log, dt_bias, normalize_qk, o_gate, o_weight, o_eps, v):
+    """Check the fused-step tensors and build the C struct (the tensors stay referenced by
+    the caller for the duration of the call)."""
+    import torch
+    _req(gate_x, "gate_x", q.dtype)
+    if gate_x.shape != q.shape:
+        raise ValueError("gate_x must have q's shape")
+    H, Dk = q.shape[-2], q.shape[-1]
+    _req(A_log, "A_log", torch.float32)
+    _req(dt_bias, "dt_bias", torch.float32)
+    if tuple(A_log.shape) != (H,) or tuple(dt_bias.shape) != (H, Dk):
+        raise ValueError(f"A_log must be [{H}] and dt_bias [{H}, {Dk}]")
+    if o_gate is not None:
+        _req(o_gate, "o_gate", q.dtype)
+        if o_gate.shape != v.shape:
+            raise ValueError("o_gate must have v's shape")
+        _req(o_weight, "o_weight", torch.float32)
+        if tuple(o_weight.shape) != (v.shape[-1],):
+            raise ValueError(f"o_weight must be [{v.shape[-1]}]")
+    return _Fusion(gate_x.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(),
+                   1 if normalize_qk else 0,
+                   None if o_gate is None else o_gate.data_ptr(),
+                   None if o_gate is None else o_weight.data_ptr(), float(o_eps))
+
+
+def _out(o, like, dtype, name="o"):
+    import torch
+    if o is None:
+        return torch.empty(like.shape, dtype=dtype, device=like.device)
+    _req(o, name, dtype)
+    if o.shape != like.shape:
+        raise ValueError(f"{name} must have shape {tuple(like.shape)}")
+    return o
+
+
 def kda_chunk_fwd(q, k, v, g, beta, *, initial_state=None, output_final_state: bool = True,
                   final_state=None, cu_seqlens=None, chunk: int = 64, scale: float = 1.0,
                   o=None, stream=None, split: bool = True, workspace=None):
@@ -117,49 +219,13 @@ def kda_chunk_fwd(q, k, v, g, beta, *, initial_state=None, output_final_state: b
     """
     import torch
     lib = load_library()
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _req(t, nm, q.dtype)
+    B, T, N, H, Dk, Dv = _prefill_layout(q, k, v, beta, cu_seqlens)
     _req(g, "g", torch.float32)
-    _req(beta, "beta", torch.float32)
-    if cu_seqlens is not None:
-        _req(cu_seqlens, "cu_seqlens", torch.int32)
-        if q.dim() == 4:
-            if q.shape[0] != 1:
-                raise ValueError("cu_seqlens requires B == 1")
-        B, T = 1, q.shape[-3]
-        N = cu_seqlens.numel() - 1
-    else:
-        if q.dim() != 4:
-            raise ValueError("q must be [B, T, H, Dk] without cu_seqlens")
-        B, T = q.shape[0], q.shape[1]
-        N = B
-    H, Dk = q.shape[-2], q.shape[-1]
-    Dv = v.shape[-1]
-    if k.shape != q.shape or g.shape != q.shape or v.shape[:-1] != q.shape[:-1] or \
-            beta.shape != q.shape[:-1]:
-        raise ValueError("inconsistent q/k/v/g/beta shapes")
-    if initial_state is not None:
-        _req(initial_state, "initial_state", torch.float32)
-        if tuple(initial_state.shape) != (N, H, Dk, Dv):
-            raise ValueError(f"initial_state must be [{N}, {H}, {Dk}, {Dv}]")
-    if final_state is None and output_final_state:
-        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
-    elif final_state is not None:
-        _req(final_state, "final_state", torch.float32)
-        if tuple(final_state.shape) != (N, H, Dk, Dv):
-            raise ValueError(f"final_state must be [{N}, {H}, {Dk}, {Dv}]")
-    if o is None:
-        o = torch.empty(v.shape, dtype=torch.float32, device=q.device)
-    else:
-        _req(o, "o", torch.float32)
-    if not split:
-        workspace, ws = None, 0
-    elif workspace is not None:
-        _req(workspace, "workspace", torch.uint8)
-        ws = workspace.numel()
-    else:
-        ws = lib.kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, _dtype_code(q), N)
-        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    if g.shape != q.shape:
+        raise ValueError("g must have q's shape")
+    final_state = _prefill_states(q, N, H, Dk, Dv, initial_state, final_state, output_final_state)
+    o = _out(o, v, torch.float32)
+    workspace, ws = _prefill_workspace(lib, q, B, T, N, H, Dk, Dv, chunk, split, workspace)
     st = lib.kda_chunk_fwd(B, T, H, Dk, Dv, chunk, _dtype_code(q), KDA_F32, float(scale),
                            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                            _ptr(initial_state), _ptr(final_state), _ptr(o),
@@ -200,5 +266,64 @@ def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, o=None, stre
     st = lib.kda_decode_step(N, H, Dk, Dv, _dtype_code(q), KDA_F32, float(scale),
                              _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                              _ptr(o), _stream(stream))
+    _check(lib, st)
+    return o
+
+
+def kda_chunk_fwd_fused(q, k, v, gate_x, A_log, dt_bias, beta, *, normalize_qk: bool = True,
+                        o_gate=None, o_weight=None, o_eps: float = 1e-6, out_dtype=None,
+                        initial_state=None, output_final_state: bool = True, final_state=None,
+                        cu_seqlens=None, chunk: int = 64, scale: float = 1.0, o=None,
+                        stream=None, split: bool = True, workspace=None):
+    """Chunked KDA prefill with the layer's fused steps (C: kda_chunk_fwd_fused).
+
+    As ``kda_chunk_fwd``, but the log-decay comes from the gate's pre-activation:
+    gate_x (q's shape and dtype), A_log float32 [H], dt_bias float32 [H, Dk]; q and k may be
+    raw (``normalize_qk``); with ``o_gate`` (v's shape and dtype), ``o_weight`` float32 [Dv]
+    and ``o_eps`` the output is the gated RMSNorm of o, in ``out_dtype`` (float32 by
+    default, or torch.bfloat16). Returns (o or y, final_state or None).
+    """
+    import torch
+    lib = load_library()
+    B, T, N, H, Dk, Dv = _prefill_layout(q, k, v, beta, cu_seqlens)
+    fz = _fusion(q, k, gate_x, A_log, dt_bias, normalize_qk, o_gate, o_weight, o_eps, v)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    final_state = _prefill_states(q, N, H, Dk, Dv, initial_state, final_state, output_final_state)
+    o = _out(o, v, out_dtype)
+    workspace, ws = _prefill_workspace(lib, q, B, T, N, H, Dk, Dv, chunk, split, workspace)
+    st = lib.kda_chunk_fwd_fused(B, T, H, Dk, Dv, chunk, _dtype_code(q), _dtype_code(o),
+                                 float(scale), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(fz),
+                                 _ptr(beta), _ptr(initial_state), _ptr(final_state), _ptr(o),
+                                 _ptr(cu_seqlens), N, _ptr(workspace), ws, _stream(stream))
+    _check(lib, st)
+    return o, final_state
+
+
+def kda_decode_step_fused(q, k, v, gate_x, A_log, dt_bias, beta, state, *,
+                          normalize_qk: bool = True, o_gate=None, o_weight=None,
+                          o_eps: float = 1e-6, out_dtype=None, scale: float = 1.0, o=None,
+                          stream=None):
+    """One KDA decode step with the layer's fused steps (C: kda_decode_step_fused): inputs as
+    ``kda_decode_step`` with gate_x/A_log/dt_bias in place of g, optional raw q/k and optional
+    output norm (see ``kda_chunk_fwd_fused``). ``state`` is updated in place."""
+    import torch
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _req(t, nm, q.dtype)
+    _req(beta, "beta", torch.float32)
+    _req(state, "state", torch.float32)
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or tuple(v.shape) != (N, H, Dv) or tuple(beta.shape) != (N, H) or \
+            tuple(state.shape) != (N, H, Dk, Dv):
+        raise ValueError("inconsistent decode shapes")
+    fz = _fusion(q, k, gate_x, A_log, dt_bias, normalize_qk, o_gate, o_weight, o_eps, v)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    o = _out(o, v, out_dtype)
+    st = lib.kda_decode_step_fused(N, H, Dk, Dv, _dtype_code(q), _dtype_code(o), float(scale),
+                                   _ptr(q), _ptr(k), _ptr(v), ctypes.byref(fz), _ptr(beta),
+                                   _ptr(state), _ptr(o), _stream(stream))
     _check(lib, st)
     return o

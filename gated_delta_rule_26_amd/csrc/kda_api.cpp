@@ -113,7 +113,8 @@ kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv
     a.beta = beta;
     a.s0 = initial_state;
     a.s_out = final_state;
-    a.o = static_cast<float *>(o);
+    a.o = o;
+    a.f = kda::Fusion{};
     a.seg_len = 0;
     a.nseg = 1;
     a.ws_r = a.ws_x = a.ws_s = nullptr;
@@ -156,9 +157,146 @@ kda_status kda_decode_step(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
     a.g = g;
     a.beta = beta;
     a.state = state;
-    a.o = static_cast<float *>(o);
+    a.o = o;
+    a.f = kda::Fusion{};
     return hip_status(kda::launch_decode(in_dtype, Dk, Dv, a, static_cast<hipStream_t>(stream)),
                       "kda_decode_step launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks of a kda_fusion shared by both fused entry points; fills `f`.
+kda_status check_fusion(const kda_fusion *fusion, int32_t out_dtype, kda::Fusion &f) {
+    if (!fusion) return fail(KDA_ERR_INVALID_ARGUMENT, "fusion is required");
+    if (!fusion->gate_x || !fusion->A_log || !fusion->dt_bias)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "gate_x, A_log and dt_bias are required");
+    if (fusion->o_gate && !fusion->o_weight)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "o_weight is required with o_gate");
+    if (fusion->o_gate && !(fusion->o_eps >= 0.f && std::isfinite(fusion->o_eps)))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "o_eps must be finite and >= 0");
+    if (out_dtype == KDA_BF16 && !fusion->o_gate)
+        return fail(KDA_ERR_UNSUPPORTED, "bf16 o needs the output norm (o_gate)");
+    const void *ptrs[] = {fusion->gate_x, fusion->A_log, fusion->dt_bias, fusion->o_gate, fusion->o_weight};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    f.gx = fusion->gate_x;
+    f.A_log = fusion->A_log;
+    f.dt_bias = fusion->dt_bias;
+    f.norm_qk = fusion->normalize_qk ? 1 : 0;
+    f.og = fusion->o_gate;
+    f.ow = fusion->o_gate ? fusion->o_weight : nullptr;
+    f.oeps = fusion->o_gate ? fusion->o_eps : 0.f;
+    f.o_bf16 = out_dtype == KDA_BF16 ? 1 : 0;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd_fused(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                               int32_t in_dtype, int32_t out_dtype, float scale,
+                               const void *q, const void *k, const void *v,
+                               const kda_fusion *fusion, const float *beta,
+                               const float *initial_state, float *final_state, void *o,
+                               const int32_t *cu_seqlens, int32_t num_seqs,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || chunk < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive (B=%d T=%d H=%d Dk=%d Dv=%d chunk=%d)",
+                    B, T, H, Dk, Dv, chunk);
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype code (in=%d out=%d)", in_dtype, out_dtype);
+    if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (cu_seqlens) {
+        if (B != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens requires B == 1 (got B=%d)", B);
+        if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
+    } else if (num_seqs != B) {
+        return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs (%d) must equal B (%d) without cu_seqlens",
+                    num_seqs, B);
+    }
+    const int64_t tokens = (int64_t)B * T;
+    if (tokens * H * (Dk > Dv ? Dk : Dv) > ((int64_t)1 << 40))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "problem too large");
+    kda::Fusion f;
+    const kda_status fs = check_fusion(fusion, out_dtype, f);
+    if (fs != KDA_OK) return fs;
+    if (tokens > 0 && (!q || !k || !v || !beta || !o))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, beta and o are required");
+    const void *ptrs[] = {q, k, v, beta, initial_state, final_state, o, cu_seqlens, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    if (workspace_bytes > 0 && !workspace)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace_bytes > 0 with a NULL workspace");
+    if (!kda::chunk_fwd_fused_supported(in_dtype, chunk, Dk, Dv))
+        return fail(KDA_ERR_UNSUPPORTED, "no fused instantiation for in_dtype=%d chunk=%d Dk=%d Dv=%d",
+                    in_dtype, chunk, Dk, Dv);
+    if (num_seqs == 0) return ok();
+
+    kda::ChunkArgs a;
+    a.n_seqs = num_seqs;
+    a.seq_len = T;
+    a.cu_seqlens = cu_seqlens;
+    a.H = H;
+    a.scale = scale;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = nullptr;
+    a.beta = beta;
+    a.s0 = initial_state;
+    a.s_out = final_state;
+    a.o = o;
+    a.f = f;
+    a.seg_len = 0;
+    a.nseg = 1;
+    a.ws_r = a.ws_x = a.ws_s = nullptr;
+    a.rec = nullptr;
+    a.rec_chunks = 0;
+    a.order = nullptr;
+    return hip_status(kda::launch_chunk_fwd(in_dtype, chunk, Dk, Dv, a, workspace, workspace_bytes,
+                                            static_cast<hipStream_t>(stream)),
+                      "kda_chunk_fwd_fused launch");
+}
+
+kda_status kda_decode_step_fused(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
+                                 int32_t in_dtype, int32_t out_dtype, float scale,
+                                 const void *q, const void *k, const void *v,
+                                 const kda_fusion *fusion, const float *beta,
+                                 float *state, void *o, void *stream) {
+    if (N < 0 || H < 1 || Dk < 1 || Dv < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes (N=%d H=%d Dk=%d Dv=%d)", N, H, Dk, Dv);
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype code (in=%d out=%d)", in_dtype, out_dtype);
+    if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if ((int64_t)N * H > 0x7fffffff) return fail(KDA_ERR_INVALID_ARGUMENT, "N*H too large");
+    kda::Fusion f;
+    const kda_status fs = check_fusion(fusion, out_dtype, f);
+    if (fs != KDA_OK) return fs;
+    if (N > 0 && (!q || !k || !v || !beta || !state || !o))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, beta, state and o are required");
+    const void *ptrs[] = {q, k, v, beta, state, o};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    if (!kda::decode_supported(in_dtype, Dk, Dv))
+        return fail(KDA_ERR_UNSUPPORTED, "no decode instantiation for in_dtype=%d Dk=%d Dv=%d",
+                    in_dtype, Dk, Dv);
+    if (N == 0) return ok();
+    kda::DecodeArgs a;
+    a.N = N;
+    a.H = H;
+    a.scale = scale;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = nullptr;
+    a.beta = beta;
+    a.state = state;
+    a.o = o;
+    a.f = f;
+    return hip_status(kda::launch_decode(in_dtype, Dk, Dv, a, static_cast<hipStream_t>(stream)),
+                      "kda_decode_step_fused launch");
 }
 
 }  // extern "C"

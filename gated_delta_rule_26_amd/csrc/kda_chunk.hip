@@ -110,7 +110,10 @@ template <typename OP, int TSZ, int C, int DK, int DV, int NW> struct ChunkShape
     static constexpr int oDd = oYt + align16(DV * LDC * SZ);
     static constexpr int oGc = oDd + align16(NB * DK * 4);
     static constexpr int oBeta = oGc + align16(DK * 4);
-    static constexpr int BYTES = oBeta + align16(C * 4);
+    // fused q/k normalisation: per-token partial sums of squares [k, q][channel half][token]
+    static constexpr int oNrm = oBeta + align16(C * 4);
+    static constexpr int oGain = oNrm + align16(4 * C * 4);  // fused output norm gain [DV]
+    static constexpr int BYTES = oGain + align16(DV * 4);
 
     static_assert(C % 16 == 0 && C >= 16 && C <= 64, "chunk must be 16, 32, 48 or 64");
     static_assert(DK % 16 == 0 && DV % 16 == 0, "head dims must be multiples of 16");
@@ -240,7 +243,97 @@ template <typename OP> __device__ __forceinline__ f32x4 mm_tn(f32x4 x, f32x4 y) 
 // later segment from zero; no outputs are written; each chunk's record (W, the read-out and
 // state-update operands, U~) is stored for the replay passes, and the segment's final state
 // R_p goes to ws_r[p] (p < nseg-1).
-template <typename Tin, typename OP, int C, int DK, int DV, int NW, bool STORE>
+// ---- the output norm (the layer's o_norm: a gated RMSNorm with a sigmoid gate), fused into
+// the output store of a chunk. The waves stage their 16-column output tiles in LDS
+// (ostage_tile); after a barrier, 8 threads per row normalise and store whole rows
+// (onorm_rows), with 16-byte loads of the output gate and 16-byte stores.
+template <int C, int DV, int NW> struct ONorm {
+    static constexpr int LD = DV + 4;                 // staged row stride (floats), 16-byte rows
+    static constexpr int BYTES = C * LD * 4;
+    static constexpr int TPRW = 64 * NW / C;          // threads per row
+    static constexpr int CPT = DV / TPRW;             // columns per thread
+    static constexpr bool OK = CPT == 16 && (TPRW & (TPRW - 1)) == 0 && TPRW <= 64;
+};
+
+// Lane (lr, q) of a wave holds rows 16I + 4q + e of column 16 * wave + lr of the chunk's outputs.
+template <int C, int DV, int NW>
+__device__ __forceinline__ void ostage_tile(float *Ob, int I, f32x4 o) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lr = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Ob[(16 * I + 4 * q4 + e) * ONorm<C, DV, NW>::LD + 16 * wave + lr] = o[e];
+}
+
+// This thread's 16 output-gate pre-activations (bf16): row tid / TPRW, columns from
+// CPT * (tid % TPRW); zero past the chunk end.
+template <int C, int DV, int NW>
+__device__ __forceinline__ void load_ogate(const ChunkArgs &a, int64_t t0, int Lc, int h, u32x4 (&zr)[2]) {
+    using ON = ONorm<C, DV, NW>;
+    const int row = threadIdx.x / ON::TPRW, c0 = ON::CPT * (threadIdx.x % ON::TPRW);
+    zr[0] = zr[1] = u32x4{0u, 0u, 0u, 0u};
+    if (row < Lc) {
+        const uint16_t *p = static_cast<const uint16_t *>(a.f.og) + (t0 + row) * (int64_t)(a.H * DV) + h * DV + c0;
+        zr[0] = *reinterpret_cast<const u32x4 *>(p);
+        zr[1] = *reinterpret_cast<const u32x4 *>(p + 8);
+    }
+}
+
+// y = o / sqrt(mean of the row's Dv squares + eps) * gain * sigmoid(z), stored as float32 or
+// bf16 for rows < Lc. Ob: the staged outputs (complete: call after a barrier); gain: [DV]
+// in LDS.
+template <int C, int DV, int NW>
+__device__ __forceinline__ void onorm_rows(const ChunkArgs &a, const float *Ob, const float *gain,
+                                           const u32x4 (&zr)[2], int64_t t0, int Lc, int h) {
+    using ON = ONorm<C, DV, NW>;
+    static_assert(ON::OK, "row epilogue shape");
+    const int row = threadIdx.x / ON::TPRW, c0 = ON::CPT * (threadIdx.x % ON::TPRW);
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(Ob + row * ON::LD + c0 + 4 * i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * i + e] = v[e];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ss += x[i] * x[i];
+#pragma unroll
+    for (int m = 1; m < ON::TPRW; m <<= 1) ss += __shfl_xor(ss, m);
+    const float rs = rsqrt_or_zero(ss * (1.f / DV) + a.f.oeps);
+    float y[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 w = *reinterpret_cast<const f32x4 *>(gain + c0 + 4 * i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * i + e;
+            const uint32_t zb = zr[j >> 3][(j >> 1) & 3];
+            const float z = bf16_to_f32((uint16_t)((j & 1) ? zb >> 16 : zb & 0xffffu));
+            y[j] = x[j] * rs * w[e] * sigmoid_f(z);
+        }
+    }
+    if (row >= Lc) return;
+    const int64_t off = (t0 + row) * (int64_t)(a.H * DV) + h * DV + c0;
+    if (a.f.o_bf16) {
+        uint16_t *p = static_cast<uint16_t *>(a.o) + off;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            u32x4 pk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                pk[e] = (uint32_t)bf16_bits(y[8 * hf + 2 * e]) | ((uint32_t)bf16_bits(y[8 * hf + 2 * e + 1]) << 16);
+            *reinterpret_cast<u32x4 *>(p + 8 * hf) = pk;
+        }
+    } else {
+        float *p = static_cast<float *>(a.o) + off;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<f32x4 *>(p + 4 * i) = f32x4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
+    }
+}
+
+// FUSE bit 0 (FIN): the gate comes from its pre-activation (a.f.gx) and q, k are normalised
+// in-kernel when a.f.norm_qk; bit 1 (FOUT): the outputs pass the gated RMSNorm (a.f.og).
+template <typename Tin, typename OP, int C, int DK, int DV, int NW, bool STORE, int FUSE>
 __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     using Sh = ChunkShape<OP, (int)sizeof(Tin), C, DK, DV, NW>;
     using MM = Mma<OP>;
@@ -250,6 +343,13 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     constexpr int NB = Sh::NB, LDK = Sh::LDK, LDC = Sh::LDC, KT = Sh::KT,
                   CPW = Sh::CPW, KS = ST::KS, TPS = ST::TPS;
     constexpr bool kBalance = std::is_same<OP, _Float16>::value;  // fp16 range balancing
+    constexpr bool FIN = (FUSE & 1) != 0, FOUT = (FUSE & 2) != 0 && !STORE;
+    // the fused steps assume one (block, channel pair) job per thread, the two 64-channel
+    // halves of a token in a pair of waves, and one value column tile per wave
+    static_assert(!FIN || (Sh::JPT == 1 && DK == 128 && 32 * NW == Sh::NEJ), "fused input shape");
+    static_assert(!FOUT || (Sh::NCT == NW && Sh::CPW == 1), "fused output shape");
+    // fused output norm: the outputs are staged over the A/M operands, dead from P4 on
+    static_assert(!FOUT || Sh::P_REUSE + ONorm<C, DV, NW>::BYTES <= Sh::P_END, "output staging");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Sh::BYTES];
     OP *const Lk = reinterpret_cast<OP *>(smem + Sh::oLk);
@@ -272,6 +372,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     Tin *const xK = reinterpret_cast<Tin *>(smem + Sh::oXK);
     Tin *const xQ = reinterpret_cast<Tin *>(smem + Sh::oXQ);
     float *const xP = reinterpret_cast<float *>(smem + Sh::oXP);
+    float *const nrm = reinterpret_cast<float *>(smem + Sh::oNrm);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, q4 = lane >> 4;
@@ -318,12 +419,22 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         jc[jj] = 2 * (lidx % (DK / 2));
         jok[jj] = jb[jj] < NB;
     }
+    // fused gate: the head's rate exp(A_log[h]) and the biases of this thread's two channels
+    float grate = 0.f, gb0 = 0.f, gb1 = 0.f;
+    if constexpr (FIN) {
+        grate = expf(a.f.A_log[h]);
+        gb0 = a.f.dt_bias[h * DK + jc[0]];
+        gb1 = a.f.dt_bias[h * DK + jc[0] + 1];
+    }
 
     // ---- state: this wave's column tiles (ct = wave + NW*j) of S (or X), float32
     // accumulator layout
     const bool owns = wave < Sh::NCT;
     const float *sinit = a.s0 ? a.s0 + sbase : nullptr;
     if (STORE && seg > 0) sinit = nullptr;
+    float *const Ob = reinterpret_cast<float *>(smem + Sh::P_REUSE);  // fused output staging
+    float *const sgain = reinterpret_cast<float *>(smem + Sh::oGain);
+    if (FOUT && tid < DV) sgain[tid] = a.f.ow[tid];  // read after the loop's first barrier
     f32x4 S[CPW][KT];
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
@@ -343,7 +454,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     // beta, and a 4-token x 4-column tile of v
     typename RW::type pk[Sh::JPT][8], pq[Sh::JPT][8];
     typename R4::type pv[Sh::VPT][4];
-    f32x2 pg[Sh::JPT][8];
+    // gate input: float32 log-decay, or (fused) its pre-activation in the input type
+    typename std::conditional<FIN, typename RW::type, f32x2>::type pg[Sh::JPT][8];
     float pbeta = 0.f;
     auto vjob = [&](int vv, int &tg, int &cg) {
         const int x = tid + vv * Sh::NT;
@@ -368,7 +480,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     auto prefetch = [&](int64_t t0, int Lc) {
         const rsrc_t rq = make_rsrc(qg + t0 * krow, (uint32_t)(Lc * krow * ESZ));
         const rsrc_t rk = make_rsrc(kg + t0 * krow, (uint32_t)(Lc * krow * ESZ));
-        const rsrc_t rg = make_rsrc(a.g + t0 * krow, (uint32_t)(Lc * krow * 4));
+        const rsrc_t rg = FIN ? make_rsrc(static_cast<const Tin *>(a.f.gx) + t0 * krow, (uint32_t)(Lc * krow * ESZ))
+                              : make_rsrc(a.g + t0 * krow, (uint32_t)(Lc * krow * 4));
         const rsrc_t rv = make_rsrc(vg + t0 * vrow, (uint32_t)(Lc * vrow * ESZ));
         const rsrc_t rb = make_rsrc(a.beta + t0 * H, (uint32_t)(Lc * H * 4));
 #pragma unroll
@@ -379,7 +492,10 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         for (int jj = 0; jj < Sh::JPT; ++jj) {
 #pragma unroll
             for (int ii = 0; ii < 8; ++ii) {
-                pg[jj][ii] = Raw2<float>::load(rg, ko[jj] * 4, ii * krow * 4);
+                if constexpr (FIN)
+                    pg[jj][ii] = RW::load(rg, ko[jj] * ESZ, ii * krow * ESZ);
+                else
+                    pg[jj][ii] = Raw2<float>::load(rg, ko[jj] * 4, ii * krow * 4);
                 pk[jj][ii] = RW::load(rk, ko[jj] * ESZ, ii * krow * ESZ);
                 pq[jj][ii] = RW::load(rq, ko[jj] * ESZ, ii * krow * ESZ);
             }
@@ -426,14 +542,33 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         // ---- P0: gates -> within-block decay products (prefix incl., suffix excl.)
         float al0[Sh::JPT][8], al1[Sh::JPT][8], sf0[Sh::JPT][8], sf1[Sh::JPT][8];
         float dk0[Sh::JPT], dk1[Sh::JPT];  // decay of the job's whole 16-token block
+        // per-token factors of this thread's 8 tokens: 1/||k|| and scale/||q|| (fused
+        // normalisation; otherwise 1 and scale), set after P0
+        float rk[8], rq[8];
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+            rk[ii] = 1.f;
+            rq[ii] = a.scale;
+        }
         // k and q of token ii of job jj (zero past the sequence end), from the prefetch registers
         auto kq = [&](int jj, int ii, float &k0, float &k1, float &q0, float &q1) {
             const f32x2 kk = RW::f32(pk[jj][ii]);
             const f32x2 qq = RW::f32(pq[jj][ii]);
-            k0 = kk.x;
-            k1 = kk.y;
-            q0 = qq.x * a.scale;
-            q1 = qq.y * a.scale;
+            k0 = kk.x * rk[ii];
+            k1 = kk.y * rk[ii];
+            q0 = qq.x * rq[ii];
+            q1 = qq.y * rq[ii];
+        };
+        // log-decay of token ii of job jj; fused: from the pre-activation, and g = 0 (no
+        // decay) for tokens past the sequence end
+        auto gval = [&](int jj, int ii) -> f32x2 {
+            if constexpr (FIN) {
+                if (16 * jb[jj] + 8 * hh + ii >= Lc) return f32x2{0.f, 0.f};
+                const f32x2 x = RW::f32(pg[jj][ii]);
+                return f32x2{-grate * softplus_f(x.x + gb0), -grate * softplus_f(x.y + gb1)};
+            } else {
+                return pg[jj][ii];
+            }
         };
         bool ext_local = false;
 #pragma unroll
@@ -441,8 +576,9 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             float h0 = 1.f, h1 = 1.f;
 #pragma unroll
             for (int ii = 0; ii < 8; ++ii) {
-                al0[jj][ii] = exp_gate<OP>(pg[jj][ii].x);
-                al1[jj][ii] = exp_gate<OP>(pg[jj][ii].y);
+                const f32x2 gg = gval(jj, ii);
+                al0[jj][ii] = exp_gate<OP>(gg.x);
+                al1[jj][ii] = exp_gate<OP>(gg.y);
             }
 #pragma unroll
             for (int ii = 7; ii >= 0; --ii) {  // exclusive suffix within this half
@@ -473,6 +609,36 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             ext_local |= jok[jj] && (dk0[jj] < extreme_block_decay<OP>() ||
                                      dk1[jj] < extreme_block_decay<OP>());
         }
+        if constexpr (FIN) {
+            if (a.f.norm_qk) {
+                // per-token sums of squares of k and q over this wave's 64 channels: a butterfly
+                // over the 16 lanes of each lane group leaves value bitrev4(lane & 15) in each
+                // lane, then the two 16-lane groups of the half-wave are added
+                float sq[16];
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) {
+                    const f32x2 kk = RW::f32(pk[0][ii]), qq = RW::f32(pq[0][ii]);
+                    sq[ii] = kk.x * kk.x + kk.y * kk.y;
+                    sq[8 + ii] = qq.x * qq.x + qq.y * qq.y;
+                }
+#pragma unroll
+                for (int m = 1, nh = 8; m < 16; m <<= 1, nh >>= 1) {
+                    const bool up = (lane & m) != 0;
+#pragma unroll
+                    for (int i = 0; i < nh; ++i) {
+                        const float send = up ? sq[i] : sq[i + nh], keep = up ? sq[i + nh] : sq[i];
+                        sq[i] = keep + __shfl_xor(send, m);
+                    }
+                }
+                sq[0] += __shfl_xor(sq[0], 16);
+                if (!(lane & 16)) {
+                    const int l = lane & 15;
+                    const int vi = ((l & 1) << 3) | ((l & 2) << 1) | ((l & 4) >> 1) | ((l & 8) >> 3);
+                    const int kind = vi >> 3, chalf = jc[0] >> 6;
+                    nrm[(2 * kind + chalf) * C + 16 * jb[0] + 8 * hh + (vi & 7)] = sq[0];
+                }
+            }
+        }
         if (tid < C) sbeta[tid] = pbeta;
 #pragma unroll
         for (int vv = 0; vv < Sh::VPT; ++vv) {  // v^T: 4 columns x 4 consecutive tokens per store
@@ -489,6 +655,25 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             }
         }
         const bool extreme = __syncthreads_or(ext_local);
+        // fused normalisation: the two channel halves' sums of each token
+        auto tok_rnorm = [&](int kind, int t) { return rsqrt_or_zero(nrm[2 * kind * C + t] + nrm[(2 * kind + 1) * C + t]); };
+        if constexpr (FIN) {
+            if (a.f.norm_qk) {
+                const int t = 16 * jb[0] + 8 * hh;
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const f32x4 k0 = *reinterpret_cast<const f32x4 *>(nrm + t + 4 * hf);
+                    const f32x4 k1 = *reinterpret_cast<const f32x4 *>(nrm + C + t + 4 * hf);
+                    const f32x4 q0 = *reinterpret_cast<const f32x4 *>(nrm + 2 * C + t + 4 * hf);
+                    const f32x4 q1 = *reinterpret_cast<const f32x4 *>(nrm + 3 * C + t + 4 * hf);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        rk[4 * hf + e] = rsqrt_or_zero(k0[e] + k1[e]);
+                        rq[4 * hf + e] = a.scale * rsqrt_or_zero(q0[e] + q1[e]);
+                    }
+                }
+            }
+        }
 
         // ---- extreme chunks: the diagonal 16x16 blocks of A and M pair by pair in float32
         // (as transposed tiles: lane (lr, q) holds row lr, columns 4q..4q+3),
@@ -504,8 +689,9 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 double c0s = 0.0, c1s = 0.0;
 #pragma unroll
                 for (int ii = 0; ii < 8; ++ii) {
-                    c0s += (double)pg[jj][ii].x;
-                    c1s += (double)pg[jj][ii].y;
+                    const f32x2 gg = gval(jj, ii);
+                    c0s += (double)gg.x;
+                    c1s += (double)gg.y;
                     G0[ii] = c0s;
                     G1[ii] = c1s;
                     const f32x2 kk = RW::f32(pk[jj][ii]);
@@ -578,11 +764,16 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                     }
                 }
                 const float bi = sbeta[16 * I + lr];
+                // raw k and q were staged: the fused normalisation scales row i and column j
+                const bool nq = FIN && a.f.norm_qk;
+                const float rki = nq ? tok_rnorm(0, 16 * I + lr) : 1.f;
+                const float rqi = nq ? tok_rnorm(1, 16 * I + lr) : 1.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int col = 4 * q4 + e;
-                    dAt[e] = lr > col ? bi * a4[e] : 0.f;
-                    dMt[e] = lr >= col ? a.scale * m4[e] : 0.f;
+                    const float rkj = nq ? tok_rnorm(0, 16 * I + col) : 1.f;
+                    dAt[e] = lr > col ? bi * a4[e] * rki * rkj : 0.f;
+                    dMt[e] = lr >= col ? a.scale * m4[e] * rqi * rkj : 0.f;
                 }
             }
             __syncthreads();  // the staging area is overwritten by the operands below
@@ -832,7 +1023,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
 
         // ---- P5: state pass, registers only: U = U~ - W S; O = Qg S + M U; S' = gC S + Kd^T U
         if (owns) {
-            const rsrc_t ro = make_rsrc(a.o + t0 * vrow, (uint32_t)(Lc * vrow * 4));
+            const rsrc_t ro = make_rsrc(static_cast<float *>(a.o) + t0 * vrow, (uint32_t)(Lc * vrow * 4));
 #pragma unroll
             for (int j = 0; j < CPW; ++j) {
                 const int cv = wave + NW * j;
@@ -852,9 +1043,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 typename ST::frag ufr[C / KS];
 #pragma unroll
                 for (int p = 0; p < C / KS; ++p) ufr[p] = ST::regs(&U[p * TPS]);
-#pragma unroll
-                for (int I = 0; I < NB; ++I) {
-                    if (STORE) break;  // split: the outputs come from the replay
+                auto o_tile = [&](int I) {
                     f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int p = 0; p < DK / KS; ++p)
@@ -862,6 +1051,16 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
                     for (int p = 0; p <= I / TPS; ++p)
                         ST::mma(o, ST::permuted(Mb + (16 * I + lr) * LDC, p * KS, q4), ufr[p]);
+                    return o;
+                };
+                if constexpr (FOUT) {
+#pragma unroll
+                    for (int I = 0; I < NB; ++I) ostage_tile<C, DV, NW>(Ob, I, o_tile(I));
+                }
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    if (STORE || FOUT) break;  // split: the outputs come from the replay
+                    const f32x4 o = o_tile(I);
                     // rows past the chunk end are dropped by the buffer bound
                     const int so = 16 * I * vrow * 4;
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.x), ro, oo, so, 0);
@@ -878,6 +1077,12 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                     S[j][r] = acc;
                 }
             }
+        }
+        if constexpr (FOUT) {
+            u32x4 zr[2];
+            load_ogate<C, DV, NW>(a, t0, Lc, h, zr);
+            __syncthreads();  // every wave's output tile is staged
+            onorm_rows<C, DV, NW>(a, Ob, sgain, zr, t0, Lc, h);
         }
     }
 
@@ -914,7 +1119,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
 //        the last segment, for p = 0 .. nseg-1.
 // The state pass is the forward kernel's: U = U~ - W S; O = Qg S + M U; S' = gC S + Kd^T U.
 // Each chunk's staged operands are loaded into registers one chunk ahead.
-template <typename OP, int C, int DK, int DV, int NW, bool XMODE>
+template <typename OP, int C, int DK, int DV, int NW, bool XMODE, bool FOUT = false>
 __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
     using Sh = ChunkShape<OP, 2, C, DK, DV, NW>;
     using Rc = Record<OP, C, DK, DV>;
@@ -923,6 +1128,7 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
     constexpr int NB = Sh::NB, LDK = Sh::LDK, LDC = Sh::LDC, KT = Sh::KT, CPW = Sh::CPW,
                   KS = ST::KS, TPS = ST::TPS, NT = 64 * NW, SZ = Rc::SZ;
     static_assert(DK == DV || !XMODE, "X lives in the state's column tiles");
+    static_assert(!FOUT || (!XMODE && Sh::NCT == NW && CPW == 1), "fused output shape");
     constexpr int WROW = DK * SZ, KROW = C * SZ, MROW = C * SZ;  // record row bytes
     // 16-byte pieces to stage: W, Qg, Kd^T, M (XMODE: W and Kd^T)
     constexpr int N16 = (XMODE ? Rc::oQ + (Rc::oM - Rc::oK) : Rc::OPS) / 16;
@@ -933,6 +1139,8 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
     __shared__ __attribute__((aligned(16))) OP Kl[DK * LDC];
     __shared__ __attribute__((aligned(16))) OP Ml[XMODE ? 8 : C * LDC];
     __shared__ __attribute__((aligned(16))) float gl[DK];
+    __shared__ __attribute__((aligned(16))) float Ob[FOUT ? C * ONorm<C, DV, NW>::LD : 4];  // output staging
+    __shared__ __attribute__((aligned(16))) float sgain[FOUT ? DV : 4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, q4 = lane >> 4;
@@ -949,6 +1157,7 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
     const int vrow = H * DV;
 
     const bool owns = wave < Sh::NCT;
+    if (FOUT && tid < DV) sgain[tid] = a.f.ow[tid];  // read after the loop's first barrier
     f32x4 S[CPW][KT];
     const float *sinit = XMODE ? nullptr : a.ws_s + ((int64_t)p * chains + chain) * DK * DV;
 #pragma unroll
@@ -1036,7 +1245,7 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
         const int64_t t0 = tok0 + (int64_t)ci * C;
         const int Lc = (int)((L - (int64_t)ci * C) < C ? (L - (int64_t)ci * C) : C);
         if (owns) {
-            const rsrc_t ro = make_rsrc(a.o + t0 * vrow, XMODE ? 0u : (uint32_t)(Lc * vrow * 4));
+            const rsrc_t ro = make_rsrc(static_cast<float *>(a.o) + t0 * vrow, XMODE ? 0u : (uint32_t)(Lc * vrow * 4));
 #pragma unroll
             for (int j = 0; j < CPW; ++j) {
                 const int cv = wave + NW * j;
@@ -1057,8 +1266,7 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int pp = 0; pp < C / KS; ++pp) ufr[pp] = ST::regs(&U[pp * TPS]);
                 if constexpr (!XMODE) {
-#pragma unroll
-                    for (int I = 0; I < NB; ++I) {
+                    auto o_tile = [&](int I) {
                         f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int pp = 0; pp < DK / KS; ++pp)
@@ -1066,6 +1274,16 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
 #pragma unroll
                         for (int pp = 0; pp <= I / TPS; ++pp)
                             ST::mma(o, ST::permuted(Ml + (16 * I + lr) * LDC, pp * KS, q4), ufr[pp]);
+                        return o;
+                    };
+                    if constexpr (FOUT) {
+#pragma unroll
+                        for (int I = 0; I < NB; ++I) ostage_tile<C, DV, NW>(Ob, I, o_tile(I));
+                    }
+#pragma unroll
+                    for (int I = 0; I < NB; ++I) {
+                        if (FOUT) break;
+                        const f32x4 o = o_tile(I);
                         const int so = 16 * I * vrow * 4;
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.x), ro, oo, so, 0);
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.y), ro, oo, so + vrow * 4, 0);
@@ -1082,6 +1300,12 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
                     S[j][r] = acc;
                 }
             }
+        }
+        if constexpr (FOUT) {
+            u32x4 zr[2];
+            load_ogate<C, DV, NW>(a, t0, Lc, h, zr);
+            __syncthreads();  // every wave's output tile is staged
+            onorm_rows<C, DV, NW>(a, Ob, sgain, zr, t0, Lc, h);
         }
     }
 
@@ -1158,18 +1382,20 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t *cu, int32_t N
     order[rank] = i;
 }
 
-template <typename Tin, typename OP, int C, int DK, int DV, int NW>
+// FIN: the fused input steps; FOUT (unsplit forward and output replay): the output norm.
+template <typename Tin, typename OP, int C, int DK, int DV, int NW, bool FIN, bool FOUT>
 hipError_t launch_t(const ChunkArgs &a, hipStream_t stream) {
     const int64_t chains = (int64_t)a.n_seqs * a.H;
     if (chains * (a.seg_len ? a.nseg : 1) > 0x7fffffff) return hipErrorInvalidValue;
+    constexpr int FUSE = (FIN ? 1 : 0) | (FOUT ? 2 : 0);
     if (!a.seg_len) {
-        hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NW, false>), dim3((unsigned)chains),
+        hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NW, false, FUSE>), dim3((unsigned)chains),
                            dim3(64 * NW), 0, stream, a);
         return hipGetLastError();
     }
     hipError_t e;
     if constexpr (DK == DV) {
-        hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NW, true>),
+        hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NW, true, FUSE & 1>),
                            dim3((unsigned)(chains * a.nseg)), dim3(64 * NW), 0, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (a.nseg > 2) {
@@ -1180,7 +1406,7 @@ hipError_t launch_t(const ChunkArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((split_combine_kernel<DK, DV>), dim3((unsigned)(chains * (DV / 16))),
                            dim3(256), 0, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((replay_kernel<OP, C, DK, DV, NW, false>),
+        hipLaunchKernelGGL((replay_kernel<OP, C, DK, DV, NW, false, FOUT>),
                            dim3((unsigned)(chains * a.nseg)), dim3(64 * NW), 0, stream, a);
         return hipGetLastError();
     } else {
@@ -1270,10 +1496,16 @@ size_t chunk_fwd_split_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_
     return plan_split(B, T, H, Dk, Dv, chunk, in_dtype).bytes;
 }
 
+bool chunk_fwd_fused_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv) {
+    return in_dtype == 1 && chunk == 64 && Dk == 128 && Dv == 128;
+}
+
 hipError_t launch_chunk_fwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv,
                             const ChunkArgs &args, void *workspace, size_t workspace_bytes,
                             hipStream_t stream) {
     if (!chunk_fwd_supported(in_dtype, chunk, Dk, Dv)) return hipErrorInvalidValue;
+    if ((args.f.gx || args.f.og) && !chunk_fwd_fused_supported(in_dtype, chunk, Dk, Dv)) return hipErrorInvalidValue;
+    if (args.f.og && !args.f.gx) return hipErrorInvalidValue;
     if (args.n_seqs == 0) return hipSuccess;
     ChunkArgs a = args;
     a.seg_len = 0;
@@ -1300,10 +1532,15 @@ hipError_t launch_chunk_fwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t
             a.rec_chunks = sp.seg_len / chunk;
         }
     }
-    if (in_dtype == 1) return launch_t<bf16_t, _Float16, 64, 128, 128, 8>(a, stream);
-    if (chunk == 16) return launch_t<float, float, 16, 16, 16, 4>(a, stream);
-    if (Dk == 32) return launch_t<float, float, 64, 32, 32, 4>(a, stream);
-    return launch_t<float, float, 64, 64, 64, 4>(a, stream);
+    if (in_dtype == 1) {
+        if (a.f.gx)
+            return a.f.og ? launch_t<bf16_t, _Float16, 64, 128, 128, 8, true, true>(a, stream)
+                          : launch_t<bf16_t, _Float16, 64, 128, 128, 8, true, false>(a, stream);
+        return launch_t<bf16_t, _Float16, 64, 128, 128, 8, false, false>(a, stream);
+    }
+    if (chunk == 16) return launch_t<float, float, 16, 16, 16, 4, false, false>(a, stream);
+    if (Dk == 32) return launch_t<float, float, 64, 32, 32, 4, false, false>(a, stream);
+    return launch_t<float, float, 64, 64, 64, 4, false, false>(a, stream);
 }
 
 }  // namespace kda

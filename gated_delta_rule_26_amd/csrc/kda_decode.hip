@@ -13,6 +13,11 @@
 // its Dk*Dv/NT values in registers between the read and the write. Both column reductions
 // (p and r) are finished in the same sweep with cross-lane shuffles and one LDS exchange
 // between waves, then the rank-1 update is applied to the values still in registers.
+//
+// Fused layer steps (kda_decode_step_fused): the gate from its pre-activation,
+// g = -exp(A_log[h]) softplus(x + dt_bias[h, c]); q and k normalised, which only rescales the
+// two reductions (p by 1/||k||, r by 1/||q||), q.k, and the rank-1 update; and the output's
+// gated RMSNorm over its Dv values, done by the threads that hold them.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -45,20 +50,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     __shared__ float sk[DK], sq[DK], sa[DK], sv[DV];
     __shared__ f32x4 red[Sh::NWAVE][2][TPR];
-    __shared__ float sqk;
+    __shared__ float sqk[3];  // scale q.k (normalised when fused), 1/||k||, 1/||q|| (or 1, 1)
 
     const int tid = threadIdx.x;
     const int64_t item = blockIdx.x;  // n * H + h
     const Tin *q = static_cast<const Tin *>(a.q) + item * DK;
     const Tin *k = static_cast<const Tin *>(a.k) + item * DK;
     const Tin *v = static_cast<const Tin *>(a.v) + item * DV;
-    const float *g = a.g + item * DK;
     float *S = a.state + item * (int64_t)(DK * DV);
+    const int h = (int)(item % a.H);
 
     for (int c = tid; c < DK; c += NT) {
         sk[c] = to_f32(k[c]);
         sq[c] = a.scale * to_f32(q[c]);
-        sa[c] = __expf(g[c]);
+        float gc;
+        if (a.f.gx)
+            gc = -expf(a.f.A_log[h]) *
+                 softplus_f(to_f32(static_cast<const Tin *>(a.f.gx)[item * DK + c]) + a.f.dt_bias[h * DK + c]);
+        else
+            gc = a.g[item * DK + c];
+        sa[c] = __expf(gc);
     }
     for (int j = tid; j < DV; j += NT) sv[j] = to_f32(v[j]);
     __syncthreads();
@@ -71,11 +82,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int p = 0; p < NPASS; ++p)
         s[p] = *reinterpret_cast<const f32x4 *>(S + (p * RPP + rr) * DV + 4 * cg);
 
-    if (wave == 0) {  // scale * (q . k), off the critical path of the state sweep
-        float acc = 0.f;
-        for (int c = lane; c < DK; c += 64) acc += sq[c] * sk[c];
-        for (int m = 32; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
-        if (lane == 0) sqk = acc;
+    if (wave == 0) {  // scale * (q . k) and the norms, off the critical path of the state sweep
+        float acc = 0.f, kk = 0.f, qq = 0.f;
+        for (int c = lane; c < DK; c += 64) {
+            acc += sq[c] * sk[c];
+            kk += sk[c] * sk[c];
+            qq += sq[c] * sq[c];
+        }
+        for (int m = 32; m > 0; m >>= 1) {
+            acc += __shfl_xor(acc, m);
+            kk += __shfl_xor(kk, m);
+            qq += __shfl_xor(qq, m);
+        }
+        if (lane == 0) {
+            // sq holds scale * q, so 1/||q|| = |scale| / ||sq|| (any scale, zero included)
+            const float rk = a.f.norm_qk ? rsqrt_or_zero(kk) : 1.f;
+            const float rq = a.f.norm_qk ? fabsf(a.scale) * rsqrt_or_zero(qq) : 1.f;
+            sqk[0] = acc * rk * rq;
+            sqk[1] = rk;
+            sqk[2] = rq;
+        }
     }
 
     f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
@@ -104,14 +130,38 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         R += red[w][1][cg];
     }
     const float b = a.beta[item];
+    const float rk = sqk[1], rq = sqk[2];
     f32x4 vv = {sv[4 * cg], sv[4 * cg + 1], sv[4 * cg + 2], sv[4 * cg + 3]};
-    const f32x4 u = b * (vv - P);
-    if (rr == 0) *reinterpret_cast<f32x4 *>(a.o + item * DV + 4 * cg) = R + sqk * u;
+    const f32x4 u = b * (vv - rk * P);
+    if (rr == 0) {
+        const f32x4 ov = rq * R + sqk[0] * u;
+        if (a.f.og) {  // gated RMSNorm over the Dv outputs, held by the TPR lanes of row 0
+            float ss = ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w;
+#pragma unroll
+            for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m);
+            const float r = rsqrt_or_zero(ss * (1.f / DV) + a.f.oeps);
+            const f32x4 z = load4(static_cast<const Tin *>(a.f.og) + item * DV + 4 * cg);
+            const f32x4 w = *reinterpret_cast<const f32x4 *>(a.f.ow + 4 * cg);
+            f32x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = ov[e] * r * w[e] * sigmoid_f(z[e]);
+            if (a.f.o_bf16) {
+                const u32x2 packed = {(uint32_t)bf16_bits(y.x) | ((uint32_t)bf16_bits(y.y) << 16),
+                                      (uint32_t)bf16_bits(y.z) | ((uint32_t)bf16_bits(y.w) << 16)};
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.o) + item * DV + 4 * cg) = packed;
+            } else {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(a.o) + item * DV + 4 * cg) = y;
+            }
+        } else {
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(a.o) + item * DV + 4 * cg) = ov;
+        }
+    }
 
+    const f32x4 uk = rk * u;  // the update writes the normalised key: k_raw (u / ||k||)^T
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
         const int r = p * RPP + rr;
-        *reinterpret_cast<f32x4 *>(S + r * DV + 4 * cg) = s[p] + sk[r] * u;
+        *reinterpret_cast<f32x4 *>(S + r * DV + 4 * cg) = s[p] + sk[r] * uk;
     }
 }
 

@@ -38,6 +38,18 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 // float32 -> bf16, round to nearest even (finite inputs).
 __device__ __forceinline__ __bf16 f32_to_bf16(float x) { return static_cast<__bf16>(x); }
 
+// Scalar helpers of the fused layer steps.
+// softplus(z) = log(1 + e^z) = max(z, 0) + log(1 + e^-|z|), finite for every finite z
+__device__ __forceinline__ float softplus_f(float z) {
+    return fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z)));
+}
+__device__ __forceinline__ float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
+// 1/sqrt(s) for s > 0, else 0 (a zero vector stays zero)
+__device__ __forceinline__ float rsqrt_or_zero(float s) { return s > 0.f ? __builtin_amdgcn_rsqf(s) : 0.f; }
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));  // round to nearest even
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
 

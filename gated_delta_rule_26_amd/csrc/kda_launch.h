@@ -6,6 +6,18 @@
 
 namespace kda {
 
+// The layer's steps fused into the kernels (kda_chunk_fwd_fused / kda_decode_step_fused).
+struct Fusion {
+    const void *gx;              // [tokens, H, Dk] in_dtype gate pre-activation (replaces g), or nullptr
+    const float *A_log;          // [H]     g = -exp(A_log[h]) * softplus(gx + dt_bias[h, c])
+    const float *dt_bias;        // [H, Dk]
+    int32_t norm_qk;             // q and k divided by their L2 norm per (token, head)
+    const void *og;              // [tokens, H, Dv] in_dtype output-gate pre-activation, or nullptr
+    const float *ow;             // [Dv] output norm gain
+    float oeps;                  // output norm epsilon
+    int32_t o_bf16;              // o is stored as bf16 (only with og)
+};
+
 struct ChunkArgs {
     int32_t n_seqs;              // number of sequences N
     int32_t seq_len;             // tokens per sequence when cu_seqlens == nullptr
@@ -17,7 +29,8 @@ struct ChunkArgs {
     const float *g, *beta;       // [tokens, H, Dk], [tokens, H]
     const float *s0;             // [N, H, Dk, Dv] or nullptr
     float *s_out;                // [N, H, Dk, Dv] or nullptr
-    float *o;                    // [tokens, H, Dv]
+    void *o;                     // [tokens, H, Dv] float32 (bf16 only with the output norm)
+    Fusion f;                    // the layer steps fused around the core (all null: none)
     // sequence split (fixed-length batches with few chains): each sequence is cut into nseg
     // segments of seg_len tokens (a multiple of the chunk); seg_len 0 = no split
     int32_t seg_len, nseg;
@@ -35,7 +48,8 @@ struct DecodeArgs {
     const void *q, *k, *v;
     const float *g, *beta;
     float *state;
-    float *o;
+    void *o;
+    Fusion f;
 };
 
 // Workspace bytes the sequence split needs for this problem on the current device (0: no
@@ -45,6 +59,7 @@ size_t chunk_fwd_split_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_
 
 // True if an instantiation exists for these parameters (in_dtype is a kda_dtype code).
 bool chunk_fwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv);
+bool chunk_fwd_fused_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv);
 bool decode_supported(int32_t in_dtype, int32_t Dk, int32_t Dv);
 
 // Enqueue the kernel on `stream`; returns the launch status (hipGetLastError).

@@ -23,7 +23,8 @@
  * for unit-norm keys ([KV-cache page] section 5: without L2-normalised q and k the state
  * blows up to NaN). The library does not normalise: callers pass normalised q and k.
  *
- * Two entry points do the work:
+ * Two entry points do the work, and two fused variants add the KDA layer's steps on
+ * either side of the core (kda_chunk_fwd_fused, kda_decode_step_fused, below):
  *   kda_chunk_fwd    prefill: the chunkwise-parallel form of the recurrence ([KV-cache page]
  *                    section 3: chunk_size 64; section 6: chunked parallel form with a WY
  *                    representation), over fixed-length batches or packed variable-length
@@ -155,6 +156,63 @@ kda_status kda_decode_step(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
                            const void *q, const void *k, const void *v,
                            const float *g, const float *beta,
                            float *state, void *o, void *stream);
+
+/*
+ * kda_fusion - the KDA layer's steps on either side of the core, done inside the kernels.
+ *
+ * Input side ([loading page] section 3: the KDA layer's gate parameters A_log, the decay
+ * rate, and dt_bias, a time-step bias; [KV-cache page] sections 3 and 5: q and k must be
+ * L2-normalised):
+ *   gate_x        [tokens, H, Dk] in_dtype, the forget gate's pre-activation (required):
+ *                 g = -exp(A_log[h]) * softplus(gate_x + dt_bias[h, c]) replaces the g input
+ *   A_log         [H] float32 (required)
+ *   dt_bias       [H, Dk] float32 (required)
+ *   normalize_qk  nonzero: q and k are divided by their L2 norm per (token, head) (a zero
+ *                 vector stays zero); zero: q and k are used as given
+ * Output side ([loading page] section 3: o_norm, a gated RMSNorm with a sigmoid gate):
+ *   o_gate        [tokens, H, Dv] in_dtype, the output gate's pre-activation, or NULL for
+ *                 the raw read-out o_t
+ *   o_weight      [Dv] float32 gain (required with o_gate)
+ *   o_eps         >= 0; with o_gate the output is, per (token, head),
+ *                 y = o / sqrt(mean(o^2) + o_eps) * o_weight * sigmoid(o_gate)
+ * Every pointer is a 16-byte aligned device pointer owned by the caller.
+ */
+typedef struct kda_fusion {
+    const void *gate_x;
+    const float *A_log;
+    const float *dt_bias;
+    int32_t normalize_qk;
+    const void *o_gate;
+    const float *o_weight;
+    float o_eps;
+} kda_fusion;
+
+/*
+ * kda_chunk_fwd_fused - kda_chunk_fwd with the fused layer steps: the gate from gate_x
+ * (no g argument), optional q/k normalisation, and optionally the output norm, written as
+ * float32 or bf16 (out_dtype KDA_BF16 requires o_gate). Every other argument, the
+ * workspace (kda_chunk_fwd_workspace_bytes), the sequence layout and the errors are those of
+ * kda_chunk_fwd; fusion == NULL or a NULL required field is KDA_ERR_INVALID_ARGUMENT.
+ * Compiled instantiation: (KDA_BF16, chunk 64, Dk = Dv = 128); others are UNSUPPORTED.
+ */
+kda_status kda_chunk_fwd_fused(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                               int32_t in_dtype, int32_t out_dtype, float scale,
+                               const void *q, const void *k, const void *v,
+                               const kda_fusion *fusion, const float *beta,
+                               const float *initial_state, float *final_state, void *o,
+                               const int32_t *cu_seqlens, int32_t num_seqs,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_decode_step_fused - kda_decode_step with the fused layer steps (gate from gate_x,
+ * optional q/k normalisation, optional output norm with float32 or bf16 output). Sizes,
+ * dtypes and errors as kda_decode_step.
+ */
+kda_status kda_decode_step_fused(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
+                                 int32_t in_dtype, int32_t out_dtype, float scale,
+                                 const void *q, const void *k, const void *v,
+                                 const kda_fusion *fusion, const float *beta,
+                                 float *state, void *o, void *stream);
 
 #ifdef __cplusplus
 }

@@ -116,3 +116,82 @@ def test_binding_fails_loudly_without_library(tmp_path):
 def test_binding_raises_kda_error_type():
     e = kda.KdaError(2, "no instantiation")
     assert e.status == 2 and "KDA_ERR_UNSUPPORTED" in str(e)
+
+
+# ------------------------------------------------------------------ fused entry points
+
+def fusion(gate_x=P, A_log=P, dt_bias=P, normalize_qk=1, o_gate=None, o_weight=None, o_eps=1e-6):
+    return kda._Fusion(gate_x.value if gate_x is not None else None,
+                       A_log.value if A_log is not None else None,
+                       dt_bias.value if dt_bias is not None else None, normalize_qk,
+                       o_gate.value if o_gate is not None else None,
+                       o_weight.value if o_weight is not None else None, o_eps)
+
+
+def chunk_fused(lib, B=1, T=64, H=2, Dk=128, Dv=128, C=64, ind=BF16, outd=F32, scale=1.0,
+                q=P, k=P, v=P, fz="default", beta=P, s0=None, s1=None, o=P, cu=None, N=None,
+                ws=None, wsb=0):
+    N = B if N is None else N
+    f = fusion() if fz == "default" else fz
+    fp = ctypes.byref(f) if f is not None else None
+    return lib.kda_chunk_fwd_fused(B, T, H, Dk, Dv, C, ind, outd, scale, q, k, v, fp, beta,
+                                   s0, s1, o, cu, N, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fz=None), INVALID), (dict(fz=fusion(gate_x=None)), INVALID),
+    (dict(fz=fusion(A_log=None)), INVALID), (dict(fz=fusion(dt_bias=None)), INVALID),
+    (dict(fz=fusion(o_gate=P)), INVALID),                                   # no o_weight
+    (dict(fz=fusion(o_gate=P, o_weight=P, o_eps=-1.0)), INVALID),
+    (dict(fz=fusion(o_gate=P, o_weight=P, o_eps=float("nan"))), INVALID),
+    (dict(fz=fusion(gate_x=MIS)), INVALID), (dict(fz=fusion(o_gate=MIS, o_weight=P)), INVALID),
+    (dict(q=None), INVALID), (dict(beta=None), INVALID), (dict(o=None), INVALID),
+    (dict(B=0), INVALID), (dict(B=2, N=1), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(outd=BF16), UNSUPPORTED),                     # bf16 output only after the norm
+    (dict(ind=F32, Dk=64, Dv=64), UNSUPPORTED), (dict(Dk=64, Dv=64), UNSUPPORTED),
+    (dict(C=16), UNSUPPORTED),
+])
+def test_chunk_fused_rejects_before_launch(lib, kw, status):
+    assert chunk_fused(lib, **kw) == status
+    assert len(lib.kda_last_error()) > 0
+
+
+def test_chunk_fused_empty_work_is_ok_without_launch(lib):
+    assert chunk_fused(lib, T=0, cu=P, N=0, q=None, k=None, v=None, beta=None, o=None) == OK
+    assert chunk_fused(lib, T=0, cu=P, N=0, q=None, k=None, v=None, beta=None, o=None,
+                       outd=BF16, fz=fusion(o_gate=P, o_weight=P)) == OK
+
+
+def decode_fused(lib, N=4, H=2, Dk=128, Dv=128, ind=BF16, outd=F32, scale=1.0, q=P, k=P, v=P,
+                 fz="default", beta=P, state=P, o=P):
+    f = fusion() if fz == "default" else fz
+    fp = ctypes.byref(f) if f is not None else None
+    return lib.kda_decode_step_fused(N, H, Dk, Dv, ind, outd, scale, q, k, v, fp, beta, state,
+                                     o, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fz=None), INVALID), (dict(fz=fusion(A_log=None)), INVALID),
+    (dict(fz=fusion(o_gate=P)), INVALID), (dict(state=None), INVALID),
+    (dict(N=-1), INVALID), (dict(q=MIS), INVALID),
+    (dict(outd=BF16), UNSUPPORTED), (dict(Dk=96, Dv=96), UNSUPPORTED),
+])
+def test_decode_fused_rejects_before_launch(lib, kw, status):
+    assert decode_fused(lib, **kw) == status
+    assert len(lib.kda_last_error()) > 0
+
+
+def test_decode_fused_zero_sequences_is_ok(lib):
+    assert decode_fused(lib, N=0, q=None, k=None, v=None, beta=None, state=None, o=None) == OK
+
+
+def test_fusion_struct_matches_the_header():
+    """The binding's ctypes mirror has the C layout of kda_fusion (offsets of a 64-bit ABI)."""
+    offs = {name: getattr(kda._Fusion, name).offset for name, _ in kda._Fusion._fields_}
+    assert offs == {"gate_x": 0, "A_log": 8, "dt_bias": 16, "normalize_qk": 24, "o_gate": 32,
+                    "o_weight": 40, "o_eps": 48}
+    assert ctypes.sizeof(kda._Fusion) == 56
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    body = re.search(r"typedef struct kda_fusion \{(.*?)\} kda_fusion;", src, re.S).group(1)
+    fields = re.findall(r"\b(\w+);", body)
+    assert fields == [n for n, _ in kda._Fusion._fields_]

@@ -1,0 +1,247 @@
+"""The fused layer steps on the GPU (kda_chunk_fwd_fused, kda_decode_step_fused) against the
+float64 oracle's composition (oracle.kda_fused_fwd): the gate from its pre-activation, q/k
+L2 normalisation, and the gated RMSNorm of the output.
+
+Tolerance, per returned tensor: max |gpu - oracle| <= 2e-2 * RMS(oracle) (bf16 inputs,
+float32 accumulation). A bf16 output also carries its own rounding, at most half a bf16 ulp
+(2^-8 relative), so there every element must satisfy
+|gpu - oracle| <= 2e-2 * RMS(oracle) * (1 + 2^-8) + 2^-8 * |oracle|.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import gated_delta_rule_26_amd as kda
+import oracle
+import synth
+from kda_testutil import assert_close, f64, note, oracle_threads, to_dev, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+TOL_F32 = 1e-4
+
+
+def fused_inputs(seed, T, H, D, stored="bf16", b_mu=-2.0, beta_mu=0.0, B=1):
+    w = synth.Workload(f"fused{seed}", 3000 + seed, H=H, K=D, V=D, chunk=64, dtype=stored,
+                       B=B, T=T, b_mu=b_mu, beta_mu=beta_mu)
+    return synth.make_inputs(w, fused=True)
+
+
+def run_oracle(x, stored, *, normalize_qk=True, onorm=False, scale=1.0, s0=None, cu=None):
+    return oracle.kda_fused_fwd(
+        f64(x["q"], stored), f64(x["k"], stored), f64(x["v"], stored), f64(x["x"], stored),
+        f64(x["A_log"]), f64(x["dt_bias"]), f64(x["beta"]), normalize_qk=normalize_qk,
+        o_gate=f64(x["z"], stored) if onorm else None, o_weight=f64(x["norm_weight"]),
+        o_eps=x["norm_eps"], scale=scale, initial_state=None if s0 is None else f64(s0),
+        cu_seqlens=cu, threads=oracle_threads())
+
+
+def gpu_fused(x, stored, *, B=1, s0=None, cu=None, scale=1.0, normalize_qk=True, onorm=False,
+              out_bf16=False, split=True, alias=False):
+    torch = torch_mod()
+    T = x["q"].shape[0] // B
+    sh = lambda a: a.reshape(B, T, *a.shape[1:]) if cu is None else a  # noqa: E731
+    q, k, v, gx, z = (to_dev(sh(x[n]), stored) for n in ("q", "k", "v", "x", "z"))
+    beta = to_dev(sh(x["beta"]))
+    A_log, dt_bias, w = to_dev(x["A_log"]), to_dev(x["dt_bias"]), to_dev(x["norm_weight"])
+    init = None if s0 is None else to_dev(np.ascontiguousarray(s0, dtype=np.float32))
+    cu_t = None if cu is None else to_dev(np.asarray(cu, dtype=np.int32))
+    o, S = kda.kda_chunk_fwd_fused(
+        q, k, v, gx, A_log, dt_bias, beta, normalize_qk=normalize_qk,
+        o_gate=z if onorm else None, o_weight=w if onorm else None, o_eps=x["norm_eps"],
+        out_dtype=torch.bfloat16 if out_bf16 else None, initial_state=init, cu_seqlens=cu_t,
+        scale=scale, split=split, final_state=init if alias else None)
+    torch.cuda.synchronize()
+    assert o.dtype == (torch.bfloat16 if out_bf16 else torch.float32)
+    return o.float().reshape(x["v"].shape).cpu().numpy(), S.cpu().numpy()
+
+
+def assert_close_out(got, ref, bf16_out: bool, what: str, tol: float = TOL):
+    """The tolerance above; for bf16 outputs the per-element rounding allowance too."""
+    if not bf16_out:
+        return assert_close(got, ref, tol, what)
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(got - ref)
+    bound = tol * rms * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref)
+    worst = float(np.max(err / bound)) if err.size else 0.0
+    print(f"[parity] {what}: max|err|/RMS = {float(np.max(err)) / rms:.3e}, "
+          f"max err/bound = {worst:.3f}", file=sys.stderr, flush=True)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    assert worst <= 1.0, f"{what}: error exceeds tol*RMS + 2^-8|ref| (ratio {worst:.3f})"
+
+
+ONORM = [("raw", False, False), ("norm_f32", True, False), ("norm_bf16", True, True)]
+
+
+# ------------------------------------------------------------------------------- prefill
+
+@pytest.mark.parametrize("mode,onorm,out_bf16", ONORM)
+@pytest.mark.parametrize("T", [1, 63, 64, 200, 1000])
+def test_fused_prefill_matches_oracle(T, mode, onorm, out_bf16):
+    """Raw q/k normalised in-kernel, the gate from its pre-activation, an initial state and a
+    query scale; ragged last chunks (the padding tokens must not decay the state)."""
+    H, D = 3, 128
+    x = fused_inputs(10 + T, T, H, D)
+    s0 = np.stack([np.stack([synth.initial_state(synth.WORKLOADS["varlen_64seq_h16"], T, h)
+                             for h in range(H)])])
+    note(f"fused prefill T={T} {mode}")
+    o, S = gpu_fused(x, "bf16", s0=s0, scale=0.37, onorm=onorm, out_bf16=out_bf16)
+    o_ref, S_ref = run_oracle(x, "bf16", onorm=onorm, scale=0.37, s0=s0)
+    assert_close_out(o, o_ref, out_bf16, f"o ({mode})")
+    assert_close(S, S_ref, TOL, "final state")
+
+
+@pytest.mark.parametrize("mode,onorm,out_bf16", ONORM)
+@pytest.mark.parametrize("B,T", [(1, 5000), (2, 8229)])
+def test_fused_split_matches_oracle_and_unsplit(B, T, mode, onorm, out_bf16):
+    """Few chains: the sequence split (store pass with the fused input steps, output replay
+    with the fused norm) against the oracle and against the unsplit launch."""
+    H, D = 2, 128
+    x = fused_inputs(20 + T, B * T, H, D, beta_mu=0.5)
+    q_probe = torch_mod().empty((B, T, H, D), dtype=torch_mod().bfloat16, device="cuda")
+    assert kda.chunk_fwd_workspace_bytes(q_probe, q_probe) > 0, "expected a split plan"
+    del q_probe
+    note(f"fused split B={B} T={T} {mode}")
+    o, S = gpu_fused(x, "bf16", B=B, onorm=onorm, out_bf16=out_bf16)
+    o1, S1 = gpu_fused(x, "bf16", B=B, onorm=onorm, out_bf16=out_bf16, split=False)
+    o_ref, S_ref = run_oracle(x, "bf16", onorm=onorm, cu=np.arange(B + 1) * T)
+    assert_close_out(o, o_ref, out_bf16, f"o split ({mode})")
+    assert_close(S, S_ref, TOL, "final state split")
+    assert_close_out(o1, o_ref, out_bf16, f"o unsplit ({mode})")
+    assert_close(S1, S_ref, TOL, "final state unsplit")
+
+
+def test_fused_packed_with_empty_sequences_and_aliasing():
+    """Packed sequences (run longest first) with zero-length ones, initial states aliased
+    with the final states, output norm in bf16."""
+    lens = [0, 700, 1, 64, 2100, 0, 333]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    H, D = 2, 128
+    x = fused_inputs(30, int(cu[-1]), H, D)
+    w = synth.WORKLOADS["varlen_64seq_h16"]
+    s0 = np.stack([np.stack([synth.initial_state(w, n, h) for h in range(H)])
+                   for n in range(len(lens))])
+    note("fused packed with empty sequences")
+    o, S = gpu_fused(x, "bf16", cu=cu, s0=s0, onorm=True, out_bf16=True, alias=True)
+    o_ref, S_ref = run_oracle(x, "bf16", onorm=True, cu=cu, s0=s0)
+    assert_close_out(o, o_ref, True, "o packed")
+    assert_close(S, S_ref, TOL, "final states packed")
+    assert np.array_equal(S[0], s0[0]) and np.array_equal(S[5], s0[5]), "empty sequences keep S0"
+
+
+def test_fused_without_qk_norm_uses_given_vectors():
+    """normalize_qk off: q and k are used as given (here already unit-norm)."""
+    T, H, D = 700, 2, 128
+    x = fused_inputs(40, T, H, D)
+    core = synth.make_inputs(synth.Workload("fused40core", 3040, H=H, K=D, V=D, chunk=64,
+                                            dtype="bf16", B=1, T=T))
+    x["q"], x["k"] = core["q"], core["k"]
+    note("fused prefill, normalize_qk off")
+    o, S = gpu_fused(x, "bf16", normalize_qk=False, onorm=True)
+    o_ref, S_ref = run_oracle(x, "bf16", normalize_qk=False, onorm=True)
+    assert_close(o, o_ref, TOL, "o")
+    assert_close(S, S_ref, TOL, "final state")
+
+
+@pytest.mark.parametrize("A_log,b_mu", [(0.0, 2.0), (1.5, 4.0), (3.0, 8.0)])
+def test_fused_strong_gates(A_log, b_mu):
+    """Strong decay from the fused gate (per-token g down to about -e^A_log (b_mu + 3)): the
+    chunks whose 16-token decay underflows take the pair-by-pair diagonal path, whose sums
+    use the raw k and q and apply the normalisation afterwards."""
+    T, H, D = 600, 2, 128
+    x = fused_inputs(50 + int(b_mu), T, H, D, b_mu=b_mu)
+    x["A_log"][:] = np.float32(A_log)
+    s0 = np.stack([np.stack([synth.initial_state(synth.WORKLOADS["varlen_64seq_h16"], 7, h)
+                             for h in range(H)])])
+    note(f"fused strong gates A_log={A_log} b_mu={b_mu}")
+    o, S = gpu_fused(x, "bf16", s0=s0, onorm=True)
+    o_ref, S_ref = run_oracle(x, "bf16", onorm=True, s0=s0)
+    assert_close(o, o_ref, TOL, "o")
+    assert_close(S, S_ref, TOL, "final state")
+
+
+def test_fused_zero_query_and_key_tokens():
+    """Tokens whose raw q or k is zero stay zero after the normalisation (no NaN)."""
+    T, H, D = 300, 2, 128
+    x = fused_inputs(60, T, H, D)
+    x["k"][[0, 17, 64, 65, 299]] = 0
+    x["q"][[3, 17, 128, 200]] = 0
+    note("fused zero q/k tokens")
+    o, S = gpu_fused(x, "bf16", onorm=True)
+    o_ref, S_ref = run_oracle(x, "bf16", onorm=True)
+    assert_close(o, o_ref, TOL, "o")
+    assert_close(S, S_ref, TOL, "final state")
+
+
+# -------------------------------------------------------------------------------- decode
+
+def gpu_decode_fused(x, stored, s0, steps, N, *, onorm, out_bf16, normalize_qk=True):
+    torch = torch_mod()
+    H = x["q"].shape[1]
+    state = to_dev(np.ascontiguousarray(s0, dtype=np.float32))
+    A_log, dt_bias, w = to_dev(x["A_log"]), to_dev(x["dt_bias"]), to_dev(x["norm_weight"])
+    outs = []
+    for s in range(steps):
+        rows = slice(s * N, (s + 1) * N)  # step s: tokens s*N .. s*N+N-1, one per sequence
+        q, k, v, gx, z = (to_dev(x[n][rows], stored) for n in ("q", "k", "v", "x", "z"))
+        beta = to_dev(x["beta"][rows])
+        o = kda.kda_decode_step_fused(q, k, v, gx, A_log, dt_bias, beta, state,
+                                      normalize_qk=normalize_qk, o_gate=z if onorm else None,
+                                      o_weight=w if onorm else None, o_eps=x["norm_eps"],
+                                      out_dtype=torch.bfloat16 if out_bf16 else None, scale=0.5)
+        outs.append(o.float().cpu().numpy())
+    torch.cuda.synchronize()
+    return np.stack(outs), state.cpu().numpy()
+
+
+@pytest.mark.parametrize("mode,onorm,out_bf16", ONORM)
+@pytest.mark.parametrize("stored", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+def test_fused_decode_steps(D, stored, mode, onorm, out_bf16):
+    N, H, steps = 4, 3, 6
+    x = fused_inputs(70 + D, N * steps, H, D, stored=stored)
+    w = synth.WORKLOADS["varlen_64seq_h16"].with_(K=D, V=D)
+    s0 = np.stack([np.stack([synth.initial_state(w, n, h) for h in range(H)]) for n in range(N)])
+    note(f"fused decode D={D} {stored} {mode}")
+    o, S = gpu_decode_fused(x, stored, s0, steps, N, onorm=onorm, out_bf16=out_bf16)
+    # the oracle: sequence n is tokens n, N + n, 2N + n, ...
+    order = np.arange(N * steps).reshape(steps, N).T.reshape(-1)
+    xs = {n: x[n][order] for n in ("q", "k", "v", "x", "z", "beta")}
+    xs.update({n: x[n] for n in ("A_log", "dt_bias", "norm_weight", "norm_eps")})
+    o_ref, S_ref = run_oracle(xs, stored, onorm=onorm, scale=0.5, s0=s0,
+                              cu=np.arange(N + 1) * steps)
+    o_ref = o_ref.reshape(N, steps, H, D).transpose(1, 0, 2, 3)
+    tol = TOL if stored == "bf16" or out_bf16 else TOL_F32
+    assert_close_out(o, o_ref, out_bf16, f"decode o ({mode})", tol=tol)
+    assert_close(S, S_ref, TOL if stored == "bf16" else TOL_F32, "decode state")
+
+
+def test_fused_prefill_then_decode_equals_prefill():
+    """A fused GPU prefill followed by fused GPU decode steps reproduces the oracle's single
+    prefill over the concatenated tokens (bf16 output with the norm)."""
+    torch = torch_mod()
+    P, steps, H, D = 450, 5, 2, 128
+    x = fused_inputs(80, P + steps, H, D)
+    pre = {n: x[n][:P] for n in ("q", "k", "v", "x", "z", "beta")}
+    pre.update({n: x[n] for n in ("A_log", "dt_bias", "norm_weight", "norm_eps")})
+    note("fused prefill then decode")
+    o_p, S = gpu_fused(pre, "bf16", onorm=True, out_bf16=True)
+    state = to_dev(S)
+    A_log, dt_bias, w = to_dev(x["A_log"]), to_dev(x["dt_bias"]), to_dev(x["norm_weight"])
+    outs = []
+    for t in range(P, P + steps):
+        q, k, v, gx, z = (to_dev(x[n][t:t + 1], "bf16") for n in ("q", "k", "v", "x", "z"))
+        o = kda.kda_decode_step_fused(q, k, v, gx, A_log, dt_bias, to_dev(x["beta"][t:t + 1]),
+                                      state, o_gate=z, o_weight=w, o_eps=x["norm_eps"],
+                                      out_dtype=torch.bfloat16)
+        outs.append(o.float().cpu().numpy()[0])
+    torch.cuda.synchronize()
+    o_ref, S_ref = run_oracle(x, "bf16", onorm=True)
+    assert_close_out(o_p, o_ref[:P], True, "prefill part")
+    assert_close_out(np.stack(outs), o_ref[P:], True, "decode part")
+    assert_close(state.cpu().numpy(), S_ref, TOL, "state after decode")

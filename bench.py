@@ -59,6 +59,19 @@ def prefill_flops_per_token_head(K: int, V: int, C: int) -> float:
     return (3 * C * C * K + 2 * C * C * V + 6 * C * K * V + C ** 3 / 3) / C
 
 
+def fused_prefill_bytes_per_token_head(K: int, V: int) -> int:
+    """Algorithmic HBM bytes per (token, head) of the fused prefill: bf16 raw q and k, bf16 v,
+    the gate's bf16 pre-activation, float32 beta, the output gate's bf16 pre-activation and
+    the bf16 normalised output."""
+    return 2 * K * 2 + V * 2 + K * 2 + 4 + V * 2 + V * 2
+
+
+def fused_decode_bytes_per_step(N: int, H: int, K: int, V: int) -> int:
+    """State read + write (float32) plus bf16 q, k, v, gate and output-gate pre-activations,
+    float32 beta and the bf16 output per (sequence, head)."""
+    return 2 * N * H * K * V * 4 + N * H * (2 * K * 2 + V * 2 + K * 2 + 4 + V * 2) + N * H * V * 2
+
+
 def decode_bytes_per_step(N: int, H: int, K: int, V: int) -> int:
     """State read + write (float32) plus one bf16 q, k, v, float32 g, beta and float32 o per
     (sequence, head)."""
@@ -152,9 +165,11 @@ def write_traffic(fetch_csv: str, write_csv: str) -> None:
     print(json.dumps(res, indent=1))
 
 
-def other_workloads(kda, synth, to_dev, torch, np, log) -> dict:
-    """Prefill tokens/s on the 4K-token and the packed variable-length workloads, and the
-    device's copy bandwidth as a practical HBM reference (events on the current stream)."""
+def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
+    """Prefill tokens/s on the 4K-token and the packed variable-length workloads, the fused
+    layer steps on the long-context prefill and on the decode step (``state``: the decode
+    workload's states), and the device's copy bandwidth as a practical HBM reference (events
+    on the current stream)."""
     out = {}
 
     def timed(fn, reps):
@@ -196,6 +211,76 @@ def other_workloads(kda, synth, to_dev, torch, np, log) -> dict:
                                "order": "longest first"}
     del q, k, v, g, b, s0, cu, ws, x
     log("timed varlen_64seq_h16")
+
+    # fused layer steps, long-context prefill shape: raw q/k normalised in-kernel, the gate
+    # from its bf16 pre-activation, the gated RMSNorm of the output written as bf16
+    w = synth.WORKLOADS["prefill_128k_h32"]
+    x = synth.make_inputs(w, fused=True)
+    q, k, v, gx, z = (to_dev(x[n][None], True) for n in ("q", "k", "v", "x", "z"))
+    b = to_dev(x["beta"][None])
+    A, dtb, wt = to_dev(x["A_log"]), to_dev(x["dt_bias"]), to_dev(x["norm_weight"])
+    y = torch.empty((1, w.T, w.H, w.V), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((1, w.H, w.K, w.V), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(kda.chunk_fwd_workspace_bytes(q, v), 1), dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: kda.kda_chunk_fwd_fused(q, k, v, gx, A, dtb, b, o_gate=z, o_weight=wt,
+                                               o_eps=x["norm_eps"], out_dtype=torch.bfloat16,
+                                               final_state=S, o=y, workspace=ws), 10)
+    fb = w.T * w.H * fused_prefill_bytes_per_token_head(w.K, w.V) + w.H * w.K * w.V * 4
+    out["prefill_128k_h32_fused"] = {
+        "ms": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+        "algorithmic_gbs": round(fb / (ms * 1e-3) / 1e9, 1),
+        "frac_hbm": round(fb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes_per_token_head": fused_prefill_bytes_per_token_head(w.K, w.V),
+        "steps": "gate from bf16 pre-activation, q/k L2 norm, gated RMSNorm, bf16 output"}
+    del q, k, v, gx, z, b, y, S, ws, x
+    log("timed prefill_128k_h32_fused")
+
+    # decode steps back to back on the decode workload's states (one token per sequence and
+    # head per step): the core step, then the fused one. The headline decode figure
+    # alternates with the prefill instead, which leaves no dirty state lines in the caches.
+    N, H = state.shape[0], state.shape[1]
+    wd = synth.WORKLOADS["decode_256x32"].with_(prefill_T=0, decode_steps=8)
+    x = synth.make_inputs(wd, seqs=range(N))
+    dq, dk, dv = (to_dev(x["dec_" + n], True) for n in ("q", "k", "v"))
+    dg, db = to_dev(x["dec_g"]), to_dev(x["dec_beta"])
+    od = torch.empty((N, H, wd.V), dtype=torch.float32, device="cuda")
+    it = iter(range(1 << 30))
+
+    def cstep():
+        i = next(it) % wd.decode_steps
+        kda.kda_decode_step(dq[i], dk[i], dv[i], dg[i], db[i], state, o=od)
+    us = timed(cstep, 50) * 1e3
+    cb = decode_bytes_per_step(N, H, wd.K, wd.V)
+    out["decode_256x32_back_to_back"] = {
+        "avg_launch_us": round(us, 2), "steps_per_s": round(1e6 / us, 1),
+        "achieved_gbs": round(cb / (us * 1e-6) / 1e9, 1),
+        "frac_hbm": round(cb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": cb}
+    del dq, dk, dv, dg, db, od, x
+    log("timed decode_256x32 back to back")
+
+    x = synth.make_inputs(wd, seqs=range(N), fused=True)
+    dq, dk, dv, dgx, dz = (to_dev(x["dec_" + n], True) for n in ("q", "k", "v", "x", "z"))
+    db = to_dev(x["dec_beta"])
+    A, dtb, wt = to_dev(x["A_log"]), to_dev(x["dt_bias"]), to_dev(x["norm_weight"])
+    yd = torch.empty((N, H, wd.V), dtype=torch.bfloat16, device="cuda")
+    it = iter(range(1 << 30))
+
+    def dstep():
+        i = next(it) % wd.decode_steps
+        kda.kda_decode_step_fused(dq[i], dk[i], dv[i], dgx[i], A, dtb, db[i], state, o_gate=dz[i],
+                                  o_weight=wt, o_eps=x["norm_eps"], out_dtype=torch.bfloat16,
+                                  o=yd)
+    us = timed(dstep, 50) * 1e3
+    db_ = fused_decode_bytes_per_step(N, H, wd.K, wd.V)
+    out["decode_256x32_fused"] = {
+        "avg_launch_us": round(us, 2), "steps_per_s": round(1e6 / us, 1),
+        "achieved_gbs": round(db_ / (us * 1e-6) / 1e9, 1),
+        "frac_hbm": round(db_ / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": db_,
+        "steps": "gate from bf16 pre-activation, q/k L2 norm, gated RMSNorm, bf16 output"}
+    del dq, dk, dv, dgx, dz, db, yd, x
+    log("timed decode_256x32_fused")
 
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
     dst = torch.empty_like(src)
@@ -391,7 +476,7 @@ def main():
     }
     if not args.no_extra:
         del pq, pk, pv, pg, pb, po, pws, tq, tk, tv, tg, tb
-        res["other_workloads"] = other_workloads(kda, synth, to_dev, torch, np, log)
+        res["other_workloads"] = other_workloads(kda, synth, to_dev, torch, np, log, state)
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(xp, min(args.cpu_sample_tokens, T))

@@ -296,8 +296,10 @@ __device__ __forceinline__ void onorm_rows(const ChunkArgs &a, const float *Ob, 
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) ss += x[i] * x[i];
-#pragma unroll
-    for (int m = 1; m < ON::TPRW; m <<= 1) ss += __shfl_xor(ss, m);
+    static_assert(ON::TPRW == 8, "row sums over 8 lanes");
+    ss += lane_xor<1>(ss);
+    ss += lane_xor<2>(ss);
+    ss += lane_xor<4>(ss);
     const float rs = rsqrt_or_zero(ss * (1.f / DV) + a.f.oeps);
     float y[16];
 #pragma unroll
@@ -621,15 +623,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                     sq[ii] = kk.x * kk.x + kk.y * kk.y;
                     sq[8 + ii] = qq.x * qq.x + qq.y * qq.y;
                 }
-#pragma unroll
-                for (int m = 1, nh = 8; m < 16; m <<= 1, nh >>= 1) {
-                    const bool up = (lane & m) != 0;
-#pragma unroll
-                    for (int i = 0; i < nh; ++i) {
-                        const float send = up ? sq[i] : sq[i + nh], keep = up ? sq[i + nh] : sq[i];
-                        sq[i] = keep + __shfl_xor(send, m);
-                    }
-                }
+                row_transpose_sum16(sq);
                 sq[0] += __shfl_xor(sq[0], 16);
                 if (!(lane & 16)) {
                     const int l = lane & 15;
@@ -655,25 +649,28 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             }
         }
         const bool extreme = __syncthreads_or(ext_local);
-        // fused normalisation: the two channel halves' sums of each token
+        // fused normalisation: 1/||.|| of token t from the two channel halves' sums
         auto tok_rnorm = [&](int kind, int t) { return rsqrt_or_zero(nrm[2 * kind * C + t] + nrm[(2 * kind + 1) * C + t]); };
-        if constexpr (FIN) {
-            if (a.f.norm_qk) {
-                const int t = 16 * jb[0] + 8 * hh;
+        // this thread's 8 tokens' factors, read where P1 consumes them (short live range)
+        auto load_rnorm = [&]() {
+            if constexpr (FIN) {
+                if (a.f.norm_qk) {
+                    const int t = 16 * jb[0] + 8 * hh;
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const f32x4 k0 = *reinterpret_cast<const f32x4 *>(nrm + t + 4 * hf);
-                    const f32x4 k1 = *reinterpret_cast<const f32x4 *>(nrm + C + t + 4 * hf);
-                    const f32x4 q0 = *reinterpret_cast<const f32x4 *>(nrm + 2 * C + t + 4 * hf);
-                    const f32x4 q1 = *reinterpret_cast<const f32x4 *>(nrm + 3 * C + t + 4 * hf);
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const f32x4 k0 = *reinterpret_cast<const f32x4 *>(nrm + t + 4 * hf);
+                        const f32x4 k1 = *reinterpret_cast<const f32x4 *>(nrm + C + t + 4 * hf);
+                        const f32x4 q0 = *reinterpret_cast<const f32x4 *>(nrm + 2 * C + t + 4 * hf);
+                        const f32x4 q1 = *reinterpret_cast<const f32x4 *>(nrm + 3 * C + t + 4 * hf);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        rk[4 * hf + e] = rsqrt_or_zero(k0[e] + k1[e]);
-                        rq[4 * hf + e] = a.scale * rsqrt_or_zero(q0[e] + q1[e]);
+                        for (int e = 0; e < 4; ++e) {
+                            rk[4 * hf + e] = rsqrt_or_zero(k0[e] + k1[e]);
+                            rq[4 * hf + e] = a.scale * rsqrt_or_zero(q0[e] + q1[e]);
+                        }
                     }
                 }
             }
-        }
+        };
 
         // ---- extreme chunks: the diagonal 16x16 blocks of A and M pair by pair in float32
         // (as transposed tiles: lane (lr, q) holds row lr, columns 4q..4q+3),
@@ -795,6 +792,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 const int b = DK >= 64 ? __builtin_amdgcn_readfirstlane(jb[jj]) : jb[jj];
                 const int c0 = jc[jj];
                 float k0[8], k1[8], q0[8], q1[8];
+                load_rnorm();
 #pragma unroll
                 for (int ii = 0; ii < 8; ++ii) kq(jj, ii, k0[ii], k1[ii], q0[ii], q1[ii]);
                 float pre0 = 1.f, pre1 = 1.f, post0 = 1.f, post1 = 1.f;

@@ -49,6 +49,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     constexpr int TPR = Sh::TPR, RPP = Sh::RPP, NT = Sh::NT, NPASS = Sh::NPASS;
 
     __shared__ float sk[DK], sq[DK], sa[DK], sv[DV];
+    __shared__ __attribute__((aligned(16))) float sz[DV];  // fused output norm: gate pre-activation
+    __shared__ __attribute__((aligned(16))) float sw[DV];  // ... and gain
     __shared__ f32x4 red[Sh::NWAVE][2][TPR];
     __shared__ float sqk[3];  // scale q.k (normalised when fused), 1/||k||, 1/||q|| (or 1, 1)
 
@@ -71,7 +73,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             gc = a.g[item * DK + c];
         sa[c] = __expf(gc);
     }
-    for (int j = tid; j < DV; j += NT) sv[j] = to_f32(v[j]);
+    for (int j = tid; j < DV; j += NT) {
+        sv[j] = to_f32(v[j]);
+        if (a.f.og) {  // loaded with the token, not at the end of the step
+            sz[j] = to_f32(static_cast<const Tin *>(a.f.og)[item * DV + j]);
+            sw[j] = a.f.ow[j];
+        }
+    }
     __syncthreads();
 
     const int cg = tid % TPR, rr = tid / TPR;
@@ -140,8 +148,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m);
             const float r = rsqrt_or_zero(ss * (1.f / DV) + a.f.oeps);
-            const f32x4 z = load4(static_cast<const Tin *>(a.f.og) + item * DV + 4 * cg);
-            const f32x4 w = *reinterpret_cast<const f32x4 *>(a.f.ow + 4 * cg);
+            const f32x4 z = *reinterpret_cast<const f32x4 *>(sz + 4 * cg);
+            const f32x4 w = *reinterpret_cast<const f32x4 *>(sw + 4 * cg);
             f32x4 y;
 #pragma unroll
             for (int e = 0; e < 4; ++e) y[e] = ov[e] * r * w[e] * sigmoid_f(z[e]);

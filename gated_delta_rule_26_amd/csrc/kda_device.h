@@ -50,6 +50,41 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));  // round to nearest even
 }
 
+// The value of lane (lane ^ M) for M in {1, 2, 4, 8}: lanes of one 16-lane row exchange
+// through DPP moves, without the LDS crossbar. quad_perm swaps within quads (M = 1, 2);
+// row_shl:M reads lane + M and row_shr:M reads lane - M, picked by the lane's bit M.
+template <int M> __device__ __forceinline__ float lane_xor(float x) {
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8, "within a 16-lane row");
+    const int v = __float_as_int(x);
+    if constexpr (M == 1) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+    } else if constexpr (M == 2) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+    } else {
+        const int below = __builtin_amdgcn_update_dpp(0, v, 0x110 + M, 0xF, 0xF, false);  // row_shr:M
+        const int above = __builtin_amdgcn_update_dpp(0, v, 0x100 + M, 0xF, 0xF, false);  // row_shl:M
+        return __int_as_float((threadIdx.x & M) ? below : above);
+    }
+}
+
+// Transposing sum over the 16 lanes of each row: every lane holds 16 values; afterwards v[0] of
+// lane l is the row's sum of value index bitrev4(l & 15). Each step keeps one half of the
+// values and adds the partner lane's copy of that half.
+template <int M, int NH> __device__ __forceinline__ void bfly_step(float (&v)[16]) {
+    const bool up = (threadIdx.x & M) != 0;
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+        const float send = up ? v[i] : v[i + NH], keep = up ? v[i + NH] : v[i];
+        v[i] = keep + lane_xor<M>(send);
+    }
+}
+__device__ __forceinline__ void row_transpose_sum16(float (&v)[16]) {
+    bfly_step<1, 8>(v);
+    bfly_step<2, 4>(v);
+    bfly_step<4, 2>(v);
+    bfly_step<8, 1>(v);
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
 

@@ -59,6 +59,21 @@ def assert_close(got, ref, tol: float, what: str):
     return e
 
 
+def assert_close_bf16_out(got, ref, tol: float, what: str):
+    """For outputs stored as bf16: every element within tol * RMS(ref) * (1 + 2^-8) plus its
+    own rounding, half a bf16 ulp (at most 2^-8 |ref| relative)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(got - ref)
+    bound = tol * rms * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref)
+    worst = float(np.max(err / bound)) if err.size else 0.0
+    print(f"[parity] {what}: max|err|/RMS = {float(np.max(err)) / rms:.3e}, "
+          f"max err/bound = {worst:.3f}", file=sys.stderr, flush=True)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    assert worst <= 1.0, f"{what}: error exceeds tol*RMS + 2^-8|ref| (ratio {worst:.3f})"
+
+
 def oracle_threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 

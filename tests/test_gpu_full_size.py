@@ -12,7 +12,8 @@ import pytest
 
 import gated_delta_rule_26_amd as kda
 import synth
-from kda_testutil import assert_close, f64, note, oracle_threads, to_dev, torch_mod
+from kda_testutil import (assert_close, assert_close_bf16_out, f64, note, oracle_threads,
+                          to_dev, torch_mod)
 
 import oracle
 
@@ -51,6 +52,35 @@ def test_prefill_128k_h32_full_size():
     o_ref, S_ref = _oracle(xs, slice(None), None)
     assert_close(o_s, o_ref, TOL, "o (heads 0, 13, 31)")
     assert_close(S_s, S_ref[0], TOL, "final state (heads 0, 13, 31)")
+
+
+def test_prefill_128k_h32_fused_full_size():
+    """The fused layer steps at the long-context size, in the launch configuration the
+    benchmark times (split; raw q/k, the gate's pre-activation, bf16 normalised output);
+    heads 0 and 31 checked over the whole sequence against the oracle's composition."""
+    torch = torch_mod()
+    w = synth.WORKLOADS["prefill_128k_h32"]
+    x = synth.make_inputs(w, fused=True)
+    q, k, v, gx, z = (to_dev(x[n][None], "bf16") for n in ("q", "k", "v", "x", "z"))
+    beta = to_dev(x["beta"][None])
+    A, dtb, wt = to_dev(x["A_log"]), to_dev(x["dt_bias"]), to_dev(x["norm_weight"])
+    assert kda.chunk_fwd_workspace_bytes(q, v) > 0, "expected the sequence split"
+    note("prefill_128k_h32 fused full size")
+    y, S = kda.kda_chunk_fwd_fused(q, k, v, gx, A, dtb, beta, o_gate=z, o_weight=wt,
+                                   o_eps=x["norm_eps"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y.float()).all()), "non-finite outputs"
+    heads = [0, 31]
+    y_s = y[0][:, heads].float().cpu().numpy()
+    S_s = S[0, heads].cpu().numpy()
+    del q, k, v, gx, z, beta, y
+    st = lambda n: f64(x[n][:, heads], "bf16")  # noqa: E731
+    y_ref, S_ref = oracle.kda_fused_fwd(st("q"), st("k"), st("v"), st("x"), f64(x["A_log"][heads]),
+                                        f64(x["dt_bias"][heads]), f64(x["beta"][:, heads]),
+                                        o_gate=st("z"), o_weight=f64(x["norm_weight"]),
+                                        o_eps=x["norm_eps"], threads=oracle_threads())
+    assert_close_bf16_out(y_s, y_ref, TOL, "y (heads 0, 31)")
+    assert_close(S_s, S_ref[0], TOL, "final state (heads 0, 31)")
 
 
 def test_decode_256x32_full_size():

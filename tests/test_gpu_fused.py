@@ -8,15 +8,14 @@ float32 accumulation). A bf16 output also carries its own rounding, at most half
 |gpu - oracle| <= 2e-2 * RMS(oracle) * (1 + 2^-8) + 2^-8 * |oracle|.
 """
 
-import sys
-
 import numpy as np
 import pytest
 
 import gated_delta_rule_26_amd as kda
 import oracle
 import synth
-from kda_testutil import assert_close, f64, note, oracle_threads, to_dev, torch_mod
+from kda_testutil import (assert_close, assert_close_bf16_out, f64, note, oracle_threads,
+                          to_dev, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,19 +59,9 @@ def gpu_fused(x, stored, *, B=1, s0=None, cu=None, scale=1.0, normalize_qk=True,
 
 
 def assert_close_out(got, ref, bf16_out: bool, what: str, tol: float = TOL):
-    """The tolerance above; for bf16 outputs the per-element rounding allowance too."""
-    if not bf16_out:
-        return assert_close(got, ref, tol, what)
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    err = np.abs(got - ref)
-    bound = tol * rms * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref)
-    worst = float(np.max(err / bound)) if err.size else 0.0
-    print(f"[parity] {what}: max|err|/RMS = {float(np.max(err)) / rms:.3e}, "
-          f"max err/bound = {worst:.3f}", file=sys.stderr, flush=True)
-    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    assert worst <= 1.0, f"{what}: error exceeds tol*RMS + 2^-8|ref| (ratio {worst:.3f})"
+    if bf16_out:
+        return assert_close_bf16_out(got, ref, tol, what)
+    return assert_close(got, ref, tol, what)
 
 
 ONORM = [("raw", False, False), ("norm_f32", True, False), ("norm_bf16", True, True)]

@@ -104,13 +104,29 @@ def _counter_rows(path: str):
 
 
 def kernel_label(name: str) -> str:
-    """Readable label of a prefill kernel from its (possibly mangled) name."""
-    if "chunk_fwd_kernel" in name:
-        split = "true>" in name or "Lb1EEEv" in name
-        return "chunk_fwd_kernel (" + ("split forward, records" if split else "forward") + ")"
-    if "replay_kernel" in name:
-        x = "true>" in name or "Lb1EEEv" in name
-        return "replay_kernel (" + ("segment maps X" if x else "outputs") + ")"
+    """Readable label of a prefill kernel from its (possibly mangled) name: the split flag and
+    the fused steps come from the template arguments (chunk_fwd_kernel<..., STORE, FUSE>,
+    replay_kernel<..., XMODE, FOUT>)."""
+    import re
+    m = re.search(r"chunk_fwd_kernel<[^>]*?(true|false), (\d+)>", name) or \
+        re.search(r"chunk_fwd_kernel\w*?ELb(\d)ELi(\d)EEEv", name)
+    if m:
+        store = m.group(1) in ("true", "1")
+        fuse = int(m.group(2))
+        tag = "split forward, records" if store else "forward"
+        if fuse & 1:
+            tag += ", fused gate and q/k norm"
+        if fuse & 2:
+            tag += ", fused output norm"
+        return f"chunk_fwd_kernel ({tag})"
+    m = re.search(r"replay_kernel<[^>]*?(true|false), (true|false)>", name) or \
+        re.search(r"replay_kernel\w*?ELb(\d)ELb(\d)EEEv", name)
+    if m:
+        if m.group(1) in ("true", "1"):
+            return "replay_kernel (segment maps X)"
+        return "replay_kernel (outputs" + (", fused output norm)" if m.group(2) in ("true", "1") else ")")
+    if "replay_kernel" in name or "chunk_fwd_kernel" in name:
+        return name
     return "split_combine_kernel"
 
 

@@ -120,6 +120,7 @@ kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv
     a.ws_r = a.ws_x = a.ws_s = nullptr;
     a.rec = nullptr;
     a.rec_chunks = 0;
+    a.out_from = 0;
     a.order = nullptr;
     return hip_status(kda::launch_chunk_fwd(in_dtype, chunk, Dk, Dv, a, workspace, workspace_bytes,
                                             static_cast<hipStream_t>(stream)),
@@ -254,6 +255,7 @@ kda_status kda_chunk_fwd_fused(int32_t B, int32_t T, int32_t H, int32_t Dk, int3
     a.ws_r = a.ws_x = a.ws_s = nullptr;
     a.rec = nullptr;
     a.rec_chunks = 0;
+    a.out_from = 0;
     a.order = nullptr;
     return hip_status(kda::launch_chunk_fwd(in_dtype, chunk, Dk, Dv, a, workspace, workspace_bytes,
                                             static_cast<hipStream_t>(stream)),

@@ -345,7 +345,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     constexpr int NB = Sh::NB, LDK = Sh::LDK, LDC = Sh::LDC, KT = Sh::KT,
                   CPW = Sh::CPW, KS = ST::KS, TPS = ST::TPS;
     constexpr bool kBalance = std::is_same<OP, _Float16>::value;  // fp16 range balancing
-    constexpr bool FIN = (FUSE & 1) != 0, FOUT = (FUSE & 2) != 0 && !STORE;
+    constexpr bool FIN = (FUSE & 1) != 0, FOUT = (FUSE & 2) != 0;
     // the fused steps assume one (block, channel pair) job per thread, the two 64-channel
     // halves of a token in a pair of waves, and one value column tile per wave
     static_assert(!FIN || (Sh::JPT == 1 && DK == 128 && 32 * NW == Sh::NEJ), "fused input shape");
@@ -389,7 +389,10 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     const int segs = STORE ? a.nseg : 1;
     if ((int)blockIdx.x >= chains * segs) return;
     const int chain = blockIdx.x / segs, seg = blockIdx.x % segs;
-    constexpr bool store = STORE;
+    // split: the segments whose outputs come from the output replay (seg >= a.out_from)
+    // record their chunks' operands; segment 0 starts from the true initial state and, with
+    // out_from = 1, writes its outputs itself
+    const bool store = STORE && seg >= a.out_from;
     // packed batches run their sequences longest first when an order is given
     const int n = a.order ? a.order[chain / H] : chain / H, h = chain % H;
     int64_t tok0, L;
@@ -1052,12 +1055,14 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                     return o;
                 };
                 if constexpr (FOUT) {
+                    if (!store) {
 #pragma unroll
-                    for (int I = 0; I < NB; ++I) ostage_tile<C, DV, NW>(Ob, I, o_tile(I));
+                        for (int I = 0; I < NB; ++I) ostage_tile<C, DV, NW>(Ob, I, o_tile(I));
+                    }
                 }
 #pragma unroll
                 for (int I = 0; I < NB; ++I) {
-                    if (STORE || FOUT) break;  // split: the outputs come from the replay
+                    if (store || FOUT) break;  // recording segments: the outputs come from the replay
                     const f32x4 o = o_tile(I);
                     // rows past the chunk end are dropped by the buffer bound
                     const int so = 16 * I * vrow * 4;
@@ -1077,10 +1082,12 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             }
         }
         if constexpr (FOUT) {
-            u32x4 zr[2];
-            load_ogate<C, DV, NW>(a, t0, Lc, h, zr);
-            __syncthreads();  // every wave's output tile is staged
-            onorm_rows<C, DV, NW>(a, Ob, sgain, zr, t0, Lc, h);
+            if (!store) {  // uniform per workgroup
+                u32x4 zr[2];
+                load_ogate<C, DV, NW>(a, t0, Lc, h, zr);
+                __syncthreads();  // every wave's output tile is staged
+                onorm_rows<C, DV, NW>(a, Ob, sgain, zr, t0, Lc, h);
+            }
         }
     }
 
@@ -1114,7 +1121,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
 // XMODE: segment p's linear part X_p (state X = I, U~ = 0, no outputs) -> ws_x[p], for
 //        p = 1 .. nseg-2.
 // else:  segment p from its true start state S_p = ws_s[p]: outputs, and the final state of
-//        the last segment, for p = 0 .. nseg-1.
+//        the last segment, for p = out_from .. nseg-1 (with out_from = 1 segment 0 wrote its
+//        outputs in the forward).
 // The state pass is the forward kernel's: U = U~ - W S; O = Qg S + M U; S' = gC S + Kd^T U.
 // Each chunk's staged operands are loaded into registers one chunk ahead.
 template <typename OP, int C, int DK, int DV, int NW, bool XMODE, bool FOUT = false>
@@ -1143,9 +1151,11 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, q4 = lane >> 4;
     const int H = a.H, chains = a.n_seqs * H;
-    const int segs = XMODE ? a.nseg - 2 : a.nseg;
+    // segments 1 .. nseg-2 (X) or out_from .. nseg-1 (outputs)
+    const int first = XMODE ? 1 : a.out_from;
+    const int segs = XMODE ? a.nseg - 2 : a.nseg - a.out_from;
     if (segs <= 0 || (int)blockIdx.x >= chains * segs) return;
-    const int chain = blockIdx.x / segs, p = (XMODE ? 1 : 0) + (int)blockIdx.x % segs;
+    const int chain = blockIdx.x / segs, p = first + (int)blockIdx.x % segs;
     const int n = chain / H, h = chain % H;
     const int64_t tok0 = (int64_t)n * a.seq_len + (int64_t)p * a.seg_len;
     const int64_t rem = (int64_t)a.seq_len - (int64_t)p * a.seg_len;
@@ -1393,6 +1403,8 @@ hipError_t launch_t(const ChunkArgs &a, hipStream_t stream) {
     }
     hipError_t e;
     if constexpr (DK == DV) {
+        // with the output norm every segment's outputs come from the replay (its epilogue
+        // is hidden there behind the record reads); otherwise segment 0 writes its own
         hipLaunchKernelGGL((chunk_fwd_kernel<Tin, OP, C, DK, DV, NW, true, FUSE & 1>),
                            dim3((unsigned)(chains * a.nseg)), dim3(64 * NW), 0, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1405,7 +1417,7 @@ hipError_t launch_t(const ChunkArgs &a, hipStream_t stream) {
                            dim3(256), 0, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((replay_kernel<OP, C, DK, DV, NW, false, FOUT>),
-                           dim3((unsigned)(chains * a.nseg)), dim3(64 * NW), 0, stream, a);
+                           dim3((unsigned)(chains * (a.nseg - a.out_from))), dim3(64 * NW), 0, stream, a);
         return hipGetLastError();
     } else {
         return hipErrorInvalidValue;  // the split is planned only for Dk == Dv
@@ -1459,7 +1471,7 @@ SplitPlan plan_split(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, in
         const int64_t nseg = (nchunks + per - 1) / per;
         if (nseg < 2) continue;
         const double cost = rounds(chains * nseg) * per + rounds(chains * (nseg - 2)) * per * kXCost +
-                            rounds(chains * nseg) * per * kOutCost + kFixedCost + 0.25 * (nseg - 2);
+                            rounds(chains * (nseg - 1)) * per * kOutCost + kFixedCost + 0.25 * (nseg - 2);
         if (cost < (sp.nseg > 1 ? 0.98 : 0.9) * best) {  // a split must gain 10%; more segments 2%
             best = cost;
             sp.nseg = (int)nseg;
@@ -1528,6 +1540,7 @@ hipError_t launch_chunk_fwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t
             a.ws_s = a.ws_x + (size_t)(sp.nseg - 1) * chains * Dk * Dk;
             a.rec = reinterpret_cast<uint8_t *>(a.ws_s + (size_t)sp.nseg * chains * Dk * Dv);
             a.rec_chunks = sp.seg_len / chunk;
+            a.out_from = a.f.og ? 0 : 1;
         }
     }
     if (in_dtype == 1) {

@@ -88,12 +88,13 @@ int32_t kda_version(void);
  *
  * Fixed-length batches (num_seqs == B): with few (sequence, head) chains the recurrence
  * would occupy only a few compute units, so each sequence may be cut into segments. The
- * chunked forward runs all segments at once (segment 0 from the initial state, the others
- * from zero) and records each chunk's operands; a replay pass computes each segment's
- * linear state map from the records, the maps are chained into the true start state of
- * every segment, and a second replay pass produces the outputs and the final state. The
- * workspace holds the records, maps and states (about 74 KB per chunk and head for the bf16
- * instantiation, plus three states per segment).
+ * chunked forward runs all segments at once: segment 0 from the initial state (writing its
+ * outputs, except with the fused output norm), the others from zero, recording each chunk's
+ * operands. A replay pass computes each later segment's linear state map from the records,
+ * the maps are chained into the true start state of every segment, and a second replay pass
+ * produces the remaining outputs and the final state. The workspace holds the records, maps
+ * and states (about 74 KB per chunk and head for the bf16 instantiation, plus three states
+ * per segment).
  * Packed batches (cu_seqlens): num_seqs int32 for running the sequences longest first.
  * The workspace is optional: with less (or NULL) the call runs unsplit / in the given order,
  * with the same result up to rounding.

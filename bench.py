@@ -298,6 +298,44 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
     del dq, dk, dv, dgx, dz, db, yd, x
     log("timed decode_256x32_fused")
 
+    # the layer's short convolutions (SiLU) on the long-context shape: raw q, k and v
+    # projections, [131072, 32 * 128] bf16 each, one launch per tensor; and one decode update
+    # of the decode workload's 256 sequences over all three (12288 channels)
+    w = synth.WORKLOADS["prefill_128k_h32"]
+    x = synth.make_inputs(w, fused=True)
+    C = w.H * w.K
+    xs = [to_dev(x[n].reshape(1, w.T, C), True) for n in ("q", "k", "v")]
+    prm = [synth.conv_params(w, C, i) for i in range(3)]
+    ws_ = [(to_dev(a), to_dev(b)) for a, b in prm]
+    ys = [torch.empty_like(t) for t in xs]
+    fs = [torch.empty((1, 3, C), dtype=torch.bfloat16, device="cuda") for _ in xs]
+
+    def conv3():
+        for i in range(3):
+            kda.kda_short_conv_fwd(xs[i], ws_[i][0], ws_[i][1], final_state=fs[i], y=ys[i])
+    ms = timed(conv3, 10)
+    cb = 3 * w.T * C * (2 + 2)
+    out["short_conv_128k_h32"] = {
+        "ms": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+        "algorithmic_gbs": round(cb / (ms * 1e-3) / 1e9, 1),
+        "frac_hbm": round(cb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes": cb, "what": "q, k, v: 3 x [131072, 4096] bf16, width-4 depthwise causal conv + SiLU"}
+    del xs, ys, fs, ws_, x
+    log("timed short_conv_128k_h32")
+    N3 = 256
+    wd = synth.WORKLOADS["decode_256x32"]
+    C3 = 3 * wd.H * wd.K
+    xt = to_dev(synth.fused_slab(wd.with_(K=C3), 0, 0, N3)["q"], True)      # [256, 12288]
+    st = to_dev(synth.conv_state(wd, N3, C3), True)
+    cw, cbias = (to_dev(a) for a in synth.conv_params(wd, C3))
+    yt = torch.empty_like(xt)
+    us = timed(lambda: kda.kda_short_conv_update(xt, cw, cbias, st, y=yt), 50) * 1e3
+    ub = N3 * C3 * (2 + 2 + 2 * 3 * 2)
+    out["short_conv_update_256"] = {
+        "avg_launch_us": round(us, 2), "achieved_gbs": round(ub / (us * 1e-6) / 1e9, 1),
+        "bytes": ub, "what": "256 sequences x 12288 channels (q, k, v), state [3, C] bf16 in place"}
+    log("timed short_conv_update_256")
+
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
     dst = torch.empty_like(src)
     ms = timed(lambda: dst.copy_(src), 10)

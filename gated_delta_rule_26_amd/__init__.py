@@ -14,8 +14,8 @@ import ctypes
 import os
 
 __all__ = ["KdaError", "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_fused",
-           "kda_decode_step_fused", "chunk_fwd_workspace_bytes", "load_library", "KDA_F32",
-           "KDA_BF16"]
+           "kda_decode_step_fused", "kda_short_conv_fwd", "kda_short_conv_update",
+           "chunk_fwd_workspace_bytes", "load_library", "KDA_F32", "KDA_BF16"]
 
 KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
@@ -76,6 +76,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_decode_step_fused.restype = i32
     lib.kda_decode_step_fused.argtypes = [i32, i32, i32, i32, i32, i32, f32,
                                           vp, vp, vp, fp, vp, vp, vp]
+    lib.kda_short_conv_fwd.restype = i32
+    lib.kda_short_conv_fwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                       vp, i32, vp]
+    lib.kda_short_conv_update.restype = i32
+    lib.kda_short_conv_update.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     if path is None:
         _LIB = lib
     return lib
@@ -327,3 +332,70 @@ def kda_decode_step_fused(q, k, v, gate_x, A_log, dt_bias, beta, state, *,
                                    _ptr(state), _ptr(o), _stream(stream))
     _check(lib, st)
     return o
+
+
+_ACT = {None: 0, "none": 0, "silu": 1}
+
+
+def kda_short_conv_fwd(x, weight, bias=None, *, initial_state=None, final_state=None,
+                       output_final_state: bool = True, cu_seqlens=None, activation="silu",
+                       y=None, stream=None):
+    """The short causal convolution over a prefill batch (C: kda_short_conv_fwd).
+
+    x: [B, T, C] (or [T, C] with ``cu_seqlens``), bf16 or float32; weight: float32 [C, W]
+    (the last tap on the current token); bias: float32 [C] or None; initial_state: [N, W-1, C]
+    in x's dtype or None. Returns (y like x, final_state [N, W-1, C] or None); the final state
+    may be given as ``final_state`` (``initial_state`` itself for an in-place cache update).
+    """
+    import torch
+    lib = load_library()
+    _req(x, "x")
+    _req(weight, "weight", torch.float32)
+    if bias is not None:
+        _req(bias, "bias", torch.float32)
+    if cu_seqlens is not None:
+        _req(cu_seqlens, "cu_seqlens", torch.int32)
+        if x.dim() == 3 and x.shape[0] != 1:
+            raise ValueError("cu_seqlens requires B == 1")
+        B, T, N = 1, x.shape[-2], cu_seqlens.numel() - 1
+    else:
+        if x.dim() != 3:
+            raise ValueError("x must be [B, T, C] without cu_seqlens")
+        B, T, N = x.shape[0], x.shape[1], x.shape[0]
+    C, W = x.shape[-1], weight.shape[-1]
+    if tuple(weight.shape) != (C, W) or (bias is not None and tuple(bias.shape) != (C,)):
+        raise ValueError(f"weight must be [{C}, W] and bias [{C}]")
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None:
+            _req(t, nm, x.dtype)
+            if tuple(t.shape) != (N, W - 1, C):
+                raise ValueError(f"{nm} must be [{N}, {W - 1}, {C}]")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, W - 1, C), dtype=x.dtype, device=x.device)
+    y = _out(y, x, x.dtype, "y")
+    st = lib.kda_short_conv_fwd(B, T, C, W, _dtype_code(x), _ACT[activation], _ptr(x),
+                                _ptr(weight), _ptr(bias), _ptr(initial_state), _ptr(final_state),
+                                _ptr(y), _ptr(cu_seqlens), N, _stream(stream))
+    _check(lib, st)
+    return y, final_state
+
+
+def kda_short_conv_update(x, weight, bias, state, *, activation="silu", y=None, stream=None):
+    """One decode token per sequence (C: kda_short_conv_update): x [N, C]; state [N, W-1, C]
+    in x's dtype, shifted in place. Returns y like x."""
+    import torch
+    lib = load_library()
+    _req(x, "x")
+    _req(weight, "weight", torch.float32)
+    if bias is not None:
+        _req(bias, "bias", torch.float32)
+    _req(state, "state", x.dtype)
+    N, C = x.shape
+    W = weight.shape[-1]
+    if tuple(weight.shape) != (C, W) or tuple(state.shape) != (N, W - 1, C):
+        raise ValueError("inconsistent short-convolution shapes")
+    y = _out(y, x, x.dtype, "y")
+    st = lib.kda_short_conv_update(N, C, W, _dtype_code(x), _ACT[activation], _ptr(x),
+                                   _ptr(weight), _ptr(bias), _ptr(state), _ptr(y), _stream(stream))
+    _check(lib, st)
+    return y

@@ -302,3 +302,85 @@ kda_status kda_decode_step_fused(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
 }
 
 }  // extern "C"
+
+extern "C" {
+
+kda_status kda_short_conv_fwd(int32_t B, int32_t T, int32_t C, int32_t W, int32_t dtype,
+                              int32_t activation, const void *x, const float *weight,
+                              const float *bias, const void *initial_state, void *final_state,
+                              void *y, const int32_t *cu_seqlens, int32_t num_seqs, void *stream) {
+    if (B < 1 || T < 0 || C < 1 || W < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes (B=%d T=%d C=%d W=%d)", B, T, C, W);
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype code %d", dtype);
+    if (activation != KDA_ACT_NONE && activation != KDA_ACT_SILU)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown activation %d", activation);
+    if (cu_seqlens) {
+        if (B != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens requires B == 1 (got B=%d)", B);
+        if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
+    } else if (num_seqs != B) {
+        return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs (%d) must equal B (%d) without cu_seqlens",
+                    num_seqs, B);
+    }
+    const int64_t tokens = (int64_t)B * T;
+    if (tokens * C > ((int64_t)1 << 40)) return fail(KDA_ERR_INVALID_ARGUMENT, "problem too large");
+    if (!weight) return fail(KDA_ERR_INVALID_ARGUMENT, "weight is required");
+    if (tokens > 0 && (!x || !y)) return fail(KDA_ERR_INVALID_ARGUMENT, "x and y are required");
+    const void *ptrs[] = {x, weight, bias, initial_state, final_state, y, cu_seqlens};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    if (!kda::conv_supported(dtype, C, W))
+        return fail(KDA_ERR_UNSUPPORTED, "no short-convolution instantiation for dtype=%d C=%d W=%d "
+                    "(W = 4, C a multiple of 8)", dtype, C, W);
+    if (num_seqs == 0) return ok();
+    kda::ConvArgs a;
+    a.n_seqs = num_seqs;
+    a.seq_len = T;
+    a.cu_seqlens = cu_seqlens;
+    a.tokens = tokens;
+    a.C = C;
+    a.x = x;
+    a.w = weight;
+    a.bias = bias;
+    a.s0 = initial_state;
+    a.s_out = final_state;
+    a.y = y;
+    a.silu = activation == KDA_ACT_SILU ? 1 : 0;
+    return hip_status(kda::launch_conv(dtype, a, false, static_cast<hipStream_t>(stream)),
+                      "kda_short_conv_fwd launch");
+}
+
+kda_status kda_short_conv_update(int32_t N, int32_t C, int32_t W, int32_t dtype, int32_t activation,
+                                 const void *x, const float *weight, const float *bias, void *state,
+                                 void *y, void *stream) {
+    if (N < 0 || C < 1 || W < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes (N=%d C=%d W=%d)", N, C, W);
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype code %d", dtype);
+    if (activation != KDA_ACT_NONE && activation != KDA_ACT_SILU)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown activation %d", activation);
+    if ((int64_t)N * C > ((int64_t)1 << 40)) return fail(KDA_ERR_INVALID_ARGUMENT, "problem too large");
+    if (!weight) return fail(KDA_ERR_INVALID_ARGUMENT, "weight is required");
+    if (N > 0 && (!x || !state || !y)) return fail(KDA_ERR_INVALID_ARGUMENT, "x, state and y are required");
+    const void *ptrs[] = {x, weight, bias, state, y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    if (!kda::conv_supported(dtype, C, W))
+        return fail(KDA_ERR_UNSUPPORTED, "no short-convolution instantiation for dtype=%d C=%d W=%d "
+                    "(W = 4, C a multiple of 8)", dtype, C, W);
+    if (N == 0) return ok();
+    kda::ConvArgs a;
+    a.n_seqs = N;
+    a.seq_len = 1;
+    a.cu_seqlens = nullptr;
+    a.tokens = N;
+    a.C = C;
+    a.x = x;
+    a.w = weight;
+    a.bias = bias;
+    a.s0 = state;
+    a.s_out = state;
+    a.y = y;
+    a.silu = activation == KDA_ACT_SILU ? 1 : 0;
+    return hip_status(kda::launch_conv(dtype, a, true, static_cast<hipStream_t>(stream)),
+                      "kda_short_conv_update launch");
+}
+
+}  // extern "C"

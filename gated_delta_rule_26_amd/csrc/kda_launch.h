@@ -53,6 +53,21 @@ struct DecodeArgs {
     Fusion f;
 };
 
+struct ConvArgs {
+    int32_t n_seqs;              // sequences N (decode: tokens, one per sequence)
+    int32_t seq_len;             // tokens per sequence when cu_seqlens == nullptr
+    const int32_t *cu_seqlens;   // device [N+1] or nullptr
+    int64_t tokens;              // rows of x and y
+    int32_t C;                   // channels per row (a multiple of 8)
+    const void *x;               // [tokens, C] dtype
+    const float *w;              // [C, 4] taps, the last on the current token
+    const float *bias;           // [C] or nullptr
+    const void *s0;              // [N, 3, C] dtype conv state, or nullptr (zeros)
+    void *s_out;                 // [N, 3, C] final conv state (decode: the state, in place)
+    void *y;                     // [tokens, C] dtype
+    int32_t silu;                // SiLU after the convolution
+};
+
 // Workspace bytes the sequence split needs for this problem on the current device (0: no
 // split). The split is used only when the call provides at least this much workspace.
 size_t chunk_fwd_split_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
@@ -62,6 +77,7 @@ size_t chunk_fwd_split_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_
 bool chunk_fwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv);
 bool chunk_fwd_fused_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv);
 bool decode_supported(int32_t in_dtype, int32_t Dk, int32_t Dv);
+bool conv_supported(int32_t dtype, int32_t C, int32_t W);
 
 // Enqueue the kernel on `stream`; returns the launch status (hipGetLastError).
 // Enqueue kda_chunk_fwd. `workspace` (may be null) enables the sequence split when it holds
@@ -71,5 +87,8 @@ hipError_t launch_chunk_fwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t
                             hipStream_t stream);
 hipError_t launch_decode(int32_t in_dtype, int32_t Dk, int32_t Dv, const DecodeArgs &a,
                          hipStream_t stream);
+// The short convolution: the prefill over packed/batched sequences (then the final states when
+// s_out is given), or (update) one decode token per sequence with the state shifted in place.
+hipError_t launch_conv(int32_t dtype, const ConvArgs &a, bool update, hipStream_t stream);
 
 }  // namespace kda

@@ -23,8 +23,10 @@
  * for unit-norm keys ([KV-cache page] section 5: without L2-normalised q and k the state
  * blows up to NaN). The library does not normalise: callers pass normalised q and k.
  *
- * Two entry points do the work, and two fused variants add the KDA layer's steps on
- * either side of the core (kda_chunk_fwd_fused, kda_decode_step_fused, below):
+ * Two entry points do the work, two fused variants add the KDA layer's steps on either
+ * side of the core (kda_chunk_fwd_fused, kda_decode_step_fused), and two more run the
+ * layer's short convolution with its conv state (kda_short_conv_fwd, kda_short_conv_update,
+ * at the end of this file):
  *   kda_chunk_fwd    prefill: the chunkwise-parallel form of the recurrence ([KV-cache page]
  *                    section 3: chunk_size 64; section 6: chunked parallel form with a WY
  *                    representation), over fixed-length batches or packed variable-length
@@ -214,6 +216,45 @@ kda_status kda_decode_step_fused(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
                                  const void *q, const void *k, const void *v,
                                  const kda_fusion *fusion, const float *beta,
                                  float *state, void *o, void *stream);
+
+/*
+ * The short causal convolution in front of the core ([loading page] section 3: the KDA
+ * layer's short convolution, kernel size 4; section 6: the decode cache carries its
+ * conv_states beside the recurrent states). Depthwise over the channels of a [tokens, C]
+ * tensor (the layer's q, k or v projections, or several side by side), per sequence:
+ *
+ *     y_t[c] = act(bias[c] + sum_{j < W} weight[c][j] * x_{t-W+1+j}[c])
+ *
+ * where the inputs before a sequence's first token come from its conv state, the W - 1
+ * previous inputs oldest first (zeros without one). act: KDA_ACT_NONE or KDA_ACT_SILU (the
+ * pages name no activation). Computed in float32, stored in dtype.
+ */
+typedef enum kda_activation { KDA_ACT_NONE = 0, KDA_ACT_SILU = 1 } kda_activation;
+
+/*
+ * kda_short_conv_fwd - the convolution over a prefill batch.
+ *   x, y           [B*T, C] dtype (KDA_F32 or KDA_BF16); sequences as in kda_chunk_fwd
+ *                  (B sequences of T tokens, or packed with cu_seqlens, B = 1)
+ *   weight         [C, W] float32; weight[c][W-1] multiplies the current token
+ *   bias           [C] float32 or NULL
+ *   initial_state  [N, W-1, C] dtype or NULL (zeros)
+ *   final_state    [N, W-1, C] dtype or NULL: each sequence's last W - 1 inputs (shifted in
+ *                  from the initial state for sequences shorter than W - 1); may equal
+ *                  initial_state
+ * Supported: W = 4, C a multiple of 8. Errors as kda_chunk_fwd.
+ */
+kda_status kda_short_conv_fwd(int32_t B, int32_t T, int32_t C, int32_t W, int32_t dtype,
+                              int32_t activation, const void *x, const float *weight,
+                              const float *bias, const void *initial_state, void *final_state,
+                              void *y, const int32_t *cu_seqlens, int32_t num_seqs, void *stream);
+
+/*
+ * kda_short_conv_update - one decode token per sequence: x, y [N, C] dtype; state
+ * [N, W-1, C] dtype, read and shifted in place (the oldest input drops out, x comes in).
+ */
+kda_status kda_short_conv_update(int32_t N, int32_t C, int32_t W, int32_t dtype, int32_t activation,
+                                 const void *x, const float *weight, const float *bias, void *state,
+                                 void *y, void *stream);
 
 #ifdef __cplusplus
 }

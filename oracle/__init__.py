@@ -17,7 +17,8 @@ Functions
 ``fused``            (oracle/fused.py) the layer's fusions around the core: the forget gate
                      from its pre-activation, q/k L2 normalisation, the gated RMSNorm of the
                      output, and their composition with ``kda_fwd`` (``kda_fused_fwd``,
-                     ``kda_fused_decode_step``). Pinned by tests/test_oracle_fused_pins.py.
+                     ``kda_fused_decode_step``); the short causal convolution with its conv
+                     state (``short_conv``). Pinned by tests/test_oracle_fused_pins.py.
 
 Nothing here is "parity unpinned".
 """
@@ -123,4 +124,4 @@ def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, threads: int
 
 
 from . import fused  # noqa: E402,F401  (needs kda_fwd above)
-from .fused import kda_fused_decode_step, kda_fused_fwd  # noqa: E402,F401
+from .fused import kda_fused_decode_step, kda_fused_fwd, short_conv  # noqa: E402,F401

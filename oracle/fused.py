@@ -24,6 +24,16 @@ What the fused entry points compute, step by step (each function below is one st
                   with z the output gate's pre-activation, weight a per-channel gain and
                   eps the config's rms_norm_eps (1e-6 in the loading page's config).
 
+5. ``short_conv``  the short causal convolution in front of the core: the loading page
+                  (section 3) gives the KDA layer a short convolution of kernel size 4, and
+                  (section 6) a decode cache holding conv_states beside the recurrent states.
+                  Reading adopted: a depthwise (per-channel) causal convolution over the
+                  tokens of each sequence, y_t[c] = act(bias[c] + sum_j w[c, j] x_{t-W+1+j}[c]),
+                  whose inputs before a sequence's first token come from its conv state (the
+                  W - 1 previous inputs, oldest first; zeros without one); the final conv
+                  state is the sequence's last W - 1 inputs. act is the identity or SiLU
+                  (the pages name none).
+
 Every function is pinned in tests/test_oracle_fused_pins.py (closed forms, identities and
 invariances, not a retyping of these formulas).
 """
@@ -113,3 +123,45 @@ def kda_fused_decode_step(q, k, v, x, A_log, dt_bias, beta, state, *, normalize_
                          o_weight=o_weight, o_eps=o_eps, scale=scale,
                          initial_state=np.asarray(state, np.float64), cu_seqlens=cu)
     return o, S
+
+
+def silu(z):
+    """z * sigmoid(z)."""
+    z = np.asarray(z, dtype=np.float64)
+    return z * sigmoid(z)
+
+
+def short_conv(x, weight, bias=None, *, initial_state=None, cu_seqlens=None,
+               activation="silu"):
+    """Depthwise causal convolution per sequence, with a conv state.
+
+    x: [T, C] (packed sequences, ``cu_seqlens`` [N + 1]; default one sequence), weight: [C, W]
+    (weight[c, W - 1] multiplies the current token), bias: [C] or None, initial_state:
+    [N, W - 1, C] (the previous inputs, oldest first) or None (zeros). activation: "silu" or
+    None. Returns (y [T, C], final_state [N, W - 1, C]), float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    T, C = x.shape
+    W = w.shape[1]
+    cu = np.array([0, T]) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    b = np.zeros(C) if bias is None else np.asarray(bias, dtype=np.float64)
+    s0 = np.zeros((N, W - 1, C)) if initial_state is None else np.asarray(initial_state,
+                                                                            dtype=np.float64)
+    y = np.zeros((T, C))
+    final = np.zeros((N, W - 1, C))
+    for n in range(N):
+        seq = x[cu[n]:cu[n + 1]]
+        hist = np.concatenate([s0[n], seq])          # [W - 1 + L, C]: history, then the tokens
+        for t in range(len(seq)):
+            acc = b.copy()
+            for j in range(W):                        # tap j sees input t - (W - 1) + j
+                acc = acc + w[:, j] * hist[t + j]
+            y[cu[n] + t] = acc
+        final[n] = hist[len(hist) - (W - 1):]
+    if activation == "silu":
+        y = silu(y)
+    elif activation is not None:
+        raise ValueError(f"unknown activation {activation!r}")
+    return y, final

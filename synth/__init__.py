@@ -12,6 +12,8 @@ from .gen import (  # noqa: F401
     Workload,
     bf16_bits_to_f32,
     bf16_bits_to_f64,
+    conv_params,
+    conv_state,
     NORM_EPS,
     f64_to_bf16_bits,
     fused_slab,

@@ -45,6 +45,7 @@ ROOT_SEED = 20260
 _T_Q, _T_K, _T_V, _T_BETA, _T_X, _T_S0 = 0, 1, 2, 3, 4, 6
 _P_A, _P_B, _P_LEN = 10, 11, 12
 _T_QR, _T_KR, _T_XG, _T_Z, _P_W = 20, 21, 22, 23, 13
+_P_CW, _P_CB, _T_CS = 14, 15, 24
 NORM_EPS = 1e-6
 
 
@@ -204,6 +205,19 @@ def slab(w: Workload, n: int, h: int, L: int | None = None,
 def norm_weight(w: Workload) -> np.ndarray:
     """float32 [V] gain of the output norm."""
     return (1.0 + 0.1 * _rng(w.wid, _P_W).standard_normal(w.V)).astype(np.float32)
+
+
+def conv_params(w: Workload, C: int, which: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """float32 taps [C, 4] and bias [C] of one short convolution (``which`` tells the
+    layer's convolutions apart)."""
+    weight = _rng(w.wid, _P_CW, which).uniform(-0.5, 0.5, size=(C, 4)).astype(np.float32)
+    bias = _rng(w.wid, _P_CB, which).uniform(-0.5, 0.5, size=C).astype(np.float32)
+    return weight, bias
+
+
+def conv_state(w: Workload, N: int, C: int, which: int = 0) -> np.ndarray:
+    """Initial conv states [N, 3, C] in the storage dtype (the 3 inputs before each sequence)."""
+    return _store(_rng(w.wid, _T_CS, which).standard_normal((N, 3, C)), w.dtype)
 
 
 def fused_slab(w: Workload, n: int, h: int, L: int | None = None) -> dict:

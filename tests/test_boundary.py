@@ -195,3 +195,41 @@ def test_fusion_struct_matches_the_header():
     body = re.search(r"typedef struct kda_fusion \{(.*?)\} kda_fusion;", src, re.S).group(1)
     fields = re.findall(r"\b(\w+);", body)
     assert fields == [n for n, _ in kda._Fusion._fields_]
+
+
+# --------------------------------------------------------------------- short convolution
+
+def conv_fwd(lib, B=1, T=64, C=256, W=4, dt=BF16, act=1, x=P, w=P, b=None, s0=None, s1=None,
+             y=P, cu=None, N=None):
+    N = B if N is None else N
+    return lib.kda_short_conv_fwd(B, T, C, W, dt, act, x, w, b, s0, s1, y, cu, N, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), INVALID), (dict(T=-1), INVALID), (dict(C=0), INVALID), (dict(W=0), INVALID),
+    (dict(dt=5), INVALID), (dict(act=2), INVALID), (dict(w=None), INVALID), (dict(x=None), INVALID),
+    (dict(y=None), INVALID), (dict(x=MIS), INVALID), (dict(s0=MIS), INVALID),
+    (dict(B=2, cu=P, N=1), INVALID), (dict(B=2, N=1), INVALID),
+    (dict(W=3), UNSUPPORTED), (dict(C=12), UNSUPPORTED),
+])
+def test_short_conv_rejects_before_launch(lib, kw, status):
+    assert conv_fwd(lib, **kw) == status
+    assert len(lib.kda_last_error()) > 0
+
+
+def test_short_conv_empty_work_is_ok(lib):
+    assert conv_fwd(lib, T=0, cu=P, N=0, x=None, y=None) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), INVALID), (dict(C=0), INVALID), (dict(dt=4), INVALID), (dict(act=-1), INVALID),
+    (dict(state=None), INVALID), (dict(w=None), INVALID), (dict(x=MIS), INVALID),
+    (dict(W=5), UNSUPPORTED), (dict(C=4), UNSUPPORTED),
+])
+def test_short_conv_update_rejects_before_launch(lib, kw, status):
+    base = dict(N=4, C=256, W=4, dt=BF16, act=1, x=P, w=P, b=None, state=P, y=P)
+    base.update(kw)
+    assert lib.kda_short_conv_update(base["N"], base["C"], base["W"], base["dt"], base["act"],
+                                     base["x"], base["w"], base["b"], base["state"], base["y"],
+                                     None) == status
+    assert len(lib.kda_last_error()) > 0

@@ -83,6 +83,25 @@ def test_prefill_128k_h32_fused_full_size():
     assert_close(S_s, S_ref[0], TOL, "final state (heads 0, 31)")
 
 
+def test_short_conv_128k_h32_full_size():
+    """The short convolution (SiLU) over the long-context workload's raw q projection,
+    [131072, 32 * 128] bf16, in one launch; heads 0 and 31 (channels 0-127, 3968-4095)
+    checked against the oracle, the final state bit for bit."""
+    torch = torch_mod()
+    w = synth.WORKLOADS["prefill_128k_h32"]
+    x = synth.make_inputs(w, fused=True)["q"].reshape(w.T, w.H * w.K)
+    weight, bias = synth.conv_params(w, w.H * w.K)
+    note("short conv 128k x 4096 full size")
+    y, sf = kda.kda_short_conv_fwd(to_dev(x[None], "bf16"), to_dev(weight), to_dev(bias))
+    torch.cuda.synchronize()
+    chans = np.r_[0:128, 3968:4096]
+    y_s = y[0][:, torch.from_numpy(chans).cuda()].float().cpu().numpy()
+    f_s = sf[0][:, torch.from_numpy(chans).cuda()].float().cpu().numpy()
+    y_ref, f_ref = oracle.short_conv(f64(x[:, chans], "bf16"), weight[chans], bias[chans])
+    assert_close_bf16_out(y_s, y_ref, 1e-5, "y (channels of heads 0, 31)")
+    assert np.array_equal(f_s, f_ref[0]), "final conv state"
+
+
 def test_decode_256x32_full_size():
     """256 sequences x 32 heads: a 2048-token prefill builds the states, then 1000 decode steps
     over all of them; sequences 0, 97 and 255 (all heads) checked against the oracle over the

@@ -216,3 +216,76 @@ def test_fused_prefill_then_decode_equals_prefill():
                                               c["beta"][t:t + 1], S, o_gate=c["z"][t:t + 1], **kw)
         np.testing.assert_allclose(y_t[0], y_all[t], rtol=1e-11, atol=1e-13)
     np.testing.assert_allclose(S, S_all, rtol=1e-11, atol=1e-13)
+
+
+# -------------------------------------------------------------------- short convolution
+
+def test_short_conv_impulse_response_by_hand():
+    """Taps (1, 2, 3, 4), the last one on the current token: an impulse at t = 1 in channel 0
+    comes out as 4, 3, 2, 1 at t = 1..4; channel 1 sees nothing (depthwise)."""
+    x = np.zeros((7, 2))
+    x[1, 0] = 1.0
+    w = np.array([[1.0, 2.0, 3.0, 4.0], [0.5, -1.0, 2.0, 1.0]])
+    y, f = oracle.short_conv(x, w, activation=None)
+    np.testing.assert_array_equal(y[:, 0], [0.0, 4.0, 3.0, 2.0, 1.0, 0.0, 0.0])
+    np.testing.assert_array_equal(y[:, 1], 0.0)
+    np.testing.assert_array_equal(f[0], x[4:7])
+
+
+def test_short_conv_step_response_and_bias():
+    """A constant input c with a zero state ramps through the partial tap sums, then holds
+    c * sum(w) + bias: c = 2, taps (1, 2, 3, 4), bias 0.5 -> 8.5, 14.5, 18.5, 20.5, 20.5."""
+    x = np.full((5, 1), 2.0)
+    y, _ = oracle.short_conv(x, np.array([[1.0, 2.0, 3.0, 4.0]]), np.array([0.5]), activation=None)
+    np.testing.assert_array_equal(y[:, 0], [8.5, 14.5, 18.5, 20.5, 20.5])
+
+
+def test_silu_closed_forms():
+    assert fused.silu(0.0) == 0.0
+    assert fused.silu(math.log(3.0)) == pytest.approx(0.75 * math.log(3.0), rel=1e-15)
+    z = np.linspace(-20.0, 20.0, 81)
+    np.testing.assert_allclose(fused.silu(-z), fused.silu(z) - z, rtol=0, atol=1e-13)
+    # the activation acts on the biased sum: zero input gives silu(bias)
+    y, _ = oracle.short_conv(np.zeros((3, 2)), np.ones((2, 4)), np.array([1.5, -2.0]))
+    np.testing.assert_allclose(y, np.broadcast_to(fused.silu(np.array([1.5, -2.0])), (3, 2)),
+                               rtol=1e-15)
+
+
+def test_short_conv_is_causal_and_carries_its_state():
+    """Outputs never depend on later tokens; running a sequence in two parts with the conv
+    state carried equals one run (outputs and final state), for every split point."""
+    rng = np.random.default_rng(20)
+    T, C, W = 11, 5, 4
+    x = rng.standard_normal((T, C))
+    w = rng.standard_normal((C, W))
+    b = rng.standard_normal(C)
+    s0 = rng.standard_normal((1, W - 1, C))
+    y, f = oracle.short_conv(x, w, b, initial_state=s0)
+    x2 = x.copy()
+    x2[6:] += 10.0
+    y2, _ = oracle.short_conv(x2, w, b, initial_state=s0)
+    np.testing.assert_array_equal(y2[:6], y[:6])
+    for m in range(T + 1):
+        ya, fa = oracle.short_conv(x[:m], w, b, initial_state=s0)
+        yb, fb = oracle.short_conv(x[m:], w, b, initial_state=fa)
+        np.testing.assert_allclose(np.concatenate([ya, yb]), y, rtol=1e-14, atol=1e-14)
+        np.testing.assert_array_equal(fb, f)
+
+
+def test_short_conv_packed_equals_separate():
+    """Packed sequences never see each other's tokens; a zero-length sequence returns its
+    state unchanged and a one-token sequence shifts it by one."""
+    rng = np.random.default_rng(21)
+    lens = [5, 0, 1, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    C, W = 3, 4
+    x = rng.standard_normal((int(cu[-1]), C))
+    w = rng.standard_normal((C, W))
+    s0 = rng.standard_normal((len(lens), W - 1, C))
+    y, f = oracle.short_conv(x, w, initial_state=s0, cu_seqlens=cu)
+    for n in range(len(lens)):
+        yn, fn = oracle.short_conv(x[cu[n]:cu[n + 1]], w, initial_state=s0[n:n + 1])
+        np.testing.assert_array_equal(y[cu[n]:cu[n + 1]], yn)
+        np.testing.assert_array_equal(f[n], fn[0])
+    np.testing.assert_array_equal(f[1], s0[1])
+    np.testing.assert_array_equal(f[2], np.concatenate([s0[2][1:], x[cu[2]:cu[3]]]))

@@ -272,8 +272,21 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
         "achieved_gbs": round(cb / (us * 1e-6) / 1e9, 1),
         "frac_hbm": round(cb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": cb}
-    del dq, dk, dv, dg, db, od, x
-    log("timed decode_256x32 back to back")
+    # 8 tokens per sequence and head in one call (the recurrent mode for short queries): the
+    # state is read and written once for the 8
+    L8 = wd.decode_steps
+    rq, rk, rv = (t.transpose(0, 1).contiguous() for t in (dq, dk, dv))    # [N, 8, H, D]
+    rg, rb = dg.transpose(0, 1).contiguous(), db.transpose(0, 1).contiguous()
+    ro = torch.empty((N, L8, H, wd.V), dtype=torch.float32, device="cuda")
+    us = timed(lambda: kda.kda_recurrent_fwd(rq, rk, rv, rg, rb, state, o=ro), 20) * 1e3
+    rbytes = 2 * N * H * wd.K * wd.V * 4 + N * L8 * H * (2 * wd.K * 2 + wd.V * 2 + wd.K * 4 + 4 + wd.V * 4)
+    out["decode_256x32_8_tokens_per_call"] = {
+        "avg_launch_us": round(us, 2), "tokens_per_s": round(N * L8 * 1e6 / us, 1),
+        "us_per_token_step": round(us / L8, 2), "achieved_gbs": round(rbytes / (us * 1e-6) / 1e9, 1),
+        "algorithmic_bytes": rbytes,
+        "what": "kda_recurrent_fwd: 256 sequences x 32 heads x 8 tokens, state read and written once"}
+    del dq, dk, dv, dg, db, od, x, rq, rk, rv, rg, rb, ro
+    log("timed decode_256x32 back to back, and 8 tokens per call")
 
     x = synth.make_inputs(wd, seqs=range(N), fused=True)
     dq, dk, dv, dgx, dz = (to_dev(x["dec_" + n], True) for n in ("q", "k", "v", "x", "z"))

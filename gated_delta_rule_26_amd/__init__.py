@@ -14,7 +14,7 @@ import ctypes
 import os
 
 __all__ = ["KdaError", "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_fused",
-           "kda_decode_step_fused", "kda_short_conv_fwd", "kda_short_conv_update",
+           "kda_decode_step_fused", "kda_recurrent_fwd", "kda_short_conv_fwd", "kda_short_conv_update",
            "chunk_fwd_workspace_bytes", "load_library", "KDA_F32", "KDA_BF16"]
 
 KDA_F32, KDA_BF16 = 0, 1
@@ -76,6 +76,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_decode_step_fused.restype = i32
     lib.kda_decode_step_fused.argtypes = [i32, i32, i32, i32, i32, i32, f32,
                                           vp, vp, vp, fp, vp, vp, vp]
+    lib.kda_recurrent_fwd.restype = i32
+    lib.kda_recurrent_fwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, f32,
+                                      vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_short_conv_fwd.restype = i32
     lib.kda_short_conv_fwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                        vp, i32, vp]
@@ -399,3 +402,27 @@ def kda_short_conv_update(x, weight, bias, state, *, activation="silu", y=None, 
                                    _ptr(weight), _ptr(bias), _ptr(state), _ptr(y), _stream(stream))
     _check(lib, st)
     return y
+
+
+def kda_recurrent_fwd(q, k, v, g, beta, state, *, scale: float = 1.0, o=None, stream=None):
+    """L tokens per (sequence, head) on the persistent state (C: kda_recurrent_fwd): q, k, g
+    [N, L, H, Dk]; v [N, L, H, Dv]; beta [N, L, H]; ``state`` float32 [N, H, Dk, Dv] is
+    updated in place. Returns o float32 [N, L, H, Dv]."""
+    import torch
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _req(t, nm, q.dtype)
+    _req(g, "g", torch.float32)
+    _req(beta, "beta", torch.float32)
+    _req(state, "state", torch.float32)
+    N, L, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or tuple(v.shape) != (N, L, H, Dv) or \
+            tuple(beta.shape) != (N, L, H) or tuple(state.shape) != (N, H, Dk, Dv):
+        raise ValueError("inconsistent recurrent shapes")
+    o = _out(o, v, torch.float32)
+    st = lib.kda_recurrent_fwd(N, L, H, Dk, Dv, _dtype_code(q), KDA_F32, float(scale),
+                               _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                               _ptr(o), _stream(stream))
+    _check(lib, st)
+    return o

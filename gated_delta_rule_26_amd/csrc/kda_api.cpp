@@ -151,6 +151,7 @@ kda_status kda_decode_step(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
     kda::DecodeArgs a;
     a.N = N;
     a.H = H;
+    a.L = 1;
     a.scale = scale;
     a.q = q;
     a.k = k;
@@ -288,6 +289,7 @@ kda_status kda_decode_step_fused(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
     kda::DecodeArgs a;
     a.N = N;
     a.H = H;
+    a.L = 1;
     a.scale = scale;
     a.q = q;
     a.k = k;
@@ -381,6 +383,51 @@ kda_status kda_short_conv_update(int32_t N, int32_t C, int32_t W, int32_t dtype,
     a.silu = activation == KDA_ACT_SILU ? 1 : 0;
     return hip_status(kda::launch_conv(dtype, a, true, static_cast<hipStream_t>(stream)),
                       "kda_short_conv_update launch");
+}
+
+}  // extern "C"
+
+extern "C" {
+
+kda_status kda_recurrent_fwd(int32_t N, int32_t L, int32_t H, int32_t Dk, int32_t Dv,
+                             int32_t in_dtype, int32_t out_dtype, float scale,
+                             const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             float *state, void *o, void *stream) {
+    if (N < 0 || L < 0 || H < 1 || Dk < 1 || Dv < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes (N=%d L=%d H=%d Dk=%d Dv=%d)", N, L, H, Dk, Dv);
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype code (in=%d out=%d)", in_dtype, out_dtype);
+    if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if ((int64_t)N * H > 0x7fffffff) return fail(KDA_ERR_INVALID_ARGUMENT, "N*H too large");
+    if ((int64_t)N * L * H * (Dk > Dv ? Dk : Dv) > ((int64_t)1 << 40))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "problem too large");
+    if ((int64_t)N * L > 0 && (!q || !k || !v || !g || !beta || !o))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and o are required");
+    if (N > 0 && !state) return fail(KDA_ERR_INVALID_ARGUMENT, "state is required");
+    const void *ptrs[] = {q, k, v, g, beta, state, o};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    if (out_dtype != KDA_F32) return fail(KDA_ERR_UNSUPPORTED, "only float32 o is supported");
+    if (!kda::decode_supported(in_dtype, Dk, Dv))
+        return fail(KDA_ERR_UNSUPPORTED, "no recurrent instantiation for in_dtype=%d Dk=%d Dv=%d",
+                    in_dtype, Dk, Dv);
+    if (N == 0 || L == 0) return ok();
+    kda::DecodeArgs a;
+    a.N = N;
+    a.H = H;
+    a.L = L;
+    a.scale = scale;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.o = o;
+    a.f = kda::Fusion{};
+    return hip_status(kda::launch_decode(in_dtype, Dk, Dv, a, static_cast<hipStream_t>(stream)),
+                      "kda_recurrent_fwd launch");
 }
 
 }  // extern "C"

@@ -1,4 +1,5 @@
-// KDA decode step: one token per (sequence, head) on a persistent float32 state.
+// KDA decode step and short recurrent prefill: L tokens per (sequence, head) on a persistent
+// float32 state (L = 1: the decode step).
 //
 // Per (sequence, head), with the state S (Dk x Dv, rows = key channels) in HBM:
 //   S' = Diag(exp(g)) S;  p = S'^T k;  r = S'^T (scale q);  u = beta (v - p)
@@ -7,7 +8,9 @@
 // o_t = S_t^T (scale q): the token-by-token recurrent mode used for incremental decoding
 // ([loading page] sections 5 and 6: the recurrent state carried by the decode cache).
 //
-// The state is read once and written once: the step is HBM-bound (7 flops per 8 bytes).
+// The state is read once and written once per call, however many tokens L the call carries
+// (the token-by-token "fused_recurrent" mode for short queries, [loading page] section 5):
+// one token is HBM-bound (7 flops per 8 bytes); L tokens divide the state traffic by L.
 // One workgroup owns one (sequence, head) state. Threads tile the state as rows x float4
 // columns, so every wave reads and writes whole contiguous 512-byte rows; each thread keeps
 // its Dk*Dv/NT values in registers between the read and the write. Both column reductions
@@ -43,141 +46,169 @@ __device__ __forceinline__ f32x4 shfl_xor4(f32x4 x, int m) {
     return r;
 }
 
-template <typename Tin, int DK, int DV>
+// MULTI: L = a.L tokens per sequence; otherwise one (the decode step: a compile-time single
+// iteration keeps the state out of loop-carried registers).
+template <typename Tin, int DK, int DV, bool MULTI>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     using Sh = DecodeShape<DK, DV>;
     constexpr int TPR = Sh::TPR, RPP = Sh::RPP, NT = Sh::NT, NPASS = Sh::NPASS;
+    static_assert(NT >= DK && NT >= DV, "one staged channel per thread");
 
-    __shared__ float sk[DK], sq[DK], sa[DK], sv[DV];
-    __shared__ __attribute__((aligned(16))) float sz[DV];  // fused output norm: gate pre-activation
-    __shared__ __attribute__((aligned(16))) float sw[DV];  // ... and gain
+    // a token's inputs, double-buffered so that staging token t + 1 never waits for readers of t
+    __shared__ float sk[2][DK], sq[2][DK], sa[2][DK];
+    __shared__ __attribute__((aligned(16))) float sv[2][DV];
+    __shared__ __attribute__((aligned(16))) float sz[2][DV];  // fused output norm: gate pre-activation
+    __shared__ __attribute__((aligned(16))) float sw[DV];     // ... and gain
     __shared__ f32x4 red[Sh::NWAVE][2][TPR];
-    __shared__ float sqk[3];  // scale q.k (normalised when fused), 1/||k||, 1/||q|| (or 1, 1)
+    __shared__ float sqk[2][3];  // scale q.k (normalised when fused), 1/||k||, 1/||q|| (or 1, 1)
 
     const int tid = threadIdx.x;
     const int64_t item = blockIdx.x;  // n * H + h
-    const Tin *q = static_cast<const Tin *>(a.q) + item * DK;
-    const Tin *k = static_cast<const Tin *>(a.k) + item * DK;
-    const Tin *v = static_cast<const Tin *>(a.v) + item * DV;
-    float *S = a.state + item * (int64_t)(DK * DV);
+    const int64_t n = item / a.H;
     const int h = (int)(item % a.H);
-
-    for (int c = tid; c < DK; c += NT) {
-        sk[c] = to_f32(k[c]);
-        sq[c] = a.scale * to_f32(q[c]);
-        float gc;
-        if (a.f.gx)
-            gc = -expf(a.f.A_log[h]) *
-                 softplus_f(to_f32(static_cast<const Tin *>(a.f.gx)[item * DK + c]) + a.f.dt_bias[h * DK + c]);
-        else
-            gc = a.g[item * DK + c];
-        sa[c] = __expf(gc);
-    }
-    for (int j = tid; j < DV; j += NT) {
-        sv[j] = to_f32(v[j]);
-        if (a.f.og) {  // loaded with the token, not at the end of the step
-            sz[j] = to_f32(static_cast<const Tin *>(a.f.og)[item * DV + j]);
-            sw[j] = a.f.ow[j];
-        }
-    }
-    __syncthreads();
-
+    float *S = a.state + item * (int64_t)(DK * DV);
     const int cg = tid % TPR, rr = tid / TPR;
     const int lane = tid & 63, wave = tid >> 6;
+    const float rate = a.f.gx ? expf(a.f.A_log[h]) : 0.f;
+    const float gbias = (a.f.gx && tid < DK) ? a.f.dt_bias[h * DK + tid] : 0.f;
+    if (a.f.og && tid < DV) sw[tid] = a.f.ow[tid];
+
+    // token t of this sequence is row (n * L + t) * H + h of the [N, L, H, D] inputs; the
+    // next token's values are loaded into registers while the current one computes
+    const int L = MULTI ? a.L : 1;
+    auto row = [&](int t) { return (n * L + t) * a.H + h; };
+    float nk = 0.f, nq = 0.f, ng = 0.f, nv = 0.f, nz = 0.f;
+    auto fetch = [&](int t) {
+        const int64_t r = row(t);
+        if (tid < DK) {
+            nk = to_f32(static_cast<const Tin *>(a.k)[r * DK + tid]);
+            nq = to_f32(static_cast<const Tin *>(a.q)[r * DK + tid]);
+            ng = a.f.gx ? to_f32(static_cast<const Tin *>(a.f.gx)[r * DK + tid]) : a.g[r * DK + tid];
+        }
+        if (tid < DV) {
+            nv = to_f32(static_cast<const Tin *>(a.v)[r * DV + tid]);
+            if (a.f.og) nz = to_f32(static_cast<const Tin *>(a.f.og)[r * DV + tid]);
+        }
+    };
+    auto stage = [&](int b) {
+        if (tid < DK) {
+            sk[b][tid] = nk;
+            sq[b][tid] = a.scale * nq;
+            sa[b][tid] = __expf(a.f.gx ? -rate * softplus_f(ng + gbias) : ng);
+        }
+        if (tid < DV) {
+            sv[b][tid] = nv;
+            if (a.f.og) sz[b][tid] = nz;
+        }
+    };
 
     f32x4 s[NPASS];
+    fetch(0);
+    for (int t = 0; t < L; ++t) {
+        const int b = t & 1;
+        stage(b);
+        if (t + 1 < L) fetch(t + 1);
+        __syncthreads();
+        if (t == 0) {
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p)
+                s[p] = *reinterpret_cast<const f32x4 *>(S + (p * RPP + rr) * DV + 4 * cg);
+        }
+
+        if (wave == 0) {  // scale * (q . k) and the norms, off the critical path of the state sweep
+            float acc = 0.f, kk = 0.f, qq = 0.f;
+            for (int c = lane; c < DK; c += 64) {
+                acc += sq[b][c] * sk[b][c];
+                kk += sk[b][c] * sk[b][c];
+                qq += sq[b][c] * sq[b][c];
+            }
+            for (int m = 32; m > 0; m >>= 1) {
+                acc += __shfl_xor(acc, m);
+                kk += __shfl_xor(kk, m);
+                qq += __shfl_xor(qq, m);
+            }
+            if (lane == 0) {
+                // sq holds scale * q, so 1/||q|| = |scale| / ||sq|| (any scale, zero included)
+                const float rk = a.f.norm_qk ? rsqrt_or_zero(kk) : 1.f;
+                const float rq = a.f.norm_qk ? fabsf(a.scale) * rsqrt_or_zero(qq) : 1.f;
+                sqk[b][0] = acc * rk * rq;
+                sqk[b][1] = rk;
+                sqk[b][2] = rq;
+            }
+        }
+
+        f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int r = p * RPP + rr;
+            s[p] *= sa[b][r];
+            pk += s[p] * sk[b][r];
+            pq += s[p] * sq[b][r];
+        }
+#pragma unroll
+        for (int m = TPR; m < 64; m <<= 1) {
+            pk += shfl_xor4(pk, m);
+            pq += shfl_xor4(pq, m);
+        }
+        if (lane < TPR) {
+            red[wave][0][cg] = pk;
+            red[wave][1][cg] = pq;
+        }
+        __syncthreads();
+
+        f32x4 P = red[0][0][cg], R = red[0][1][cg];
+#pragma unroll
+        for (int w = 1; w < Sh::NWAVE; ++w) {
+            P += red[w][0][cg];
+            R += red[w][1][cg];
+        }
+        const float bt = a.beta[row(t)];
+        const float rk = sqk[b][1], rq = sqk[b][2];
+        const f32x4 vv = *reinterpret_cast<const f32x4 *>(&sv[b][4 * cg]);
+        const f32x4 u = bt * (vv - rk * P);
+        if (rr == 0) {
+            const f32x4 ov = rq * R + sqk[b][0] * u;
+            const int64_t oo = row(t) * DV + 4 * cg;
+            if (a.f.og) {  // gated RMSNorm over the Dv outputs, held by the TPR lanes of row 0
+                float ss = ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w;
+#pragma unroll
+                for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m);
+                const float r = rsqrt_or_zero(ss * (1.f / DV) + a.f.oeps);
+                const f32x4 z = *reinterpret_cast<const f32x4 *>(&sz[b][4 * cg]);
+                const f32x4 w = *reinterpret_cast<const f32x4 *>(sw + 4 * cg);
+                f32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = ov[e] * r * w[e] * sigmoid_f(z[e]);
+                if (a.f.o_bf16) {
+                    const u32x2 packed = {(uint32_t)bf16_bits(y.x) | ((uint32_t)bf16_bits(y.y) << 16),
+                                          (uint32_t)bf16_bits(y.z) | ((uint32_t)bf16_bits(y.w) << 16)};
+                    *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.o) + oo) = packed;
+                } else {
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(a.o) + oo) = y;
+                }
+            } else {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(a.o) + oo) = ov;
+            }
+        }
+
+        const f32x4 uk = rk * u;  // the update writes the normalised key: k_raw (u / ||k||)^T
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) s[p] += sk[b][p * RPP + rr] * uk;
+    }
+
 #pragma unroll
     for (int p = 0; p < NPASS; ++p)
-        s[p] = *reinterpret_cast<const f32x4 *>(S + (p * RPP + rr) * DV + 4 * cg);
-
-    if (wave == 0) {  // scale * (q . k) and the norms, off the critical path of the state sweep
-        float acc = 0.f, kk = 0.f, qq = 0.f;
-        for (int c = lane; c < DK; c += 64) {
-            acc += sq[c] * sk[c];
-            kk += sk[c] * sk[c];
-            qq += sq[c] * sq[c];
-        }
-        for (int m = 32; m > 0; m >>= 1) {
-            acc += __shfl_xor(acc, m);
-            kk += __shfl_xor(kk, m);
-            qq += __shfl_xor(qq, m);
-        }
-        if (lane == 0) {
-            // sq holds scale * q, so 1/||q|| = |scale| / ||sq|| (any scale, zero included)
-            const float rk = a.f.norm_qk ? rsqrt_or_zero(kk) : 1.f;
-            const float rq = a.f.norm_qk ? fabsf(a.scale) * rsqrt_or_zero(qq) : 1.f;
-            sqk[0] = acc * rk * rq;
-            sqk[1] = rk;
-            sqk[2] = rq;
-        }
-    }
-
-    f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-        const int r = p * RPP + rr;
-        s[p] *= sa[r];
-        pk += s[p] * sk[r];
-        pq += s[p] * sq[r];
-    }
-#pragma unroll
-    for (int m = TPR; m < 64; m <<= 1) {
-        pk += shfl_xor4(pk, m);
-        pq += shfl_xor4(pq, m);
-    }
-    if (lane < TPR) {
-        red[wave][0][cg] = pk;
-        red[wave][1][cg] = pq;
-    }
-    __syncthreads();
-
-    f32x4 P = red[0][0][cg], R = red[0][1][cg];
-#pragma unroll
-    for (int w = 1; w < Sh::NWAVE; ++w) {
-        P += red[w][0][cg];
-        R += red[w][1][cg];
-    }
-    const float b = a.beta[item];
-    const float rk = sqk[1], rq = sqk[2];
-    f32x4 vv = {sv[4 * cg], sv[4 * cg + 1], sv[4 * cg + 2], sv[4 * cg + 3]};
-    const f32x4 u = b * (vv - rk * P);
-    if (rr == 0) {
-        const f32x4 ov = rq * R + sqk[0] * u;
-        if (a.f.og) {  // gated RMSNorm over the Dv outputs, held by the TPR lanes of row 0
-            float ss = ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w;
-#pragma unroll
-            for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m);
-            const float r = rsqrt_or_zero(ss * (1.f / DV) + a.f.oeps);
-            const f32x4 z = *reinterpret_cast<const f32x4 *>(sz + 4 * cg);
-            const f32x4 w = *reinterpret_cast<const f32x4 *>(sw + 4 * cg);
-            f32x4 y;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = ov[e] * r * w[e] * sigmoid_f(z[e]);
-            if (a.f.o_bf16) {
-                const u32x2 packed = {(uint32_t)bf16_bits(y.x) | ((uint32_t)bf16_bits(y.y) << 16),
-                                      (uint32_t)bf16_bits(y.z) | ((uint32_t)bf16_bits(y.w) << 16)};
-                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.o) + item * DV + 4 * cg) = packed;
-            } else {
-                *reinterpret_cast<f32x4 *>(static_cast<float *>(a.o) + item * DV + 4 * cg) = y;
-            }
-        } else {
-            *reinterpret_cast<f32x4 *>(static_cast<float *>(a.o) + item * DV + 4 * cg) = ov;
-        }
-    }
-
-    const f32x4 uk = rk * u;  // the update writes the normalised key: k_raw (u / ||k||)^T
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-        const int r = p * RPP + rr;
-        *reinterpret_cast<f32x4 *>(S + r * DV + 4 * cg) = s[p] + sk[r] * uk;
-    }
+        *reinterpret_cast<f32x4 *>(S + (p * RPP + rr) * DV + 4 * cg) = s[p];
 }
 
 template <typename Tin, int D>
 hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     using Sh = DecodeShape<D, D>;
     const int64_t items = (int64_t)a.N * a.H;
-    hipLaunchKernelGGL((decode_kernel<Tin, D, D>), dim3((unsigned)items), dim3(Sh::NT), 0, stream, a);
+    if (a.L > 1)
+        hipLaunchKernelGGL((decode_kernel<Tin, D, D, true>), dim3((unsigned)items), dim3(Sh::NT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<Tin, D, D, false>), dim3((unsigned)items), dim3(Sh::NT), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -202,7 +233,7 @@ bool decode_supported(int32_t in_dtype, int32_t Dk, int32_t Dv) {
 hipError_t launch_decode(int32_t in_dtype, int32_t Dk, int32_t Dv, const DecodeArgs &a,
                          hipStream_t stream) {
     if (!decode_supported(in_dtype, Dk, Dv)) return hipErrorInvalidValue;
-    if (a.N == 0) return hipSuccess;
+    if (a.N == 0 || a.L == 0) return hipSuccess;
     return in_dtype == 1 ? launch_decode_d<bf16_t>(Dk, a, stream)
                          : launch_decode_d<float>(Dk, a, stream);
 }

@@ -45,6 +45,7 @@ struct ChunkArgs {
 
 struct DecodeArgs {
     int32_t N, H;
+    int32_t L;                   // tokens per sequence ([N, L, H, D] inputs; 1 = decode step)
     float scale;
     const void *q, *k, *v;
     const float *g, *beta;

@@ -23,10 +23,11 @@
  * for unit-norm keys ([KV-cache page] section 5: without L2-normalised q and k the state
  * blows up to NaN). The library does not normalise: callers pass normalised q and k.
  *
- * Two entry points do the work, two fused variants add the KDA layer's steps on either
- * side of the core (kda_chunk_fwd_fused, kda_decode_step_fused), and two more run the
- * layer's short convolution with its conv state (kda_short_conv_fwd, kda_short_conv_update,
- * at the end of this file):
+ * Two entry points do the work; kda_recurrent_fwd runs several tokens per sequence in the
+ * decode kernel's way; two fused variants add the KDA layer's steps on either side of the
+ * core (kda_chunk_fwd_fused, kda_decode_step_fused); and two more run the layer's short
+ * convolution with its conv state (kda_short_conv_fwd, kda_short_conv_update, at the end of
+ * this file):
  *   kda_chunk_fwd    prefill: the chunkwise-parallel form of the recurrence ([KV-cache page]
  *                    section 3: chunk_size 64; section 6: chunked parallel form with a WY
  *                    representation), over fixed-length batches or packed variable-length
@@ -159,6 +160,27 @@ kda_status kda_decode_step(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
                            const void *q, const void *k, const void *v,
                            const float *g, const float *beta,
                            float *state, void *o, void *stream);
+
+/*
+ * kda_recurrent_fwd - L tokens per (sequence, head), token by token, on a persistent float32
+ * state: the recurrent ("fused_recurrent") mode that the layer uses for short queries
+ * ([loading page] section 5), e.g. several tokens per decode step. The state is read once and
+ * written once per call, whatever L is; kda_decode_step is the case L = 1.
+ *
+ *   q, k, g [N, L, H, Dk]; v [N, L, H, Dv]; beta [N, L, H]  (in_dtype / float32 as in
+ *   kda_decode_step; token t of sequence n is row n*L + t)
+ *   state   [N, H, Dk, Dv] float32, S_0 in, S_L out (in place)
+ *   o       [N, L, H, Dv] out_dtype (KDA_F32)
+ *
+ * The same result as kda_chunk_fwd over those L tokens with initial_state = final_state =
+ * state, up to rounding. Dk = Dv in {16, 32, 64, 128}; L >= 0 (L = 0 leaves the state as it
+ * is). Errors as kda_decode_step.
+ */
+kda_status kda_recurrent_fwd(int32_t N, int32_t L, int32_t H, int32_t Dk, int32_t Dv,
+                             int32_t in_dtype, int32_t out_dtype, float scale,
+                             const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             float *state, void *o, void *stream);
 
 /*
  * kda_fusion - the KDA layer's steps on either side of the core, done inside the kernels.

@@ -233,3 +233,27 @@ def test_short_conv_update_rejects_before_launch(lib, kw, status):
                                      base["x"], base["w"], base["b"], base["state"], base["y"],
                                      None) == status
     assert len(lib.kda_last_error()) > 0
+
+
+# ------------------------------------------------------------------ recurrent (L tokens)
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), INVALID), (dict(L=-1), INVALID), (dict(H=0), INVALID), (dict(ind=3), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(state=None), INVALID), (dict(o=None), INVALID),
+    (dict(g=None), INVALID), (dict(q=MIS), INVALID),
+    (dict(Dk=96, Dv=96), UNSUPPORTED), (dict(outd=BF16), UNSUPPORTED),
+])
+def test_recurrent_rejects_before_launch(lib, kw, status):
+    base = dict(N=4, L=3, H=2, Dk=128, Dv=128, ind=BF16, outd=F32, scale=1.0, q=P, k=P, v=P, g=P,
+                beta=P, state=P, o=P)
+    base.update(kw)
+    b = base
+    assert lib.kda_recurrent_fwd(b["N"], b["L"], b["H"], b["Dk"], b["Dv"], b["ind"], b["outd"],
+                                 b["scale"], b["q"], b["k"], b["v"], b["g"], b["beta"], b["state"],
+                                 b["o"], None) == status
+    assert len(lib.kda_last_error()) > 0
+
+
+def test_recurrent_zero_tokens_is_ok(lib):
+    assert lib.kda_recurrent_fwd(4, 0, 2, 128, 128, BF16, F32, 1.0, None, None, None, None, None,
+                                 P, None, None) == OK

@@ -1334,44 +1334,86 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
 }
 
 // Split combine: S_0 = the initial state (or zero), S_1 = R_0 (segment 0 ran from the
-// initial state), then S_{p+1} = X_p S_p + R_p. One workgroup per (chain, 16-column block);
-// float32 FMA with the running block in LDS. Writes ws_s[p] for p = 0 .. nseg-1.
+// initial state), then S_{p+1} = X_p S_p + R_p. One workgroup per (chain, 16-column block).
+// Each step is a [Dk x Dk] x [Dk x 16] product on the float32 matrix cores: every wave owns
+// 16-row tiles of the result, X_p is staged in LDS with coalesced 16-byte loads (rows padded
+// against bank conflicts) while X_{p+1}'s loads are in flight, and the running block S_p
+// stays in LDS, where the next step reads it as the B operand. Writes ws_s[p], p < nseg.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void split_combine_kernel(ChunkArgs a) {
-    __shared__ float cur[DK][16];
+    using ST = Step<float>;
+    constexpr int LDX = DK + 4;                  // padded row of X in LDS (floats)
+    constexpr int LDS_ = 20;                     // padded row of the running 16-column block
+    constexpr int PIECES = DK * DK / 4;          // 16-byte pieces of X
+    constexpr int NX = (PIECES + 255) / 256;     // ... per thread
+    constexpr int RT = DK / 16;                  // 16-row tiles of the result
+    constexpr int TPW = (RT + 3) / 4;            // ... per wave
+    __shared__ __attribute__((aligned(16))) float cur[DK * LDS_];
+    __shared__ __attribute__((aligned(16))) float Xs[DK * LDX];
     const int chains = a.n_seqs * a.H;
     const int chain = blockIdx.x / (DV / 16), cb = blockIdx.x % (DV / 16);
     if (chain >= chains) return;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, q4 = lane >> 4;
     const int64_t cstride = (int64_t)chains * DK * DV;
     float *const s_base = a.ws_s + (int64_t)chain * DK * DV + 16 * cb;
+    f32x4 xr[NX];      // the next X, in flight
+    f32x4 rr[TPW];     // ... and this lane's values of the next R
+    auto fetch_x = [&](int p) {
+        const f32x4 *X = reinterpret_cast<const f32x4 *>(a.ws_x + ((int64_t)p * chains + chain) * DK * DK);
+#pragma unroll
+        for (int i = 0; i < NX; ++i)
+            if (PIECES % 256 == 0 || tid + 256 * i < PIECES) xr[i] = X[tid + 256 * i];
+        const float *R = a.ws_r + ((int64_t)p * chains + chain) * DK * DV + 16 * cb;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int i = wave + 4 * t;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rr[t][e] = i < RT ? R[(int64_t)(16 * i + 4 * q4 + e) * DV + lr] : 0.f;
+        }
+    };
+    if (a.nseg > 2) fetch_x(1);
     for (int idx = tid; idx < DK * 16; idx += 256) {
         const int r = idx / 16, c = idx % 16;
         const int64_t e = (int64_t)chain * DK * DV + (int64_t)r * DV + 16 * cb + c;
         s_base[(int64_t)r * DV + c] = a.s0 ? a.s0[e] : 0.f;  // S_0
-        cur[r][c] = a.ws_r[e];                              // S_1 = R_0
+        cur[r * LDS_ + c] = a.ws_r[e];                      // S_1 = R_0
     }
     __syncthreads();
     for (int p = 1; p < a.nseg; ++p) {
         float *sp = s_base + p * cstride;
-        for (int idx = tid; idx < DK * 16; idx += 256) sp[(int64_t)(idx / 16) * DV + idx % 16] = cur[idx / 16][idx % 16];
+        for (int idx = tid; idx < DK * 16; idx += 256) sp[(int64_t)(idx / 16) * DV + idx % 16] = cur[(idx / 16) * LDS_ + idx % 16];
         if (p + 1 >= a.nseg) break;
-        // next = X_p cur + R_p
-        const float *X = a.ws_x + ((int64_t)p * chains + chain) * DK * DK;
-        const float *R = a.ws_r + ((int64_t)p * chains + chain) * DK * DV + 16 * cb;
-        constexpr int PER = DK * 16 / 256;  // outputs per thread
-        float acc[PER];
-        const int r = tid / (256 / DK), c0 = (tid % (256 / DK)) * PER;
+        // next = X_p cur + R_p, tile by tile: rows 16i + 4q + e, column lr in lane (lr, q)
 #pragma unroll
-        for (int u = 0; u < PER; ++u) acc[u] = R[(int64_t)r * DV + c0 + u];
-        for (int kk = 0; kk < DK; ++kk) {
-            const float x = X[(int64_t)r * DK + kk];
-#pragma unroll
-            for (int u = 0; u < PER; ++u) acc[u] += x * cur[kk][c0 + u];
+        for (int i = 0; i < NX; ++i) {
+            const int e = 4 * (tid + 256 * i);  // element index in X_p (row-major DK x DK)
+            if (PIECES % 256 == 0 || e < DK * DK) *reinterpret_cast<f32x4 *>(Xs + (e / DK) * LDX + e % DK) = xr[i];
         }
-        __syncthreads();
+        f32x4 acc[TPW];
 #pragma unroll
-        for (int u = 0; u < PER; ++u) cur[r][c0 + u] = acc[u];
+        for (int t = 0; t < TPW; ++t) acc[t] = rr[t];
+        __syncthreads();                      // X_p staged
+        if (p + 2 < a.nseg) fetch_x(p + 1);  // in flight during this step
+#pragma unroll
+        for (int ks = 0; ks < RT; ++ks) {     // reduction indices 16 ks .. 16 ks + 15
+            f32x4 b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[e] = cur[(16 * ks + 4 * q4 + e) * LDS_ + lr];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int i = wave + 4 * t;
+                if (i < RT) ST::mma(acc[t], ST::contig(Xs + (16 * i + lr) * LDX, 16 * ks, q4), b);
+            }
+        }
+        __syncthreads();                      // every reader of cur and Xs is done
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int i = wave + 4 * t;
+            if (i < RT) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cur[(16 * i + 4 * q4 + e) * LDS_ + lr] = acc[t][e];
+            }
+        }
         __syncthreads();
     }
 }

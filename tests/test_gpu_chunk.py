@@ -8,8 +8,8 @@ import pytest
 
 import gated_delta_rule_26_amd as kda
 import synth
-from kda_testutil import (assert_close, note, random_inputs, random_states, run_oracle, to_dev,
-                          torch_mod)
+from kda_testutil import (assert_close, f64, note, random_inputs, random_states, run_oracle,
+                          to_dev, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -310,3 +310,61 @@ def test_split_without_initial_state():
     o_ref, S_ref = run_oracle(x, "bf16")
     assert_close(o, o_ref, TOL_BF16, "o (split, no s0)")
     assert_close(S, S_ref, TOL_BF16, "final state (split, no s0)")
+
+
+# --------------------------------------------------------------- the method's degenerate cases
+
+DEGEN = [("bf16", 128, 64), ("f32", 32, 64), ("f32", 16, 16)]
+
+
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("stored,D,C", DEGEN)
+def test_no_decay_is_deltanet(stored, D, C, split):
+    """g = 0 (alpha = 1): the plain delta rule, with an initial state; unsplit and split."""
+    T, H = 2100, 2
+    x = random_inputs(400 + D, T, H, D, stored, g_const=0.0)
+    s0 = random_states(401, 1, H, D)
+    note(f"no decay {stored} D={D} split={split}")
+    o, S = gpu_chunk(x, stored, chunk=C, s0=s0, split=split)
+    o_ref, S_ref = run_oracle(x, stored, initial_state=s0)
+    tol = TOL_F32 if stored == "f32" else TOL_BF16
+    assert_close(o, o_ref, tol, "o")
+    assert_close(S, S_ref, tol, "final state")
+
+
+@pytest.mark.parametrize("stored,D,C", DEGEN)
+def test_zero_write_strength_is_pure_decay(stored, D, C):
+    """beta = 0: nothing is written; the state only decays, row by row (key channels), and
+    o_t reads the decayed initial state."""
+    T, H = 500, 2
+    x = random_inputs(410 + D, T, H, D, stored)
+    x["beta"][:] = 0.0
+    s0 = random_states(411, 1, H, D)
+    note(f"pure decay {stored} D={D}")
+    o, S = gpu_chunk(x, stored, chunk=C, s0=s0)
+    o_ref, S_ref = run_oracle(x, stored, initial_state=s0)
+    tol = TOL_F32 if stored == "f32" else TOL_BF16
+    assert_close(o, o_ref, tol, "o")
+    assert_close(S, S_ref, tol, "final state")
+    decay = np.exp(np.sum(f64(x["g"]), axis=0))               # [H, D]: per key channel
+    np.testing.assert_allclose(S_ref[0], s0[0] * decay[:, :, None], rtol=1e-10, atol=1e-300)
+
+
+@pytest.mark.parametrize("stored,D,C", DEGEN)
+def test_full_write_with_query_on_key_overwrites(stored, D, C):
+    """beta = 1 and q = k: each token overwrites the state along its key, so o_t is v_t
+    scaled by ||k_t||^2 plus what the decayed state held off that direction, which is
+    exactly 0 for a unit key (the rounded keys are off unit norm by ~3e-3 in bf16)."""
+    T, H = 300, 2
+    x = random_inputs(420 + D, T, H, D, stored)
+    x["beta"][:] = 1.0
+    x["q"] = x["k"].copy()
+    s0 = random_states(421, 1, H, D)
+    note(f"overwrite {stored} D={D}")
+    o, S = gpu_chunk(x, stored, chunk=C, s0=s0)
+    o_ref, S_ref = run_oracle(x, stored, initial_state=s0)
+    tol = TOL_F32 if stored == "f32" else TOL_BF16
+    assert_close(o, o_ref, tol, "o")
+    assert_close(S, S_ref, tol, "final state")
+    if stored == "f32":  # unit keys to float32 rounding: o_t = v_t
+        np.testing.assert_allclose(o_ref, f64(x["v"]), rtol=0, atol=1e-5 * np.sqrt(np.mean(o_ref ** 2)))

@@ -13,9 +13,12 @@
 // one token is HBM-bound (7 flops per 8 bytes); L tokens divide the state traffic by L.
 // One workgroup owns one (sequence, head) state. Threads tile the state as rows x float4
 // columns, so every wave reads and writes whole contiguous 512-byte rows; each thread keeps
-// its Dk*Dv/NT values in registers between the read and the write. Both column reductions
-// (p and r) are finished in the same sweep with cross-lane shuffles and one LDS exchange
-// between waves, then the rank-1 update is applied to the values still in registers.
+// its Dk*Dv/NT values in registers between the read and the write. The read is non-temporal
+// (measured faster, both when steps alternate with other kernels and back to back); the
+// write is not (a non-temporal write measured slower when steps alternate with other
+// kernels). Both column reductions (p and r) are finished in the same sweep with cross-lane
+// shuffles and one LDS exchange between waves, then the rank-1 update is applied to the
+// values still in registers.
 //
 // Fused layer steps (kda_decode_step_fused): the gate from its pre-activation,
 // g = -exp(A_log[h]) softplus(x + dt_bias[h, c]); q and k normalised, which only rescales the
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         if (t == 0) {
 #pragma unroll
             for (int p = 0; p < NPASS; ++p)
-                s[p] = *reinterpret_cast<const f32x4 *>(S + (p * RPP + rr) * DV + 4 * cg);
+                s[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (p * RPP + rr) * DV + 4 * cg));
         }
 
         if (wave == 0) {  // scale * (q . k) and the norms, off the critical path of the state sweep

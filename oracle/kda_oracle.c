@@ -147,3 +147,190 @@ int kda_oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Backward pass: the gradient of a scalar loss through the recurrence above, by reverse-mode
+ * differentiation of its five steps, token by token in reverse order (the training side of
+ * the layer: chunk mode is the one used for training, revolution page, the KDA section).
+ *
+ * Given the loss's gradients do_t = dL/do_t for every token and dS_T = dL/dS_final (NULL:
+ * zero), it returns dL/dq, dL/dk, dL/dv, dL/dg, dL/dbeta per token and dL/dS_init per
+ * (sequence, head). With dS the gradient with respect to the state after step t (from the
+ * later tokens), each token t in reverse order takes
+ *   5. o = S_t^T (scale q):  dq = scale S_t do,   dS += scale q do^T
+ *   4. S_t = S' + k u^T:     dk = dS u,           du = dS^T k          (S' = Diag(a) S_{t-1})
+ *      u = beta (v - p):     dv = beta du,        dbeta = du . (v - p),  dp = -beta du
+ *   3. p = S'^T k:           dS' = dS + k dp^T,   dk += S' dp
+ *   1-2. S' = Diag(e^g) S_{t-1}:
+ *                            dg[c] = sum_j S'[c][j] dS'[c][j]   (d e^g / dg = e^g)
+ *                            dS_{t-1} = Diag(a) dS'
+ * and dS_init is dS after the first token. The states S_{t-1} of every token of the chain
+ * are kept from a forward sweep (the same arithmetic as the forward above), so memory is
+ * (tokens of the chain) x K x V doubles per thread.
+ */
+static int chain_bwd(int64_t t0, int64_t t1, int64_t h, int64_t H, int64_t K, int64_t V,
+                     const double *q, const double *k, const double *v, const double *g,
+                     const double *beta, double scale, const double *s0, const double *dout,
+                     const double *dsT, double *dq, double *dk, double *dv, double *dg,
+                     double *dbeta, double *ds0)
+{
+    const int64_t L = t1 - t0, KV = K * V;
+    double *Sp = (double *)malloc((size_t)((L + 3) * KV + K + 4 * V + L * V) * sizeof(double));
+    if (!Sp)
+        return 2;
+    double *S = Sp + L * KV;      /* running state */
+    double *dS = S + KV;          /* gradient with respect to the state */
+    double *Sd = dS + KV;         /* S' of the current token */
+    double *a = Sd + KV;
+    double *p = a + K, *du = p + V, *dp = du + V, *tv = dp + V;
+    double *r = tv + V;           /* v_t - p_t of every token, [L][V] */
+
+    /* forward sweep: keep S_{t-1} and v_t - p_t */
+    if (s0)
+        memcpy(S, s0, (size_t)KV * sizeof(double));
+    else
+        memset(S, 0, (size_t)KV * sizeof(double));
+    for (int64_t t = t0; t < t1; ++t) {
+        const int64_t i = t - t0;
+        const double *kt = k + (t * H + h) * K, *gt = g + (t * H + h) * K;
+        const double *vt = v + (t * H + h) * V;
+        const double bt = beta[t * H + h];
+        memcpy(Sp + i * KV, S, (size_t)KV * sizeof(double));
+        for (int64_t c = 0; c < K; ++c)
+            a[c] = exp(gt[c]);
+        for (int64_t c = 0; c < K; ++c)
+            for (int64_t j = 0; j < V; ++j)
+                S[c * V + j] *= a[c];
+        for (int64_t j = 0; j < V; ++j)
+            p[j] = 0.0;
+        for (int64_t c = 0; c < K; ++c)
+            for (int64_t j = 0; j < V; ++j)
+                p[j] += S[c * V + j] * kt[c];
+        for (int64_t j = 0; j < V; ++j) {
+            r[i * V + j] = vt[j] - p[j];
+            p[j] = bt * r[i * V + j];
+        }
+        for (int64_t c = 0; c < K; ++c)
+            for (int64_t j = 0; j < V; ++j)
+                S[c * V + j] += kt[c] * p[j];
+    }
+
+    /* reverse sweep */
+    if (dsT)
+        memcpy(dS, dsT, (size_t)KV * sizeof(double));
+    else
+        memset(dS, 0, (size_t)KV * sizeof(double));
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+        const int64_t i = t - t0;
+        const double *qt = q + (t * H + h) * K, *kt = k + (t * H + h) * K;
+        const double *gt = g + (t * H + h) * K, *dot = dout + (t * H + h) * V;
+        const double bt = beta[t * H + h];
+        const double *rt = r + i * V;
+        double *dqt = dq + (t * H + h) * K, *dkt = dk + (t * H + h) * K;
+        double *dgt = dg + (t * H + h) * K, *dvt = dv + (t * H + h) * V;
+
+        /* recompute S' = Diag(a) S_{t-1}, u = beta (v - p) and S_t = S' + k u^T */
+        for (int64_t c = 0; c < K; ++c)
+            a[c] = exp(gt[c]);
+        for (int64_t c = 0; c < K; ++c)
+            for (int64_t j = 0; j < V; ++j)
+                Sd[c * V + j] = Sp[i * KV + c * V + j] * a[c];
+        for (int64_t j = 0; j < V; ++j)
+            tv[j] = bt * rt[j];     /* u */
+
+        /* 5: read-out */
+        for (int64_t c = 0; c < K; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < V; ++j)
+                acc += (Sd[c * V + j] + kt[c] * tv[j]) * dot[j];
+            dqt[c] = scale * acc;
+        }
+        for (int64_t c = 0; c < K; ++c)
+            for (int64_t j = 0; j < V; ++j)
+                dS[c * V + j] += scale * qt[c] * dot[j];
+
+        /* 4: write with u = beta (v - p) */
+        for (int64_t c = 0; c < K; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < V; ++j)
+                acc += dS[c * V + j] * tv[j];
+            dkt[c] = acc;
+        }
+        for (int64_t j = 0; j < V; ++j) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < K; ++c)
+                acc += dS[c * V + j] * kt[c];
+            du[j] = acc;
+        }
+        double db = 0.0;
+        for (int64_t j = 0; j < V; ++j) {
+            dvt[j] = bt * du[j];
+            db += du[j] * rt[j];
+            dp[j] = -bt * du[j];
+        }
+        dbeta[t * H + h] = db;
+
+        /* 3: prediction p = S'^T k */
+        for (int64_t c = 0; c < K; ++c)
+            for (int64_t j = 0; j < V; ++j)
+                dS[c * V + j] += kt[c] * dp[j];     /* dS now holds dS' */
+        for (int64_t c = 0; c < K; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < V; ++j)
+                acc += Sd[c * V + j] * dp[j];
+            dkt[c] += acc;
+        }
+
+        /* 1-2: decay */
+        for (int64_t c = 0; c < K; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < V; ++j)
+                acc += Sd[c * V + j] * dS[c * V + j];
+            dgt[c] = acc;
+        }
+        for (int64_t c = 0; c < K; ++c)
+            for (int64_t j = 0; j < V; ++j)
+                dS[c * V + j] *= a[c];
+    }
+    if (ds0)
+        memcpy(ds0, dS, (size_t)KV * sizeof(double));
+    free(Sp);
+    return 0;
+}
+
+/* Layouts as kda_oracle_fwd; dout [T_total, H, V]; dsT, ds0 [N, H, K, V] (dsT may be NULL:
+ * zero; ds0 may be NULL: not written). Returns 0, 1 (invalid arguments) or 2 (no memory). */
+int kda_oracle_bwd(int64_t n_seqs, const int64_t *cu_seqlens, int64_t H, int64_t K, int64_t V,
+                   const double *q, const double *k, const double *v, const double *g,
+                   const double *beta, double scale, const double *s0, const double *dout,
+                   const double *dsT, double *dq, double *dk, double *dv, double *dg,
+                   double *dbeta, double *ds0, int nthreads)
+{
+    if (n_seqs < 0 || H <= 0 || K <= 0 || V <= 0 || !cu_seqlens)
+        return 1;
+    if (cu_seqlens[0] != 0)
+        return 1;
+    for (int64_t n = 0; n < n_seqs; ++n)
+        if (cu_seqlens[n + 1] < cu_seqlens[n])
+            return 1;
+    if (cu_seqlens[n_seqs] > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv ||
+                                   !dg || !dbeta))
+        return 1;
+
+    const int64_t items = n_seqs * H;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+#endif
+    for (int64_t it = 0; it < items; ++it) {
+        const int64_t n = it / H, h = it % H;
+        const int64_t off = (n * H + h) * K * V;
+        err |= chain_bwd(cu_seqlens[n], cu_seqlens[n + 1], h, H, K, V, q, k, v, g, beta, scale,
+                         s0 ? s0 + off : NULL, dout, dsT ? dsT + off : NULL, dq, dk, dv, dg,
+                         dbeta, ds0 ? ds0 + off : NULL);
+    }
+    (void)nthreads;
+    return err;
+}

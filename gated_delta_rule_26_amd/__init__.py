@@ -15,7 +15,7 @@ import os
 
 __all__ = ["KdaError", "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_fused",
            "kda_decode_step_fused", "kda_recurrent_fwd", "kda_short_conv_fwd", "kda_short_conv_update",
-           "chunk_fwd_workspace_bytes", "load_library", "KDA_F32", "KDA_BF16"]
+           "kda_chunk_bwd", "chunk_fwd_workspace_bytes", "chunk_bwd_workspace_bytes", "load_library", "KDA_F32", "KDA_BF16"]
 
 KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
@@ -66,6 +66,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_chunk_fwd.restype = i32
     lib.kda_chunk_fwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, f32,
                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.kda_chunk_bwd_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [i32] * 8
+    lib.kda_chunk_bwd.restype = i32
+    lib.kda_chunk_bwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, f32,
+                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  vp, i32, vp, sz, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, f32,
                                     vp, vp, vp, vp, vp, vp, vp, vp]
@@ -240,6 +246,66 @@ def kda_chunk_fwd(q, k, v, g, beta, *, initial_state=None, output_final_state: b
                            _ptr(cu_seqlens), N, _ptr(workspace), ws, _stream(stream))
     _check(lib, st)
     return o, final_state
+
+
+def kda_chunk_bwd(q, k, v, g, beta, do, *, initial_state=None, dfinal_state=None,
+                  cu_seqlens=None, chunk: int = 64, scale: float = 1.0,
+                  want_dinitial_state: bool = True, grads=None, workspace=None, stream=None):
+    """Backward pass of ``kda_chunk_fwd`` (C: kda_chunk_bwd).
+
+    q, k, v, g, beta, initial_state, cu_seqlens, chunk and scale are those of the forward
+    call; do: float32 like v (dL/do); dfinal_state: float32 [N, H, Dk, Dv] (dL/dS_final) or
+    None (zero). ``grads`` may supply the five output tensors (dq, dk, dv, dg, dbeta) and
+    ``workspace`` a device uint8 tensor of at least ``chunk_bwd_workspace_bytes(...)`` bytes;
+    otherwise they are allocated. Returns (dq, dk, dv, dg, dbeta, dinitial_state or None),
+    all float32.
+    """
+    import torch
+    lib = load_library()
+    B, T, N, H, Dk, Dv = _prefill_layout(q, k, v, beta, cu_seqlens)
+    _req(g, "g", torch.float32)
+    if g.shape != q.shape:
+        raise ValueError("g must have q's shape")
+    _req(do, "do", torch.float32)
+    if do.shape != v.shape:
+        raise ValueError("do must have v's shape")
+    _prefill_states(q, N, H, Dk, Dv, initial_state, None, False)
+    if dfinal_state is not None:
+        _req(dfinal_state, "dfinal_state", torch.float32)
+        if tuple(dfinal_state.shape) != (N, H, Dk, Dv):
+            raise ValueError(f"dfinal_state must be [{N}, {H}, {Dk}, {Dv}]")
+    if grads is None:
+        grads = (None,) * 5
+    dq, dk, dv, dg, db = grads
+    dq = _out(dq, q, torch.float32, "dq")
+    dk = _out(dk, q, torch.float32, "dk")
+    dv = _out(dv, v, torch.float32, "dv")
+    dg = _out(dg, q, torch.float32, "dg")
+    db = _out(db, beta, torch.float32, "dbeta")
+    ds0 = (torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+           if want_dinitial_state else None)
+    need = lib.kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk, _dtype_code(q), N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _req(workspace, "workspace", torch.uint8)
+    st = lib.kda_chunk_bwd(B, T, H, Dk, Dv, chunk, _dtype_code(q), float(scale),
+                           _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                           _ptr(do), _ptr(dfinal_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                           _ptr(db), _ptr(ds0), _ptr(cu_seqlens), N, _ptr(workspace),
+                           workspace.numel(), _stream(stream))
+    _check(lib, st)
+    return dq, dk, dv, dg, db, ds0
+
+
+def chunk_bwd_workspace_bytes(q, v, *, chunk: int = 64, num_seqs: int | None = None) -> int:
+    """Bytes of workspace kda_chunk_bwd needs for q [B, T, H, Dk] (or [T, H, Dk] packed) / v
+    (C: kda_chunk_bwd_workspace_bytes)."""
+    lib = load_library()
+    B, T, H, Dk = q.shape if q.dim() == 4 else (1, *q.shape)
+    N = B if num_seqs is None else num_seqs
+    return int(lib.kda_chunk_bwd_workspace_bytes(B, T, H, Dk, v.shape[-1], chunk,
+                                                 _dtype_code(q), N))
 
 
 def chunk_fwd_workspace_bytes(q, v, *, chunk: int = 64, num_seqs: int | None = None) -> int:

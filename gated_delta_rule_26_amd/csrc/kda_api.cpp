@@ -127,6 +127,77 @@ kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv
                       "kda_chunk_fwd launch");
 }
 
+size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                                     int32_t chunk, int32_t in_dtype, int32_t num_seqs) {
+    if (!valid_dtype(in_dtype)) return 0;
+    return kda::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk, in_dtype, num_seqs);
+}
+
+kda_status kda_chunk_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                         int32_t in_dtype, float scale,
+                         const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *initial_state,
+                         const float *d_o, const float *d_final_state,
+                         float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                         float *d_initial_state,
+                         const int32_t *cu_seqlens, int32_t num_seqs,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || chunk < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive (B=%d T=%d H=%d Dk=%d Dv=%d chunk=%d)",
+                    B, T, H, Dk, Dv, chunk);
+    if (!valid_dtype(in_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype code (in=%d)", in_dtype);
+    if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (cu_seqlens) {
+        if (B != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens requires B == 1 (got B=%d)", B);
+        if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
+    } else if (num_seqs != B) {
+        return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs (%d) must equal B (%d) without cu_seqlens",
+                    num_seqs, B);
+    }
+    const int64_t tokens = (int64_t)B * T;
+    if (tokens * H * (Dk > Dv ? Dk : Dv) > ((int64_t)1 << 40))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "problem too large");
+    if (tokens > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, g, beta, d_o, dq, dk, dv, dg and dbeta are required");
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg, dbeta,
+                          d_initial_state, cu_seqlens, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    if (!kda::chunk_bwd_supported(in_dtype, chunk, Dk, Dv))
+        return fail(KDA_ERR_UNSUPPORTED, "no backward instantiation for in_dtype=%d chunk=%d Dk=%d Dv=%d",
+                    in_dtype, chunk, Dk, Dv);
+    const size_t need = kda::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk, in_dtype, num_seqs);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "kda_chunk_bwd needs %zu workspace bytes (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (num_seqs == 0) return ok();
+
+    kda::BwdArgs a;
+    a.n_seqs = num_seqs;
+    a.seq_len = T;
+    a.cu_seqlens = cu_seqlens;
+    a.H = H;
+    a.scale = scale;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.s0 = initial_state;
+    a.dout = d_o;
+    a.dsT = d_final_state;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dg = dg;
+    a.dbeta = dbeta;
+    a.ds0 = d_initial_state;
+    a.ws = static_cast<float *>(workspace);
+    a.nslots = num_seqs + (tokens + chunk - 1) / chunk;
+    return hip_status(kda::launch_chunk_bwd(in_dtype, chunk, Dk, Dv, a, static_cast<hipStream_t>(stream)),
+                      "kda_chunk_bwd launch");
+}
+
 kda_status kda_decode_step(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
                            int32_t in_dtype, int32_t out_dtype, float scale,
                            const void *q, const void *k, const void *v,

@@ -1,0 +1,859 @@
+// KDA chunked backward pass (gfx950): the gradients of a loss through the chunked prefill,
+// i.e. dq, dk, dv, dg, dbeta and dS_init from dL/do and dL/dS_final. Training runs the layer in
+// chunk mode only ([loading page] section 5, the mode switch); the forward it differentiates is
+// the chunkwise form of [KV-cache page] section 6.
+//
+// Per chunk of C tokens, with G_i the running sum of g inside the chunk, gC = G_{C-1}, S the
+// state entering the chunk and dS' = dL/d(state leaving it), the forward computes
+//   A~_ij = sum_c k_i k_j e^{G_i - G_j} (j < i),  M_ij = scale sum_c q_i k_j e^{G_i - G_j} (j <= i)
+//   T = (I + Diag(beta) A~)^-1,  W = T Diag(beta) (k e^G),  U~ = T Diag(beta) V
+//   U = U~ - W S,  O = (scale q e^G) S + M U,  S' = Diag(e^{gC}) S + (k e^{gC - G})^T U
+// and its reverse-mode derivative is, with Qg = scale q e^G, Kd = k e^{gC - G}, Kg = k e^G,
+//   dU  = M^T dO + Kd dS'                        dS = Diag(e^{gC}) dS' + Qg^T dO - W^T dU
+//   dQg = dO S^T,  dKd = U dS'^T,  dW = -dU S^T,  dM = tril(dO U^T),  d e^{gC} = rowsum(S * dS')
+//   dT  = dU (Diag(beta) V)^T + dW (Diag(beta) Kg)^T
+//   dv  = Diag(beta) T^T dU,  dKg = Diag(beta) T^T dW,  dA = -strictly_lower(T^T dT T^T)
+// plus the pairwise terms of A~ and M (per channel, e^{G_i - G_j} <= 1 for j <= i) and, for g,
+// the reverse running sum of dL/dG inside the chunk.
+//
+// Mapping to the MI355X. Everything is float32 (fp32 matrix cores, v_mfma_f32_16x16x4f32).
+// Five kernels, each a plain pass over a per-(chunk, head) record in the workspace:
+//  1. prep    (one workgroup per chunk and head): G, Qg, Kd, e^{gC}, A~ and M pair by pair (one
+//             exp per pair and channel: exact for any decay), T by column substitution in one
+//             wave, W and U~ on the matrix cores.
+//  2. forward state pass (per chain and 16 value columns, chunks in order): stores the state
+//             entering each chunk and U; the waves split the key channels and sum U through LDS.
+//  3. reverse state pass (per chain and 16 value columns, chunks in reverse): stores dS' and dU,
+//             writes dS_init.
+//  4. grad1   (per chunk and head): the products with S, dS', U and dU, then T^T dW, T^T dU and
+//             T^T dT T^T; writes dv and dbeta, partial dq, dk, dG and the pair gradients dA~, dM.
+//  5. grad2   (per chunk, head and 64 channels): the pair terms, one thread per channel and
+//             direction, then the reverse running sum of dG.
+// Chunks of a packed batch are numbered by slot n + floor(start_n / C) + j (sequence n, chunk j),
+// which is unique and below N + ceil(tokens / C), so the records need no host-side lengths.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+// Per-(chunk, head) record in the workspace (float offsets; rows are tokens of the chunk).
+template <int C, int DK, int DV> struct BRec {
+    static constexpr int64_t oG = 0;                  // [C][DK] G (running sum of g)
+    static constexpr int64_t oQg = oG + C * DK;       // [C][DK] scale q e^G
+    static constexpr int64_t oKd = oQg + C * DK;      // [C][DK] k e^{gC - G}
+    static constexpr int64_t oW = oKd + C * DK;       // [C][DK] W
+    static constexpr int64_t oU = oW + C * DK;        // [C][DV] U~, then U
+    static constexpr int64_t odU = oU + C * DV;       // [C][DV] dU
+    static constexpr int64_t oEg = odU + C * DV;      // [DK]    e^{gC}
+    static constexpr int64_t oA = oEg + DK;           // [C][C]  A~ (strictly lower), then dA~
+    static constexpr int64_t oM = oA + C * C;         // [C][C]  M (lower), then dM
+    static constexpr int64_t oT = oM + C * C;         // [C][C]  T
+    static constexpr int64_t oH = oT + C * C;         // [DK][DV] state entering the chunk
+    static constexpr int64_t odH = oH + DK * DV;      // [DK][DV] dL/d(state leaving the chunk)
+    static constexpr int64_t FLOATS = (odH + DK * DV + 63) & ~int64_t(63);
+};
+
+__device__ __forceinline__ int64_t seq_start(const BwdArgs &a, int n) {
+    return a.cu_seqlens ? (int64_t)a.cu_seqlens[n] : (int64_t)n * a.seq_len;
+}
+
+template <int C> __device__ __forceinline__ int64_t slot_base(const BwdArgs &a, int n) {
+    return n + seq_start(a, n) / C;
+}
+
+// The chunk of record slot s: its sequence n, first token t0 and valid rows L (false: unused).
+template <int C> __device__ bool locate(const BwdArgs &a, int64_t s, int &n, int64_t &t0, int &L) {
+    int lo = 0, hi = a.n_seqs - 1;  // the last n with slot_base(n) <= s (strictly increasing)
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (slot_base<C>(a, mid) <= s) lo = mid;
+        else hi = mid - 1;
+    }
+    n = lo;
+    const int64_t st = seq_start(a, n), len = seq_start(a, n + 1) - st;
+    const int64_t j = s - slot_base<C>(a, n);
+    if (j < 0 || j * C >= len) return false;
+    t0 = st + j * C;
+    L = (int)(len - j * C < C ? len - j * C : C);
+    return true;
+}
+
+__device__ __forceinline__ float sum16(float x) {  // over the 16 lanes of a row
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+
+__device__ __forceinline__ void mma(f32x4 &acc, f32x4 a, f32x4 b) { Mma<float>::mma(acc, a, b); }
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ------------------------------------------------------------------------------------------
+// 1. prep
+// ------------------------------------------------------------------------------------------
+template <typename Tin, int C, int DK, int DV>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+    using R = BRec<C, DK, DV>;
+    constexpr int NT = 256;
+    constexpr int DX = DK > DV ? DK : DV;
+    constexpr int LDK = DK + 4, LDX = DX + 4, LDA = C + 4;
+    __shared__ __align__(16) float sK[C * LDK];
+    __shared__ __align__(16) float sQ[C * LDX];   // q, then beta k e^G
+    __shared__ __align__(16) float sG[C * LDX];   // G, then beta v
+    __shared__ __align__(16) float sA[C * LDA];   // A~
+    __shared__ __align__(16) float sT[C * LDA];   // T
+    __shared__ float sB[C];
+
+    const int64_t s = blockIdx.x;
+    const int h = blockIdx.y;
+    int n, L;
+    int64_t t0;
+    if (!locate<C>(a, s, n, t0, L)) return;
+    float *rec = a.ws + (s * a.H + h) * R::FLOATS;
+    const int tid = threadIdx.x;
+    const int64_t rsk = (int64_t)a.H * DK, rsv = (int64_t)a.H * DV;
+
+    for (int idx = tid; idx < C * DK / 4; idx += NT) {
+        const int i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+        f32x4 kv = zero4(), qv = zero4(), gv = zero4();
+        if (i < L) {
+            const int64_t off = (t0 + i) * rsk + (int64_t)h * DK + c;
+            kv = load4(static_cast<const Tin *>(a.k) + off);
+            qv = load4(static_cast<const Tin *>(a.q) + off);
+            gv = load4(a.g + off);
+        }
+        *reinterpret_cast<f32x4 *>(sK + i * LDK + c) = kv;
+        *reinterpret_cast<f32x4 *>(sQ + i * LDX + c) = qv;
+        *reinterpret_cast<f32x4 *>(sG + i * LDX + c) = gv;
+    }
+    if (tid < C) sB[tid] = tid < L ? a.beta[(t0 + tid) * a.H + h] : 0.f;
+    __syncthreads();
+    if (tid < DK) {  // running sum along the chunk, one thread per channel
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            acc += sG[i * LDX + tid];
+            sG[i * LDX + tid] = acc;
+        }
+        rec[R::oEg + tid] = __expf(acc);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < C * DK / 4; idx += NT) {
+        const int i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+        const f32x4 G = *reinterpret_cast<const f32x4 *>(sG + i * LDX + c);
+        const f32x4 gC = *reinterpret_cast<const f32x4 *>(sG + (C - 1) * LDX + c);
+        const f32x4 kv = *reinterpret_cast<const f32x4 *>(sK + i * LDK + c);
+        const f32x4 qv = *reinterpret_cast<const f32x4 *>(sQ + i * LDX + c);
+        f32x4 qg, kd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qg[e] = a.scale * qv[e] * __expf(G[e]);
+            kd[e] = kv[e] * __expf(gC[e] - G[e]);
+        }
+        *reinterpret_cast<f32x4 *>(rec + R::oG + i * DK + c) = G;
+        *reinterpret_cast<f32x4 *>(rec + R::oQg + i * DK + c) = qg;
+        *reinterpret_cast<f32x4 *>(rec + R::oKd + i * DK + c) = kd;
+    }
+    // A~ and M pair by pair: pair p of the lower triangle is row i, column j <= i
+    constexpr int NP = C * (C + 1) / 2;
+    for (int p = tid; p < NP; p += NT) {
+        int i = (int)((__builtin_sqrtf(8.f * (float)p + 1.f) - 1.f) * 0.5f);
+        while ((i + 1) * (i + 2) / 2 <= p) ++i;
+        while (i * (i + 1) / 2 > p) --i;
+        const int j = p - i * (i + 1) / 2;
+        float sa = 0.f, sm = 0.f;
+#pragma unroll 4
+        for (int c = 0; c < DK; c += 4) {
+            const f32x4 ki = *reinterpret_cast<const f32x4 *>(sK + i * LDK + c);
+            const f32x4 kj = *reinterpret_cast<const f32x4 *>(sK + j * LDK + c);
+            const f32x4 qi = *reinterpret_cast<const f32x4 *>(sQ + i * LDX + c);
+            const f32x4 Gi = *reinterpret_cast<const f32x4 *>(sG + i * LDX + c);
+            const f32x4 Gj = *reinterpret_cast<const f32x4 *>(sG + j * LDX + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float kjE = kj[e] * __expf(Gi[e] - Gj[e]);
+                sa += ki[e] * kjE;
+                sm += qi[e] * kjE;
+            }
+        }
+        const float av = j < i ? sa : 0.f;
+        sA[i * LDA + j] = av;
+        rec[R::oA + i * C + j] = av;
+        rec[R::oM + i * C + j] = a.scale * sm;
+    }
+    for (int p = tid; p < C * C; p += NT) {
+        const int i = p / C, j = p % C;
+        if (j > i) {
+            sA[i * LDA + j] = 0.f;
+            rec[R::oA + p] = 0.f;
+            rec[R::oM + p] = 0.f;
+        }
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // T = (I + Diag(beta) A~)^-1 by forward substitution, lane = column
+        const int col = tid;
+        float x[C];
+#pragma unroll
+        for (int i = 0; i < C; ++i) x[i] = 0.f;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < (i + 3) / 4 * 4; m += 4) {
+                const f32x4 ar = *reinterpret_cast<const f32x4 *>(sA + i * LDA + m);
+                acc += ar[0] * x[m] + ar[1] * x[m + 1] + ar[2] * x[m + 2] + ar[3] * x[m + 3];
+            }
+            x[i] = (i == col ? 1.f : 0.f) - sB[i] * acc;
+        }
+        if (col < C) {
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                sT[i * LDA + col] = x[i];
+                rec[R::oT + i * C + col] = x[i];
+            }
+        }
+    } else {
+        for (int idx = tid - 64; idx < C * DK / 4; idx += NT - 64) {  // beta k e^G over q
+            const int i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+            const f32x4 kv = *reinterpret_cast<const f32x4 *>(sK + i * LDK + c);
+            const f32x4 G = *reinterpret_cast<const f32x4 *>(sG + i * LDX + c);
+            f32x4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = sB[i] * kv[e] * __expf(G[e]);
+            *reinterpret_cast<f32x4 *>(sQ + i * LDX + c) = r;
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < C * DV / 4; idx += NT) {  // beta v over G
+        const int i = idx / (DV / 4), c = 4 * (idx % (DV / 4));
+        f32x4 vv = zero4();
+        if (i < L) vv = load4(static_cast<const Tin *>(a.v) + (t0 + i) * rsv + (int64_t)h * DV + c);
+        *reinterpret_cast<f32x4 *>(sG + i * LDX + c) = vv * sB[i];
+    }
+    __syncthreads();
+    // W = T (beta k e^G), U~ = T (beta v): 16 x 16 tiles over the waves
+    const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, q4 = lane >> 4;
+    constexpr int TW = (C / 16) * (DK / 16), TU = (C / 16) * (DV / 16);
+    for (int t = wave; t < TW + TU; t += NT / 64) {
+        const bool isW = t < TW;
+        const int tt = isW ? t : t - TW;
+        const int nct = isW ? DK / 16 : DV / 16;
+        const int it = tt / nct, nt = tt % nct;
+        const float *X = isW ? sQ : sG;
+        f32x4 acc = zero4();
+        for (int ms = 0; ms <= it; ++ms) {
+            const int m0 = 16 * ms + 4 * q4;
+            const f32x4 A = *reinterpret_cast<const f32x4 *>(sT + (16 * it + lr) * LDA + m0);
+            f32x4 B;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) B[e] = X[(m0 + e) * LDX + 16 * nt + lr];
+            mma(acc, A, B);
+        }
+        float *dst = rec + (isW ? R::oW : R::oU);
+        const int ld = isW ? DK : DV;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(16 * it + 4 * q4 + e) * ld + 16 * nt + lr] = acc[e];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// 2. forward state pass: one workgroup per (chain, 16 value columns); wave w holds the 16x16
+//    state tiles of its key-channel tiles in accumulator registers.
+// ------------------------------------------------------------------------------------------
+template <int C, int DK, int DV> struct StatePass {
+    static constexpr int KT = DK / 16;
+    static constexpr int NW = KT < 4 ? KT : 4;
+    static constexpr int KTW = KT / NW;
+    static constexpr int IT = C / 16;
+    static_assert(KT % NW == 0, "key tiles spread evenly");
+};
+
+template <int C, int DK, int DV>
+__global__ __launch_bounds__(256) void bwd_fwd_state_kernel(BwdArgs a) {
+    using R = BRec<C, DK, DV>;
+    using P = StatePass<C, DK, DV>;
+    constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW;
+    __shared__ f32x4 sPart[NW][IT][64];
+    const int chain = blockIdx.x, vb = blockIdx.y;
+    const int n = chain / a.H, h = chain % a.H;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, q4 = lane >> 4;
+    const int64_t st = seq_start(a, n), len = seq_start(a, n + 1) - st;
+    const int nch = (int)((len + C - 1) / C);
+    const int64_t base = slot_base<C>(a, n);
+    const int col = 16 * vb + lr;
+
+    f32x4 S[KTW];
+#pragma unroll
+    for (int kk = 0; kk < KTW; ++kk) {
+        const int kt = wave * KTW + kk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[kk][e] = a.s0 ? a.s0[(((int64_t)n * a.H + h) * DK + 16 * kt + 4 * q4 + e) * DV + col] : 0.f;
+    }
+    for (int j = 0; j < nch; ++j) {
+        float *rec = a.ws + ((base + j) * a.H + h) * R::FLOATS;
+#pragma unroll
+        for (int kk = 0; kk < KTW; ++kk) {
+            const int kt = wave * KTW + kk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rec[R::oH + (16 * kt + 4 * q4 + e) * DV + col] = S[kk][e];
+        }
+        f32x4 part[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < KTW; ++kk) {
+                const int kt = wave * KTW + kk;
+                mma(acc, *reinterpret_cast<const f32x4 *>(rec + R::oW + (16 * it + lr) * DK + 16 * kt + 4 * q4),
+                    S[kk]);
+            }
+            if (it % NW == wave) {  // the owner of row tile it adds U~ (and later stores U there)
+                f32x4 ut;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ut[e] = rec[R::oU + (16 * it + 4 * q4 + e) * DV + col];
+                part[it] = ut - acc;
+            } else {
+                part[it] = -acc;
+            }
+            sPart[wave][it][lane] = part[it];
+        }
+        __syncthreads();
+        f32x4 U[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            U[it] = sPart[0][it][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) U[it] += sPart[w][it][lane];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+            if (it % NW == wave) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rec[R::oU + (16 * it + 4 * q4 + e) * DV + col] = U[it][e];
+            }
+#pragma unroll
+        for (int kk = 0; kk < KTW; ++kk) {
+            const int kt = wave * KTW + kk;
+            f32x4 eg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) eg[e] = rec[R::oEg + 16 * kt + 4 * q4 + e];
+            S[kk] *= eg;
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                f32x4 A;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) A[e] = rec[R::oKd + (16 * it + 4 * q4 + e) * DK + 16 * kt + lr];
+                mma(S[kk], A, U[it]);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// 3. reverse state pass: dS held like S above, chunks in reverse order.
+// ------------------------------------------------------------------------------------------
+template <int C, int DK, int DV>
+__global__ __launch_bounds__(256) void bwd_rev_state_kernel(BwdArgs a) {
+    using R = BRec<C, DK, DV>;
+    using P = StatePass<C, DK, DV>;
+    constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW;
+    __shared__ f32x4 sPart[NW][IT][64];
+    const int chain = blockIdx.x, vb = blockIdx.y;
+    const int n = chain / a.H, h = chain % a.H;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, q4 = lane >> 4;
+    const int64_t st = seq_start(a, n), len = seq_start(a, n + 1) - st;
+    const int nch = (int)((len + C - 1) / C);
+    const int64_t base = slot_base<C>(a, n);
+    const int col = 16 * vb + lr;
+    const int64_t sbase = ((int64_t)n * a.H + h) * DK;
+
+    f32x4 dS[KTW];
+#pragma unroll
+    for (int kk = 0; kk < KTW; ++kk) {
+        const int kt = wave * KTW + kk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dS[kk][e] = a.dsT ? a.dsT[(sbase + 16 * kt + 4 * q4 + e) * DV + col] : 0.f;
+    }
+    for (int j = nch - 1; j >= 0; --j) {
+        float *rec = a.ws + ((base + j) * a.H + h) * R::FLOATS;
+        const int64_t t0 = st + (int64_t)j * C;
+        const int L = (int)(len - (int64_t)j * C < C ? len - (int64_t)j * C : C);
+#pragma unroll
+        for (int kk = 0; kk < KTW; ++kk) {
+            const int kt = wave * KTW + kk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rec[R::odH + (16 * kt + 4 * q4 + e) * DV + col] = dS[kk][e];
+        }
+        f32x4 dOf[IT];  // dO rows 16 ms + 4 q4 + e, column col (zero past the sequence end)
+#pragma unroll
+        for (int ms = 0; ms < IT; ++ms)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * ms + 4 * q4 + e;
+                dOf[ms][e] = r < L ? a.dout[((t0 + r) * a.H + h) * DV + col] : 0.f;
+            }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < KTW; ++kk) {
+                const int kt = wave * KTW + kk;
+                mma(acc, *reinterpret_cast<const f32x4 *>(rec + R::oKd + (16 * it + lr) * DK + 16 * kt + 4 * q4),
+                    dS[kk]);
+            }
+            if (it % NW == wave) {  // M^T dO for the owned row tile (M[m][i] = 0 for m < i)
+#pragma unroll
+                for (int ms = it; ms < IT; ++ms) {
+                    f32x4 A;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) A[e] = rec[R::oM + (16 * ms + 4 * q4 + e) * C + 16 * it + lr];
+                    mma(acc, A, dOf[ms]);
+                }
+            }
+            sPart[wave][it][lane] = acc;
+        }
+        __syncthreads();
+        f32x4 dU[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            dU[it] = sPart[0][it][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) dU[it] += sPart[w][it][lane];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+            if (it % NW == wave) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rec[R::odU + (16 * it + 4 * q4 + e) * DV + col] = dU[it][e];
+            }
+#pragma unroll
+        for (int kk = 0; kk < KTW; ++kk) {
+            const int kt = wave * KTW + kk;
+            f32x4 eg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) eg[e] = rec[R::oEg + 16 * kt + 4 * q4 + e];
+            dS[kk] *= eg;
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                f32x4 Aq, Aw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Aq[e] = rec[R::oQg + (16 * it + 4 * q4 + e) * DK + 16 * kt + lr];
+                    Aw[e] = -rec[R::oW + (16 * it + 4 * q4 + e) * DK + 16 * kt + lr];
+                }
+                mma(dS[kk], Aq, dOf[it]);
+                mma(dS[kk], Aw, dU[it]);
+            }
+        }
+    }
+    if (a.ds0) {
+#pragma unroll
+        for (int kk = 0; kk < KTW; ++kk) {
+            const int kt = wave * KTW + kk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.ds0[(sbase + 16 * kt + 4 * q4 + e) * DV + col] = dS[kk][e];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// 4. grad1: one workgroup of 8 waves per (chunk, head)
+// ------------------------------------------------------------------------------------------
+template <typename Tin, int C, int DK, int DV>
+__global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
+    using R = BRec<C, DK, DV>;
+    constexpr int NT = 512, NWV = 8, IT = C / 16, KT = DK / 16, VT = DV / 16;
+    constexpr int NLT = IT * (IT + 1) / 2;  // lower-triangle 16x16 tiles (it >= mt)
+    constexpr int LDK = DK + 4, LDA = C + 4;
+    constexpr int NSRC = KT + VT + IT;      // dbeta partial sums, one row per source
+    static_assert(KT <= NWV && VT <= NWV, "one key / value column tile per wave");
+    __shared__ __align__(16) float sW[C * LDK];   // dW
+    __shared__ __align__(16) float sT[C * LDA];   // T
+    __shared__ __align__(16) float sdT[C * LDA];  // dT
+    __shared__ __align__(16) float sX[C * LDA];   // T^T dT
+    __shared__ float sDb[NSRC][C];
+
+    const int64_t s = blockIdx.x;
+    const int h = blockIdx.y;
+    int n, L;
+    int64_t t0;
+    if (!locate<C>(a, s, n, t0, L)) return;
+    float *rec = a.ws + (s * a.H + h) * R::FLOATS;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, q4 = lane >> 4;
+    const int64_t rsk = (int64_t)a.H * DK, rsv = (int64_t)a.H * DV;
+    const Tin *kin = static_cast<const Tin *>(a.k);
+    const Tin *vin = static_cast<const Tin *>(a.v);
+    auto tile_of = [](int p, int &it, int &mt) {  // p-th lower tile, row-major
+        it = 0;
+        while ((it + 1) * (it + 2) / 2 <= p) ++it;
+        mt = p - it * (it + 1) / 2;
+    };
+    auto beta_of = [&](int i) { return i < L ? a.beta[(t0 + i) * a.H + h] : 0.f; };
+
+    for (int idx = tid; idx < C * C / 4; idx += NT) {
+        const int i = idx / (C / 4), m = 4 * (idx % (C / 4));
+        *reinterpret_cast<f32x4 *>(sT + i * LDA + m) = *reinterpret_cast<const f32x4 *>(rec + R::oT + i * C + m);
+    }
+    for (int idx = tid; idx < NSRC * C; idx += NT) (&sDb[0][0])[idx] = 0.f;
+    for (int p = tid; p < C * C; p += NT) {  // dT above the diagonal tiles is never formed
+        const int i = p / C, m = p % C;
+        if ((m >> 4) > (i >> 4)) sdT[i * LDA + m] = 0.f;
+    }
+
+    // dQg = dO S^T, dKd = U dS'^T, dW = -dU S^T for key tile ct = wave
+    const int ct = wave;
+    f32x4 dq_p[IT], dk_p[IT], dG_p[IT];
+    if (ct < KT) {
+        f32x4 aQ[IT], aK[IT], aW[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) aQ[it] = aK[it] = aW[it] = zero4();
+        for (int js = 0; js < VT; ++js) {
+            const int j0 = 16 * js + 4 * q4;
+            const f32x4 hB = *reinterpret_cast<const f32x4 *>(rec + R::oH + (16 * ct + lr) * DV + j0);
+            const f32x4 dhB = *reinterpret_cast<const f32x4 *>(rec + R::odH + (16 * ct + lr) * DV + j0);
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int i = 16 * it + lr;
+                f32x4 dOa = zero4();
+                if (i < L) dOa = *reinterpret_cast<const f32x4 *>(a.dout + ((t0 + i) * a.H + h) * DV + j0);
+                const f32x4 Ua = *reinterpret_cast<const f32x4 *>(rec + R::oU + i * DV + j0);
+                const f32x4 dUa = *reinterpret_cast<const f32x4 *>(rec + R::odU + i * DV + j0);
+                mma(aQ[it], dOa, hB);
+                mma(aK[it], Ua, dhB);
+                mma(aW[it], dUa, hB);
+            }
+        }
+        const int c = 16 * ct + lr;
+        const float gC = rec[R::oG + (C - 1) * DK + c];
+        float cs = 0.f;
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * it + 4 * q4 + e;
+                const float G = rec[R::oG + i * DK + c], Qg = rec[R::oQg + i * DK + c];
+                const float Kd = rec[R::oKd + i * DK + c];
+                sW[i * LDK + c] = -aW[it][e];
+                dq_p[it][e] = a.scale * __expf(G) * aQ[it][e];
+                dk_p[it][e] = __expf(gC - G) * aK[it][e];
+                dG_p[it][e] = Qg * aQ[it][e] - Kd * aK[it][e];
+                cs += Kd * aK[it][e];
+            }
+        cs += __shfl_xor(cs, 16);
+        cs += __shfl_xor(cs, 32);
+        // d e^{gC}: sum_j S[c][j] dS'[c][j]; lane (lr, q4) takes columns 16 js + 4 q4 .. + 3
+        float dgc = 0.f;
+        for (int js = 0; js < VT; ++js) {
+            const f32x4 hv = *reinterpret_cast<const f32x4 *>(rec + R::oH + c * DV + 16 * js + 4 * q4);
+            const f32x4 dhv = *reinterpret_cast<const f32x4 *>(rec + R::odH + c * DV + 16 * js + 4 * q4);
+            dgc += hv[0] * dhv[0] + hv[1] * dhv[1] + hv[2] * dhv[2] + hv[3] * dhv[3];
+        }
+        dgc += __shfl_xor(dgc, 16);
+        dgc += __shfl_xor(dgc, 32);
+        // gC is G of the last valid row (g is zero past it): its gradient goes to row L - 1
+        const float term = rec[R::oEg + c] * dgc + cs;
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (16 * it + 4 * q4 + e == L - 1) dG_p[it][e] += term;
+    }
+    // dM = tril(dO U^T), written over M
+    for (int p = wave; p < NLT; p += NWV) {
+        int it, mt;
+        tile_of(p, it, mt);
+        f32x4 acc = zero4();
+        const int i = 16 * it + lr;
+        for (int js = 0; js < VT; ++js) {
+            const int j0 = 16 * js + 4 * q4;
+            f32x4 dOa = zero4();
+            if (i < L) dOa = *reinterpret_cast<const f32x4 *>(a.dout + ((t0 + i) * a.H + h) * DV + j0);
+            mma(acc, dOa, *reinterpret_cast<const f32x4 *>(rec + R::oU + (16 * mt + lr) * DV + j0));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * it + 4 * q4 + e, m = 16 * mt + lr;
+            rec[R::oM + r * C + m] = m <= r ? acc[e] : 0.f;
+        }
+    }
+    __syncthreads();  // sW, sT, sdT zeros, sDb ready
+
+    // dT = dU (beta v)^T + dW (beta k e^G)^T, lower tiles
+    for (int p = wave; p < NLT; p += NWV) {
+        int it, mt;
+        tile_of(p, it, mt);
+        const int m = 16 * mt + lr;
+        const float bm = beta_of(m);
+        f32x4 acc = zero4();
+        for (int js = 0; js < VT; ++js) {
+            const int j0 = 16 * js + 4 * q4;
+            f32x4 vb = zero4();
+            if (m < L) vb = load4(vin + (t0 + m) * rsv + (int64_t)h * DV + j0) * bm;
+            mma(acc, *reinterpret_cast<const f32x4 *>(rec + R::odU + (16 * it + lr) * DV + j0), vb);
+        }
+        for (int cs = 0; cs < KT; ++cs) {
+            const int c0 = 16 * cs + 4 * q4;
+            f32x4 kb = zero4();
+            if (m < L) {
+                const f32x4 kv = load4(kin + (t0 + m) * rsk + (int64_t)h * DK + c0);
+                const f32x4 G = *reinterpret_cast<const f32x4 *>(rec + R::oG + m * DK + c0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kb[e] = bm * kv[e] * __expf(G[e]);
+            }
+            mma(acc, *reinterpret_cast<const f32x4 *>(sW + (16 * it + lr) * LDK + c0), kb);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sdT[(16 * it + 4 * q4 + e) * LDA + m] = acc[e];
+    }
+    // dKg = Diag(beta) T^T dW for key tile ct (T[m][i] = 0 for m < i)
+    if (ct < KT) {
+        const int c = 16 * ct + lr;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            f32x4 acc = zero4();
+            for (int ms = it; ms < IT; ++ms) {
+                f32x4 A, B;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = 16 * ms + 4 * q4 + e;
+                    A[e] = sT[m * LDA + 16 * it + lr];
+                    B[e] = sW[m * LDK + c];
+                }
+                mma(acc, A, B);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * it + 4 * q4 + e;
+                const float bi = beta_of(i);
+                const float G = rec[R::oG + i * DK + c];
+                const float eG = __expf(G);
+                const float kv = i < L ? to_f32(kin[(t0 + i) * rsk + (int64_t)h * DK + c]) : 0.f;
+                const float dKg = bi * acc[e];
+                dk_p[it][e] += eG * dKg;
+                dG_p[it][e] += kv * eG * dKg;
+                const float rs = sum16(acc[e] * kv * eG);
+                if (lr == 0) sDb[ct][i] = rs;
+                if (i < L) {
+                    const int64_t o = (t0 + i) * rsk + (int64_t)h * DK + c;
+                    a.dq[o] = dq_p[it][e];
+                    a.dk[o] = dk_p[it][e];
+                    a.dg[o] = dG_p[it][e];
+                }
+            }
+        }
+    }
+    // dv = Diag(beta) T^T dU for value tile vt = wave
+    if (wave < VT) {
+        const int vt = wave, j = 16 * vt + lr;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            f32x4 acc = zero4();
+            for (int ms = it; ms < IT; ++ms) {
+                f32x4 A, B;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = 16 * ms + 4 * q4 + e;
+                    A[e] = sT[m * LDA + 16 * it + lr];
+                    B[e] = rec[R::odU + m * DV + j];
+                }
+                mma(acc, A, B);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * it + 4 * q4 + e;
+                const float vv = i < L ? to_f32(vin[(t0 + i) * rsv + (int64_t)h * DV + j]) : 0.f;
+                const float rs = sum16(acc[e] * vv);
+                if (lr == 0) sDb[KT + vt][i] = rs;
+                if (i < L) a.dv[(t0 + i) * rsv + (int64_t)h * DV + j] = beta_of(i) * acc[e];
+            }
+        }
+    }
+    __syncthreads();  // sdT complete
+    // X = T^T dT (lower tiles suffice)
+    for (int p = wave; p < NLT; p += NWV) {
+        int it, lt;
+        tile_of(p, it, lt);
+        f32x4 acc = zero4();
+        for (int ms = it; ms < IT; ++ms) {
+            f32x4 A, B;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = 16 * ms + 4 * q4 + e;
+                A[e] = sT[m * LDA + 16 * it + lr];
+                B[e] = sdT[m * LDA + 16 * lt + lr];
+            }
+            mma(acc, A, B);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sX[(16 * it + 4 * q4 + e) * LDA + 16 * lt + lr] = acc[e];
+    }
+    __syncthreads();
+    // dA = -strictly_lower(X T^T); dbeta += rowsum(dA A~); dA~ = Diag(beta) dA over A~
+    for (int p = wave; p < NLT; p += NWV) {
+        int it, jt;
+        tile_of(p, it, jt);
+        f32x4 acc = zero4();
+        for (int ls = 0; ls <= jt; ++ls) {
+            const f32x4 A = *reinterpret_cast<const f32x4 *>(sX + (16 * it + lr) * LDA + 16 * ls + 4 * q4);
+            const f32x4 B = *reinterpret_cast<const f32x4 *>(sT + (16 * jt + lr) * LDA + 16 * ls + 4 * q4);
+            mma(acc, A, B);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * it + 4 * q4 + e, j = 16 * jt + lr;
+            const float dA = j < i ? -acc[e] : 0.f;
+            const float At = rec[R::oA + i * C + j];
+            const float rs = sum16(dA * At);
+            if (lr == 0) sDb[KT + VT + jt][i] = rs;
+            rec[R::oA + i * C + j] = beta_of(i) * dA;
+        }
+    }
+    __syncthreads();
+    if (tid < L) {
+        float db = 0.f;
+#pragma unroll
+        for (int r = 0; r < NSRC; ++r) db += sDb[r][tid];
+        a.dbeta[(t0 + tid) * a.H + h] = db;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// 5. grad2: the pair terms of A~ and M, per channel (threads [0, CPW): pairs (i, j <= i) by
+//    row i; threads [CPW, 2 CPW): by column j), then dk, dq and the reverse running sum of dG.
+// ------------------------------------------------------------------------------------------
+template <typename Tin, int C, int DK, int DV, int CPW>
+__global__ __launch_bounds__(2 * CPW) void bwd_grad2_kernel(BwdArgs a) {
+    using R = BRec<C, DK, DV>;
+    constexpr int LDX = C + 1;
+    __shared__ float sk[C * CPW], sq[C * CPW], sG[C * CPW];
+    __shared__ float sdkA[C * CPW], sdGA[C * CPW], sdkB[C * CPW];
+    __shared__ float sX[C * LDX];   // dM in the lower triangle (with the diagonal), dA~^T above
+
+    const int64_t s = blockIdx.x;
+    const int h = blockIdx.y, c0 = blockIdx.z * CPW;
+    int n, L;
+    int64_t t0;
+    if (!locate<C>(a, s, n, t0, L)) return;
+    const float *rec = a.ws + (s * a.H + h) * R::FLOATS;
+    const int t = threadIdx.x;
+    const int64_t rsk = (int64_t)a.H * DK;
+    for (int idx = t; idx < C * CPW; idx += 2 * CPW) {
+        const int i = idx / CPW, c = idx % CPW;
+        float kv = 0.f, qv = 0.f;
+        if (i < L) {
+            const int64_t o = (t0 + i) * rsk + (int64_t)h * DK + c0 + c;
+            kv = to_f32(static_cast<const Tin *>(a.k)[o]);
+            qv = to_f32(static_cast<const Tin *>(a.q)[o]);
+        }
+        sk[idx] = kv;
+        sq[idx] = qv;
+        sG[idx] = rec[R::oG + i * DK + c0 + c];
+    }
+    for (int idx = t; idx < C * C; idx += 2 * CPW) {
+        const int i = idx / C, j = idx % C;
+        if (j <= i) sX[i * LDX + j] = rec[R::oM + idx];
+        if (j < i) sX[j * LDX + i] = rec[R::oA + idx];
+    }
+    __syncthreads();
+    const float scale = a.scale;
+    if (t < CPW) {
+        const int c = t;
+        for (int i = 0; i < C; ++i) {
+            const float Gi = sG[i * CPW + c];
+            float aq = sX[i * LDX + i] * sk[i * CPW + c], ak = 0.f;  // j = i: E = 1, no A~ term
+            for (int j = 0; j < i; ++j) {
+                const float kjE = sk[j * CPW + c] * __expf(Gi - sG[j * CPW + c]);
+                aq += sX[i * LDX + j] * kjE;
+                ak += sX[j * LDX + i] * kjE;
+            }
+            sdkA[i * CPW + c] = ak;
+            sdGA[i * CPW + c] = sk[i * CPW + c] * ak + sq[i * CPW + c] * scale * aq;
+            if (i < L) {
+                const int64_t o = (t0 + i) * rsk + (int64_t)h * DK + c0 + c;
+                a.dq[o] += scale * aq;
+            }
+        }
+    } else {
+        const int c = t - CPW;
+        for (int j = 0; j < C; ++j) {
+            const float Gj = sG[j * CPW + c];
+            float acc = scale * sX[j * LDX + j] * sq[j * CPW + c];
+            for (int i = j + 1; i < C; ++i) {
+                const float E = __expf(sG[i * CPW + c] - Gj);
+                acc += (sX[j * LDX + i] * sk[i * CPW + c] + scale * sX[i * LDX + j] * sq[i * CPW + c]) * E;
+            }
+            sdkB[j * CPW + c] = acc;
+        }
+    }
+    __syncthreads();
+    if (t < CPW) {
+        const int c = t;
+        float cum = 0.f;
+        for (int i = L - 1; i >= 0; --i) {
+            const int64_t o = (t0 + i) * rsk + (int64_t)h * DK + c0 + c;
+            const float dkB = sdkB[i * CPW + c];
+            cum += a.dg[o] + sdGA[i * CPW + c] - sk[i * CPW + c] * dkB;
+            a.dg[o] = cum;
+            a.dk[o] += sdkA[i * CPW + c] + dkB;
+        }
+    }
+}
+
+template <typename Tin, int C, int DK, int DV>
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
+    using P = StatePass<C, DK, DV>;
+    constexpr int CPW = DK < 64 ? DK : 64;
+    const dim3 gs((unsigned)a.nslots, (unsigned)a.H);
+    hipLaunchKernelGGL((bwd_prep_kernel<Tin, C, DK, DV>), gs, dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 gc((unsigned)(a.n_seqs * a.H), (unsigned)(DV / 16));
+    hipLaunchKernelGGL((bwd_fwd_state_kernel<C, DK, DV>), gc, dim3(64 * P::NW), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_rev_state_kernel<C, DK, DV>), gc, dim3(64 * P::NW), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_grad1_kernel<Tin, C, DK, DV>), gs, dim3(512), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_grad2_kernel<Tin, C, DK, DV, CPW>), dim3((unsigned)a.nslots, (unsigned)a.H, DK / CPW),
+                       dim3(2 * CPW), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int C, int DK, int DV> constexpr int64_t rec_floats() { return BRec<C, DK, DV>::FLOATS; }
+
+}  // namespace
+
+bool chunk_bwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv) {
+    if (chunk == 64 && Dk == 128 && Dv == 128) return in_dtype == 0 || in_dtype == 1;
+    if (chunk == 16 && Dk == 16 && Dv == 16) return in_dtype == 0;
+    return false;
+}
+
+size_t chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                                 int32_t in_dtype, int32_t num_seqs) {
+    if (!chunk_bwd_supported(in_dtype, chunk, Dk, Dv) || B < 1 || T < 0 || H < 1 || num_seqs < 0) return 0;
+    const int64_t tokens = (int64_t)B * T;
+    const int64_t slots = num_seqs + (tokens + chunk - 1) / chunk;
+    const int64_t rec = chunk == 64 ? rec_floats<64, 128, 128>() : rec_floats<16, 16, 16>();
+    return (size_t)(slots * H * rec * (int64_t)sizeof(float));
+}
+
+hipError_t launch_chunk_bwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv, const BwdArgs &a,
+                            hipStream_t stream) {
+    if (!chunk_bwd_supported(in_dtype, chunk, Dk, Dv)) return hipErrorInvalidValue;
+    if (a.n_seqs == 0) return hipSuccess;
+    if (chunk == 64) {
+        return in_dtype == 1 ? launch_bwd_t<bf16_t, 64, 128, 128>(a, stream)
+                             : launch_bwd_t<float, 64, 128, 128>(a, stream);
+    }
+    return launch_bwd_t<float, 16, 16, 16>(a, stream);
+}
+
+}  // namespace kda

@@ -69,6 +69,25 @@ struct ConvArgs {
     int32_t silu;                // SiLU after the convolution
 };
 
+struct BwdArgs {
+    int32_t n_seqs;              // number of sequences N
+    int32_t seq_len;             // tokens per sequence when cu_seqlens == nullptr
+    const int32_t *cu_seqlens;   // device [N+1] or nullptr
+    int32_t H;
+    float scale;
+    const void *q, *k, *v;       // [tokens, H, Dk] / [tokens, H, Dv], in_dtype
+    const float *g, *beta;       // [tokens, H, Dk], [tokens, H]
+    const float *s0;             // [N, H, Dk, Dv] or nullptr (zeros)
+    const float *dout;           // [tokens, H, Dv] dL/do
+    const float *dsT;            // [N, H, Dk, Dv] dL/dS_final or nullptr (zero)
+    float *dq, *dk, *dg;         // [tokens, H, Dk]
+    float *dv;                   // [tokens, H, Dv]
+    float *dbeta;                // [tokens, H]
+    float *ds0;                  // [N, H, Dk, Dv] dL/dS_init or nullptr (not written)
+    float *ws;                   // per-(chunk, head) records, chunk_bwd_workspace_bytes(...)
+    int64_t nslots;              // N + ceil(tokens / chunk) record slots per head
+};
+
 // Workspace bytes the sequence split needs for this problem on the current device (0: no
 // split). The split is used only when the call provides at least this much workspace.
 size_t chunk_fwd_split_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
@@ -79,6 +98,10 @@ bool chunk_fwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv
 bool chunk_fwd_fused_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv);
 bool decode_supported(int32_t in_dtype, int32_t Dk, int32_t Dv);
 bool conv_supported(int32_t dtype, int32_t C, int32_t W);
+bool chunk_bwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv);
+// Workspace bytes of the backward pass (always required; 0: unsupported parameters).
+size_t chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                                 int32_t in_dtype, int32_t num_seqs);
 
 // Enqueue the kernel on `stream`; returns the launch status (hipGetLastError).
 // Enqueue kda_chunk_fwd. `workspace` (may be null) enables the sequence split when it holds
@@ -91,5 +114,8 @@ hipError_t launch_decode(int32_t in_dtype, int32_t Dk, int32_t Dv, const DecodeA
 // The short convolution: the prefill over packed/batched sequences (then the final states when
 // s_out is given), or (update) one decode token per sequence with the state shifted in place.
 hipError_t launch_conv(int32_t dtype, const ConvArgs &a, bool update, hipStream_t stream);
+// The chunked backward pass: five kernels in stream order over the workspace records.
+hipError_t launch_chunk_bwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv, const BwdArgs &a,
+                            hipStream_t stream);
 
 }  // namespace kda

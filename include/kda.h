@@ -254,6 +254,41 @@ kda_status kda_decode_step_fused(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
 typedef enum kda_activation { KDA_ACT_NONE = 0, KDA_ACT_SILU = 1 } kda_activation;
 
 /*
+ * kda_chunk_bwd - the backward pass of kda_chunk_fwd (the training side of the layer, which
+ * runs in chunk mode: [loading page] section 5, the mode switch): the gradients of a scalar
+ * loss L with respect to every input of the forward, given dL/do and dL/dS_final. It is the
+ * reverse-mode derivative of the recurrence S_t = (I - beta k k^T) Diag(e^g) S_{t-1} + beta k v^T,
+ * o_t = S_t^T (scale q) ([KV-cache page] section 5), evaluated in its chunkwise form
+ * ([KV-cache page] section 6).
+ *   B, T, H, Dk, Dv, chunk, in_dtype, scale, q, k, v, g, beta, initial_state, cu_seqlens,
+ *   num_seqs     exactly as in the kda_chunk_fwd call being differentiated (the forward's
+ *                outputs are not needed: the states are recomputed)
+ *   d_o          [B*T, H, Dv] float32, dL/do
+ *   d_final_state [N, H, Dk, Dv] float32 or NULL (zero)
+ *   dq, dk, dg   [B*T, H, Dk] float32 outputs (dL/dq, dL/dk, dL/dg)
+ *   dv           [B*T, H, Dv] float32 output
+ *   dbeta        [B*T, H] float32 output
+ *   d_initial_state [N, H, Dk, Dv] float32 output or NULL (not written); written also when
+ *                initial_state is NULL (the gradient at a zero initial state)
+ *   workspace    device buffer of at least kda_chunk_bwd_workspace_bytes(...) bytes (required);
+ *                it holds per-(chunk, head) intermediates and is overwritten
+ * All arithmetic is float32. Supported: as kda_chunk_fwd. Output buffers must not overlap the
+ * inputs or each other. Errors as kda_chunk_fwd (KDA_ERR_WORKSPACE_TOO_SMALL for a short
+ * workspace); nothing is launched and no output is written on an error.
+ */
+size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                                     int32_t chunk, int32_t in_dtype, int32_t num_seqs);
+kda_status kda_chunk_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                         int32_t in_dtype, float scale,
+                         const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *initial_state,
+                         const float *d_o, const float *d_final_state,
+                         float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                         float *d_initial_state,
+                         const int32_t *cu_seqlens, int32_t num_seqs,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * kda_short_conv_fwd - the convolution over a prefill batch.
  *   x, y           [B*T, C] dtype (KDA_F32 or KDA_BF16); sequences as in kda_chunk_fwd
  *                  (B sequences of T tokens, or packed with cu_seqlens, B = 1)

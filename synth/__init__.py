@@ -18,6 +18,8 @@ from .gen import (  # noqa: F401
     f64_to_bf16_bits,
     fused_slab,
     gate_params,
+    grad_out,
+    grad_state,
     initial_state,
     make_inputs,
     norm_weight,

@@ -46,6 +46,7 @@ _T_Q, _T_K, _T_V, _T_BETA, _T_X, _T_S0 = 0, 1, 2, 3, 4, 6
 _P_A, _P_B, _P_LEN = 10, 11, 12
 _T_QR, _T_KR, _T_XG, _T_Z, _P_W = 20, 21, 22, 23, 13
 _P_CW, _P_CB, _T_CS = 14, 15, 24
+_T_DO, _T_DST = 25, 26    # upstream gradients of the backward pass: dL/do, dL/dS_final
 NORM_EPS = 1e-6
 
 
@@ -218,6 +219,19 @@ def conv_params(w: Workload, C: int, which: int = 0) -> tuple[np.ndarray, np.nda
 def conv_state(w: Workload, N: int, C: int, which: int = 0) -> np.ndarray:
     """Initial conv states [N, 3, C] in the storage dtype (the 3 inputs before each sequence)."""
     return _store(_rng(w.wid, _T_CS, which).standard_normal((N, 3, C)), w.dtype)
+
+
+def grad_out(w: Workload, n: int, h: int, L: int | None = None) -> np.ndarray:
+    """float32 [L, V] upstream gradient dL/do of sequence ``n``, head ``h``: N(0, 1), like
+    the gradient a loss hands back through the layer."""
+    if L is None:
+        L = int(seq_lengths(w)[n]) if w.packed else w.tokens_per_seq
+    return _rng(w.wid, _T_DO, n, h).standard_normal((L, w.V)).astype(np.float32)
+
+
+def grad_state(w: Workload, N: int) -> np.ndarray:
+    """float32 [N, H, K, V] upstream gradient dL/dS_final, N(0, 1)."""
+    return _rng(w.wid, _T_DST).standard_normal((N, w.H, w.K, w.V)).astype(np.float32)
 
 
 def fused_slab(w: Workload, n: int, h: int, L: int | None = None) -> dict:

@@ -257,3 +257,42 @@ def test_recurrent_rejects_before_launch(lib, kw, status):
 def test_recurrent_zero_tokens_is_ok(lib):
     assert lib.kda_recurrent_fwd(4, 0, 2, 128, 128, BF16, F32, 1.0, None, None, None, None, None,
                                  P, None, None) == OK
+
+
+def bwd(lib, B=1, T=64, H=2, Dk=128, Dv=128, C=64, ind=BF16, scale=1.0, q=P, k=P, v=P, g=P,
+        beta=P, s0=None, do=P, dsT=None, dq=P, dk=P, dv=P, dg=P, db=P, ds0=None, cu=None, N=None,
+        ws=P, wsb=None):
+    N = B if N is None else N
+    if wsb is None:
+        wsb = lib.kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, C, ind, N)
+    return lib.kda_chunk_bwd(B, T, H, Dk, Dv, C, ind, scale, q, k, v, g, beta, s0, do, dsT,
+                             dq, dk, dv, dg, db, ds0, cu, N, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), INVALID), (dict(T=-1), INVALID), (dict(H=0), INVALID), (dict(C=0), INVALID),
+    (dict(ind=5), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(B=2, cu=P, N=1), INVALID), (dict(B=2, N=1), INVALID),
+    (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(db=None), INVALID),
+    (dict(dg=MIS), INVALID), (dict(ds0=MIS), INVALID), (dict(ws=MIS), INVALID),
+    (dict(Dk=64, Dv=64), UNSUPPORTED), (dict(C=32), UNSUPPORTED),
+    (dict(ind=BF16, Dk=16, Dv=16, C=16), UNSUPPORTED),
+    (dict(ws=None, wsb=0), WS_SMALL), (dict(wsb=1024), WS_SMALL),
+])
+def test_chunk_bwd_rejects_before_launch(lib, kw, status):
+    assert bwd(lib, **kw) == status
+    assert len(lib.kda_last_error()) > 0
+
+
+def test_chunk_bwd_workspace_bytes(lib):
+    # one float32 record per (chunk slot, head); slots = sequences + ceil(tokens / chunk)
+    one = lib.kda_chunk_bwd_workspace_bytes(1, 64, 1, 128, 128, 64, BF16, 1)
+    assert one > 0 and one % 256 == 0
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 4096, 16, 128, 128, 64, BF16, 1) == (1 + 64) * 16 * one // 2
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 4096, 16, 128, 128, 64, BF16, 7) == (7 + 64) * 16 * one // 2
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 64, 1, 96, 96, 64, BF16, 1) == 0
+
+
+def test_chunk_bwd_empty_work_is_ok_without_launch(lib):
+    assert bwd(lib, T=0, cu=P, N=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None,
+               dk=None, dv=None, dg=None, db=None, ws=None) == OK

@@ -59,6 +59,12 @@ def prefill_flops_per_token_head(K: int, V: int, C: int) -> float:
     return (3 * C * C * K + 2 * C * C * V + 6 * C * K * V + C ** 3 / 3) / C
 
 
+def bwd_bytes_per_token_head(K: int, V: int) -> int:
+    """Algorithmic HBM bytes of the backward pass per (token, head): q, k, v bf16, g, beta
+    and dL/do float32 read once; dq, dk, dg, dv, dbeta float32 written once."""
+    return (2 * K * 2 + V * 2 + K * 4 + 4 + V * 4) + (3 * K * 4 + V * 4 + 4)
+
+
 def fused_prefill_bytes_per_token_head(K: int, V: int) -> int:
     """Algorithmic HBM bytes per (token, head) of the fused prefill: bf16 raw q and k, bf16 v,
     the gate's bf16 pre-activation, float32 beta, the output gate's bf16 pre-activation and
@@ -209,6 +215,26 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
                              "B": 1, "T": w.T, "H": w.H, "dk": w.K, "dv": w.V, "chunk": w.chunk}
     del q, k, v, g, b, ws, x
     log("timed prefill_4k_h16")
+
+    # backward pass at the same shape (the training side): dL/do seeded, dL/dS_final zero
+    x = synth.make_inputs(w)
+    q, k, v = (to_dev(x[n][None], True) for n in ("q", "k", "v"))
+    g, b = to_dev(x["g"][None]), to_dev(x["beta"][None])
+    do = torch.from_numpy(np.stack([synth.grad_out(w, 0, h) for h in range(w.H)], axis=1)[None]).cuda()
+    wsb = torch.empty(kda.chunk_bwd_workspace_bytes(q, v), dtype=torch.uint8, device="cuda")
+    grads = tuple(torch.empty_like(t, dtype=torch.float32) for t in (g, g, do, g, b))
+    ms = timed(lambda: kda.kda_chunk_bwd(q, k, v, g, b, do, grads=grads, workspace=wsb,
+                                         want_dinitial_state=False), 20)
+    bb = w.T * w.H * bwd_bytes_per_token_head(w.K, w.V)
+    out["backward_4k_h16"] = {
+        "ms": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+        "algorithmic_gbs": round(bb / (ms * 1e-3) / 1e9, 1),
+        "frac_hbm": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes_per_token_head": bwd_bytes_per_token_head(w.K, w.V),
+        "workspace_bytes": wsb.numel(),
+        "what": "kda_chunk_bwd: dq, dk, dv, dg, dbeta from dL/do (float32 arithmetic)"}
+    del q, k, v, g, b, do, wsb, grads, x
+    log("timed backward_4k_h16")
 
     w = synth.WORKLOADS["varlen_64seq_h16"]
     x = synth.make_inputs(w)

@@ -27,8 +27,9 @@
 //             writes dS_init.
 //  4. grad1   (per chunk and head): the products with S, dS', U and dU, then T^T dW, T^T dU and
 //             T^T dT T^T; writes dv and dbeta, partial dq, dk, dG and the pair gradients dA~, dM.
-//  5. grad2   (per chunk, head and 64 channels): the pair terms, one thread per channel and
-//             direction, then the reverse running sum of dG.
+//  5. grad2   (per chunk and head): the pair terms on the matrix cores, 16x16 block pairs
+//             split at block boundaries (pair by pair for channels of extremely decaying
+//             blocks), then the reverse running sum of dG.
 // Chunks of a packed batch are numbered by slot n + floor(start_n / C) + j (sequence n, chunk j),
 // which is unique and below N + ceil(tokens / C), so the records need no host-side lengths.
 #include "kda_device.h"
@@ -47,9 +48,12 @@ template <int C, int DK, int DV> struct BRec {
     static constexpr int64_t odU = oU + C * DV;       // [C][DV] dU
     static constexpr int64_t oEg = odU + C * DV;      // [DK]    e^{gC}
     static constexpr int64_t oA = oEg + DK;           // [C][C]  A~ (strictly lower), then dA~
-    static constexpr int64_t oM = oA + C * C;         // [C][C]  M (lower), then dM
+    static constexpr int64_t oM = oA + C * C;         // [C][C]  M^T (upper), then dM (lower)
     static constexpr int64_t oT = oM + C * C;         // [C][C]  T
-    static constexpr int64_t oH = oT + C * C;         // [DK][DV] state entering the chunk
+    static constexpr int64_t oKdT = oT + C * C;       // [DK][C] Kd^T
+    static constexpr int64_t oWT = oKdT + DK * C;     // [DK][C] W^T
+    static constexpr int64_t oQgT = oWT + DK * C;     // [DK][C] Qg^T
+    static constexpr int64_t oH = oQgT + DK * C;      // [DK][DV] state entering the chunk
     static constexpr int64_t odH = oH + DK * DV;      // [DK][DV] dL/d(state leaving the chunk)
     static constexpr int64_t FLOATS = (odH + DK * DV + 63) & ~int64_t(63);
 };
@@ -156,6 +160,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
         *reinterpret_cast<f32x4 *>(rec + R::oQg + i * DK + c) = qg;
         *reinterpret_cast<f32x4 *>(rec + R::oKd + i * DK + c) = kd;
     }
+    for (int idx = tid; idx < DK * C / 4; idx += NT) {  // the same, transposed ([channel][row])
+        const int c = idx / (C / 4), i0 = 4 * (idx % (C / 4));
+        f32x4 qg, kd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float G = sG[(i0 + e) * LDX + c], gC = sG[(C - 1) * LDX + c];
+            qg[e] = a.scale * sQ[(i0 + e) * LDX + c] * __expf(G);
+            kd[e] = sK[(i0 + e) * LDK + c] * __expf(gC - G);
+        }
+        *reinterpret_cast<f32x4 *>(rec + R::oQgT + c * C + i0) = qg;
+        *reinterpret_cast<f32x4 *>(rec + R::oKdT + c * C + i0) = kd;
+    }
     // A~ and M pair by pair: pair p of the lower triangle is row i, column j <= i
     constexpr int NP = C * (C + 1) / 2;
     for (int p = tid; p < NP; p += NT) {
@@ -181,14 +197,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
         const float av = j < i ? sa : 0.f;
         sA[i * LDA + j] = av;
         rec[R::oA + i * C + j] = av;
-        rec[R::oM + i * C + j] = a.scale * sm;
+        rec[R::oM + j * C + i] = a.scale * sm;   // M^T
     }
     for (int p = tid; p < C * C; p += NT) {
         const int i = p / C, j = p % C;
         if (j > i) {
             sA[i * LDA + j] = 0.f;
             rec[R::oA + p] = 0.f;
-            rec[R::oM + p] = 0.f;
+            rec[R::oM + j * C + i] = 0.f;
         }
     }
     __syncthreads();
@@ -256,26 +272,38 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
         const int ld = isW ? DK : DV;
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[(16 * it + 4 * q4 + e) * ld + 16 * nt + lr] = acc[e];
+        if (isW) *reinterpret_cast<f32x4 *>(rec + R::oWT + (16 * nt + lr) * C + 16 * it + 4 * q4) = acc;
     }
 }
 
 // ------------------------------------------------------------------------------------------
 // 2. forward state pass: one workgroup per (chain, 16 value columns); wave w holds the 16x16
-//    state tiles of its key-channel tiles in accumulator registers.
+//    state tiles of its key-channel tiles in accumulator registers. Every operand is one
+//    16-byte load per lane, and the next chunk's operands are loaded while this one computes.
 // ------------------------------------------------------------------------------------------
 template <int C, int DK, int DV> struct StatePass {
     static constexpr int KT = DK / 16;
     static constexpr int NW = KT < 4 ? KT : 4;
     static constexpr int KTW = KT / NW;
     static constexpr int IT = C / 16;
+    static constexpr int NOWN = IT >= NW ? IT / NW : 1;   // row tiles whose U a wave owns
     static_assert(KT % NW == 0, "key tiles spread evenly");
+    static_assert(IT % NW == 0 || IT == 1, "row tiles spread evenly");
+};
+
+template <int C, int DK, int DV> struct FwdOps {
+    using P = StatePass<C, DK, DV>;
+    f32x4 W[P::IT][P::KTW];     // W rows 16 it + lr, channels 16 kt + 4 q4 ..
+    f32x4 KdT[P::KTW][P::IT];   // Kd^T rows 16 kt + lr, tokens 16 it + 4 q4 ..
+    f32x4 eg[P::KTW];           // e^{gC} of channels 16 kt + 4 q4 ..
+    f32x4 Ut[P::NOWN];          // U~ of the owned row tiles, accumulator layout
 };
 
 template <int C, int DK, int DV>
 __global__ __launch_bounds__(256) void bwd_fwd_state_kernel(BwdArgs a) {
     using R = BRec<C, DK, DV>;
     using P = StatePass<C, DK, DV>;
-    constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW;
+    constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW, NOWN = P::NOWN;
     __shared__ f32x4 sPart[NW][IT][64];
     const int chain = blockIdx.x, vb = blockIdx.y;
     const int n = chain / a.H, h = chain % a.H;
@@ -284,6 +312,25 @@ __global__ __launch_bounds__(256) void bwd_fwd_state_kernel(BwdArgs a) {
     const int nch = (int)((len + C - 1) / C);
     const int64_t base = slot_base<C>(a, n);
     const int col = 16 * vb + lr;
+    auto rec_of = [&](int j) { return a.ws + ((base + j) * a.H + h) * R::FLOATS; };
+    auto own = [&](int o) { return wave + NW * o; };
+    auto load = [&](const float *rec, FwdOps<C, DK, DV> &o) {
+#pragma unroll
+        for (int kk = 0; kk < KTW; ++kk) {
+            const int kt = wave * KTW + kk;
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                o.W[it][kk] = *reinterpret_cast<const f32x4 *>(rec + R::oW + (16 * it + lr) * DK + 16 * kt + 4 * q4);
+                o.KdT[kk][it] = *reinterpret_cast<const f32x4 *>(rec + R::oKdT + (16 * kt + lr) * C + 16 * it + 4 * q4);
+            }
+            o.eg[kk] = *reinterpret_cast<const f32x4 *>(rec + R::oEg + 16 * kt + 4 * q4);
+        }
+#pragma unroll
+        for (int ow = 0; ow < NOWN; ++ow)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o.Ut[ow][e] = own(ow) < IT ? rec[R::oU + (16 * own(ow) + 4 * q4 + e) * DV + col] : 0.f;
+    };
 
     f32x4 S[KTW];
 #pragma unroll
@@ -293,33 +340,27 @@ __global__ __launch_bounds__(256) void bwd_fwd_state_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e)
             S[kk][e] = a.s0 ? a.s0[(((int64_t)n * a.H + h) * DK + 16 * kt + 4 * q4 + e) * DV + col] : 0.f;
     }
-    for (int j = 0; j < nch; ++j) {
-        float *rec = a.ws + ((base + j) * a.H + h) * R::FLOATS;
+    // one chunk with operands `cur`, loading the next chunk's into `nxt`; the loop below
+    // alternates two operand sets, so the loads stay in flight across the chunk
+    auto step = [&](int j, FwdOps<C, DK, DV> &cur, FwdOps<C, DK, DV> &nxt) {
+        float *rec = rec_of(j);
+        if (j + 1 < nch) load(rec_of(j + 1), nxt);
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk) {
             const int kt = wave * KTW + kk;
 #pragma unroll
             for (int e = 0; e < 4; ++e) rec[R::oH + (16 * kt + 4 * q4 + e) * DV + col] = S[kk][e];
         }
-        f32x4 part[IT];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KTW; ++kk) {
-                const int kt = wave * KTW + kk;
-                mma(acc, *reinterpret_cast<const f32x4 *>(rec + R::oW + (16 * it + lr) * DK + 16 * kt + 4 * q4),
-                    S[kk]);
-            }
-            if (it % NW == wave) {  // the owner of row tile it adds U~ (and later stores U there)
-                f32x4 ut;
+            for (int kk = 0; kk < KTW; ++kk) mma(acc, cur.W[it][kk], S[kk]);
+            f32x4 part = -acc;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ut[e] = rec[R::oU + (16 * it + 4 * q4 + e) * DV + col];
-                part[it] = ut - acc;
-            } else {
-                part[it] = -acc;
-            }
-            sPart[wave][it][lane] = part[it];
+            for (int ow = 0; ow < NOWN; ++ow)
+                if (own(ow) == it) part += cur.Ut[ow];   // the owner of row tile it adds U~
+            sPart[wave][it][lane] = part;
         }
         __syncthreads();
         f32x4 U[IT];
@@ -331,37 +372,47 @@ __global__ __launch_bounds__(256) void bwd_fwd_state_kernel(BwdArgs a) {
         }
         __syncthreads();
 #pragma unroll
-        for (int it = 0; it < IT; ++it)
-            if (it % NW == wave) {
+        for (int ow = 0; ow < NOWN; ++ow)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) rec[R::oU + (16 * it + 4 * q4 + e) * DV + col] = U[it][e];
-            }
+            for (int it = 0; it < IT; ++it)
+                if (own(ow) == it) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rec[R::oU + (16 * it + 4 * q4 + e) * DV + col] = U[it][e];
+                }
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk) {
-            const int kt = wave * KTW + kk;
-            f32x4 eg;
+            S[kk] *= cur.eg[kk];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) eg[e] = rec[R::oEg + 16 * kt + 4 * q4 + e];
-            S[kk] *= eg;
-#pragma unroll
-            for (int it = 0; it < IT; ++it) {
-                f32x4 A;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) A[e] = rec[R::oKd + (16 * it + 4 * q4 + e) * DK + 16 * kt + lr];
-                mma(S[kk], A, U[it]);
-            }
+            for (int it = 0; it < IT; ++it) mma(S[kk], cur.KdT[kk][it], U[it]);
         }
+    };
+    FwdOps<C, DK, DV> o0, o1;
+    if (nch > 0) load(rec_of(0), o0);
+    int j = 0;
+    for (; j + 1 < nch; j += 2) {
+        step(j, o0, o1);
+        step(j + 1, o1, o0);
     }
+    if (j < nch) step(j, o0, o1);
 }
 
 // ------------------------------------------------------------------------------------------
-// 3. reverse state pass: dS held like S above, chunks in reverse order.
+// 3. reverse state pass: dS held like S above, chunks in reverse order; the next chunk's Kd,
+//    M^T, e^{gC} and dO are loaded while this one computes.
 // ------------------------------------------------------------------------------------------
+template <int C, int DK, int DV> struct RevOps {
+    using P = StatePass<C, DK, DV>;
+    f32x4 Kd[P::IT][P::KTW];    // Kd rows 16 it + lr, channels 16 kt + 4 q4 ..
+    f32x4 MT[P::NOWN][P::IT];   // M^T rows of the owned tiles, tokens 16 ms + 4 q4 ..
+    f32x4 eg[P::KTW];
+    f32x4 dO[P::IT];            // dO rows 16 ms + 4 q4 + e, column col (zero past the end)
+};
+
 template <int C, int DK, int DV>
 __global__ __launch_bounds__(256) void bwd_rev_state_kernel(BwdArgs a) {
     using R = BRec<C, DK, DV>;
     using P = StatePass<C, DK, DV>;
-    constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW;
+    constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW, NOWN = P::NOWN;
     __shared__ f32x4 sPart[NW][IT][64];
     const int chain = blockIdx.x, vb = blockIdx.y;
     const int n = chain / a.H, h = chain % a.H;
@@ -371,6 +422,35 @@ __global__ __launch_bounds__(256) void bwd_rev_state_kernel(BwdArgs a) {
     const int64_t base = slot_base<C>(a, n);
     const int col = 16 * vb + lr;
     const int64_t sbase = ((int64_t)n * a.H + h) * DK;
+    const int64_t rsv = (int64_t)a.H * DV;
+    auto rec_of = [&](int j) { return a.ws + ((base + j) * a.H + h) * R::FLOATS; };
+    auto own = [&](int o) { return wave + NW * o; };
+    auto load = [&](int j, RevOps<C, DK, DV> &o) {
+        const float *rec = rec_of(j);
+#pragma unroll
+        for (int kk = 0; kk < KTW; ++kk) {
+            const int kt = wave * KTW + kk;
+#pragma unroll
+            for (int it = 0; it < IT; ++it)
+                o.Kd[it][kk] = *reinterpret_cast<const f32x4 *>(rec + R::oKd + (16 * it + lr) * DK + 16 * kt + 4 * q4);
+            o.eg[kk] = *reinterpret_cast<const f32x4 *>(rec + R::oEg + 16 * kt + 4 * q4);
+        }
+#pragma unroll
+        for (int ow = 0; ow < NOWN; ++ow)
+#pragma unroll
+            for (int ms = 0; ms < IT; ++ms)
+                o.MT[ow][ms] = own(ow) < IT && ms >= own(ow)   // M[m][i] = 0 for m < i
+                    ? *reinterpret_cast<const f32x4 *>(rec + R::oM + (16 * own(ow) + lr) * C + 16 * ms + 4 * q4)
+                    : zero4();
+        const int64_t t0 = st + (int64_t)j * C;
+        const int L = (int)(len - (int64_t)j * C < C ? len - (int64_t)j * C : C);
+        const float *dorow = a.dout + (t0 + 4 * q4) * rsv + (int64_t)h * DV + col;
+#pragma unroll
+        for (int ms = 0; ms < IT; ++ms)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o.dO[ms][e] = 16 * ms + 4 * q4 + e < L ? dorow[(int64_t)(16 * ms + e) * rsv] : 0.f;
+    };
 
     f32x4 dS[KTW];
 #pragma unroll
@@ -380,42 +460,37 @@ __global__ __launch_bounds__(256) void bwd_rev_state_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e)
             dS[kk][e] = a.dsT ? a.dsT[(sbase + 16 * kt + 4 * q4 + e) * DV + col] : 0.f;
     }
-    for (int j = nch - 1; j >= 0; --j) {
-        float *rec = a.ws + ((base + j) * a.H + h) * R::FLOATS;
-        const int64_t t0 = st + (int64_t)j * C;
-        const int L = (int)(len - (int64_t)j * C < C ? len - (int64_t)j * C : C);
+    auto step = [&](int j, RevOps<C, DK, DV> &cur, RevOps<C, DK, DV> &nxt) {
+        float *rec = rec_of(j);
+        if (j > 0) load(j - 1, nxt);
+        f32x4 QgT[KTW][IT], WT[KTW][IT];   // needed after the exchange below
+#pragma unroll
+        for (int kk = 0; kk < KTW; ++kk) {
+            const int kt = wave * KTW + kk;
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                QgT[kk][it] = *reinterpret_cast<const f32x4 *>(rec + R::oQgT + (16 * kt + lr) * C + 16 * it + 4 * q4);
+                WT[kk][it] = -*reinterpret_cast<const f32x4 *>(rec + R::oWT + (16 * kt + lr) * C + 16 * it + 4 * q4);
+            }
+        }
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk) {
             const int kt = wave * KTW + kk;
 #pragma unroll
             for (int e = 0; e < 4; ++e) rec[R::odH + (16 * kt + 4 * q4 + e) * DV + col] = dS[kk][e];
         }
-        f32x4 dOf[IT];  // dO rows 16 ms + 4 q4 + e, column col (zero past the sequence end)
-#pragma unroll
-        for (int ms = 0; ms < IT; ++ms)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * ms + 4 * q4 + e;
-                dOf[ms][e] = r < L ? a.dout[((t0 + r) * a.H + h) * DV + col] : 0.f;
-            }
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KTW; ++kk) {
-                const int kt = wave * KTW + kk;
-                mma(acc, *reinterpret_cast<const f32x4 *>(rec + R::oKd + (16 * it + lr) * DK + 16 * kt + 4 * q4),
-                    dS[kk]);
-            }
-            if (it % NW == wave) {  // M^T dO for the owned row tile (M[m][i] = 0 for m < i)
+            for (int kk = 0; kk < KTW; ++kk) mma(acc, cur.Kd[it][kk], dS[kk]);
 #pragma unroll
-                for (int ms = it; ms < IT; ++ms) {
-                    f32x4 A;
+            for (int ow = 0; ow < NOWN; ++ow)
+                if (own(ow) == it) {   // M^T dO for the owned row tile
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) A[e] = rec[R::oM + (16 * ms + 4 * q4 + e) * C + 16 * it + lr];
-                    mma(acc, A, dOf[ms]);
+                    for (int ms = 0; ms < IT; ++ms)
+                        if (ms >= it) mma(acc, cur.MT[ow][ms], cur.dO[ms]);
                 }
-            }
             sPart[wave][it][lane] = acc;
         }
         __syncthreads();
@@ -428,31 +503,31 @@ __global__ __launch_bounds__(256) void bwd_rev_state_kernel(BwdArgs a) {
         }
         __syncthreads();
 #pragma unroll
-        for (int it = 0; it < IT; ++it)
-            if (it % NW == wave) {
+        for (int ow = 0; ow < NOWN; ++ow)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) rec[R::odU + (16 * it + 4 * q4 + e) * DV + col] = dU[it][e];
-            }
+            for (int it = 0; it < IT; ++it)
+                if (own(ow) == it) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rec[R::odU + (16 * it + 4 * q4 + e) * DV + col] = dU[it][e];
+                }
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk) {
-            const int kt = wave * KTW + kk;
-            f32x4 eg;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) eg[e] = rec[R::oEg + 16 * kt + 4 * q4 + e];
-            dS[kk] *= eg;
+            dS[kk] *= cur.eg[kk];
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
-                f32x4 Aq, Aw;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    Aq[e] = rec[R::oQg + (16 * it + 4 * q4 + e) * DK + 16 * kt + lr];
-                    Aw[e] = -rec[R::oW + (16 * it + 4 * q4 + e) * DK + 16 * kt + lr];
-                }
-                mma(dS[kk], Aq, dOf[it]);
-                mma(dS[kk], Aw, dU[it]);
+                mma(dS[kk], QgT[kk][it], cur.dO[it]);
+                mma(dS[kk], WT[kk][it], dU[it]);
             }
         }
+    };
+    RevOps<C, DK, DV> o0, o1;
+    if (nch > 0) load(nch - 1, o0);
+    int j = nch - 1;
+    for (; j >= 1; j -= 2) {
+        step(j, o0, o1);
+        step(j - 1, o1, o0);
     }
+    if (j == 0) step(0, o0, o1);
     if (a.ds0) {
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk) {
@@ -725,83 +800,188 @@ __global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// 5. grad2: the pair terms of A~ and M, per channel (threads [0, CPW): pairs (i, j <= i) by
-//    row i; threads [CPW, 2 CPW): by column j), then dk, dq and the reverse running sum of dG.
+// 5. grad2: the pair terms of A~ and M, on the matrix cores. Wave w takes key channels
+//    16 w .. 16 w + 15 for all rows; lane (lr, q4) holds rows 16 X + 4 q4 + e of channel
+//    16 w + lr, which is both the accumulator layout and the B-fragment layout. For the block
+//    pair (I, J), J <= I, e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j} with r the last row of
+//    block J (J < I: both factors <= 1) or the first row of block I (diagonal: the second
+//    factor is at most the block's inverse decay). A channel whose diagonal block decays below
+//    e^-60 takes that block pair by pair instead (exact for any decay).
+//      dKa = dA~ Kb,  dQa = scale dM Kb,  dKb = dA~^T Ka + scale dM^T Qa
+//      dk += dKa e^{G_i - G_r} + dKb e^{G_r - G_j},  dq += dQa e^{G_i - G_r}
+//      dG_i += Ka dKa + Qa dQa,  dG_j -= Kb dKb
+//    then dq, dk are completed and dg is the reverse running sum of dG inside the chunk.
 // ------------------------------------------------------------------------------------------
-template <typename Tin, int C, int DK, int DV, int CPW>
-__global__ __launch_bounds__(2 * CPW) void bwd_grad2_kernel(BwdArgs a) {
+constexpr float kExtremeLogDecay = 60.f;
+
+template <typename Tin, int C, int DK, int DV>
+__global__ __launch_bounds__(DK * 4) void bwd_grad2_kernel(BwdArgs a) {
     using R = BRec<C, DK, DV>;
-    constexpr int LDX = C + 1;
-    __shared__ float sk[C * CPW], sq[C * CPW], sG[C * CPW];
-    __shared__ float sdkA[C * CPW], sdGA[C * CPW], sdkB[C * CPW];
-    __shared__ float sX[C * LDX];   // dM in the lower triangle (with the diagonal), dA~^T above
+    constexpr int IT = C / 16, LDA = C + 4, LDG = DK + 1;
+    __shared__ __align__(16) float sAM[2 * C * LDA];
+    float *sdA = sAM;                              // dA~ (strictly lower)
+    float *sdM = sAM + C * LDA;                    // dM (lower, with the diagonal)
+    __shared__ float sGs[IT][DK], sGe[IT][DK];     // G at the first / last row of each block
+    __shared__ float sBlk[DK / 16][3 * 16 * 16];   // per wave: one block's k, q, G (extreme decay)
+    float *sDG = sdA;                              // dG for the running sum, after the pairs
+    static_assert(C * LDG <= 2 * C * LDA, "dG fits over dA~ and dM");
 
     const int64_t s = blockIdx.x;
-    const int h = blockIdx.y, c0 = blockIdx.z * CPW;
+    const int h = blockIdx.y;
     int n, L;
     int64_t t0;
     if (!locate<C>(a, s, n, t0, L)) return;
     const float *rec = a.ws + (s * a.H + h) * R::FLOATS;
-    const int t = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, q4 = lane >> 4;
+    const int c = 16 * wave + lr;
     const int64_t rsk = (int64_t)a.H * DK;
-    for (int idx = t; idx < C * CPW; idx += 2 * CPW) {
-        const int i = idx / CPW, c = idx % CPW;
-        float kv = 0.f, qv = 0.f;
-        if (i < L) {
-            const int64_t o = (t0 + i) * rsk + (int64_t)h * DK + c0 + c;
-            kv = to_f32(static_cast<const Tin *>(a.k)[o]);
-            qv = to_f32(static_cast<const Tin *>(a.q)[o]);
-        }
-        sk[idx] = kv;
-        sq[idx] = qv;
-        sG[idx] = rec[R::oG + i * DK + c0 + c];
-    }
-    for (int idx = t; idx < C * C; idx += 2 * CPW) {
-        const int i = idx / C, j = idx % C;
-        if (j <= i) sX[i * LDX + j] = rec[R::oM + idx];
-        if (j < i) sX[j * LDX + i] = rec[R::oA + idx];
-    }
-    __syncthreads();
     const float scale = a.scale;
-    if (t < CPW) {
-        const int c = t;
-        for (int i = 0; i < C; ++i) {
-            const float Gi = sG[i * CPW + c];
-            float aq = sX[i * LDX + i] * sk[i * CPW + c], ak = 0.f;  // j = i: E = 1, no A~ term
-            for (int j = 0; j < i; ++j) {
-                const float kjE = sk[j * CPW + c] * __expf(Gi - sG[j * CPW + c]);
-                aq += sX[i * LDX + j] * kjE;
-                ak += sX[j * LDX + i] * kjE;
-            }
-            sdkA[i * CPW + c] = ak;
-            sdGA[i * CPW + c] = sk[i * CPW + c] * ak + sq[i * CPW + c] * scale * aq;
-            if (i < L) {
-                const int64_t o = (t0 + i) * rsk + (int64_t)h * DK + c0 + c;
-                a.dq[o] += scale * aq;
-            }
+
+    for (int idx = tid; idx < C * C / 4; idx += DK * 4) {
+        const int i = idx / (C / 4), m = 4 * (idx % (C / 4));
+        *reinterpret_cast<f32x4 *>(sdA + i * LDA + m) = *reinterpret_cast<const f32x4 *>(rec + R::oA + i * C + m);
+        *reinterpret_cast<f32x4 *>(sdM + i * LDA + m) = *reinterpret_cast<const f32x4 *>(rec + R::oM + i * C + m);
+    }
+    for (int idx = tid; idx < IT * DK; idx += DK * 4) {
+        const int b = idx / DK, cc = idx % DK;
+        sGs[b][cc] = rec[R::oG + (16 * b) * DK + cc];
+        sGe[b][cc] = rec[R::oG + (16 * b + 15) * DK + cc];
+    }
+    // this lane's rows of k, q, G (zero past the sequence end; G is constant there). Row
+    // 16 X + 4 q4 + e of the token arrays is at lane_off + (16 X + e) * rsk: one per-lane
+    // offset plus a uniform one, so no per-row address stays live.
+    const int64_t lane_off = (t0 + 4 * q4) * rsk + (int64_t)h * DK + c;
+    const Tin *kin = static_cast<const Tin *>(a.k) + lane_off;
+    const Tin *qin = static_cast<const Tin *>(a.q) + lane_off;
+    float kr[IT][4], qr[IT][4], Gr[IT][4];
+#pragma unroll
+    for (int X = 0; X < IT; ++X)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * X + 4 * q4 + e;
+            const int64_t ro = (int64_t)(16 * X + e) * rsk;
+            kr[X][e] = i < L ? to_f32(kin[ro]) : 0.f;
+            qr[X][e] = i < L ? to_f32(qin[ro]) : 0.f;
+            Gr[X][e] = rec[R::oG + i * DK + c];
         }
-    } else {
-        const int c = t - CPW;
-        for (int j = 0; j < C; ++j) {
-            const float Gj = sG[j * CPW + c];
-            float acc = scale * sX[j * LDX + j] * sq[j * CPW + c];
-            for (int i = j + 1; i < C; ++i) {
-                const float E = __expf(sG[i * CPW + c] - Gj);
-                acc += (sX[j * LDX + i] * sk[i * CPW + c] + scale * sX[i * LDX + j] * sq[i * CPW + c]) * E;
+    __syncthreads();
+
+    float dq[IT][4], dk[IT][4], dG[IT][4];
+#pragma unroll
+    for (int X = 0; X < IT; ++X)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dq[X][e] = dk[X][e] = dG[X][e] = 0.f;
+
+#pragma unroll
+    for (int I = 0; I < IT; ++I) {
+#pragma unroll
+        for (int J = 0; J <= I; ++J) {
+            const bool diag = J == I;
+            const float Gref = diag ? sGs[I][c] : sGe[J][c];
+            // a channel whose diagonal block decays below e^-60 is done pair by pair below;
+            // zero factors drop its block-pair terms (and keep its MFMA columns finite)
+            const bool ext = diag && (sGs[I][c] - sGe[I][c] > kExtremeLogDecay);
+            f32x4 Ka, Qa, Kb, EI, EJ;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                EI[e] = ext ? 0.f : __expf(Gr[I][e] - Gref);          // <= 1
+                EJ[e] = ext ? 0.f : __expf(Gref - Gr[J][e]);          // <= 1 off the diagonal
+                Ka[e] = kr[I][e] * EI[e];
+                Qa[e] = qr[I][e] * EI[e];
+                Kb[e] = kr[J][e] * EJ[e];
             }
-            sdkB[j * CPW + c] = acc;
+            f32x4 aKa = zero4(), aQa = zero4(), aKb = zero4();
+            {
+                const f32x4 Ar = *reinterpret_cast<const f32x4 *>(sdA + (16 * I + lr) * LDA + 16 * J + 4 * q4);
+                const f32x4 Mr = *reinterpret_cast<const f32x4 *>(sdM + (16 * I + lr) * LDA + 16 * J + 4 * q4);
+                mma(aKa, Ar, Kb);
+                mma(aQa, Mr * scale, Kb);
+                f32x4 Ac, Mc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Ac[e] = sdA[(16 * I + 4 * q4 + e) * LDA + 16 * J + lr];
+                    Mc[e] = sdM[(16 * I + 4 * q4 + e) * LDA + 16 * J + lr] * scale;
+                }
+                mma(aKb, Ac, Ka);
+                mma(aKb, Mc, Qa);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dk[I][e] += aKa[e] * EI[e];
+                dq[I][e] += aQa[e] * EI[e];
+                dk[J][e] += aKb[e] * EJ[e];
+                dG[I][e] += Ka[e] * aKa[e] + Qa[e] * aQa[e];
+                dG[J][e] -= Kb[e] * aKb[e];
+            }
+            if (diag && __any(ext)) {
+                // pair by pair for the channels of an extreme block: the block's rows of this
+                // wave's channels go through LDS ([k, q, G][row][channel])
+                float *blk = sBlk[wave];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * q4 + e;
+                    blk[(0 * 16 + r) * 16 + lr] = kr[I][e];
+                    blk[(1 * 16 + r) * 16 + lr] = qr[I][e];
+                    blk[(2 * 16 + r) * 16 + lr] = Gr[I][e];
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                if (ext) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int ri = 4 * q4 + e, i = 16 * I + ri;
+                        const float ki = kr[I][e], qi = qr[I][e], Gi = Gr[I][e];
+                        float pq = 0.f, pk = 0.f, pg = 0.f;
+#pragma unroll 1
+                        for (int r = 0; r < 16; ++r) {
+                            const int j = 16 * I + r;
+                            const float kj = blk[r * 16 + lr], qj = blk[(16 + r) * 16 + lr];
+                            const float Gj = blk[(32 + r) * 16 + lr];
+                            if (r <= ri) {   // as the row: pairs (i, j <= i)
+                                const float E = __expf(Gi - Gj);
+                                const float dAij = sdA[i * LDA + j], dMij = scale * sdM[i * LDA + j];
+                                pq += dMij * kj * E;
+                                pk += dAij * kj * E;
+                                pg += (dAij * ki + dMij * qi) * kj * E;
+                            }
+                            if (r >= ri) {   // as the column: pairs (j >= i, i)
+                                const float E = __expf(Gj - Gi);
+                                const float z = (sdA[j * LDA + i] * kj + scale * sdM[j * LDA + i] * qj) * E;
+                                pk += z;
+                                pg -= z * ki;
+                            }
+                        }
+                        dq[I][e] += pq;
+                        dk[I][e] += pk;
+                        dG[I][e] += pg;
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one block pair at a time (register pressure)
         }
     }
+    __syncthreads();  // dA~, dM no longer read: their space takes dG
+    // complete dq and dk; dG with grad1's part into LDS for the running sum
+#pragma unroll
+    for (int X = 0; X < IT; ++X)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * X + 4 * q4 + e;
+            float g1 = 0.f;
+            if (i < L) {
+                const int64_t o = lane_off + (int64_t)(16 * X + e) * rsk;
+                a.dq[o] += dq[X][e];
+                a.dk[o] += dk[X][e];
+                g1 = a.dg[o];
+            }
+            sDG[i * LDG + c] = g1 + dG[X][e];
+        }
     __syncthreads();
-    if (t < CPW) {
-        const int c = t;
+    if (tid < DK) {
         float cum = 0.f;
         for (int i = L - 1; i >= 0; --i) {
-            const int64_t o = (t0 + i) * rsk + (int64_t)h * DK + c0 + c;
-            const float dkB = sdkB[i * CPW + c];
-            cum += a.dg[o] + sdGA[i * CPW + c] - sk[i * CPW + c] * dkB;
-            a.dg[o] = cum;
-            a.dk[o] += sdkA[i * CPW + c] + dkB;
+            cum += sDG[i * LDG + tid];
+            a.dg[(t0 + i) * rsk + (int64_t)h * DK + tid] = cum;
         }
     }
 }
@@ -809,7 +989,6 @@ __global__ __launch_bounds__(2 * CPW) void bwd_grad2_kernel(BwdArgs a) {
 template <typename Tin, int C, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     using P = StatePass<C, DK, DV>;
-    constexpr int CPW = DK < 64 ? DK : 64;
     const dim3 gs((unsigned)a.nslots, (unsigned)a.H);
     hipLaunchKernelGGL((bwd_prep_kernel<Tin, C, DK, DV>), gs, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
@@ -821,8 +1000,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grad1_kernel<Tin, C, DK, DV>), gs, dim3(512), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_grad2_kernel<Tin, C, DK, DV, CPW>), dim3((unsigned)a.nslots, (unsigned)a.H, DK / CPW),
-                       dim3(2 * CPW), 0, stream, a);
+    hipLaunchKernelGGL((bwd_grad2_kernel<Tin, C, DK, DV>), gs, dim3(DK * 4), 0, stream, a);
     return hipGetLastError();
 }
 

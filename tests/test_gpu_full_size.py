@@ -181,3 +181,25 @@ def test_varlen_64seq_h16_full_size():
     o_ref, S_ref = _oracle(x, rows, sub_cu, s0=x["initial_state"][seqs])
     assert_close(o_s, o_ref, TOL, f"o (sequences {seqs}, lengths {lens[seqs].tolist()})")
     assert_close(S_s, S_ref, TOL, "final states (sampled sequences)")
+
+
+def test_backward_4k_h16_full_size():
+    """kda_chunk_bwd at the 4K-token, 16-head training shape (bf16 q/k/v, the launch the
+    benchmark times), dL/do and dL/dS_final seeded; every head checked against the oracle's
+    backward over the whole sequence (the bf16 backward bound of the backward tests, 1e-3)."""
+    torch = torch_mod()
+    w = synth.WORKLOADS["prefill_4k_h16"]
+    x = synth.make_inputs(w)
+    do = np.stack([synth.grad_out(w, 0, h) for h in range(w.H)], axis=1)     # [T, H, V]
+    dsT = synth.grad_state(w, 1)
+    q, k, v = (to_dev(x[n][None], "bf16") for n in ("q", "k", "v"))
+    g, beta = to_dev(x["g"][None]), to_dev(x["beta"][None])
+    note("backward 4k_h16 full size")
+    got = kda.kda_chunk_bwd(q, k, v, g, beta, to_dev(do[None]), dfinal_state=to_dev(dsT))
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy() for t in got]
+    ref = oracle.kda_bwd(f64(x["q"], "bf16"), f64(x["k"], "bf16"), f64(x["v"], "bf16"),
+                         f64(x["g"]), f64(x["beta"]), f64(do), dfinal_state=f64(dsT),
+                         threads=oracle_threads())
+    for name, a, b in zip(["dq", "dk", "dv", "dg", "dbeta", "dS_init"], got, ref):
+        assert_close(a.reshape(b.shape), b, 1e-3, name)

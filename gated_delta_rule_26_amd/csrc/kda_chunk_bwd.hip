@@ -18,13 +18,13 @@
 //
 // Mapping to the MI355X. Everything is float32 (fp32 matrix cores, v_mfma_f32_16x16x4f32).
 // Five kernels, each a plain pass over a per-(chunk, head) record in the workspace:
-//  1. prep    (one workgroup per chunk and head): G, Qg, Kd, e^{gC}, A~ and M pair by pair (one
-//             exp per pair and channel: exact for any decay), T by column substitution in one
-//             wave, W and U~ on the matrix cores.
+//  1. prep    (one workgroup per chunk and head): G, Qg, Kd, e^{gC}, A~ and M as 16x16 block
+//             pairs on the matrix cores (decay split at block boundaries; pair by pair for a
+//             block decaying below e^-60), T by column substitution in one wave, W and U~.
 //  2. forward state pass (per chain and 16 value columns, chunks in order): stores the state
 //             entering each chunk and U; the waves split the key channels and sum U through LDS.
 //  3. reverse state pass (per chain and 16 value columns, chunks in reverse): stores dS' and dU,
-//             writes dS_init.
+//             writes dS_init. It needs only prep's records, so 2 and 3 share one launch.
 //  4. grad1   (per chunk and head): the products with S, dS', U and dU, then T^T dW, T^T dU and
 //             T^T dT T^T; writes dv and dbeta, partial dq, dk, dG and the pair gradients dA~, dM.
 //  5. grad2   (per chunk and head): the pair terms on the matrix cores, 16x16 block pairs
@@ -92,6 +92,10 @@ __device__ __forceinline__ float sum16(float x) {  // over the 16 lanes of a row
 }
 
 __device__ __forceinline__ void mma(f32x4 &acc, f32x4 a, f32x4 b) { Mma<float>::mma(acc, a, b); }
+
+// A 16-token block whose decay falls below e^-60 in some channel has diagonal-block factors
+// beyond float32's comfortable range; such blocks are summed pair by pair.
+constexpr float kExtremeLogDecay = 60.f;
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // ------------------------------------------------------------------------------------------
@@ -109,6 +113,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     __shared__ __align__(16) float sA[C * LDA];   // A~
     __shared__ __align__(16) float sT[C * LDA];   // T
     __shared__ float sB[C];
+    __shared__ int sExt[C / 16];                   // 16-token blocks decaying below e^-60
 
     const int64_t s = blockIdx.x;
     const int h = blockIdx.y;
@@ -133,6 +138,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
         *reinterpret_cast<f32x4 *>(sG + i * LDX + c) = gv;
     }
     if (tid < C) sB[tid] = tid < L ? a.beta[(t0 + tid) * a.H + h] : 0.f;
+    if (tid < C / 16) sExt[tid] = 0;
     __syncthreads();
     if (tid < DK) {  // running sum along the chunk, one thread per channel
         float acc = 0.f;
@@ -142,6 +148,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
             sG[i * LDX + tid] = acc;
         }
         rec[R::oEg + tid] = __expf(acc);
+#pragma unroll
+        for (int b = 0; b < C / 16; ++b)
+            if (sG[16 * b * LDX + tid] - sG[(16 * b + 15) * LDX + tid] > kExtremeLogDecay) sExt[b] = 1;
     }
     __syncthreads();
     for (int idx = tid; idx < C * DK / 4; idx += NT) {
@@ -172,36 +181,88 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
         *reinterpret_cast<f32x4 *>(rec + R::oQgT + c * C + i0) = qg;
         *reinterpret_cast<f32x4 *>(rec + R::oKdT + c * C + i0) = kd;
     }
-    // A~ and M pair by pair: pair p of the lower triangle is row i, column j <= i
-    constexpr int NP = C * (C + 1) / 2;
-    for (int p = tid; p < NP; p += NT) {
-        int i = (int)((__builtin_sqrtf(8.f * (float)p + 1.f) - 1.f) * 0.5f);
-        while ((i + 1) * (i + 2) / 2 <= p) ++i;
-        while (i * (i + 1) / 2 > p) --i;
-        const int j = p - i * (i + 1) / 2;
-        float sa = 0.f, sm = 0.f;
-#pragma unroll 4
-        for (int c = 0; c < DK; c += 4) {
-            const f32x4 ki = *reinterpret_cast<const f32x4 *>(sK + i * LDK + c);
-            const f32x4 kj = *reinterpret_cast<const f32x4 *>(sK + j * LDK + c);
-            const f32x4 qi = *reinterpret_cast<const f32x4 *>(sQ + i * LDX + c);
-            const f32x4 Gi = *reinterpret_cast<const f32x4 *>(sG + i * LDX + c);
-            const f32x4 Gj = *reinterpret_cast<const f32x4 *>(sG + j * LDX + c);
+    // A~ and M as 16x16 block pairs (I, J <= I) on the matrix cores, one pair per wave at a time:
+    // e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j} with r the last row of block J (both factors
+    // <= 1) or, on the diagonal, the block's first row (the second factor at most the block's
+    // inverse decay). A diagonal block decaying below e^-60 in some channel is summed pair by
+    // pair instead (one exp per pair and channel, exact for any decay).
+    {
+        const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, q4 = lane >> 4;
+        constexpr int IT = C / 16, NPB = IT * (IT + 1) / 2;
+        for (int pb = wave; pb < NPB; pb += NT / 64) {
+            int I = 0;
+            while ((I + 1) * (I + 2) / 2 <= pb) ++I;
+            const int J = pb - I * (I + 1) / 2;
+            const bool diag = I == J;
+            if (diag && sExt[I]) {
+                for (int pp = lane; pp < 136; pp += 64) {   // pairs (i, j <= i) of the block
+                    int ri = 0;
+                    while ((ri + 1) * (ri + 2) / 2 <= pp) ++ri;
+                    const int i = 16 * I + ri, j = 16 * I + pp - ri * (ri + 1) / 2;
+                    float sa = 0.f, sm = 0.f;
+                    for (int c = 0; c < DK; c += 4) {
+                        const f32x4 ki = *reinterpret_cast<const f32x4 *>(sK + i * LDK + c);
+                        const f32x4 kj = *reinterpret_cast<const f32x4 *>(sK + j * LDK + c);
+                        const f32x4 qi = *reinterpret_cast<const f32x4 *>(sQ + i * LDX + c);
+                        const f32x4 Gi = *reinterpret_cast<const f32x4 *>(sG + i * LDX + c);
+                        const f32x4 Gj = *reinterpret_cast<const f32x4 *>(sG + j * LDX + c);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float kjE = kj[e] * __expf(Gi[e] - Gj[e]);
+                            sa += ki[e] * kjE;
+                            sm += qi[e] * kjE;
+                        }
+                    }
+                    const float av = j < i ? sa : 0.f;
+                    sA[i * LDA + j] = av;
+                    rec[R::oA + i * C + j] = av;
+                    rec[R::oM + j * C + i] = a.scale * sm;   // M^T
+                }
+                for (int pp = lane; pp < 256; pp += 64) {   // the block above its diagonal
+                    const int i = 16 * I + (pp >> 4), j = 16 * I + (pp & 15);
+                    if (j > i) {
+                        sA[i * LDA + j] = 0.f;
+                        rec[R::oA + i * C + j] = 0.f;
+                        rec[R::oM + j * C + i] = 0.f;
+                    }
+                }
+                continue;
+            }
+            const int r = diag ? 16 * I : 16 * J + 15;
+            f32x4 accA = zero4(), accM = zero4();
+#pragma unroll 2
+            for (int cs = 0; cs < DK / 16; ++cs) {
+                const int c0 = 16 * cs + 4 * q4;
+                const f32x4 Gr = *reinterpret_cast<const f32x4 *>(sG + r * LDX + c0);
+                const f32x4 ki = *reinterpret_cast<const f32x4 *>(sK + (16 * I + lr) * LDK + c0);
+                const f32x4 qi = *reinterpret_cast<const f32x4 *>(sQ + (16 * I + lr) * LDX + c0);
+                const f32x4 Gi = *reinterpret_cast<const f32x4 *>(sG + (16 * I + lr) * LDX + c0);
+                const f32x4 kj = *reinterpret_cast<const f32x4 *>(sK + (16 * J + lr) * LDK + c0);
+                const f32x4 Gj = *reinterpret_cast<const f32x4 *>(sG + (16 * J + lr) * LDX + c0);
+                f32x4 Ka, Qa, Kb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float EI = __expf(Gi[e] - Gr[e]);
+                    Ka[e] = ki[e] * EI;
+                    Qa[e] = qi[e] * EI;
+                    Kb[e] = kj[e] * __expf(Gr[e] - Gj[e]);
+                }
+                mma(accA, Ka, Kb);
+                mma(accM, Qa, Kb);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float kjE = kj[e] * __expf(Gi[e] - Gj[e]);
-                sa += ki[e] * kjE;
-                sm += qi[e] * kjE;
+                const int i = 16 * I + 4 * q4 + e, j = 16 * J + lr;
+                const float av = j < i ? accA[e] : 0.f;
+                sA[i * LDA + j] = av;
+                rec[R::oA + i * C + j] = av;
+                rec[R::oM + j * C + i] = j <= i ? a.scale * accM[e] : 0.f;   // M^T
             }
         }
-        const float av = j < i ? sa : 0.f;
-        sA[i * LDA + j] = av;
-        rec[R::oA + i * C + j] = av;
-        rec[R::oM + j * C + i] = a.scale * sm;   // M^T
     }
-    for (int p = tid; p < C * C; p += NT) {
+    for (int p = tid; p < C * C; p += NT) {   // blocks above the diagonal
         const int i = p / C, j = p % C;
-        if (j > i) {
+        if ((j >> 4) > (i >> 4)) {
             sA[i * LDA + j] = 0.f;
             rec[R::oA + p] = 0.f;
             rec[R::oM + j * C + i] = 0.f;
@@ -300,12 +361,11 @@ template <int C, int DK, int DV> struct FwdOps {
 };
 
 template <int C, int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_fwd_state_kernel(BwdArgs a) {
+__device__ __forceinline__ void fwd_state_pass(const BwdArgs &a, int chain, int vb) {
     using R = BRec<C, DK, DV>;
     using P = StatePass<C, DK, DV>;
     constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW, NOWN = P::NOWN;
     __shared__ f32x4 sPart[NW][IT][64];
-    const int chain = blockIdx.x, vb = blockIdx.y;
     const int n = chain / a.H, h = chain % a.H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, q4 = lane >> 4;
     const int64_t st = seq_start(a, n), len = seq_start(a, n + 1) - st;
@@ -409,12 +469,11 @@ template <int C, int DK, int DV> struct RevOps {
 };
 
 template <int C, int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_rev_state_kernel(BwdArgs a) {
+__device__ __forceinline__ void rev_state_pass(const BwdArgs &a, int chain, int vb) {
     using R = BRec<C, DK, DV>;
     using P = StatePass<C, DK, DV>;
     constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW, NOWN = P::NOWN;
     __shared__ f32x4 sPart[NW][IT][64];
-    const int chain = blockIdx.x, vb = blockIdx.y;
     const int n = chain / a.H, h = chain % a.H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, q4 = lane >> 4;
     const int64_t st = seq_start(a, n), len = seq_start(a, n + 1) - st;
@@ -463,7 +522,9 @@ __global__ __launch_bounds__(256) void bwd_rev_state_kernel(BwdArgs a) {
     auto step = [&](int j, RevOps<C, DK, DV> &cur, RevOps<C, DK, DV> &nxt) {
         float *rec = rec_of(j);
         if (j > 0) load(j - 1, nxt);
-        f32x4 QgT[KTW][IT], WT[KTW][IT];   // needed after the exchange below
+        // Qg^T and W^T are needed only after the exchange below: loaded here, not a chunk ahead
+        // (a third prefetched set costs more in register moves than it saves)
+        f32x4 QgT[KTW][IT], WT[KTW][IT];
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk) {
             const int kt = wave * KTW + kk;
@@ -538,6 +599,14 @@ __global__ __launch_bounds__(256) void bwd_rev_state_kernel(BwdArgs a) {
     }
 }
 
+// The two state passes depend only on prep's records (and dL/do), not on each other: one
+// launch runs both, the forward chains in grid layer z = 0 and the reverse ones in z = 1.
+template <int C, int DK, int DV>
+__global__ __launch_bounds__(256) void bwd_state_kernel(BwdArgs a) {
+    if (blockIdx.z == 0) fwd_state_pass<C, DK, DV>(a, blockIdx.x, blockIdx.y);
+    else rev_state_pass<C, DK, DV>(a, blockIdx.x, blockIdx.y);
+}
+
 // ------------------------------------------------------------------------------------------
 // 4. grad1: one workgroup of 8 waves per (chunk, head)
 // ------------------------------------------------------------------------------------------
@@ -546,14 +615,17 @@ __global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
     using R = BRec<C, DK, DV>;
     constexpr int NT = 512, NWV = 8, IT = C / 16, KT = DK / 16, VT = DV / 16;
     constexpr int NLT = IT * (IT + 1) / 2;  // lower-triangle 16x16 tiles (it >= mt)
-    constexpr int LDK = DK + 4, LDA = C + 4;
+    constexpr int LDK = DK + 4, LDA = C + 4, LDV = DV + 4;
     constexpr int NSRC = KT + VT + IT;      // dbeta partial sums, one row per source
     static_assert(KT <= NWV && VT <= NWV, "one key / value column tile per wave");
+    constexpr int NOU = 2 * C * LDV > 3 * C * LDA ? 2 * C * LDV : 3 * C * LDA;
+    // dU, and dO then U, staged once for all waves; T, dT and T^T dT later take dO's and U's space
+    __shared__ __align__(16) float sdU[C * LDV];
+    __shared__ __align__(16) float sOU[NOU];
     __shared__ __align__(16) float sW[C * LDK];   // dW
-    __shared__ __align__(16) float sT[C * LDA];   // T
-    __shared__ __align__(16) float sdT[C * LDA];  // dT
-    __shared__ __align__(16) float sX[C * LDA];   // T^T dT
     __shared__ float sDb[NSRC][C];
+    float *sdO = sOU, *sU = sOU + C * LDV;
+    float *sT = sOU, *sdT = sOU + C * LDA, *sX = sOU + 2 * C * LDA;
 
     const int64_t s = blockIdx.x;
     const int h = blockIdx.y;
@@ -572,38 +644,45 @@ __global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
     };
     auto beta_of = [&](int i) { return i < L ? a.beta[(t0 + i) * a.H + h] : 0.f; };
 
-    for (int idx = tid; idx < C * C / 4; idx += NT) {
-        const int i = idx / (C / 4), m = 4 * (idx % (C / 4));
-        *reinterpret_cast<f32x4 *>(sT + i * LDA + m) = *reinterpret_cast<const f32x4 *>(rec + R::oT + i * C + m);
+    for (int idx = tid; idx < C * DV / 4; idx += NT) {
+        const int i = idx / (DV / 4), j = 4 * (idx % (DV / 4));
+        f32x4 dOv = zero4();
+        if (i < L) dOv = *reinterpret_cast<const f32x4 *>(a.dout + (t0 + i) * rsv + (int64_t)h * DV + j);
+        *reinterpret_cast<f32x4 *>(sdO + i * LDV + j) = dOv;
+        *reinterpret_cast<f32x4 *>(sU + i * LDV + j) = *reinterpret_cast<const f32x4 *>(rec + R::oU + i * DV + j);
+        *reinterpret_cast<f32x4 *>(sdU + i * LDV + j) = *reinterpret_cast<const f32x4 *>(rec + R::odU + i * DV + j);
     }
     for (int idx = tid; idx < NSRC * C; idx += NT) (&sDb[0][0])[idx] = 0.f;
-    for (int p = tid; p < C * C; p += NT) {  // dT above the diagonal tiles is never formed
-        const int i = p / C, m = p % C;
-        if ((m >> 4) > (i >> 4)) sdT[i * LDA + m] = 0.f;
-    }
-
-    // dQg = dO S^T, dKd = U dS'^T, dW = -dU S^T for key tile ct = wave
+    // this wave's rows of S and dS' (key tile ct = wave): the B fragments below
     const int ct = wave;
+    f32x4 hB[VT], dhB[VT];
+    if (ct < KT) {
+#pragma unroll
+        for (int js = 0; js < VT; ++js) {
+            hB[js] = *reinterpret_cast<const f32x4 *>(rec + R::oH + (16 * ct + lr) * DV + 16 * js + 4 * q4);
+            dhB[js] = *reinterpret_cast<const f32x4 *>(rec + R::odH + (16 * ct + lr) * DV + 16 * js + 4 * q4);
+        }
+    }
+    __syncthreads();
+
+    // dQg = dO S^T, dKd = U dS'^T, dW = -dU S^T for key tile ct; d e^{gC} = rowsum(S * dS')
     f32x4 dq_p[IT], dk_p[IT], dG_p[IT];
     if (ct < KT) {
         f32x4 aQ[IT], aK[IT], aW[IT];
 #pragma unroll
         for (int it = 0; it < IT; ++it) aQ[it] = aK[it] = aW[it] = zero4();
+        float dgc = 0.f;
+#pragma unroll
         for (int js = 0; js < VT; ++js) {
             const int j0 = 16 * js + 4 * q4;
-            const f32x4 hB = *reinterpret_cast<const f32x4 *>(rec + R::oH + (16 * ct + lr) * DV + j0);
-            const f32x4 dhB = *reinterpret_cast<const f32x4 *>(rec + R::odH + (16 * ct + lr) * DV + j0);
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
                 const int i = 16 * it + lr;
-                f32x4 dOa = zero4();
-                if (i < L) dOa = *reinterpret_cast<const f32x4 *>(a.dout + ((t0 + i) * a.H + h) * DV + j0);
-                const f32x4 Ua = *reinterpret_cast<const f32x4 *>(rec + R::oU + i * DV + j0);
-                const f32x4 dUa = *reinterpret_cast<const f32x4 *>(rec + R::odU + i * DV + j0);
-                mma(aQ[it], dOa, hB);
-                mma(aK[it], Ua, dhB);
-                mma(aW[it], dUa, hB);
+                mma(aQ[it], *reinterpret_cast<const f32x4 *>(sdO + i * LDV + j0), hB[js]);
+                mma(aK[it], *reinterpret_cast<const f32x4 *>(sU + i * LDV + j0), dhB[js]);
+                mma(aW[it], *reinterpret_cast<const f32x4 *>(sdU + i * LDV + j0), hB[js]);
             }
+            dgc += hB[js][0] * dhB[js][0] + hB[js][1] * dhB[js][1] + hB[js][2] * dhB[js][2] + hB[js][3] * dhB[js][3];
         }
         const int c = 16 * ct + lr;
         const float gC = rec[R::oG + (C - 1) * DK + c];
@@ -623,13 +702,6 @@ __global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
             }
         cs += __shfl_xor(cs, 16);
         cs += __shfl_xor(cs, 32);
-        // d e^{gC}: sum_j S[c][j] dS'[c][j]; lane (lr, q4) takes columns 16 js + 4 q4 .. + 3
-        float dgc = 0.f;
-        for (int js = 0; js < VT; ++js) {
-            const f32x4 hv = *reinterpret_cast<const f32x4 *>(rec + R::oH + c * DV + 16 * js + 4 * q4);
-            const f32x4 dhv = *reinterpret_cast<const f32x4 *>(rec + R::odH + c * DV + 16 * js + 4 * q4);
-            dgc += hv[0] * dhv[0] + hv[1] * dhv[1] + hv[2] * dhv[2] + hv[3] * dhv[3];
-        }
         dgc += __shfl_xor(dgc, 16);
         dgc += __shfl_xor(dgc, 32);
         // gC is G of the last valid row (g is zero past it): its gradient goes to row L - 1
@@ -645,12 +717,11 @@ __global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
         int it, mt;
         tile_of(p, it, mt);
         f32x4 acc = zero4();
-        const int i = 16 * it + lr;
+#pragma unroll
         for (int js = 0; js < VT; ++js) {
             const int j0 = 16 * js + 4 * q4;
-            f32x4 dOa = zero4();
-            if (i < L) dOa = *reinterpret_cast<const f32x4 *>(a.dout + ((t0 + i) * a.H + h) * DV + j0);
-            mma(acc, dOa, *reinterpret_cast<const f32x4 *>(rec + R::oU + (16 * mt + lr) * DV + j0));
+            mma(acc, *reinterpret_cast<const f32x4 *>(sdO + (16 * it + lr) * LDV + j0),
+                *reinterpret_cast<const f32x4 *>(sU + (16 * mt + lr) * LDV + j0));
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -658,7 +729,16 @@ __global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
             rec[R::oM + r * C + m] = m <= r ? acc[e] : 0.f;
         }
     }
-    __syncthreads();  // sW, sT, sdT zeros, sDb ready
+    __syncthreads();  // dO and U no longer read: T, dT, X take their space; sW complete
+    for (int idx = tid; idx < C * C / 4; idx += NT) {
+        const int i = idx / (C / 4), m = 4 * (idx % (C / 4));
+        *reinterpret_cast<f32x4 *>(sT + i * LDA + m) = *reinterpret_cast<const f32x4 *>(rec + R::oT + i * C + m);
+    }
+    for (int p = tid; p < C * C; p += NT) {  // dT above the diagonal tiles is never formed
+        const int i = p / C, m = p % C;
+        if ((m >> 4) > (i >> 4)) sdT[i * LDA + m] = 0.f;
+    }
+    __syncthreads();
 
     // dT = dU (beta v)^T + dW (beta k e^G)^T, lower tiles
     for (int p = wave; p < NLT; p += NWV) {
@@ -671,7 +751,7 @@ __global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
             const int j0 = 16 * js + 4 * q4;
             f32x4 vb = zero4();
             if (m < L) vb = load4(vin + (t0 + m) * rsv + (int64_t)h * DV + j0) * bm;
-            mma(acc, *reinterpret_cast<const f32x4 *>(rec + R::odU + (16 * it + lr) * DV + j0), vb);
+            mma(acc, *reinterpret_cast<const f32x4 *>(sdU + (16 * it + lr) * LDV + j0), vb);
         }
         for (int cs = 0; cs < KT; ++cs) {
             const int c0 = 16 * cs + 4 * q4;
@@ -736,7 +816,7 @@ __global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     const int m = 16 * ms + 4 * q4 + e;
                     A[e] = sT[m * LDA + 16 * it + lr];
-                    B[e] = rec[R::odU + m * DV + j];
+                    B[e] = sdU[m * LDV + j];
                 }
                 mma(acc, A, B);
             }
@@ -812,7 +892,6 @@ __global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
 //      dG_i += Ka dKa + Qa dQa,  dG_j -= Kb dKb
 //    then dq, dk are completed and dg is the reverse running sum of dG inside the chunk.
 // ------------------------------------------------------------------------------------------
-constexpr float kExtremeLogDecay = 60.f;
 
 template <typename Tin, int C, int DK, int DV>
 __global__ __launch_bounds__(DK * 4) void bwd_grad2_kernel(BwdArgs a) {
@@ -993,10 +1072,8 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_prep_kernel<Tin, C, DK, DV>), gs, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 gc((unsigned)(a.n_seqs * a.H), (unsigned)(DV / 16));
-    hipLaunchKernelGGL((bwd_fwd_state_kernel<C, DK, DV>), gc, dim3(64 * P::NW), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_rev_state_kernel<C, DK, DV>), gc, dim3(64 * P::NW), 0, stream, a);
+    const dim3 gc((unsigned)(a.n_seqs * a.H), (unsigned)(DV / 16), 2);
+    hipLaunchKernelGGL((bwd_state_kernel<C, DK, DV>), gc, dim3(64 * P::NW), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grad1_kernel<Tin, C, DK, DV>), gs, dim3(512), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

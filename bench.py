@@ -17,8 +17,10 @@ combine and chunked-forward kernels). The roofline fraction uses algorithmic byt
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
   python bench.py --counter-pass [--steps K]
-      only the prefill calls, then a plain copy-like kernel (out = -x over COPY_BYTES) as the
-      HBM-counter calibration; run it under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE
+      only the prefill calls (then two backward calls at the 4K-token, 16-head shape), then a
+      plain copy-like kernel (out = -x over COPY_BYTES) as the HBM-counter calibration; run it
+      under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (and MfmaUtil MfmaFlopsF16 MfmaFlopsF32
+      for the matrix-core counters)
   python bench.py --traffic-from FETCH_CSV WRITE_CSV
       turn the two counter_collection.csv files of those runs into the per-call HBM traffic
       (profiles/kda_chunk_fwd_prefill_128k_h32_traffic.json), tagged with the kernel source hash
@@ -455,6 +457,16 @@ def main():
         for _ in range(args.warmup + args.steps):
             kda.kda_chunk_fwd(pq, pk, pv, pg, pb, final_state=pS, o=po, workspace=pws)
         torch.cuda.synchronize()
+        # two backward calls at the 4K-token, 16-head training shape (matrix-core counters)
+        wb = synth.WORKLOADS["prefill_4k_h16"]
+        xb = synth.make_inputs(wb)
+        bq, bk, bv = (to_dev(xb[n][None], True) for n in ("q", "k", "v"))
+        bg, bb = to_dev(xb["g"][None]), to_dev(xb["beta"][None])
+        bdo = torch.from_numpy(np.stack([synth.grad_out(wb, 0, h) for h in range(wb.H)], axis=1)[None]).to(dev)
+        for _ in range(2):
+            kda.kda_chunk_bwd(bq, bk, bv, bg, bb, bdo, want_dinitial_state=False)
+        torch.cuda.synchronize()
+        del bq, bk, bv, bg, bb, bdo, xb
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):

@@ -139,3 +139,32 @@ def test_bf16_strong_decay_and_degenerate_gates():
     note("bwd bf16 strong decay")
     got, ref = run_case(x, "bf16", [T], chunk=64, dsT=dsT, do=do)
     check(got, ref, TOL_BF16)
+
+
+def test_f32_d16_extreme_decay():
+    """The fp32 16-token-chunk instantiation with decay far beyond e^-60 inside a chunk (the
+    pair-by-pair paths of prep and grad2), write strengths of zero on some tokens."""
+    T, H = 70, 2
+    x = random_inputs(600, T, H, 16, "f32")
+    x["g"][10:40] *= 60.0
+    x["beta"][45:50] = 0.0
+    s0 = random_states(601, 1, H, 16)
+    do, dsT = upstream(602, [T], H, 16, 16)
+    note("bwd f32 D=16 extreme decay")
+    got, ref = run_case(x, "f32", [T], chunk=16, s0=s0, dsT=dsT, do=do, scale=0.9)
+    check(got, ref, TOL_F32)
+
+
+def test_empty_sequence_hands_back_the_state_gradient():
+    """B = 1, T = 0: no tokens, dS_init = dL/dS_final exactly."""
+    torch = torch_mod()
+    H, D = 2, 128
+    dsT = random_states(610, 1, H, D)
+    e = torch.empty((1, 0, H, D), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((1, 0, H, D), dtype=torch.float32, device="cuda")
+    b = torch.empty((1, 0, H), dtype=torch.float32, device="cuda")
+    note("bwd empty batch")
+    got = kda.kda_chunk_bwd(e, e, e, g, b, g, dfinal_state=to_dev(dsT))
+    torch.cuda.synchronize()
+    assert np.array_equal(got[5].cpu().numpy(), dsT)
+    assert all(t.numel() == 0 for t in got[:5])

@@ -422,7 +422,7 @@ def main():
         write_traffic(*args.traffic_from)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               "(the KDA core needs no collectives: (sequence, head) chains are independent)",
               file=sys.stderr)
         sys.exit(2)

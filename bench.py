@@ -382,6 +382,28 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
     ms = timed(lambda: dst.copy_(src), 10)
     out["copy_reference"] = {"bytes": 2 << 30, "gbs": round((2 << 30) / (ms * 1e-3) / 1e9, 1),
                              "what": "device-to-device copy of 1 GiB (read + write)"}
+    # the device's practical peaks, from the library's probes: a copy with 16-byte
+    # non-temporal loads, and a loop of independent fp16 matrix-core products on every CU
+    ms = timed(lambda: kda.kda_probe_copy(src, dst), 10)
+    copy_gbs = (2 << 30) / (ms * 1e-3) / 1e9
+    blocks, iters = 2048, 2000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    tf = {}
+    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+        flops = kda.kda_probe_mfma_f16(iters, blocks, sink, shape=shape)
+        ms = timed(lambda: kda.kda_probe_mfma_f16(iters, blocks, sink, shape=shape), 5)
+        tf[name] = flops / (ms * 1e-3) / 1e12
+    best = max(tf.values())
+    best_copy = max(copy_gbs, out["copy_reference"]["gbs"])
+    out["measured_peaks"] = {
+        "hbm_gbs": round(best_copy, 1), "hbm_frac_of_published": round(best_copy / HBM_PEAK_GBS, 4),
+        "hbm_gbs_by_copy": {"kda_probe_copy": round(copy_gbs, 1), "torch copy_": out["copy_reference"]["gbs"]},
+        "mfma_f16_tflops": round(best, 1),
+        "mfma_f16_tflops_by_instruction": {k: round(v, 1) for k, v in tf.items()},
+        "mfma_frac_of_published": round(best / MFMA_F16_PEAK_TFLOPS, 4),
+        "what": "the better of two 1 GiB copies (read + write); kda_probe_mfma_f16, 2048 x 256 threads"}
+    del src, dst, sink
+    log("measured the copy and fp16 matrix-core peaks")
     return out
 
 
@@ -582,6 +604,9 @@ def main():
     if not args.no_extra:
         del pq, pk, pv, pg, pb, po, pws, tq, tk, tv, tg, tb
         res["other_workloads"] = other_workloads(kda, synth, to_dev, torch, np, log, state)
+        mp = res["other_workloads"]["measured_peaks"]
+        res["roofline"]["frac_of_measured_peak"] = round(res["roofline"]["achieved"] / mp["hbm_gbs"], 4)
+        res["decode"]["frac_of_measured_peak"] = round(res["decode"]["achieved_gbs"] / mp["hbm_gbs"], 4)
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(xp, min(args.cpu_sample_tokens, T))

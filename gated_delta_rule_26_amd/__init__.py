@@ -72,6 +72,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_chunk_bwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, f32,
                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   vp, i32, vp, sz, vp]
+    lib.kda_probe_copy.restype = i32
+    lib.kda_probe_copy.argtypes = [vp, vp, sz, vp]
+    lib.kda_probe_mfma_f16.restype = i32
+    lib.kda_probe_mfma_f16.argtypes = [i32, i32, i32, vp, vp]
+    lib.kda_probe_mfma_f16_flops.restype = ctypes.c_double
+    lib.kda_probe_mfma_f16_flops.argtypes = [i32, i32]
     lib.kda_decode_step.restype = i32
     lib.kda_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, f32,
                                     vp, vp, vp, vp, vp, vp, vp, vp]
@@ -296,6 +302,31 @@ def kda_chunk_bwd(q, k, v, g, beta, do, *, initial_state=None, dfinal_state=None
                            workspace.numel(), _stream(stream))
     _check(lib, st)
     return dq, dk, dv, dg, db, ds0
+
+
+def kda_probe_copy(src, dst, stream=None):
+    """dst = src with the library's copy probe (C: kda_probe_copy); both contiguous device
+    tensors of the same byte size (a multiple of 16)."""
+    lib = load_library()
+    _req(src, "src")
+    _req(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same byte size")
+    _check(lib, lib.kda_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def kda_probe_mfma_f16(iters: int, blocks: int, sink, shape: int = 0, stream=None) -> float:
+    """Run the fp16 matrix-core probe (C: kda_probe_mfma_f16; shape 0: 16x16x32, 1: 32x32x16
+    instructions) into ``sink`` (float32, at least blocks * 256 elements); returns the launch's
+    dense fp16 flops."""
+    import torch
+    lib = load_library()
+    _req(sink, "sink", torch.float32)
+    if sink.numel() < blocks * 256:
+        raise ValueError("sink needs blocks * 256 elements")
+    _check(lib, lib.kda_probe_mfma_f16(int(shape), int(iters), int(blocks), _ptr(sink), _stream(stream)))
+    return float(lib.kda_probe_mfma_f16_flops(int(iters), int(blocks)))
 
 
 def chunk_bwd_workspace_bytes(q, v, *, chunk: int = 64, num_seqs: int | None = None) -> int:

@@ -10,7 +10,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_bwd.hip", "kda_decode.hip", "kda_conv.hip"]
+SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_bwd.hip", "kda_decode.hip", "kda_conv.hip", "kda_probe.hip"]
 ARCH = "gfx950"
 
 

@@ -501,4 +501,25 @@ kda_status kda_recurrent_fwd(int32_t N, int32_t L, int32_t H, int32_t Dk, int32_
                       "kda_recurrent_fwd launch");
 }
 
+kda_status kda_probe_copy(const void *src, void *dst, size_t bytes, void *stream) {
+    if (!src || !dst || bytes == 0 || bytes % 16 != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "src, dst and a positive multiple of 16 bytes are required");
+    if (!aligned16(src) || !aligned16(dst))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    return hip_status(kda::launch_probe_copy(src, dst, (int64_t)bytes, static_cast<hipStream_t>(stream)),
+                      "kda_probe_copy launch");
+}
+
+kda_status kda_probe_mfma_f16(int32_t shape, int32_t iters, int32_t blocks, float *sink, void *stream) {
+    if (shape < 0 || shape > 1 || iters < 1 || blocks < 1 || !sink)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "shape 0 or 1, positive iters and blocks, and sink are required");
+    if (!aligned16(sink)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    return hip_status(kda::launch_probe_mfma(shape, iters, blocks, sink, static_cast<hipStream_t>(stream)),
+                      "kda_probe_mfma_f16 launch");
+}
+
+double kda_probe_mfma_f16_flops(int32_t iters, int32_t blocks) {
+    return (double)iters * (double)blocks * 256.0 * (double)kda::probe_mfma_flops_per_iter_and_thread();
+}
+
 }  // extern "C"

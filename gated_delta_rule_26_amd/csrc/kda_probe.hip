@@ -1,0 +1,102 @@
+// Measurement probes: the device's practical peaks, against which the KDA kernels' roofline
+// fractions are also reported (next to the published ones).
+//
+// * copy: dst = src over `bytes`, 16-byte vectors, non-temporal loads (the state stream of the
+//   decode step reads the same way): the practical HBM bandwidth of a kernel that reads each
+//   byte once and writes each byte once.
+// * fp16 matrix cores: every wave runs a loop of independent fp16 matrix-core products on
+//   several accumulators (16x16x32 or 32x32x16 instructions, the same flops per iteration),
+//   the operands held in registers; the accumulators are written out at the end so nothing is
+//   optimised away.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+// Eight 16-byte loads per thread are issued before any store (the decode step's pattern: a
+// thread reads its whole slice, then writes it), so enough bytes are in flight per CU.
+constexpr int kCopyVec = 8;
+
+__global__ __launch_bounds__(256) void probe_copy_kernel(const f32x4 *__restrict__ src, f32x4 *__restrict__ dst,
+                                                         int64_t n) {
+    const int64_t base = (int64_t)blockIdx.x * 256 * kCopyVec + threadIdx.x;
+    f32x4 v[kCopyVec];
+#pragma unroll
+    for (int u = 0; u < kCopyVec; ++u) {
+        const int64_t i = base + (int64_t)u * 256;
+        if (i < n) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyVec; ++u) {
+        const int64_t i = base + (int64_t)u * 256;
+        if (i < n) dst[i] = v[u];
+    }
+}
+
+constexpr int kProbeAcc = 8;
+
+// SHAPE 0: v_mfma_f32_16x16x32_f16 (eight 4-float accumulators per lane);
+// SHAPE 1: v_mfma_f32_32x32x16_f16 (four 16-float accumulators per lane).
+template <int SHAPE> __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float *sink) {
+    f16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = static_cast<_Float16>(1e-3f * (threadIdx.x + e));
+        b[e] = static_cast<_Float16>(1e-3f * (blockIdx.x + e));
+    }
+    float out = 0.f;
+    if constexpr (SHAPE == 0) {
+        f32x4 acc[kProbeAcc];
+#pragma unroll
+        for (int j = 0; j < kProbeAcc; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < kProbeAcc; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kProbeAcc; ++j) out += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    } else {
+        typedef float f32x16 __attribute__((ext_vector_type(16)));
+        f32x16 acc[kProbeAcc / 2];
+#pragma unroll
+        for (int j = 0; j < kProbeAcc / 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < kProbeAcc / 2; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kProbeAcc / 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) out += acc[j][e];
+    }
+    sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = out;
+}
+
+}  // namespace
+
+hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream) {
+    const int64_t n = bytes / 16, blocks = (n + 256 * kCopyVec - 1) / (256 * kCopyVec);
+    hipLaunchKernelGGL(probe_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const f32x4 *>(src), static_cast<f32x4 *>(dst), n);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma(int32_t shape, int32_t iters, int32_t blocks, float *sink, hipStream_t stream) {
+    if (shape == 0)
+        hipLaunchKernelGGL(probe_mfma_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, iters, sink);
+    else
+        hipLaunchKernelGGL(probe_mfma_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, iters, sink);
+    return hipGetLastError();
+}
+
+int64_t probe_mfma_flops_per_iter_and_thread() {
+    // per wave and iteration: eight 16x16x32 products, or four 32x32x16 ones (the same
+    // 2 * 8 * 16 * 16 * 32 flops), shared by the wave's 64 lanes
+    return (int64_t)kProbeAcc * 2 * 16 * 16 * 32 / 64;
+}
+
+}  // namespace kda

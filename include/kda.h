@@ -313,6 +313,24 @@ kda_status kda_short_conv_update(int32_t N, int32_t C, int32_t W, int32_t dtype,
                                  const void *x, const float *weight, const float *bias, void *state,
                                  void *y, void *stream);
 
+/*
+ * Measurement probes: the device's practical peaks, which the benchmark reports the kernels'
+ * roofline fractions against (next to the published peaks). Not part of the KDA path.
+ *
+ * kda_probe_copy - dst = src over `bytes` (a multiple of 16; both 16-byte aligned device
+ *   pointers, not overlapping), read with non-temporal 16-byte loads: the HBM bandwidth of a
+ *   kernel that reads and writes each byte once is 2 * bytes / time.
+ * kda_probe_mfma_f16 - `blocks` workgroups of 256 threads each run `iters` iterations of
+ *   independent fp16 matrix-core products per wave: eight v_mfma_f32_16x16x32_f16 (shape 0)
+ *   or four v_mfma_f32_32x32x16_f16 (shape 1), the same flops; sink [blocks * 256] float32
+ *   receives the accumulators (so nothing is optimised away). kda_probe_mfma_f16_flops gives
+ *   the launch's dense fp16 flops.
+ * Errors as kda_chunk_fwd (invalid sizes or pointers, nothing launched).
+ */
+kda_status kda_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
+kda_status kda_probe_mfma_f16(int32_t shape, int32_t iters, int32_t blocks, float *sink, void *stream);
+double kda_probe_mfma_f16_flops(int32_t iters, int32_t blocks);
+
 #ifdef __cplusplus
 }
 #endif

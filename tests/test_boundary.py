@@ -296,3 +296,20 @@ def test_chunk_bwd_workspace_bytes(lib):
 def test_chunk_bwd_empty_work_is_ok_without_launch(lib):
     assert bwd(lib, T=0, cu=P, N=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None,
                dk=None, dv=None, dg=None, db=None, ws=None) == OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, P, 1024), INVALID), ((P, None, 1024), INVALID), ((P, P, 0), INVALID),
+    ((P, P, 1000), INVALID), ((MIS, P, 1024), INVALID), ((P, MIS, 1024), INVALID),
+])
+def test_probe_copy_rejects_before_launch(lib, args, status):
+    assert lib.kda_probe_copy(*args, None) == status
+
+
+def test_probe_mfma_rejects_and_counts(lib):
+    assert lib.kda_probe_mfma_f16(0, 0, 1, P, None) == INVALID
+    assert lib.kda_probe_mfma_f16(0, 1, 0, P, None) == INVALID
+    assert lib.kda_probe_mfma_f16(0, 1, 1, None, None) == INVALID
+    assert lib.kda_probe_mfma_f16(2, 1, 1, P, None) == INVALID
+    # 8 accumulators x 2*16*16*32 flops per wave and iteration, 4 waves per workgroup
+    assert lib.kda_probe_mfma_f16_flops(10, 3) == 10 * 3 * 4 * 8 * 2 * 16 * 16 * 32

@@ -17,19 +17,17 @@
 // the reverse running sum of dL/dG inside the chunk.
 //
 // Mapping to the MI355X. Everything is float32 (fp32 matrix cores, v_mfma_f32_16x16x4f32).
-// Five kernels, each a plain pass over a per-(chunk, head) record in the workspace:
+// Three launches, each a plain pass over a per-(chunk, head) record in the workspace:
 //  1. prep    (one workgroup per chunk and head): G, Qg, Kd, e^{gC}, A~ and M as 16x16 block
 //             pairs on the matrix cores (decay split at block boundaries; pair by pair for a
 //             block decaying below e^-60), T by column substitution in one wave, W and U~.
-//  2. forward state pass (per chain and 16 value columns, chunks in order): stores the state
-//             entering each chunk and U; the waves split the key channels and sum U through LDS.
-//  3. reverse state pass (per chain and 16 value columns, chunks in reverse): stores dS' and dU,
-//             writes dS_init. It needs only prep's records, so 2 and 3 share one launch.
-//  4. grad1   (per chunk and head): the products with S, dS', U and dU, then T^T dW, T^T dU and
-//             T^T dT T^T; writes dv and dbeta, partial dq, dk, dG and the pair gradients dA~, dM.
-//  5. grad2   (per chunk and head): the pair terms on the matrix cores, 16x16 block pairs
-//             split at block boundaries (pair by pair for channels of extremely decaying
-//             blocks), then the reverse running sum of dG.
+//  2. state   the forward state pass (chunks in order: the state entering each chunk, and U)
+//             and the reverse one (chunks in reverse: dS' and dU, then dS_init) side by side,
+//             per chain and 16 value columns; the reverse pass needs only prep's records.
+//  3. grad    (per chunk and head): the products with S, dS', U and dU, then T^T dW, T^T dU
+//             and T^T dT T^T (dv, dbeta), then the pair terms of A~ and M on the matrix cores
+//             (pair by pair for channels of extremely decaying blocks), then dq, dk and the
+//             reverse running sum of dG; the partial gradients never leave the registers.
 // Chunks of a packed batch are numbered by slot n + floor(start_n / C) + j (sequence n, chunk j),
 // which is unique and below N + ceil(tokens / C), so the records need no host-side lengths.
 #include "kda_device.h"
@@ -608,24 +606,36 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// 4. grad1: one workgroup of 8 waves per (chunk, head)
+// 4. grad: one workgroup of 8 waves per (chunk, head). First the products with S, dS', U and
+//    dU, then T^T dW, T^T dU and T^T dT T^T (dv, dbeta, partial dq, dk, dG, and dA~, dM kept in
+//    LDS), then the pair terms of A~ and M (below), then dq, dk and the reverse running sum of
+//    dG. Wave w holds key channels 16 w .. 16 w + 15; lane (lr, q4) holds rows 16 X + 4 q4 + e
+//    of channel 16 w + lr throughout, so the partial gradients stay in registers.
 // ------------------------------------------------------------------------------------------
 template <typename Tin, int C, int DK, int DV>
-__global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     using R = BRec<C, DK, DV>;
     constexpr int NT = 512, NWV = 8, IT = C / 16, KT = DK / 16, VT = DV / 16;
     constexpr int NLT = IT * (IT + 1) / 2;  // lower-triangle 16x16 tiles (it >= mt)
     constexpr int LDK = DK + 4, LDA = C + 4, LDV = DV + 4;
     constexpr int NSRC = KT + VT + IT;      // dbeta partial sums, one row per source
     static_assert(KT <= NWV && VT <= NWV, "one key / value column tile per wave");
-    constexpr int NOU = 2 * C * LDV > 3 * C * LDA ? 2 * C * LDV : 3 * C * LDA;
+    constexpr int LDG = DK + 1;
+    // the pair-term phase's arrays, over dO / U / T / dT / X once those are done
+    constexpr int NG2 = 2 * IT * DK + KT * 768 + C * LDG;
+    constexpr int NOU0 = 2 * C * LDV > 3 * C * LDA ? 2 * C * LDV : 3 * C * LDA;
+    constexpr int NOU = NOU0 > NG2 ? NOU0 : NG2;
     // dU, and dO then U, staged once for all waves; T, dT and T^T dT later take dO's and U's space
     __shared__ __align__(16) float sdU[C * LDV];
     __shared__ __align__(16) float sOU[NOU];
-    __shared__ __align__(16) float sW[C * LDK];   // dW
+    __shared__ __align__(16) float sW[C * LDK];   // dW, then dA~ ([C][LDA])
+    __shared__ __align__(16) float sdM[C * LDA];  // dM (lower, with the diagonal)
     __shared__ float sDb[NSRC][C];
     float *sdO = sOU, *sU = sOU + C * LDV;
     float *sT = sOU, *sdT = sOU + C * LDA, *sX = sOU + 2 * C * LDA;
+    float *sdA = sW;
+    float *sGs = sOU, *sGe = sOU + IT * DK, *sBlk = sOU + 2 * IT * DK, *sDG = sBlk + KT * 768;
+    static_assert(C * LDA <= C * LDK, "dA~ fits over dW");
 
     const int64_t s = blockIdx.x;
     const int h = blockIdx.y;
@@ -726,7 +736,7 @@ __global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * it + 4 * q4 + e, m = 16 * mt + lr;
-            rec[R::oM + r * C + m] = m <= r ? acc[e] : 0.f;
+            sdM[r * LDA + m] = m <= r ? acc[e] : 0.f;
         }
     }
     __syncthreads();  // dO and U no longer read: T, dT, X take their space; sW complete
@@ -795,12 +805,6 @@ __global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
                 dG_p[it][e] += kv * eG * dKg;
                 const float rs = sum16(acc[e] * kv * eG);
                 if (lr == 0) sDb[ct][i] = rs;
-                if (i < L) {
-                    const int64_t o = (t0 + i) * rsk + (int64_t)h * DK + c;
-                    a.dq[o] = dq_p[it][e];
-                    a.dk[o] = dk_p[it][e];
-                    a.dg[o] = dG_p[it][e];
-                }
             }
         }
     }
@@ -867,194 +871,163 @@ __global__ __launch_bounds__(512) void bwd_grad1_kernel(BwdArgs a) {
             const float At = rec[R::oA + i * C + j];
             const float rs = sum16(dA * At);
             if (lr == 0) sDb[KT + VT + jt][i] = rs;
-            rec[R::oA + i * C + j] = beta_of(i) * dA;
+            sdA[i * LDA + j] = beta_of(i) * dA;
         }
     }
-    __syncthreads();
+    // the tiles above the diagonal of dA~ (in dW's space) are read by no block pair below
+    __syncthreads();  // dA~ complete; T, dT and X no longer read
     if (tid < L) {
         float db = 0.f;
 #pragma unroll
         for (int r = 0; r < NSRC; ++r) db += sDb[r][tid];
         a.dbeta[(t0 + tid) * a.H + h] = db;
     }
-}
 
-// ------------------------------------------------------------------------------------------
-// 5. grad2: the pair terms of A~ and M, on the matrix cores. Wave w takes key channels
-//    16 w .. 16 w + 15 for all rows; lane (lr, q4) holds rows 16 X + 4 q4 + e of channel
-//    16 w + lr, which is both the accumulator layout and the B-fragment layout. For the block
-//    pair (I, J), J <= I, e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j} with r the last row of
-//    block J (J < I: both factors <= 1) or the first row of block I (diagonal: the second
-//    factor is at most the block's inverse decay). A channel whose diagonal block decays below
-//    e^-60 takes that block pair by pair instead (exact for any decay).
-//      dKa = dA~ Kb,  dQa = scale dM Kb,  dKb = dA~^T Ka + scale dM^T Qa
-//      dk += dKa e^{G_i - G_r} + dKb e^{G_r - G_j},  dq += dQa e^{G_i - G_r}
-//      dG_i += Ka dKa + Qa dQa,  dG_j -= Kb dKb
-//    then dq, dk are completed and dg is the reverse running sum of dG inside the chunk.
-// ------------------------------------------------------------------------------------------
-
-template <typename Tin, int C, int DK, int DV>
-__global__ __launch_bounds__(DK * 4) void bwd_grad2_kernel(BwdArgs a) {
-    using R = BRec<C, DK, DV>;
-    constexpr int IT = C / 16, LDA = C + 4, LDG = DK + 1;
-    __shared__ __align__(16) float sAM[2 * C * LDA];
-    float *sdA = sAM;                              // dA~ (strictly lower)
-    float *sdM = sAM + C * LDA;                    // dM (lower, with the diagonal)
-    __shared__ float sGs[IT][DK], sGe[IT][DK];     // G at the first / last row of each block
-    __shared__ float sBlk[DK / 16][3 * 16 * 16];   // per wave: one block's k, q, G (extreme decay)
-    float *sDG = sdA;                              // dG for the running sum, after the pairs
-    static_assert(C * LDG <= 2 * C * LDA, "dG fits over dA~ and dM");
-
-    const int64_t s = blockIdx.x;
-    const int h = blockIdx.y;
-    int n, L;
-    int64_t t0;
-    if (!locate<C>(a, s, n, t0, L)) return;
-    const float *rec = a.ws + (s * a.H + h) * R::FLOATS;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, q4 = lane >> 4;
-    const int c = 16 * wave + lr;
-    const int64_t rsk = (int64_t)a.H * DK;
-    const float scale = a.scale;
-
-    for (int idx = tid; idx < C * C / 4; idx += DK * 4) {
-        const int i = idx / (C / 4), m = 4 * (idx % (C / 4));
-        *reinterpret_cast<f32x4 *>(sdA + i * LDA + m) = *reinterpret_cast<const f32x4 *>(rec + R::oA + i * C + m);
-        *reinterpret_cast<f32x4 *>(sdM + i * LDA + m) = *reinterpret_cast<const f32x4 *>(rec + R::oM + i * C + m);
-    }
-    for (int idx = tid; idx < IT * DK; idx += DK * 4) {
+    // ---- the pair terms of A~ and M on the matrix cores. For the block pair (I, J), J <= I,
+    // e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j} with r the last row of block J (J < I: both
+    // factors <= 1) or the first row of block I (diagonal: the second factor is at most the
+    // block's inverse decay). A channel whose diagonal block decays below e^-60 takes that
+    // block pair by pair instead (exact for any decay).
+    //   dKa = dA~ Kb,  dQa = scale dM Kb,  dKb = dA~^T Ka + scale dM^T Qa
+    //   dk += dKa e^{G_i - G_r} + dKb e^{G_r - G_j},  dq += dQa e^{G_i - G_r}
+    //   dG_i += Ka dKa + Qa dQa,  dG_j -= Kb dKb
+    for (int idx = tid; idx < IT * DK; idx += NT) {
         const int b = idx / DK, cc = idx % DK;
-        sGs[b][cc] = rec[R::oG + (16 * b) * DK + cc];
-        sGe[b][cc] = rec[R::oG + (16 * b + 15) * DK + cc];
+        sGs[b * DK + cc] = rec[R::oG + (16 * b) * DK + cc];
+        sGe[b * DK + cc] = rec[R::oG + (16 * b + 15) * DK + cc];
     }
-    // this lane's rows of k, q, G (zero past the sequence end; G is constant there). Row
-    // 16 X + 4 q4 + e of the token arrays is at lane_off + (16 X + e) * rsk: one per-lane
-    // offset plus a uniform one, so no per-row address stays live.
-    const int64_t lane_off = (t0 + 4 * q4) * rsk + (int64_t)h * DK + c;
-    const Tin *kin = static_cast<const Tin *>(a.k) + lane_off;
-    const Tin *qin = static_cast<const Tin *>(a.q) + lane_off;
-    float kr[IT][4], qr[IT][4], Gr[IT][4];
-#pragma unroll
-    for (int X = 0; X < IT; ++X)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * X + 4 * q4 + e;
-            const int64_t ro = (int64_t)(16 * X + e) * rsk;
-            kr[X][e] = i < L ? to_f32(kin[ro]) : 0.f;
-            qr[X][e] = i < L ? to_f32(qin[ro]) : 0.f;
-            Gr[X][e] = rec[R::oG + i * DK + c];
-        }
     __syncthreads();
-
-    float dq[IT][4], dk[IT][4], dG[IT][4];
+    const float scale = a.scale;
+    if (ct < KT) {
+        const int c = 16 * ct + lr;
+        // this lane's rows of k, q, G (zero past the sequence end; G is constant there). Row
+        // 16 X + 4 q4 + e of the token arrays is at lane_off + (16 X + e) * rsk: one per-lane
+        // offset plus a uniform one, so no per-row address stays live.
+        const int64_t lane_off = (t0 + 4 * q4) * rsk + (int64_t)h * DK + c;
+        const Tin *kl = kin + lane_off;
+        const Tin *ql = static_cast<const Tin *>(a.q) + lane_off;
+        float kr[IT][4], qr[IT][4], Gr[IT][4];
 #pragma unroll
-    for (int X = 0; X < IT; ++X)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dq[X][e] = dk[X][e] = dG[X][e] = 0.f;
-
-#pragma unroll
-    for (int I = 0; I < IT; ++I) {
-#pragma unroll
-        for (int J = 0; J <= I; ++J) {
-            const bool diag = J == I;
-            const float Gref = diag ? sGs[I][c] : sGe[J][c];
-            // a channel whose diagonal block decays below e^-60 is done pair by pair below;
-            // zero factors drop its block-pair terms (and keep its MFMA columns finite)
-            const bool ext = diag && (sGs[I][c] - sGe[I][c] > kExtremeLogDecay);
-            f32x4 Ka, Qa, Kb, EI, EJ;
+        for (int X = 0; X < IT; ++X)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                EI[e] = ext ? 0.f : __expf(Gr[I][e] - Gref);          // <= 1
-                EJ[e] = ext ? 0.f : __expf(Gref - Gr[J][e]);          // <= 1 off the diagonal
-                Ka[e] = kr[I][e] * EI[e];
-                Qa[e] = qr[I][e] * EI[e];
-                Kb[e] = kr[J][e] * EJ[e];
+                const int i = 16 * X + 4 * q4 + e;
+                const int64_t ro = (int64_t)(16 * X + e) * rsk;
+                kr[X][e] = i < L ? to_f32(kl[ro]) : 0.f;
+                qr[X][e] = i < L ? to_f32(ql[ro]) : 0.f;
+                Gr[X][e] = rec[R::oG + i * DK + c];
             }
-            f32x4 aKa = zero4(), aQa = zero4(), aKb = zero4();
-            {
-                const f32x4 Ar = *reinterpret_cast<const f32x4 *>(sdA + (16 * I + lr) * LDA + 16 * J + 4 * q4);
-                const f32x4 Mr = *reinterpret_cast<const f32x4 *>(sdM + (16 * I + lr) * LDA + 16 * J + 4 * q4);
-                mma(aKa, Ar, Kb);
-                mma(aQa, Mr * scale, Kb);
-                f32x4 Ac, Mc;
+        float dq[IT][4], dk[IT][4], dG[IT][4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    Ac[e] = sdA[(16 * I + 4 * q4 + e) * LDA + 16 * J + lr];
-                    Mc[e] = sdM[(16 * I + 4 * q4 + e) * LDA + 16 * J + lr] * scale;
-                }
-                mma(aKb, Ac, Ka);
-                mma(aKb, Mc, Qa);
-            }
+        for (int X = 0; X < IT; ++X)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                dk[I][e] += aKa[e] * EI[e];
-                dq[I][e] += aQa[e] * EI[e];
-                dk[J][e] += aKb[e] * EJ[e];
-                dG[I][e] += Ka[e] * aKa[e] + Qa[e] * aQa[e];
-                dG[J][e] -= Kb[e] * aKb[e];
+                dq[X][e] = dq_p[X][e];
+                dk[X][e] = dk_p[X][e];
+                dG[X][e] = dG_p[X][e];
             }
-            if (diag && __any(ext)) {
-                // pair by pair for the channels of an extreme block: the block's rows of this
-                // wave's channels go through LDS ([k, q, G][row][channel])
-                float *blk = sBlk[wave];
+#pragma unroll
+        for (int I = 0; I < IT; ++I) {
+#pragma unroll
+            for (int J = 0; J <= I; ++J) {
+                const bool diag = J == I;
+                const float Gref = diag ? sGs[I * DK + c] : sGe[J * DK + c];
+                // a channel whose diagonal block decays below e^-60 is done pair by pair below;
+                // zero factors drop its block-pair terms (and keep its MFMA columns finite)
+                const bool ext = diag && (sGs[I * DK + c] - sGe[I * DK + c] > kExtremeLogDecay);
+                f32x4 Ka, Qa, Kb, EI, EJ;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * q4 + e;
-                    blk[(0 * 16 + r) * 16 + lr] = kr[I][e];
-                    blk[(1 * 16 + r) * 16 + lr] = qr[I][e];
-                    blk[(2 * 16 + r) * 16 + lr] = Gr[I][e];
+                    EI[e] = ext ? 0.f : __expf(Gr[I][e] - Gref);          // <= 1
+                    EJ[e] = ext ? 0.f : __expf(Gref - Gr[J][e]);          // <= 1 off the diagonal
+                    Ka[e] = kr[I][e] * EI[e];
+                    Qa[e] = qr[I][e] * EI[e];
+                    Kb[e] = kr[J][e] * EJ[e];
                 }
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                if (ext) {
+                f32x4 aKa = zero4(), aQa = zero4(), aKb = zero4();
+                {
+                    const f32x4 Ar = *reinterpret_cast<const f32x4 *>(sdA + (16 * I + lr) * LDA + 16 * J + 4 * q4);
+                    const f32x4 Mr = *reinterpret_cast<const f32x4 *>(sdM + (16 * I + lr) * LDA + 16 * J + 4 * q4);
+                    mma(aKa, Ar, Kb);
+                    mma(aQa, Mr * scale, Kb);
+                    f32x4 Ac, Mc;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int ri = 4 * q4 + e, i = 16 * I + ri;
-                        const float ki = kr[I][e], qi = qr[I][e], Gi = Gr[I][e];
-                        float pq = 0.f, pk = 0.f, pg = 0.f;
+                        Ac[e] = sdA[(16 * I + 4 * q4 + e) * LDA + 16 * J + lr];
+                        Mc[e] = sdM[(16 * I + 4 * q4 + e) * LDA + 16 * J + lr] * scale;
+                    }
+                    mma(aKb, Ac, Ka);
+                    mma(aKb, Mc, Qa);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dk[I][e] += aKa[e] * EI[e];
+                    dq[I][e] += aQa[e] * EI[e];
+                    dk[J][e] += aKb[e] * EJ[e];
+                    dG[I][e] += Ka[e] * aKa[e] + Qa[e] * aQa[e];
+                    dG[J][e] -= Kb[e] * aKb[e];
+                }
+                if (diag && __any(ext)) {
+                    // pair by pair for the channels of an extreme block: the block's rows of this
+                    // wave's channels go through LDS ([k, q, G][row][channel])
+                    float *blk = sBlk + ct * 768;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * q4 + e;
+                        blk[(0 * 16 + r) * 16 + lr] = kr[I][e];
+                        blk[(1 * 16 + r) * 16 + lr] = qr[I][e];
+                        blk[(2 * 16 + r) * 16 + lr] = Gr[I][e];
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    if (ext) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int ri = 4 * q4 + e, i = 16 * I + ri;
+                            const float ki = kr[I][e], qi = qr[I][e], Gi = Gr[I][e];
+                            float pq = 0.f, pk = 0.f, pg = 0.f;
 #pragma unroll 1
-                        for (int r = 0; r < 16; ++r) {
-                            const int j = 16 * I + r;
-                            const float kj = blk[r * 16 + lr], qj = blk[(16 + r) * 16 + lr];
-                            const float Gj = blk[(32 + r) * 16 + lr];
-                            if (r <= ri) {   // as the row: pairs (i, j <= i)
-                                const float E = __expf(Gi - Gj);
-                                const float dAij = sdA[i * LDA + j], dMij = scale * sdM[i * LDA + j];
-                                pq += dMij * kj * E;
-                                pk += dAij * kj * E;
-                                pg += (dAij * ki + dMij * qi) * kj * E;
+                            for (int r = 0; r < 16; ++r) {
+                                const int j = 16 * I + r;
+                                const float kj = blk[r * 16 + lr], qj = blk[(16 + r) * 16 + lr];
+                                const float Gj = blk[(32 + r) * 16 + lr];
+                                if (r <= ri) {   // as the row: pairs (i, j <= i)
+                                    const float E = __expf(Gi - Gj);
+                                    const float dAij = sdA[i * LDA + j], dMij = scale * sdM[i * LDA + j];
+                                    pq += dMij * kj * E;
+                                    pk += dAij * kj * E;
+                                    pg += (dAij * ki + dMij * qi) * kj * E;
+                                }
+                                if (r >= ri) {   // as the column: pairs (j >= i, i)
+                                    const float E = __expf(Gj - Gi);
+                                    const float z = (sdA[j * LDA + i] * kj + scale * sdM[j * LDA + i] * qj) * E;
+                                    pk += z;
+                                    pg -= z * ki;
+                                }
                             }
-                            if (r >= ri) {   // as the column: pairs (j >= i, i)
-                                const float E = __expf(Gj - Gi);
-                                const float z = (sdA[j * LDA + i] * kj + scale * sdM[j * LDA + i] * qj) * E;
-                                pk += z;
-                                pg -= z * ki;
-                            }
+                            dq[I][e] += pq;
+                            dk[I][e] += pk;
+                            dG[I][e] += pg;
                         }
-                        dq[I][e] += pq;
-                        dk[I][e] += pk;
-                        dG[I][e] += pg;
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);  // one block pair at a time (register pressure)
             }
-            __builtin_amdgcn_sched_barrier(0);  // one block pair at a time (register pressure)
         }
+        // dq and dk are complete; dG goes to LDS for the running sum
+#pragma unroll
+        for (int X = 0; X < IT; ++X)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * X + 4 * q4 + e;
+                if (i < L) {
+                    const int64_t o = lane_off + (int64_t)(16 * X + e) * rsk;
+                    a.dq[o] = dq[X][e];
+                    a.dk[o] = dk[X][e];
+                }
+                sDG[i * LDG + c] = dG[X][e];
+            }
     }
-    __syncthreads();  // dA~, dM no longer read: their space takes dG
-    // complete dq and dk; dG with grad1's part into LDS for the running sum
-#pragma unroll
-    for (int X = 0; X < IT; ++X)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * X + 4 * q4 + e;
-            float g1 = 0.f;
-            if (i < L) {
-                const int64_t o = lane_off + (int64_t)(16 * X + e) * rsk;
-                a.dq[o] += dq[X][e];
-                a.dk[o] += dk[X][e];
-                g1 = a.dg[o];
-            }
-            sDG[i * LDG + c] = g1 + dG[X][e];
-        }
     __syncthreads();
     if (tid < DK) {
         float cum = 0.f;
@@ -1075,9 +1048,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     const dim3 gc((unsigned)(a.n_seqs * a.H), (unsigned)(DV / 16), 2);
     hipLaunchKernelGGL((bwd_state_kernel<C, DK, DV>), gc, dim3(64 * P::NW), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_grad1_kernel<Tin, C, DK, DV>), gs, dim3(512), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_grad2_kernel<Tin, C, DK, DV>), gs, dim3(DK * 4), 0, stream, a);
+    hipLaunchKernelGGL((bwd_grad_kernel<Tin, C, DK, DV>), gs, dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 

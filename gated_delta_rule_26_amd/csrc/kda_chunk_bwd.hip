@@ -100,9 +100,9 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // 1. prep
 // ------------------------------------------------------------------------------------------
 template <typename Tin, int C, int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
     using R = BRec<C, DK, DV>;
-    constexpr int NT = 256;
+    constexpr int NT = 512;
     constexpr int DX = DK > DV ? DK : DV;
     constexpr int LDK = DK + 4, LDX = DX + 4, LDA = C + 4;
     __shared__ __align__(16) float sK[C * LDK];
@@ -1042,7 +1042,7 @@ template <typename Tin, int C, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     using P = StatePass<C, DK, DV>;
     const dim3 gs((unsigned)a.nslots, (unsigned)a.H);
-    hipLaunchKernelGGL((bwd_prep_kernel<Tin, C, DK, DV>), gs, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_prep_kernel<Tin, C, DK, DV>), gs, dim3(512), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 gc((unsigned)(a.n_seqs * a.H), (unsigned)(DV / 16), 2);

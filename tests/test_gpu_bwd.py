@@ -168,3 +168,15 @@ def test_empty_sequence_hands_back_the_state_gradient():
     torch.cuda.synchronize()
     assert np.array_equal(got[5].cpu().numpy(), dsT)
     assert all(t.numel() == 0 for t in got[:5])
+
+
+def test_bf16_long_sequence_with_states():
+    """One 16K-token sequence (256 chunks per chain: the state passes' long recurrences),
+    an initial state and a final-state gradient, two heads."""
+    T, H = 16384, 2
+    x = random_inputs(620, T, H, 128, "bf16")
+    s0 = random_states(621, 1, H, 128)
+    do, dsT = upstream(622, [T], H, 128, 128)
+    note("bwd bf16 T=16384")
+    got, ref = run_case(x, "bf16", [T], chunk=64, s0=s0, dsT=dsT, do=do)
+    check(got, ref, TOL_BF16)

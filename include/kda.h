@@ -25,9 +25,11 @@
  *
  * Two entry points do the work; kda_recurrent_fwd runs several tokens per sequence in the
  * decode kernel's way; two fused variants add the KDA layer's steps on either side of the
- * core (kda_chunk_fwd_fused, kda_decode_step_fused); and two more run the layer's short
- * convolution with its conv state (kda_short_conv_fwd, kda_short_conv_update, at the end of
- * this file):
+ * core (kda_chunk_fwd_fused, kda_decode_step_fused); two more run the layer's short
+ * convolution with its conv state (kda_short_conv_fwd, kda_short_conv_update); kda_chunk_bwd
+ * is the backward pass of kda_chunk_fwd (training); and two measurement probes report the
+ * device's practical copy and matrix-core peaks (kda_probe_copy, kda_probe_mfma_f16, at the
+ * end of this file):
  *   kda_chunk_fwd    prefill: the chunkwise-parallel form of the recurrence ([KV-cache page]
  *                    section 3: chunk_size 64; section 6: chunked parallel form with a WY
  *                    representation), over fixed-length batches or packed variable-length
@@ -41,10 +43,12 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Pointers. Every tensor pointer is a DEVICE pointer (HIP device memory) owned by the
- *   caller; the library allocates nothing and keeps no per-call state. Tensors are dense and
+ *   caller; the library allocates nothing and keeps no per-call state (scratch space, where
+ *   a call needs it, is the caller's workspace argument). Tensors are dense and
  *   contiguous with the last dimension innermost ("... h d" layout), and 16-byte aligned.
  * - Dtypes. q, k, v are KDA_F32 or KDA_BF16 (in_dtype); g (log-decay, <= 0), beta, states
- *   and o are float32 (out_dtype must be KDA_F32).
+ *   and o are float32 (out_dtype must be KDA_F32, except after the fused output norm); the
+ *   backward pass's gradients are float32.
  * - Streams. `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work on
  *   it and never synchronise the host. Calls on different streams are independent.
  * - Errors. Arguments are validated on the host before any HIP call: on an error nothing is

@@ -1536,7 +1536,7 @@ bool chunk_fwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv
     if (Dk != Dv) return false;
     if (in_dtype == 1) return chunk == 64 && Dk == 128;
     if (in_dtype == 0)
-        return (chunk == 16 && Dk == 16) || (chunk == 64 && (Dk == 32 || Dk == 64));
+        return (chunk == 16 && (Dk == 16 || Dk == 32)) || (chunk == 64 && (Dk == 32 || Dk == 64));
     return false;
 }
 
@@ -1591,7 +1591,9 @@ hipError_t launch_chunk_fwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t
                           : launch_t<bf16_t, _Float16, 64, 128, 128, 8, true, false>(a, stream);
         return launch_t<bf16_t, _Float16, 64, 128, 128, 8, false, false>(a, stream);
     }
-    if (chunk == 16) return launch_t<float, float, 16, 16, 16, 4, false, false>(a, stream);
+    if (chunk == 16)
+        return Dk == 16 ? launch_t<float, float, 16, 16, 16, 4, false, false>(a, stream)
+                        : launch_t<float, float, 16, 32, 32, 4, false, false>(a, stream);
     if (Dk == 32) return launch_t<float, float, 64, 32, 32, 4, false, false>(a, stream);
     return launch_t<float, float, 64, 64, 64, 4, false, false>(a, stream);
 }

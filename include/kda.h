@@ -137,8 +137,10 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk
  *                         by powers of two into fp16's range), float32 accumulation and
  *                         state; exact for any finite g <= 0 (chunks whose 16-token decay
  *                         falls below e^-12 sum their diagonal blocks pair by pair)
- *   (KDA_F32, 16, 16), (KDA_F32, 64, 32), (KDA_F32, 64, 64)
- *                         float32 matrix-core path (reference-precision instantiations)
+ *   (KDA_F32, 16, 16), (KDA_F32, 16, 32), (KDA_F32, 64, 32), (KDA_F32, 64, 64)
+ *                         float32 matrix-core path (reference-precision instantiations;
+ *                         D = 32 runs at both chunk sizes, which give the same result up
+ *                         to rounding)
  * Other combinations return KDA_ERR_UNSUPPORTED.
  */
 kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
@@ -276,7 +278,9 @@ typedef enum kda_activation { KDA_ACT_NONE = 0, KDA_ACT_SILU = 1 } kda_activatio
  *                initial_state is NULL (the gradient at a zero initial state)
  *   workspace    device buffer of at least kda_chunk_bwd_workspace_bytes(...) bytes (required);
  *                it holds per-(chunk, head) intermediates and is overwritten
- * All arithmetic is float32. Supported: as kda_chunk_fwd. Output buffers must not overlap the
+ * All arithmetic is float32. Compiled instantiations (in_dtype, chunk, Dk = Dv): (KDA_BF16, 64,
+ * 128), (KDA_F32, 64, 128) and (KDA_F32, 16, 16); others return KDA_ERR_UNSUPPORTED (the
+ * forward need not have an instantiation of its own at the same sizes). Output buffers must not overlap the
  * inputs or each other. Errors as kda_chunk_fwd (KDA_ERR_WORKSPACE_TOO_SMALL for a short
  * workspace); nothing is launched and no output is written on an error.
  */

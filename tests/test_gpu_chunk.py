@@ -44,7 +44,7 @@ def test_tiny_f32_workload():
     assert_close(S, S_ref, TOL_F32, "final state")
 
 
-@pytest.mark.parametrize("D,C", [(16, 16), (32, 64), (64, 64)])
+@pytest.mark.parametrize("D,C", [(16, 16), (32, 16), (32, 64), (64, 64)])
 @pytest.mark.parametrize("T", [1, 15, 50, 64, 65, 200, 333])
 def test_f32_ragged_lengths_with_state(D, C, T):
     H = 3
@@ -57,7 +57,7 @@ def test_f32_ragged_lengths_with_state(D, C, T):
     assert_close(S, S_ref, TOL_F32, "final state")
 
 
-@pytest.mark.parametrize("D,C", [(16, 16), (32, 64)])
+@pytest.mark.parametrize("D,C", [(16, 16), (32, 16), (32, 64)])
 def test_f32_batched_sequences(D, C):
     B, T, H = 3, 150, 2
     x = random_inputs(110 + D, B * T, H, D, "f32")
@@ -69,7 +69,7 @@ def test_f32_batched_sequences(D, C):
     assert_close(S, S_ref, TOL_F32, "final state")
 
 
-@pytest.mark.parametrize("D,C", [(16, 16), (32, 64), (64, 64)])
+@pytest.mark.parametrize("D,C", [(16, 16), (32, 16), (32, 64), (64, 64)])
 def test_f32_packed_with_empty_sequences(D, C):
     lens = [0, 70, 1, 128, 5, 0, 300]
     cu = np.concatenate([[0], np.cumsum(lens)])
@@ -368,3 +368,23 @@ def test_full_write_with_query_on_key_overwrites(stored, D, C):
     assert_close(S, S_ref, tol, "final state")
     if stored == "f32":  # unit keys to float32 rounding: o_t = v_t
         np.testing.assert_allclose(o_ref, f64(x["v"]), rtol=0, atol=1e-5 * np.sqrt(np.mean(o_ref ** 2)))
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_chunk_size_invariance(split):
+    """The chunk size changes only the rounding: chunks of 16 and of 64 tokens on the same
+    inputs (float32, D = 32, a ragged 333-token sequence with an initial state) each match
+    the oracle within the float32 bound, and each other within twice it."""
+    T, H, D = 333, 2, 32
+    x = random_inputs(700, T, H, D, "f32")
+    s0 = random_states(701, 1, H, D)
+    note(f"chunk-size invariance split={split}")
+    o16, S16 = gpu_chunk(x, "f32", chunk=16, s0=s0, split=split)
+    o64, S64 = gpu_chunk(x, "f32", chunk=64, s0=s0, split=split)
+    o_ref, S_ref = run_oracle(x, "f32", initial_state=s0)
+    assert_close(o16, o_ref, TOL_F32, "o, chunk 16")
+    assert_close(o64, o_ref, TOL_F32, "o, chunk 64")
+    assert_close(S16, S_ref, TOL_F32, "final state, chunk 16")
+    assert_close(S64, S_ref, TOL_F32, "final state, chunk 64")
+    assert_close(o16, o64, 2 * TOL_F32, "o, chunk 16 against chunk 64")
+    assert_close(S16, S64, 2 * TOL_F32, "final state, chunk 16 against chunk 64")

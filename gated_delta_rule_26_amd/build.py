@@ -12,6 +12,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_bwd.hip", "kda_decode.hip", "kda_conv.hip", "kda_probe.hip"]
 ARCH = "gfx950"
+# Per-source extra flags. The matrix-core probe's loop-carried accumulators are kept in the
+# VGPR form of the instruction: in the AGPR form the register allocator rotates the 4-float
+# accumulators of the 16x16x32 products through copies in every iteration, and the probe
+# would time the copies instead of the matrix cores.
+EXTRA = {"kda_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def lib_path() -> str:
@@ -35,7 +40,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     def compile_one(src):
         obj = os.path.join(objdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc, *_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *_flags(), *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

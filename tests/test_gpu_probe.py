@@ -1,6 +1,8 @@
 """The measurement probes on the GPU: the copy reproduces its input bit for bit; the fp16
-matrix-core loop runs and leaves finite accumulators."""
+matrix-core loop gives the sums its fixed operands imply (every product of every iteration
+was done)."""
 
+import numpy as np
 import pytest
 
 import gated_delta_rule_26_amd as kda
@@ -19,12 +21,41 @@ def test_probe_copy_is_exact():
     assert torch.equal(src, dst)
 
 
+def probe_expected(shape, iters, blocks):
+    """What every thread of the probe writes: the sum of its accumulator elements after
+    `iters` products. Each lane's A fragment holds 8 fp16 values 1e-3 * (thread + e) and its
+    B fragment 1e-3 * (block + e), e = 0..7, so B does not depend on the column and every
+    column of D = A B is the same vector d[row] = sum over the k slices of A[row, k] b[k].
+    16x16x32: lane 16 s + i holds row i, k = 8 s + e of A; the lane's 4 accumulator elements
+    are rows 4 s .. 4 s + 3; 8 accumulators. 32x32x16: lane 32 s + i holds row i, k = 8 s + e;
+    its 16 elements are rows 8 u + 4 s + r (u, r = 0..3); 4 accumulators."""
+    f16 = lambda x: (np.float32(1e-3) * np.asarray(x, np.float32)).astype(np.float16).astype(np.float64)  # noqa: E731
+    e = np.arange(8)
+    out = np.zeros((blocks, 256))
+    rows, nk, nacc = (16, 4, 8) if shape == 0 else (32, 2, 4)
+    for blk in range(blocks):
+        bb = f16(blk + e)
+        for w in range(4):
+            d = np.zeros(rows)
+            for i in range(rows):
+                d[i] = sum(float(f16(64 * w + rows * s + i + e) @ bb) for s in range(nk))
+            for lane in range(64):
+                s_ = lane // rows
+                own = ([4 * s_ + r for r in range(4)] if shape == 0 else
+                       [8 * u + 4 * s_ + r for u in range(4) for r in range(4)])
+                out[blk, 64 * w + lane] = nacc * iters * d[own].sum()
+    return out.reshape(-1)
+
+
 @pytest.mark.parametrize("shape", [0, 1])
-def test_probe_mfma_runs(shape):
+def test_probe_mfma_result(shape):
     torch = torch_mod()
-    sink = torch.full((4 * 256,), float("nan"), device="cuda")
-    note(f"probe mfma shape {shape}, 4 blocks")
-    flops = kda.kda_probe_mfma_f16(10, 4, sink, shape=shape)
+    iters, blocks = 10, 4
+    sink = torch.full((blocks * 256,), float("nan"), device="cuda")
+    note(f"probe mfma shape {shape}, {blocks} blocks")
+    flops = kda.kda_probe_mfma_f16(iters, blocks, sink, shape=shape)
     torch.cuda.synchronize()
-    assert flops == 10 * 4 * 4 * 8 * 2 * 16 * 16 * 32
-    assert bool(torch.isfinite(sink).all())
+    assert flops == iters * blocks * 4 * 8 * 2 * 16 * 16 * 32
+    got = sink.cpu().numpy().astype(np.float64)
+    ref = probe_expected(shape, iters, blocks)
+    np.testing.assert_allclose(got, ref, rtol=1e-4)

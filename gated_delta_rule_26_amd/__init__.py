@@ -15,7 +15,7 @@ import os
 
 __all__ = ["KdaError", "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_fused",
            "kda_decode_step_fused", "kda_recurrent_fwd", "kda_short_conv_fwd", "kda_short_conv_update",
-           "kda_chunk_bwd", "chunk_fwd_workspace_bytes", "chunk_bwd_workspace_bytes", "load_library", "KDA_F32", "KDA_BF16"]
+           "kda_chunk_bwd", "check_cu_seqlens", "chunk_fwd_workspace_bytes", "chunk_bwd_workspace_bytes", "load_library", "KDA_F32", "KDA_BF16"]
 
 KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
@@ -23,6 +23,12 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
 
 _LIB = None
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+# Debugging aid: with KDA_CHECK_CU_SEQLENS=1 in the environment, every call that takes packed
+# offsets first checks them on the host (a copy that synchronises the stream). Without it the
+# offsets are a precondition: the kernels clamp them to [0, T], so malformed offsets give
+# wrong results but no access outside the caller's arrays.
+CHECK_CU_SEQLENS = os.environ.get("KDA_CHECK_CU_SEQLENS", "0") not in ("", "0")
 
 
 class _Fusion(ctypes.Structure):
@@ -135,6 +141,34 @@ def _req(t, name, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def check_cu_seqlens(cu_seqlens, T: int) -> None:
+    """Raise ValueError unless the packed offsets are valid for T tokens: int32, one
+    dimension, cu[0] = 0, nondecreasing, cu[-1] = T. Accepts a torch tensor (copied to the
+    host) or anything numpy can read."""
+    import numpy as np
+    try:
+        import torch
+        if isinstance(cu_seqlens, torch.Tensor):
+            if cu_seqlens.dtype != torch.int32:
+                raise ValueError(f"cu_seqlens must be int32, got {cu_seqlens.dtype}")
+            cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    except ImportError:
+        pass
+    cu = np.asarray(cu_seqlens)
+    if cu.ndim != 1 or cu.size < 1:
+        raise ValueError("cu_seqlens must be one-dimensional with N + 1 >= 1 entries")
+    if cu.dtype != np.int32:
+        raise ValueError(f"cu_seqlens must be int32, got {cu.dtype}")
+    if cu[0] != 0:
+        raise ValueError(f"cu_seqlens[0] must be 0, got {int(cu[0])}")
+    d = np.diff(cu.astype(np.int64))
+    if (d < 0).any():
+        i = int(np.argmax(d < 0))
+        raise ValueError(f"cu_seqlens must be nondecreasing: cu[{i}] = {int(cu[i])} > cu[{i + 1}] = {int(cu[i + 1])}")
+    if int(cu[-1]) != T:
+        raise ValueError(f"cu_seqlens[-1] must equal the token count {T}, got {int(cu[-1])}")
+
+
 def _prefill_layout(q, k, v, beta, cu_seqlens):
     """(B, T, N, H, Dk, Dv) of a prefill call, after checking q, k, v, beta, cu_seqlens."""
     import torch
@@ -157,6 +191,8 @@ def _prefill_layout(q, k, v, beta, cu_seqlens):
     Dv = v.shape[-1]
     if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or beta.shape != q.shape[:-1]:
         raise ValueError("inconsistent q/k/v/beta shapes")
+    if cu_seqlens is not None and CHECK_CU_SEQLENS:
+        check_cu_seqlens(cu_seqlens, T)
     return B, T, N, H, Dk, Dv
 
 
@@ -458,6 +494,8 @@ def kda_short_conv_fwd(x, weight, bias=None, *, initial_state=None, final_state=
         if x.dim() == 3 and x.shape[0] != 1:
             raise ValueError("cu_seqlens requires B == 1")
         B, T, N = 1, x.shape[-2], cu_seqlens.numel() - 1
+        if CHECK_CU_SEQLENS:
+            check_cu_seqlens(cu_seqlens, T)
     else:
         if x.dim() != 3:
             raise ValueError("x must be [B, T, C] without cu_seqlens")

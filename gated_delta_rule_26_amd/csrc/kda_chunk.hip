@@ -397,8 +397,9 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     const int n = a.order ? a.order[chain / H] : chain / H, h = chain % H;
     int64_t tok0, L;
     if (a.cu_seqlens) {
-        tok0 = a.cu_seqlens[n];
-        L = (int64_t)a.cu_seqlens[n + 1] - tok0;
+        int64_t end;
+        packed_range(a.cu_seqlens, n, a.seq_len, tok0, end);
+        L = end - tok0;
     } else {
         tok0 = (int64_t)n * a.seq_len;
         L = a.seq_len;

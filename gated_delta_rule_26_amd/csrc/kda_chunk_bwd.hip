@@ -56,8 +56,20 @@ template <int C, int DK, int DV> struct BRec {
     static constexpr int64_t FLOATS = (odH + DK * DV + 63) & ~int64_t(63);
 };
 
+// Token range [start, end) of sequence n (packed offsets clamped to [0, T]).
+__device__ __forceinline__ void seq_range(const BwdArgs &a, int n, int64_t &start, int64_t &end) {
+    if (a.cu_seqlens) {
+        packed_range(a.cu_seqlens, n, a.seq_len, start, end);
+    } else {
+        start = (int64_t)n * a.seq_len;
+        end = start + a.seq_len;
+    }
+}
+
 __device__ __forceinline__ int64_t seq_start(const BwdArgs &a, int n) {
-    return a.cu_seqlens ? (int64_t)a.cu_seqlens[n] : (int64_t)n * a.seq_len;
+    int64_t s, e;
+    seq_range(a, n, s, e);
+    return s;
 }
 
 template <int C> __device__ __forceinline__ int64_t slot_base(const BwdArgs &a, int n) {
@@ -73,7 +85,9 @@ template <int C> __device__ bool locate(const BwdArgs &a, int64_t s, int &n, int
         else hi = mid - 1;
     }
     n = lo;
-    const int64_t st = seq_start(a, n), len = seq_start(a, n + 1) - st;
+    int64_t st, en;
+    seq_range(a, n, st, en);
+    const int64_t len = en - st;
     const int64_t j = s - slot_base<C>(a, n);
     if (j < 0 || j * C >= len) return false;
     t0 = st + j * C;
@@ -366,7 +380,9 @@ __device__ __forceinline__ void fwd_state_pass(const BwdArgs &a, int chain, int 
     __shared__ f32x4 sPart[NW][IT][64];
     const int n = chain / a.H, h = chain % a.H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, q4 = lane >> 4;
-    const int64_t st = seq_start(a, n), len = seq_start(a, n + 1) - st;
+    int64_t st, en;
+    seq_range(a, n, st, en);
+    const int64_t len = en - st;
     const int nch = (int)((len + C - 1) / C);
     const int64_t base = slot_base<C>(a, n);
     const int col = 16 * vb + lr;
@@ -474,7 +490,9 @@ __device__ __forceinline__ void rev_state_pass(const BwdArgs &a, int chain, int 
     __shared__ f32x4 sPart[NW][IT][64];
     const int n = chain / a.H, h = chain % a.H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, q4 = lane >> 4;
-    const int64_t st = seq_start(a, n), len = seq_start(a, n + 1) - st;
+    int64_t st, en;
+    seq_range(a, n, st, en);
+    const int64_t len = en - st;
     const int nch = (int)((len + C - 1) / C);
     const int64_t base = slot_base<C>(a, n);
     const int col = 16 * vb + lr;

@@ -69,8 +69,7 @@ __device__ __forceinline__ void seq_of(const ConvArgs &a, int64_t t, int &n, int
             else hi = mid - 1;
         }
         n = lo;
-        start = a.cu_seqlens[n];
-        end = a.cu_seqlens[n + 1];
+        packed_range(a.cu_seqlens, n, a.tokens, start, end);
     } else {
         n = (int)(t / a.seq_len);
         start = (int64_t)n * a.seq_len;
@@ -83,7 +82,7 @@ template <typename T>
 __device__ __forceinline__ void hist_row(const ConvArgs &a, int n, int64_t start, int64_t p, int c0, float (&v)[8]) {
     if (p >= 0) {
         Vec8<T>::load(static_cast<const T *>(a.x) + (start + p) * a.C + c0, v);
-    } else if (a.s0) {
+    } else if (a.s0 && p >= -(kConvW - 1)) {  // (p is below that only for invalid offsets)
         Vec8<T>::load(static_cast<const T *>(a.s0) + ((int64_t)n * (kConvW - 1) + (kConvW - 1) + p) * a.C + c0, v);
     } else {
 #pragma unroll
@@ -150,8 +149,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_state_kernel(ConvArgs a) {
     if (c0 >= a.C) return;
     int64_t start, end;
     if (a.cu_seqlens) {
-        start = a.cu_seqlens[n];
-        end = a.cu_seqlens[n + 1];
+        packed_range(a.cu_seqlens, n, a.tokens, start, end);
     } else {
         start = (int64_t)n * a.seq_len;
         end = start + a.seq_len;

@@ -46,6 +46,19 @@ __device__ __forceinline__ float softplus_f(float z) {
 __device__ __forceinline__ float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 // 1/sqrt(s) for s > 0, else 0 (a zero vector stays zero)
 __device__ __forceinline__ float rsqrt_or_zero(float s) { return s > 0.f ? __builtin_amdgcn_rsqf(s) : 0.f; }
+
+// Token range [start, end) of packed sequence n, from the device-resident offsets cu[n] and
+// cu[n + 1] clamped to [0, T] with end >= start. Valid offsets (cu[0] = 0, nondecreasing,
+// cu[N] = T) pass unchanged; invalid ones give wrong results but never an access outside
+// the caller's [T, ...] arrays.
+__device__ __forceinline__ void packed_range(const int32_t *cu, int n, int64_t T, int64_t &start,
+                                             int64_t &end) {
+    int64_t s = cu[n], e = cu[n + 1];
+    s = s < 0 ? 0 : (s > T ? T : s);
+    e = e < s ? s : (e > T ? T : e);
+    start = s;
+    end = e;
+}
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));  // round to nearest even
 }

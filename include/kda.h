@@ -56,7 +56,10 @@
  *   the last error on the calling thread is available from kda_last_error().
  * - Not checked (preconditions): the contents of device arrays (cu_seqlens values, NaN or
  *   Inf inputs, which propagate), and overlaps between outputs and inputs other than the
- *   allowed final_state == initial_state aliasing.
+ *   allowed final_state == initial_state aliasing. The kernels clamp packed offsets: sequence
+ *   n covers [s, e) with s = cu[n] and e = cu[n+1] clamped to [0, T] and e >= s, so offsets
+ *   that break the precondition give the result of those clamped ranges (wrong, and racy
+ *   where two ranges overlap) but never an access outside the caller's arrays.
  * - Supported sizes: see kda_chunk_fwd and kda_decode_step.
  */
 #ifndef KDA_H

@@ -483,31 +483,43 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         int tg, cg;
         vo[vv] = vjob(vv, tg, cg) ? 4 * tg * vrow + h * DV + 4 * cg : C * vrow;
     }
-    auto prefetch = [&](int64_t t0, int Lc) {
+    // part 1: v, g and beta (consumed by P0 and the extreme-chunk path); part 2: k and q
+    // (consumed up to P1); 0: both
+    auto prefetch = [&](int64_t t0, int Lc, int part) {
         const rsrc_t rq = make_rsrc(qg + t0 * krow, (uint32_t)(Lc * krow * ESZ));
         const rsrc_t rk = make_rsrc(kg + t0 * krow, (uint32_t)(Lc * krow * ESZ));
         const rsrc_t rg = FIN ? make_rsrc(static_cast<const Tin *>(a.f.gx) + t0 * krow, (uint32_t)(Lc * krow * ESZ))
                               : make_rsrc(a.g + t0 * krow, (uint32_t)(Lc * krow * 4));
         const rsrc_t rv = make_rsrc(vg + t0 * vrow, (uint32_t)(Lc * vrow * ESZ));
         const rsrc_t rb = make_rsrc(a.beta + t0 * H, (uint32_t)(Lc * H * 4));
+        if (part != 2) {
 #pragma unroll
-        for (int vv = 0; vv < Sh::VPT; ++vv)
+            for (int vv = 0; vv < Sh::VPT; ++vv)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pv[vv][r] = R4::load(rv, vo[vv] * ESZ, r * vrow * ESZ);
+                for (int r = 0; r < 4; ++r) pv[vv][r] = R4::load(rv, vo[vv] * ESZ, r * vrow * ESZ);
 #pragma unroll
-        for (int jj = 0; jj < Sh::JPT; ++jj) {
+            for (int jj = 0; jj < Sh::JPT; ++jj) {
 #pragma unroll
-            for (int ii = 0; ii < 8; ++ii) {
-                if constexpr (FIN)
-                    pg[jj][ii] = RW::load(rg, ko[jj] * ESZ, ii * krow * ESZ);
-                else
-                    pg[jj][ii] = Raw2<float>::load(rg, ko[jj] * 4, ii * krow * 4);
-                pk[jj][ii] = RW::load(rk, ko[jj] * ESZ, ii * krow * ESZ);
-                pq[jj][ii] = RW::load(rq, ko[jj] * ESZ, ii * krow * ESZ);
+                for (int ii = 0; ii < 8; ++ii) {
+                    if constexpr (FIN)
+                        pg[jj][ii] = RW::load(rg, ko[jj] * ESZ, ii * krow * ESZ);
+                    else
+                        pg[jj][ii] = Raw2<float>::load(rg, ko[jj] * 4, ii * krow * 4);
+                }
+            }
+            pbeta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  rb, (tid < C ? tid * H + h : C * H) * 4, 0, 0));
+        }
+        if (part != 1) {
+#pragma unroll
+            for (int jj = 0; jj < Sh::JPT; ++jj) {
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) {
+                    pk[jj][ii] = RW::load(rk, ko[jj] * ESZ, ii * krow * ESZ);
+                    pq[jj][ii] = RW::load(rq, ko[jj] * ESZ, ii * krow * ESZ);
+                }
             }
         }
-        pbeta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                              rb, (tid < C ? tid * H + h : C * H) * 4, 0, 0));
     };
 
     const int64_t nchunks = (L + C - 1) / C;
@@ -537,7 +549,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         if (tid < DK / 4)
             *reinterpret_cast<f32x4 *>(rp + Rc::oG + 16 * tid) = *reinterpret_cast<const f32x4 *>(gC + 4 * tid);
     };
-    if (nchunks > 0) prefetch(tok0, (int)(L < C ? L : C));
+    if (nchunks > 0) prefetch(tok0, (int)(L < C ? L : C), 0);
 
     for (int64_t ci = 0; ci < nchunks; ++ci) {
         const int64_t t0 = tok0 + ci * C;
@@ -780,6 +792,13 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             __syncthreads();  // the staging area is overwritten by the operands below
         }
 
+        // the next chunk's v, g and beta: their registers are free from here on, and the
+        // loads overlap P1
+        if (ci + 1 < nchunks) {
+            const int64_t rem = L - (ci + 1) * C;
+            prefetch(t0 + C, (int)(rem < C ? rem : C), 1);
+        }
+
         // ---- P1: matrix-core operands
         // fp16, ordinary chunks: rows of block I carry a per-channel power of two 2^e_I near
         // D_I^(-1/2) and the right operands paired with block I carry 2^-e_I (exact: products
@@ -877,10 +896,10 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             }
         }
 
-        // the next chunk's inputs are in flight from here on
+        // the next chunk's k and q (read by P1 up to here): all its inputs are in flight
         if (ci + 1 < nchunks) {
             const int64_t rem = L - (ci + 1) * C;
-            prefetch(t0 + C, (int)(rem < C ? rem : C));
+            prefetch(t0 + C, (int)(rem < C ? rem : C), 2);
         }
         __syncthreads();
 

@@ -555,7 +555,6 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         const int64_t t0 = tok0 + ci * C;
         const int Lc = (int)((L - ci * C) < C ? (L - ci * C) : C);
         __syncthreads();  // the previous chunk's readers of LDS are done
-        if (store && ci > 0) record_ops(ci - 1);
 
         // ---- P0: gates -> within-block decay products (prefix incl., suffix excl.)
         float al0[Sh::JPT][8], al1[Sh::JPT][8], sf0[Sh::JPT][8], sf1[Sh::JPT][8];
@@ -1030,7 +1029,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         __syncthreads();
 
         // ---- split segments after the first: record U~ of this chunk (the LDS operands are
-        // recorded at the top of the next iteration, where fewer registers are live)
+        // recorded after P5, where fewer registers are live; waves done with P5 copy while
+        // the others finish)
         if (store && owns) {
             using Rc = Record<OP, C, DK, DV>;
             uint8_t *const rp = a.rec + (((int64_t)seg * chains + chain) * a.rec_chunks + ci) * Rc::BYTES;
@@ -1109,12 +1109,9 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 onorm_rows<C, DV, NW>(a, Ob, sgain, zr, t0, Lc, h);
             }
         }
+        if (store) record_ops(ci);
     }
 
-    if (store && nchunks > 0) {
-        __syncthreads();
-        record_ops(nchunks - 1);
-    }
 
     float *dst = nullptr;
     if (STORE)  // split: segment p's final state (from the initial state for p = 0, else zero)

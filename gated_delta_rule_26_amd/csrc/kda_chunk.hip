@@ -367,6 +367,13 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     OP *const Qg = reinterpret_cast<OP *>(smem + Sh::oQg);
     OP *const KdT = reinterpret_cast<OP *>(smem + Sh::oKdT);
     OP *const Yt = reinterpret_cast<OP *>(smem + Sh::oYt);
+    // V^T row r holds 4-token groups in XOR-swizzled order (group tg at tg ^ ((r >> 3) & m)):
+    // the staging stores of 16 lanes, rows 4 apart, then fall in distinct LDS banks, and so
+    // do the 16 rows that one lane group of the reader spans
+    auto yt_col = [](int r, int tg) {
+        constexpr int m = C / 4 - 1 < 7 ? C / 4 - 1 : 7;
+        return 4 * (tg ^ ((r >> 3) & m));
+    };
     float *const Dd = reinterpret_cast<float *>(smem + Sh::oDd);
     float *const gC = reinterpret_cast<float *>(smem + Sh::oGc);
     float *const sbeta = reinterpret_cast<float *>(smem + Sh::oBeta);
@@ -659,7 +666,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 typedef typename MM::frag f4;
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    *reinterpret_cast<f4 *>(Yt + (4 * cg + c) * LDC + 4 * tg) =
+                    *reinterpret_cast<f4 *>(Yt + (4 * cg + c) * LDC + yt_col(4 * cg + c, tg)) =
                         MM::from_f32(f32x4{vr[0][c], vr[1][c], vr[2][c], vr[3][c]});
             }
         }
@@ -1023,7 +1030,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             for (int I = 0; I < NB; ++I) Ur[j][I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int I = 0; I < NB; ++I)
-                Ur[j][I] = subst_row(Ur[j], I, MM::to_f32(MM::load(Yt + (16 * cv + lr) * LDC + 16 * I + 4 * q4)) *
+                Ur[j][I] = subst_row(Ur[j], I, MM::to_f32(MM::load(Yt + (16 * cv + lr) * LDC + yt_col(16 * cv + lr, 4 * I + q4))) *
                                                    *reinterpret_cast<const f32x4 *>(sbeta + 16 * I + 4 * q4));
         }
         __syncthreads();

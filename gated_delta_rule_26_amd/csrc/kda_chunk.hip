@@ -530,6 +530,11 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     };
 
     const int64_t nchunks = (L + C - 1) / C;
+    // Without the fused input steps, the next chunk's v, g and beta loads go out before P1 and
+    // each chunk's operands are recorded after its own state pass; with them (a heavier P0),
+    // all loads go out after P1 and the records are copied at the top of the next chunk, which
+    // measured faster there.
+    constexpr bool kEarlyLoads = !FIN, kLateRecords = !FIN;
     // record the LDS operands (W, Qg, Kd^T, M, gC) of chunk cr of a split segment
     // (each thread copies 16-byte pieces tid, tid + NT, ...: one base offset per row width)
     auto record_ops = [&](int64_t cr) {
@@ -562,6 +567,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         const int64_t t0 = tok0 + ci * C;
         const int Lc = (int)((L - ci * C) < C ? (L - ci * C) : C);
         __syncthreads();  // the previous chunk's readers of LDS are done
+        if (!kLateRecords && store && ci > 0) record_ops(ci - 1);
 
         // ---- P0: gates -> within-block decay products (prefix incl., suffix excl.)
         float al0[Sh::JPT][8], al1[Sh::JPT][8], sf0[Sh::JPT][8], sf1[Sh::JPT][8];
@@ -798,9 +804,9 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             __syncthreads();  // the staging area is overwritten by the operands below
         }
 
-        // the next chunk's v, g and beta: their registers are free from here on, and the
-        // loads overlap P1
-        if (ci + 1 < nchunks) {
+        // the next chunk's v, g and beta (without the fused input steps): their registers are
+        // free from here on, and the loads overlap P1
+        if (kEarlyLoads && ci + 1 < nchunks) {
             const int64_t rem = L - (ci + 1) * C;
             prefetch(t0 + C, (int)(rem < C ? rem : C), 1);
         }
@@ -905,7 +911,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         // the next chunk's k and q (read by P1 up to here): all its inputs are in flight
         if (ci + 1 < nchunks) {
             const int64_t rem = L - (ci + 1) * C;
-            prefetch(t0 + C, (int)(rem < C ? rem : C), 2);
+            prefetch(t0 + C, (int)(rem < C ? rem : C), kEarlyLoads ? 2 : 0);
         }
         __syncthreads();
 
@@ -1036,8 +1042,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         __syncthreads();
 
         // ---- split segments after the first: record U~ of this chunk (the LDS operands are
-        // recorded after P5, where fewer registers are live; waves done with P5 copy while
-        // the others finish)
+        // recorded after P5, where fewer registers are live and waves done with P5 copy while
+        // the others finish; with the fused input steps, at the top of the next chunk)
         if (store && owns) {
             using Rc = Record<OP, C, DK, DV>;
             uint8_t *const rp = a.rec + (((int64_t)seg * chains + chain) * a.rec_chunks + ci) * Rc::BYTES;
@@ -1116,7 +1122,12 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 onorm_rows<C, DV, NW>(a, Ob, sgain, zr, t0, Lc, h);
             }
         }
-        if (store) record_ops(ci);
+        if (kLateRecords && store) record_ops(ci);
+    }
+
+    if (!kLateRecords && store && nchunks > 0) {
+        __syncthreads();
+        record_ops(nchunks - 1);
     }
 
 

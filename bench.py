@@ -449,8 +449,10 @@ def cpu_baseline(x: dict, sample_tokens: int) -> dict:
     oracle.kda_fwd(*args, threads=threads)
     dt = time.perf_counter() - t0
     return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"prefill_128k_h32, first {sample_tokens} tokens x {x['q'].shape[1]} heads "
-                      f"(float64 recurrence, {dt:.1f} s wall)"}
+            "sample": (f"prefill_128k_h32, " +
+                       ("all" if sample_tokens == x["q"].shape[0] else "first") +
+                       f" {sample_tokens} tokens x {x['q'].shape[1]} heads "
+                       f"(float64 recurrence, {dt:.1f} s wall)")}
 
 
 def main():
@@ -459,7 +461,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
     ap.add_argument("--decode-seqs", type=int, default=256)
     ap.add_argument("--counter-pass", action="store_true")
     ap.add_argument("--no-extra", action="store_true",

@@ -69,7 +69,7 @@ template <typename OP, int TSZ, int C, int DK, int DV, int NW> struct ChunkShape
     static constexpr int WPW = KT >= NW ? KT / NW : 1;      // W column tiles per wave
     static constexpr int NOFFA = NB * (NB - 1) / 2;         // off-diagonal blocks of A
     static constexpr int NOFF = 2 * NOFFA;                  // ... and of M
-    static constexpr int OFFW = NW > NB ? NW - NB : NW;     // waves doing off-diagonal jobs
+    static constexpr int OFFW = NW;                         // waves doing off-diagonal jobs
     static constexpr int OPW = NOFF > 0 ? (NOFF + OFFW - 1) / OFFW : 1;
     static constexpr int NVJ = (C / 4) * (DV / 4);          // 4x4 value-tile jobs per chunk
     static constexpr int VPT = (NVJ + NT - 1) / NT;           // value-tile jobs per thread
@@ -957,7 +957,9 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             }
         }
         f32x4 offv[Sh::OPW];
-        const int ow = NW > NB ? wave - NB : wave;  // index among the off-diagonal waves
+        // off-diagonal jobs x = ow + OFFW j, dealt from the last wave down: the waves that also
+        // invert a diagonal block (wave < NB) get the fewest
+        const int ow = NW - 1 - wave;
 #pragma unroll
         for (int j = 0; j < Sh::OPW; ++j) {
             offv[j] = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -113,7 +113,8 @@ template <typename OP, int TSZ, int C, int DK, int DV, int NW> struct ChunkShape
     // fused q/k normalisation: per-token partial sums of squares [k, q][channel half][token]
     static constexpr int oNrm = oBeta + align16(C * 4);
     static constexpr int oGain = oNrm + align16(4 * C * 4);  // fused output norm gain [DV]
-    static constexpr int BYTES = oGain + align16(DV * 4);
+    static constexpr int oFlag = oGain + align16(DV * 4);   // per-wave extreme-chunk votes [NW]
+    static constexpr int BYTES = oFlag + align16(NW * 4);
 
     static_assert(C % 16 == 0 && C >= 16 && C <= 64, "chunk must be 16, 32, 48 or 64");
     static_assert(DK % 16 == 0 && DV % 16 == 0, "head dims must be multiples of 16");
@@ -447,6 +448,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     if (STORE && seg > 0) sinit = nullptr;
     float *const Ob = reinterpret_cast<float *>(smem + Sh::P_REUSE);  // fused output staging
     float *const sgain = reinterpret_cast<float *>(smem + Sh::oGain);
+    int *const sflag = reinterpret_cast<int *>(smem + Sh::oFlag);
     if (FOUT && tid < DV) sgain[tid] = a.f.ow[tid];  // read after the loop's first barrier
     f32x4 S[CPW][KT];
 #pragma unroll
@@ -676,7 +678,16 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                         MM::from_f32(f32x4{vr[0][c], vr[1][c], vr[2][c], vr[3][c]});
             }
         }
-        const bool extreme = __syncthreads_or(ext_local);
+        // work-group OR of the votes with one barrier: a ballot per wave into its own slot
+        // (rewritten every chunk; the previous chunk's reads are behind the loop's first
+        // barrier), then every thread ORs the slots
+        const bool wave_ext = __ballot(ext_local) != 0ull;  // every lane's vote (all lanes active)
+        if (lane == 0) sflag[wave] = wave_ext;
+        __syncthreads();
+        int any_ext = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) any_ext |= sflag[w];
+        const bool extreme = any_ext != 0;
         // fused normalisation: 1/||.|| of token t from the two channel halves' sums
         auto tok_rnorm = [&](int kind, int t) { return rsqrt_or_zero(nrm[2 * kind * C + t] + nrm[(2 * kind + 1) * C + t]); };
         // this thread's 8 tokens' factors, read where P1 consumes them (short live range)

@@ -208,6 +208,23 @@ def test_bf16_constant_channel_decay(g_c):
     assert_close(S, S_ref, TOL_BF16, "final state")
 
 
+@pytest.mark.parametrize("where", ["block0", "block2"])
+def test_bf16_single_channel_extreme(where):
+    """One channel alone (77, odd, owned by neither the first lane nor the first wave) decays
+    by e^-5 per token for 16 tokens inside one chunk: a single thread's vote must switch the
+    whole chunk to the pair-by-pair diagonal path."""
+    T, H, D = 256, 2, 128
+    x = random_inputs(178, T, H, D, "bf16")
+    t0 = 64 + (0 if where == "block0" else 32)
+    x["g"][t0:t0 + 16, :, 77] = np.float32(-5.0)
+    s0 = random_states(179, 1, H, D)
+    note(f"bf16 single channel extreme {where}")
+    o, S = gpu_chunk(x, "bf16", chunk=64, s0=s0, scale=D ** -0.5)
+    o_ref, S_ref = run_oracle(x, "bf16", scale=D ** -0.5, initial_state=s0)
+    assert_close(o, o_ref, TOL_BF16, "o")
+    assert_close(S, S_ref, TOL_BF16, "final state")
+
+
 def test_bf16_prefill_then_decode_equals_prefill():
     torch = torch_mod()
     P, steps, H, D = 200, 24, 2, 128

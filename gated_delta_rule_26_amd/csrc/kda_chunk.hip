@@ -20,8 +20,9 @@
 //   accumulator registers. The state pass (U, O, S update) runs entirely from registers:
 //   an accumulator tile is directly a matrix-core B fragment, so the only shared operands
 //   are the per-chunk A-side matrices in LDS and the state pass has no barrier.
-// * The next chunk's q, k, g and beta are loaded into registers while the current chunk
-//   computes (all loads unconditional; rows past the sequence end are clamped and masked).
+// * The next chunk's q, k, v, g and beta are loaded into registers while the current chunk
+//   computes: v, g and beta once P0 has consumed the current ones, k and q after P1. Rows
+//   past the sequence end fall outside the buffer bounds and read as zero.
 // * Decay factors never overflow: inside a chunk every e^{G_i - G_j} is split at a
 //   16-token block boundary, so each operand carries a factor <= 1 or, inside a diagonal
 //   16x16 block, at most the inverse decay D^-1 of the block's 16 tokens. One exp per

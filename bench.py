@@ -414,11 +414,12 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
     copy_gbs = (2 << 30) / (ms * 1e-3) / 1e9
     blocks, iters = 2048, 2000
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
-    tf = {}
-    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
-        flops = kda.kda_probe_mfma_f16(iters, blocks, sink, shape=shape)
-        ms = timed(lambda: kda.kda_probe_mfma_f16(iters, blocks, sink, shape=shape), 5)
-        tf[name] = flops / (ms * 1e-3) / 1e12
+    tf, tb = {}, {}
+    for probe, rates in ((kda.kda_probe_mfma_f16, tf), (kda.kda_probe_mfma_bf16, tb)):
+        for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+            flops = probe(iters, blocks, sink, shape=shape)
+            ms = timed(lambda: probe(iters, blocks, sink, shape=shape), 5)
+            rates[name] = flops / (ms * 1e-3) / 1e12
     best = max(tf.values())
     best_copy = max(copy_gbs, out["copy_reference"]["gbs"])
     out["measured_peaks"] = {
@@ -426,10 +427,11 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
         "hbm_gbs_by_copy": {"kda_probe_copy": round(copy_gbs, 1), "torch copy_": out["copy_reference"]["gbs"]},
         "mfma_f16_tflops": round(best, 1),
         "mfma_f16_tflops_by_instruction": {k: round(v, 1) for k, v in tf.items()},
+        "mfma_bf16_tflops_by_instruction": {k: round(v, 1) for k, v in tb.items()},
         "mfma_frac_of_published": round(best / MFMA_F16_PEAK_TFLOPS, 4),
-        "what": "the better of two 1 GiB copies (read + write); kda_probe_mfma_f16, 2048 x 256 threads"}
+        "what": "the better of two 1 GiB copies (read + write); kda_probe_mfma_f16 / _bf16, 2048 x 256 threads"}
     del src, dst, sink
-    log("measured the copy and fp16 matrix-core peaks")
+    log("measured the copy and fp16 / bf16 matrix-core peaks")
     return out
 
 
@@ -448,11 +450,27 @@ def cpu_baseline(x: dict, sample_tokens: int) -> dict:
     t0 = time.perf_counter()
     oracle.kda_fwd(*args, threads=threads)
     dt = time.perf_counter() - t0
+    # one thread on a shorter prefix (the rate per token is the same: every token costs the
+    # same recurrence step)
+    t1 = min(sample_tokens, 4096)
+    s1 = slice(0, t1)
+    t0 = time.perf_counter()
+    oracle.kda_fwd(*(a[s1] for a in args), threads=1)
+    dt1 = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"prefill_128k_h32, " +
                        ("all" if sample_tokens == x["q"].shape[0] else "first") +
                        f" {sample_tokens} tokens x {x['q'].shape[1]} heads "
-                       f"(float64 recurrence, {dt:.1f} s wall)")}
+                       f"(float64 recurrence, {dt:.1f} s wall)"),
+            "single_thread": {"value": t1 / dt1, "unit": "tokens/s",
+                              "sample": f"first {t1} tokens x {x['q'].shape[1]} heads ({dt1:.1f} s wall)"},
+            "host": {"nproc": os.cpu_count(), "cpu": model}}
 
 
 def main():

@@ -82,6 +82,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_probe_copy.argtypes = [vp, vp, sz, vp]
     lib.kda_probe_mfma_f16.restype = i32
     lib.kda_probe_mfma_f16.argtypes = [i32, i32, i32, vp, vp]
+    lib.kda_probe_mfma_bf16.restype = i32
+    lib.kda_probe_mfma_bf16.argtypes = [i32, i32, i32, vp, vp]
     lib.kda_probe_mfma_f16_flops.restype = ctypes.c_double
     lib.kda_probe_mfma_f16_flops.argtypes = [i32, i32]
     lib.kda_decode_step.restype = i32
@@ -362,6 +364,18 @@ def kda_probe_mfma_f16(iters: int, blocks: int, sink, shape: int = 0, stream=Non
     if sink.numel() < blocks * 256:
         raise ValueError("sink needs blocks * 256 elements")
     _check(lib, lib.kda_probe_mfma_f16(int(shape), int(iters), int(blocks), _ptr(sink), _stream(stream)))
+    return float(lib.kda_probe_mfma_f16_flops(int(iters), int(blocks)))
+
+
+def kda_probe_mfma_bf16(iters: int, blocks: int, sink, shape: int = 0, stream=None) -> float:
+    """The same probe with bf16 operands (C: kda_probe_mfma_bf16); returns the launch's dense
+    bf16 flops."""
+    import torch
+    lib = load_library()
+    _req(sink, "sink", torch.float32)
+    if sink.numel() < blocks * 256:
+        raise ValueError("sink needs blocks * 256 elements")
+    _check(lib, lib.kda_probe_mfma_bf16(int(shape), int(iters), int(blocks), _ptr(sink), _stream(stream)))
     return float(lib.kda_probe_mfma_f16_flops(int(iters), int(blocks)))
 
 

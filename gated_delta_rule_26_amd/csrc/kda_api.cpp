@@ -510,12 +510,21 @@ kda_status kda_probe_copy(const void *src, void *dst, size_t bytes, void *stream
                       "kda_probe_copy launch");
 }
 
-kda_status kda_probe_mfma_f16(int32_t shape, int32_t iters, int32_t blocks, float *sink, void *stream) {
+static kda_status probe_mfma(int32_t bf16, int32_t shape, int32_t iters, int32_t blocks, float *sink,
+                             void *stream) {
     if (shape < 0 || shape > 1 || iters < 1 || blocks < 1 || !sink)
         return fail(KDA_ERR_INVALID_ARGUMENT, "shape 0 or 1, positive iters and blocks, and sink are required");
     if (!aligned16(sink)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
-    return hip_status(kda::launch_probe_mfma(shape, iters, blocks, sink, static_cast<hipStream_t>(stream)),
-                      "kda_probe_mfma_f16 launch");
+    return hip_status(kda::launch_probe_mfma(bf16, shape, iters, blocks, sink, static_cast<hipStream_t>(stream)),
+                      bf16 ? "kda_probe_mfma_bf16 launch" : "kda_probe_mfma_f16 launch");
+}
+
+kda_status kda_probe_mfma_f16(int32_t shape, int32_t iters, int32_t blocks, float *sink, void *stream) {
+    return probe_mfma(0, shape, iters, blocks, sink, stream);
+}
+
+kda_status kda_probe_mfma_bf16(int32_t shape, int32_t iters, int32_t blocks, float *sink, void *stream) {
+    return probe_mfma(1, shape, iters, blocks, sink, stream);
 }
 
 double kda_probe_mfma_f16_flops(int32_t iters, int32_t blocks) {

@@ -117,7 +117,8 @@ hipError_t launch_conv(int32_t dtype, const ConvArgs &a, bool update, hipStream_
 // Measurement probes (the device's practical peaks): a 16-byte-vector copy and a pure fp16
 // matrix-core loop (shape 0: 16x16x32, 1: 32x32x16) over `blocks` workgroups of 256 threads.
 hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
-hipError_t launch_probe_mfma(int32_t shape, int32_t iters, int32_t blocks, float *sink, hipStream_t stream);
+hipError_t launch_probe_mfma(int32_t bf16, int32_t shape, int32_t iters, int32_t blocks, float *sink,
+                             hipStream_t stream);
 int64_t probe_mfma_flops_per_iter_and_thread();
 // The chunked backward pass: five kernels in stream order over the workspace records.
 hipError_t launch_chunk_bwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv, const BwdArgs &a,

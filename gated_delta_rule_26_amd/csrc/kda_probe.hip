@@ -4,7 +4,7 @@
 // * copy: dst = src over `bytes`, 16-byte vectors, non-temporal loads (the state stream of the
 //   decode step reads the same way): the practical HBM bandwidth of a kernel that reads each
 //   byte once and writes each byte once.
-// * fp16 matrix cores: every wave runs a loop of independent fp16 matrix-core products on
+// * fp16 / bf16 matrix cores: every wave runs a loop of independent matrix-core products on
 //   several accumulators (16x16x32 or 32x32x16 instructions, the same flops per iteration),
 //   the operands held in registers; the accumulators are written out at the end so nothing is
 //   optimised away.
@@ -36,14 +36,28 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(const f32x4 *__restrict
 
 constexpr int kProbeAcc = 8;
 
-// SHAPE 0: v_mfma_f32_16x16x32_f16 (eight 4-float accumulators per lane);
-// SHAPE 1: v_mfma_f32_32x32x16_f16 (four 16-float accumulators per lane).
-template <int SHAPE> __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float *sink) {
-    f16x8 a, b;
+// SHAPE 0: v_mfma_f32_16x16x32_{f16,bf16} (eight 4-float accumulators per lane);
+// SHAPE 1: v_mfma_f32_32x32x16_{f16,bf16} (four 16-float accumulators per lane).
+// H: the operand type, _Float16 or __bf16.
+template <typename H> struct ProbeOps;
+template <> struct ProbeOps<_Float16> {
+    typedef f16x8 V;
+    static __device__ f32x4 m16(V a, V b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+    template <typename A> static __device__ A m32(V a, V b, A c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+};
+template <> struct ProbeOps<__bf16> {
+    typedef bf16x8 V;
+    static __device__ f32x4 m16(V a, V b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+    template <typename A> static __device__ A m32(V a, V b, A c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
+};
+
+template <int SHAPE, typename H> __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float *sink) {
+    using Ops = ProbeOps<H>;
+    typename Ops::V a, b;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        a[e] = static_cast<_Float16>(1e-3f * (threadIdx.x + e));
-        b[e] = static_cast<_Float16>(1e-3f * (blockIdx.x + e));
+        a[e] = static_cast<H>(1e-3f * (threadIdx.x + e));
+        b[e] = static_cast<H>(1e-3f * (blockIdx.x + e));
     }
     float out = 0.f;
     if constexpr (SHAPE == 0) {
@@ -52,7 +66,7 @@ template <int SHAPE> __global__ __launch_bounds__(256) void probe_mfma_kernel(in
         for (int j = 0; j < kProbeAcc; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int it = 0; it < iters; ++it) {
 #pragma unroll
-            for (int j = 0; j < kProbeAcc; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+            for (int j = 0; j < kProbeAcc; ++j) acc[j] = Ops::m16(a, b, acc[j]);
         }
 #pragma unroll
         for (int j = 0; j < kProbeAcc; ++j) out += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
@@ -66,7 +80,7 @@ template <int SHAPE> __global__ __launch_bounds__(256) void probe_mfma_kernel(in
         for (int it = 0; it < iters; ++it) {
 #pragma unroll
             for (int j = 0; j < kProbeAcc / 2; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
+                acc[j] = Ops::m32(a, b, acc[j]);
         }
 #pragma unroll
         for (int j = 0; j < kProbeAcc / 2; ++j)
@@ -85,11 +99,16 @@ hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStrea
     return hipGetLastError();
 }
 
-hipError_t launch_probe_mfma(int32_t shape, int32_t iters, int32_t blocks, float *sink, hipStream_t stream) {
-    if (shape == 0)
-        hipLaunchKernelGGL(probe_mfma_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, iters, sink);
-    else
-        hipLaunchKernelGGL(probe_mfma_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, iters, sink);
+hipError_t launch_probe_mfma(int32_t bf16, int32_t shape, int32_t iters, int32_t blocks, float *sink,
+                             hipStream_t stream) {
+    const dim3 g((unsigned)blocks), t(256);
+    if (bf16) {
+        if (shape == 0) hipLaunchKernelGGL((probe_mfma_kernel<0, __bf16>), g, t, 0, stream, iters, sink);
+        else hipLaunchKernelGGL((probe_mfma_kernel<1, __bf16>), g, t, 0, stream, iters, sink);
+    } else {
+        if (shape == 0) hipLaunchKernelGGL((probe_mfma_kernel<0, _Float16>), g, t, 0, stream, iters, sink);
+        else hipLaunchKernelGGL((probe_mfma_kernel<1, _Float16>), g, t, 0, stream, iters, sink);
+    }
     return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@
  * core (kda_chunk_fwd_fused, kda_decode_step_fused); two more run the layer's short
  * convolution with its conv state (kda_short_conv_fwd, kda_short_conv_update); kda_chunk_bwd
  * is the backward pass of kda_chunk_fwd (training); and two measurement probes report the
- * device's practical copy and matrix-core peaks (kda_probe_copy, kda_probe_mfma_f16, at the
+ * device's practical copy and matrix-core peaks (kda_probe_copy, kda_probe_mfma_f16/bf16, at the
  * end of this file):
  *   kda_chunk_fwd    prefill: the chunkwise-parallel form of the recurrence ([KV-cache page]
  *                    section 3: chunk_size 64; section 6: chunked parallel form with a WY
@@ -335,11 +335,14 @@ kda_status kda_short_conv_update(int32_t N, int32_t C, int32_t W, int32_t dtype,
  *   independent fp16 matrix-core products per wave: eight v_mfma_f32_16x16x32_f16 (shape 0)
  *   or four v_mfma_f32_32x32x16_f16 (shape 1), the same flops; sink [blocks * 256] float32
  *   receives the accumulators (so nothing is optimised away). kda_probe_mfma_f16_flops gives
- *   the launch's dense fp16 flops.
+ *   the launch's dense flops.
+ * kda_probe_mfma_bf16 - the same loop with bf16 operands (v_mfma_f32_16x16x32_bf16 or
+ *   v_mfma_f32_32x32x16_bf16) and the same flops (kda_probe_mfma_f16_flops).
  * Errors as kda_chunk_fwd (invalid sizes or pointers, nothing launched).
  */
 kda_status kda_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
 kda_status kda_probe_mfma_f16(int32_t shape, int32_t iters, int32_t blocks, float *sink, void *stream);
+kda_status kda_probe_mfma_bf16(int32_t shape, int32_t iters, int32_t blocks, float *sink, void *stream);
 double kda_probe_mfma_f16_flops(int32_t iters, int32_t blocks);
 
 #ifdef __cplusplus

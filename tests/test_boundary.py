@@ -311,5 +311,7 @@ def test_probe_mfma_rejects_and_counts(lib):
     assert lib.kda_probe_mfma_f16(0, 1, 0, P, None) == INVALID
     assert lib.kda_probe_mfma_f16(0, 1, 1, None, None) == INVALID
     assert lib.kda_probe_mfma_f16(2, 1, 1, P, None) == INVALID
+    for bad in ((0, 0, 1, P), (0, 1, 0, P), (0, 1, 1, None), (-1, 1, 1, P), (2, 1, 1, P)):
+        assert lib.kda_probe_mfma_bf16(*bad, None) == INVALID
     # 8 accumulators x 2*16*16*32 flops per wave and iteration, 4 waves per workgroup
     assert lib.kda_probe_mfma_f16_flops(10, 3) == 10 * 3 * 4 * 8 * 2 * 16 * 16 * 32

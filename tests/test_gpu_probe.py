@@ -21,7 +21,7 @@ def test_probe_copy_is_exact():
     assert torch.equal(src, dst)
 
 
-def probe_expected(shape, iters, blocks):
+def probe_expected(shape, iters, blocks, bf16=False):
     """What every thread of the probe writes: the sum of its accumulator elements after
     `iters` products. Each lane's A fragment holds 8 fp16 values 1e-3 * (thread + e) and its
     B fragment 1e-3 * (block + e), e = 0..7, so B does not depend on the column and every
@@ -29,7 +29,13 @@ def probe_expected(shape, iters, blocks):
     16x16x32: lane 16 s + i holds row i, k = 8 s + e of A; the lane's 4 accumulator elements
     are rows 4 s .. 4 s + 3; 8 accumulators. 32x32x16: lane 32 s + i holds row i, k = 8 s + e;
     its 16 elements are rows 8 u + 4 s + r (u, r = 0..3); 4 accumulators."""
-    f16 = lambda x: (np.float32(1e-3) * np.asarray(x, np.float32)).astype(np.float16).astype(np.float64)  # noqa: E731
+    if bf16:  # round to nearest even to 8 significant bits
+        def f16(x):
+            u = (np.float32(1e-3) * np.asarray(x, np.float32)).view(np.uint32).astype(np.uint64)
+            u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+            return u.astype(np.uint32).view(np.float32).astype(np.float64)
+    else:
+        f16 = lambda x: (np.float32(1e-3) * np.asarray(x, np.float32)).astype(np.float16).astype(np.float64)  # noqa: E731
     e = np.arange(8)
     out = np.zeros((blocks, 256))
     rows, nk, nacc = (16, 4, 8) if shape == 0 else (32, 2, 4)
@@ -47,15 +53,17 @@ def probe_expected(shape, iters, blocks):
     return out.reshape(-1)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("shape", [0, 1])
-def test_probe_mfma_result(shape):
+def test_probe_mfma_result(shape, bf16):
     torch = torch_mod()
     iters, blocks = 10, 4
     sink = torch.full((blocks * 256,), float("nan"), device="cuda")
-    note(f"probe mfma shape {shape}, {blocks} blocks")
-    flops = kda.kda_probe_mfma_f16(iters, blocks, sink, shape=shape)
+    note(f"probe mfma shape {shape} {'bf16' if bf16 else 'fp16'}, {blocks} blocks")
+    probe = kda.kda_probe_mfma_bf16 if bf16 else kda.kda_probe_mfma_f16
+    flops = probe(iters, blocks, sink, shape=shape)
     torch.cuda.synchronize()
     assert flops == iters * blocks * 4 * 8 * 2 * 16 * 16 * 32
     got = sink.cpu().numpy().astype(np.float64)
-    ref = probe_expected(shape, iters, blocks)
+    ref = probe_expected(shape, iters, blocks, bf16)
     np.testing.assert_allclose(got, ref, rtol=1e-4)

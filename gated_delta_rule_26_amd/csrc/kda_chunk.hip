@@ -36,6 +36,7 @@
 //   (I - L)(I + L^2)(I + L^4)(I + L^8) on the matrix cores (transposes by products with the
 //   identity), and W and U~ come from block forward substitution (I + A) W = beta k e^G,
 //   (I + A) U~ = Diag(beta) V.
+#include <atomic>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -1526,16 +1527,18 @@ struct SplitPlan {
     size_t bytes = 0;
 };
 
+// Compute units of the current device, queried once per device (callers on several host
+// threads may race to fill a slot; they all store the same value).
 int device_cus() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (!cached[dev]) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (!n) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 int64_t record_bytes(int32_t in_dtype, int32_t C, int32_t Dk, int32_t Dv) {

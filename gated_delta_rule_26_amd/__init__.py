@@ -95,7 +95,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                         vp, vp, vp, fp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.kda_decode_step_fused.restype = i32
     lib.kda_decode_step_fused.argtypes = [i32, i32, i32, i32, i32, i32, f32,
-                                          vp, vp, vp, fp, vp, vp, vp]
+                                          vp, vp, vp, fp, vp, vp, vp, vp]
     lib.kda_recurrent_fwd.restype = i32
     lib.kda_recurrent_fwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, f32,
                                       vp, vp, vp, vp, vp, vp, vp, vp]

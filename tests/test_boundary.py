@@ -42,6 +42,39 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def _category(c_param):
+    """ctypes category of one C parameter declaration."""
+    if "*" in c_param:
+        return "ptr"
+    t = c_param.split()[0] if c_param.split() else ""
+    return {"int32_t": "i32", "float": "f32", "size_t": "sz", "double": "f64"}.get(t, t)
+
+
+def _ctypes_category(t):
+    if t in (ctypes.c_void_p, ctypes.c_char_p) or (isinstance(t, type) and issubclass(t, ctypes._Pointer)):
+        return "ptr"
+    return {ctypes.c_int32: "i32", ctypes.c_float: "f32", ctypes.c_size_t: "sz", ctypes.c_double: "f64"}.get(t, repr(t))
+
+
+def test_binding_signatures_match_the_header(lib):
+    """Every prototype in include/kda.h against the argtypes the ctypes binding declares for
+    it: the same number of parameters, and per position the same kind (pointer, int32,
+    float, size_t)."""
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    protos = re.findall(r"\b(kda_[a-z_0-9]+)\s*\(([^)]*)\)\s*;", src)
+    checked = 0
+    for name, params in protos:
+        params = [x.strip() for x in params.split(",") if x.strip() and x.strip() != "void"]
+        argtypes = getattr(lib, name).argtypes
+        assert argtypes is not None, f"{name}: the binding declares no argtypes"
+        assert len(argtypes) == len(params), f"{name}: {len(argtypes)} argtypes, {len(params)} in the header"
+        for i, (c, t) in enumerate(zip(params, argtypes)):
+            assert _category(c) == _ctypes_category(t), f"{name} parameter {i} ({c}): {t}"
+        checked += 1
+    assert checked >= 15
+
+
 def test_status_strings_and_version(lib):
     assert lib.kda_status_string(OK) == b"KDA_OK"
     assert lib.kda_status_string(INVALID) == b"KDA_ERR_INVALID_ARGUMENT"

@@ -73,6 +73,14 @@ def test_binding_signatures_match_the_header(lib):
             assert _category(c) == _ctypes_category(t), f"{name} parameter {i} ({c}): {t}"
         checked += 1
     assert checked >= 15
+    # return types: kda_status and int32_t as int32, size_t, double, const char *
+    rets = dict((n, r.split()[-1] if "*" not in r else "ptr")
+                for r, n in re.findall(r"(?:^|;|})\s*((?:const\s+)?\w+\s*\*?)\s*(kda_[a-z_0-9]+)\s*\(", src))
+    want = {"kda_status": ctypes.c_int32, "int32_t": ctypes.c_int32, "size_t": ctypes.c_size_t,
+            "double": ctypes.c_double, "ptr": ctypes.c_char_p}
+    for name, _ in protos:
+        assert name in rets, name
+        assert getattr(lib, name).restype is want[rets[name]], f"{name}: returns {rets[name]}"
 
 
 def test_status_strings_and_version(lib):

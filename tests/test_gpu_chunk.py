@@ -44,7 +44,7 @@ def test_tiny_f32_workload():
     assert_close(S, S_ref, TOL_F32, "final state")
 
 
-@pytest.mark.parametrize("D,C", [(16, 16), (32, 16), (32, 64), (64, 64)])
+@pytest.mark.parametrize("D,C", [(16, 16), (32, 16), (32, 64), (64, 64), (128, 32)])
 @pytest.mark.parametrize("T", [1, 15, 50, 64, 65, 200, 333])
 def test_f32_ragged_lengths_with_state(D, C, T):
     H = 3
@@ -57,7 +57,7 @@ def test_f32_ragged_lengths_with_state(D, C, T):
     assert_close(S, S_ref, TOL_F32, "final state")
 
 
-@pytest.mark.parametrize("D,C", [(16, 16), (32, 16), (32, 64)])
+@pytest.mark.parametrize("D,C", [(16, 16), (32, 16), (32, 64), (128, 32)])
 def test_f32_batched_sequences(D, C):
     B, T, H = 3, 150, 2
     x = random_inputs(110 + D, B * T, H, D, "f32")
@@ -69,7 +69,7 @@ def test_f32_batched_sequences(D, C):
     assert_close(S, S_ref, TOL_F32, "final state")
 
 
-@pytest.mark.parametrize("D,C", [(16, 16), (32, 16), (32, 64), (64, 64)])
+@pytest.mark.parametrize("D,C", [(16, 16), (32, 16), (32, 64), (64, 64), (128, 32)])
 def test_f32_packed_with_empty_sequences(D, C):
     lens = [0, 70, 1, 128, 5, 0, 300]
     cu = np.concatenate([[0], np.cumsum(lens)])
@@ -85,7 +85,7 @@ def test_f32_packed_with_empty_sequences(D, C):
     np.testing.assert_array_equal(S[5], s0[5])
 
 
-@pytest.mark.parametrize("D,C", [(16, 16), (32, 64)])
+@pytest.mark.parametrize("D,C", [(16, 16), (32, 64), (128, 32)])
 def test_f32_strong_decay(D, C):
     """g = -3 per token: the decay over a 64-token chunk is e^-192, far below float32's range;
     the per-16-token factorisation keeps every operand finite."""
@@ -114,7 +114,7 @@ def extreme_gates(x, seed: int, g_min: float):
     return x
 
 
-@pytest.mark.parametrize("D,C", [(16, 16), (32, 64), (64, 64)])
+@pytest.mark.parametrize("D,C", [(16, 16), (32, 64), (64, 64), (128, 32)])
 @pytest.mark.parametrize("g_min", [-8.0, -40.0, -400.0])
 def test_f32_extreme_decay(D, C, g_min):
     """Per-token decays down to e^-400 (block decays far below e^-60): the diagonal blocks are
@@ -127,6 +127,25 @@ def test_f32_extreme_decay(D, C, g_min):
     o_ref, S_ref = run_oracle(x, "f32", scale=D ** -0.5, initial_state=s0)
     assert_close(o, o_ref, TOL_F32, "o")
     assert_close(S, S_ref, TOL_F32, "final state")
+
+
+def test_f32_prefill_4k_h16_inputs_at_head_size_128():
+    """The 4K-token, 16-head workload's bf16 inputs upcast exactly to float32, through the
+    float32 instantiation at the real head size (Dk = Dv = 128, 32-token chunks): the 1e-4
+    float32 bound at D = 128 separates the algorithm's own error from the bf16 path's fp16
+    operand rounding."""
+    w = synth.WORKLOADS["prefill_4k_h16"]
+    x = synth.make_inputs(w)
+    for key in ("q", "k", "v"):
+        x[key] = synth.bf16_bits_to_f32(x[key])
+    note("prefill_4k_h16 inputs, float32 instantiation (C=32, D=128)")
+    o, S = gpu_chunk(x, "f32", chunk=32)
+    o_ref, S_ref = run_oracle(x, "f32")
+    assert_close(o, o_ref, TOL_F32, "o")
+    assert_close(S, S_ref, TOL_F32, "final state")
+    o1, S1 = gpu_chunk(x, "f32", chunk=32, split=False)
+    assert_close(o1, o_ref, TOL_F32, "o (one pass)")
+    assert_close(S1, S_ref, TOL_F32, "final state (one pass)")
 
 
 # ----------------------------------------------------------------------- bf16 instantiation
@@ -284,6 +303,8 @@ SPLIT_CASES = [
     ("f32", 16, 16, 1, 700, 1),
     ("f32", 32, 64, 1, 3000, 2),
     ("f32", 64, 64, 2, 4100, 2),
+    ("f32", 128, 32, 1, 3000, 2),
+    ("f32", 128, 32, 2, 1500 + 17, 1),
 ]
 
 
@@ -331,7 +352,7 @@ def test_split_without_initial_state():
 
 # --------------------------------------------------------------- the method's degenerate cases
 
-DEGEN = [("bf16", 128, 64), ("f32", 32, 64), ("f32", 16, 16)]
+DEGEN = [("bf16", 128, 64), ("f32", 32, 64), ("f32", 16, 16), ("f32", 128, 32)]
 
 
 @pytest.mark.parametrize("split", [False, True])

@@ -80,6 +80,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                   vp, i32, vp, sz, vp]
     lib.kda_probe_copy.restype = i32
     lib.kda_probe_copy.argtypes = [vp, vp, sz, vp]
+    lib.kda_probe_read.restype = i32
+    lib.kda_probe_read.argtypes = [vp, sz, vp]
+    lib.kda_probe_rmw.restype = i32
+    lib.kda_probe_rmw.argtypes = [vp, sz, f32, vp]
     lib.kda_probe_mfma_f16.restype = i32
     lib.kda_probe_mfma_f16.argtypes = [i32, i32, i32, vp, vp]
     lib.kda_probe_mfma_bf16.restype = i32
@@ -116,6 +120,24 @@ def _check(lib, status: int):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _on_stream(fn):
+    """Run the call with ``stream`` (when given) as torch's current stream, so that every
+    buffer the binding allocates (outputs, the internal workspace) comes from the stream the
+    kernels run on. torch's caching allocator ties a block to the stream current when it was
+    allocated: a workspace taken from another stream and freed on return could be handed to
+    that stream's next allocation while the kernels on ``stream`` still use it."""
+    import functools
+
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        import torch
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return call
 
 
 def _dtype_code(t):
@@ -259,6 +281,7 @@ def _out(o, like, dtype, name="o"):
     return o
 
 
+@_on_stream
 def kda_chunk_fwd(q, k, v, g, beta, *, initial_state=None, output_final_state: bool = True,
                   final_state=None, cu_seqlens=None, chunk: int = 64, scale: float = 1.0,
                   o=None, stream=None, split: bool = True, workspace=None):
@@ -292,6 +315,7 @@ def kda_chunk_fwd(q, k, v, g, beta, *, initial_state=None, output_final_state: b
     return o, final_state
 
 
+@_on_stream
 def kda_chunk_bwd(q, k, v, g, beta, do, *, initial_state=None, dfinal_state=None,
                   cu_seqlens=None, chunk: int = 64, scale: float = 1.0,
                   want_dinitial_state: bool = True, grads=None, workspace=None, stream=None):
@@ -354,6 +378,23 @@ def kda_probe_copy(src, dst, stream=None):
     _check(lib, lib.kda_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 
+def kda_probe_read(src, stream=None):
+    """Read all of ``src`` (a contiguous device tensor, a multiple of 16 bytes) with the
+    library's read probe (C: kda_probe_read)."""
+    lib = load_library()
+    _req(src, "src")
+    _check(lib, lib.kda_probe_read(_ptr(src), src.numel() * src.element_size(), _stream(stream)))
+
+
+def kda_probe_rmw(buf, factor: float = 1.0, stream=None):
+    """buf *= factor in place with the library's read-modify-write probe (C: kda_probe_rmw);
+    ``buf`` is a contiguous float32 device tensor."""
+    import torch
+    lib = load_library()
+    _req(buf, "buf", torch.float32)
+    _check(lib, lib.kda_probe_rmw(_ptr(buf), buf.numel() * 4, float(factor), _stream(stream)))
+
+
 def kda_probe_mfma_f16(iters: int, blocks: int, sink, shape: int = 0, stream=None) -> float:
     """Run the fp16 matrix-core probe (C: kda_probe_mfma_f16; shape 0: 16x16x32, 1: 32x32x16
     instructions) into ``sink`` (float32, at least blocks * 256 elements); returns the launch's
@@ -399,6 +440,7 @@ def chunk_fwd_workspace_bytes(q, v, *, chunk: int = 64, num_seqs: int | None = N
                                                  _dtype_code(q), N))
 
 
+@_on_stream
 def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, o=None, stream=None):
     """One KDA decode step (C: kda_decode_step): q, k, g [N, H, Dk]; v [N, H, Dv]; beta
     [N, H]; ``state`` float32 [N, H, Dk, Dv] is updated in place. Returns o float32 [N, H, Dv]."""
@@ -425,6 +467,7 @@ def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, o=None, stre
     return o
 
 
+@_on_stream
 def kda_chunk_fwd_fused(q, k, v, gate_x, A_log, dt_bias, beta, *, normalize_qk: bool = True,
                         o_gate=None, o_weight=None, o_eps: float = 1e-6, out_dtype=None,
                         initial_state=None, output_final_state: bool = True, final_state=None,
@@ -456,6 +499,7 @@ def kda_chunk_fwd_fused(q, k, v, gate_x, A_log, dt_bias, beta, *, normalize_qk: 
     return o, final_state
 
 
+@_on_stream
 def kda_decode_step_fused(q, k, v, gate_x, A_log, dt_bias, beta, state, *,
                           normalize_qk: bool = True, o_gate=None, o_weight=None,
                           o_eps: float = 1e-6, out_dtype=None, scale: float = 1.0, o=None,
@@ -487,6 +531,7 @@ def kda_decode_step_fused(q, k, v, gate_x, A_log, dt_bias, beta, state, *,
 _ACT = {None: 0, "none": 0, "silu": 1}
 
 
+@_on_stream
 def kda_short_conv_fwd(x, weight, bias=None, *, initial_state=None, final_state=None,
                        output_final_state: bool = True, cu_seqlens=None, activation="silu",
                        y=None, stream=None):
@@ -532,6 +577,7 @@ def kda_short_conv_fwd(x, weight, bias=None, *, initial_state=None, final_state=
     return y, final_state
 
 
+@_on_stream
 def kda_short_conv_update(x, weight, bias, state, *, activation="silu", y=None, stream=None):
     """One decode token per sequence (C: kda_short_conv_update): x [N, C]; state [N, W-1, C]
     in x's dtype, shifted in place. Returns y like x."""
@@ -553,6 +599,7 @@ def kda_short_conv_update(x, weight, bias, state, *, activation="silu", y=None, 
     return y
 
 
+@_on_stream
 def kda_recurrent_fwd(q, k, v, g, beta, state, *, scale: float = 1.0, o=None, stream=None):
     """L tokens per (sequence, head) on the persistent state (C: kda_recurrent_fwd): q, k, g
     [N, L, H, Dk]; v [N, L, H, Dv]; beta [N, L, H]; ``state`` float32 [N, H, Dk, Dv] is

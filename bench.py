@@ -42,9 +42,14 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA prefill tokens/s (H=32,d=128) + decode state-update HBM GB/s, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, published
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix peak, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_prefill_128k_h32_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_26_amd", "csrc", "kda_chunk.hip")
 PREFILL_KERNELS = ("chunk_fwd_kernel", "replay_kernel", "split_combine_kernel")  # one call
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_decode_step_decode_256x32_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_26_amd", "csrc", "kda_decode.hip")
+DECODE_KERNELS = ("decode_kernel",)
+DECODE_STEPS = 1000   # the decode workload: 1000 consecutive steps per timed block
 COPY_BYTES = 1 << 30  # calibration: read 1 GiB, write 1 GiB
 
 
@@ -67,6 +72,17 @@ def bwd_bytes_per_token_head(K: int, V: int) -> int:
     return (2 * K * 2 + V * 2 + K * 4 + 4 + V * 4) + (3 * K * 4 + V * 4 + 4)
 
 
+def bwd_flops_per_token_head(K: int, V: int, C: int) -> float:
+    """Algorithmic flops per (token, head) of the chunked backward pass, per chunk (triangular
+    products counted at half, as in the forward): recomputing A~, M, W (3 C^2 K), U~ (C^2 V),
+    T (C^3/3), U = U~ - W S and the state update (4 CKV); the reverse state pass M^T dO (C^2 V),
+    Kd dS', Qg^T dO, W^T dU (6 CKV); the gradient products dO S^T, U dS'^T, dU S^T (6 CKV),
+    dM = dO U^T (C^2 V), dT = dU (beta v)^T + dW (beta K e^G)^T (C^2 V + C^2 K), T^T dU (C^2 V),
+    T^T dW (C^2 K), T^T dT and its product with T^T (2 C^3/3), and the pair terms of A~ and M
+    (4 C^2 K). Total 9 C^2 K + 5 C^2 V + 16 C K V + C^3 per chunk."""
+    return (9 * C * C * K + 5 * C * C * V + 16 * C * K * V + C ** 3) / C
+
+
 def fused_prefill_bytes_per_token_head(K: int, V: int) -> int:
     """Algorithmic HBM bytes per (token, head) of the fused prefill: bf16 raw q and k, bf16 v,
     the gate's bf16 pre-activation, float32 beta, the output gate's bf16 pre-activation and
@@ -86,20 +102,21 @@ def decode_bytes_per_step(N: int, H: int, K: int, V: int) -> int:
     return 2 * N * H * K * V * 4 + N * H * (2 * K * 2 + V * 2 + K * 4 + 4) + N * H * V * 4
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_sha(src: str | None = None) -> str:
+    with open(src or KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(launch_bytes: float):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, or None when it is
-    missing or was taken on a different version of the kernel source."""
+def load_traffic(launch_bytes: float, path: str | None = None, src: str | None = None):
+    """HBM traffic per launch from a committed rocprofv3 counter summary (the prefill's by
+    default), or None when it is missing or was taken on a different version of the kernel
+    source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path or TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha") != kernel_sha():
+    if t.get("kernel_source_sha") != kernel_sha(src):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -138,26 +155,28 @@ def kernel_label(name: str) -> str:
     return "split_combine_kernel"
 
 
-def traffic_from(fetch_csv: str, write_csv: str) -> dict:
-    """Per-call HBM bytes of the prefill from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
-    dispatch), each scaled by known bytes / counted bytes of the copy-like calibration kernel
-    (it reads and writes COPY_BYTES)."""
+def traffic_from(fetch_csv: str, write_csv: str, kernels=PREFILL_KERNELS,
+                 call_kernel: str = "chunk_fwd_kernel") -> dict:
+    """Per-call HBM bytes of one entry point (the prefill's kernels by default; one dispatch of
+    ``call_kernel`` per call) from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by known bytes / counted bytes of the copy-like calibration kernel (it reads and
+    writes COPY_BYTES)."""
     out = {}
     for key, path in (("fetch", fetch_csv), ("write", write_csv)):
         per_kernel, copy, calls = {}, [], set()
         for name, disp, cname, val in _counter_rows(path):
             if cname not in ("FETCH_SIZE", "WRITE_SIZE"):
                 continue
-            if any(k in name for k in PREFILL_KERNELS):
-                short = kernel_label(name)
+            if any(k in name for k in kernels):
+                short = kernel_label(name) if kernels == PREFILL_KERNELS else kernels[0]
                 kib, n = per_kernel.get(short, (0.0, 0))
                 per_kernel[short] = (kib + val, n + 1)
-                if "chunk_fwd_kernel" in name:
-                    calls.add(disp)  # one forward dispatch per call
+                if call_kernel in name:
+                    calls.add(disp)
             elif "neg_kernel" in name:
                 copy.append(val)
         if not copy or not calls:
-            raise SystemExit(f"{path}: no prefill or calibration dispatches found")
+            raise SystemExit(f"{path}: no {call_kernel} or calibration dispatches found")
         copy_kib = sum(copy) / len(copy)
         scale = (COPY_BYTES / 1024.0) / copy_kib
         total_kib = sum(kib for kib, _ in per_kernel.values())
@@ -172,21 +191,27 @@ def traffic_from(fetch_csv: str, write_csv: str) -> dict:
 
 
 def write_traffic(fetch_csv: str, write_csv: str) -> None:
-    t = traffic_from(fetch_csv, write_csv)
-    res = {
-        "kernel_source_sha": kernel_sha(),
-        "workload": "prefill_128k_h32 (one kda_chunk_fwd call)",
-        "hbm_bytes_per_launch": round(t["fetch"]["bytes_per_call"] + t["write"]["bytes_per_call"]),
-        "fetch_bytes_per_launch": round(t["fetch"]["bytes_per_call"]),
-        "write_bytes_per_launch": round(t["write"]["bytes_per_call"]),
-        "calibration": {"kernel": "torch.neg over 1 GiB float32 (reads 1 GiB, writes 1 GiB)",
-                        "fetch_scale": t["fetch"]["scale"], "write_scale": t["write"]["scale"]},
-        "counters": t,
-    }
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(res, f, indent=1)
-    print(json.dumps(res, indent=1))
+    """The prefill call's and the decode step's traffic files from the counter pass."""
+    for path, src, workload, kernels, call in (
+            (TRAFFIC_FILE, KERNEL_SRC, "prefill_128k_h32 (one kda_chunk_fwd call)", PREFILL_KERNELS,
+             "chunk_fwd_kernel"),
+            (DECODE_TRAFFIC_FILE, DECODE_SRC, "decode_256x32 (one kda_decode_step call)", DECODE_KERNELS,
+             "decode_kernel")):
+        t = traffic_from(fetch_csv, write_csv, kernels, call)
+        res = {
+            "kernel_source_sha": kernel_sha(src),
+            "workload": workload,
+            "hbm_bytes_per_launch": round(t["fetch"]["bytes_per_call"] + t["write"]["bytes_per_call"]),
+            "fetch_bytes_per_launch": round(t["fetch"]["bytes_per_call"]),
+            "write_bytes_per_launch": round(t["write"]["bytes_per_call"]),
+            "calibration": {"kernel": "torch.neg over 1 GiB float32 (reads 1 GiB, writes 1 GiB)",
+                            "fetch_scale": t["fetch"]["scale"], "write_scale": t["write"]["scale"]},
+            "counters": t,
+        }
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res, indent=1))
 
 
 def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
@@ -233,10 +258,14 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
     ws = torch.empty(max(kda.chunk_fwd_workspace_bytes(q, v), 1), dtype=torch.uint8, device="cuda")
     fwd = lambda: kda.kda_chunk_fwd(q, k, v, g, b, workspace=ws)  # noqa: E731
     ms, ms_cold = timed(fwd, 20), timed_cold(fwd, 20)
+    pb = w.T * w.H * prefill_bytes_per_token_head(w.K, w.V) + w.H * w.K * w.V * 4
     out["prefill_4k_h16"] = {"ms": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
                              "cache": "resident (back to back)",
                              "ms_cold": round(ms_cold, 4),
                              "tokens_per_s_cold": round(w.T / (ms_cold * 1e-3), 1),
+                             "algorithmic_gbs_cold": round(pb / (ms_cold * 1e-3) / 1e9, 1),
+                             "frac_hbm_cold": round(pb / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "algorithmic_bytes": pb,
                              "B": 1, "T": w.T, "H": w.H, "dk": w.K, "dv": w.V, "chunk": w.chunk}
     del q, k, v, g, b, ws, x
     log("timed prefill_4k_h16")
@@ -252,10 +281,17 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
                                     want_dinitial_state=False)
     ms, ms_cold = timed(bwd, 20), timed_cold(bwd, 20)
     bb = w.T * w.H * bwd_bytes_per_token_head(w.K, w.V)
+    bf = w.T * w.H * bwd_flops_per_token_head(w.K, w.V, w.chunk)
     out["backward_4k_h16"] = {
         "ms": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
         "cache": "resident (back to back)",
         "ms_cold": round(ms_cold, 4), "tokens_per_s_cold": round(w.T / (ms_cold * 1e-3), 1),
+        # float32 throughout: the fp32 matrix cores bind (about 99 flop per algorithmic byte
+        # against a ridge of about 20), not HBM
+        "roofline": {"bound": "mfma_f32", "achieved": round(bf / (ms * 1e-3) / 1e12, 2),
+                     "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bf / (ms * 1e-3) / 1e12 / MFMA_F32_PEAK_TFLOPS, 4),
+                     "algorithmic_flops": round(bf)},
         "algorithmic_gbs": round(bb / (ms * 1e-3) / 1e9, 1),
         "frac_hbm": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "bytes_per_token_head": bwd_bytes_per_token_head(w.K, w.V),
@@ -275,7 +311,11 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
                      dtype=torch.uint8, device="cuda")
     ms = timed(lambda: kda.kda_chunk_fwd(q, k, v, g, b, initial_state=s0, cu_seqlens=cu,
                                          workspace=ws), 3)
+    vb = n_tok * w.H * prefill_bytes_per_token_head(w.K, w.V) + 2 * len(x["lengths"]) * w.H * w.K * w.V * 4
     out["varlen_64seq_h16"] = {"ms": round(ms, 4), "tokens_per_s": round(n_tok / (ms * 1e-3), 1),
+                               "algorithmic_gbs": round(vb / (ms * 1e-3) / 1e9, 1),
+                               "frac_hbm": round(vb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               "algorithmic_bytes": vb,
                                "sequences": len(x["lengths"]), "tokens": n_tok,
                                "longest": int(max(x["lengths"])), "H": w.H, "dk": w.K,
                                "order": "longest first"}
@@ -305,29 +345,13 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
     del q, k, v, gx, z, b, y, S, ws, x
     log("timed prefill_128k_h32_fused")
 
-    # decode steps back to back on the decode workload's states (one token per sequence and
-    # head per step): the core step, then the fused one. The headline decode figure
-    # alternates with the prefill instead, which leaves no dirty state lines in the caches.
+    # 8 tokens per sequence and head in one call (the recurrent mode for short queries) on the
+    # decode workload's states: the state is read and written once for the 8
     N, H = state.shape[0], state.shape[1]
     wd = synth.WORKLOADS["decode_256x32"].with_(prefill_T=0, decode_steps=8)
     x = synth.make_inputs(wd, seqs=range(N))
     dq, dk, dv = (to_dev(x["dec_" + n], True) for n in ("q", "k", "v"))
     dg, db = to_dev(x["dec_g"]), to_dev(x["dec_beta"])
-    od = torch.empty((N, H, wd.V), dtype=torch.float32, device="cuda")
-    it = iter(range(1 << 30))
-
-    def cstep():
-        i = next(it) % wd.decode_steps
-        kda.kda_decode_step(dq[i], dk[i], dv[i], dg[i], db[i], state, o=od)
-    us = timed(cstep, 50) * 1e3
-    cb = decode_bytes_per_step(N, H, wd.K, wd.V)
-    out["decode_256x32_back_to_back"] = {
-        "avg_launch_us": round(us, 2), "steps_per_s": round(1e6 / us, 1),
-        "achieved_gbs": round(cb / (us * 1e-6) / 1e9, 1),
-        "frac_hbm": round(cb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-        "algorithmic_bytes_per_step": cb}
-    # 8 tokens per sequence and head in one call (the recurrent mode for short queries): the
-    # state is read and written once for the 8
     L8 = wd.decode_steps
     rq, rk, rv = (t.transpose(0, 1).contiguous() for t in (dq, dk, dv))    # [N, 8, H, D]
     rg, rb = dg.transpose(0, 1).contiguous(), db.transpose(0, 1).contiguous()
@@ -337,10 +361,11 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
     out["decode_256x32_8_tokens_per_call"] = {
         "avg_launch_us": round(us, 2), "tokens_per_s": round(N * L8 * 1e6 / us, 1),
         "us_per_token_step": round(us / L8, 2), "achieved_gbs": round(rbytes / (us * 1e-6) / 1e9, 1),
+        "frac_hbm": round(rbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": rbytes,
         "what": "kda_recurrent_fwd: 256 sequences x 32 heads x 8 tokens, state read and written once"}
-    del dq, dk, dv, dg, db, od, x, rq, rk, rv, rg, rb, ro
-    log("timed decode_256x32 back to back, and 8 tokens per call")
+    del dq, dk, dv, dg, db, x, rq, rk, rv, rg, rb, ro
+    log("timed decode_256x32 with 8 tokens per call")
 
     x = synth.make_inputs(wd, seqs=range(N), fused=True)
     dq, dk, dv, dgx, dz = (to_dev(x["dec_" + n], True) for n in ("q", "k", "v", "x", "z"))
@@ -400,6 +425,7 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
     ub = N3 * C3 * (2 + 2 + 2 * 3 * 2)
     out["short_conv_update_256"] = {
         "avg_launch_us": round(us, 2), "achieved_gbs": round(ub / (us * 1e-6) / 1e9, 1),
+        "frac_hbm": round(ub / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "bytes": ub, "what": "256 sequences x 12288 channels (q, k, v), state [3, C] bf16 in place"}
     log("timed short_conv_update_256")
 
@@ -409,9 +435,15 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
     out["copy_reference"] = {"bytes": 2 << 30, "gbs": round((2 << 30) / (ms * 1e-3) / 1e9, 1),
                              "what": "device-to-device copy of 1 GiB (read + write)"}
     # the device's practical peaks, from the library's probes: a copy with 16-byte
-    # non-temporal loads, and a loop of independent fp16 matrix-core products on every CU
+    # non-temporal loads; a read-only stream (the bound of the read-mostly prefill); an
+    # in-place read-modify-write stream (the decode step's state pattern); and a loop of
+    # independent fp16 / bf16 matrix-core products on every CU
     ms = timed(lambda: kda.kda_probe_copy(src, dst), 10)
     copy_gbs = (2 << 30) / (ms * 1e-3) / 1e9
+    ms = timed(lambda: kda.kda_probe_read(src), 10)
+    read_gbs = (1 << 30) / (ms * 1e-3) / 1e9
+    ms = timed(lambda: kda.kda_probe_rmw(src, 1.0), 10)
+    rmw_gbs = (2 << 30) / (ms * 1e-3) / 1e9
     blocks, iters = 2048, 2000
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     tf, tb = {}, {}
@@ -423,15 +455,19 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
     best = max(tf.values())
     best_copy = max(copy_gbs, out["copy_reference"]["gbs"])
     out["measured_peaks"] = {
-        "hbm_gbs": round(best_copy, 1), "hbm_frac_of_published": round(best_copy / HBM_PEAK_GBS, 4),
+        "hbm_read_gbs": round(read_gbs, 1), "hbm_read_frac_of_published": round(read_gbs / HBM_PEAK_GBS, 4),
+        "hbm_rmw_gbs": round(rmw_gbs, 1), "hbm_rmw_frac_of_published": round(rmw_gbs / HBM_PEAK_GBS, 4),
+        "hbm_copy_gbs": round(best_copy, 1),
         "hbm_gbs_by_copy": {"kda_probe_copy": round(copy_gbs, 1), "torch copy_": out["copy_reference"]["gbs"]},
         "mfma_f16_tflops": round(best, 1),
         "mfma_f16_tflops_by_instruction": {k: round(v, 1) for k, v in tf.items()},
         "mfma_bf16_tflops_by_instruction": {k: round(v, 1) for k, v in tb.items()},
         "mfma_frac_of_published": round(best / MFMA_F16_PEAK_TFLOPS, 4),
-        "what": "the better of two 1 GiB copies (read + write); kda_probe_mfma_f16 / _bf16, 2048 x 256 threads"}
+        "what": ("1 GiB: kda_probe_read (non-temporal loads, 64 KB per workgroup), kda_probe_rmw (in place, "
+                 "non-temporal loads and stores, 16 KB per workgroup), the better of two copies; "
+                 "kda_probe_mfma_f16 / _bf16, 2048 x 256 threads")}
     del src, dst, sink
-    log("measured the copy and fp16 / bf16 matrix-core peaks")
+    log("measured the read, read-modify-write, copy and matrix-core peaks")
     return out
 
 
@@ -473,6 +509,30 @@ def cpu_baseline(x: dict, sample_tokens: int) -> dict:
             "host": {"nproc": os.cpu_count(), "cpu": model}}
 
 
+
+def cpu_baseline_decode(tok: dict, N: int, H: int, K: int, V: int) -> dict:
+    """The float64 oracle's decode step (unchanged) over consecutive tokens of the decode
+    workload, all N x H states, on the host's cores. The states start at zero: a step costs
+    the same whatever their values, and starting from the 2048-token prefill would add its
+    own minutes of oracle time to the baseline."""
+    import numpy as np
+
+    import oracle
+    import synth
+    steps = tok["q"].shape[0]
+    threads = min(os.cpu_count() or 1, 16)
+    st = lambda a: synth.stored_to_f64(a, "bf16")  # noqa: E731
+    args = [(st(tok["q"][j]), st(tok["k"][j]), st(tok["v"][j]), tok["g"][j].astype(np.float64),
+             tok["beta"][j].astype(np.float64)) for j in range(steps)]
+    state = np.zeros((N, H, K, V))
+    t0 = time.perf_counter()
+    for a in args:
+        _, state = oracle.kda_decode_step(*a, state, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": steps / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"decode_256x32: {steps} consecutive steps over all {N} x {H} states "
+                      f"(float64 recurrence, {dt:.1f} s wall)"}
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,7 +540,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
+    ap.add_argument("--cpu-decode-steps", type=int, default=8,
+                    help="consecutive oracle decode steps timed for the CPU baseline")
     ap.add_argument("--decode-seqs", type=int, default=256)
+    ap.add_argument("--decode-steps", type=int, default=DECODE_STEPS,
+                    help="consecutive decode steps in each step's timed block (the workload's 1000)")
     ap.add_argument("--counter-pass", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads (4K prefill, packed varlen) and the copy reference")
@@ -521,10 +585,22 @@ def main():
     ws_bytes = kda.chunk_fwd_workspace_bytes(pq, pv, chunk=C)
     pws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     if args.counter_pass:
-        # prefill calls only, then the copy-like calibration kernel
+        # prefill calls only, then decode steps, then the copy-like calibration kernel
         for _ in range(args.warmup + args.steps):
             kda.kda_chunk_fwd(pq, pk, pv, pg, pb, final_state=pS, o=po, workspace=pws)
         torch.cuda.synchronize()
+        # decode steps on 256 x 32 states (the traffic does not depend on the values)
+        wd = synth.WORKLOADS["decode_256x32"].with_(prefill_T=0, decode_steps=8)
+        xd = synth.make_inputs(wd, seqs=range(args.decode_seqs))
+        tq, tk, tv = (to_dev(xd["dec_" + n], True) for n in ("q", "k", "v"))
+        tg, tb = to_dev(xd["dec_g"]), to_dev(xd["dec_beta"])
+        state = torch.zeros((args.decode_seqs, H, K, V), dtype=torch.float32, device=dev)
+        to = torch.empty((args.decode_seqs, H, V), dtype=torch.float32, device=dev)
+        for i in range(args.steps):
+            j = i % wd.decode_steps
+            kda.kda_decode_step(tq[j], tk[j], tv[j], tg[j], tb[j], state, o=to)
+        torch.cuda.synchronize()
+        del tq, tk, tv, tg, tb, state, to, xd
         # two backward calls at the 4K-token, 16-head training shape (matrix-core counters)
         wb = synth.WORKLOADS["prefill_4k_h16"]
         xb = synth.make_inputs(wb)
@@ -540,14 +616,16 @@ def main():
         for _ in range(3):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        log(f"counter pass: {args.warmup + args.steps} prefill calls "
-            f"(workspace {ws_bytes} B), 3 calibration copies of {COPY_BYTES} B")
+        log(f"counter pass: {args.warmup + args.steps} prefill calls (workspace {ws_bytes} B), "
+            f"{args.steps} decode steps, 3 calibration copies of {COPY_BYTES} B")
         return
 
     # ----------------------------------------------------------------- decode workload
-    wd = synth.WORKLOADS["decode_256x32"]
-    nsteps = args.warmup + args.steps
-    wd = wd.with_(decode_steps=nsteps)
+    # 256 sequences x 32 heads; the states come from a 2048-token prefill, then each step of
+    # the benchmark runs the workload's consecutive decode steps (one token per sequence and
+    # head per step, the state updated in place and read back by the next step)
+    nd = args.decode_steps
+    wd = synth.WORKLOADS["decode_256x32"].with_(decode_steps=nd)
     t0 = time.perf_counter()
     xd = synth.make_inputs(wd, seqs=range(args.decode_seqs))
     log(f"generated decode inputs in {time.perf_counter() - t0:.1f}s")
@@ -560,38 +638,42 @@ def main():
     del dq, dk, dv, dg, db
     tq, tk, tv = (to_dev(xd["dec_" + n], True) for n in ("q", "k", "v"))
     tg, tb = to_dev(xd["dec_g"]), to_dev(xd["dec_beta"])
+    dec_tok = {n: xd["dec_" + n][:args.cpu_decode_steps] for n in ("q", "k", "v", "g", "beta")}
+    del xd
+    tokens = [(tq[j], tk[j], tv[j], tg[j], tb[j]) for j in range(nd)]
     to = torch.empty((N, H, V), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     log("inputs resident in HBM")
 
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(ev=None):
         if ev:
             ev[0].record(stream)
         kda.kda_chunk_fwd(pq, pk, pv, pg, pb, final_state=pS, o=po, workspace=pws)
         if ev:
             ev[1].record(stream)
-        kda.kda_decode_step(tq[i], tk[i], tv[i], tg[i], tb[i], state, o=to)
+        for t in tokens:
+            kda.kda_decode_step(*t, state, o=to)
         if ev:
             ev[2].record(stream)
 
-    for i in range(args.warmup):
-        step(i)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(evs[i])
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    blk_ms = [e[1].elapsed_time(e[2]) for e in evs]
     pre_avg = sum(pre_ms) / len(pre_ms)
-    dec_avg = sum(dec_ms) / len(dec_ms)
+    dec_avg = sum(blk_ms) / len(blk_ms) / nd   # ms per decode step, over blocks of nd steps
 
     tok_s = T / (pre_avg * 1e-3)
     p_bytes = T * H * prefill_bytes_per_token_head(K, V) + H * K * V * 4  # + final state
@@ -601,6 +683,7 @@ def main():
     d_gbs = d_bytes / (dec_avg * 1e-3) / 1e9
 
     traffic = load_traffic(p_bytes)
+    d_traffic = load_traffic(d_bytes, DECODE_TRAFFIC_FILE, DECODE_SRC) if N == 256 else None
     res = {
         "metric": METRIC,
         "value": round(tok_s, 1),
@@ -615,11 +698,11 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": "prefill_128k_h32 + decode_256x32",
+            "workload": f"prefill_128k_h32 + decode_256x32 ({nd} consecutive steps)",
             "prefill": {"B": 1, "T": T, "H": H, "dk": K, "dv": V, "chunk": C,
                         "inputs": "bf16 q/k/v, f32 g/beta", "outputs": "f32 o and final state"},
             "decode": {"N": N, "H": H, "dk": K, "dv": V, "state": "f32, updated in place",
-                       "state_init": "2048-token prefill"},
+                       "state_init": "2048-token prefill", "steps_per_step": nd},
             "compute": "fp16 matrix-core operands, f32 accumulation and state",
         },
         "roofline": {
@@ -636,6 +719,8 @@ def main():
         },
         "decode": {
             "kernel": "kda_decode_step (decode_256x32)",
+            "protocol": f"{nd} consecutive steps between one pair of events (each step reads the "
+                        "state the previous one wrote)",
             "avg_launch_us": round(dec_avg * 1e3, 2),
             "steps_per_s": round(1e3 / dec_avg, 1),
             "tokens_per_s": round(N * 1e3 / dec_avg, 1),
@@ -643,19 +728,21 @@ def main():
             "peak_gbs": HBM_PEAK_GBS,
             "frac": round(d_gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_step": d_bytes,
+            "traffic": d_traffic,
         },
         "cpu_baseline": None,
         "other_workloads": None,
     }
     if not args.no_extra:
-        del pq, pk, pv, pg, pb, po, pws, tq, tk, tv, tg, tb
+        del pq, pk, pv, pg, pb, po, pws, tq, tk, tv, tg, tb, tokens
         res["other_workloads"] = other_workloads(kda, synth, to_dev, torch, np, log, state)
         mp = res["other_workloads"]["measured_peaks"]
-        res["roofline"]["frac_of_measured_peak"] = round(res["roofline"]["achieved"] / mp["hbm_gbs"], 4)
-        res["decode"]["frac_of_measured_peak"] = round(res["decode"]["achieved_gbs"] / mp["hbm_gbs"], 4)
+        res["roofline"]["frac_of_measured_peak"] = round(res["roofline"]["achieved"] / mp["hbm_read_gbs"], 4)
+        res["decode"]["frac_of_measured_peak"] = round(res["decode"]["achieved_gbs"] / mp["hbm_rmw_gbs"], 4)
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(xp, min(args.cpu_sample_tokens, T))
+        res["cpu_baseline"]["decode"] = cpu_baseline_decode(dec_tok, N, H, K, V)
     print(json.dumps(res), flush=True)
 
 

@@ -133,15 +133,18 @@ size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk
     return kda::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk, in_dtype, num_seqs);
 }
 
-kda_status kda_chunk_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
-                         int32_t in_dtype, float scale,
-                         const void *q, const void *k, const void *v,
-                         const float *g, const float *beta, const float *initial_state,
-                         const float *d_o, const float *d_final_state,
-                         float *dq, float *dk, float *dv, float *dg, float *dbeta,
-                         float *d_initial_state,
-                         const int32_t *cu_seqlens, int32_t num_seqs,
-                         void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of kda_chunk_bwd's arguments other than the workspace, before any HIP call; fills
+// `a` (all but the workspace) on success.
+kda_status check_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                     int32_t in_dtype, float scale, const void *q, const void *k, const void *v,
+                     const float *g, const float *beta, const float *initial_state,
+                     const float *d_o, const float *d_final_state, float *dq, float *dk, float *dv,
+                     float *dg, float *dbeta, float *d_initial_state, const int32_t *cu_seqlens,
+                     int32_t num_seqs, kda::BwdArgs &a) {
     if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || chunk < 1)
         return fail(KDA_ERR_INVALID_ARGUMENT, "sizes must be positive (B=%d T=%d H=%d Dk=%d Dv=%d chunk=%d)",
                     B, T, H, Dk, Dv, chunk);
@@ -160,19 +163,12 @@ kda_status kda_chunk_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv
     if (tokens > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
         return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, g, beta, d_o, dq, dk, dv, dg and dbeta are required");
     const void *ptrs[] = {q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg, dbeta,
-                          d_initial_state, cu_seqlens, workspace};
+                          d_initial_state, cu_seqlens};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
     if (!kda::chunk_bwd_supported(in_dtype, chunk, Dk, Dv))
         return fail(KDA_ERR_UNSUPPORTED, "no backward instantiation for in_dtype=%d chunk=%d Dk=%d Dv=%d",
                     in_dtype, chunk, Dk, Dv);
-    const size_t need = kda::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk, in_dtype, num_seqs);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "kda_chunk_bwd needs %zu workspace bytes (got %zu)", need,
-                    workspace ? workspace_bytes : (size_t)0);
-    if (num_seqs == 0) return ok();
-
-    kda::BwdArgs a;
     a.n_seqs = num_seqs;
     a.seq_len = T;
     a.cu_seqlens = cu_seqlens;
@@ -192,8 +188,37 @@ kda_status kda_chunk_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv
     a.dg = dg;
     a.dbeta = dbeta;
     a.ds0 = d_initial_state;
-    a.ws = static_cast<float *>(workspace);
+    a.ws = nullptr;
     a.nslots = num_seqs + (tokens + chunk - 1) / chunk;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                         int32_t in_dtype, float scale,
+                         const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *initial_state,
+                         const float *d_o, const float *d_final_state,
+                         float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                         float *d_initial_state,
+                         const int32_t *cu_seqlens, int32_t num_seqs,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    kda::BwdArgs a;
+    const kda_status st = check_bwd(B, T, H, Dk, Dv, chunk, in_dtype, scale, q, k, v, g, beta, initial_state,
+                                    d_o, d_final_state, dq, dk, dv, dg, dbeta, d_initial_state, cu_seqlens,
+                                    num_seqs, a);
+    if (st != KDA_OK) return st;
+    if (workspace && !aligned16(workspace))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    const size_t need = kda::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk, in_dtype, num_seqs);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "kda_chunk_bwd needs %zu workspace bytes (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (num_seqs == 0) return ok();
+    a.ws = static_cast<float *>(workspace);
     return hip_status(kda::launch_chunk_bwd(in_dtype, chunk, Dk, Dv, a, static_cast<hipStream_t>(stream)),
                       "kda_chunk_bwd launch");
 }
@@ -508,6 +533,23 @@ kda_status kda_probe_copy(const void *src, void *dst, size_t bytes, void *stream
         return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
     return hip_status(kda::launch_probe_copy(src, dst, (int64_t)bytes, static_cast<hipStream_t>(stream)),
                       "kda_probe_copy launch");
+}
+
+kda_status kda_probe_read(const void *src, size_t bytes, void *stream) {
+    if (!src || bytes == 0 || bytes % 16 != 0 || bytes > ((size_t)1 << 40))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "src and a positive multiple of 16 bytes are required");
+    if (!aligned16(src)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    return hip_status(kda::launch_probe_read(src, (int64_t)bytes, static_cast<hipStream_t>(stream)),
+                      "kda_probe_read launch");
+}
+
+kda_status kda_probe_rmw(void *buf, size_t bytes, float factor, void *stream) {
+    if (!buf || bytes == 0 || bytes % 16 != 0 || bytes > ((size_t)1 << 40))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "buf and a positive multiple of 16 bytes are required");
+    if (!aligned16(buf)) return fail(KDA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    if (!std::isfinite(factor)) return fail(KDA_ERR_INVALID_ARGUMENT, "factor must be finite");
+    return hip_status(kda::launch_probe_rmw(buf, (int64_t)bytes, factor, static_cast<hipStream_t>(stream)),
+                      "kda_probe_rmw launch");
 }
 
 static kda_status probe_mfma(int32_t bf16, int32_t shape, int32_t iters, int32_t blocks, float *sink,

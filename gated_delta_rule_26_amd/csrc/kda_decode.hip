@@ -14,11 +14,14 @@
 // One workgroup owns one (sequence, head) state. Threads tile the state as rows x float4
 // columns, so every wave reads and writes whole contiguous 512-byte rows; each thread keeps
 // its Dk*Dv/NT values in registers between the read and the write. The read is non-temporal
-// (measured faster, both when steps alternate with other kernels and back to back); the
-// write is not (a non-temporal write measured slower when steps alternate with other
-// kernels). Both column reductions (p and r) are finished in the same sweep with cross-lane
-// shuffles and one LDS exchange between waves, then the rank-1 update is applied to the
-// values still in registers.
+// and so is the write: with 1000 steps back to back (each step reads the state the previous
+// one has just written) both hints together reach the device's in-place read-modify-write
+// rate for 64 KB per workgroup, about 5.6-5.7 TB/s, against about 5.3 TB/s with plain stores.
+// (Splitting a state's value columns over four workgroups, exact since column j of the update
+// needs only column j of S, measured slower: 128-byte row pieces 512 bytes apart instead of
+// contiguous rows.) Both column reductions (p and r) are finished in the same sweep with
+// cross-lane shuffles and one LDS exchange between waves, then the rank-1 update is applied
+// to the values still in registers.
 //
 // Fused layer steps (kda_decode_step_fused): the gate from its pre-activation,
 // g = -exp(A_log[h]) softplus(x + dt_bias[h, c]); q and k normalised, which only rescales the
@@ -50,8 +53,9 @@ __device__ __forceinline__ f32x4 shfl_xor4(f32x4 x, int m) {
 }
 
 // MULTI: L = a.L tokens per sequence; otherwise one (the decode step: a compile-time single
-// iteration keeps the state out of loop-carried registers).
-template <typename Tin, int DK, int DV, bool MULTI>
+// iteration keeps the state out of loop-carried registers). FUSED: the layer steps of a.f
+// (otherwise compiled out: the core step carries no branches or registers for them).
+template <typename Tin, int DK, int DV, bool MULTI, bool FUSED>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     using Sh = DecodeShape<DK, DV>;
     constexpr int TPR = Sh::TPR, RPP = Sh::RPP, NT = Sh::NT, NPASS = Sh::NPASS;
@@ -67,56 +71,59 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     const int tid = threadIdx.x;
     const int64_t item = blockIdx.x;  // n * H + h
-    const int64_t n = item / a.H;
-    const int h = (int)(item % a.H);
+    // the sequence and head are needed only for several tokens per call (their rows) and for
+    // the fused gate's per-head parameters: one token's row is the item itself
+    const int64_t n = MULTI ? item / a.H : 0;
+    const int h = MULTI || FUSED ? (int)(item % a.H) : 0;
     float *S = a.state + item * (int64_t)(DK * DV);
     const int cg = tid % TPR, rr = tid / TPR;
     const int lane = tid & 63, wave = tid >> 6;
-    const float rate = a.f.gx ? expf(a.f.A_log[h]) : 0.f;
-    const float gbias = (a.f.gx && tid < DK) ? a.f.dt_bias[h * DK + tid] : 0.f;
-    if (a.f.og && tid < DV) sw[tid] = a.f.ow[tid];
+    const bool fgate = FUSED && a.f.gx, fnorm = FUSED && a.f.og, fqk = FUSED && a.f.norm_qk;
+    const float rate = fgate ? expf(a.f.A_log[h]) : 0.f;
+    const float gbias = (fgate && tid < DK) ? a.f.dt_bias[h * DK + tid] : 0.f;
+    if (fnorm && tid < DV) sw[tid] = a.f.ow[tid];
 
     // token t of this sequence is row (n * L + t) * H + h of the [N, L, H, D] inputs; the
     // next token's values are loaded into registers while the current one computes
     const int L = MULTI ? a.L : 1;
-    auto row = [&](int t) { return (n * L + t) * a.H + h; };
+    auto row = [&](int t) { return MULTI ? (n * L + t) * a.H + h : item; };
     float nk = 0.f, nq = 0.f, ng = 0.f, nv = 0.f, nz = 0.f;
     auto fetch = [&](int t) {
         const int64_t r = row(t);
         if (tid < DK) {
             nk = to_f32(static_cast<const Tin *>(a.k)[r * DK + tid]);
             nq = to_f32(static_cast<const Tin *>(a.q)[r * DK + tid]);
-            ng = a.f.gx ? to_f32(static_cast<const Tin *>(a.f.gx)[r * DK + tid]) : a.g[r * DK + tid];
+            ng = fgate ? to_f32(static_cast<const Tin *>(a.f.gx)[r * DK + tid]) : a.g[r * DK + tid];
         }
         if (tid < DV) {
             nv = to_f32(static_cast<const Tin *>(a.v)[r * DV + tid]);
-            if (a.f.og) nz = to_f32(static_cast<const Tin *>(a.f.og)[r * DV + tid]);
+            if (fnorm) nz = to_f32(static_cast<const Tin *>(a.f.og)[r * DV + tid]);
         }
     };
     auto stage = [&](int b) {
         if (tid < DK) {
             sk[b][tid] = nk;
             sq[b][tid] = a.scale * nq;
-            sa[b][tid] = __expf(a.f.gx ? -rate * softplus_f(ng + gbias) : ng);
+            sa[b][tid] = __expf(fgate ? -rate * softplus_f(ng + gbias) : ng);
         }
         if (tid < DV) {
             sv[b][tid] = nv;
-            if (a.f.og) sz[b][tid] = nz;
+            if (fnorm) sz[b][tid] = nz;
         }
     };
 
+    // the state's loads go out first: they depend on nothing, and the token's own loads and
+    // staging then overlap them
     f32x4 s[NPASS];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p)
+        s[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (p * RPP + rr) * DV + 4 * cg));
     fetch(0);
     for (int t = 0; t < L; ++t) {
         const int b = t & 1;
         stage(b);
         if (t + 1 < L) fetch(t + 1);
         __syncthreads();
-        if (t == 0) {
-#pragma unroll
-            for (int p = 0; p < NPASS; ++p)
-                s[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (p * RPP + rr) * DV + 4 * cg));
-        }
 
         if (wave == 0) {  // scale * (q . k) and the norms, off the critical path of the state sweep
             float acc = 0.f, kk = 0.f, qq = 0.f;
@@ -132,8 +139,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             }
             if (lane == 0) {
                 // sq holds scale * q, so 1/||q|| = |scale| / ||sq|| (any scale, zero included)
-                const float rk = a.f.norm_qk ? rsqrt_or_zero(kk) : 1.f;
-                const float rq = a.f.norm_qk ? fabsf(a.scale) * rsqrt_or_zero(qq) : 1.f;
+                const float rk = fqk ? rsqrt_or_zero(kk) : 1.f;
+                const float rq = fqk ? fabsf(a.scale) * rsqrt_or_zero(qq) : 1.f;
                 sqk[b][0] = acc * rk * rq;
                 sqk[b][1] = rk;
                 sqk[b][2] = rq;
@@ -166,13 +173,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             R += red[w][1][cg];
         }
         const float bt = a.beta[row(t)];
-        const float rk = sqk[b][1], rq = sqk[b][2];
+        const float rk = FUSED ? sqk[b][1] : 1.f, rq = FUSED ? sqk[b][2] : 1.f;
         const f32x4 vv = *reinterpret_cast<const f32x4 *>(&sv[b][4 * cg]);
         const f32x4 u = bt * (vv - rk * P);
         if (rr == 0) {
             const f32x4 ov = rq * R + sqk[b][0] * u;
             const int64_t oo = row(t) * DV + 4 * cg;
-            if (a.f.og) {  // gated RMSNorm over the Dv outputs, held by the TPR lanes of row 0
+            if (fnorm) {  // gated RMSNorm over the Dv outputs, held by the TPR lanes of row 0
                 float ss = ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w;
 #pragma unroll
                 for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m);
@@ -201,17 +208,24 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
 #pragma unroll
     for (int p = 0; p < NPASS; ++p)
-        *reinterpret_cast<f32x4 *>(S + (p * RPP + rr) * DV + 4 * cg) = s[p];
+        __builtin_nontemporal_store(s[p], reinterpret_cast<f32x4 *>(S + (p * RPP + rr) * DV + 4 * cg));
 }
 
 template <typename Tin, int D>
 hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     using Sh = DecodeShape<D, D>;
     const int64_t items = (int64_t)a.N * a.H;
-    if (a.L > 1)
-        hipLaunchKernelGGL((decode_kernel<Tin, D, D, true>), dim3((unsigned)items), dim3(Sh::NT), 0, stream, a);
+    // the core step and the core recurrent mode share one arithmetic (no fused steps compiled
+    // in), so L tokens in one call give the bits of L successive decode steps
+    const bool fused = a.f.gx || a.f.og || a.f.norm_qk;
+    if (a.L > 1 && fused)
+        hipLaunchKernelGGL((decode_kernel<Tin, D, D, true, true>), dim3((unsigned)items), dim3(Sh::NT), 0, stream, a);
+    else if (a.L > 1)
+        hipLaunchKernelGGL((decode_kernel<Tin, D, D, true, false>), dim3((unsigned)items), dim3(Sh::NT), 0, stream, a);
+    else if (fused)
+        hipLaunchKernelGGL((decode_kernel<Tin, D, D, false, true>), dim3((unsigned)items), dim3(Sh::NT), 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_kernel<Tin, D, D, false>), dim3((unsigned)items), dim3(Sh::NT), 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<Tin, D, D, false, false>), dim3((unsigned)items), dim3(Sh::NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -4,6 +4,11 @@
 // * copy: dst = src over `bytes`, 16-byte vectors, non-temporal loads (the state stream of the
 //   decode step reads the same way): the practical HBM bandwidth of a kernel that reads each
 //   byte once and writes each byte once.
+// * read: a read-only stream (non-temporal 16-byte loads, 64 KB per workgroup), the practical
+//   read bandwidth: the bound of a read-mostly kernel such as the prefill.
+// * rmw: an in-place read-modify-write stream (x *= factor, non-temporal loads and stores,
+//   16 KB per workgroup): the access pattern of the decode step's state, and its practical
+//   bound.
 // * fp16 / bf16 matrix cores: every wave runs a loop of independent matrix-core products on
 //   several accumulators (16x16x32 or 32x32x16 instructions, the same flops per iteration),
 //   the operands held in registers; the accumulators are written out at the end so nothing is
@@ -33,6 +38,42 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(const f32x4 *__restrict
         if (i < n) dst[i] = v[u];
     }
 }
+
+// Read and in-place read-modify-write streams: each workgroup of 256 threads owns one slab of
+// NV * 4 KB, issues all its 16-byte non-temporal loads, then (RMW) writes the slab back with
+// non-temporal stores. Buffer resources bound every slab by the array's end (loads past it
+// read zero, stores past it are dropped). Measured on this part: reads peak with 64 KB slabs,
+// in-place read-modify-write with 16 KB slabs (more workgroups in flight per CU).
+template <int NV> __device__ __forceinline__ rsrc_t slab_rsrc(const void *base, int64_t bytes) {
+    const int64_t start = (int64_t)blockIdx.x * NV * 4096;
+    const int64_t left = bytes - start;
+    return make_rsrc(static_cast<const char *>(base) + start, (uint32_t)(left < NV * 4096 ? left : NV * 4096));
+}
+
+template <int NV> __global__ __launch_bounds__(256) void probe_read_kernel(const void *src, int64_t bytes) {
+    const rsrc_t r = slab_rsrc<NV>(src, bytes);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < NV; ++p)
+        acc += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (p * 256 + threadIdx.x) * 16, 0, 2));
+    // the sum is consumed by an empty statement the compiler must keep, so every load is
+    // issued and waited for, and nothing is written
+    __asm__ volatile("" : : "v"(acc.x), "v"(acc.y), "v"(acc.z), "v"(acc.w));
+}
+
+template <int NV> __global__ __launch_bounds__(256) void probe_rmw_kernel(void *buf, int64_t bytes, float factor) {
+    const rsrc_t r = slab_rsrc<NV>(buf, bytes);
+    f32x4 v[NV];
+#pragma unroll
+    for (int p = 0; p < NV; ++p)
+        v[p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (p * 256 + threadIdx.x) * 16, 0, 2));
+#pragma unroll
+    for (int p = 0; p < NV; ++p)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[p] * factor), r, (p * 256 + threadIdx.x) * 16, 0, 2);
+}
+
+constexpr int kReadSlab = 16;  // 64 KB per workgroup
+constexpr int kRmwSlab = 4;    // 16 KB per workgroup
 
 constexpr int kProbeAcc = 8;
 
@@ -96,6 +137,18 @@ hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStrea
     const int64_t n = bytes / 16, blocks = (n + 256 * kCopyVec - 1) / (256 * kCopyVec);
     hipLaunchKernelGGL(probe_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const f32x4 *>(src), static_cast<f32x4 *>(dst), n);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void *src, int64_t bytes, hipStream_t stream) {
+    const int64_t blocks = (bytes + kReadSlab * 4096 - 1) / (kReadSlab * 4096);
+    hipLaunchKernelGGL((probe_read_kernel<kReadSlab>), dim3((unsigned)blocks), dim3(256), 0, stream, src, bytes);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_rmw(void *buf, int64_t bytes, float factor, hipStream_t stream) {
+    const int64_t blocks = (bytes + kRmwSlab * 4096 - 1) / (kRmwSlab * 4096);
+    hipLaunchKernelGGL((probe_rmw_kernel<kRmwSlab>), dim3((unsigned)blocks), dim3(256), 0, stream, buf, bytes, factor);
     return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@
  * core (kda_chunk_fwd_fused, kda_decode_step_fused); two more run the layer's short
  * convolution with its conv state (kda_short_conv_fwd, kda_short_conv_update); kda_chunk_bwd
  * is the backward pass of kda_chunk_fwd (training); and two measurement probes report the
- * device's practical copy and matrix-core peaks (kda_probe_copy, kda_probe_mfma_f16/bf16, at the
+ * device's practical bandwidth and matrix-core peaks (kda_probe_copy/read/rmw, kda_probe_mfma_f16/bf16, at the
  * end of this file):
  *   kda_chunk_fwd    prefill: the chunkwise-parallel form of the recurrence ([KV-cache page]
  *                    section 3: chunk_size 64; section 6: chunked parallel form with a WY
@@ -139,11 +139,20 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk
  *   (KDA_BF16, 64, 128)   bf16 inputs; fp16 matrix-core operands (decay factors balanced
  *                         by powers of two into fp16's range), float32 accumulation and
  *                         state; exact for any finite g <= 0 (chunks whose 16-token decay
- *                         falls below e^-12 sum their diagonal blocks pair by pair)
- *   (KDA_F32, 16, 16), (KDA_F32, 16, 32), (KDA_F32, 64, 32), (KDA_F32, 64, 64)
- *                         float32 matrix-core path (reference-precision instantiations;
- *                         D = 32 runs at both chunk sizes, which give the same result up
- *                         to rounding)
+ *                         falls below e^-12 sum their diagonal blocks pair by pair).
+ *                         Range precondition (not checked): the state S, the intra-chunk
+ *                         values U~ = T Diag(beta) V and U = U~ - W S, and v itself enter the
+ *                         matrix cores as fp16, so their magnitudes must stay below fp16's
+ *                         largest value, 65504; beyond it the outputs turn non-finite. With
+ *                         unit-norm keys and beta in [0, 1] the state stays within a small
+ *                         multiple of max |v| and of the initial state (the erase term has
+ *                         spectral norm <= 1), so |v| and |initial_state| up to about 10^3 are
+ *                         far inside it. The float32 instantiations have no such limit.
+ *   (KDA_F32, 16, 16), (KDA_F32, 16, 32), (KDA_F32, 32, 128), (KDA_F32, 64, 32),
+ *   (KDA_F32, 64, 64)     float32 matrix-core path (reference-precision instantiations;
+ *                         D = 32 runs at two chunk sizes, which give the same result up to
+ *                         rounding; at D = 128 the float32 operands fit one CU's LDS with
+ *                         32-token chunks)
  * Other combinations return KDA_ERR_UNSUPPORTED.
  */
 kda_status kda_chunk_fwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
@@ -331,6 +340,13 @@ kda_status kda_short_conv_update(int32_t N, int32_t C, int32_t W, int32_t dtype,
  * kda_probe_copy - dst = src over `bytes` (a multiple of 16; both 16-byte aligned device
  *   pointers, not overlapping), read with non-temporal 16-byte loads: the HBM bandwidth of a
  *   kernel that reads and writes each byte once is 2 * bytes / time.
+ * kda_probe_read - reads `bytes` at src (a multiple of 16, 16-byte aligned) with
+ *   non-temporal 16-byte loads, 64 KB per workgroup, and writes nothing: the practical read
+ *   bandwidth is bytes / time.
+ * kda_probe_rmw - buf *= factor in place over `bytes` (a multiple of 16, 16-byte aligned),
+ *   non-temporal loads and stores, 16 KB per workgroup: the access pattern of the decode
+ *   step's state (each byte read once, then written once in place), whose practical bandwidth
+ *   is 2 * bytes / time.
  * kda_probe_mfma_f16 - `blocks` workgroups of 256 threads each run `iters` iterations of
  *   independent fp16 matrix-core products per wave: eight v_mfma_f32_16x16x32_f16 (shape 0)
  *   or four v_mfma_f32_32x32x16_f16 (shape 1), the same flops; sink [blocks * 256] float32
@@ -341,6 +357,8 @@ kda_status kda_short_conv_update(int32_t N, int32_t C, int32_t W, int32_t dtype,
  * Errors as kda_chunk_fwd (invalid sizes or pointers, nothing launched).
  */
 kda_status kda_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
+kda_status kda_probe_read(const void *src, size_t bytes, void *stream);
+kda_status kda_probe_rmw(void *buf, size_t bytes, float factor, void *stream);
 kda_status kda_probe_mfma_f16(int32_t shape, int32_t iters, int32_t blocks, float *sink, void *stream);
 kda_status kda_probe_mfma_bf16(int32_t shape, int32_t iters, int32_t blocks, float *sink, void *stream);
 double kda_probe_mfma_f16_flops(int32_t iters, int32_t blocks);

@@ -31,6 +31,8 @@ def test_algorithmic_counts():
     # 6KV + 3CK + 2CV + C^2/3 per token-head at C = 64
     assert abs(bench.prefill_flops_per_token_head(128, 128, 64) - (6 * 128 * 128 + 3 * 64 * 128 + 2 * 64 * 128 + 64 * 64 / 3)) < 1e-9
     assert round(bench.prefill_flops_per_token_head(128, 128, 64)) == 140_629
+    # backward: 9CK + 5CV + 16KV + C^2 per token-head at C = 64, K = V = 128
+    assert bench.bwd_flops_per_token_head(128, 128, 64) == 9 * 64 * 128 + 5 * 64 * 128 + 16 * 128 * 128 + 64 * 64 == 380_928
 
 
 def test_kernel_labels():

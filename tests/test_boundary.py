@@ -339,12 +339,14 @@ def test_chunk_bwd_empty_work_is_ok_without_launch(lib):
                dk=None, dv=None, dg=None, db=None, ws=None) == OK
 
 
-@pytest.mark.parametrize("args,status", [
-    ((None, P, 1024), INVALID), ((P, None, 1024), INVALID), ((P, P, 0), INVALID),
-    ((P, P, 1000), INVALID), ((MIS, P, 1024), INVALID), ((P, MIS, 1024), INVALID),
+@pytest.mark.parametrize("call", [
+    lambda lib: lib.kda_probe_read(None, 1024, None), lambda lib: lib.kda_probe_read(P, 0, None),
+    lambda lib: lib.kda_probe_read(P, 1000, None), lambda lib: lib.kda_probe_read(MIS, 1024, None),
+    lambda lib: lib.kda_probe_rmw(None, 1024, 1.0, None), lambda lib: lib.kda_probe_rmw(P, 1000, 1.0, None),
+    lambda lib: lib.kda_probe_rmw(MIS, 1024, 1.0, None), lambda lib: lib.kda_probe_rmw(P, 1024, float("inf"), None),
 ])
-def test_probe_copy_rejects_before_launch(lib, args, status):
-    assert lib.kda_probe_copy(*args, None) == status
+def test_probe_streams_reject_before_launch(lib, call):
+    assert call(lib) == INVALID
 
 
 def test_probe_mfma_rejects_and_counts(lib):

@@ -16,9 +16,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_bench_json_line():
-    print("[gpu-case] bench.py --steps 2 --warmup 1 --no-extra", file=sys.stderr, flush=True)
+    print("[gpu-case] bench.py --steps 2 --warmup 1 --no-extra --decode-steps 50", file=sys.stderr, flush=True)
     r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "2", "--warmup", "1",
-                        "--no-extra", "--cpu-sample-tokens", "2048"],
+                        "--no-extra", "--cpu-sample-tokens", "2048", "--decode-steps", "50",
+                        "--cpu-decode-steps", "2"],
                        capture_output=True, text=True, timeout=280, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
@@ -41,3 +42,11 @@ def test_bench_json_line():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["unit"] == "tokens/s"
     assert "2048 tokens" in cb["sample"]
+    assert cb["decode"]["unit"] == "steps/s" and cb["decode"]["value"] > 0 and "2 consecutive steps" in cb["decode"]["sample"]
+    # the decode block: consecutive steps between one pair of events, against 8 TB/s
+    dec = d["decode"]
+    assert "50 consecutive steps" in dec["protocol"] and d["config"]["decode"]["steps_per_step"] == 50
+    assert abs(dec["frac"] - dec["achieved_gbs"] / dec["peak_gbs"]) < 1e-3
+    assert abs(dec["steps_per_s"] * dec["avg_launch_us"] - 1e6) < 1e3
+    # one step: one prefill call and 50 decode steps, all inside the step's time
+    assert d["ms_per_step"] >= rl["avg_launch_ms"] + 50 * dec["avg_launch_us"] * 1e-3 * 0.99

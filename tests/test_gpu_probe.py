@@ -1,4 +1,5 @@
-"""The measurement probes on the GPU: the copy reproduces its input bit for bit; the fp16
+"""The measurement probes on the GPU: the copy reproduces its input bit for bit, the in-place
+read-modify-write scales exactly its buffer and nothing past it; the fp16
 matrix-core loop gives the sums its fixed operands imply (every product of every iteration
 was done)."""
 
@@ -19,6 +20,21 @@ def test_probe_copy_is_exact():
     kda.kda_probe_copy(src, dst)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+@pytest.mark.parametrize("n", [1 << 22, (1 << 22) + 12])
+def test_probe_rmw_is_exact_and_bounded(n):
+    """buf *= 2 in place, a power of two (exact); a ragged tail past the last full 16 KB slab
+    is scaled too, and nothing past the buffer's end is touched."""
+    torch = torch_mod()
+    big = torch.randn(n + 1024, device="cuda")
+    ref = big.clone()
+    note(f"probe rmw {n} floats")
+    kda.kda_probe_rmw(big[:n], 2.0)
+    kda.kda_probe_read(big[:n])
+    torch.cuda.synchronize()
+    assert torch.equal(big[:n], 2 * ref[:n])
+    assert torch.equal(big[n:], ref[n:])
 
 
 def probe_expected(shape, iters, blocks, bf16=False):

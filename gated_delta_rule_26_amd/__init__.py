@@ -15,7 +15,7 @@ import os
 
 __all__ = ["KdaError", "kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_fused",
            "kda_decode_step_fused", "kda_recurrent_fwd", "kda_short_conv_fwd", "kda_short_conv_update",
-           "kda_chunk_bwd", "check_cu_seqlens", "chunk_fwd_workspace_bytes", "chunk_bwd_workspace_bytes", "load_library", "KDA_F32", "KDA_BF16"]
+           "kda_chunk_bwd", "kda_chunk_bwd_noalloc", "check_cu_seqlens", "chunk_fwd_workspace_bytes", "chunk_bwd_workspace_bytes", "load_library", "KDA_F32", "KDA_BF16"]
 
 KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
@@ -78,6 +78,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kda_chunk_bwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, f32,
                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   vp, i32, vp, sz, vp]
+    lib.kda_chunk_bwd_noalloc.restype = i32
+    lib.kda_chunk_bwd_noalloc.argtypes = [i32, i32, i32, i32, i32, i32, i32, f32,
+                                          vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          vp, i32, vp]
     lib.kda_probe_copy.restype = i32
     lib.kda_probe_copy.argtypes = [vp, vp, sz, vp]
     lib.kda_probe_read.restype = i32
@@ -364,6 +368,46 @@ def kda_chunk_bwd(q, k, v, g, beta, do, *, initial_state=None, dfinal_state=None
                            workspace.numel(), _stream(stream))
     _check(lib, st)
     return dq, dk, dv, dg, db, ds0
+
+
+@_on_stream
+def kda_chunk_bwd_noalloc(q, k, v, g, beta, do, *, grads, dinitial_state=None, initial_state=None,
+                          dfinal_state=None, cu_seqlens=None, chunk: int = 64, scale: float = 1.0,
+                          stream=None):
+    """Backward pass with the library's fixed scratch in place of a workspace (C:
+    kda_chunk_bwd_noalloc), for callers that cannot allocate: the five gradient tensors
+    (dq, dk, dv, dg, dbeta) must be given in ``grads``, and ``dinitial_state`` (float32
+    [N, H, Dk, Dv]) if that gradient is wanted; nothing is allocated. Arguments otherwise as
+    ``kda_chunk_bwd``; returns (dq, dk, dv, dg, dbeta, dinitial_state)."""
+    import torch
+    lib = load_library()
+    B, T, N, H, Dk, Dv = _prefill_layout(q, k, v, beta, cu_seqlens)
+    _req(g, "g", torch.float32)
+    if g.shape != q.shape:
+        raise ValueError("g must have q's shape")
+    _req(do, "do", torch.float32)
+    if do.shape != v.shape:
+        raise ValueError("do must have v's shape")
+    _prefill_states(q, N, H, Dk, Dv, initial_state, None, False)
+    if dfinal_state is not None:
+        _req(dfinal_state, "dfinal_state", torch.float32)
+        if tuple(dfinal_state.shape) != (N, H, Dk, Dv):
+            raise ValueError(f"dfinal_state must be [{N}, {H}, {Dk}, {Dv}]")
+    if dinitial_state is not None:
+        _req(dinitial_state, "dinitial_state", torch.float32)
+        if tuple(dinitial_state.shape) != (N, H, Dk, Dv):
+            raise ValueError(f"dinitial_state must be [{N}, {H}, {Dk}, {Dv}]")
+    dq, dk, dv, dg, db = grads
+    for t, like, nm in ((dq, q, "dq"), (dk, q, "dk"), (dv, v, "dv"), (dg, q, "dg"), (db, beta, "dbeta")):
+        _req(t, nm, torch.float32)
+        if t.shape != like.shape:
+            raise ValueError(f"{nm} must have shape {tuple(like.shape)}")
+    st = lib.kda_chunk_bwd_noalloc(B, T, H, Dk, Dv, chunk, _dtype_code(q), float(scale),
+                                   _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                   _ptr(do), _ptr(dfinal_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                   _ptr(db), _ptr(dinitial_state), _ptr(cu_seqlens), N, _stream(stream))
+    _check(lib, st)
+    return dq, dk, dv, dg, db, dinitial_state
 
 
 def kda_probe_copy(src, dst, stream=None):

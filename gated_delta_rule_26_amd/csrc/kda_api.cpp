@@ -223,6 +223,34 @@ kda_status kda_chunk_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv
                       "kda_chunk_bwd launch");
 }
 
+kda_status kda_chunk_bwd_noalloc(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                                 int32_t in_dtype, float scale,
+                                 const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta, const float *initial_state,
+                                 const float *d_o, const float *d_final_state,
+                                 float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                                 float *d_initial_state,
+                                 const int32_t *cu_seqlens, int32_t num_seqs, void *stream) {
+    kda::BwdArgs a;
+    const kda_status st = check_bwd(B, T, H, Dk, Dv, chunk, in_dtype, scale, q, k, v, g, beta, initial_state,
+                                    d_o, d_final_state, dq, dk, dv, dg, dbeta, d_initial_state, cu_seqlens,
+                                    num_seqs, a);
+    if (st != KDA_OK) return st;
+    const size_t need = kda::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk, in_dtype, num_seqs);
+    if (need > kda::kBwdScratchBytes)
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
+                    "kda_chunk_bwd_noalloc: this problem needs %zu bytes of records, beyond the fixed "
+                    "scratch of %zu bytes (call kda_chunk_bwd with a workspace instead)",
+                    need, kda::kBwdScratchBytes);
+    if (num_seqs == 0) return ok();
+    void *scratch = nullptr;
+    const kda_status ss = hip_status(kda::bwd_scratch(&scratch), "kda_chunk_bwd_noalloc scratch lookup");
+    if (ss != KDA_OK) return ss;
+    a.ws = static_cast<float *>(scratch);
+    return hip_status(kda::launch_chunk_bwd(in_dtype, chunk, Dk, Dv, a, static_cast<hipStream_t>(stream)),
+                      "kda_chunk_bwd_noalloc launch");
+}
+
 kda_status kda_decode_step(int32_t N, int32_t H, int32_t Dk, int32_t Dv,
                            int32_t in_dtype, int32_t out_dtype, float scale,
                            const void *q, const void *k, const void *v,

@@ -30,10 +30,20 @@
 //             reverse running sum of dG; the partial gradients never leave the registers.
 // Chunks of a packed batch are numbered by slot n + floor(start_n / C) + j (sequence n, chunk j),
 // which is unique and below N + ceil(tokens / C), so the records need no host-side lengths.
+#include <atomic>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
+
+// The records of kda_chunk_bwd_noalloc, for callers that cannot allocate (code under graph
+// capture, tight training loops): one copy of this array per device the library runs on,
+// held until the process ends. In host code the name stands for a host-side shadow, not for
+// device memory: host code uses only the address bwd_scratch() looks up. Calls that overlap
+// on one device share it and race.
+static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
+
 namespace {
 
 // Per-(chunk, head) record in the workspace (float offsets; rows are tokens of the chunk).
@@ -1073,6 +1083,23 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
 template <int C, int DK, int DV> constexpr int64_t rec_floats() { return BRec<C, DK, DV>::FLOATS; }
 
 }  // namespace
+
+hipError_t bwd_scratch(void **ptr) {
+    static std::atomic<void *> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void *p = cache[dev].load(std::memory_order_acquire);
+    if (!p) {  // first use on this device, with the device current: its copy's address
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        cache[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 bool chunk_bwd_supported(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv) {
     if (chunk == 64 && Dk == 128 && Dv == 128) return in_dtype == 0 || in_dtype == 1;

@@ -123,6 +123,11 @@ hipError_t launch_probe_rmw(void *buf, int64_t bytes, float factor, hipStream_t 
 hipError_t launch_probe_mfma(int32_t bf16, int32_t shape, int32_t iters, int32_t blocks, float *sink,
                              hipStream_t stream);
 int64_t probe_mfma_flops_per_iter_and_thread();
+// Fixed scratch of kda_chunk_bwd_noalloc: a device array of this many bytes per device,
+// which holds the backward pass's records in place of a caller-provided workspace.
+constexpr size_t kBwdScratchBytes = (size_t)512 << 20;
+// Device address of the current device's scratch array (looked up once per device).
+hipError_t bwd_scratch(void **ptr);
 // The chunked backward pass: three kernels in stream order over the workspace records.
 hipError_t launch_chunk_bwd(int32_t in_dtype, int32_t chunk, int32_t Dk, int32_t Dv, const BwdArgs &a,
                             hipStream_t stream);

@@ -27,7 +27,8 @@
  * decode kernel's way; two fused variants add the KDA layer's steps on either side of the
  * core (kda_chunk_fwd_fused, kda_decode_step_fused); two more run the layer's short
  * convolution with its conv state (kda_short_conv_fwd, kda_short_conv_update); kda_chunk_bwd
- * is the backward pass of kda_chunk_fwd (training); and two measurement probes report the
+ * is the backward pass of kda_chunk_fwd (training), and kda_chunk_bwd_noalloc the same for
+ * callers that cannot allocate a workspace; and two measurement probes report the
  * device's practical bandwidth and matrix-core peaks (kda_probe_copy/read/rmw, kda_probe_mfma_f16/bf16, at the
  * end of this file):
  *   kda_chunk_fwd    prefill: the chunkwise-parallel form of the recurrence ([KV-cache page]
@@ -44,8 +45,10 @@
  * ---------------------------------------
  * - Pointers. Every tensor pointer is a DEVICE pointer (HIP device memory) owned by the
  *   caller; the library allocates nothing and keeps no per-call state (scratch space, where
- *   a call needs it, is the caller's workspace argument). Tensors are dense and
- *   contiguous with the last dimension innermost ("... h d" layout), and 16-byte aligned.
+ *   a call needs it, is the caller's workspace argument; the one exception,
+ *   kda_chunk_bwd_noalloc, uses a fixed device array the library holds instead). Tensors
+ *   are dense and contiguous with the last dimension innermost ("... h d" layout), and
+ *   16-byte aligned.
  * - Dtypes. q, k, v are KDA_F32 or KDA_BF16 (in_dtype); g (log-decay, <= 0), beta, states
  *   and o are float32 (out_dtype must be KDA_F32, except after the fused output norm); the
  *   backward pass's gradients are float32.
@@ -67,6 +70,9 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+/* Bytes of the fixed device scratch behind kda_chunk_bwd_noalloc (per device). */
+#define KDA_BWD_SCRATCH_BYTES ((size_t)512 << 20)
 
 #ifdef __cplusplus
 extern "C" {
@@ -307,6 +313,33 @@ kda_status kda_chunk_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv
                          float *d_initial_state,
                          const int32_t *cu_seqlens, int32_t num_seqs,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_chunk_bwd_noalloc - kda_chunk_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight training loops, harnesses that forbid hipMalloc): the same
+ * arguments, results and errors, minus the workspace. The per-(chunk, head) records live in a
+ * fixed device array inside the library instead, KDA_BWD_SCRATCH_BYTES (512 MiB) per device,
+ * which each device holds from the library's load until the process ends. The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine): the outputs are the
+ * caller's.
+ *   A problem whose records need more than KDA_BWD_SCRATCH_BYTES, i.e. whose
+ *   kda_chunk_bwd_workspace_bytes(...) exceeds it (at chunk 64, Dk = Dv = 128: 1128 record
+ *   slots x heads, where a sequence takes one slot more than its chunks; e.g. 4096 tokens
+ *   fit with up to 17 heads), returns KDA_ERR_WORKSPACE_TOO_SMALL with nothing launched.
+ *   Every call on one device uses that device's single array: calls that overlap on one
+ *   device (on different streams, or from several host threads) race and give wrong
+ *   results; calls in one stream's order do not. Nothing in the array needs to start at zero
+ *   (every record is written before it is read), so a call never depends on what an earlier
+ *   one left there.
+ */
+kda_status kda_chunk_bwd_noalloc(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,
+                                 int32_t in_dtype, float scale,
+                                 const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta, const float *initial_state,
+                                 const float *d_o, const float *d_final_state,
+                                 float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                                 float *d_initial_state,
+                                 const int32_t *cu_seqlens, int32_t num_seqs, void *stream);
 
 /*
  * kda_short_conv_fwd - the convolution over a prefill batch.

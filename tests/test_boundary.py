@@ -339,6 +339,50 @@ def test_chunk_bwd_empty_work_is_ok_without_launch(lib):
                dk=None, dv=None, dg=None, db=None, ws=None) == OK
 
 
+def bwd_noalloc(lib, B=1, T=64, H=2, Dk=128, Dv=128, C=64, ind=BF16, scale=1.0, q=P, k=P, v=P, g=P,
+                beta=P, s0=None, do=P, dsT=None, dq=P, dk=P, dv=P, dg=P, db=P, ds0=None, cu=None, N=None):
+    N = B if N is None else N
+    return lib.kda_chunk_bwd_noalloc(B, T, H, Dk, Dv, C, ind, scale, q, k, v, g, beta, s0, do, dsT,
+                                     dq, dk, dv, dg, db, ds0, cu, N, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), INVALID), (dict(T=-1), INVALID), (dict(H=0), INVALID), (dict(C=0), INVALID),
+    (dict(ind=5), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(B=2, cu=P, N=1), INVALID), (dict(B=2, N=1), INVALID),
+    (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(db=None), INVALID),
+    (dict(dg=MIS), INVALID), (dict(ds0=MIS), INVALID),
+    (dict(Dk=64, Dv=64), UNSUPPORTED), (dict(C=32), UNSUPPORTED),
+    # records beyond the fixed scratch: 4096 tokens x 18 heads, or 128K tokens x 32 heads
+    (dict(T=4096, H=18), WS_SMALL), (dict(T=131072, H=32), WS_SMALL),
+])
+def test_chunk_bwd_noalloc_rejects_before_launch(lib, kw, status):
+    assert bwd_noalloc(lib, **kw) == status
+    assert len(lib.kda_last_error()) > 0
+
+
+def test_chunk_bwd_noalloc_scratch_limit(lib):
+    """The fixed scratch (512 MiB) holds the records of 4096 tokens x 17 heads, not 18."""
+    limit = 512 << 20
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 4096, 17, 128, 128, 64, BF16, 1) <= limit
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 4096, 18, 128, 128, 64, BF16, 1) > limit
+    assert bwd_noalloc(lib, T=4096, H=18) == WS_SMALL
+    assert b"fixed scratch" in lib.kda_last_error()
+
+
+def test_chunk_bwd_noalloc_empty_work_is_ok_without_launch(lib):
+    assert bwd_noalloc(lib, T=0, cu=P, N=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None,
+                       dk=None, dv=None, dg=None, db=None) == OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, P, 1024), INVALID), ((P, None, 1024), INVALID), ((P, P, 0), INVALID),
+    ((P, P, 1000), INVALID), ((MIS, P, 1024), INVALID), ((P, MIS, 1024), INVALID),
+])
+def test_probe_copy_rejects_before_launch(lib, args, status):
+    assert lib.kda_probe_copy(*args, None) == status
+
+
 @pytest.mark.parametrize("call", [
     lambda lib: lib.kda_probe_read(None, 1024, None), lambda lib: lib.kda_probe_read(P, 0, None),
     lambda lib: lib.kda_probe_read(P, 1000, None), lambda lib: lib.kda_probe_read(MIS, 1024, None),

@@ -47,24 +47,35 @@ static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
 namespace {
 
 // Per-(chunk, head) record in the workspace (float offsets; rows are tokens of the chunk).
+// The operands of the state passes' products are stored split and in fragment order: each
+// 16x16 tile is 64 lane groups of 16 bytes, lane (lr, q4) holding row lr, columns 4 q4 ..
+// 4 q4 + 3 of the tile as four bf16 heads and four bf16 tails, so that one load of a wave
+// reads 1 KB in one piece.
 template <int C, int DK, int DV> struct BRec {
     static constexpr int64_t oG = 0;                  // [C][DK] G (running sum of g)
-    static constexpr int64_t oQg = oG + C * DK;       // [C][DK] scale q e^G
-    static constexpr int64_t oKd = oQg + C * DK;      // [C][DK] k e^{gC - G}
-    static constexpr int64_t oW = oKd + C * DK;       // [C][DK] W
-    static constexpr int64_t oU = oW + C * DK;        // [C][DV] U~, then U
-    static constexpr int64_t odU = oU + C * DV;       // [C][DV] dU
+    static constexpr int64_t oKd = oG + C * DK;       // [C][DK] Kd = k e^{gC - G} (split tiles)
+    static constexpr int64_t oW = oKd + C * DK;       // [C][DK] W (split tiles)
+    static constexpr int64_t oU = oW + C * DK;        // [C][DV] U~, then U (fragment order)
+    static constexpr int64_t odU = oU + C * DV;       // [C][DV] M^T dO, then dU (fragment order)
     static constexpr int64_t oEg = odU + C * DV;      // [DK]    e^{gC}
     static constexpr int64_t oA = oEg + DK;           // [C][C]  A~ (strictly lower), then dA~
-    static constexpr int64_t oM = oA + C * C;         // [C][C]  M^T (upper), then dM (lower)
+    static constexpr int64_t oM = oA + C * C;         // [C][C]  M^T (upper, split tiles)
     static constexpr int64_t oT = oM + C * C;         // [C][C]  T
-    static constexpr int64_t oKdT = oT + C * C;       // [DK][C] Kd^T
-    static constexpr int64_t oWT = oKdT + DK * C;     // [DK][C] W^T
-    static constexpr int64_t oQgT = oWT + DK * C;     // [DK][C] Qg^T
-    static constexpr int64_t oH = oQgT + DK * C;      // [DK][DV] state entering the chunk
-    static constexpr int64_t odH = oH + DK * DV;      // [DK][DV] dL/d(state leaving the chunk)
+    static constexpr int64_t oKdT = oT + C * C;       // [DK][C] Kd^T (split tiles)
+    static constexpr int64_t oWT = oKdT + DK * C;     // [DK][C] -W^T (split tiles)
+    static constexpr int64_t oQgT = oWT + DK * C;     // [DK][C] Qg^T (split tiles)
+    static constexpr int64_t oH = oQgT + DK * C;      // [DK][DV] state entering the chunk (fragment order)
+    static constexpr int64_t odH = oH + DK * DV;      // [DK][DV] Qg^T dO, then dL/d(state leaving the chunk)
+                                                      //         (fragment order)
     static constexpr int64_t FLOATS = (odH + DK * DV + 63) & ~int64_t(63);
 };
+
+// Offset (floats) of lane `lane`'s 16-byte fragment of tile (rt, ct) of a matrix stored in
+// accumulator-fragment order: tile-major over NCT column tiles, each tile 64 lanes x 4 floats,
+// lane (lr, q4) holding rows 16 rt + 4 q4 + e (e = 0..3) of column 16 ct + lr.
+template <int NCT> __device__ __forceinline__ int64_t afrag(int rt, int ct, int lane) {
+    return ((int64_t)(rt * NCT + ct) * 64 + lane) * 4;
+}
 
 // Token range [start, end) of sequence n (packed offsets clamped to [0, T]).
 __device__ __forceinline__ void seq_range(const BwdArgs &a, int n, int64_t &start, int64_t &end) {
@@ -115,6 +126,37 @@ __device__ __forceinline__ float sum16(float x) {  // over the 16 lanes of a row
 
 __device__ __forceinline__ void mma(f32x4 &acc, f32x4 a, f32x4 b) { Mma<float>::mma(acc, a, b); }
 
+// A float32 4-vector as bf16 heads and bf16 tails (head + tail equals each value to about
+// 2^-17 of it), packed in the vector's 16 bytes: [heads 0..3 | tails 0..3]. A product of two
+// split factors is three bf16 matrix-core products (tail x head, head x tail, head x head) at
+// about float32 accuracy, and bf16 products run several times faster than float32 ones.
+struct Split {
+    bf16x4 h, t;
+};
+__device__ __forceinline__ Split split(f32x4 x) {
+    Split r;
+    r.h = Mma<__bf16>::from_f32(x);
+    r.t = Mma<__bf16>::from_f32(x - Mma<__bf16>::to_f32(r.h));
+    return r;
+}
+__device__ __forceinline__ f32x4 pack(Split s) { return __builtin_bit_cast(f32x4, s); }
+__device__ __forceinline__ f32x4 split_pack(f32x4 x) { return pack(split(x)); }
+__device__ __forceinline__ Split unpack(f32x4 v) { return __builtin_bit_cast(Split, v); }
+__device__ __forceinline__ f32x4 unsplit(f32x4 v) {
+    const Split s = unpack(v);
+    return Mma<__bf16>::to_f32(s.h) + Mma<__bf16>::to_f32(s.t);
+}
+// Offset (floats) of the 16-byte group holding element (r, c) .. (r, c + 3), c % 4 == 0, of a
+// matrix of NCT column tiles stored as split tiles.
+template <int NCT> __device__ __forceinline__ int64_t split_at(int r, int c) {
+    return afrag<NCT>(r >> 4, c >> 4, (r & 15) + 16 * ((c & 15) >> 2));
+}
+__device__ __forceinline__ void mma3(f32x4 &acc, Split a, Split b) {
+    Mma<__bf16>::mma(acc, a.t, b.h);
+    Mma<__bf16>::mma(acc, a.h, b.t);
+    Mma<__bf16>::mma(acc, a.h, b.h);
+}
+
 // A 16-token block whose decay falls below e^-60 in some channel has diagonal-block factors
 // beyond float32's comfortable range; such blocks are summed pair by pair.
 constexpr float kExtremeLogDecay = 60.f;
@@ -146,6 +188,31 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
     const int tid = threadIdx.x;
     const int64_t rsk = (int64_t)a.H * DK, rsv = (int64_t)a.H * DV;
 
+    // v is loaded with the other inputs and kept in registers until beta v is formed after T
+    constexpr int NVL = (C * DV / 4 + NT - 1) / NT;
+    f32x4 vpre[NVL];
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+        const int idx = tid + u * NT, i = idx / (DV / 4), c = 4 * (idx % (DV / 4));
+        vpre[u] = idx < C * DV / 4 && i < L
+                      ? load4(static_cast<const Tin *>(a.v) + (t0 + i) * rsv + (int64_t)h * DV + c) : zero4();
+    }
+    // dO for the products at the end: wave w takes value-column tile w, lane (lr, q4) the rows
+    // 16 ms + 4 q4 + e of column 16 w + lr (zero past the sequence end)
+    constexpr int VTP = DV / 16, ITP = C / 16;
+    static_assert(VTP <= NT / 64, "one value-column tile per wave");
+    f32x4 dpre[ITP];
+    {
+        const int w = tid >> 6, l = tid & 63;
+        const float *dcol = a.dout + (t0 + 4 * (l >> 4)) * rsv + (int64_t)h * DV + 16 * (w < VTP ? w : 0) + (l & 15);
+#pragma unroll
+        for (int ms = 0; ms < ITP; ++ms)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * ms + 4 * (l >> 4) + e;
+                dpre[ms][e] = w < VTP && r < L ? dcol[(int64_t)(16 * ms + e) * rsv] : 0.f;
+            }
+    }
     for (int idx = tid; idx < C * DK / 4; idx += NT) {
         const int i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
         f32x4 kv = zero4(), qv = zero4(), gv = zero4();
@@ -180,16 +247,11 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
         const f32x4 G = *reinterpret_cast<const f32x4 *>(sG + i * LDX + c);
         const f32x4 gC = *reinterpret_cast<const f32x4 *>(sG + (C - 1) * LDX + c);
         const f32x4 kv = *reinterpret_cast<const f32x4 *>(sK + i * LDK + c);
-        const f32x4 qv = *reinterpret_cast<const f32x4 *>(sQ + i * LDX + c);
-        f32x4 qg, kd;
+        f32x4 kd;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            qg[e] = a.scale * qv[e] * __expf(G[e]);
-            kd[e] = kv[e] * __expf(gC[e] - G[e]);
-        }
+        for (int e = 0; e < 4; ++e) kd[e] = kv[e] * __expf(gC[e] - G[e]);
         *reinterpret_cast<f32x4 *>(rec + R::oG + i * DK + c) = G;
-        *reinterpret_cast<f32x4 *>(rec + R::oQg + i * DK + c) = qg;
-        *reinterpret_cast<f32x4 *>(rec + R::oKd + i * DK + c) = kd;
+        *reinterpret_cast<f32x4 *>(rec + R::oKd + split_at<DK / 16>(i, c)) = split_pack(kd);
     }
     for (int idx = tid; idx < DK * C / 4; idx += NT) {  // the same, transposed ([channel][row])
         const int c = idx / (C / 4), i0 = 4 * (idx % (C / 4));
@@ -200,8 +262,8 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
             qg[e] = a.scale * sQ[(i0 + e) * LDX + c] * __expf(G);
             kd[e] = sK[(i0 + e) * LDK + c] * __expf(gC - G);
         }
-        *reinterpret_cast<f32x4 *>(rec + R::oQgT + c * C + i0) = qg;
-        *reinterpret_cast<f32x4 *>(rec + R::oKdT + c * C + i0) = kd;
+        *reinterpret_cast<f32x4 *>(rec + R::oQgT + split_at<C / 16>(c, i0)) = split_pack(qg);
+        *reinterpret_cast<f32x4 *>(rec + R::oKdT + split_at<C / 16>(c, i0)) = split_pack(kd);
     }
     // A~ and M as 16x16 block pairs (I, J <= I) on the matrix cores, one pair per wave at a time:
     // e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j} with r the last row of block J (both factors
@@ -217,37 +279,34 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
             const int J = pb - I * (I + 1) / 2;
             const bool diag = I == J;
             if (diag && sExt[I]) {
-                for (int pp = lane; pp < 136; pp += 64) {   // pairs (i, j <= i) of the block
-                    int ri = 0;
-                    while ((ri + 1) * (ri + 2) / 2 <= pp) ++ri;
-                    const int i = 16 * I + ri, j = 16 * I + pp - ri * (ri + 1) / 2;
+                // lane (jl, ig): column j = 16 I + jl, rows i = 16 I + 4 ig + e (e = 0..3), i.e.
+                // one 4-value group of M^T's row j and four values of A~'s column j
+                const int jl = lane & 15, ig = lane >> 4, j = 16 * I + jl, i0 = 16 * I + 4 * ig;
+                f32x4 mt = zero4();
+                for (int e = 0; e < 4; ++e) {
+                    const int i = i0 + e;
                     float sa = 0.f, sm = 0.f;
-                    for (int c = 0; c < DK; c += 4) {
-                        const f32x4 ki = *reinterpret_cast<const f32x4 *>(sK + i * LDK + c);
-                        const f32x4 kj = *reinterpret_cast<const f32x4 *>(sK + j * LDK + c);
-                        const f32x4 qi = *reinterpret_cast<const f32x4 *>(sQ + i * LDX + c);
-                        const f32x4 Gi = *reinterpret_cast<const f32x4 *>(sG + i * LDX + c);
-                        const f32x4 Gj = *reinterpret_cast<const f32x4 *>(sG + j * LDX + c);
+                    if (j <= i) {
+                        for (int c = 0; c < DK; c += 4) {
+                            const f32x4 ki = *reinterpret_cast<const f32x4 *>(sK + i * LDK + c);
+                            const f32x4 kj = *reinterpret_cast<const f32x4 *>(sK + j * LDK + c);
+                            const f32x4 qi = *reinterpret_cast<const f32x4 *>(sQ + i * LDX + c);
+                            const f32x4 Gi = *reinterpret_cast<const f32x4 *>(sG + i * LDX + c);
+                            const f32x4 Gj = *reinterpret_cast<const f32x4 *>(sG + j * LDX + c);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float kjE = kj[e] * __expf(Gi[e] - Gj[e]);
-                            sa += ki[e] * kjE;
-                            sm += qi[e] * kjE;
+                            for (int u = 0; u < 4; ++u) {
+                                const float kjE = kj[u] * __expf(Gi[u] - Gj[u]);
+                                sa += ki[u] * kjE;
+                                sm += qi[u] * kjE;
+                            }
                         }
                     }
                     const float av = j < i ? sa : 0.f;
                     sA[i * LDA + j] = av;
                     rec[R::oA + i * C + j] = av;
-                    rec[R::oM + j * C + i] = a.scale * sm;   // M^T
+                    mt[e] = j <= i ? a.scale * sm : 0.f;
                 }
-                for (int pp = lane; pp < 256; pp += 64) {   // the block above its diagonal
-                    const int i = 16 * I + (pp >> 4), j = 16 * I + (pp & 15);
-                    if (j > i) {
-                        sA[i * LDA + j] = 0.f;
-                        rec[R::oA + i * C + j] = 0.f;
-                        rec[R::oM + j * C + i] = 0.f;
-                    }
-                }
+                *reinterpret_cast<f32x4 *>(rec + R::oM + split_at<C / 16>(j, i0)) = split_pack(mt);   // M^T
                 continue;
             }
             const int r = diag ? 16 * I : 16 * J + 15;
@@ -272,65 +331,108 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
                 mma(accA, Ka, Kb);
                 mma(accM, Qa, Kb);
             }
+            f32x4 mt;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * q4 + e, j = 16 * J + lr;
                 const float av = j < i ? accA[e] : 0.f;
                 sA[i * LDA + j] = av;
                 rec[R::oA + i * C + j] = av;
-                rec[R::oM + j * C + i] = j <= i ? a.scale * accM[e] : 0.f;   // M^T
+                mt[e] = j <= i ? a.scale * accM[e] : 0.f;
             }
+            // M^T: row 16 J + lr, the four values of columns 16 I + 4 q4 ..
+            *reinterpret_cast<f32x4 *>(rec + R::oM + split_at<C / 16>(16 * J + lr, 16 * I + 4 * q4)) = split_pack(mt);
         }
     }
-    for (int p = tid; p < C * C; p += NT) {   // blocks above the diagonal
+    for (int p = tid; p < C * C; p += NT) {   // blocks above the diagonal (whole split groups of 0)
         const int i = p / C, j = p % C;
         if ((j >> 4) > (i >> 4)) {
             sA[i * LDA + j] = 0.f;
             rec[R::oA + p] = 0.f;
-            rec[R::oM + j * C + i] = 0.f;
+            rec[R::oM + split_at<C / 16>(j, i & ~3) + (i & 3)] = 0.f;
         }
     }
     __syncthreads();
-    if (tid < 64) {
-        // T = (I + Diag(beta) A~)^-1 by forward substitution, lane = column
-        const int col = tid;
-        float x[C];
+    for (int idx = tid; idx < C * DK / 4; idx += NT) {  // beta k e^G over q (k and G die here)
+        const int i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+        const f32x4 kv = *reinterpret_cast<const f32x4 *>(sK + i * LDK + c);
+        const f32x4 G = *reinterpret_cast<const f32x4 *>(sG + i * LDX + c);
+        f32x4 r;
 #pragma unroll
-        for (int i = 0; i < C; ++i) x[i] = 0.f;
+        for (int e = 0; e < 4; ++e) r[e] = sB[i] * kv[e] * __expf(G[e]);
+        *reinterpret_cast<f32x4 *>(sQ + i * LDX + c) = r;
+    }
+    __syncthreads();  // k is dead: its array holds the tiles below
+    // T = (I + N)^-1 with N = Diag(beta) A~ (strictly lower): each diagonal 16x16 block by
+    // forward substitution (one wave per block, lane = column: 16 dependent steps, the blocks
+    // side by side), then block forward substitution T_IJ = -T_II sum_{J <= K < I} N_IK T_KJ on
+    // the matrix cores, one block row per level. Intermediate tiles live over k's array.
+    {
+        constexpr int NBK = C / 16, LDT = 20;         // scratch tile: 16 rows of 20 floats
+        // one tile per substituting wave, over k's array where it fits (k is dead), else apart
+        constexpr int NSCR = NBK * 16 * LDT;
+        constexpr bool kOverK = NSCR <= C * LDK;
+        __shared__ __align__(16) float sScr[kOverK ? 4 : NSCR];
+        float *const scr = kOverK ? sK : sScr;
+        const int wv = tid >> 6, ln = tid & 63, tr = ln & 15, tq = ln >> 4;
+        // D (16 x 16: rows 4 tq + e, column tr in this lane) = init + A B, both operands 16 x 16
+        // tiles in LDS (A row-major with a per-row scale, B row-major read by columns)
+        auto prod = [&](const float *A, int lda, float ascale_row, const float *B, int ldb, f32x4 init) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(A + tr * lda + 4 * tq) * ascale_row;
+            f32x4 b;
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            float acc = 0.f;
+            for (int e = 0; e < 4; ++e) b[e] = B[(4 * tq + e) * ldb + tr];
+            f32x4 acc = init;
+            mma(acc, a, b);
+            return acc;
+        };
+        auto put = [&](float *D, int ld, f32x4 v) {
 #pragma unroll
-            for (int m = 0; m < (i + 3) / 4 * 4; m += 4) {
-                const f32x4 ar = *reinterpret_cast<const f32x4 *>(sA + i * LDA + m);
-                acc += ar[0] * x[m] + ar[1] * x[m + 1] + ar[2] * x[m + 2] + ar[3] * x[m + 3];
+            for (int e = 0; e < 4; ++e) D[(4 * tq + e) * ld + tr] = v[e];
+        };
+        if (wv < NBK && ln < 16) {  // T_II, column ln: x_i = delta_i,col - beta_i sum_{m<i} A~_im x_m
+            const int I0 = 16 * wv;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) acc += sA[(I0 + i) * LDA + I0 + m] * x[m];
+                x[i] = (i == ln ? 1.f : 0.f) - sB[I0 + i] * acc;
             }
-            x[i] = (i == col ? 1.f : 0.f) - sB[i] * acc;
-        }
-        if (col < C) {
 #pragma unroll
-            for (int i = 0; i < C; ++i) {
-                sT[i * LDA + col] = x[i];
-                rec[R::oT + i * C + col] = x[i];
+            for (int i = 0; i < 16; ++i) sT[(I0 + i) * LDA + I0 + ln] = x[i];
+        }
+        // the blocks above the diagonal are zero
+        for (int idx = tid; idx < C * C; idx += NT) {
+            const int i = idx / C, j = idx % C;
+            if ((j >> 4) > (i >> 4)) sT[i * LDA + j] = 0.f;
+        }
+        __syncthreads();
+        // block rows I = 1 .. NBK - 1: wave J computes T_IJ, J < I
+        for (int I = 1; I < NBK; ++I) {
+            const bool act = wv < I;
+            const int J = wv;
+            float *R = scr + wv * 16 * LDT;             // sum_{K = J}^{I-1} N_IK T_KJ
+            if (act) {
+                f32x4 r = zero4();
+                for (int K = J; K < I; ++K)
+                    r = prod(sA + 16 * I * LDA + 16 * K, LDA, sB[16 * I + tr], sT + 16 * K * LDA + 16 * J, LDA, r);
+                put(R, LDT, r);
             }
+            __syncthreads();
+            if (act) put(sT + 16 * I * LDA + 16 * J, LDA, -prod(sT + 16 * I * LDA + 16 * I, LDA, 1.f, R, LDT, zero4()));
+            __syncthreads();
         }
-    } else {
-        for (int idx = tid - 64; idx < C * DK / 4; idx += NT - 64) {  // beta k e^G over q
-            const int i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
-            const f32x4 kv = *reinterpret_cast<const f32x4 *>(sK + i * LDK + c);
-            const f32x4 G = *reinterpret_cast<const f32x4 *>(sG + i * LDX + c);
-            f32x4 r;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) r[e] = sB[i] * kv[e] * __expf(G[e]);
-            *reinterpret_cast<f32x4 *>(sQ + i * LDX + c) = r;
+        for (int idx = tid; idx < C * C / 4; idx += NT) {
+            const int i = idx / (C / 4), j = 4 * (idx % (C / 4));
+            *reinterpret_cast<f32x4 *>(rec + R::oT + i * C + j) = *reinterpret_cast<const f32x4 *>(sT + i * LDA + j);
         }
     }
-    __syncthreads();
-    for (int idx = tid; idx < C * DV / 4; idx += NT) {  // beta v over G
-        const int i = idx / (DV / 4), c = 4 * (idx % (DV / 4));
-        f32x4 vv = zero4();
-        if (i < L) vv = load4(static_cast<const Tin *>(a.v) + (t0 + i) * rsv + (int64_t)h * DV + c);
-        *reinterpret_cast<f32x4 *>(sG + i * LDX + c) = vv * sB[i];
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {  // beta v over G
+        const int idx = tid + u * NT, i = idx / (DV / 4), c = 4 * (idx % (DV / 4));
+        if (idx < C * DV / 4) *reinterpret_cast<f32x4 *>(sG + i * LDX + c) = vpre[u] * sB[i];
     }
     __syncthreads();
     // W = T (beta k e^G), U~ = T (beta v): 16 x 16 tiles over the waves
@@ -342,7 +444,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
         const int nct = isW ? DK / 16 : DV / 16;
         const int it = tt / nct, nt = tt % nct;
         const float *X = isW ? sQ : sG;
-        f32x4 acc = zero4();
+        f32x4 acc = zero4(), accT = zero4();
         for (int ms = 0; ms <= it; ++ms) {
             const int m0 = 16 * ms + 4 * q4;
             const f32x4 A = *reinterpret_cast<const f32x4 *>(sT + (16 * it + lr) * LDA + m0);
@@ -350,22 +452,56 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) B[e] = X[(m0 + e) * LDX + 16 * nt + lr];
             mma(acc, A, B);
+            if (isW) mma(accT, B, A);   // the same tile transposed: four channels of one row
         }
-        float *dst = rec + (isW ? R::oW : R::oU);
-        const int ld = isW ? DK : DV;
+        if (isW) {
+            *reinterpret_cast<f32x4 *>(rec + R::oW + afrag<DK / 16>(it, nt, lane)) = split_pack(accT);
+            *reinterpret_cast<f32x4 *>(rec + R::oWT + afrag<C / 16>(nt, it, lane)) = split_pack(-acc);
+        } else {
+            *reinterpret_cast<f32x4 *>(rec + R::oU + afrag<DV / 16>(it, nt, lane)) = acc;
+        }
+    }
+    // The parts of the reverse state pass that do not depend on the state gradient, in the
+    // slots of dU and dH (which that pass reads before it writes them): M^T dO (the dO part of
+    // dU) and Qg^T dO (the dO part of dS). Wave w takes value-column tile w; the split M^T and
+    // Qg^T tiles were written above by this workgroup (the barrier's fence orders them).
+    __syncthreads();
+    if (wave < VTP) {
+        constexpr int KTP = DK / 16;
+        Split dOs[ITP];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(16 * it + 4 * q4 + e) * ld + 16 * nt + lr] = acc[e];
-        if (isW) *reinterpret_cast<f32x4 *>(rec + R::oWT + (16 * nt + lr) * C + 16 * it + 4 * q4) = acc;
+        for (int ms = 0; ms < ITP; ++ms) dOs[ms] = split(dpre[ms]);
+        for (int kt = 0; kt < KTP; ++kt) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ms = 0; ms < ITP; ++ms)
+                mma3(acc, unpack(*reinterpret_cast<const f32x4 *>(rec + R::oQgT + afrag<ITP>(kt, ms, lane))), dOs[ms]);
+            *reinterpret_cast<f32x4 *>(rec + R::odH + afrag<VTP>(kt, wave, lane)) = acc;
+        }
+#pragma unroll
+        for (int it = 0; it < ITP; ++it) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ms = it; ms < ITP; ++ms)   // M[m][i] = 0 for m < i
+                mma3(acc, unpack(*reinterpret_cast<const f32x4 *>(rec + R::oM + afrag<ITP>(it, ms, lane))), dOs[ms]);
+            *reinterpret_cast<f32x4 *>(rec + R::odU + afrag<VTP>(it, wave, lane)) = acc;
+        }
     }
 }
 
 // ------------------------------------------------------------------------------------------
 // 2. forward state pass: one workgroup per (chain, 16 value columns); wave w holds the 16x16
-//    state tiles of its key-channel tiles in accumulator registers. Every operand is one
-//    16-byte load per lane, and the next chunk's operands are loaded while this one computes.
+//    state tiles of its key-channel tiles in accumulator registers. Every operand but dO is one
+//    16-byte load per lane. The next chunk's operands are loaded while this one computes, their
+//    loads interleaved with this chunk's products (a wave issues in order: a burst of loads
+//    would hold its products back while the CU's memory pipeline drains it), and the chunk after
+//    that is touched into the L2 (each of a chain's value-column workgroups touches an eighth of
+//    its lines), so those loads hit the cache. The loop body has no branches, so that the
+//    scheduling fences below order it.
 // ------------------------------------------------------------------------------------------
 template <int C, int DK, int DV> struct StatePass {
     static constexpr int KT = DK / 16;
+    static constexpr int VT = DV / 16;
     static constexpr int NW = KT < 4 ? KT : 4;
     static constexpr int KTW = KT / NW;
     static constexpr int IT = C / 16;
@@ -374,20 +510,46 @@ template <int C, int DK, int DV> struct StatePass {
     static_assert(IT % NW == 0 || IT == 1, "row tiles spread evenly");
 };
 
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// L2 touch of one step's operands: the 128-byte lines of NR record regions are
+// numbered in turn; value-column block vb touches the lines vb, vb + nvb, ..., one load per
+// thread (threads past the last line load the first one). The loaded word is kept and consumed
+// two steps later, so that the load is issued and nothing waits for it before then.
+template <int NR> struct TouchSet {
+    const float *base[NR];
+    int lines[NR];
+};
+
+template <int NR> __device__ __forceinline__ float touch(const TouchSet<NR> &t, int vb, int nvb) {
+    int l = vb + nvb * (int)threadIdx.x;
+    const float *p = t.base[0];
+    bool found = false;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const bool in = !found && l < t.lines[r];
+        p = in ? t.base[r] + (int64_t)l * 32 : p;
+        found = found || in;
+        l = found ? l : l - t.lines[r];
+    }
+    return *p;
+}
+
 template <int C, int DK, int DV> struct FwdOps {
     using P = StatePass<C, DK, DV>;
     f32x4 W[P::IT][P::KTW];     // W rows 16 it + lr, channels 16 kt + 4 q4 ..
     f32x4 KdT[P::KTW][P::IT];   // Kd^T rows 16 kt + lr, tokens 16 it + 4 q4 ..
     f32x4 eg[P::KTW];           // e^{gC} of channels 16 kt + 4 q4 ..
-    f32x4 Ut[P::NOWN];          // U~ of the owned row tiles, accumulator layout
+    f32x4 Ut[P::NOWN];          // U~ of the owned row tiles (accumulator fragments)
+    float pf;                   // the L2 touch of the chunk two steps ahead
 };
 
 template <int C, int DK, int DV>
 __device__ __forceinline__ void fwd_state_pass(const BwdArgs &a, int chain, int vb) {
     using R = BRec<C, DK, DV>;
     using P = StatePass<C, DK, DV>;
-    constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW, NOWN = P::NOWN;
-    __shared__ f32x4 sPart[NW][IT][64];
+    constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW, NOWN = P::NOWN, VT = P::VT;
+    __shared__ f32x4 sPart[2][NW][IT][64];   // by step parity: one barrier per step
     const int n = chain / a.H, h = chain % a.H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, q4 = lane >> 4;
     int64_t st, en;
@@ -398,22 +560,32 @@ __device__ __forceinline__ void fwd_state_pass(const BwdArgs &a, int chain, int 
     const int col = 16 * vb + lr;
     auto rec_of = [&](int j) { return a.ws + ((base + j) * a.H + h) * R::FLOATS; };
     auto own = [&](int o) { return wave + NW * o; };
-    auto load = [&](const float *rec, FwdOps<C, DK, DV> &o) {
+    auto loadW = [&](const float *rec, FwdOps<C, DK, DV> &o, int it) {
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk) {
             const int kt = wave * KTW + kk;
-#pragma unroll
-            for (int it = 0; it < IT; ++it) {
-                o.W[it][kk] = *reinterpret_cast<const f32x4 *>(rec + R::oW + (16 * it + lr) * DK + 16 * kt + 4 * q4);
-                o.KdT[kk][it] = *reinterpret_cast<const f32x4 *>(rec + R::oKdT + (16 * kt + lr) * C + 16 * it + 4 * q4);
-            }
-            o.eg[kk] = *reinterpret_cast<const f32x4 *>(rec + R::oEg + 16 * kt + 4 * q4);
+            o.W[it][kk] = *reinterpret_cast<const f32x4 *>(rec + R::oW + afrag<P::KT>(it, kt, lane));
+            o.KdT[kk][it] = *reinterpret_cast<const f32x4 *>(rec + R::oKdT + afrag<IT>(kt, it, lane));
         }
+    };
+    auto loadRest = [&](const float *rec, FwdOps<C, DK, DV> &o) {
 #pragma unroll
-        for (int ow = 0; ow < NOWN; ++ow)
+        for (int kk = 0; kk < KTW; ++kk)
+            o.eg[kk] = *reinterpret_cast<const f32x4 *>(rec + R::oEg + 16 * (wave * KTW + kk) + 4 * q4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                o.Ut[ow][e] = own(ow) < IT ? rec[R::oU + (16 * own(ow) + 4 * q4 + e) * DV + col] : 0.f;
+        for (int ow = 0; ow < NOWN; ++ow) {
+            if constexpr (IT >= NW) o.Ut[ow] = *reinterpret_cast<const f32x4 *>(rec + R::oU + afrag<VT>(own(ow), vb, lane));
+            else o.Ut[ow] = own(ow) < IT ? *reinterpret_cast<const f32x4 *>(rec + R::oU + afrag<VT>(own(ow), vb, lane)) : zero4();
+        }
+    };
+    auto touch_chunk = [&](int j) {
+        const float *rec = rec_of(j);
+        TouchSet<4> t;
+        t.base[0] = rec + R::oW;   t.lines[0] = C * DK / 32;
+        t.base[1] = rec + R::oKdT; t.lines[1] = DK * C / 32;
+        t.base[2] = rec + R::oU;   t.lines[2] = C * DV / 32;
+        t.base[3] = rec + R::oEg;  t.lines[3] = (DK + 31) / 32;
+        return touch(t, vb, DV / 16);
     };
 
     f32x4 S[KTW];
@@ -424,80 +596,106 @@ __device__ __forceinline__ void fwd_state_pass(const BwdArgs &a, int chain, int 
         for (int e = 0; e < 4; ++e)
             S[kk][e] = a.s0 ? a.s0[(((int64_t)n * a.H + h) * DK + 16 * kt + 4 * q4 + e) * DV + col] : 0.f;
     }
-    // one chunk with operands `cur`, loading the next chunk's into `nxt`; the loop below
-    // alternates two operand sets, so the loads stay in flight across the chunk
+    float sink = 0.f;
+    // one chunk with operands `cur`, loading the next chunk's into `nxt` (the last chunk reloads
+    // its own: no branch); the loop below alternates the two operand sets
     auto step = [&](int j, FwdOps<C, DK, DV> &cur, FwdOps<C, DK, DV> &nxt) {
         float *rec = rec_of(j);
-        if (j + 1 < nch) load(rec_of(j + 1), nxt);
+        const float *nrec = rec_of(j + 1 < nch ? j + 1 : j);
 #pragma unroll
-        for (int kk = 0; kk < KTW; ++kk) {
-            const int kt = wave * KTW + kk;
+        for (int kk = 0; kk < KTW; ++kk)
+            *reinterpret_cast<f32x4 *>(rec + R::oH + afrag<VT>(wave * KTW + kk, vb, lane)) = S[kk];
+        Split Ss[KTW];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rec[R::oH + (16 * kt + 4 * q4 + e) * DV + col] = S[kk][e];
-        }
+        for (int kk = 0; kk < KTW; ++kk) Ss[kk] = split(S[kk]);
+        f32x4 acc[IT];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            f32x4 acc = zero4();
+            loadW(nrec, nxt, it);
+            sched_fence();
+            acc[it] = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KTW; ++kk) mma(acc, cur.W[it][kk], S[kk]);
-            f32x4 part = -acc;
+            for (int kk = 0; kk < KTW; ++kk) mma3(acc[it], unpack(cur.W[it][kk]), Ss[kk]);
+            sched_fence();
+        }
+        loadRest(nrec, nxt);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            f32x4 part = -acc[it];
 #pragma unroll
             for (int ow = 0; ow < NOWN; ++ow)
-                if (own(ow) == it) part += cur.Ut[ow];   // the owner of row tile it adds U~
-            sPart[wave][it][lane] = part;
+                part += own(ow) == it ? cur.Ut[ow] : zero4();   // the owner of row tile it adds U~
+            sPart[j & 1][wave][it][lane] = part;
         }
         __syncthreads();
         f32x4 U[IT];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            U[it] = sPart[0][it][lane];
+            U[it] = sPart[j & 1][0][it][lane];
 #pragma unroll
-            for (int w = 1; w < NW; ++w) U[it] += sPart[w][it][lane];
+            for (int w = 1; w < NW; ++w) U[it] += sPart[j & 1][w][it][lane];
         }
-        __syncthreads();
+        // the touch issued two steps ago is complete (cur's loads came after it): consume it
+        // (tied to U so that it stays after them) and touch the chunk two steps ahead
+        sink += cur.pf * U[0][0];
+        cur.pf = touch_chunk(j + 2 < nch ? j + 2 : nch - 1);
 #pragma unroll
-        for (int ow = 0; ow < NOWN; ++ow)
+        for (int ow = 0; ow < NOWN; ++ow) {
+            f32x4 u = zero4();
 #pragma unroll
-            for (int it = 0; it < IT; ++it)
-                if (own(ow) == it) {
+            for (int it = 0; it < IT; ++it) u = own(ow) == it ? U[it] : u;
+            if (IT >= NW || own(ow) < IT)
+                *reinterpret_cast<f32x4 *>(rec + R::oU + afrag<VT>(own(ow), vb, lane)) = u;
+        }
+        Split Us[IT];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) rec[R::oU + (16 * it + 4 * q4 + e) * DV + col] = U[it][e];
-                }
+        for (int it = 0; it < IT; ++it) Us[it] = split(U[it]);
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk) {
             S[kk] *= cur.eg[kk];
 #pragma unroll
-            for (int it = 0; it < IT; ++it) mma(S[kk], cur.KdT[kk][it], U[it]);
+            for (int it = 0; it < IT; ++it) mma3(S[kk], unpack(cur.KdT[kk][it]), Us[it]);
         }
     };
     FwdOps<C, DK, DV> o0, o1;
-    if (nch > 0) load(rec_of(0), o0);
+    o0.pf = o1.pf = 0.f;
+    if (nch > 0) {
+        const float *r0 = rec_of(0);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) loadW(r0, o0, it);
+        loadRest(r0, o0);
+    }
+    if (nch > 1) o1.pf = touch_chunk(1);
     int j = 0;
     for (; j + 1 < nch; j += 2) {
         step(j, o0, o1);
         step(j + 1, o1, o0);
     }
     if (j < nch) step(j, o0, o1);
+    __asm__ volatile("" : : "v"(sink), "v"(o0.pf), "v"(o1.pf));
 }
 
 // ------------------------------------------------------------------------------------------
-// 3. reverse state pass: dS held like S above, chunks in reverse order; the next chunk's Kd,
-//    M^T, e^{gC} and dO are loaded while this one computes.
+// 3. reverse state pass: dS held like S above, chunks in reverse order, the same pipeline as
+//    the forward pass. With P1 = M^T dO and P2 = Qg^T dO from the prep (in the dU and dH
+//    slots), a chunk is dU = Kd dS' + P1 (exchanged like U), then dS = e^{gC} dS' + P2 - W^T dU.
 // ------------------------------------------------------------------------------------------
 template <int C, int DK, int DV> struct RevOps {
     using P = StatePass<C, DK, DV>;
     f32x4 Kd[P::IT][P::KTW];    // Kd rows 16 it + lr, channels 16 kt + 4 q4 ..
-    f32x4 MT[P::NOWN][P::IT];   // M^T rows of the owned tiles, tokens 16 ms + 4 q4 ..
+    f32x4 WT[P::KTW][P::IT];    // -W^T rows 16 kt + lr, tokens 16 it + 4 q4 ..
     f32x4 eg[P::KTW];
-    f32x4 dO[P::IT];            // dO rows 16 ms + 4 q4 + e, column col (zero past the end)
+    f32x4 P1[P::NOWN];          // M^T dO of the owned row tiles (accumulator fragments)
+    f32x4 P2[P::KTW];           // Qg^T dO of the wave's key tiles (accumulator fragments)
+    float pf;
 };
 
 template <int C, int DK, int DV>
 __device__ __forceinline__ void rev_state_pass(const BwdArgs &a, int chain, int vb) {
     using R = BRec<C, DK, DV>;
     using P = StatePass<C, DK, DV>;
-    constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW, NOWN = P::NOWN;
-    __shared__ f32x4 sPart[NW][IT][64];
+    constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW, NOWN = P::NOWN, VT = P::VT;
+    __shared__ f32x4 sPart[2][NW][IT][64];
     const int n = chain / a.H, h = chain % a.H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, q4 = lane >> 4;
     int64_t st, en;
@@ -507,34 +705,38 @@ __device__ __forceinline__ void rev_state_pass(const BwdArgs &a, int chain, int 
     const int64_t base = slot_base<C>(a, n);
     const int col = 16 * vb + lr;
     const int64_t sbase = ((int64_t)n * a.H + h) * DK;
-    const int64_t rsv = (int64_t)a.H * DV;
     auto rec_of = [&](int j) { return a.ws + ((base + j) * a.H + h) * R::FLOATS; };
     auto own = [&](int o) { return wave + NW * o; };
-    auto load = [&](int j, RevOps<C, DK, DV> &o) {
-        const float *rec = rec_of(j);
+    auto loadKW = [&](const float *rec, RevOps<C, DK, DV> &o, int it) {
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk) {
             const int kt = wave * KTW + kk;
+            o.Kd[it][kk] = *reinterpret_cast<const f32x4 *>(rec + R::oKd + afrag<P::KT>(it, kt, lane));
+            o.WT[kk][it] = *reinterpret_cast<const f32x4 *>(rec + R::oWT + afrag<IT>(kt, it, lane));
+        }
+    };
+    auto loadRest = [&](const float *rec, RevOps<C, DK, DV> &o) {
 #pragma unroll
-            for (int it = 0; it < IT; ++it)
-                o.Kd[it][kk] = *reinterpret_cast<const f32x4 *>(rec + R::oKd + (16 * it + lr) * DK + 16 * kt + 4 * q4);
+        for (int kk = 0; kk < KTW; ++kk) {
+            const int kt = wave * KTW + kk;
             o.eg[kk] = *reinterpret_cast<const f32x4 *>(rec + R::oEg + 16 * kt + 4 * q4);
+            o.P2[kk] = *reinterpret_cast<const f32x4 *>(rec + R::odH + afrag<VT>(kt, vb, lane));
         }
 #pragma unroll
-        for (int ow = 0; ow < NOWN; ++ow)
-#pragma unroll
-            for (int ms = 0; ms < IT; ++ms)
-                o.MT[ow][ms] = own(ow) < IT && ms >= own(ow)   // M[m][i] = 0 for m < i
-                    ? *reinterpret_cast<const f32x4 *>(rec + R::oM + (16 * own(ow) + lr) * C + 16 * ms + 4 * q4)
-                    : zero4();
-        const int64_t t0 = st + (int64_t)j * C;
-        const int L = (int)(len - (int64_t)j * C < C ? len - (int64_t)j * C : C);
-        const float *dorow = a.dout + (t0 + 4 * q4) * rsv + (int64_t)h * DV + col;
-#pragma unroll
-        for (int ms = 0; ms < IT; ++ms)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                o.dO[ms][e] = 16 * ms + 4 * q4 + e < L ? dorow[(int64_t)(16 * ms + e) * rsv] : 0.f;
+        for (int ow = 0; ow < NOWN; ++ow) {
+            if constexpr (IT >= NW) o.P1[ow] = *reinterpret_cast<const f32x4 *>(rec + R::odU + afrag<VT>(own(ow), vb, lane));
+            else o.P1[ow] = own(ow) < IT ? *reinterpret_cast<const f32x4 *>(rec + R::odU + afrag<VT>(own(ow), vb, lane)) : zero4();
+        }
+    };
+    auto touch_chunk = [&](int j) {
+        const float *rec = rec_of(j);
+        TouchSet<5> t;
+        t.base[0] = rec + R::oKd;  t.lines[0] = C * DK / 32;
+        t.base[1] = rec + R::oWT;  t.lines[1] = DK * C / 32;
+        t.base[2] = rec + R::odU;  t.lines[2] = C * DV / 32;
+        t.base[3] = rec + R::odH;  t.lines[3] = DK * DV / 32;
+        t.base[4] = rec + R::oEg;  t.lines[4] = (DK + 31) / 32;
+        return touch(t, vb, DV / 16);
     };
 
     f32x4 dS[KTW];
@@ -545,76 +747,79 @@ __device__ __forceinline__ void rev_state_pass(const BwdArgs &a, int chain, int 
         for (int e = 0; e < 4; ++e)
             dS[kk][e] = a.dsT ? a.dsT[(sbase + 16 * kt + 4 * q4 + e) * DV + col] : 0.f;
     }
+    float sink = 0.f;
     auto step = [&](int j, RevOps<C, DK, DV> &cur, RevOps<C, DK, DV> &nxt) {
         float *rec = rec_of(j);
-        if (j > 0) load(j - 1, nxt);
-        // Qg^T and W^T are needed only after the exchange below: loaded here, not a chunk ahead
-        // (a third prefetched set costs more in register moves than it saves)
-        f32x4 QgT[KTW][IT], WT[KTW][IT];
+        const float *nrec = rec_of(j > 0 ? j - 1 : 0);
+        Split dSs[KTW];
 #pragma unroll
-        for (int kk = 0; kk < KTW; ++kk) {
-            const int kt = wave * KTW + kk;
-#pragma unroll
-            for (int it = 0; it < IT; ++it) {
-                QgT[kk][it] = *reinterpret_cast<const f32x4 *>(rec + R::oQgT + (16 * kt + lr) * C + 16 * it + 4 * q4);
-                WT[kk][it] = -*reinterpret_cast<const f32x4 *>(rec + R::oWT + (16 * kt + lr) * C + 16 * it + 4 * q4);
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk < KTW; ++kk) {
-            const int kt = wave * KTW + kk;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rec[R::odH + (16 * kt + 4 * q4 + e) * DV + col] = dS[kk][e];
-        }
+        for (int kk = 0; kk < KTW; ++kk) dSs[kk] = split(dS[kk]);
+        f32x4 acc[IT];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            f32x4 acc = zero4();
+            loadKW(nrec, nxt, it);
+            sched_fence();
+            acc[it] = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KTW; ++kk) mma(acc, cur.Kd[it][kk], dS[kk]);
+            for (int kk = 0; kk < KTW; ++kk) mma3(acc[it], unpack(cur.Kd[it][kk]), dSs[kk]);
+            sched_fence();
+        }
+        loadRest(nrec, nxt);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            f32x4 part = acc[it];
 #pragma unroll
             for (int ow = 0; ow < NOWN; ++ow)
-                if (own(ow) == it) {   // M^T dO for the owned row tile
-#pragma unroll
-                    for (int ms = 0; ms < IT; ++ms)
-                        if (ms >= it) mma(acc, cur.MT[ow][ms], cur.dO[ms]);
-                }
-            sPart[wave][it][lane] = acc;
+                part += own(ow) == it ? cur.P1[ow] : zero4();   // the owner of row tile it adds M^T dO
+            sPart[j & 1][wave][it][lane] = part;
         }
         __syncthreads();
         f32x4 dU[IT];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            dU[it] = sPart[0][it][lane];
+            dU[it] = sPart[j & 1][0][it][lane];
 #pragma unroll
-            for (int w = 1; w < NW; ++w) dU[it] += sPart[w][it][lane];
+            for (int w = 1; w < NW; ++w) dU[it] += sPart[j & 1][w][it][lane];
         }
-        __syncthreads();
+        sink += cur.pf * dU[0][0];
+        cur.pf = touch_chunk(j >= 2 ? j - 2 : 0);
+        // dU and dS' over this chunk's P1 and P2 (read above, before these stores)
 #pragma unroll
-        for (int ow = 0; ow < NOWN; ++ow)
+        for (int ow = 0; ow < NOWN; ++ow) {
+            f32x4 u = zero4();
 #pragma unroll
-            for (int it = 0; it < IT; ++it)
-                if (own(ow) == it) {
+            for (int it = 0; it < IT; ++it) u = own(ow) == it ? dU[it] : u;
+            if (IT >= NW || own(ow) < IT)
+                *reinterpret_cast<f32x4 *>(rec + R::odU + afrag<VT>(own(ow), vb, lane)) = u;
+        }
+        Split dUs[IT];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) rec[R::odU + (16 * it + 4 * q4 + e) * DV + col] = dU[it][e];
-                }
+        for (int it = 0; it < IT; ++it) dUs[it] = split(dU[it]);
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk) {
-            dS[kk] *= cur.eg[kk];
+            const f32x4 dSo = dS[kk];
+            dS[kk] = dS[kk] * cur.eg[kk] + cur.P2[kk];
 #pragma unroll
-            for (int it = 0; it < IT; ++it) {
-                mma(dS[kk], QgT[kk][it], cur.dO[it]);
-                mma(dS[kk], WT[kk][it], dU[it]);
-            }
+            for (int it = 0; it < IT; ++it) mma3(dS[kk], unpack(cur.WT[kk][it]), dUs[it]);   // -W^T dU
+            *reinterpret_cast<f32x4 *>(rec + R::odH + afrag<VT>(wave * KTW + kk, vb, lane)) = dSo;
         }
     };
     RevOps<C, DK, DV> o0, o1;
-    if (nch > 0) load(nch - 1, o0);
+    o0.pf = o1.pf = 0.f;
+    if (nch > 0) {
+        const float *rl = rec_of(nch - 1);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) loadKW(rl, o0, it);
+        loadRest(rl, o0);
+    }
+    if (nch > 1) o1.pf = touch_chunk(nch - 2);
     int j = nch - 1;
     for (; j >= 1; j -= 2) {
         step(j, o0, o1);
         step(j - 1, o1, o0);
     }
     if (j == 0) step(0, o0, o1);
+    __asm__ volatile("" : : "v"(sink), "v"(o0.pf), "v"(o1.pf));
     if (a.ds0) {
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk) {
@@ -626,11 +831,24 @@ __device__ __forceinline__ void rev_state_pass(const BwdArgs &a, int chain, int 
 }
 
 // The two state passes depend only on prep's records (and dL/do), not on each other: one
-// launch runs both, the forward chains in grid layer z = 0 and the reverse ones in z = 1.
+// launch runs both. Workgroup b maps to (direction, chain, value block) so that the value
+// blocks of one chain and direction share b mod 8, i.e. one XCD and its L2 (workgroups go to
+// the XCDs round robin): pair p = direction * chains + chain takes XCD p mod 8 and, on it,
+// the slots (p / 8) * NVB .. + NVB - 1. Slots past the last pair exit at once.
 template <int C, int DK, int DV>
 __global__ __launch_bounds__(256) void bwd_state_kernel(BwdArgs a) {
-    if (blockIdx.z == 0) fwd_state_pass<C, DK, DV>(a, blockIdx.x, blockIdx.y);
-    else rev_state_pass<C, DK, DV>(a, blockIdx.x, blockIdx.y);
+    constexpr int NVB = DV / 16;
+    const int b = blockIdx.x, k = b >> 3;
+    const int p = (k / NVB) * 8 + (b & 7), vb = k % NVB;
+    const int chains = a.n_seqs * a.H;
+    if (p >= 2 * chains) return;
+    if (p < chains) fwd_state_pass<C, DK, DV>(a, p, vb);
+    else rev_state_pass<C, DK, DV>(a, p - chains, vb);
+}
+
+// The state kernel's grid: 8 XCD lanes x NVB slots per group of 8 (direction, chain) pairs.
+template <int DV> unsigned state_blocks(int chains) {
+    return (unsigned)(((2 * chains + 7) / 8) * 8 * (DV / 16));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -687,8 +905,16 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
         f32x4 dOv = zero4();
         if (i < L) dOv = *reinterpret_cast<const f32x4 *>(a.dout + (t0 + i) * rsv + (int64_t)h * DV + j);
         *reinterpret_cast<f32x4 *>(sdO + i * LDV + j) = dOv;
-        *reinterpret_cast<f32x4 *>(sU + i * LDV + j) = *reinterpret_cast<const f32x4 *>(rec + R::oU + i * DV + j);
-        *reinterpret_cast<f32x4 *>(sdU + i * LDV + j) = *reinterpret_cast<const f32x4 *>(rec + R::odU + i * DV + j);
+        // U and dU are in fragment order: vector idx is lane idx % 64 of tile idx / 64
+        const f32x4 u = *reinterpret_cast<const f32x4 *>(rec + R::oU + 4 * idx);
+        const f32x4 du = *reinterpret_cast<const f32x4 *>(rec + R::odU + 4 * idx);
+        const int tile = idx >> 6, fl = idx & 63;
+        const int r0 = 16 * (tile / VT) + 4 * (fl >> 4), cu = 16 * (tile % VT) + (fl & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sU[(r0 + e) * LDV + cu] = u[e];
+            sdU[(r0 + e) * LDV + cu] = du[e];
+        }
     }
     for (int idx = tid; idx < NSRC * C; idx += NT) (&sDb[0][0])[idx] = 0.f;
     // this wave's rows of S and dS' (key tile ct = wave): the B fragments below
@@ -697,8 +923,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     if (ct < KT) {
 #pragma unroll
         for (int js = 0; js < VT; ++js) {
-            hB[js] = *reinterpret_cast<const f32x4 *>(rec + R::oH + (16 * ct + lr) * DV + 16 * js + 4 * q4);
-            dhB[js] = *reinterpret_cast<const f32x4 *>(rec + R::odH + (16 * ct + lr) * DV + 16 * js + 4 * q4);
+            // S[16 ct + lr][16 js + 4 q4 + e] from fragment order: lane 16 (lr / 4) + 4 q4 + e of
+            // tile (ct, js), element lr % 4
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t o = afrag<VT>(ct, js, 16 * (lr >> 2) + 4 * q4 + e) + (lr & 3);
+                hB[js][e] = rec[R::oH + o];
+                dhB[js][e] = rec[R::odH + o];
+            }
         }
     }
     __syncthreads();
@@ -706,6 +938,21 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     // dQg = dO S^T, dKd = U dS'^T, dW = -dU S^T for key tile ct; d e^{gC} = rowsum(S * dS')
     f32x4 dq_p[IT], dk_p[IT], dG_p[IT];
     if (ct < KT) {
+        // this lane's G, Qg, Kd (channel 16 ct + lr, rows 16 it + 4 q4 + e), read before the
+        // products so that their latency hides under them
+        const int c = 16 * ct + lr;
+        // Qg and Kd of rows 16 it + 4 q4 .. + 3: one group of the split Qg^T and Kd^T tiles
+        // (head + tail, float32 to about 2^-17)
+        const float gC = rec[R::oG + (C - 1) * DK + c];
+        float Gl[IT][4];
+        f32x4 Ql[IT], Kl[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            Ql[it] = unsplit(*reinterpret_cast<const f32x4 *>(rec + R::oQgT + afrag<IT>(ct, it, lane)));
+            Kl[it] = unsplit(*reinterpret_cast<const f32x4 *>(rec + R::oKdT + afrag<IT>(ct, it, lane)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Gl[it][e] = rec[R::oG + (16 * it + 4 * q4 + e) * DK + c];
+        }
         f32x4 aQ[IT], aK[IT], aW[IT];
 #pragma unroll
         for (int it = 0; it < IT; ++it) aQ[it] = aK[it] = aW[it] = zero4();
@@ -722,16 +969,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
             }
             dgc += hB[js][0] * dhB[js][0] + hB[js][1] * dhB[js][1] + hB[js][2] * dhB[js][2] + hB[js][3] * dhB[js][3];
         }
-        const int c = 16 * ct + lr;
-        const float gC = rec[R::oG + (C - 1) * DK + c];
         float cs = 0.f;
 #pragma unroll
         for (int it = 0; it < IT; ++it)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * it + 4 * q4 + e;
-                const float G = rec[R::oG + i * DK + c], Qg = rec[R::oQg + i * DK + c];
-                const float Kd = rec[R::oKd + i * DK + c];
+                const float G = Gl[it][e], Qg = Ql[it][e], Kd = Kl[it][e];
                 sW[i * LDK + c] = -aW[it][e];
                 dq_p[it][e] = a.scale * __expf(G) * aQ[it][e];
                 dk_p[it][e] = __expf(gC - G) * aK[it][e];
@@ -783,82 +1027,82 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
         int it, mt;
         tile_of(p, it, mt);
         const int m = 16 * mt + lr;
-        const float bm = beta_of(m);
-        f32x4 acc = zero4();
-        for (int js = 0; js < VT; ++js) {
-            const int j0 = 16 * js + 4 * q4;
-            f32x4 vb = zero4();
-            if (m < L) vb = load4(vin + (t0 + m) * rsv + (int64_t)h * DV + j0) * bm;
-            mma(acc, *reinterpret_cast<const f32x4 *>(sdU + (16 * it + lr) * LDV + j0), vb);
-        }
-        for (int cs = 0; cs < KT; ++cs) {
-            const int c0 = 16 * cs + 4 * q4;
-            f32x4 kb = zero4();
-            if (m < L) {
-                const f32x4 kv = load4(kin + (t0 + m) * rsk + (int64_t)h * DK + c0);
-                const f32x4 G = *reinterpret_cast<const f32x4 *>(rec + R::oG + m * DK + c0);
+        const float bm = beta_of(m);  // 0 past the sequence end, which zeroes those rows
+        // every load of the tile goes out before its products (a row past the end reads the
+        // last valid row: finite, then zeroed by bm)
+        const int64_t mrow = t0 + (m < L ? m : L - 1);
+        f32x4 vb[VT];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) kb[e] = bm * kv[e] * __expf(G[e]);
-            }
-            mma(acc, *reinterpret_cast<const f32x4 *>(sW + (16 * it + lr) * LDK + c0), kb);
+        for (int js = 0; js < VT; ++js) vb[js] = load4(vin + mrow * rsv + (int64_t)h * DV + 16 * js + 4 * q4);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int js = 0; js < VT; ++js)
+            mma(acc, *reinterpret_cast<const f32x4 *>(sdU + (16 * it + lr) * LDV + 16 * js + 4 * q4), vb[js] * bm);
+        f32x4 kv[KT], Gm[KT];
+#pragma unroll
+        for (int cs = 0; cs < KT; ++cs) {
+            kv[cs] = load4(kin + mrow * rsk + (int64_t)h * DK + 16 * cs + 4 * q4);
+            Gm[cs] = *reinterpret_cast<const f32x4 *>(rec + R::oG + m * DK + 16 * cs + 4 * q4);
+        }
+#pragma unroll
+        for (int cs = 0; cs < KT; ++cs) {
+            f32x4 kb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kb[e] = bm * kv[cs][e] * __expf(Gm[cs][e]);
+            mma(acc, *reinterpret_cast<const f32x4 *>(sW + (16 * it + lr) * LDK + 16 * cs + 4 * q4), kb);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) sdT[(16 * it + 4 * q4 + e) * LDA + m] = acc[e];
     }
-    // dKg = Diag(beta) T^T dW for key tile ct (T[m][i] = 0 for m < i)
-    if (ct < KT) {
-        const int c = 16 * ct + lr;
+    // dKg = Diag(beta) T^T dW for key tile ct and dv = Diag(beta) T^T dU for value tile vt (both
+    // the wave's; T[m][i] = 0 for m < i). This lane's rows i = 16 it + 4 q4 + e of beta, G, k
+    // (channel 16 ct + lr) and v (column 16 vt + lr) are all loaded before the products.
+    const bool doK = ct < KT, doV = wave < VT;
+    if (doK || doV) {
+        const int c = 16 * (doK ? ct : 0) + lr, j = 16 * (doV ? wave : 0) + lr;
+        float bl[IT][4], Gl[IT][4], kl[IT][4], vl[IT][4];
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * it + 4 * q4 + e;
+                const int64_t row = t0 + (i < L ? i : L - 1);   // rows past the end: zeroed by beta
+                bl[it][e] = beta_of(i);
+                Gl[it][e] = rec[R::oG + i * DK + c];
+                kl[it][e] = i < L ? to_f32(kin[row * rsk + (int64_t)h * DK + c]) : 0.f;
+                vl[it][e] = i < L ? to_f32(vin[row * rsv + (int64_t)h * DV + j]) : 0.f;
+            }
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            f32x4 acc = zero4();
-            for (int ms = it; ms < IT; ++ms) {
-                f32x4 A, B;
+            f32x4 acc = zero4(), accv = zero4();
+#pragma unroll
+            for (int ms = 0; ms < IT; ++ms) {
+                if (ms < it) continue;
+                f32x4 A, B, Bv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int m = 16 * ms + 4 * q4 + e;
                     A[e] = sT[m * LDA + 16 * it + lr];
                     B[e] = sW[m * LDK + c];
+                    Bv[e] = sdU[m * LDV + j];
                 }
                 mma(acc, A, B);
+                mma(accv, A, Bv);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * it + 4 * q4 + e;
-                const float bi = beta_of(i);
-                const float G = rec[R::oG + i * DK + c];
-                const float eG = __expf(G);
-                const float kv = i < L ? to_f32(kin[(t0 + i) * rsk + (int64_t)h * DK + c]) : 0.f;
-                const float dKg = bi * acc[e];
-                dk_p[it][e] += eG * dKg;
-                dG_p[it][e] += kv * eG * dKg;
-                const float rs = sum16(acc[e] * kv * eG);
-                if (lr == 0) sDb[ct][i] = rs;
-            }
-        }
-    }
-    // dv = Diag(beta) T^T dU for value tile vt = wave
-    if (wave < VT) {
-        const int vt = wave, j = 16 * vt + lr;
-#pragma unroll
-        for (int it = 0; it < IT; ++it) {
-            f32x4 acc = zero4();
-            for (int ms = it; ms < IT; ++ms) {
-                f32x4 A, B;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = 16 * ms + 4 * q4 + e;
-                    A[e] = sT[m * LDA + 16 * it + lr];
-                    B[e] = sdU[m * LDV + j];
+                const float eG = __expf(Gl[it][e]);
+                const float dKg = bl[it][e] * acc[e];
+                if (doK) {
+                    dk_p[it][e] += eG * dKg;
+                    dG_p[it][e] += kl[it][e] * eG * dKg;
                 }
-                mma(acc, A, B);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * it + 4 * q4 + e;
-                const float vv = i < L ? to_f32(vin[(t0 + i) * rsv + (int64_t)h * DV + j]) : 0.f;
-                const float rs = sum16(acc[e] * vv);
-                if (lr == 0) sDb[KT + vt][i] = rs;
-                if (i < L) a.dv[(t0 + i) * rsv + (int64_t)h * DV + j] = beta_of(i) * acc[e];
+                const float rs = sum16(acc[e] * kl[it][e] * eG);
+                if (doK && lr == 0) sDb[ct][i] = rs;
+                const float rv = sum16(accv[e] * vl[it][e]);
+                if (doV && lr == 0) sDb[KT + wave][i] = rv;
+                if (doV && i < L) a.dv[(t0 + i) * rsv + (int64_t)h * DV + j] = bl[it][e] * accv[e];
             }
         }
     }
@@ -1073,8 +1317,8 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_prep_kernel<Tin, C, DK, DV>), gs, dim3(512), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 gc((unsigned)(a.n_seqs * a.H), (unsigned)(DV / 16), 2);
-    hipLaunchKernelGGL((bwd_state_kernel<C, DK, DV>), gc, dim3(64 * P::NW), 0, stream, a);
+    hipLaunchKernelGGL((bwd_state_kernel<C, DK, DV>), dim3(state_blocks<DV>(a.n_seqs * a.H)), dim3(64 * P::NW), 0,
+                       stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grad_kernel<Tin, C, DK, DV>), gs, dim3(512), 0, stream, a);
     return hipGetLastError();

@@ -197,6 +197,38 @@ def test_bf16_strong_decay():
     assert_close(S, S_ref, TOL_BF16, "final state")
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_bf16_large_values_within_fp16_range(split):
+    """Values and states 512 times larger than the workloads' (v ~ N(0, 512^2), initial
+    states of spectral norm 512): the fp16 matrix-core operands (S, U~, U, v) stay below fp16's
+    largest value 65504, the range precondition of the bf16 instantiation, and the result
+    holds the bf16 bound. (The scale is a power of two: the bf16 values are exact.)"""
+    T, H, D = 2500, 2, 128
+    x = random_inputs(185, T, H, D, "bf16")
+    x["v"] = synth.f64_to_bf16_bits(512.0 * synth.bf16_bits_to_f64(x["v"]))
+    s0 = 512.0 * random_states(186, 1, H, D)
+    note(f"bf16 large values split={split}")
+    o, S = gpu_chunk(x, "bf16", chunk=64, s0=s0, split=split)
+    o_ref, S_ref = run_oracle(x, "bf16", initial_state=s0)
+    assert float(np.max(np.abs(S_ref))) < 65504 and float(np.max(np.abs(o_ref))) < 65504
+    assert_close(o, o_ref, TOL_BF16, "o")
+    assert_close(S, S_ref, TOL_BF16, "final state")
+
+
+def test_f32_large_values_have_no_range_limit():
+    """The float32 instantiations carry no fp16 operands: values 10^6 times the workloads'."""
+    T, H, D = 700, 2, 64
+    x = random_inputs(187, T, H, D, "f32")
+    x["v"] = (x["v"].astype(np.float64) * 1e6).astype(np.float32)
+    s0 = (1e6 * random_states(188, 1, H, D)).astype(np.float32)
+    note("f32 large values")
+    o, S = gpu_chunk(x, "f32", chunk=64, s0=s0)
+    o_ref, S_ref = run_oracle(x, "f32", initial_state=s0)
+    assert float(np.max(np.abs(S_ref))) > 1e6
+    assert_close(o, o_ref, TOL_F32, "o")
+    assert_close(S, S_ref, TOL_F32, "final state")
+
+
 @pytest.mark.parametrize("g_min", [-2.0, -8.0, -40.0, -400.0])
 def test_bf16_extreme_decay(g_min):
     """Chunks whose blocks decay below e^-20 in some channels: bf16 off-diagonal operands and

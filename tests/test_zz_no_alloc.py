@@ -77,7 +77,12 @@ def test_noalloc_backward_matches_workspace_entry_point_twice():
 def test_noalloc_backward_rejects_beyond_scratch():
     """Records beyond the fixed scratch: refused before any launch, the outputs untouched."""
     torch = torch_mod()
-    T, H, D = 4096, 18, 128
+    # the fewest heads whose records at 4096 tokens exceed the fixed scratch (512 MiB)
+    T, D = 4096, 128
+    one = torch.zeros((1, T, 1, D), dtype=torch.bfloat16)
+    per_head = kda.chunk_bwd_workspace_bytes(one, one)
+    H = (512 << 20) // per_head + 1
+    assert per_head * H > 512 << 20 >= per_head * (H - 1)
     q = torch.zeros((1, T, H, D), dtype=torch.bfloat16, device="cuda")
     g = torch.zeros((1, T, H, D), dtype=torch.float32, device="cuda")
     beta = torch.zeros((1, T, H), dtype=torch.float32, device="cuda")

@@ -174,8 +174,11 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
     __shared__ __align__(16) float sK[C * LDK];
     __shared__ __align__(16) float sQ[C * LDX];   // q, then beta k e^G
     __shared__ __align__(16) float sG[C * LDX];   // G, then beta v
-    __shared__ __align__(16) float sA[C * LDA];   // A~
-    __shared__ __align__(16) float sT[C * LDA];   // T
+    // A~ and T; before A~ is formed, the split Qg^T tiles (for Qg^T dO)
+    __shared__ __align__(16) float sAT[2 * C * LDA];
+    float *const sA = sAT, *const sT = sAT + C * LDA;
+    static_assert(DK * C <= 2 * C * LDA, "split Qg^T tiles fit over A~ and T");
+    __shared__ __align__(16) f32x4 sMT[(C / 16) * (C / 16) * 64];   // split M^T tiles (for M^T dO)
     __shared__ float sB[C];
     __shared__ int sExt[C / 16];                   // 16-token blocks decaying below e^-60
 
@@ -262,9 +265,31 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
             qg[e] = a.scale * sQ[(i0 + e) * LDX + c] * __expf(G);
             kd[e] = sK[(i0 + e) * LDK + c] * __expf(gC - G);
         }
-        *reinterpret_cast<f32x4 *>(rec + R::oQgT + split_at<C / 16>(c, i0)) = split_pack(qg);
+        const f32x4 qgs = split_pack(qg);
+        *reinterpret_cast<f32x4 *>(rec + R::oQgT + split_at<C / 16>(c, i0)) = qgs;
+        *reinterpret_cast<f32x4 *>(sAT + split_at<C / 16>(c, i0)) = qgs;
         *reinterpret_cast<f32x4 *>(rec + R::oKdT + split_at<C / 16>(c, i0)) = split_pack(kd);
     }
+    // Qg^T dO (the dO part of dS in the reverse state pass) into dH's slot, which that pass
+    // reads before it writes it: wave w takes value-column tile w
+    constexpr int KTP = DK / 16;
+    Split dOs[ITP];
+#pragma unroll
+    for (int ms = 0; ms < ITP; ++ms) dOs[ms] = split(dpre[ms]);
+    __syncthreads();
+    {
+        const int w = tid >> 6, l = tid & 63;
+        if (w < VTP) {
+            for (int kt = 0; kt < KTP; ++kt) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ms = 0; ms < ITP; ++ms)
+                    mma3(acc, unpack(*reinterpret_cast<const f32x4 *>(sAT + afrag<ITP>(kt, ms, l))), dOs[ms]);
+                *reinterpret_cast<f32x4 *>(rec + R::odH + afrag<VTP>(kt, w, l)) = acc;
+            }
+        }
+    }
+    __syncthreads();  // A~ goes over the Qg^T tiles
     // A~ and M as 16x16 block pairs (I, J <= I) on the matrix cores, one pair per wave at a time:
     // e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j} with r the last row of block J (both factors
     // <= 1) or, on the diagonal, the block's first row (the second factor at most the block's
@@ -306,7 +331,9 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
                     rec[R::oA + i * C + j] = av;
                     mt[e] = j <= i ? a.scale * sm : 0.f;
                 }
-                *reinterpret_cast<f32x4 *>(rec + R::oM + split_at<C / 16>(j, i0)) = split_pack(mt);   // M^T
+                const f32x4 mts = split_pack(mt);   // M^T
+                *reinterpret_cast<f32x4 *>(rec + R::oM + split_at<C / 16>(j, i0)) = mts;
+                sMT[split_at<C / 16>(j, i0) / 4] = mts;
                 continue;
             }
             const int r = diag ? 16 * I : 16 * J + 15;
@@ -341,7 +368,9 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
                 mt[e] = j <= i ? a.scale * accM[e] : 0.f;
             }
             // M^T: row 16 J + lr, the four values of columns 16 I + 4 q4 ..
-            *reinterpret_cast<f32x4 *>(rec + R::oM + split_at<C / 16>(16 * J + lr, 16 * I + 4 * q4)) = split_pack(mt);
+            const f32x4 mts = split_pack(mt);
+            *reinterpret_cast<f32x4 *>(rec + R::oM + split_at<C / 16>(16 * J + lr, 16 * I + 4 * q4)) = mts;
+            sMT[split_at<C / 16>(16 * J + lr, 16 * I + 4 * q4) / 4] = mts;
         }
     }
     for (int p = tid; p < C * C; p += NT) {   // blocks above the diagonal (whole split groups of 0)
@@ -353,6 +382,19 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
+    {   // M^T dO (the dO part of dU in the reverse state pass) into dU's slot: wave w takes
+        // value-column tile w; M[m][i] = 0 for m < i
+        const int w = tid >> 6, l = tid & 63;
+        if (w < VTP) {
+#pragma unroll
+            for (int it = 0; it < ITP; ++it) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ms = it; ms < ITP; ++ms) mma3(acc, unpack(sMT[afrag<ITP>(it, ms, l) / 4]), dOs[ms]);
+                *reinterpret_cast<f32x4 *>(rec + R::odU + afrag<VTP>(it, w, l)) = acc;
+            }
+        }
+    }
     for (int idx = tid; idx < C * DK / 4; idx += NT) {  // beta k e^G over q (k and G die here)
         const int i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
         const f32x4 kv = *reinterpret_cast<const f32x4 *>(sK + i * LDK + c);
@@ -459,32 +501,6 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
             *reinterpret_cast<f32x4 *>(rec + R::oWT + afrag<C / 16>(nt, it, lane)) = split_pack(-acc);
         } else {
             *reinterpret_cast<f32x4 *>(rec + R::oU + afrag<DV / 16>(it, nt, lane)) = acc;
-        }
-    }
-    // The parts of the reverse state pass that do not depend on the state gradient, in the
-    // slots of dU and dH (which that pass reads before it writes them): M^T dO (the dO part of
-    // dU) and Qg^T dO (the dO part of dS). Wave w takes value-column tile w; the split M^T and
-    // Qg^T tiles were written above by this workgroup (the barrier's fence orders them).
-    __syncthreads();
-    if (wave < VTP) {
-        constexpr int KTP = DK / 16;
-        Split dOs[ITP];
-#pragma unroll
-        for (int ms = 0; ms < ITP; ++ms) dOs[ms] = split(dpre[ms]);
-        for (int kt = 0; kt < KTP; ++kt) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int ms = 0; ms < ITP; ++ms)
-                mma3(acc, unpack(*reinterpret_cast<const f32x4 *>(rec + R::oQgT + afrag<ITP>(kt, ms, lane))), dOs[ms]);
-            *reinterpret_cast<f32x4 *>(rec + R::odH + afrag<VTP>(kt, wave, lane)) = acc;
-        }
-#pragma unroll
-        for (int it = 0; it < ITP; ++it) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int ms = it; ms < ITP; ++ms)   // M[m][i] = 0 for m < i
-                mma3(acc, unpack(*reinterpret_cast<const f32x4 *>(rec + R::oM + afrag<ITP>(it, ms, lane))), dOs[ms]);
-            *reinterpret_cast<f32x4 *>(rec + R::odU + afrag<VTP>(it, wave, lane)) = acc;
         }
     }
 }
@@ -937,6 +953,12 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
 
     // dQg = dO S^T, dKd = U dS'^T, dW = -dU S^T for key tile ct; d e^{gC} = rowsum(S * dS')
     f32x4 dq_p[IT], dk_p[IT], dG_p[IT];
+    // this lane's G (channel 16 ct + lr, rows 16 X + 4 q4 + e), kept for the phases below
+    float Gr[IT][4];
+#pragma unroll
+    for (int X = 0; X < IT; ++X)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Gr[X][e] = 0.f;
     if (ct < KT) {
         // this lane's G, Qg, Kd (channel 16 ct + lr, rows 16 it + 4 q4 + e), read before the
         // products so that their latency hides under them
@@ -944,15 +966,15 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
         // Qg and Kd of rows 16 it + 4 q4 .. + 3: one group of the split Qg^T and Kd^T tiles
         // (head + tail, float32 to about 2^-17)
         const float gC = rec[R::oG + (C - 1) * DK + c];
-        float Gl[IT][4];
         f32x4 Ql[IT], Kl[IT];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             Ql[it] = unsplit(*reinterpret_cast<const f32x4 *>(rec + R::oQgT + afrag<IT>(ct, it, lane)));
             Kl[it] = unsplit(*reinterpret_cast<const f32x4 *>(rec + R::oKdT + afrag<IT>(ct, it, lane)));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Gl[it][e] = rec[R::oG + (16 * it + 4 * q4 + e) * DK + c];
+            for (int e = 0; e < 4; ++e) Gr[it][e] = rec[R::oG + (16 * it + 4 * q4 + e) * DK + c];
         }
+        const float (&Gl)[IT][4] = Gr;
         f32x4 aQ[IT], aK[IT], aW[IT];
 #pragma unroll
         for (int it = 0; it < IT; ++it) aQ[it] = aK[it] = aW[it] = zero4();
@@ -993,6 +1015,39 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (16 * it + 4 * q4 + e == L - 1) dG_p[it][e] += term;
+    }
+    // This lane's rows i = 16 X + 4 q4 + e of k, q (channel 16 ct + lr), of v (column 16 wave
+    // + lr) and of beta, for the dKg / dv products and the pair terms (G: Gr above), and the A~ and
+    // beta of this wave's lower tiles for dA: all loaded here, so that their latency hides
+    // under the products in between (rows past the sequence end read the last row and are
+    // zeroed where they are used)
+    const int cpr = 16 * (ct < KT ? ct : 0) + lr, jpr = 16 * (wave < VT ? wave : 0) + lr;
+    Tin kraw[IT][4], qraw[IT][4], vraw[IT][4];
+    float bl[IT][4];
+#pragma unroll
+    for (int X = 0; X < IT; ++X)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * X + 4 * q4 + e;
+            const int64_t row = t0 + (i < L ? i : L - 1);
+            const int64_t o = row * rsk + (int64_t)h * DK + cpr;
+            kraw[X][e] = kin[o];
+            qraw[X][e] = static_cast<const Tin *>(a.q)[o];
+            vraw[X][e] = vin[row * rsv + (int64_t)h * DV + jpr];
+            bl[X][e] = beta_of(i);
+        }
+    constexpr int NPT = (NLT + NWV - 1) / NWV;   // lower tiles per wave, at most
+    float Atp[NPT][4], btp[NPT][4];
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+        int it, jt;
+        tile_of(wave + u * NWV < NLT ? wave + u * NWV : 0, it, jt);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * it + 4 * q4 + e;
+            Atp[u][e] = rec[R::oA + i * C + 16 * jt + lr];
+            btp[u][e] = beta_of(i);
+        }
     }
     // dM = tril(dO U^T), written over M
     for (int p = wave; p < NLT; p += NWV) {
@@ -1055,22 +1110,19 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) sdT[(16 * it + 4 * q4 + e) * LDA + m] = acc[e];
     }
     // dKg = Diag(beta) T^T dW for key tile ct and dv = Diag(beta) T^T dU for value tile vt (both
-    // the wave's; T[m][i] = 0 for m < i). This lane's rows i = 16 it + 4 q4 + e of beta, G, k
-    // (channel 16 ct + lr) and v (column 16 vt + lr) are all loaded before the products.
+    // the wave's; T[m][i] = 0 for m < i), with the rows of beta, G, k and v loaded above
     const bool doK = ct < KT, doV = wave < VT;
     if (doK || doV) {
-        const int c = 16 * (doK ? ct : 0) + lr, j = 16 * (doV ? wave : 0) + lr;
-        float bl[IT][4], Gl[IT][4], kl[IT][4], vl[IT][4];
+        const int c = cpr, j = jpr;
+        float Gl[IT][4], kl[IT][4], vl[IT][4];
 #pragma unroll
         for (int it = 0; it < IT; ++it)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = 16 * it + 4 * q4 + e;
-                const int64_t row = t0 + (i < L ? i : L - 1);   // rows past the end: zeroed by beta
-                bl[it][e] = beta_of(i);
-                Gl[it][e] = rec[R::oG + i * DK + c];
-                kl[it][e] = i < L ? to_f32(kin[row * rsk + (int64_t)h * DK + c]) : 0.f;
-                vl[it][e] = i < L ? to_f32(vin[row * rsv + (int64_t)h * DV + j]) : 0.f;
+                const bool in = 16 * it + 4 * q4 + e < L;   // rows past the end: zeroed by beta too
+                Gl[it][e] = Gr[it][e];
+                kl[it][e] = in ? to_f32(kraw[it][e]) : 0.f;
+                vl[it][e] = in ? to_f32(vraw[it][e]) : 0.f;
             }
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
@@ -1127,7 +1179,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     }
     __syncthreads();
     // dA = -strictly_lower(X T^T); dbeta += rowsum(dA A~); dA~ = Diag(beta) dA over A~
-    for (int p = wave; p < NLT; p += NWV) {
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+        const int p = wave + u * NWV;
+        if (p >= NLT) break;
         int it, jt;
         tile_of(p, it, jt);
         f32x4 acc = zero4();
@@ -1140,10 +1195,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * it + 4 * q4 + e, j = 16 * jt + lr;
             const float dA = j < i ? -acc[e] : 0.f;
-            const float At = rec[R::oA + i * C + j];
-            const float rs = sum16(dA * At);
+            const float rs = sum16(dA * Atp[u][e]);
             if (lr == 0) sDb[KT + VT + jt][i] = rs;
-            sdA[i * LDA + j] = beta_of(i) * dA;
+            sdA[i * LDA + j] = btp[u][e] * dA;
         }
     }
     // the tiles above the diagonal of dA~ (in dW's space) are read by no block pair below
@@ -1172,22 +1226,18 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     const float scale = a.scale;
     if (ct < KT) {
         const int c = 16 * ct + lr;
-        // this lane's rows of k, q, G (zero past the sequence end; G is constant there). Row
-        // 16 X + 4 q4 + e of the token arrays is at lane_off + (16 X + e) * rsk: one per-lane
-        // offset plus a uniform one, so no per-row address stays live.
+        // this lane's rows of k and q (zero past the sequence end; G is constant there). Row
+        // 16 X + 4 q4 + e of the token arrays is at lane_off + (16 X + e) * rsk (the stores of
+        // dq and dk below).
         const int64_t lane_off = (t0 + 4 * q4) * rsk + (int64_t)h * DK + c;
-        const Tin *kl = kin + lane_off;
-        const Tin *ql = static_cast<const Tin *>(a.q) + lane_off;
-        float kr[IT][4], qr[IT][4], Gr[IT][4];
+        float kr[IT][4], qr[IT][4];
 #pragma unroll
         for (int X = 0; X < IT; ++X)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = 16 * X + 4 * q4 + e;
-                const int64_t ro = (int64_t)(16 * X + e) * rsk;
-                kr[X][e] = i < L ? to_f32(kl[ro]) : 0.f;
-                qr[X][e] = i < L ? to_f32(ql[ro]) : 0.f;
-                Gr[X][e] = rec[R::oG + i * DK + c];
+                const bool in = 16 * X + 4 * q4 + e < L;
+                kr[X][e] = in ? to_f32(kraw[X][e]) : 0.f;
+                qr[X][e] = in ? to_f32(qraw[X][e]) : 0.f;
             }
         float dq[IT][4], dk[IT][4], dG[IT][4];
 #pragma unroll
@@ -1283,7 +1333,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
                         }
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);  // one block pair at a time (register pressure)
             }
         }
         // dq and dk are complete; dG goes to LDS for the running sum

@@ -887,7 +887,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     constexpr int NG2 = 2 * IT * DK + KT * 768 + C * LDG;
     constexpr int NOU0 = 2 * C * LDV > 3 * C * LDA ? 2 * C * LDV : 3 * C * LDA;
     constexpr int NOU = NOU0 > NG2 ? NOU0 : NG2;
-    // dU, and dO then U, staged once for all waves; T, dT and T^T dT later take dO's and U's space
+    // dU, and dO then U (both split: 4-column groups of heads and tails), staged once for all
+    // waves; T, dT and T^T dT later take dO's and U's space
     __shared__ __align__(16) float sdU[C * LDV];
     __shared__ __align__(16) float sOU[NOU];
     __shared__ __align__(16) float sW[C * LDK];   // dW, then dA~ ([C][LDA])
@@ -920,33 +921,41 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
         const int i = idx / (DV / 4), j = 4 * (idx % (DV / 4));
         f32x4 dOv = zero4();
         if (i < L) dOv = *reinterpret_cast<const f32x4 *>(a.dout + (t0 + i) * rsv + (int64_t)h * DV + j);
-        *reinterpret_cast<f32x4 *>(sdO + i * LDV + j) = dOv;
-        // U and dU are in fragment order: vector idx is lane idx % 64 of tile idx / 64
+        *reinterpret_cast<f32x4 *>(sdO + i * LDV + j) = split_pack(dOv);
+        // U and dU are in fragment order: vector idx is lane idx % 64 of tile idx / 64. U goes
+        // to LDS split, element (r, c) as the head and tail at slots c % 4 and 4 + c % 4 of its
+        // row's 4-column group
         const f32x4 u = *reinterpret_cast<const f32x4 *>(rec + R::oU + 4 * idx);
         const f32x4 du = *reinterpret_cast<const f32x4 *>(rec + R::odU + 4 * idx);
         const int tile = idx >> 6, fl = idx & 63;
         const int r0 = 16 * (tile / VT) + 4 * (fl >> 4), cu = 16 * (tile % VT) + (fl & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            sU[(r0 + e) * LDV + cu] = u[e];
+            __bf16 *ug = reinterpret_cast<__bf16 *>(sU + (r0 + e) * LDV + (cu & ~3));
+            const __bf16 uh = static_cast<__bf16>(u[e]);
+            ug[cu & 3] = uh;
+            ug[4 + (cu & 3)] = static_cast<__bf16>(u[e] - static_cast<float>(uh));
             sdU[(r0 + e) * LDV + cu] = du[e];
         }
     }
     for (int idx = tid; idx < NSRC * C; idx += NT) (&sDb[0][0])[idx] = 0.f;
-    // this wave's rows of S and dS' (key tile ct = wave): the B fragments below
+    // this wave's rows of S and dS' (key tile ct = wave), split: the B fragments below
     const int ct = wave;
-    f32x4 hB[VT], dhB[VT];
+    Split hB[VT], dhB[VT];
     if (ct < KT) {
 #pragma unroll
         for (int js = 0; js < VT; ++js) {
             // S[16 ct + lr][16 js + 4 q4 + e] from fragment order: lane 16 (lr / 4) + 4 q4 + e of
             // tile (ct, js), element lr % 4
+            f32x4 hv, dhv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int64_t o = afrag<VT>(ct, js, 16 * (lr >> 2) + 4 * q4 + e) + (lr & 3);
-                hB[js][e] = rec[R::oH + o];
-                dhB[js][e] = rec[R::odH + o];
+                hv[e] = rec[R::oH + o];
+                dhv[e] = rec[R::odH + o];
             }
+            hB[js] = split(hv);
+            dhB[js] = split(dhv);
         }
     }
     __syncthreads();
@@ -985,11 +994,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
                 const int i = 16 * it + lr;
-                mma(aQ[it], *reinterpret_cast<const f32x4 *>(sdO + i * LDV + j0), hB[js]);
-                mma(aK[it], *reinterpret_cast<const f32x4 *>(sU + i * LDV + j0), dhB[js]);
-                mma(aW[it], *reinterpret_cast<const f32x4 *>(sdU + i * LDV + j0), hB[js]);
+                mma3(aQ[it], unpack(*reinterpret_cast<const f32x4 *>(sdO + i * LDV + j0)), hB[js]);
+                mma3(aK[it], unpack(*reinterpret_cast<const f32x4 *>(sU + i * LDV + j0)), dhB[js]);
+                mma3(aW[it], split(*reinterpret_cast<const f32x4 *>(sdU + i * LDV + j0)), hB[js]);
             }
-            dgc += hB[js][0] * dhB[js][0] + hB[js][1] * dhB[js][1] + hB[js][2] * dhB[js][2] + hB[js][3] * dhB[js][3];
+            const f32x4 hv = Mma<__bf16>::to_f32(hB[js].h) + Mma<__bf16>::to_f32(hB[js].t);
+            const f32x4 dhv = Mma<__bf16>::to_f32(dhB[js].h) + Mma<__bf16>::to_f32(dhB[js].t);
+            dgc += hv[0] * dhv[0] + hv[1] * dhv[1] + hv[2] * dhv[2] + hv[3] * dhv[3];
         }
         float cs = 0.f;
 #pragma unroll
@@ -1057,8 +1068,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int js = 0; js < VT; ++js) {
             const int j0 = 16 * js + 4 * q4;
-            mma(acc, *reinterpret_cast<const f32x4 *>(sdO + (16 * it + lr) * LDV + j0),
-                *reinterpret_cast<const f32x4 *>(sU + (16 * mt + lr) * LDV + j0));
+            mma3(acc, unpack(*reinterpret_cast<const f32x4 *>(sdO + (16 * it + lr) * LDV + j0)),
+                 unpack(*reinterpret_cast<const f32x4 *>(sU + (16 * mt + lr) * LDV + j0)));
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

@@ -165,6 +165,32 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // ------------------------------------------------------------------------------------------
 // 1. prep
 // ------------------------------------------------------------------------------------------
+// Four consecutive input elements kept as loaded (bf16: 8 bytes) until they are used, so that a
+// load issued early does not make the wave wait for it right away.
+template <typename Tin> struct In4;
+template <> struct In4<float> {
+    typedef f32x4 T;
+    static __device__ __forceinline__ T load(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+    static __device__ __forceinline__ T zero() { return zero4(); }
+    static __device__ __forceinline__ f32x4 f32(T x) { return x; }
+};
+template <> struct In4<bf16_t> {
+    typedef u32x2 T;
+    static __device__ __forceinline__ T load(const bf16_t *p) { return *reinterpret_cast<const u32x2 *>(p); }
+    static __device__ __forceinline__ T zero() { return u32x2{0u, 0u}; }
+    static __device__ __forceinline__ f32x4 f32(T u) {
+        f32x4 r;
+        r.x = __uint_as_float(u.x << 16);
+        r.y = __uint_as_float(u.x & 0xffff0000u);
+        r.z = __uint_as_float(u.y << 16);
+        r.w = __uint_as_float(u.y & 0xffff0000u);
+        return r;
+    }
+};
+
+// Prep runs persistently: each workgroup takes the (slot, head) items b, b + grid, ... and
+// loads the next item's inputs into registers while it computes the current one (one
+// workgroup fills a compute unit's LDS, so nothing else would hide that load).
 template <typename Tin, int C, int DK, int DV>
 __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
     using R = BRec<C, DK, DV>;
@@ -182,54 +208,87 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
     __shared__ float sB[C];
     __shared__ int sExt[C / 16];                   // 16-token blocks decaying below e^-60
 
-    const int64_t s = blockIdx.x;
-    const int h = blockIdx.y;
-    int n, L;
-    int64_t t0;
-    if (!locate<C>(a, s, n, t0, L)) return;
-    float *rec = a.ws + (s * a.H + h) * R::FLOATS;
     const int tid = threadIdx.x;
     const int64_t rsk = (int64_t)a.H * DK, rsv = (int64_t)a.H * DV;
-
-    // v is loaded with the other inputs and kept in registers until beta v is formed after T
-    constexpr int NVL = (C * DV / 4 + NT - 1) / NT;
-    f32x4 vpre[NVL];
-#pragma unroll
-    for (int u = 0; u < NVL; ++u) {
-        const int idx = tid + u * NT, i = idx / (DV / 4), c = 4 * (idx % (DV / 4));
-        vpre[u] = idx < C * DV / 4 && i < L
-                      ? load4(static_cast<const Tin *>(a.v) + (t0 + i) * rsv + (int64_t)h * DV + c) : zero4();
-    }
-    // dO for the products at the end: wave w takes value-column tile w, lane (lr, q4) the rows
-    // 16 ms + 4 q4 + e of column 16 w + lr (zero past the sequence end)
+    using I4 = In4<Tin>;
+    constexpr int NVL = (C * DV / 4 + NT - 1) / NT, NKL = (C * DK / 4 + NT - 1) / NT;
     constexpr int VTP = DV / 16, ITP = C / 16;
     static_assert(VTP <= NT / 64, "one value-column tile per wave");
+    // one item's inputs as loaded: k, q, g rows (4-element groups tid, tid + NT, ...), v rows
+    // and beta; zero past the sequence end
+    typename I4::T kin4[NKL], qin4[NKL], vin4[NVL];
+    f32x4 gin4[NKL];
+    float bin;
+    auto fetch = [&](int w) {
+        int n, L;
+        int64_t t0;
+        const int h = w % a.H;
+        if (!locate<C>(a, w / a.H, n, t0, L)) return false;
+#pragma unroll
+        for (int u = 0; u < NVL; ++u) {
+            const int idx = tid + u * NT, i = idx / (DV / 4), c = 4 * (idx % (DV / 4));
+            vin4[u] = idx < C * DV / 4 && i < L ? I4::load(static_cast<const Tin *>(a.v) + (t0 + i) * rsv + (int64_t)h * DV + c)
+                                                : I4::zero();
+        }
+#pragma unroll
+        for (int u = 0; u < NKL; ++u) {
+            const int idx = tid + u * NT, i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+            const bool in = idx < C * DK / 4 && i < L;
+            const int64_t off = (t0 + i) * rsk + (int64_t)h * DK + c;
+            kin4[u] = in ? I4::load(static_cast<const Tin *>(a.k) + off) : I4::zero();
+            qin4[u] = in ? I4::load(static_cast<const Tin *>(a.q) + off) : I4::zero();
+            gin4[u] = in ? *reinterpret_cast<const f32x4 *>(a.g + off) : zero4();
+        }
+        bin = tid < C && tid < L ? a.beta[(t0 + tid) * a.H + h] : 0.f;
+        return true;
+    };
+    const int items = (int)(a.nslots * a.H);   // below 2^31 (checked by the host)
+    bool have = (int)blockIdx.x < items && fetch(blockIdx.x);
+    for (int w = blockIdx.x; w < items; w += gridDim.x) {
+    // the thread index through an empty asm statement: the per-thread offsets below are
+    // recomputed for each item instead of being hoisted out of the loop and held in registers
+    int tid_ = threadIdx.x;
+    __asm__ volatile("" : "+v"(tid_));
+    const int tid = tid_;
+    const int h = w % a.H;
+    int n, L;
+    int64_t t0;
+    if (!locate<C>(a, w / a.H, n, t0, L)) {   // an unused slot: fetch the next item instead
+        have = w + gridDim.x < items && fetch(w + gridDim.x);
+        continue;
+    }
+    if (!have) fetch(w);
+    float *rec = a.ws + (int64_t)w * R::FLOATS;
+
+    // dO for the products below (wave w: value-column tile w, lane (lr, q4): rows
+    // 16 ms + 4 q4 + e of column 16 w + lr; zero past the sequence end)
     f32x4 dpre[ITP];
     {
-        const int w = tid >> 6, l = tid & 63;
-        const float *dcol = a.dout + (t0 + 4 * (l >> 4)) * rsv + (int64_t)h * DV + 16 * (w < VTP ? w : 0) + (l & 15);
+        const int w6 = tid >> 6, l = tid & 63;
+        const float *dcol = a.dout + (t0 + 4 * (l >> 4)) * rsv + (int64_t)h * DV + 16 * (w6 < VTP ? w6 : 0) + (l & 15);
 #pragma unroll
         for (int ms = 0; ms < ITP; ++ms)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * ms + 4 * (l >> 4) + e;
-                dpre[ms][e] = w < VTP && r < L ? dcol[(int64_t)(16 * ms + e) * rsv] : 0.f;
+                dpre[ms][e] = w6 < VTP && r < L ? dcol[(int64_t)(16 * ms + e) * rsv] : 0.f;
             }
     }
-    for (int idx = tid; idx < C * DK / 4; idx += NT) {
-        const int i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
-        f32x4 kv = zero4(), qv = zero4(), gv = zero4();
-        if (i < L) {
-            const int64_t off = (t0 + i) * rsk + (int64_t)h * DK + c;
-            kv = load4(static_cast<const Tin *>(a.k) + off);
-            qv = load4(static_cast<const Tin *>(a.q) + off);
-            gv = load4(a.g + off);
+    // this item's inputs to LDS (v stays in registers), then the next item's loads
+    f32x4 vpre[NVL];
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) vpre[u] = I4::f32(vin4[u]);
+#pragma unroll
+    for (int u = 0; u < NKL; ++u) {
+        const int idx = tid + u * NT, i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+        if (idx < C * DK / 4) {
+            *reinterpret_cast<f32x4 *>(sK + i * LDK + c) = I4::f32(kin4[u]);
+            *reinterpret_cast<f32x4 *>(sQ + i * LDX + c) = I4::f32(qin4[u]);
+            *reinterpret_cast<f32x4 *>(sG + i * LDX + c) = gin4[u];
         }
-        *reinterpret_cast<f32x4 *>(sK + i * LDK + c) = kv;
-        *reinterpret_cast<f32x4 *>(sQ + i * LDX + c) = qv;
-        *reinterpret_cast<f32x4 *>(sG + i * LDX + c) = gv;
     }
-    if (tid < C) sB[tid] = tid < L ? a.beta[(t0 + tid) * a.H + h] : 0.f;
+    if (tid < C) sB[tid] = bin;
+    have = w + gridDim.x < items && fetch(w + gridDim.x);
     if (tid < C / 16) sExt[tid] = 0;
     __syncthreads();
     if (tid < DK) {  // running sum along the chunk, one thread per channel
@@ -502,6 +561,8 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
         } else {
             *reinterpret_cast<f32x4 *>(rec + R::oU + afrag<DV / 16>(it, nt, lane)) = acc;
         }
+    }
+    __syncthreads();  // the LDS is the next item's
     }
 }
 
@@ -1370,11 +1431,27 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     }
 }
 
+// Compute units of the current device, queried once per device (0 if the query fails).
+int64_t compute_units() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (!n) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <typename Tin, int C, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     using P = StatePass<C, DK, DV>;
     const dim3 gs((unsigned)a.nslots, (unsigned)a.H);
-    hipLaunchKernelGGL((bwd_prep_kernel<Tin, C, DK, DV>), gs, dim3(512), 0, stream, a);
+    // prep: one persistent workgroup per compute unit (at most one per item)
+    const int64_t items = a.nslots * a.H, cus = compute_units();
+    const unsigned gp = (unsigned)(cus > 0 && cus < items ? cus : items);
+    hipLaunchKernelGGL((bwd_prep_kernel<Tin, C, DK, DV>), dim3(gp), dim3(512), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_state_kernel<C, DK, DV>), dim3(state_blocks<DV>(a.n_seqs * a.H)), dim3(64 * P::NW), 0,

@@ -64,9 +64,9 @@ template <int C, int DK, int DV> struct BRec {
     static constexpr int64_t oKdT = oT + C * C;       // [DK][C] Kd^T (split tiles)
     static constexpr int64_t oWT = oKdT + DK * C;     // [DK][C] -W^T (split tiles)
     static constexpr int64_t oQgT = oWT + DK * C;     // [DK][C] Qg^T (split tiles)
-    static constexpr int64_t oH = oQgT + DK * C;      // [DK][DV] state entering the chunk (fragment order)
-    static constexpr int64_t odH = oH + DK * DV;      // [DK][DV] Qg^T dO, then dL/d(state leaving the chunk)
-                                                      //         (fragment order)
+    static constexpr int64_t oH = oQgT + DK * C;      // [DK][DV] state entering the chunk (operand tiles)
+    static constexpr int64_t odH = oH + DK * DV;      // [DK][DV] Qg^T dO (fragment order), then
+                                                      //         dL/d(state leaving the chunk) (operand tiles)
     static constexpr int64_t FLOATS = (odH + DK * DV + 63) & ~int64_t(63);
 };
 
@@ -589,6 +589,23 @@ template <int C, int DK, int DV> struct StatePass {
 
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// A 16x16 tile from accumulator layout (lane (lr, q4): rows 4 q4 + e of column lr) to operand
+// layout (lane (lr, q4): row lr, columns 4 q4 + e), through a wave-private LDS tile of 16 rows
+// of 20 floats (the reads of one e fall in distinct banks).
+__device__ __forceinline__ f32x4 transpose16(f32x4 x, float *t, int lr, int q4) {
+    *reinterpret_cast<f32x4 *>(t + lr * 20 + 4 * q4) = x;   // t[c][r] = x[r][c]
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = t[(4 * q4 + e) * 20 + lr];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();   // every lane has read before the tile is written again
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return r;
+}
+
 // L2 touch of one step's operands: the 128-byte lines of NR record regions are
 // numbered in turn; value-column block vb touches the lines vb, vb + nvb, ..., one load per
 // thread (threads past the last line load the first one). The loaded word is kept and consumed
@@ -627,6 +644,7 @@ __device__ __forceinline__ void fwd_state_pass(const BwdArgs &a, int chain, int 
     using P = StatePass<C, DK, DV>;
     constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW, NOWN = P::NOWN, VT = P::VT;
     __shared__ f32x4 sPart[2][NW][IT][64];   // by step parity: one barrier per step
+    __shared__ float sTr[NW][16 * 20];        // per-wave transpose tile
     const int n = chain / a.H, h = chain % a.H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, q4 = lane >> 4;
     int64_t st, en;
@@ -681,7 +699,8 @@ __device__ __forceinline__ void fwd_state_pass(const BwdArgs &a, int chain, int 
         const float *nrec = rec_of(j + 1 < nch ? j + 1 : j);
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk)
-            *reinterpret_cast<f32x4 *>(rec + R::oH + afrag<VT>(wave * KTW + kk, vb, lane)) = S[kk];
+            *reinterpret_cast<f32x4 *>(rec + R::oH + afrag<VT>(wave * KTW + kk, vb, lane)) =
+                transpose16(S[kk], sTr[wave], lr, q4);   // operand layout: row lr, 4 columns
         Split Ss[KTW];
 #pragma unroll
         for (int kk = 0; kk < KTW; ++kk) Ss[kk] = split(S[kk]);
@@ -773,6 +792,7 @@ __device__ __forceinline__ void rev_state_pass(const BwdArgs &a, int chain, int 
     using P = StatePass<C, DK, DV>;
     constexpr int IT = P::IT, KTW = P::KTW, NW = P::NW, NOWN = P::NOWN, VT = P::VT;
     __shared__ f32x4 sPart[2][NW][IT][64];
+    __shared__ float sTr[NW][16 * 20];        // per-wave transpose tile
     const int n = chain / a.H, h = chain % a.H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, q4 = lane >> 4;
     int64_t st, en;
@@ -878,7 +898,8 @@ __device__ __forceinline__ void rev_state_pass(const BwdArgs &a, int chain, int 
             dS[kk] = dS[kk] * cur.eg[kk] + cur.P2[kk];
 #pragma unroll
             for (int it = 0; it < IT; ++it) mma3(dS[kk], unpack(cur.WT[kk][it]), dUs[it]);   // -W^T dU
-            *reinterpret_cast<f32x4 *>(rec + R::odH + afrag<VT>(wave * KTW + kk, vb, lane)) = dSo;
+            *reinterpret_cast<f32x4 *>(rec + R::odH + afrag<VT>(wave * KTW + kk, vb, lane)) =
+                transpose16(dSo, sTr[wave], lr, q4);   // operand layout: row lr, 4 columns
         }
     };
     RevOps<C, DK, DV> o0, o1;
@@ -1006,17 +1027,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     if (ct < KT) {
 #pragma unroll
         for (int js = 0; js < VT; ++js) {
-            // S[16 ct + lr][16 js + 4 q4 + e] from fragment order: lane 16 (lr / 4) + 4 q4 + e of
-            // tile (ct, js), element lr % 4
-            f32x4 hv, dhv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t o = afrag<VT>(ct, js, 16 * (lr >> 2) + 4 * q4 + e) + (lr & 3);
-                hv[e] = rec[R::oH + o];
-                dhv[e] = rec[R::odH + o];
-            }
-            hB[js] = split(hv);
-            dhB[js] = split(dhv);
+            // S[16 ct + lr][16 js + 4 q4 + e]: the state passes store H and dH tiles in operand
+            // layout, so this lane's 4 values are one 16-byte group
+            hB[js] = split(*reinterpret_cast<const f32x4 *>(rec + R::oH + afrag<VT>(ct, js, lane)));
+            dhB[js] = split(*reinterpret_cast<const f32x4 *>(rec + R::odH + afrag<VT>(ct, js, lane)));
         }
     }
     __syncthreads();

@@ -49,6 +49,9 @@ PREFILL_KERNELS = ("chunk_fwd_kernel", "replay_kernel", "split_combine_kernel") 
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_decode_step_decode_256x32_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_26_amd", "csrc", "kda_decode.hip")
 DECODE_KERNELS = ("decode_kernel",)
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_bwd_backward_4k_h16_traffic.json")
+BWD_SRC = os.path.join(ROOT, "gated_delta_rule_26_amd", "csrc", "kda_chunk_bwd.hip")
+BWD_KERNELS = ("bwd_prep_kernel", "bwd_state_kernel", "bwd_grad_kernel")
 DECODE_STEPS = 1000   # the decode workload: 1000 consecutive steps per timed block
 COPY_BYTES = 1 << 30  # calibration: read 1 GiB, write 1 GiB
 
@@ -168,7 +171,7 @@ def traffic_from(fetch_csv: str, write_csv: str, kernels=PREFILL_KERNELS,
             if cname not in ("FETCH_SIZE", "WRITE_SIZE"):
                 continue
             if any(k in name for k in kernels):
-                short = kernel_label(name) if kernels == PREFILL_KERNELS else kernels[0]
+                short = kernel_label(name) if kernels == PREFILL_KERNELS else next(k for k in kernels if k in name)
                 kib, n = per_kernel.get(short, (0.0, 0))
                 per_kernel[short] = (kib + val, n + 1)
                 if call_kernel in name:
@@ -191,12 +194,15 @@ def traffic_from(fetch_csv: str, write_csv: str, kernels=PREFILL_KERNELS,
 
 
 def write_traffic(fetch_csv: str, write_csv: str) -> None:
-    """The prefill call's and the decode step's traffic files from the counter pass."""
+    """The prefill call's, the decode step's and the backward call's traffic files from the
+    counter pass."""
     for path, src, workload, kernels, call in (
             (TRAFFIC_FILE, KERNEL_SRC, "prefill_128k_h32 (one kda_chunk_fwd call)", PREFILL_KERNELS,
              "chunk_fwd_kernel"),
             (DECODE_TRAFFIC_FILE, DECODE_SRC, "decode_256x32 (one kda_decode_step call)", DECODE_KERNELS,
-             "decode_kernel")):
+             "decode_kernel"),
+            (BWD_TRAFFIC_FILE, BWD_SRC, "backward_4k_h16 (one kda_chunk_bwd call)", BWD_KERNELS,
+             "bwd_grad_kernel")):
         t = traffic_from(fetch_csv, write_csv, kernels, call)
         res = {
             "kernel_source_sha": kernel_sha(src),
@@ -286,8 +292,9 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
         "ms": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
         "cache": "resident (back to back)",
         "ms_cold": round(ms_cold, 4), "tokens_per_s_cold": round(w.T / (ms_cold * 1e-3), 1),
-        # float32 throughout: the fp32 matrix cores bind (about 99 flop per algorithmic byte
-        # against a ridge of about 20), not HBM
+        # float32-accurate throughout (products in float32 or as three bf16 products of split
+        # factors): the matrix cores bind (about 99 flop per algorithmic byte against a ridge
+        # of about 20), priced at the fp32 matrix peak
         "roofline": {"bound": "mfma_f32", "achieved": round(bf / (ms * 1e-3) / 1e12, 2),
                      "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bf / (ms * 1e-3) / 1e12 / MFMA_F32_PEAK_TFLOPS, 4),
@@ -296,7 +303,8 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
         "frac_hbm": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "bytes_per_token_head": bwd_bytes_per_token_head(w.K, w.V),
         "workspace_bytes": wsb.numel(),
-        "what": "kda_chunk_bwd: dq, dk, dv, dg, dbeta from dL/do (float32 arithmetic)"}
+        "traffic": load_traffic(bb, BWD_TRAFFIC_FILE, BWD_SRC),
+        "what": "kda_chunk_bwd: dq, dk, dv, dg, dbeta from dL/do (float32 accuracy)"}
     del q, k, v, g, b, do, wsb, grads, x, flush
     log("timed backward_4k_h16")
 

@@ -16,11 +16,15 @@
 // plus the pairwise terms of A~ and M (per channel, e^{G_i - G_j} <= 1 for j <= i) and, for g,
 // the reverse running sum of dL/dG inside the chunk.
 //
-// Mapping to the MI355X. Everything is float32 (fp32 matrix cores, v_mfma_f32_16x16x4f32).
-// Three launches, each a plain pass over a per-(chunk, head) record in the workspace:
-//  1. prep    (one workgroup per chunk and head): G, Qg, Kd, e^{gC}, A~ and M as 16x16 block
-//             pairs on the matrix cores (decay split at block boundaries; pair by pair for a
-//             block decaying below e^-60), T by column substitution in one wave, W and U~.
+// Mapping to the MI355X. Every result is float32-accurate: products run either on the fp32
+// matrix cores (v_mfma_f32_16x16x4f32) or, where their operands are stored or staged split into
+// bf16 heads and tails, as three bf16 matrix-core products (tail x head, head x tail, head x
+// head; about 2^-17 relative). Three launches over a per-(chunk, head) record in the workspace:
+//  1. prep    (persistent: one workgroup per compute unit, each taking (chunk, head) items in
+//             turn and prefetching the next item's inputs): G, Kd, e^{gC}, A~ and M as 16x16
+//             block pairs on the matrix cores (decay split at block boundaries; pair by pair
+//             for a block decaying below e^-60), T by blocked substitution, W and U~, and the
+//             parts of the reverse state pass that do not depend on dS' (M^T dO, Qg^T dO).
 //  2. state   the forward state pass (chunks in order: the state entering each chunk, and U)
 //             and the reverse one (chunks in reverse: dS' and dU, then dS_init) side by side,
 //             per chain and 16 value columns; the reverse pass needs only prep's records.
@@ -59,8 +63,7 @@ template <int C, int DK, int DV> struct BRec {
     static constexpr int64_t odU = oU + C * DV;       // [C][DV] M^T dO, then dU (fragment order)
     static constexpr int64_t oEg = odU + C * DV;      // [DK]    e^{gC}
     static constexpr int64_t oA = oEg + DK;           // [C][C]  A~ (strictly lower), then dA~
-    static constexpr int64_t oM = oA + C * C;         // [C][C]  M^T (upper, split tiles)
-    static constexpr int64_t oT = oM + C * C;         // [C][C]  T
+    static constexpr int64_t oT = oA + C * C;         // [C][C]  T
     static constexpr int64_t oKdT = oT + C * C;       // [DK][C] Kd^T (split tiles)
     static constexpr int64_t oWT = oKdT + DK * C;     // [DK][C] -W^T (split tiles)
     static constexpr int64_t oQgT = oWT + DK * C;     // [DK][C] Qg^T (split tiles)
@@ -390,9 +393,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
                     rec[R::oA + i * C + j] = av;
                     mt[e] = j <= i ? a.scale * sm : 0.f;
                 }
-                const f32x4 mts = split_pack(mt);   // M^T
-                *reinterpret_cast<f32x4 *>(rec + R::oM + split_at<C / 16>(j, i0)) = mts;
-                sMT[split_at<C / 16>(j, i0) / 4] = mts;
+                sMT[split_at<C / 16>(j, i0) / 4] = split_pack(mt);   // M^T
                 continue;
             }
             const int r = diag ? 16 * I : 16 * J + 15;
@@ -427,17 +428,14 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
                 mt[e] = j <= i ? a.scale * accM[e] : 0.f;
             }
             // M^T: row 16 J + lr, the four values of columns 16 I + 4 q4 ..
-            const f32x4 mts = split_pack(mt);
-            *reinterpret_cast<f32x4 *>(rec + R::oM + split_at<C / 16>(16 * J + lr, 16 * I + 4 * q4)) = mts;
-            sMT[split_at<C / 16>(16 * J + lr, 16 * I + 4 * q4) / 4] = mts;
+            sMT[split_at<C / 16>(16 * J + lr, 16 * I + 4 * q4) / 4] = split_pack(mt);
         }
     }
-    for (int p = tid; p < C * C; p += NT) {   // blocks above the diagonal (whole split groups of 0)
+    for (int p = tid; p < C * C; p += NT) {   // A~'s blocks above the diagonal
         const int i = p / C, j = p % C;
         if ((j >> 4) > (i >> 4)) {
             sA[i * LDA + j] = 0.f;
             rec[R::oA + p] = 0.f;
-            rec[R::oM + split_at<C / 16>(j, i & ~3) + (i & 3)] = 0.f;
         }
     }
     __syncthreads();

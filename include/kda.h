@@ -323,9 +323,9 @@ kda_status kda_chunk_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv
  * nothing (no hipMalloc, hipFree or allocating library routine): the outputs are the
  * caller's.
  *   A problem whose records need more than KDA_BWD_SCRATCH_BYTES, i.e. whose
- *   kda_chunk_bwd_workspace_bytes(...) exceeds it (at chunk 64, Dk = Dv = 128: 1212 record
+ *   kda_chunk_bwd_workspace_bytes(...) exceeds it (at chunk 64, Dk = Dv = 128: 1258 record
  *   slots x heads, where a sequence takes one slot more than its chunks; e.g. 4096 tokens
- *   fit with up to 18 heads), returns KDA_ERR_WORKSPACE_TOO_SMALL with nothing launched.
+ *   fit with up to 19 heads), returns KDA_ERR_WORKSPACE_TOO_SMALL with nothing launched.
  *   Every call on one device uses that device's single array: calls that overlap on one
  *   device (on different streams, or from several host threads) race and give wrong
  *   results; calls in one stream's order do not. Nothing in the array needs to start at zero

@@ -354,7 +354,7 @@ def bwd_noalloc(lib, B=1, T=64, H=2, Dk=128, Dv=128, C=64, ind=BF16, scale=1.0, 
     (dict(dg=MIS), INVALID), (dict(ds0=MIS), INVALID),
     (dict(Dk=64, Dv=64), UNSUPPORTED), (dict(C=32), UNSUPPORTED),
     # records beyond the fixed scratch: 4096 tokens x 18 heads, or 128K tokens x 32 heads
-    (dict(T=4096, H=19), WS_SMALL), (dict(T=131072, H=32), WS_SMALL),
+    (dict(T=4096, H=20), WS_SMALL), (dict(T=131072, H=32), WS_SMALL),
 ])
 def test_chunk_bwd_noalloc_rejects_before_launch(lib, kw, status):
     assert bwd_noalloc(lib, **kw) == status
@@ -362,11 +362,11 @@ def test_chunk_bwd_noalloc_rejects_before_launch(lib, kw, status):
 
 
 def test_chunk_bwd_noalloc_scratch_limit(lib):
-    """The fixed scratch (512 MiB) holds the records of 4096 tokens x 18 heads, not 19."""
+    """The fixed scratch (512 MiB) holds the records of 4096 tokens x 19 heads, not 20."""
     limit = 512 << 20
-    assert lib.kda_chunk_bwd_workspace_bytes(1, 4096, 18, 128, 128, 64, BF16, 1) <= limit
-    assert lib.kda_chunk_bwd_workspace_bytes(1, 4096, 19, 128, 128, 64, BF16, 1) > limit
-    assert bwd_noalloc(lib, T=4096, H=19) == WS_SMALL
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 4096, 19, 128, 128, 64, BF16, 1) <= limit
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 4096, 20, 128, 128, 64, BF16, 1) > limit
+    assert bwd_noalloc(lib, T=4096, H=20) == WS_SMALL
     assert b"fixed scratch" in lib.kda_last_error()
 
 

@@ -190,6 +190,8 @@ kda_status check_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, in
     a.ds0 = d_initial_state;
     a.ws = nullptr;
     a.nslots = num_seqs + (tokens + chunk - 1) / chunk;
+    // record slots x heads index the kernels' work items in 32 bits (far beyond any workspace)
+    if (a.nslots * H > ((int64_t)1 << 30)) return fail(KDA_ERR_INVALID_ARGUMENT, "problem too large");
     return KDA_OK;
 }
 

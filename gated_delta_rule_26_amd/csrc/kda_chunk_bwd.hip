@@ -62,7 +62,7 @@ template <int C, int DK, int DV> struct BRec {
     static constexpr int64_t oU = oW + C * DK;        // [C][DV] U~, then U (fragment order)
     static constexpr int64_t odU = oU + C * DV;       // [C][DV] M^T dO, then dU (fragment order)
     static constexpr int64_t oEg = odU + C * DV;      // [DK]    e^{gC}
-    static constexpr int64_t oA = oEg + DK;           // [C][C]  A~ (strictly lower), then dA~
+    static constexpr int64_t oA = oEg + DK;           // [C][C]  A~ (strictly lower)
     static constexpr int64_t oT = oA + C * C;         // [C][C]  T
     static constexpr int64_t oKdT = oT + C * C;       // [DK][C] Kd^T (split tiles)
     static constexpr int64_t oWT = oKdT + DK * C;     // [DK][C] -W^T (split tiles)
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
         bin = tid < C && tid < L ? a.beta[(t0 + tid) * a.H + h] : 0.f;
         return true;
     };
-    const int items = (int)(a.nslots * a.H);   // below 2^31 (checked by the host)
+    const int items = (int)(a.nslots * a.H);   // at most 2^30 (checked by the host)
     bool have = (int)blockIdx.x < items && fetch(blockIdx.x);
     for (int w = blockIdx.x; w < items; w += gridDim.x) {
     // the thread index through an empty asm statement: the per-thread offsets below are

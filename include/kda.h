@@ -296,11 +296,15 @@ typedef enum kda_activation { KDA_ACT_NONE = 0, KDA_ACT_SILU = 1 } kda_activatio
  *                initial_state is NULL (the gradient at a zero initial state)
  *   workspace    device buffer of at least kda_chunk_bwd_workspace_bytes(...) bytes (required);
  *                it holds per-(chunk, head) intermediates and is overwritten
- * All arithmetic is float32. Compiled instantiations (in_dtype, chunk, Dk = Dv): (KDA_BF16, 64,
- * 128), (KDA_F32, 64, 128) and (KDA_F32, 16, 16); others return KDA_ERR_UNSUPPORTED (the
- * forward need not have an instantiation of its own at the same sizes). Output buffers must not overlap the
- * inputs or each other. Errors as kda_chunk_fwd (KDA_ERR_WORKSPACE_TOO_SMALL for a short
- * workspace); nothing is launched and no output is written on an error.
+ * Every result is float32-accurate: products run on the fp32 matrix cores or as three bf16
+ * products of factors split into bf16 heads and tails (about 2^-17 relative). Compiled
+ * instantiations (in_dtype, chunk, Dk = Dv): (KDA_BF16, 64, 128), (KDA_F32, 64, 128) and
+ * (KDA_F32, 16, 16); others return KDA_ERR_UNSUPPORTED (the forward need not have an
+ * instantiation of its own at the same sizes). Output buffers must not overlap the inputs or
+ * each other. Errors as kda_chunk_fwd (KDA_ERR_WORKSPACE_TOO_SMALL for a short workspace;
+ * KDA_ERR_INVALID_ARGUMENT also when the record slots times heads, (num_seqs +
+ * ceil(B*T / chunk)) * H, exceed 2^30); nothing is launched and no output is written on an
+ * error.
  */
 size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
                                      int32_t chunk, int32_t in_dtype, int32_t num_seqs);

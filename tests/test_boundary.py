@@ -316,6 +316,7 @@ def bwd(lib, B=1, T=64, H=2, Dk=128, Dv=128, C=64, ind=BF16, scale=1.0, q=P, k=P
     (dict(B=2, cu=P, N=1), INVALID), (dict(B=2, N=1), INVALID),
     (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(db=None), INVALID),
     (dict(dg=MIS), INVALID), (dict(ds0=MIS), INVALID), (dict(ws=MIS), INVALID),
+    (dict(cu=P, N=1 << 29, H=4), INVALID),   # record slots x heads beyond 2^30
     (dict(Dk=64, Dv=64), UNSUPPORTED), (dict(C=32), UNSUPPORTED),
     (dict(ind=BF16, Dk=16, Dv=16, C=16), UNSUPPORTED),
     (dict(ws=None, wsb=0), WS_SMALL), (dict(wsb=1024), WS_SMALL),
@@ -351,6 +352,7 @@ def bwd_noalloc(lib, B=1, T=64, H=2, Dk=128, Dv=128, C=64, ind=BF16, scale=1.0, 
     (dict(ind=5), INVALID), (dict(scale=float("nan")), INVALID),
     (dict(B=2, cu=P, N=1), INVALID), (dict(B=2, N=1), INVALID),
     (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(db=None), INVALID),
+    (dict(cu=P, N=1 << 29, H=4), INVALID),
     (dict(dg=MIS), INVALID), (dict(ds0=MIS), INVALID),
     (dict(Dk=64, Dv=64), UNSUPPORTED), (dict(C=32), UNSUPPORTED),
     # records beyond the fixed scratch: 4096 tokens x 18 heads, or 128K tokens x 32 heads

@@ -962,6 +962,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     constexpr int LDK = DK + 4, LDA = C + 4, LDV = DV + 4;
     constexpr int NSRC = KT + VT + IT;      // dbeta partial sums, one row per source
     static_assert(KT <= NWV && VT <= NWV, "one key / value column tile per wave");
+    static_assert((IT / 2 + 1) * (IT - IT / 2) <= 2 * NWV, "the dT tile pairs fit the waves");
     constexpr int LDG = DK + 1;
     // the pair-term phase's arrays, over dO / U / T / dT / X once those are done
     constexpr int NG2 = 2 * IT * DK + KT * 768 + C * LDG;
@@ -997,39 +998,67 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     };
     auto beta_of = [&](int i) { return i < L ? a.beta[(t0 + i) * a.H + h] : 0.f; };
 
-    for (int idx = tid; idx < C * DV / 4; idx += NT) {
+    // Every load of this phase goes out before the first LDS store: dO, U and dU for the
+    // staging (NI 16-byte groups per thread), then this wave's rows of S and dS' (key tile
+    // ct = wave), which become the split B fragments below.
+    constexpr int NG = C * DV / 4, NI = (NG + NT - 1) / NT;
+    f32x4 dOv[NI], uv[NI], duv[NI];
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+        const int idx = NG % NT == 0 || tid + m * NT < NG ? tid + m * NT : 0;  // past NG: unused
         const int i = idx / (DV / 4), j = 4 * (idx % (DV / 4));
-        f32x4 dOv = zero4();
-        if (i < L) dOv = *reinterpret_cast<const f32x4 *>(a.dout + (t0 + i) * rsv + (int64_t)h * DV + j);
-        *reinterpret_cast<f32x4 *>(sdO + i * LDV + j) = split_pack(dOv);
+        // rows past the end read the last valid row (L >= 1 here) and are zeroed below
+        dOv[m] = *reinterpret_cast<const f32x4 *>(a.dout + (t0 + (i < L ? i : L - 1)) * rsv + (int64_t)h * DV + j);
+        uv[m] = *reinterpret_cast<const f32x4 *>(rec + R::oU + 4 * idx);
+        duv[m] = *reinterpret_cast<const f32x4 *>(rec + R::odU + 4 * idx);
+    }
+    const int ct = wave;
+    // (without a branch: waves past the last key tile load the last one and do not use it, so
+    // that the waits below are counted for the loads in flight on every path)
+    const int ctl = ct < KT ? ct : KT - 1;
+    f32x4 hraw[VT], dhraw[VT];
+#pragma unroll
+    for (int js = 0; js < VT; ++js) {
+        // S[16 ct + lr][16 js + 4 q4 + e]: the state passes store H and dH tiles in operand
+        // layout, so this lane's 4 values are one 16-byte group
+        hraw[js] = *reinterpret_cast<const f32x4 *>(rec + R::oH + afrag<VT>(ctl, js, lane));
+        dhraw[js] = *reinterpret_cast<const f32x4 *>(rec + R::odH + afrag<VT>(ctl, js, lane));
+    }
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+        const int idx = tid + m * NT;
+        if (NG % NT != 0 && idx >= NG) break;
+        const int i = idx / (DV / 4), j = 4 * (idx % (DV / 4));
+        // zeroed by a bit mask rather than a select, which the compiler would turn back into
+        // a load under a branch (and then wait for every load in flight at the merge)
+        const uint32_t keep = i < L ? 0xffffffffu : 0u;
+        f32x4 d;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = __uint_as_float(__float_as_uint(dOv[m][e]) & keep);
+        *reinterpret_cast<f32x4 *>(sdO + i * LDV + j) = split_pack(d);
         // U and dU are in fragment order: vector idx is lane idx % 64 of tile idx / 64. U goes
         // to LDS split, element (r, c) as the head and tail at slots c % 4 and 4 + c % 4 of its
         // row's 4-column group
-        const f32x4 u = *reinterpret_cast<const f32x4 *>(rec + R::oU + 4 * idx);
-        const f32x4 du = *reinterpret_cast<const f32x4 *>(rec + R::odU + 4 * idx);
         const int tile = idx >> 6, fl = idx & 63;
         const int r0 = 16 * (tile / VT) + 4 * (fl >> 4), cu = 16 * (tile % VT) + (fl & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             __bf16 *ug = reinterpret_cast<__bf16 *>(sU + (r0 + e) * LDV + (cu & ~3));
-            const __bf16 uh = static_cast<__bf16>(u[e]);
+            const __bf16 uh = static_cast<__bf16>(uv[m][e]);
             ug[cu & 3] = uh;
-            ug[4 + (cu & 3)] = static_cast<__bf16>(u[e] - static_cast<float>(uh));
-            sdU[(r0 + e) * LDV + cu] = du[e];
+            ug[4 + (cu & 3)] = static_cast<__bf16>(uv[m][e] - static_cast<float>(uh));
+            sdU[(r0 + e) * LDV + cu] = duv[m][e];
         }
     }
     for (int idx = tid; idx < NSRC * C; idx += NT) (&sDb[0][0])[idx] = 0.f;
-    // this wave's rows of S and dS' (key tile ct = wave), split: the B fragments below
-    const int ct = wave;
+    // the split B fragments of this wave's rows of S and dS'
     Split hB[VT], dhB[VT];
-    if (ct < KT) {
 #pragma unroll
-        for (int js = 0; js < VT; ++js) {
-            // S[16 ct + lr][16 js + 4 q4 + e]: the state passes store H and dH tiles in operand
-            // layout, so this lane's 4 values are one 16-byte group
-            hB[js] = split(*reinterpret_cast<const f32x4 *>(rec + R::oH + afrag<VT>(ct, js, lane)));
-            dhB[js] = split(*reinterpret_cast<const f32x4 *>(rec + R::odH + afrag<VT>(ct, js, lane)));
-        }
+    for (int js = 0; js < VT; ++js) {
+        hB[js] = split(hraw[js]);
+        dhB[js] = split(dhraw[js]);
+        // formed here, once: without the pin the compiler re-forms them at every use below
+        asm volatile("" : "+v"(hB[js].h), "+v"(hB[js].t), "+v"(dhB[js].h), "+v"(dhB[js].t));
     }
     __syncthreads();
 
@@ -1161,37 +1190,54 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // dT = dU (beta v)^T + dW (beta k e^G)^T, lower tiles
-    for (int p = wave; p < NLT; p += NWV) {
-        int it, mt;
-        tile_of(p, it, mt);
-        const int m = 16 * mt + lr;
-        const float bm = beta_of(m);  // 0 past the sequence end, which zeroes those rows
-        // every load of the tile goes out before its products (a row past the end reads the
-        // last valid row: finite, then zeroed by bm)
-        const int64_t mrow = t0 + (m < L ? m : L - 1);
-        f32x4 vb[VT];
-#pragma unroll
-        for (int js = 0; js < VT; ++js) vb[js] = load4(vin + mrow * rsv + (int64_t)h * DV + 16 * js + 4 * q4);
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int js = 0; js < VT; ++js)
-            mma(acc, *reinterpret_cast<const f32x4 *>(sdU + (16 * it + lr) * LDV + 16 * js + 4 * q4), vb[js] * bm);
-        f32x4 kv[KT], Gm[KT];
-#pragma unroll
-        for (int cs = 0; cs < KT; ++cs) {
-            kv[cs] = load4(kin + mrow * rsk + (int64_t)h * DK + 16 * cs + 4 * q4);
-            Gm[cs] = *reinterpret_cast<const f32x4 *>(rec + R::oG + m * DK + 16 * cs + 4 * q4);
+    // dT = dU (beta v)^T + dW (beta k e^G)^T, lower tiles. The tiles (it, mt) of one column
+    // block mt share their right operands (rows 16 mt .. 16 mt + 15 of beta v and of
+    // beta k e^G): they go in pairs to one wave, which loads those rows once for both.
+    {
+        int g = wave, mt = 0;   // this wave's pair: column block mt, rows it0 (and it0 + 1)
+        while (mt < IT && g >= (IT - mt + 1) / 2) {
+            g -= (IT - mt + 1) / 2;
+            ++mt;
         }
+        if (mt < IT) {
+            const int it0 = mt + 2 * g;
+            const bool two = it0 + 1 < IT;
+            const int it1 = two ? it0 + 1 : it0;
+            const int m = 16 * mt + lr;
+            const float bm = beta_of(m);  // 0 past the sequence end, which zeroes those rows
+            // every load goes out before its products (a row past the end reads the last
+            // valid row: finite, then zeroed by bm)
+            const int64_t mrow = t0 + (m < L ? m : L - 1);
+            f32x4 vb[VT];
 #pragma unroll
-        for (int cs = 0; cs < KT; ++cs) {
-            f32x4 kb;
+            for (int js = 0; js < VT; ++js) vb[js] = load4(vin + mrow * rsv + (int64_t)h * DV + 16 * js + 4 * q4);
+            f32x4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) kb[e] = bm * kv[cs][e] * __expf(Gm[cs][e]);
-            mma(acc, *reinterpret_cast<const f32x4 *>(sW + (16 * it + lr) * LDK + 16 * cs + 4 * q4), kb);
+            for (int js = 0; js < VT; ++js) {
+                const f32x4 b = vb[js] * bm;
+                mma(acc0, *reinterpret_cast<const f32x4 *>(sdU + (16 * it0 + lr) * LDV + 16 * js + 4 * q4), b);
+                if (two) mma(acc1, *reinterpret_cast<const f32x4 *>(sdU + (16 * it1 + lr) * LDV + 16 * js + 4 * q4), b);
+            }
+            f32x4 kv[KT], Gm[KT];
+#pragma unroll
+            for (int cs = 0; cs < KT; ++cs) {
+                kv[cs] = load4(kin + mrow * rsk + (int64_t)h * DK + 16 * cs + 4 * q4);
+                Gm[cs] = *reinterpret_cast<const f32x4 *>(rec + R::oG + m * DK + 16 * cs + 4 * q4);
+            }
+#pragma unroll
+            for (int cs = 0; cs < KT; ++cs) {
+                f32x4 kb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kb[e] = bm * kv[cs][e] * __expf(Gm[cs][e]);
+                mma(acc0, *reinterpret_cast<const f32x4 *>(sW + (16 * it0 + lr) * LDK + 16 * cs + 4 * q4), kb);
+                if (two) mma(acc1, *reinterpret_cast<const f32x4 *>(sW + (16 * it1 + lr) * LDK + 16 * cs + 4 * q4), kb);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sdT[(16 * it0 + 4 * q4 + e) * LDA + m] = acc0[e];
+                if (two) sdT[(16 * it1 + 4 * q4 + e) * LDA + m] = acc1[e];
+            }
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sdT[(16 * it + 4 * q4 + e) * LDA + m] = acc[e];
     }
     // dKg = Diag(beta) T^T dW for key tile ct and dv = Diag(beta) T^T dU for value tile vt (both
     // the wave's; T[m][i] = 0 for m < i), with the rows of beta, G, k and v loaded above

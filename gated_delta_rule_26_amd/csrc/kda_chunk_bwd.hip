@@ -217,16 +217,18 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
     constexpr int NVL = (C * DV / 4 + NT - 1) / NT, NKL = (C * DK / 4 + NT - 1) / NT;
     constexpr int VTP = DV / 16, ITP = C / 16;
     static_assert(VTP <= NT / 64, "one value-column tile per wave");
-    // one item's inputs as loaded: k, q, g rows (4-element groups tid, tid + NT, ...), v rows
-    // and beta; zero past the sequence end
+    // one item's inputs as loaded: k, q, g rows (4-element groups tid, tid + NT, ...), v rows,
+    // beta and this thread's dO values (wave w: value-column tile w, lane (lr, q4): rows
+    // 16 ms + 4 q4 + e of column 16 w + lr); zero past the sequence end
     typename I4::T kin4[NKL], qin4[NKL], vin4[NVL];
     f32x4 gin4[NKL];
+    f32x4 dpre[ITP];
     float bin;
-    auto fetch = [&](int w) {
+    auto fetch = [&](int w) {   // w: a valid item
         int n, L;
         int64_t t0;
         const int h = w % a.H;
-        if (!locate<C>(a, w / a.H, n, t0, L)) return false;
+        locate<C>(a, w / a.H, n, t0, L);
 #pragma unroll
         for (int u = 0; u < NVL; ++u) {
             const int idx = tid + u * NT, i = idx / (DV / 4), c = 4 * (idx % (DV / 4));
@@ -243,30 +245,6 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
             gin4[u] = in ? *reinterpret_cast<const f32x4 *>(a.g + off) : zero4();
         }
         bin = tid < C && tid < L ? a.beta[(t0 + tid) * a.H + h] : 0.f;
-        return true;
-    };
-    const int items = (int)(a.nslots * a.H);   // at most 2^30 (checked by the host)
-    bool have = (int)blockIdx.x < items && fetch(blockIdx.x);
-    for (int w = blockIdx.x; w < items; w += gridDim.x) {
-    // the thread index through an empty asm statement: the per-thread offsets below are
-    // recomputed for each item instead of being hoisted out of the loop and held in registers
-    int tid_ = threadIdx.x;
-    __asm__ volatile("" : "+v"(tid_));
-    const int tid = tid_;
-    const int h = w % a.H;
-    int n, L;
-    int64_t t0;
-    if (!locate<C>(a, w / a.H, n, t0, L)) {   // an unused slot: fetch the next item instead
-        have = w + gridDim.x < items && fetch(w + gridDim.x);
-        continue;
-    }
-    if (!have) fetch(w);
-    float *rec = a.ws + (int64_t)w * R::FLOATS;
-
-    // dO for the products below (wave w: value-column tile w, lane (lr, q4): rows
-    // 16 ms + 4 q4 + e of column 16 w + lr; zero past the sequence end)
-    f32x4 dpre[ITP];
-    {
         const int w6 = tid >> 6, l = tid & 63;
         const float *dcol = a.dout + (t0 + 4 * (l >> 4)) * rsv + (int64_t)h * DV + 16 * (w6 < VTP ? w6 : 0) + (l & 15);
 #pragma unroll
@@ -276,7 +254,51 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
                 const int r = 16 * ms + 4 * (l >> 4) + e;
                 dpre[ms][e] = w6 < VTP && r < L ? dcol[(int64_t)(16 * ms + e) * rsv] : 0.f;
             }
+    };
+    const int items = (int)(a.nslots * a.H);   // at most 2^30 (checked by the host)
+    // the first item at or after w in this workgroup's sequence that is a chunk (slots past a
+    // sequence's last chunk are unused)
+    auto next_item = [&](int w) {
+        for (; w < items; w += gridDim.x) {
+            int n, L;
+            int64_t t0;
+            if (locate<C>(a, w / a.H, n, t0, L)) break;
+        }
+        return w;
+    };
+    // Every input of an item is loaded during the item before it, ahead of that item's record
+    // stores, and every wave retires its memory operations in issue order: so an item waits
+    // for its own inputs only, never for the previous item's stores, which drain while it
+    // computes. (The first item's loads are waited for before the loop, so that the loop's
+    // waits count from the loads issued inside it.)
+    int w = next_item(blockIdx.x);
+    if (w < items) {
+        fetch(w);
+#pragma unroll
+        for (int u = 0; u < NKL; ++u) __asm__ volatile("" : : "v"(kin4[u]), "v"(qin4[u]), "v"(gin4[u]));
+#pragma unroll
+        for (int u = 0; u < NVL; ++u) __asm__ volatile("" : : "v"(vin4[u]));
+#pragma unroll
+        for (int ms = 0; ms < ITP; ++ms) __asm__ volatile("" : : "v"(dpre[ms]));
+        __asm__ volatile("" : : "v"(bin));
     }
+    while (w < items) {
+    const int wn = next_item(w + gridDim.x);
+    // the thread index through an empty asm statement: the per-thread offsets below are
+    // recomputed for each item instead of being hoisted out of the loop and held in registers
+    int tid_ = threadIdx.x;
+    __asm__ volatile("" : "+v"(tid_));
+    const int tid = tid_;
+    const int h = w % a.H;
+    int n, L;
+    int64_t t0;
+    locate<C>(a, w / a.H, n, t0, L);
+    float *rec = a.ws + (int64_t)w * R::FLOATS;
+
+    // dO as the B fragments of the products below
+    Split dOs[ITP];
+#pragma unroll
+    for (int ms = 0; ms < ITP; ++ms) dOs[ms] = split(dpre[ms]);
     // this item's inputs to LDS (v stays in registers), then the next item's loads
     f32x4 vpre[NVL];
 #pragma unroll
@@ -291,7 +313,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
         }
     }
     if (tid < C) sB[tid] = bin;
-    have = w + gridDim.x < items && fetch(w + gridDim.x);
+    if (wn < items) fetch(wn);
     if (tid < C / 16) sExt[tid] = 0;
     __syncthreads();
     if (tid < DK) {  // running sum along the chunk, one thread per channel
@@ -335,9 +357,6 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
     // Qg^T dO (the dO part of dS in the reverse state pass) into dH's slot, which that pass
     // reads before it writes it: wave w takes value-column tile w
     constexpr int KTP = DK / 16;
-    Split dOs[ITP];
-#pragma unroll
-    for (int ms = 0; ms < ITP; ++ms) dOs[ms] = split(dpre[ms]);
     __syncthreads();
     {
         const int w = tid >> 6, l = tid & 63;
@@ -561,6 +580,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
         }
     }
     __syncthreads();  // the LDS is the next item's
+    w = wn;
     }
 }
 

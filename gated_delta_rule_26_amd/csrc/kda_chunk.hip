@@ -503,7 +503,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                               : make_rsrc(a.g + t0 * krow, (uint32_t)(Lc * krow * 4));
         const rsrc_t rv = make_rsrc(vg + t0 * vrow, (uint32_t)(Lc * vrow * ESZ));
         const rsrc_t rb = make_rsrc(a.beta + t0 * H, (uint32_t)(Lc * H * 4));
-        if (part != 2) {
+        auto part1 = [&]() {
 #pragma unroll
             for (int vv = 0; vv < Sh::VPT; ++vv)
 #pragma unroll
@@ -520,8 +520,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             }
             pbeta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                   rb, (tid < C ? tid * H + h : C * H) * 4, 0, 0));
-        }
-        if (part != 1) {
+        };
+        auto part2 = [&]() {
 #pragma unroll
             for (int jj = 0; jj < Sh::JPT; ++jj) {
 #pragma unroll
@@ -530,6 +530,14 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                     pq[jj][ii] = RW::load(rq, ko[jj] * ESZ, ii * krow * ESZ);
                 }
             }
+        };
+        // with the fused input steps P0 reads k and q first (their norms), so they go first
+        if (FIN && part == 0) {
+            part2();
+            part1();
+        } else {
+            if (part != 2) part1();
+            if (part != 1) part2();
         }
     };
 
@@ -604,6 +612,28 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
                 return pg[jj][ii];
             }
         };
+        if constexpr (FIN) {
+            if (a.f.norm_qk) {
+                // per-token sums of squares of k and q over this wave's 64 channels: a butterfly
+                // over the 16 lanes of each lane group leaves value bitrev4(lane & 15) in each
+                // lane, then the two 16-lane groups of the half-wave are added
+                float sq[16];
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) {
+                    const f32x2 kk = RW::f32(pk[0][ii]), qq = RW::f32(pq[0][ii]);
+                    sq[ii] = kk.x * kk.x + kk.y * kk.y;
+                    sq[8 + ii] = qq.x * qq.x + qq.y * qq.y;
+                }
+                row_transpose_sum16(sq);
+                sq[0] += __shfl_xor(sq[0], 16);
+                if (!(lane & 16)) {
+                    const int l = lane & 15;
+                    const int vi = ((l & 1) << 3) | ((l & 2) << 1) | ((l & 4) >> 1) | ((l & 8) >> 3);
+                    const int kind = vi >> 3, chalf = jc[0] >> 6;
+                    nrm[(2 * kind + chalf) * C + 16 * jb[0] + 8 * hh + (vi & 7)] = sq[0];
+                }
+            }
+        }
         bool ext_local = false;
 #pragma unroll
         for (int jj = 0; jj < Sh::JPT; ++jj) {
@@ -642,28 +672,6 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
             }
             ext_local |= jok[jj] && (dk0[jj] < extreme_block_decay<OP>() ||
                                      dk1[jj] < extreme_block_decay<OP>());
-        }
-        if constexpr (FIN) {
-            if (a.f.norm_qk) {
-                // per-token sums of squares of k and q over this wave's 64 channels: a butterfly
-                // over the 16 lanes of each lane group leaves value bitrev4(lane & 15) in each
-                // lane, then the two 16-lane groups of the half-wave are added
-                float sq[16];
-#pragma unroll
-                for (int ii = 0; ii < 8; ++ii) {
-                    const f32x2 kk = RW::f32(pk[0][ii]), qq = RW::f32(pq[0][ii]);
-                    sq[ii] = kk.x * kk.x + kk.y * kk.y;
-                    sq[8 + ii] = qq.x * qq.x + qq.y * qq.y;
-                }
-                row_transpose_sum16(sq);
-                sq[0] += __shfl_xor(sq[0], 16);
-                if (!(lane & 16)) {
-                    const int l = lane & 15;
-                    const int vi = ((l & 1) << 3) | ((l & 2) << 1) | ((l & 4) >> 1) | ((l & 8) >> 3);
-                    const int kind = vi >> 3, chalf = jc[0] >> 6;
-                    nrm[(2 * kind + chalf) * C + 16 * jb[0] + 8 * hh + (vi & 7)] = sq[0];
-                }
-            }
         }
         if (tid < C) sbeta[tid] = pbeta;
 #pragma unroll

@@ -673,13 +673,15 @@ __device__ __forceinline__ void fwd_state_pass(const BwdArgs &a, int chain, int 
     const int col = 16 * vb + lr;
     auto rec_of = [&](int j) { return a.ws + ((base + j) * a.H + h) * R::FLOATS; };
     auto own = [&](int o) { return wave + NW * o; };
+    // W goes out with this chunk's W S products, Kd^T with its state update: the compute
+    // unit's memory pipeline then works through the whole step instead of its first phase
     auto loadW = [&](const float *rec, FwdOps<C, DK, DV> &o, int it) {
 #pragma unroll
-        for (int kk = 0; kk < KTW; ++kk) {
-            const int kt = wave * KTW + kk;
-            o.W[it][kk] = *reinterpret_cast<const f32x4 *>(rec + R::oW + afrag<P::KT>(it, kt, lane));
-            o.KdT[kk][it] = *reinterpret_cast<const f32x4 *>(rec + R::oKdT + afrag<IT>(kt, it, lane));
-        }
+        for (int kk = 0; kk < KTW; ++kk)
+            o.W[it][kk] = *reinterpret_cast<const f32x4 *>(rec + R::oW + afrag<P::KT>(it, wave * KTW + kk, lane));
+    };
+    auto loadK = [&](const float *rec, FwdOps<C, DK, DV> &o, int kk, int it) {
+        o.KdT[kk][it] = *reinterpret_cast<const f32x4 *>(rec + R::oKdT + afrag<IT>(wave * KTW + kk, it, lane));
     };
     auto loadRest = [&](const float *rec, FwdOps<C, DK, DV> &o) {
 #pragma unroll
@@ -768,7 +770,12 @@ __device__ __forceinline__ void fwd_state_pass(const BwdArgs &a, int chain, int 
         for (int kk = 0; kk < KTW; ++kk) {
             S[kk] *= cur.eg[kk];
 #pragma unroll
-            for (int it = 0; it < IT; ++it) mma3(S[kk], unpack(cur.KdT[kk][it]), Us[it]);
+            for (int it = 0; it < IT; ++it) {
+                loadK(nrec, nxt, kk, it);
+                sched_fence();
+                mma3(S[kk], unpack(cur.KdT[kk][it]), Us[it]);
+                sched_fence();
+            }
         }
     };
     FwdOps<C, DK, DV> o0, o1;
@@ -776,7 +783,11 @@ __device__ __forceinline__ void fwd_state_pass(const BwdArgs &a, int chain, int 
     if (nch > 0) {
         const float *r0 = rec_of(0);
 #pragma unroll
-        for (int it = 0; it < IT; ++it) loadW(r0, o0, it);
+        for (int it = 0; it < IT; ++it) {
+            loadW(r0, o0, it);
+#pragma unroll
+            for (int kk = 0; kk < KTW; ++kk) loadK(r0, o0, kk, it);
+        }
         loadRest(r0, o0);
     }
     if (nch > 1) o1.pf = touch_chunk(1);
@@ -822,13 +833,14 @@ __device__ __forceinline__ void rev_state_pass(const BwdArgs &a, int chain, int 
     const int64_t sbase = ((int64_t)n * a.H + h) * DK;
     auto rec_of = [&](int j) { return a.ws + ((base + j) * a.H + h) * R::FLOATS; };
     auto own = [&](int o) { return wave + NW * o; };
-    auto loadKW = [&](const float *rec, RevOps<C, DK, DV> &o, int it) {
+    // Kd goes out with this chunk's dU products, -W^T with its dS update (as in the forward pass)
+    auto loadKd = [&](const float *rec, RevOps<C, DK, DV> &o, int it) {
 #pragma unroll
-        for (int kk = 0; kk < KTW; ++kk) {
-            const int kt = wave * KTW + kk;
-            o.Kd[it][kk] = *reinterpret_cast<const f32x4 *>(rec + R::oKd + afrag<P::KT>(it, kt, lane));
-            o.WT[kk][it] = *reinterpret_cast<const f32x4 *>(rec + R::oWT + afrag<IT>(kt, it, lane));
-        }
+        for (int kk = 0; kk < KTW; ++kk)
+            o.Kd[it][kk] = *reinterpret_cast<const f32x4 *>(rec + R::oKd + afrag<P::KT>(it, wave * KTW + kk, lane));
+    };
+    auto loadWT = [&](const float *rec, RevOps<C, DK, DV> &o, int kk, int it) {
+        o.WT[kk][it] = *reinterpret_cast<const f32x4 *>(rec + R::oWT + afrag<IT>(wave * KTW + kk, it, lane));
     };
     auto loadRest = [&](const float *rec, RevOps<C, DK, DV> &o) {
 #pragma unroll
@@ -872,7 +884,7 @@ __device__ __forceinline__ void rev_state_pass(const BwdArgs &a, int chain, int 
         f32x4 acc[IT];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            loadKW(nrec, nxt, it);
+            loadKd(nrec, nxt, it);
             sched_fence();
             acc[it] = zero4();
 #pragma unroll
@@ -915,7 +927,12 @@ __device__ __forceinline__ void rev_state_pass(const BwdArgs &a, int chain, int 
             const f32x4 dSo = dS[kk];
             dS[kk] = dS[kk] * cur.eg[kk] + cur.P2[kk];
 #pragma unroll
-            for (int it = 0; it < IT; ++it) mma3(dS[kk], unpack(cur.WT[kk][it]), dUs[it]);   // -W^T dU
+            for (int it = 0; it < IT; ++it) {
+                loadWT(nrec, nxt, kk, it);
+                sched_fence();
+                mma3(dS[kk], unpack(cur.WT[kk][it]), dUs[it]);   // -W^T dU
+                sched_fence();
+            }
             *reinterpret_cast<f32x4 *>(rec + R::odH + afrag<VT>(wave * KTW + kk, vb, lane)) =
                 transpose16(dSo, sTr[wave], lr, q4);   // operand layout: row lr, 4 columns
         }
@@ -925,7 +942,11 @@ __device__ __forceinline__ void rev_state_pass(const BwdArgs &a, int chain, int 
     if (nch > 0) {
         const float *rl = rec_of(nch - 1);
 #pragma unroll
-        for (int it = 0; it < IT; ++it) loadKW(rl, o0, it);
+        for (int it = 0; it < IT; ++it) {
+            loadKd(rl, o0, it);
+#pragma unroll
+            for (int kk = 0; kk < KTW; ++kk) loadWT(rl, o0, kk, it);
+        }
         loadRest(rl, o0);
     }
     if (nch > 1) o1.pf = touch_chunk(nch - 2);

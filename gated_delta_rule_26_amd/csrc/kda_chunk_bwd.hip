@@ -329,19 +329,27 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
             if (sG[16 * b * LDX + tid] - sG[(16 * b + 15) * LDX + tid] > kExtremeLogDecay) sExt[b] = 1;
     }
     __syncthreads();
+    // Record stores go out as whole 1 KB pieces per wave: G row by row, the split tiles
+    // fragment by fragment (vector idx is lane idx % 64 of tile idx / 64), each thread
+    // gathering its fragment's four values from LDS.
     for (int idx = tid; idx < C * DK / 4; idx += NT) {
         const int i = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+        *reinterpret_cast<f32x4 *>(rec + R::oG + i * DK + c) = *reinterpret_cast<const f32x4 *>(sG + i * LDX + c);
+    }
+    for (int idx = tid; idx < C * DK / 4; idx += NT) {
+        const int tile = idx >> 6, ln = idx & 63;
+        const int i = 16 * (tile / (DK / 16)) + (ln & 15), c = 16 * (tile % (DK / 16)) + 4 * (ln >> 4);
         const f32x4 G = *reinterpret_cast<const f32x4 *>(sG + i * LDX + c);
         const f32x4 gC = *reinterpret_cast<const f32x4 *>(sG + (C - 1) * LDX + c);
         const f32x4 kv = *reinterpret_cast<const f32x4 *>(sK + i * LDK + c);
         f32x4 kd;
 #pragma unroll
         for (int e = 0; e < 4; ++e) kd[e] = kv[e] * __expf(gC[e] - G[e]);
-        *reinterpret_cast<f32x4 *>(rec + R::oG + i * DK + c) = G;
-        *reinterpret_cast<f32x4 *>(rec + R::oKd + split_at<DK / 16>(i, c)) = split_pack(kd);
+        *reinterpret_cast<f32x4 *>(rec + R::oKd + 4 * idx) = split_pack(kd);   // = split_at<DK / 16>(i, c)
     }
     for (int idx = tid; idx < DK * C / 4; idx += NT) {  // the same, transposed ([channel][row])
-        const int c = idx / (C / 4), i0 = 4 * (idx % (C / 4));
+        const int tile = idx >> 6, ln = idx & 63;
+        const int c = 16 * (tile / (C / 16)) + (ln & 15), i0 = 16 * (tile % (C / 16)) + 4 * (ln >> 4);
         f32x4 qg, kd;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -407,9 +415,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
                             }
                         }
                     }
-                    const float av = j < i ? sa : 0.f;
-                    sA[i * LDA + j] = av;
-                    rec[R::oA + i * C + j] = av;
+                    sA[i * LDA + j] = j < i ? sa : 0.f;
                     mt[e] = j <= i ? a.scale * sm : 0.f;
                 }
                 sMT[split_at<C / 16>(j, i0) / 4] = split_pack(mt);   // M^T
@@ -441,9 +447,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * q4 + e, j = 16 * J + lr;
-                const float av = j < i ? accA[e] : 0.f;
-                sA[i * LDA + j] = av;
-                rec[R::oA + i * C + j] = av;
+                sA[i * LDA + j] = j < i ? accA[e] : 0.f;
                 mt[e] = j <= i ? a.scale * accM[e] : 0.f;
             }
             // M^T: row 16 J + lr, the four values of columns 16 I + 4 q4 ..
@@ -452,10 +456,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
     }
     for (int p = tid; p < C * C; p += NT) {   // A~'s blocks above the diagonal
         const int i = p / C, j = p % C;
-        if ((j >> 4) > (i >> 4)) {
-            sA[i * LDA + j] = 0.f;
-            rec[R::oA + p] = 0.f;
-        }
+        if ((j >> 4) > (i >> 4)) sA[i * LDA + j] = 0.f;
     }
     __syncthreads();
     {   // M^T dO (the dO part of dU in the reverse state pass) into dU's slot: wave w takes
@@ -542,9 +543,10 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(BwdArgs a) {
             if (act) put(sT + 16 * I * LDA + 16 * J, LDA, -prod(sT + 16 * I * LDA + 16 * I, LDA, 1.f, R, LDT, zero4()));
             __syncthreads();
         }
-        for (int idx = tid; idx < C * C / 4; idx += NT) {
+        for (int idx = tid; idx < C * C / 4; idx += NT) {   // T and A~ row by row
             const int i = idx / (C / 4), j = 4 * (idx % (C / 4));
             *reinterpret_cast<f32x4 *>(rec + R::oT + i * C + j) = *reinterpret_cast<const f32x4 *>(sT + i * LDA + j);
+            *reinterpret_cast<f32x4 *>(rec + R::oA + i * C + j) = *reinterpret_cast<const f32x4 *>(sA + i * LDA + j);
         }
     }
 #pragma unroll

@@ -267,6 +267,8 @@ def other_workloads(kda, synth, to_dev, torch, np, log, state) -> dict:
     pb = w.T * w.H * prefill_bytes_per_token_head(w.K, w.V) + w.H * w.K * w.V * 4
     out["prefill_4k_h16"] = {"ms": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
                              "cache": "resident (back to back)",
+                             "algorithmic_gbs": round(pb / (ms * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(pb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                              "ms_cold": round(ms_cold, 4),
                              "tokens_per_s_cold": round(w.T / (ms_cold * 1e-3), 1),
                              "algorithmic_gbs_cold": round(pb / (ms_cold * 1e-3) / 1e9, 1),

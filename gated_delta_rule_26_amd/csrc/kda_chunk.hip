@@ -1409,7 +1409,12 @@ __global__ __launch_bounds__(256) void split_combine_kernel(ChunkArgs a) {
     __shared__ __attribute__((aligned(16))) float cur[DK * LDS_];
     __shared__ __attribute__((aligned(16))) float Xs[DK * LDX];
     const int chains = a.n_seqs * a.H;
-    const int chain = blockIdx.x / (DV / 16), cb = blockIdx.x % (DV / 16);
+    // Workgroup b runs on XCD b % 8: a chain's DV / 16 column blocks all take the same
+    // residue, so they share one XCD's L2 and each X_p comes from HBM once per chain, not once
+    // per column block (the grid is rounded up to whole groups of 8 chains)
+    constexpr int NCB = DV / 16;
+    const int kb = (int)blockIdx.x >> 3;
+    const int chain = (kb / NCB) * 8 + (int)(blockIdx.x & 7), cb = kb % NCB;
     if (chain >= chains) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, q4 = lane >> 4;
     const int64_t cstride = (int64_t)chains * DK * DV;
@@ -1513,7 +1518,7 @@ hipError_t launch_t(const ChunkArgs &a, hipStream_t stream) {
                                dim3((unsigned)(chains * (a.nseg - 2))), dim3(64 * NW), 0, stream, a);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        hipLaunchKernelGGL((split_combine_kernel<DK, DV>), dim3((unsigned)(chains * (DV / 16))),
+        hipLaunchKernelGGL((split_combine_kernel<DK, DV>), dim3((unsigned)((chains + 7) / 8 * 8 * (DV / 16))),
                            dim3(256), 0, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((replay_kernel<OP, C, DK, DV, NW, false, FOUT>),

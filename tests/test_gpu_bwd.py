@@ -118,6 +118,22 @@ def test_d128_packed_with_empty_sequences(stored):
 
 
 @pytest.mark.parametrize("stored", ["f32", "bf16"])
+def test_d128_packed_many_chunk_aligned_sequences(stored):
+    """40 packed sequences, many of whole chunks and some empty, over 4 heads: the record
+    slots past each sequence's last chunk are unused, and with more (slot, head) items than
+    compute units the persistent prep takes several items per workgroup with unused slots
+    between them."""
+    lens = [64, 0, 128, 64, 1, 192, 0, 64] * 5
+    H = 4
+    x = random_inputs(590, int(np.sum(lens)), H, 128, stored)
+    s0 = random_states(591, len(lens), H, 128)
+    do, dsT = upstream(592, lens, H, 128, 128)
+    note(f"bwd packed chunk-aligned {stored}")
+    got, ref = run_case(x, stored, lens, chunk=64, s0=s0, dsT=dsT, do=do)
+    check(got, ref, TOL_F32 if stored == "f32" else TOL_BF16)
+
+
+@pytest.mark.parametrize("stored", ["f32", "bf16"])
 def test_d128_batched(stored):
     B, T, H = 3, 150, 2
     x = random_inputs(560, B * T, H, 128, stored)

@@ -1205,6 +1205,7 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
     __shared__ __attribute__((aligned(16))) float gl[DK];
     __shared__ __attribute__((aligned(16))) float Ob[FOUT ? C * ONorm<C, DV, NW>::LD : 4];  // output staging
     __shared__ __attribute__((aligned(16))) float sgain[FOUT ? DV : 4];
+    __shared__ __attribute__((aligned(16))) float Xs[XMODE ? DK * DV : 4];  // X_p, reordered
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, q4 = lane >> 4;
@@ -1375,11 +1376,41 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
         }
     }
 
+    if constexpr (XMODE) {
+        // X_p as the combine reads it, built in LDS and then copied out in 16-byte pieces.
+        // Float32 path: element (row 16 i + m, column 16 s + 4 g + j) at float
+        // ((i * KT + s) * 64 + m + 16 g) * 4 + j. Otherwise split into bf16 head and tail:
+        // element (row 16 i + m, column 32 s + 8 g + j) at bf16 (((i * KT/2 + s) * 2 + h) * 64
+        // + m + 16 g) * 8 + j, h = 0 for the head and 1 for the tail.
+        if (owns) {
+#pragma unroll
+            for (int j = 0; j < CPW; ++j) {
+                const int ct = wave + NW * j;
+#pragma unroll
+                for (int r = 0; r < KT; ++r)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = S[j][r][e];
+                        if constexpr (std::is_same<OP, float>::value) {
+                            Xs[((r * KT + ct) * 64 + 4 * q4 + e + 16 * (lr >> 2)) * 4 + (lr & 3)] = v;
+                        } else {
+                            const int o = (((r * (KT / 2) + (ct >> 1)) * 2) * 64 + 4 * q4 + e +
+                                           16 * (2 * (ct & 1) + (lr >> 3))) * 8 + (lr & 7);
+                            const __bf16 hd = f32_to_bf16(v);
+                            const __bf16 tl = f32_to_bf16(v - static_cast<float>(hd));
+                            reinterpret_cast<__bf16 *>(Xs)[o] = hd;
+                            reinterpret_cast<__bf16 *>(Xs)[o + 64 * 8] = tl;
+                        }
+                    }
+            }
+        }
+        __syncthreads();
+        u32x4 *const xd = reinterpret_cast<u32x4 *>(a.ws_x + ((int64_t)p * chains + chain) * DK * DV);
+        for (int x = tid; x < DK * DV / 4; x += NT) xd[x] = reinterpret_cast<const u32x4 *>(Xs)[x];
+        return;
+    }
     float *dst = nullptr;
-    if (XMODE)
-        dst = a.ws_x + ((int64_t)p * chains + chain) * DK * DV;
-    else if (a.s_out && p == a.nseg - 1)
-        dst = a.s_out + (int64_t)chain * DK * DV;
+    if (a.s_out && p == a.nseg - 1) dst = a.s_out + (int64_t)chain * DK * DV;
     if (owns && dst) {
 #pragma unroll
         for (int j = 0; j < CPW; ++j)
@@ -1393,21 +1424,30 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
 
 // Split combine: S_0 = the initial state (or zero), S_1 = R_0 (segment 0 ran from the
 // initial state), then S_{p+1} = X_p S_p + R_p. One workgroup per (chain, 16-column block).
-// Each step is a [Dk x Dk] x [Dk x 16] product on the float32 matrix cores: every wave owns
-// 16-row tiles of the result, X_p is staged in LDS with coalesced 16-byte loads (rows padded
-// against bank conflicts) while X_{p+1}'s loads are in flight, and the running block S_p
-// stays in LDS, where the next step reads it as the B operand. Writes ws_s[p], p < nseg.
-template <int DK, int DV>
+// Each step is a [Dk x Dk] x [Dk x 16] product on the matrix cores, float32-accurate: with
+// SPLIT, each factor is a bf16 head plus a bf16 tail and the three leading cross products
+// are summed (16x16x32 bf16 instructions); otherwise float32 instructions. Every wave owns
+// 16-row tiles of the result and keeps them in its accumulators. The X replay stores X_p in
+// this product's A-operand order (with SPLIT already split, heads and tails in separate
+// 16-byte pieces), so a wave loads its own fragments straight into registers with
+// contiguous 16-byte loads, two steps ahead, into the registers the previous step has
+// finished with (X and R do not depend on S); the loads go out group by group between the
+// products, so that the memory pipeline's queue does not hold up the matrix cores. The
+// running block S_p reaches the other waves through LDS, transposed so that a B fragment is
+// contiguous (with SPLIT already split by its writer), in two buffers by step parity: one
+// barrier per step. Writes ws_s[p], p < nseg.
+template <int DK, int DV, bool SPLIT>
 __global__ __launch_bounds__(256) void split_combine_kernel(ChunkArgs a) {
-    using ST = Step<float>;
-    constexpr int LDX = DK + 4;                  // padded row of X in LDS (floats)
-    constexpr int LDS_ = 20;                     // padded row of the running 16-column block
-    constexpr int PIECES = DK * DK / 4;          // 16-byte pieces of X
-    constexpr int NX = (PIECES + 255) / 256;     // ... per thread
-    constexpr int RT = DK / 16;                  // 16-row tiles of the result
-    constexpr int TPW = (RT + 3) / 4;            // ... per wave
-    __shared__ __attribute__((aligned(16))) float cur[DK * LDS_];
-    __shared__ __attribute__((aligned(16))) float Xs[DK * LDX];
+    constexpr int RT = DK / 16;           // 16-row tiles of the result
+    constexpr int TPW = (RT + 3) / 4;     // tiles per wave: wave w owns tiles w, w + 4, ...
+    constexpr int KW = SPLIT ? 32 : 16;   // reduction indices per instruction group
+    constexpr int NK = DK / KW;           // ... groups per product
+    constexpr int NP = SPLIT ? 2 : 1;     // 16-byte pieces per lane and group (head, tail)
+    constexpr int LDT = DK + 4;           // padded row of the transposed running block (floats)
+    constexpr int LDH = DK + 8;           // ... of its bf16 head and tail
+    static_assert(DK % KW == 0, "split maps need Dk a multiple of 32");
+    __shared__ __attribute__((aligned(16))) float curT[SPLIT ? 1 : 2][16 * LDT];
+    __shared__ __attribute__((aligned(16))) __bf16 curH[SPLIT ? 2 : 1][2][16 * LDH];
     const int chains = a.n_seqs * a.H;
     // Workgroup b runs on XCD b % 8: a chain's DV / 16 column blocks all take the same
     // residue, so they share one XCD's L2 and each X_p comes from HBM once per chain, not once
@@ -1416,68 +1456,121 @@ __global__ __launch_bounds__(256) void split_combine_kernel(ChunkArgs a) {
     const int kb = (int)blockIdx.x >> 3;
     const int chain = (kb / NCB) * 8 + (int)(blockIdx.x & 7), cb = kb % NCB;
     if (chain >= chains) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, q4 = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, q4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // tile t of this wave exists (always, once there are at least four tiles)
+    auto has = [&](int t) { return RT % 4 == 0 || wave + 4 * t < RT; };
+    const int nseg = a.nseg;
     const int64_t cstride = (int64_t)chains * DK * DV;
-    float *const s_base = a.ws_s + (int64_t)chain * DK * DV + 16 * cb;
-    f32x4 xr[NX];      // the next X, in flight
-    f32x4 rr[TPW];     // ... and this lane's values of the next R
-    auto fetch_x = [&](int p) {
-        const f32x4 *X = reinterpret_cast<const f32x4 *>(a.ws_x + ((int64_t)p * chains + chain) * DK * DK);
-#pragma unroll
-        for (int i = 0; i < NX; ++i)
-            if (PIECES % 256 == 0 || tid + 256 * i < PIECES) xr[i] = X[tid + 256 * i];
-        const float *R = a.ws_r + ((int64_t)p * chains + chain) * DK * DV + 16 * cb;
+    // this lane's elements of a state-shaped [DK x DV] block: rows 16 i + 4 q4 + e of the
+    // wave's tiles i, column 16 cb + lr
+    const int64_t lane_off = (int64_t)chain * DK * DV + (int64_t)(4 * q4) * DV + 16 * cb + lr;
+    u32x4 x[3][TPW][NK][NP];  // A fragments of X_{p-1}, X_p, X_{p+1}, by p mod 3
+    f32x4 r[3][TPW];          // this lane's values of R_{p-1}, R_p, R_{p+1}
+    // Loads of X_p's group k (and with k = 0, R_p). Every step issues the same loads (p is
+    // clamped into the maps that exist, 0 .. nseg-2, and a clamped load is never used), so
+    // the wait before each use counts exactly the loads issued after it.
+    auto fetch = [&](u32x4 (&xb)[TPW][NK][NP], f32x4 (&rb)[TPW], int p, int k) {
+        p = p < nseg - 2 ? p : nseg - 2;
+        const u32x4 *X = reinterpret_cast<const u32x4 *>(a.ws_x + ((int64_t)p * chains + chain) * DK * DK);
+        const float *R = a.ws_r + (int64_t)p * cstride + lane_off;
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int i = wave + 4 * t;
+            if (has(t)) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rr[t][e] = i < RT ? R[(int64_t)(16 * i + 4 * q4 + e) * DV + lr] : 0.f;
+                for (int h = 0; h < NP; ++h) xb[t][k][h] = X[((i * NK + k) * NP + h) * 64 + lane];
+                if (k == 0) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rb[t][e] = R[(int64_t)(16 * i + e) * DV];
+                }
+            }
         }
     };
-    if (a.nseg > 2) fetch_x(1);
-    for (int idx = tid; idx < DK * 16; idx += 256) {
-        const int r = idx / 16, c = idx % 16;
-        const int64_t e = (int64_t)chain * DK * DV + (int64_t)r * DV + 16 * cb + c;
-        s_base[(int64_t)r * DV + c] = a.s0 ? a.s0[e] : 0.f;  // S_0
-        cur[r * LDS_ + c] = a.ws_r[e];                      // S_1 = R_0
-    }
-    __syncthreads();
-    for (int p = 1; p < a.nseg; ++p) {
-        float *sp = s_base + p * cstride;
-        for (int idx = tid; idx < DK * 16; idx += 256) sp[(int64_t)(idx / 16) * DV + idx % 16] = cur[(idx / 16) * LDS_ + idx % 16];
-        if (p + 1 >= a.nseg) break;
-        // next = X_p cur + R_p, tile by tile: rows 16i + 4q + e, column lr in lane (lr, q)
+    f32x4 acc[TPW];  // this wave's tiles of S_p
 #pragma unroll
-        for (int i = 0; i < NX; ++i) {
-            const int e = 4 * (tid + 256 * i);  // element index in X_p (row-major DK x DK)
-            if (PIECES % 256 == 0 || e < DK * DK) *reinterpret_cast<f32x4 *>(Xs + (e / DK) * LDX + e % DK) = xr[i];
-        }
-        f32x4 acc[TPW];
+    for (int t = 0; t < TPW; ++t) {
+        const int i = wave + 4 * t;
+        if (has(t)) {
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) acc[t] = rr[t];
-        __syncthreads();                      // X_p staged
-        if (p + 2 < a.nseg) fetch_x(p + 1);  // in flight during this step
-#pragma unroll
-        for (int ks = 0; ks < RT; ++ks) {     // reduction indices 16 ks .. 16 ks + 15
-            f32x4 b;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) b[e] = cur[(16 * ks + 4 * q4 + e) * LDS_ + lr];
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int i = wave + 4 * t;
-                if (i < RT) ST::mma(acc[t], ST::contig(Xs + (16 * i + lr) * LDX, 16 * ks, q4), b);
+            for (int e = 0; e < 4; ++e) {
+                const int64_t o = lane_off + (int64_t)(16 * i + e) * DV;
+                a.ws_s[o] = a.s0 ? a.s0[o] : 0.f;  // S_0
+                acc[t][e] = a.ws_r[o];             // S_1 = R_0
             }
         }
-        __syncthreads();                      // every reader of cur and Xs is done
+    }
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        fetch(x[1], r[1], 1, k);
+        fetch(x[2], r[2], 2, k);
+    }
+    // One step: write S_p; if another follows, S_{p+1} = X_p S_p + R_p from xb, rb, while
+    // X_{p+2}, R_{p+2} go out into xn, rn (step p-1's registers). Returns false after the
+    // last state.
+    auto step = [&](u32x4 (&xb)[TPW][NK][NP], f32x4 (&rb)[TPW], u32x4 (&xn)[TPW][NK][NP],
+                    f32x4 (&rn)[TPW], int p) -> bool {
+        float *const sp = a.ws_s + (int64_t)p * cstride;
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int i = wave + 4 * t;
-            if (i < RT) {
+            if (has(t)) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) cur[(16 * i + 4 * q4 + e) * LDS_ + lr] = acc[t][e];
+                for (int e = 0; e < 4; ++e) sp[lane_off + (int64_t)(16 * i + e) * DV] = acc[t][e];
             }
         }
-        __syncthreads();
+        if (p + 1 >= nseg) return false;
+        // S_p into LDS: row lr of the transposed block holds column lr of S_p
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int i = wave + 4 * t;
+            if (has(t)) {
+                if constexpr (SPLIT) {
+                    bf16x4 hd, tl;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        hd[e] = f32_to_bf16(acc[t][e]);
+                        tl[e] = f32_to_bf16(acc[t][e] - static_cast<float>(hd[e]));
+                    }
+                    *reinterpret_cast<bf16x4 *>(curH[p & 1][0] + lr * LDH + 16 * i + 4 * q4) = hd;
+                    *reinterpret_cast<bf16x4 *>(curH[p & 1][1] + lr * LDH + 16 * i + 4 * q4) = tl;
+                } else {
+                    *reinterpret_cast<f32x4 *>(curT[p & 1] + lr * LDT + 16 * i + 4 * q4) = acc[t];
+                }
+            }
+        }
+        __syncthreads();  // S_p complete in LDS (the other buffer's readers finished a step ago)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) acc[t] = rb[t];
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            fetch(xn, rn, p + 2, k);
+            if constexpr (SPLIT) {
+                // B: rows 32 k + 8 q4 .. + 7 of S_p's column lr, head and tail
+                const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(curH[p & 1][0] + lr * LDH + 32 * k + 8 * q4);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(curH[p & 1][1] + lr * LDH + 32 * k + 8 * q4);
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+                    if (has(t)) {
+                        const bf16x8 ah = __builtin_bit_cast(bf16x8, xb[t][k][0]);
+                        const bf16x8 al = __builtin_bit_cast(bf16x8, xb[t][k][NP - 1]);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[t], 0, 0, 0);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[t], 0, 0, 0);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[t], 0, 0, 0);
+                    }
+            } else {
+                const f32x4 bv = *reinterpret_cast<const f32x4 *>(curT[p & 1] + lr * LDT + 16 * k + 4 * q4);
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+                    if (has(t)) Mma<float>::mma(acc[t], __builtin_bit_cast(f32x4, xb[t][k][0]), bv);
+            }
+        }
+        return true;
+    };
+    for (int p = 1;; p += 3) {
+        if (!step(x[1], r[1], x[0], r[0], p)) break;
+        if (!step(x[2], r[2], x[1], r[1], p + 1)) break;
+        if (!step(x[0], r[0], x[2], r[2], p + 2)) break;
     }
 }
 
@@ -1518,7 +1611,7 @@ hipError_t launch_t(const ChunkArgs &a, hipStream_t stream) {
                                dim3((unsigned)(chains * (a.nseg - 2))), dim3(64 * NW), 0, stream, a);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        hipLaunchKernelGGL((split_combine_kernel<DK, DV>), dim3((unsigned)((chains + 7) / 8 * 8 * (DV / 16))),
+        hipLaunchKernelGGL((split_combine_kernel<DK, DV, !std::is_same<OP, float>::value>), dim3((unsigned)((chains + 7) / 8 * 8 * (DV / 16))),
                            dim3(256), 0, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((replay_kernel<OP, C, DK, DV, NW, false, FOUT>),
@@ -1574,7 +1667,7 @@ SplitPlan plan_split(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, in
     double best = rounds(chains) * (double)nchunks;
     for (int64_t P = 2; P <= 16; ++P) {
         const int64_t per = (nchunks + P - 1) / P;  // chunks per segment
-        if (per < 8) break;
+        if (per < 4) break;
         const int64_t nseg = (nchunks + per - 1) / per;
         if (nseg < 2) continue;
         const double cost = rounds(chains * nseg) * per + rounds(chains * (nseg - 2)) * per * kXCost +

@@ -36,7 +36,7 @@ struct ChunkArgs {
     int32_t seg_len, nseg;
     float *ws_r;                 // [nseg-1][N*H][Dk][Dv] R_p: segment p's final state (p = 0:
                                  //   from the initial state; p > 0: from zero)
-    float *ws_x;                 // [nseg-1][N*H][Dk][Dk] X_p: segment p's linear part (p >= 1)
+    float *ws_x;                 // [nseg-1][N*H][Dk*Dk] X_p: segment p's linear part (p >= 1), in the combine's operand order
     float *ws_s;                 // [nseg][N*H][Dk][Dv]   S_p: segment p's true start state
     uint8_t *rec;                // [nseg][N*H][rec_chunks] chunk records of segments out_from..
     int32_t out_from;            // first segment whose outputs come from the output replay

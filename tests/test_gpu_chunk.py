@@ -359,6 +359,45 @@ def test_split_matches_oracle_and_unsplit(stored, D, C, B, T, H):
     assert_close(S, S1, tol, "state split vs one pass")
 
 
+# Few segments: the combine's first steps and its three-step register rotation end at every
+# position (no segment map at all with two segments, one with three, two with four).
+FEW_SEGMENT_CASES = [
+    # (stored, D, C, T, H, segments, chunks per segment) on a 256-compute-unit device
+    ("bf16", 128, 64, 768, 1, 3, 4),
+    ("bf16", 128, 64, 837, 1, 4, 4),
+    ("bf16", 128, 64, 1100, 100, 2, 9),
+    ("f32", 128, 32, 384, 1, 3, 4),
+    ("f32", 128, 32, 448, 1, 4, 4),
+    ("f32", 128, 32, 560, 100, 2, 9),
+]
+
+
+def split_plan_bytes(T, H, D, C, stored, nseg, per):
+    """Workspace bytes of a split into nseg segments of per chunks: maps R and X, start
+    states, and per-chunk records (2 C Dk + Dk C + C^2 + C Dv operands and Dk decays)."""
+    sz = 2 if stored == "bf16" else 4
+    rec = (2 * C * D + D * C + C * C + C * D) * sz + D * 4
+    rec = (rec + 255) // 256 * 256
+    return (nseg - 1) * H * (D * D + D * D) * 4 + nseg * H * D * D * 4 + nseg * H * per * rec
+
+
+@pytest.mark.parametrize("stored,D,C,T,H,nseg,per", FEW_SEGMENT_CASES)
+def test_split_few_segments(stored, D, C, T, H, nseg, per):
+    torch = torch_mod()
+    got = split_bytes(1, T, H, D, C, stored)
+    assert got > 0, "case does not exercise the split"
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert got == split_plan_bytes(T, H, D, C, stored, nseg, per), "not the intended plan"
+    x = random_inputs(700 + T + H, T, H, D, stored)
+    s0 = random_states(701 + T, 1, H, D)
+    tol = TOL_BF16 if stored == "bf16" else TOL_F32
+    note(f"split {stored} D={D} C={C} T={T} H={H} into {nseg} segments")
+    o, S = gpu_chunk(x, stored, chunk=C, s0=s0, scale=D ** -0.5)
+    o_ref, S_ref = run_oracle(x, stored, scale=D ** -0.5, initial_state=s0)
+    assert_close(o, o_ref, tol, "o (split)")
+    assert_close(S, S_ref, tol, "final state (split)")
+
+
 def test_split_bf16_strong_decay_and_aliasing():
     """Split with near-total forgetting (tiny state maps) and final_state == initial_state."""
     B, T, H, D = 1, 4096 + 100, 2, 128

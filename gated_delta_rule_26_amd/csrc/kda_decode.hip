@@ -87,38 +87,45 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // next token's values are loaded into registers while the current one computes
     const int L = MULTI ? a.L : 1;
     auto row = [&](int t) { return MULTI ? (n * L + t) * a.H + h : item; };
-    float nk = 0.f, nq = 0.f, ng = 0.f, nv = 0.f, nz = 0.f;
+    // raw token values, converted when staged: every thread loads (lanes past Dk or Dv repeat a
+    // channel), so no branch holds a wait for them
+    Tin nk{}, nq{}, nv{}, nz{}, ngx{};
+    float ng = 0.f, nb = 0.f, bcur = 0.f;
     auto fetch = [&](int t) {
         const int64_t r = row(t);
-        if (tid < DK) {
-            nk = to_f32(static_cast<const Tin *>(a.k)[r * DK + tid]);
-            nq = to_f32(static_cast<const Tin *>(a.q)[r * DK + tid]);
-            ng = fgate ? to_f32(static_cast<const Tin *>(a.f.gx)[r * DK + tid]) : a.g[r * DK + tid];
-        }
-        if (tid < DV) {
-            nv = to_f32(static_cast<const Tin *>(a.v)[r * DV + tid]);
-            if (fnorm) nz = to_f32(static_cast<const Tin *>(a.f.og)[r * DV + tid]);
-        }
+        const int ck = tid % DK, cv = tid % DV;
+        nb = a.beta[r];
+        nk = static_cast<const Tin *>(a.k)[r * DK + ck];
+        nq = static_cast<const Tin *>(a.q)[r * DK + ck];
+        if (fgate)
+            ngx = static_cast<const Tin *>(a.f.gx)[r * DK + ck];
+        else
+            ng = a.g[r * DK + ck];
+        nv = static_cast<const Tin *>(a.v)[r * DV + cv];
+        if (fnorm) nz = static_cast<const Tin *>(a.f.og)[r * DV + cv];
     };
     auto stage = [&](int b) {
+        bcur = nb;
         if (tid < DK) {
-            sk[b][tid] = nk;
-            sq[b][tid] = a.scale * nq;
-            sa[b][tid] = __expf(fgate ? -rate * softplus_f(ng + gbias) : ng);
+            sk[b][tid] = to_f32(nk);
+            sq[b][tid] = a.scale * to_f32(nq);
+            sa[b][tid] = __expf(fgate ? -rate * softplus_f(to_f32(ngx) + gbias) : ng);
         }
         if (tid < DV) {
-            sv[b][tid] = nv;
-            if (fnorm) sz[b][tid] = nz;
+            sv[b][tid] = to_f32(nv);
+            if (fnorm) sz[b][tid] = to_f32(nz);
         }
     };
 
-    // the state's loads go out first: they depend on nothing, and the token's own loads and
-    // staging then overlap them
+    // the token's few loads go out first and the state's after them: loads complete in issue
+    // order, so staging the token (and its barrier) then waits for its own loads only and
+    // overlaps the state's, which the sweep waits for
+    fetch(0);
     f32x4 s[NPASS];
 #pragma unroll
     for (int p = 0; p < NPASS; ++p)
         s[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (p * RPP + rr) * DV + 4 * cg));
-    fetch(0);
+    __builtin_amdgcn_sched_barrier(0);  // nothing that waits for the token moves above the state's loads
     for (int t = 0; t < L; ++t) {
         const int b = t & 1;
         stage(b);
@@ -172,7 +179,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             P += red[w][0][cg];
             R += red[w][1][cg];
         }
-        const float bt = a.beta[row(t)];
+        const float bt = bcur;
         const float rk = FUSED ? sqk[b][1] : 1.f, rq = FUSED ? sqk[b][2] : 1.f;
         const f32x4 vv = *reinterpret_cast<const f32x4 *>(&sv[b][4 * cg]);
         const f32x4 u = bt * (vv - rk * P);

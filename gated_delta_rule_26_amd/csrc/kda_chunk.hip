@@ -129,10 +129,48 @@ template <typename OP, int TSZ, int C, int DK, int DV, int NW> struct ChunkShape
     static_assert(DK % (4 * SPL) == 0, "channel split");
 };
 
+// The part of M [C][C] (columns in step order) that the product M U reads: the 16-row band I
+// reads its first KS (I / TPS + 1) columns, i.e. the 16x16 blocks on and below the diagonal
+// plus, with two-tile steps, the zero block right of the diagonal for even I. The record
+// keeps only those columns, band after band, each row contiguous (fp16 operands, C = 64:
+// 6 KB instead of 8).
+template <typename OP, int C> struct MBands {
+    static constexpr int KS = Step<OP>::KS, TPS = Step<OP>::TPS, SZ = (int)sizeof(OP), NB = C / 16;
+    static_assert(C % KS == 0 && KS * ((NB - 1) / TPS + 1) <= C, "bands within the chunk");
+    // 16-byte pieces per row of band I, and the first piece of band I
+    static constexpr int ppr(int I) { return KS * (I / TPS + 1) * SZ / 16; }
+    static constexpr int base(int I) {
+        int b = 0;
+        for (int i = 0; i < I; ++i) b += 16 * ppr(i);
+        return b;
+    }
+    static constexpr int NP = base(NB);  // pieces in all
+    // Every band is a whole number of 64-piece groups (16 rows of KS * SZ = 64 bytes or a
+    // multiple), so the 64 pieces y = 64 g .. 64 g + 63 that one wave copies lie in one band.
+    static_assert(KS * SZ % 64 == 0, "bands of whole 64-piece groups");
+    // piece y (0 <= y < NP) -> row and first column (elements) of its 16 bytes; the lanes of
+    // a wave must pass y of one 64-piece group (the band is then worked out once per wave)
+    static __device__ __forceinline__ void piece(int y, int &row, int &col) {
+        const int g = __builtin_amdgcn_readfirstlane(y & ~63);
+        int I = 0;
+#pragma unroll
+        for (int k = 1; k < NB; ++k) I += g >= base(k) ? 1 : 0;
+        row = 0;
+        col = 0;
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+            if (I == k) {
+                const int yy = y - base(k);
+                row = 16 * k + yy / ppr(k);
+                col = (yy % ppr(k)) * (16 / SZ);
+            }
+    }
+};
+
 // Per-chunk record of a split segment (global memory, written by the chunked forward and read
 // by the replay passes). Dense copies of the LDS operands in the same element order:
-// W [C][Dk] and Qg [C][Dk] (columns in step order), Kd^T [Dk][C], M [C][C] (columns in step
-// order), then gC [Dk] float32 and U~ (operand type) in accumulator order
+// W [C][Dk] and Qg [C][Dk] (columns in step order), Kd^T [Dk][C], the bands of M read by
+// M U (MBands), then gC [Dk] float32 and U~ (operand type) in accumulator order
 // [Dv/16][C/16][64 lanes][4].
 template <typename OP, int C, int DK, int DV> struct Record {
     static constexpr int SZ = (int)sizeof(OP);
@@ -140,7 +178,7 @@ template <typename OP, int C, int DK, int DV> struct Record {
     static constexpr int oQ = oW + C * DK * SZ;
     static constexpr int oK = oQ + C * DK * SZ;
     static constexpr int oM = oK + DK * C * SZ;
-    static constexpr int OPS = oM + C * C * SZ;  // the LDS-staged part
+    static constexpr int OPS = oM + 16 * MBands<OP, C>::NP;  // the LDS-staged part
     static constexpr int oG = OPS;
     static constexpr int oU = oG + DK * 4;
     static constexpr int BYTES = (oU + C * DV * SZ + 255) & ~255;
@@ -549,6 +587,18 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
     constexpr bool kEarlyLoads = !FIN, kLateRecords = !FIN;
     // record the LDS operands (W, Qg, Kd^T, M, gC) of chunk cr of a split segment
     // (each thread copies 16-byte pieces tid, tid + NT, ...: one base offset per row width)
+    // M's banded pieces at LDS offsets worked out once (with the fused input steps, where
+    // the records are copied at the top of the next chunk, at the copy: fewer registers held)
+    using MB = MBands<OP, C>;
+    constexpr int MPT = (MB::NP + Sh::NT - 1) / Sh::NT;
+    auto m_offset = [&](int m) {
+        int r = 0, c = 0;
+        if (tid + m * Sh::NT < MB::NP) MB::piece(tid + m * Sh::NT, r, c);
+        return r * LDC + c;
+    };
+    int moff[MPT];
+#pragma unroll
+    for (int m = 0; m < MPT; ++m) moff[m] = kLateRecords ? m_offset(m) : 0;
     auto record_ops = [&](int64_t cr) {
         using Rc = Record<OP, C, DK, DV>;
         uint8_t *const rp = a.rec + (((int64_t)seg * chains + chain) * a.rec_chunks + cr) * Rc::BYTES;
@@ -569,7 +619,13 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         copy_rows(Wb, LDK, std::integral_constant<int, C>{}, std::integral_constant<int, DK * Rc::SZ / 16>{}, rp + Rc::oW);
         copy_rows(Qg, LDK, std::integral_constant<int, C>{}, std::integral_constant<int, DK * Rc::SZ / 16>{}, rp + Rc::oQ);
         copy_rows(KdT, LDC, std::integral_constant<int, DK>{}, std::integral_constant<int, C * Rc::SZ / 16>{}, rp + Rc::oK);
-        copy_rows(Mb, LDC, std::integral_constant<int, C>{}, std::integral_constant<int, C * Rc::SZ / 16>{}, rp + Rc::oM);
+#pragma unroll
+        for (int m = 0; m < MPT; ++m) {
+            const int y = tid + m * NT;
+            if (MB::NP % NT == 0 || y < MB::NP)
+                *reinterpret_cast<u32x4 *>(rp + Rc::oM + 16 * y) =
+                    *reinterpret_cast<const u32x4 *>(Mb + (kLateRecords ? moff[m] : m_offset(m)));
+        }
         if (tid < DK / 4)
             *reinterpret_cast<f32x4 *>(rp + Rc::oG + 16 * tid) = *reinterpret_cast<const f32x4 *>(gC + 4 * tid);
     };
@@ -1193,9 +1249,10 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
                   KS = ST::KS, TPS = ST::TPS, NT = 64 * NW, SZ = Rc::SZ;
     static_assert(DK == DV || !XMODE, "X lives in the state's column tiles");
     static_assert(!FOUT || (!XMODE && Sh::NCT == NW && CPW == 1), "fused output shape");
-    constexpr int WROW = DK * SZ, KROW = C * SZ, MROW = C * SZ;  // record row bytes
+    constexpr int WROW = DK * SZ, KROW = C * SZ;  // record row bytes
     // 16-byte pieces to stage: W, Qg, Kd^T, M (XMODE: W and Kd^T)
     constexpr int N16 = (XMODE ? Rc::oQ + (Rc::oM - Rc::oK) : Rc::OPS) / 16;
+    static_assert(Rc::oM % (16 * 64) == 0, "a wave's staged pieces of M lie in one band");
     constexpr int PPT = (N16 + NT - 1) / NT;                      // pieces per thread
 
     __shared__ __attribute__((aligned(16))) OP Wl[C * LDK];
@@ -1246,11 +1303,21 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
         const int b = 16 * x;
         return (XMODE && b >= Rc::oQ) ? b - Rc::oQ + Rc::oK : b;
     };
-    auto lds_of = [&](int b) -> OP * {
+    // LDS offsets of the pieces of M this thread stages, worked out once (M's pieces start at
+    // a multiple of 64, so each wave's pieces are all of M or all before it)
+    int mlo[PPT];
+#pragma unroll
+    for (int m = 0; m < PPT; ++m) {
+        const int x = tid + m * NT;
+        int r = 0, c = 0;
+        if (!XMODE && x >= Rc::oM / 16 && x < N16) MBands<OP, C>::piece(x - Rc::oM / 16, r, c);
+        mlo[m] = r * LDC + c;
+    }
+    auto lds_of = [&](int b, int m) -> OP * {
         if (b < Rc::oQ) return Wl + (b / WROW) * LDK + (b % WROW) / SZ;
         if (b < Rc::oK) return Ql + ((b - Rc::oQ) / WROW) * LDK + ((b - Rc::oQ) % WROW) / SZ;
         if (b < Rc::oM) return Kl + ((b - Rc::oK) / KROW) * LDC + ((b - Rc::oK) % KROW) / SZ;
-        return Ml + ((b - Rc::oM) / MROW) * LDC + ((b - Rc::oM) % MROW) / SZ;
+        return Ml + mlo[m];
     };
     u32x4 pre[PPT];
     f32x4 preg = {0.f, 0.f, 0.f, 0.f};
@@ -1280,7 +1347,7 @@ __global__ __launch_bounds__(64 * NW, 1) void replay_kernel(ChunkArgs a) {
 #pragma unroll
         for (int m = 0; m < PPT; ++m) {
             const int x = tid + m * NT;
-            if (x < N16) *reinterpret_cast<u32x4 *>(lds_of(rec_off(x))) = pre[m];
+            if (x < N16) *reinterpret_cast<u32x4 *>(lds_of(rec_off(x), m)) = pre[m];
         }
         if (tid < DK / 4) *reinterpret_cast<f32x4 *>(gl + 4 * tid) = preg;
         f32x4 Ur[CPW][NB];
@@ -1647,10 +1714,16 @@ int device_cus() {
     return n;
 }
 
+// Bytes of one chunk record, from the layout the kernels use (0 for a shape not built).
 int64_t record_bytes(int32_t in_dtype, int32_t C, int32_t Dk, int32_t Dv) {
-    const int64_t sz = in_dtype == 1 ? 2 : 4;  // matrix-core operand size
-    const int64_t b = (2 * (int64_t)C * Dk + (int64_t)Dk * C + (int64_t)C * C + (int64_t)C * Dv) * sz + Dk * 4;
-    return (b + 255) & ~(int64_t)255;
+    if (Dk != Dv) return 0;
+    if (in_dtype == 1) return C == 64 && Dk == 128 ? Record<_Float16, 64, 128, 128>::BYTES : 0;
+    if (C == 16 && Dk == 16) return Record<float, 16, 16, 16>::BYTES;
+    if (C == 16 && Dk == 32) return Record<float, 16, 32, 32>::BYTES;
+    if (C == 32 && Dk == 128) return Record<float, 32, 128, 128>::BYTES;
+    if (C == 64 && Dk == 32) return Record<float, 64, 32, 32>::BYTES;
+    if (C == 64 && Dk == 64) return Record<float, 64, 64, 64>::BYTES;
+    return 0;
 }
 
 SplitPlan plan_split(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t chunk,

@@ -374,9 +374,14 @@ FEW_SEGMENT_CASES = [
 
 def split_plan_bytes(T, H, D, C, stored, nseg, per):
     """Workspace bytes of a split into nseg segments of per chunks: maps R and X, start
-    states, and per-chunk records (2 C Dk + Dk C + C^2 + C Dv operands and Dk decays)."""
+    states, and per-chunk records (2 C Dk + Dk C + C Dv operands, the part of M that M U
+    reads, and Dk decays). M U runs in steps of ks reduction indices (32 with fp16 operands,
+    16 with float32, two or one 16-column tiles per step); 16-row band i reads its first
+    ks * (i // tiles + 1) columns."""
     sz = 2 if stored == "bf16" else 4
-    rec = (2 * C * D + D * C + C * C + C * D) * sz + D * 4
+    ks, tiles = (32, 2) if stored == "bf16" else (16, 1)
+    m_elems = sum(16 * ks * (i // tiles + 1) for i in range(C // 16))
+    rec = (2 * C * D + D * C + C * D + m_elems) * sz + D * 4
     rec = (rec + 255) // 256 * 256
     return (nseg - 1) * H * (D * D + D * D) * 4 + nseg * H * D * D * 4 + nseg * H * per * rec
 

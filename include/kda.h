@@ -355,7 +355,8 @@ kda_status kda_chunk_bwd_noalloc(int32_t B, int32_t T, int32_t H, int32_t Dk, in
  *   final_state    [N, W-1, C] dtype or NULL: each sequence's last W - 1 inputs (shifted in
  *                  from the initial state for sequences shorter than W - 1); may equal
  *                  initial_state
- * Supported: W = 4, C a multiple of 8. Errors as kda_chunk_fwd.
+ * y must not overlap x or the states. Supported: W = 4, C a multiple of 8. Errors as
+ * kda_chunk_fwd.
  */
 kda_status kda_short_conv_fwd(int32_t B, int32_t T, int32_t C, int32_t W, int32_t dtype,
                               int32_t activation, const void *x, const float *weight,

@@ -48,10 +48,11 @@ def raw(t, stored):
 
 @pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("stored", ["f32", "bf16"])
-@pytest.mark.parametrize("T,C", [(1, 8), (3, 256), (33, 2056), (100, 4096)])
+@pytest.mark.parametrize("T,C", [(1, 8), (3, 256), (33, 2056), (100, 4096), (300, 64)])
 def test_conv_batched_matches_oracle(T, C, stored, act):
-    """B = 2 sequences of T tokens (strips of 32 tokens, partial channel blocks), initial
-    states, final states."""
+    """B = 2 sequences of T tokens (strips of 64 tokens loaded in batches of 8 rows, a
+    sequence starting inside a strip and inside a batch, partial strips and channel blocks),
+    initial states, final states."""
     B = 2
     x, w, b, s0 = conv_case(T * 7 + C, B * T, C, stored, N=B)
     note(f"conv batched T={T} C={C} {stored} {act}")

@@ -603,8 +603,13 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_fwd_kernel(ChunkArgs a) {
         using Rc = Record<OP, C, DK, DV>;
         uint8_t *const rp = a.rec + (((int64_t)seg * chains + chain) * a.rec_chunks + cr) * Rc::BYTES;
         constexpr int NT = Sh::NT;
+        // the copy offsets are recomputed from the thread index at each copy (a few integer
+        // operations) rather than kept across the chunk loop, where they would be spilled
+        int tid_ = tid;
+        if (!kLateRecords) asm volatile("" : "+v"(tid_));
         auto copy_rows = [&](const OP *src, int ld, auto rows_c, auto per_c, uint8_t *dst) {
             constexpr int rows = decltype(rows_c)::value, per = decltype(per_c)::value;  // per: pieces per row
+            const int tid = tid_;
             const int r0 = tid / per, c0 = tid % per;
             const uint8_t *s0 = reinterpret_cast<const uint8_t *>(src + r0 * ld) + c0 * 16;
 #pragma unroll
